@@ -1,0 +1,144 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each mutant swaps one oracle building block for a plausibly wrong variant (a sign, an
+index, a transposed operand, a dropped term) and re-runs the pin tests; at least one
+pin has to fail.  The mutants live only inside this test and are undone afterwards.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import mla_oracle as M
+from tests import test_oracle_pins as pins
+
+PIN_TESTS = [
+    pins.test_worked_example_both_orders,
+    lambda: pins.test_rope_first_pair_is_plain_rotation(2.5),
+    pins.test_rope_frequency_ladder,
+    pins.test_rope_invariants,
+    pins.test_expanded_matches_library_sdpa,
+    pins.test_latent_attention_is_mqa_sdpa,
+    pins.test_softmax_weights_sum_to_one,
+    pins.test_single_token_returns_its_value,
+    pins.test_zero_query_gives_mean,
+    lambda: pins.test_absorbed_equals_expanded(0),
+    pins.test_head_blocks_are_row_blocks,
+    pins.test_combine_equals_unsplit,
+    pins.test_combine_closed_form,
+    pins.test_page_slot_example,
+    pins.test_gather_permuted_pool_equals_contiguous,
+    pins.test_append_then_gather,
+    pins.test_paged_decode_matches_per_sequence_sdpa,
+    pins.test_layer_single_token_closed_form,
+    pins.test_layer_matches_sdpa_composition,
+    pins.test_cache_sizes_from_pages,
+    pins.test_default_scale,
+]
+
+
+def _rope_clockwise(x, pos, base=10000.0):
+    return M_rope_orig(x, -np.asarray(pos, dtype=float), base)
+
+
+def _rope_wrong_freq(x, pos, base=10000.0):
+    x = np.asarray(x, float)
+    d = x.shape[-1]
+    k = np.arange(d // 2)
+    ang = np.asarray(pos, float)[..., None] * float(base) ** (-k / d)
+    c, s = np.cos(ang), np.sin(ang)
+    out = np.empty(np.broadcast_shapes(x.shape, ang.shape[:-1] + (d,)))
+    out[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+    out[..., 1::2] = x[..., 0::2] * s + x[..., 1::2] * c
+    return out
+
+
+def _rope_half_split(x, pos, base=10000.0):
+    """rotate-half pairing (i, i + d/2) instead of adjacent pairs"""
+    x = np.asarray(x, float)
+    d = x.shape[-1]
+    perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])
+    inv = np.argsort(perm)
+    y = M_rope_orig(x[..., inv], pos, base)
+    return y[..., perm]
+
+
+def _head_block_interleaved(w, i, d_h):
+    w = np.asarray(w, float)
+    H = w.shape[0] // d_h
+    return w[i::H, :]
+
+
+def _softmax_no_norm(s, axis=-1):
+    s = np.asarray(s, float)
+    return np.exp(s - np.max(s, axis=axis, keepdims=True))
+
+
+def _softmax_wrong_axis(s, axis=-1):
+    return M_softmax_orig(s, axis=0)
+
+
+def _page_slot_swapped(row, pos, P):
+    return int(row[pos % P]), pos // P
+
+
+def _combine_no_shift(o_parts, lse_parts):
+    o_parts, lse_parts = np.asarray(o_parts, float), np.asarray(lse_parts, float)
+    w = np.where(np.isfinite(lse_parts), lse_parts, 0.0)
+    den = np.sum(w, axis=0)
+    den_safe = np.where(den != 0, den, 1.0)
+    return np.sum(w[..., None] * o_parts, axis=0) / den_safe[..., None], np.log(np.abs(den_safe))
+
+
+def _cache_bytes_kv_twice(B, T, L, d_c, d_R, s):
+    return B * T * L * (2 * d_c + d_R) * s
+
+
+def _logsumexp_log2(s, axis=-1):
+    return M_lse_orig(s, axis) / math.log(2)
+
+
+def _absorb_no_transpose(q_c, w_uk):
+    # uses the column block of W^UK^T instead of the row block's transpose
+    q_c = np.asarray(q_c, float)
+    H, d_h = q_c.shape[-2], q_c.shape[-1]
+    w = np.asarray(w_uk, float)
+    out = np.empty(q_c.shape[:-1] + (w.shape[1],))
+    for i in range(H):
+        blk = w[i * d_h:(i + 1) * d_h, :]
+        out[..., i, :] = (q_c[..., i, :][..., ::-1]) @ blk
+    return out
+
+
+M_rope_orig = M.rope
+M_softmax_orig = M.softmax
+M_lse_orig = M.logsumexp
+
+MUTANTS = {
+    "rope_clockwise": ("rope", _rope_clockwise),
+    "rope_wrong_frequency": ("rope", _rope_wrong_freq),
+    "rope_rotate_half_pairs": ("rope", _rope_half_split),
+    "head_block_interleaved": ("head_block", _head_block_interleaved),
+    "softmax_unnormalised": ("softmax", _softmax_no_norm),
+    "softmax_wrong_axis": ("softmax", _softmax_wrong_axis),
+    "page_slot_swapped": ("page_slot", _page_slot_swapped),
+    "combine_linear_weights": ("combine_splits", _combine_no_shift),
+    "cache_bytes_k_and_v": ("cache_bytes", _cache_bytes_kv_twice),
+    "lse_in_log2": ("logsumexp", _logsumexp_log2),
+    "absorb_reversed_index": ("absorb_query", _absorb_no_transpose),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(M, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn)
+    failures = 0
+    for t in PIN_TESTS:
+        try:
+            t()
+        except Exception:  # an assertion or a shape error: the pin noticed
+            failures += 1
+    assert failures > 0, f"planted mistake {name} passed every pin"
