@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of absorbed MLA decode on one MI355X.
+
+One step = the decode hot path over one batch of the DeepSeek-V2-shaped workload
+(B=32 sequences, T=4096 cached tokens each, H=128 heads, d_c=512, d_R=64, bf16 cache and
+queries, 64-token pages): split-K attention over the paged latent cache followed by the
+log-sum-exp combine, both from libmla.  Inputs are seeded synthetic data, resident in HBM
+before timing starts.  Four copies of the 151 MB cache rotate between steps so the 256 MB
+Infinity Cache cannot serve a repeat.
+
+Prints ONE JSON line: throughput (latent-cache GB/s), the attention kernel's roofline
+position (HIP-event time per launch on the launch stream), and the fp64 CPU oracle timed
+on the host cores as a baseline.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MLA absorbed decode: latent-cache GB/s + MFMA TFLOP/s vs roofline, B32 T4K H128"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+ROW_BYTES = 576 * 2             # one cached token: c^KV (512) + k^R (64), bf16
+FLOP_PER_TOKEN_HEAD = 2 * (576 + 512)
+N_CACHE_COPIES = 4
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_dsv2_b32_t4k_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "head_latent_attention_15_amd", "csrc", "attn_mfma.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(launch_bytes_alg: float):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, n_seq: int):
+    """The fp64 oracle (unchanged) on the first n_seq sequences of the same workload."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity mask size
+        threads = len(os.sched_getaffinity(0))
+    bt = inp["block_table"].numpy()
+    sl = inp["seq_lens"].numpy()
+    P = inp["cache"].shape[1]
+    t0 = time.perf_counter()
+    toks = 0
+    for b in range(n_seq):
+        rows = oracle.gather_rows(W.to_f64(inp["cache"][bt[b, :math.ceil(sl[b] / P)].astype(np.int64)]),
+                                  np.arange(math.ceil(sl[b] / P)), int(sl[b]), P)
+        oracle.latent_attention(W.to_f64(inp["q_lat"][b]), W.to_f64(inp["q_pe"][b]), rows, 512,
+                                inp["scale"])
+        toks += int(sl[b])
+    dt = time.perf_counter() - t0
+    return {"value": round(toks * ROW_BYTES / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_seq} of 32 sequences x 4096 tokens (fp64 NumPy latent attention, "
+                      f"{dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--splits", type=int, default=0, help="split count (0: library suggestion)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=32)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration for --pmc runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the decode path here has no multi-GPU mode "
+              "(sequences shard across GPUs with no communication); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import head_latent_attention_15_amd as mla
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    num_cus = props.multi_processor_count
+
+    log("generating dsv2_b32_t4k inputs")
+    inp = W.dsv2_b32_t4k()
+    B, H, T = 32, 128, 4096
+    S = args.splits or mla.mla_suggest_num_splits(B, T, 0, 64, num_cus)
+    caches = [inp["cache"].to(dev)]
+    for _ in range(N_CACHE_COPIES - 1):
+        caches.append(caches[0].clone())
+    q_lat, q_pe = inp["q_lat"].to(dev), inp["q_pe"].to(dev)
+    bt, sl = inp["block_table"].to(dev), inp["seq_lens"].to(dev)
+    o_part = torch.empty(B, H, S, 512, device=dev)
+    lse_part = torch.empty(B, H, S, device=dev)
+    out = torch.empty(B, H, 512, device=dev)
+    lse = torch.empty(B, H, device=dev)
+    scale = inp["scale"]
+
+    def step(k, ev=None):
+        if ev is not None:
+            ev[0].record()
+        mla.mla_decode_attn(q_lat, q_pe, caches[k % N_CACHE_COPIES], bt, sl, scale, S, o_part, lse_part)
+        if ev is not None:
+            ev[1].record()
+        mla.mla_splitk_combine(o_part, lse_part, out, lse)
+        if ev is not None:
+            ev[2].record()
+
+    log(f"warmup {args.warmup} steps, S={S}, {num_cus} CUs")
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        step(k, evs[k])
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    comb_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    comb_avg = sum(comb_ms) / len(comb_ms)
+    log(f"step {ms_step * 1e3:.1f} us; attention {attn_avg * 1e3:.1f} us (min {min(attn_ms) * 1e3:.1f}); "
+        f"combine {comb_avg * 1e3:.1f} us")
+
+    # plain streaming read of one cache copy: the practical HBM read ceiling
+    sink = torch.empty(4096, device=dev)
+    for _ in range(3):
+        mla.mla_stream_read(caches[1], sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for k in range(reps):
+        mla.mla_stream_read(caches[k % N_CACHE_COPIES], sink)
+    e1.record()
+    torch.cuda.synchronize()
+    stream_gbps = caches[0].numel() * 2 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b_ = torch.empty_like(a)
+        b_.copy_(a)
+        torch.cuda.synchronize()
+        del a, b_
+
+    tokens = B * T
+    cache_bytes = tokens * ROW_BYTES
+    step_alg_bytes = cache_bytes + B * H * 576 * 2 + B * H * 512 * 4 + bt.numel() * 4 + B * 4
+    flops = tokens * H * FLOP_PER_TOKEN_HEAD
+    attn_s = attn_avg * 1e-3
+    achieved = cache_bytes / attn_s / 1e9
+    traffic = measured_traffic(cache_bytes)
+    result = {
+        "metric": METRIC,
+        "value": round(cache_bytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "dsv2_b32_t4k", "B": B, "T": T, "H": H, "d_c": 512, "d_R": 64,
+                   "page_size": 64, "num_splits": S, "cache_copies": N_CACHE_COPIES,
+                   "parallelism": "none"},
+        "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "query_tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "step_bytes_algorithmic": step_alg_bytes,
+        "attn_us": round(attn_avg * 1e3, 2),
+        "combine_us": round(comb_avg * 1e3, 2),
+        "attn_tflops": round(flops / attn_s / 1e12, 2),
+        "mfma_frac_of_peak": round(flops / attn_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "stream_read_GBps": round(stream_gbps, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": "attn_mfma_kernel (8 waves x 16 heads)",
+                     "bytes_per_launch_algorithmic": cache_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the fp64 oracle on {args.cpu_seqs} sequences")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

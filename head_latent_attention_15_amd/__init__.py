@@ -1,0 +1,313 @@
+"""MI355X (gfx950) weight-absorbed MLA decode.
+
+Thin ctypes binding of ``libmla.so`` (C ABI in ``include/mla.h``).  Every step of the
+decode path runs in the library's HIP kernels; this module only checks torch tensors
+(device, dtype, contiguity, shapes), passes their device pointers and the current HIP
+stream, and raises :class:`MLAError` on a non-OK status.  PyTorch is used for device
+memory and streams only.  There is no fallback: if the library is missing, importing the
+bindings raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+# torch first: it ships its own libamdhip64 (SONAME libamdhip64.so.7).  Loaded before
+# libmla.so, that copy satisfies libmla's dependency, so the process has one HIP runtime
+# and libmla's kernels run on torch's device context and streams.
+import torch  # noqa: F401
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "mla.h")
+
+MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED = 0, 1, 2, 3
+MLA_ERR_WORKSPACE, MLA_ERR_LAUNCH, MLA_ERR_INDEX = 4, 5, 6
+MLA_F32, MLA_BF16 = 0, 1
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_status_name(status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class _PagedShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+_SP = ctypes.POINTER(_PagedShape)
+
+_SIGNATURES = {
+    "mla_cache_bytes": (_SZ, [_I64, _I64, _I64, _I32, _I32, _I32]),
+    "mla_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "mla_suggest_num_splits": (_I32, [_I32, _I32, _I64, _I32, _I32]),
+    "mla_absorb_q": (_I32, [_P, _P, _P, _P, _F, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                            _I32, _P]),
+    "mla_kv_append": (_I32, [_P, _P, _I32, _P, _P, _P, _F, _SP, _I32, _P]),
+    "mla_decode_attn": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _P, _I32, _P]),
+    "mla_splitk_combine": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    "mla_decode": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _SZ, _P, _P, _I32, _P]),
+    "mla_out_proj": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    "mla_linear": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P]),
+    "mla_validate_indices": (_I32, [_P, _P, _SP, _P, _P]),
+    "mla_stream_read": (_I32, [_P, _SZ, _P, _P]),
+    "mla_status_string": (ctypes.c_char_p, [_I32]),
+    "mla_last_error_detail": (ctypes.c_char_p, []),
+}
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/mla.h."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m head_latent_attention_15_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _status_name(st: int) -> str:
+    return lib.mla_status_string(st).decode()
+
+
+def _check(st: int) -> None:
+    if st != MLA_OK:
+        raise MLAError(st, lib.mla_last_error_detail().decode())
+
+
+# ----------------------------------------------------------------------------- helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MLA_F32
+    if t.dtype == torch.bfloat16:
+        return MLA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    """Device pointer of a contiguous GPU tensor (None -> NULL)."""
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _expect(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def paged_shape(kv_cache, block_table, num_heads: int, d_latent: int) -> _PagedShape:
+    pages, P, row = kv_cache.shape
+    B, maxp = block_table.shape
+    return _PagedShape(B, num_heads, d_latent, row - d_latent, P, maxp, pages)
+
+
+# ----------------------------------------------------------------------------- sizes
+def mla_cache_bytes(B, T, layers, d_c, d_R, elem_bytes) -> int:
+    return int(lib.mla_cache_bytes(B, T, layers, d_c, d_R, elem_bytes))
+
+
+def mla_decode_workspace_bytes(B, H, d_c, num_splits) -> int:
+    return int(lib.mla_decode_workspace_bytes(B, H, d_c, num_splits))
+
+
+def mla_suggest_num_splits(B, max_seq_len, total_tokens=0, page_size=64, num_cus=256) -> int:
+    return int(lib.mla_suggest_num_splits(B, max_seq_len, total_tokens, page_size, num_cus))
+
+
+def mla_status_string(status: int) -> str:
+    return _status_name(status)
+
+
+def mla_last_error_detail() -> str:
+    return lib.mla_last_error_detail().decode()
+
+
+# ----------------------------------------------------------------------------- hot path
+def mla_absorb_q(q_c, w_uk, q_r, seq_lens, rope_base, q_lat, q_pe, stream=None):
+    """q_lat = W^UK_i^T q^C_i per head; q_pe = RoPE(q_r, seq_lens - 1).
+    q_c [B,H,d_h] f32, w_uk [H*d_h, d_c], q_r [B,H,d_R] f32 or None, q_lat [B,H,d_c],
+    q_pe [B,H,d_R] (q_lat / q_pe share one dtype)."""
+    torch = _torch()
+    B, H, d_h = q_c.shape
+    d_c = w_uk.shape[1]
+    _expect(w_uk.shape[0] == H * d_h, "w_uk must be [H*d_h, d_c]")
+    _expect(tuple(q_lat.shape) == (B, H, d_c), "q_lat must be [B,H,d_c]")
+    d_R = q_r.shape[2] if q_r is not None else 0
+    if q_r is not None:
+        _expect(tuple(q_r.shape) == (B, H, d_R) and tuple(q_pe.shape) == (B, H, d_R),
+                "q_r and q_pe must be [B,H,d_R]")
+        _expect(q_pe.dtype == q_lat.dtype, "q_pe and q_lat must share a dtype")
+        _expect(tuple(seq_lens.shape) == (B,), "seq_lens must be [B]")
+    _check(lib.mla_absorb_q(
+        _dev(q_c, "q_c", torch.float32, 3), _dev(w_uk, "w_uk", None, 2),
+        _dev(q_r, "q_r", torch.float32, 3), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        float(rope_base), _dev(q_lat, "q_lat", None, 3), _dev(q_pe, "q_pe", None, 3),
+        B, H, d_h, d_c, d_R, _dtype_code(w_uk), _dtype_code(q_lat), _stream(stream)))
+
+
+def mla_kv_append(c_kv, k_r, seq_lens_before, block_table, kv_cache, rope_base, stream=None):
+    """Write [c_kv | RoPE(k_r, pos)] rows at positions seq_lens_before[b] + t.
+    c_kv [B,n,d_c] f32, k_r [B,n,d_R] f32, kv_cache [pages, P, d_c + d_R]."""
+    torch = _torch()
+    B, n, d_c = c_kv.shape
+    _expect(k_r.shape[0] == B and k_r.shape[1] == n, "k_r must be [B,n,d_R]")
+    _expect(kv_cache.shape[2] == d_c + k_r.shape[2], "cache row must be d_c + d_R wide")
+    _expect(block_table.shape[0] == B and tuple(seq_lens_before.shape) == (B,), "batch mismatch")
+    shp = paged_shape(kv_cache, block_table, 1, d_c)
+    _check(lib.mla_kv_append(
+        _dev(c_kv, "c_kv", torch.float32, 3), _dev(k_r, "k_r", torch.float32, 3), n,
+        _dev(seq_lens_before, "seq_lens_before", torch.int32, 1),
+        _dev(block_table, "block_table", torch.int32, 2), _dev(kv_cache, "kv_cache", None, 3),
+        float(rope_base), ctypes.byref(shp), _dtype_code(kv_cache), _stream(stream)))
+
+
+def mla_decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale, num_splits,
+                    o_part, lse_part=None, stream=None):
+    """Split-K decode attention; o_part [B,H,S,d_c] (or [B,H,d_c] when S == 1),
+    lse_part [B,H,S] (or [B,H] / None when S == 1)."""
+    torch = _torch()
+    B, H, d_c = q_lat.shape
+    _expect(q_pe.shape[0] == B and q_pe.shape[1] == H, "q_pe must be [B,H,d_R]")
+    _expect(q_pe.dtype == q_lat.dtype == kv_cache.dtype, "q_lat, q_pe, kv_cache share a dtype")
+    _expect(kv_cache.shape[2] == d_c + q_pe.shape[2], "cache row must be d_c + d_R wide")
+    _expect(block_table.shape[0] == B and tuple(seq_lens.shape) == (B,), "batch mismatch")
+    S = int(num_splits)
+    want = (B, H, d_c) if S == 1 else (B, H, S, d_c)
+    _expect(tuple(o_part.shape) == want or (S == 1 and tuple(o_part.shape) == (B, H, 1, d_c)),
+            f"o_part must be {want}")
+    if lse_part is not None:
+        _expect(lse_part.numel() == B * H * S, "lse_part must hold B*H*S floats")
+    shp = paged_shape(kv_cache, block_table, H, d_c)
+    _check(lib.mla_decode_attn(
+        _dev(q_lat, "q_lat", None, 3), _dev(q_pe, "q_pe", None, 3),
+        _dev(kv_cache, "kv_cache", None, 3), _dev(block_table, "block_table", torch.int32, 2),
+        _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), float(softmax_scale), S,
+        _dev(o_part, "o_part", torch.float32), _dev(lse_part, "lse_part", torch.float32),
+        _dtype_code(q_lat), _stream(stream)))
+
+
+def mla_splitk_combine(o_part, lse_part, out, lse_out=None, stream=None):
+    torch = _torch()
+    B, H, S, d_c = o_part.shape
+    _expect(tuple(lse_part.shape) == (B, H, S), "lse_part must be [B,H,S]")
+    _expect(tuple(out.shape) == (B, H, d_c), "out must be [B,H,d_c]")
+    if lse_out is not None:
+        _expect(tuple(lse_out.shape) == (B, H), "lse_out must be [B,H]")
+    _check(lib.mla_splitk_combine(
+        _dev(o_part, "o_part", torch.float32, 4), _dev(lse_part, "lse_part", torch.float32, 3),
+        B, H, S, d_c, _dev(out, "out", torch.float32, 3),
+        _dev(lse_out, "lse_out", torch.float32, 2), _stream(stream)))
+
+
+def mla_decode(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale, num_splits,
+               workspace, out, lse_out=None, stream=None):
+    """Attention + combine with the split partials in `workspace` (uint8 tensor of at
+    least mla_decode_workspace_bytes bytes; may be None when num_splits == 1)."""
+    torch = _torch()
+    B, H, d_c = q_lat.shape
+    _expect(q_pe.dtype == q_lat.dtype == kv_cache.dtype, "q_lat, q_pe, kv_cache share a dtype")
+    _expect(tuple(out.shape) == (B, H, d_c), "out must be [B,H,d_c]")
+    shp = paged_shape(kv_cache, block_table, H, d_c)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.mla_decode(
+        _dev(q_lat, "q_lat", None, 3), _dev(q_pe, "q_pe", None, 3),
+        _dev(kv_cache, "kv_cache", None, 3), _dev(block_table, "block_table", torch.int32, 2),
+        _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), float(softmax_scale),
+        int(num_splits), ws_ptr, ws_bytes, _dev(out, "out", torch.float32, 3),
+        _dev(lse_out, "lse_out", torch.float32, 2), _dtype_code(q_lat), _stream(stream)))
+
+
+def mla_out_proj(o_lat, w_uv, w_o, o_heads, u=None, stream=None):
+    """o_heads = W^UV_i o_lat_i per head; u = W^O concat(o_heads) when w_o is given."""
+    torch = _torch()
+    B, H, d_c = o_lat.shape
+    d_h = w_uv.shape[0] // H
+    _expect(tuple(w_uv.shape) == (H * d_h, d_c), "w_uv must be [H*d_h, d_c]")
+    _expect(tuple(o_heads.shape) == (B, H, d_h), "o_heads must be [B,H,d_h]")
+    d_model = 0
+    if w_o is not None:
+        d_model = w_o.shape[0]
+        _expect(tuple(w_o.shape) == (d_model, H * d_h), "w_o must be [d_model, H*d_h]")
+        _expect(w_o.dtype == w_uv.dtype, "w_o and w_uv share a dtype")
+        _expect(u is not None and tuple(u.shape) == (B, d_model), "u must be [B, d_model]")
+    _check(lib.mla_out_proj(
+        _dev(o_lat, "o_lat", torch.float32, 3), _dev(w_uv, "w_uv", None, 2),
+        _dev(w_o, "w_o", None, 2), B, H, d_c, d_h, d_model, _dtype_code(w_uv),
+        _dev(o_heads, "o_heads", torch.float32, 3), _dev(u, "u", torch.float32, 2),
+        _stream(stream)))
+
+
+def mla_linear(x, w, y, stream=None):
+    """y = x w^T; x [M,K], w [N,K], y [M,N] fp32."""
+    torch = _torch()
+    M, K = x.shape
+    N = w.shape[0]
+    _expect(w.shape[1] == K and tuple(y.shape) == (M, N), "shapes must be x[M,K] w[N,K] y[M,N]")
+    _check(lib.mla_linear(_dev(x, "x", None, 2), _dtype_code(x), _dev(w, "w", None, 2),
+                          _dtype_code(w), M, N, K, _dev(y, "y", torch.float32, 2),
+                          _stream(stream)))
+
+
+def mla_validate_indices(block_table, seq_lens, page_size, num_pages, dev_count, stream=None):
+    torch = _torch()
+    B, maxp = block_table.shape
+    shp = _PagedShape(B, 1, 1, 2, page_size, maxp, num_pages)
+    _check(lib.mla_validate_indices(
+        _dev(block_table, "block_table", torch.int32, 2), _dev(seq_lens, "seq_lens", torch.int32, 1),
+        ctypes.byref(shp), _dev(dev_count, "dev_count", torch.int32), _stream(stream)))
+
+
+def mla_stream_read(src, sink, stream=None):
+    torch = _torch()
+    _expect(sink.numel() >= 4096, "sink must hold 4096 floats")
+    _check(lib.mla_stream_read(_dev(src, "src"), src.numel() * src.element_size(),
+                               _dev(sink, "sink", torch.float32), _stream(stream)))

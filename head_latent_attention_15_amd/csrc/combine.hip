@@ -1,0 +1,80 @@
+// Log-sum-exp combine of split-K partials.
+//
+// Split s of a (sequence, head) saw a disjoint token range and produced its own
+// normalised latent sum o_s and lse_s = ln sum_j e^{score_j}.  The softmax over all tokens
+// is recovered exactly by weighting each split with e^{lse_s - M} (M = max lse): the
+// softmax denominator is a sum over the tokens (qiita.com/joule "Attention 計算").
+//
+// One workgroup per (sequence, head); each thread owns 4 consecutive latent columns
+// (one 16-byte load per split), the weights live in LDS.  Deterministic: fixed summation
+// order, no atomics.
+#include "device_common.h"
+#include "launchers.h"
+
+namespace mla {
+
+constexpr int kCombineThreads = 128;
+
+__global__ __launch_bounds__(kCombineThreads) void splitk_combine_kernel(
+    const float* __restrict__ o_part, const float* __restrict__ lse_part, int S, int d_c,
+    float* __restrict__ out, float* __restrict__ lse_out) {
+  extern __shared__ float w_lds[];  // S weights
+  __shared__ float red[kCombineThreads / 64];
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* lse = lse_part + static_cast<int64_t>(bh) * S;
+
+  float m = -INFINITY;
+  for (int s = tid; s < S; s += kCombineThreads) m = fmaxf(m, lse[s]);
+  m = wave_max(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < kCombineThreads / 64; ++w) m = fmaxf(m, red[w]);
+  __syncthreads();
+
+  const float msafe = (m == -INFINITY) ? 0.f : m;
+  float part = 0.f;
+  for (int s = tid; s < S; s += kCombineThreads) {
+    const float x = lse[s];
+    const float w = (x == -INFINITY) ? 0.f : expf(x - msafe);
+    w_lds[s] = w;
+    part += w;
+  }
+  part = wave_sum(part);
+  if ((tid & 63) == 0) red[tid >> 6] = part;
+  __syncthreads();
+  float den = 0.f;
+#pragma unroll
+  for (int w = 0; w < kCombineThreads / 64; ++w) den += red[w];
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+
+  const float* base = o_part + static_cast<int64_t>(bh) * S * d_c;
+  for (int c = tid * 4; c < d_c; c += kCombineThreads * 4) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < S; ++s) {
+      const float w = w_lds[s];
+      if (w != 0.f) {
+        const float4 v = *reinterpret_cast<const float4*>(base + static_cast<int64_t>(s) * d_c + c);
+        acc.x += w * v.x;
+        acc.y += w * v.y;
+        acc.z += w * v.z;
+        acc.w += w * v.w;
+      }
+    }
+    acc.x *= inv; acc.y *= inv; acc.z *= inv; acc.w *= inv;
+    *reinterpret_cast<float4*>(out + static_cast<int64_t>(bh) * d_c + c) = acc;
+  }
+  if (tid == 0 && lse_out != nullptr) lse_out[bh] = den > 0.f ? msafe + logf(den) : -INFINITY;
+}
+
+hipError_t launch_splitk_combine(const float* o_part, const float* lse_part, int B, int H,
+                                 int S, int d_c, float* out, float* lse_out, hipStream_t st) {
+  const size_t lds = static_cast<size_t>(S) * sizeof(float);
+  hipLaunchKernelGGL(splitk_combine_kernel, dim3(B * H), dim3(kCombineThreads), lds, st,
+                     o_part, lse_part, S, d_c, out, lse_out);
+  return hipGetLastError();
+}
+
+}  // namespace mla

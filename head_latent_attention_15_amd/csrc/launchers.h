@@ -1,0 +1,61 @@
+// Host-side launchers of the libmla kernels.  Arguments are validated by the C ABI layer
+// (mla_api.cpp) before any of these is called; each launcher only sizes the grid and
+// enqueues on the given stream, returning the runtime's launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct PagedArgs {
+  const void* q_lat;
+  const void* q_pe;
+  const void* cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int32_t B, H, d_c, d_R, page_size, max_pages, num_pages;
+  float scale;
+  int32_t num_splits;
+  int32_t pages_per_split;
+  float* o_part;
+  float* lse_part;
+};
+
+// Decode attention, one wavefront per (sequence, head, split), fp32 VALU math.
+hipError_t launch_attn_generic_f32_64_16(const PagedArgs& a, hipStream_t s);
+hipError_t launch_attn_generic_bf16_512_64(const PagedArgs& a, hipStream_t s);
+// Decode attention on bf16 MFMA, all heads of a (sequence, split) per workgroup.
+hipError_t launch_attn_mfma_bf16_512_64(const PagedArgs& a, hipStream_t s);
+bool attn_mfma_supported(const PagedArgs& a);
+
+hipError_t launch_splitk_combine(const float* o_part, const float* lse_part, int B, int H,
+                                 int S, int d_c, float* out, float* lse_out, hipStream_t s);
+
+// Batched small-M GEMM: y[z][m][n] = sum_k x[z][m][k] * W_z(n, k), with
+// W_z(n, k) = w[z*sw + n*ldw + k] when w_nk, else w[z*sw + k*ldw + n].
+// x/w dtype: 0 = fp32, 1 = bf16; y dtype likewise.
+struct GemmArgs {
+  const void* x; int64_t ldx, sx; int x_bf16;
+  const void* w; int64_t ldw, sw; int w_bf16; bool w_nk;
+  void* y; int64_t ldy, sy; int y_bf16;
+  int M, N, K, batch;
+};
+hipError_t launch_gemm_small(const GemmArgs& g, hipStream_t s);
+
+hipError_t launch_rope_rows(const float* x, int64_t rows, int rows_per_seq, int d_R,
+                            const int32_t* seq_lens, int pos_offset, float base, void* out,
+                            int out_bf16, hipStream_t s);
+
+hipError_t launch_kv_append(const float* c_kv, const float* k_r, int n_new,
+                            const int32_t* seq_lens_before, const int32_t* block_table,
+                            void* cache, int cache_bf16, float base, int B, int d_c, int d_R,
+                            int page_size, int max_pages, hipStream_t s);
+
+hipError_t launch_validate_indices(const int32_t* block_table, const int32_t* seq_lens, int B,
+                                   int page_size, int max_pages, int num_pages, int32_t* count,
+                                   hipStream_t s);
+
+hipError_t launch_stream_read(const void* src, size_t bytes, float* sink, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,322 @@
+// C ABI of libmla: host-side validation, split planning and dispatch to the kernels.
+// Every check runs before any HIP call, so a rejected call touches no device state.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launchers.h"
+#include "mla.h"
+
+namespace {
+
+thread_local char g_detail[512] = "";
+
+mla_status_t fail(mla_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+mla_status_t ok() {
+  g_detail[0] = '\0';
+  return MLA_OK;
+}
+
+mla_status_t launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MLA_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+bool is_dtype(mla_dtype_t d) { return d == MLA_F32 || d == MLA_BF16; }
+
+constexpr int kMaxSplits = 4096;
+
+int32_t pages_per_split(int32_t max_pages, int32_t num_splits) {
+  return (max_pages + num_splits - 1) / num_splits;
+}
+
+mla_status_t check_paged_shape(const mla_paged_shape_t* shp) {
+  if (shp == nullptr) return fail(MLA_ERR_NULL, "shape is NULL");
+  if (shp->batch < 1 || shp->num_heads < 1 || shp->d_latent < 1 || shp->d_rope < 1 ||
+      shp->page_size < 1 || shp->max_pages_per_seq < 1 || shp->num_pages < 1)
+    return fail(MLA_ERR_SHAPE,
+                "shape fields must be >= 1 (B=%d H=%d d_c=%d d_R=%d P=%d max_pages=%d pages=%d)",
+                shp->batch, shp->num_heads, shp->d_latent, shp->d_rope, shp->page_size,
+                shp->max_pages_per_seq, shp->num_pages);
+  if (shp->page_size % 16 != 0)
+    return fail(MLA_ERR_SHAPE, "page_size %d is not a multiple of 16", shp->page_size);
+  if (shp->d_rope % 2 != 0) return fail(MLA_ERR_SHAPE, "d_rope %d is odd", shp->d_rope);
+  if (static_cast<int64_t>(shp->max_pages_per_seq) * shp->page_size > INT32_MAX)
+    return fail(MLA_ERR_SHAPE, "max_pages_per_seq * page_size overflows int32");
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status_t st) {
+  switch (st) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_LAUNCH: return "MLA_ERR_LAUNCH";
+    case MLA_ERR_INDEX: return "MLA_ERR_INDEX";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+const char* mla_last_error_detail(void) { return g_detail; }
+
+size_t mla_cache_bytes(int64_t B, int64_t T, int64_t layers, int32_t d_c, int32_t d_R,
+                       int32_t elem_bytes) {
+  if (B < 0 || T < 0 || layers < 0 || d_c < 0 || d_R < 0 || elem_bytes < 0) return 0;
+  return static_cast<size_t>(B) * static_cast<size_t>(T) * static_cast<size_t>(layers) *
+         static_cast<size_t>(d_c + d_R) * static_cast<size_t>(elem_bytes);
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+size_t mla_decode_workspace_bytes(int32_t B, int32_t H, int32_t d_c, int32_t num_splits) {
+  if (B < 1 || H < 1 || d_c < 1 || num_splits < 1) return 0;
+  const size_t rows = static_cast<size_t>(B) * H * num_splits;
+  return align256(rows * d_c * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+int32_t mla_suggest_num_splits(int32_t B, int32_t max_seq_len, int64_t total_tokens,
+                               int32_t page_size, int32_t num_cus) {
+  if (B < 1 || max_seq_len < 1 || page_size < 1) return 1;
+  if (num_cus < 1) num_cus = 256;
+  const int64_t max_pages = (static_cast<int64_t>(max_seq_len) + page_size - 1) / page_size;
+  int64_t S;
+  if (total_tokens <= 0 || total_tokens >= static_cast<int64_t>(B) * max_seq_len) {
+    // uniform lengths: one (sequence, split) item per compute unit
+    S = (num_cus + B - 1) / B;
+  } else {
+    // ragged: split size from the mean load per compute unit, at most a quarter of it so
+    // that uneven sequence ends still balance
+    const int64_t total_pages = (total_tokens + page_size - 1) / page_size;
+    int64_t cps = total_pages / (4 * static_cast<int64_t>(num_cus));
+    if (cps < 1) cps = 1;
+    S = (max_pages + cps - 1) / cps;
+  }
+  if (S > max_pages) S = max_pages;
+  if (S > kMaxSplits) S = kMaxSplits;
+  if (S < 1) S = 1;
+  return static_cast<int32_t>(S);
+}
+
+mla_status_t mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_cache,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const mla_paged_shape_t* shape, float softmax_scale,
+                             int32_t num_splits, float* o_part, float* lse_part,
+                             mla_dtype_t dtype, void* stream) {
+  if (!q_lat || !q_pe || !kv_cache || !block_table || !seq_lens || !o_part)
+    return fail(MLA_ERR_NULL, "mla_decode_attn: a required pointer is NULL");
+  mla_status_t st = check_paged_shape(shape);
+  if (st != MLA_OK) return st;
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(MLA_ERR_SHAPE, "num_splits %d outside [1, %d]", num_splits, kMaxSplits);
+  if (num_splits > 1 && lse_part == nullptr)
+    return fail(MLA_ERR_NULL, "lse_part is NULL with num_splits %d > 1", num_splits);
+  if (!std::isfinite(softmax_scale))
+    return fail(MLA_ERR_SHAPE, "softmax_scale is not finite");
+  if (!is_dtype(dtype)) return fail(MLA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+
+  mla::PagedArgs a;
+  a.q_lat = q_lat;
+  a.q_pe = q_pe;
+  a.cache = kv_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.B = shape->batch;
+  a.H = shape->num_heads;
+  a.d_c = shape->d_latent;
+  a.d_R = shape->d_rope;
+  a.page_size = shape->page_size;
+  a.max_pages = shape->max_pages_per_seq;
+  a.num_pages = shape->num_pages;
+  a.scale = softmax_scale;
+  a.num_splits = num_splits;
+  a.pages_per_split = pages_per_split(shape->max_pages_per_seq, num_splits);
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  hipStream_t s = as_stream(stream);
+
+  if (dtype == MLA_BF16 && a.d_c == 512 && a.d_R == 64 && a.H <= 128) {
+    if (mla::attn_mfma_supported(a))
+      return launched(mla::launch_attn_mfma_bf16_512_64(a, s), "attention (bf16 MFMA)");
+    return launched(mla::launch_attn_generic_bf16_512_64(a, s), "attention (bf16 generic)");
+  }
+  if (dtype == MLA_F32 && a.d_c == 64 && a.d_R == 16 && a.H <= 64)
+    return launched(mla::launch_attn_generic_f32_64_16(a, s), "attention (fp32)");
+  return fail(MLA_ERR_UNSUPPORTED,
+              "mla_decode_attn: (d_latent=%d, d_rope=%d, H=%d, dtype=%d) is not compiled; "
+              "supported: (512, 64, H<=128, BF16) and (64, 16, H<=64, F32)",
+              a.d_c, a.d_R, a.H, dtype);
+}
+
+mla_status_t mla_splitk_combine(const float* o_part, const float* lse_part, int32_t B,
+                                int32_t H, int32_t num_splits, int32_t d_c, float* out,
+                                float* lse_out, void* stream) {
+  if (!o_part || !lse_part || !out)
+    return fail(MLA_ERR_NULL, "mla_splitk_combine: a required pointer is NULL");
+  if (B < 1 || H < 1 || d_c < 1 || num_splits < 1 || num_splits > kMaxSplits)
+    return fail(MLA_ERR_SHAPE, "mla_splitk_combine: bad sizes B=%d H=%d S=%d d_c=%d", B, H,
+                num_splits, d_c);
+  if (d_c % 4 != 0) return fail(MLA_ERR_SHAPE, "mla_splitk_combine: d_c %d %% 4 != 0", d_c);
+  return launched(mla::launch_splitk_combine(o_part, lse_part, B, H, num_splits, d_c, out,
+                                             lse_out, as_stream(stream)),
+                  "split-K combine");
+}
+
+mla_status_t mla_decode(const void* q_lat, const void* q_pe, const void* kv_cache,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        const mla_paged_shape_t* shape, float softmax_scale,
+                        int32_t num_splits, void* workspace, size_t workspace_bytes,
+                        float* out, float* lse_out, mla_dtype_t dtype, void* stream) {
+  if (num_splits == 1)
+    return mla_decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, shape, softmax_scale,
+                           1, out, lse_out, dtype, stream);
+  mla_status_t st = check_paged_shape(shape);
+  if (st != MLA_OK) return st;
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(MLA_ERR_SHAPE, "num_splits %d outside [1, %d]", num_splits, kMaxSplits);
+  const size_t need =
+      mla_decode_workspace_bytes(shape->batch, shape->num_heads, shape->d_latent, num_splits);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "mla_decode: workspace %zu bytes, need %zu",
+                workspace ? workspace_bytes : static_cast<size_t>(0), need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(MLA_ERR_WORKSPACE, "mla_decode: workspace is not 16-byte aligned");
+  const size_t rows = static_cast<size_t>(shape->batch) * shape->num_heads * num_splits;
+  float* o_part = static_cast<float*>(workspace);
+  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             align256(rows * shape->d_latent * sizeof(float)));
+  st = mla_decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, shape, softmax_scale,
+                       num_splits, o_part, lse_part, dtype, stream);
+  if (st != MLA_OK) return st;
+  return mla_splitk_combine(o_part, lse_part, shape->batch, shape->num_heads, num_splits,
+                            shape->d_latent, out, lse_out, stream);
+}
+
+mla_status_t mla_absorb_q(const float* q_c, const void* w_uk, const float* q_r,
+                          const int32_t* seq_lens, float rope_base, void* q_lat, void* q_pe,
+                          int32_t B, int32_t H, int32_t d_h, int32_t d_c, int32_t d_R,
+                          mla_dtype_t w_dtype, mla_dtype_t out_dtype, void* stream) {
+  if (!q_c || !w_uk || !q_lat) return fail(MLA_ERR_NULL, "mla_absorb_q: NULL q_c/w_uk/q_lat");
+  if (q_r && (!q_pe || !seq_lens))
+    return fail(MLA_ERR_NULL, "mla_absorb_q: q_r given but q_pe or seq_lens is NULL");
+  if (B < 1 || H < 1 || d_h < 1 || d_c < 1 || (q_r && d_R < 1))
+    return fail(MLA_ERR_SHAPE, "mla_absorb_q: sizes must be >= 1");
+  if (q_r && d_R % 2) return fail(MLA_ERR_SHAPE, "mla_absorb_q: d_R %d is odd", d_R);
+  if (!is_dtype(w_dtype) || !is_dtype(out_dtype))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_absorb_q: unknown dtype");
+  if (q_r && !std::isfinite(rope_base))
+    return fail(MLA_ERR_SHAPE, "mla_absorb_q: rope_base not finite");
+  hipStream_t s = as_stream(stream);
+  mla::GemmArgs g;
+  g.x = q_c; g.ldx = static_cast<int64_t>(H) * d_h; g.sx = d_h; g.x_bf16 = 0;
+  g.w = w_uk; g.ldw = d_c; g.sw = static_cast<int64_t>(d_h) * d_c; g.w_bf16 = w_dtype == MLA_BF16;
+  g.w_nk = false;
+  g.y = q_lat; g.ldy = static_cast<int64_t>(H) * d_c; g.sy = d_c; g.y_bf16 = out_dtype == MLA_BF16;
+  g.M = B; g.N = d_c; g.K = d_h; g.batch = H;
+  mla_status_t st = launched(mla::launch_gemm_small(g, s), "absorb GEMM");
+  if (st != MLA_OK || !q_r) return st;
+  return launched(mla::launch_rope_rows(q_r, static_cast<int64_t>(B) * H, H, d_R, seq_lens, -1,
+                                        rope_base, q_pe, out_dtype == MLA_BF16, s),
+                  "query RoPE");
+}
+
+mla_status_t mla_kv_append(const float* c_kv, const float* k_r, int32_t n_new,
+                           const int32_t* seq_lens_before, const int32_t* block_table,
+                           void* kv_cache, float rope_base, const mla_paged_shape_t* shape,
+                           mla_dtype_t cache_dtype, void* stream) {
+  if (!c_kv || !k_r || !seq_lens_before || !block_table || !kv_cache)
+    return fail(MLA_ERR_NULL, "mla_kv_append: a required pointer is NULL");
+  mla_status_t st = check_paged_shape(shape);
+  if (st != MLA_OK) return st;
+  if (n_new < 1) return fail(MLA_ERR_SHAPE, "mla_kv_append: n_new %d < 1", n_new);
+  if (n_new > 65535) return fail(MLA_ERR_SHAPE, "mla_kv_append: n_new %d > 65535", n_new);
+  if (!is_dtype(cache_dtype)) return fail(MLA_ERR_UNSUPPORTED, "mla_kv_append: unknown dtype");
+  if (!std::isfinite(rope_base)) return fail(MLA_ERR_SHAPE, "mla_kv_append: rope_base");
+  return launched(mla::launch_kv_append(c_kv, k_r, n_new, seq_lens_before, block_table, kv_cache,
+                                        cache_dtype == MLA_BF16, rope_base, shape->batch,
+                                        shape->d_latent, shape->d_rope, shape->page_size,
+                                        shape->max_pages_per_seq, as_stream(stream)),
+                  "cache append");
+}
+
+mla_status_t mla_out_proj(const float* o_lat, const void* w_uv, const void* w_o, int32_t B,
+                          int32_t H, int32_t d_c, int32_t d_h, int32_t d_model,
+                          mla_dtype_t w_dtype, float* o_heads, float* u, void* stream) {
+  if (!o_lat || !w_uv || !o_heads) return fail(MLA_ERR_NULL, "mla_out_proj: NULL o_lat/w_uv/o_heads");
+  if ((w_o == nullptr) != (u == nullptr))
+    return fail(MLA_ERR_NULL, "mla_out_proj: w_o and u must both be given or both NULL");
+  if (B < 1 || H < 1 || d_c < 1 || d_h < 1 || (w_o && d_model < 1))
+    return fail(MLA_ERR_SHAPE, "mla_out_proj: sizes must be >= 1");
+  if (!is_dtype(w_dtype)) return fail(MLA_ERR_UNSUPPORTED, "mla_out_proj: unknown dtype");
+  hipStream_t s = as_stream(stream);
+  mla::GemmArgs g;
+  g.x = o_lat; g.ldx = static_cast<int64_t>(H) * d_c; g.sx = d_c; g.x_bf16 = 0;
+  g.w = w_uv; g.ldw = d_c; g.sw = static_cast<int64_t>(d_h) * d_c; g.w_bf16 = w_dtype == MLA_BF16;
+  g.w_nk = true;
+  g.y = o_heads; g.ldy = static_cast<int64_t>(H) * d_h; g.sy = d_h; g.y_bf16 = 0;
+  g.M = B; g.N = d_h; g.K = d_c; g.batch = H;
+  mla_status_t st = launched(mla::launch_gemm_small(g, s), "W^UV GEMM");
+  if (st != MLA_OK || !w_o) return st;
+  mla::GemmArgs o;
+  o.x = o_heads; o.ldx = static_cast<int64_t>(H) * d_h; o.sx = 0; o.x_bf16 = 0;
+  o.w = w_o; o.ldw = static_cast<int64_t>(H) * d_h; o.sw = 0; o.w_bf16 = w_dtype == MLA_BF16;
+  o.w_nk = true;
+  o.y = u; o.ldy = d_model; o.sy = 0; o.y_bf16 = 0;
+  o.M = B; o.N = d_model; o.K = H * d_h; o.batch = 1;
+  return launched(mla::launch_gemm_small(o, s), "W^O GEMM");
+}
+
+mla_status_t mla_linear(const void* x, mla_dtype_t x_dtype, const void* w,
+                        mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K, float* y,
+                        void* stream) {
+  if (!x || !w || !y) return fail(MLA_ERR_NULL, "mla_linear: a required pointer is NULL");
+  if (M < 1 || N < 1 || K < 1) return fail(MLA_ERR_SHAPE, "mla_linear: sizes must be >= 1");
+  if (M > 65535 * 64) return fail(MLA_ERR_SHAPE, "mla_linear: M %d too large", M);
+  if (!is_dtype(x_dtype) || !is_dtype(w_dtype))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_linear: unknown dtype");
+  mla::GemmArgs g;
+  g.x = x; g.ldx = K; g.sx = 0; g.x_bf16 = x_dtype == MLA_BF16;
+  g.w = w; g.ldw = K; g.sw = 0; g.w_bf16 = w_dtype == MLA_BF16; g.w_nk = true;
+  g.y = y; g.ldy = N; g.sy = 0; g.y_bf16 = 0;
+  g.M = M; g.N = N; g.K = K; g.batch = 1;
+  return launched(mla::launch_gemm_small(g, as_stream(stream)), "linear GEMM");
+}
+
+mla_status_t mla_validate_indices(const int32_t* block_table, const int32_t* seq_lens,
+                                  const mla_paged_shape_t* shape, int32_t* dev_count,
+                                  void* stream) {
+  if (!block_table || !seq_lens || !dev_count)
+    return fail(MLA_ERR_NULL, "mla_validate_indices: a required pointer is NULL");
+  mla_status_t st = check_paged_shape(shape);
+  if (st != MLA_OK) return st;
+  return launched(mla::launch_validate_indices(block_table, seq_lens, shape->batch,
+                                               shape->page_size, shape->max_pages_per_seq,
+                                               shape->num_pages, dev_count, as_stream(stream)),
+                  "index validation");
+}
+
+mla_status_t mla_stream_read(const void* src, size_t bytes, float* sink, void* stream) {
+  if (!src || !sink) return fail(MLA_ERR_NULL, "mla_stream_read: NULL pointer");
+  if (bytes == 0 || bytes % 16 != 0)
+    return fail(MLA_ERR_SHAPE, "mla_stream_read: bytes %zu must be a positive multiple of 16", bytes);
+  return launched(mla::launch_stream_read(src, bytes, sink, as_stream(stream)), "stream read");
+}
+
+}  // extern "C"

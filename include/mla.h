@@ -1,0 +1,220 @@
+/*
+ * mla.h — C ABI of the MI355X (gfx950) weight-absorbed MLA decode library (libmla.so).
+ *
+ * The method (Multi-head Latent Attention of DeepSeek-V2):
+ *   - the cache keeps, per token and layer, only the latent c^KV (d_c = 512) and the
+ *     rotated shared RoPE key k^R (d_R = 64): 576 elements
+ *     ("論文解説: DeepSeek-V2 — MoEモデルのKVキャッシュを93.3%削減するMulti-head Latent
+ *     Attention", 0h-n0.github.io, sections "MLA: 低ランクKV結合圧縮" and "Decoupled RoPE");
+ *   - W^UK moves onto the query (q~_i = W^UK_i^T q^C_i) and W^UV is applied after the
+ *     weighted sum of latents (same page, section "行列吸収トリック"; kasblo.com/?p=4663,
+ *     sections "K側は…Qを変換する" and "V側は、小さな表現の加重和を先に求める");
+ *   - scores (q~_i . c_j + q^R_i . k^R_j) / sqrt(d_h + d_h^R), softmax over the cached
+ *     tokens, u = W^O [o_1; ...; o_H] (qiita.com/joule/items/57d9b3f4fc27959eaa0d,
+ *     section "Attention 計算").
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller; every tensor is dense,
+ *     row-major, in the shape given.  The library never allocates, frees or synchronises;
+ *     it enqueues kernels on `stream` (a hipStream_t passed as void*; NULL = the null
+ *     stream) and returns.  Structs of sizes (mla_paged_shape_t) are HOST pointers.
+ *   - All arguments are validated on the host before anything is launched; on any
+ *     violation the call returns an error code, launches nothing, and
+ *     mla_last_error_detail() describes the problem (thread-local string).
+ *   - A launch failure reported by the runtime returns MLA_ERR_LAUNCH.  Faults inside a
+ *     kernel surface at the caller's next synchronisation.
+ *   - Block-table entries and seq_lens are read on the device and are NOT bounds-checked
+ *     there: out-of-range values are undefined behaviour.  mla_validate_indices checks
+ *     them on the device beforehand.
+ *   - Results are deterministic for fixed inputs and arguments (no floating-point atomics).
+ *
+ * Paged latent cache: kv_cache[num_pages][page_size][d_latent + d_rope]; a row is
+ * [c^KV (d_latent) | RoPE(k^R) (d_rope)].  Token j (0-based) of sequence b lives at
+ * page block_table[b * max_pages_per_seq + j / page_size], slot j % page_size.
+ * Entries past ceil(seq_len / page_size) are never read (conventionally -1).
+ *
+ * RoPE: pair (x[2k], x[2k+1]) is rotated by pos * rope_base^(-2k/d_rope) with the
+ * rotation [[cos, -sin], [sin, cos]]; the angle, sine and cosine are evaluated in fp64.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,        /* a required pointer is NULL                               */
+  MLA_ERR_SHAPE = 2,       /* a size is out of range or sizes are inconsistent         */
+  MLA_ERR_UNSUPPORTED = 3, /* valid but not compiled (dims / dtype combination)        */
+  MLA_ERR_WORKSPACE = 4,   /* caller workspace too small                               */
+  MLA_ERR_LAUNCH = 5,      /* the HIP runtime rejected a launch                        */
+  MLA_ERR_INDEX = 6        /* reserved for index errors found on the host              */
+} mla_status_t;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype_t;
+
+typedef struct {
+  int32_t batch;             /* B: sequences                                        */
+  int32_t num_heads;         /* H: query heads                                      */
+  int32_t d_latent;          /* d_c: latent width (512 DeepSeek-V2, 64 tiny)        */
+  int32_t d_rope;            /* d_R: shared RoPE key width (64 / 16), even          */
+  int32_t page_size;         /* tokens per page, a multiple of 16                   */
+  int32_t max_pages_per_seq; /* row length of block_table                           */
+  int32_t num_pages;         /* pages in the pool                                   */
+} mla_paged_shape_t;
+
+/* ---------------------------------------------------------------------------------
+ * Sizes and planning (pure host functions, no device access)
+ * -------------------------------------------------------------------------------*/
+
+/* Bytes of a latent cache of B sequences x T tokens x `layers` layers with
+ * (d_c + d_R) elements of `elem_bytes` each (kasblo.com/?p=4663, "容量を計算する").
+ * Returns 0 if any argument is negative. */
+size_t mla_cache_bytes(int64_t B, int64_t T, int64_t layers, int32_t d_c, int32_t d_R,
+                       int32_t elem_bytes);
+
+/* Bytes of workspace mla_decode needs for num_splits > 1: the fp32 split partials
+ * o_part [B][H][S][d_c] followed by lse_part [B][H][S] (256-byte aligned). */
+size_t mla_decode_workspace_bytes(int32_t B, int32_t H, int32_t d_c, int32_t num_splits);
+
+/* A split count for mla_decode_attn: enough (sequence, split) work items to cover
+ * `num_cus` compute units when every sequence holds `max_seq_len` tokens, and no more
+ * splits than pages.  total_tokens (sum of seq_lens, or <= 0 if unknown) lets ragged
+ * batches use smaller splits.  Always >= 1. */
+int32_t mla_suggest_num_splits(int32_t B, int32_t max_seq_len, int64_t total_tokens,
+                               int32_t page_size, int32_t num_cus);
+
+/* ---------------------------------------------------------------------------------
+ * Hot path
+ * -------------------------------------------------------------------------------*/
+
+/* Query absorption and query RoPE.
+ *   q_lat[b][i][c] = sum_d w_uk[i*d_h + d][c] * q_c[b][i][d]        (q~_i = W^UK_i^T q^C_i)
+ *   q_pe[b][i][:]  = RoPE(q_r[b][i][:], pos = seq_lens[b] - 1)
+ * ("論文解説: DeepSeek-V2 …", "行列吸収トリック"; qiita "RoPE の扱い": q^R = RoPE(W^QR c^Q).)
+ *   q_c      [B][H][d_h]       fp32
+ *   w_uk     [H*d_h][d_c]      w_dtype   (nn.Linear weight of W^UK; head i = row block i)
+ *   q_r      [B][H][d_R]       fp32, pre-rotation; NULL skips the RoPE part
+ *   seq_lens [B]               int32, context length INCLUDING the query token (>= 1)
+ *   q_lat    [B][H][d_c]       out_dtype (written)
+ *   q_pe     [B][H][d_R]       out_dtype (written; may be NULL iff q_r is NULL)
+ * Errors: NULL, SHAPE (non-positive sizes, odd d_R), UNSUPPORTED (dtype). */
+mla_status_t mla_absorb_q(const float* q_c, const void* w_uk, const float* q_r,
+                          const int32_t* seq_lens, float rope_base, void* q_lat, void* q_pe,
+                          int32_t B, int32_t H, int32_t d_h, int32_t d_c, int32_t d_R,
+                          mla_dtype_t w_dtype, mla_dtype_t out_dtype, void* stream);
+
+/* Append n_new tokens per sequence to the paged cache.
+ * Token t of sequence b goes to position pos = seq_lens_before[b] + t and its row is
+ * [c_kv[b][t][:] | RoPE(k_r[b][t][:], pos)] converted to cache_dtype
+ * ("論文解説: DeepSeek-V2 …", "Decoupled RoPE": only c^KV and the rotated k^R are cached;
+ * qiita "RoPE の扱い": k^R = RoPE(W^KR h)).
+ *   c_kv [B][n_new][d_latent] fp32;  k_r [B][n_new][d_rope] fp32 (pre-rotation)
+ *   seq_lens_before [B] int32;  block_table [B][max_pages_per_seq] int32
+ *   kv_cache as described above (written only at the appended rows)
+ * Errors: NULL, SHAPE (n_new < 1, any shape field < 1, page_size % 16, odd d_rope),
+ * UNSUPPORTED (dtype). */
+mla_status_t mla_kv_append(const float* c_kv, const float* k_r, int32_t n_new,
+                           const int32_t* seq_lens_before, const int32_t* block_table,
+                           void* kv_cache, float rope_base, const mla_paged_shape_t* shape,
+                           mla_dtype_t cache_dtype, void* stream);
+
+/* Decode attention over the paged latent cache, split over tokens.
+ * For every sequence b, head i and split s (s = 0..num_splits-1), with
+ * cps = ceil(max_pages_per_seq / num_splits) pages per split, split s covers the cached
+ * tokens j in [s*cps*P, (s+1)*cps*P) with j < seq_lens[b] and computes
+ *   score_j = softmax_scale * ([q_lat[b][i]; q_pe[b][i]] . row_j)     (576-wide dot)
+ *   o_part[b][i][s][:] = sum_j e^{score_j} c_j / sum_j e^{score_j}   (c_j = row_j[0:d_c])
+ *   lse_part[b][i][s]  = ln sum_j e^{score_j}
+ * (qiita "Attention 計算" in the absorbed order; kasblo "V側は…" for the latent sum).
+ * A split with no tokens writes o = 0 and lse = -inf.
+ *   q_lat [B][H][d_latent], q_pe [B][H][d_rope]: `dtype` (q_pe already rotated)
+ *   kv_cache: `dtype`;  block_table [B][max_pages_per_seq], seq_lens [B]: int32, device
+ *   o_part [B][H][S][d_latent] fp32;  lse_part [B][H][S] fp32.
+ *   With num_splits == 1, o_part is the final o~ [B][H][d_latent] and lse_part may be NULL.
+ * softmax_scale is normally 1/sqrt(d_h + d_R) (1/sqrt(192) at DeepSeek-V2 shape).
+ * Supported: (d_latent, d_rope, dtype) = (512, 64, BF16) with H <= 128, or
+ * (64, 16, F32) with H <= 64; otherwise UNSUPPORTED.
+ * Errors: NULL, SHAPE (sizes < 1, page_size % 16, odd d_rope, num_splits < 1,
+ * seq_lens bound max_pages_per_seq*page_size does not fit int32), UNSUPPORTED. */
+mla_status_t mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_cache,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const mla_paged_shape_t* shape, float softmax_scale,
+                             int32_t num_splits, float* o_part, float* lse_part,
+                             mla_dtype_t dtype, void* stream);
+
+/* Log-sum-exp combine of split partials (exact re-assembly of one softmax whose sum
+ * over tokens was cut into disjoint ranges; qiita "Attention 計算").
+ *   M = max_s lse_s; w_s = e^{lse_s - M} (0 for lse_s = -inf)
+ *   out[b][i][:] = sum_s w_s o_part[b][i][s][:] / sum_s w_s;  lse_out = M + ln sum_s w_s
+ * All splits empty: out = 0, lse_out = -inf.
+ *   o_part [B][H][S][d_c], lse_part [B][H][S] fp32;  out [B][H][d_c] fp32;
+ *   lse_out [B][H] fp32 or NULL.
+ * Errors: NULL, SHAPE (sizes < 1, d_c % 4). */
+mla_status_t mla_splitk_combine(const float* o_part, const float* lse_part, int32_t B,
+                                int32_t H, int32_t num_splits, int32_t d_c, float* out,
+                                float* lse_out, void* stream);
+
+/* mla_decode_attn followed by mla_splitk_combine, with the split partials in a caller
+ * workspace of at least mla_decode_workspace_bytes(B, H, d_latent, num_splits) bytes
+ * (unused when num_splits == 1).  out [B][H][d_latent] fp32; lse_out [B][H] or NULL.
+ * Errors: as the two calls, plus WORKSPACE when the workspace is NULL or too small. */
+mla_status_t mla_decode(const void* q_lat, const void* q_pe, const void* kv_cache,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        const mla_paged_shape_t* shape, float softmax_scale,
+                        int32_t num_splits, void* workspace, size_t workspace_bytes,
+                        float* out, float* lse_out, mla_dtype_t dtype, void* stream);
+
+/* Value up-projection and output projection.
+ *   o_heads[b][i][d] = sum_c w_uv[i*d_h + d][c] * o_lat[b][i][c]    (o_i = W^UV_i o~_i)
+ *   u[b][n] = sum_k w_o[n][k] * o_heads[b][k]   (k over H*d_h; u = W^O [o_1;...;o_H])
+ * (kasblo "V側は…": up-project after the weighted sum; qiita "Attention 計算" for u.)
+ *   o_lat [B][H][d_c] fp32;  w_uv [H*d_h][d_c] w_dtype;  w_o [d_model][H*d_h] w_dtype or NULL
+ *   o_heads [B][H][d_h] fp32 (always written);  u [B][d_model] fp32 (NULL iff w_o NULL)
+ * Errors: NULL, SHAPE, UNSUPPORTED (dtype). */
+mla_status_t mla_out_proj(const float* o_lat, const void* w_uv, const void* w_o, int32_t B,
+                          int32_t H, int32_t d_c, int32_t d_h, int32_t d_model,
+                          mla_dtype_t w_dtype, float* o_heads, float* u, void* stream);
+
+/* y = x w^T for an nn.Linear weight: y[m][n] = sum_k x[m][k] w[n][k], fp32 accumulate,
+ * fp32 output.  Used for the projections c^Q = W^DQ h, q^C = W^UQ c^Q, q^R = W^QR c^Q,
+ * c^KV = W^DKV h, k^R = W^KR h (qiita "Query の圧縮", "RoPE の扱い").
+ *   x [M][K] x_dtype;  w [N][K] w_dtype;  y [M][N] fp32.
+ * Errors: NULL, SHAPE (sizes < 1), UNSUPPORTED (dtype). */
+mla_status_t mla_linear(const void* x, mla_dtype_t x_dtype, const void* w,
+                        mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K, float* y,
+                        void* stream);
+
+/* Device-side check of the paging indices: counts sequences whose seq_len is negative or
+ * exceeds max_pages_per_seq*page_size, and referenced block-table entries outside
+ * [0, num_pages).  Writes the count to *dev_count (device int32; 0 = valid).
+ * Errors: NULL, SHAPE. */
+mla_status_t mla_validate_indices(const int32_t* block_table, const int32_t* seq_lens,
+                                  const mla_paged_shape_t* shape, int32_t* dev_count,
+                                  void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Measurement aid and diagnostics
+ * -------------------------------------------------------------------------------*/
+
+/* Streams `bytes` (a multiple of 16) from src and writes one float per workgroup to
+ * sink[0 .. 4095] so the reads cannot be elided: a plain read kernel giving the
+ * practical HBM read ceiling next to the attention kernel.  Errors: NULL, SHAPE. */
+mla_status_t mla_stream_read(const void* src, size_t bytes, float* sink, void* stream);
+
+/* Static string for a status code. */
+const char* mla_status_string(mla_status_t status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* mla_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

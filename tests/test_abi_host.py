@@ -1,0 +1,160 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared function, the
+pure host functions compute what the pages fix, and host-side validation rejects bad
+arguments before anything is launched (no kernel runs in these tests)."""
+import ctypes
+import json
+import os
+
+import pytest
+
+import head_latent_attention_15_amd as mla
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+FAKE = 0x1000  # non-NULL pointer value; never dereferenced because validation fails first
+
+
+def test_every_declared_symbol_is_exported():
+    names = mla.header_functions()
+    assert len(names) >= 14
+    so = ctypes.CDLL(mla.LIB_PATH)
+    for n in names:
+        assert hasattr(so, n), f"{n} declared in mla.h but not exported"
+        assert callable(getattr(mla, n)), f"{n} has no Python binding of the same name"
+
+
+def test_status_strings():
+    assert mla.mla_status_string(0) == "MLA_OK"
+    assert mla.mla_status_string(4) == "MLA_ERR_WORKSPACE"
+    assert mla.mla_status_string(99) == "MLA_ERR_UNKNOWN"
+
+
+def test_cache_bytes_match_pages():
+    g = json.load(open(os.path.join(GOLD, "cache_sizes.json")))
+    for c in g["cases"]:
+        assert mla.mla_cache_bytes(c["B"], c["T"], g["layers"], g["d_c"], g["d_R"],
+                                   g["elem_bytes"]) == c["MiB"] * 2 ** 20
+    assert mla.mla_cache_bytes(1, 4096, 60, 512, 64, 2) == 283115520
+    assert mla.mla_cache_bytes(-1, 4096, 60, 512, 64, 2) == 0
+
+
+def test_workspace_bytes():
+    # o_part 32*128*8*512 floats + lse 32*128*8 floats, each 256-aligned
+    assert mla.mla_decode_workspace_bytes(32, 128, 512, 8) == 32 * 128 * 8 * 512 * 4 + 32 * 128 * 8 * 4
+    assert mla.mla_decode_workspace_bytes(1, 1, 4, 1) == 256 + 256
+    assert mla.mla_decode_workspace_bytes(0, 1, 4, 1) == 0
+
+
+def test_suggest_num_splits():
+    assert mla.mla_suggest_num_splits(32, 4096, 0, 64, 256) == 8
+    assert mla.mla_suggest_num_splits(4, 32768, 0, 64, 256) == 64
+    assert mla.mla_suggest_num_splits(1024, 4096, 0, 64, 256) == 1
+    assert mla.mla_suggest_num_splits(1, 100, 0, 64, 256) == 2       # capped by pages
+    s = mla.mla_suggest_num_splits(128, 8192, 532480, 64, 256)
+    assert 1 <= s <= 128
+    assert mla.mla_suggest_num_splits(0, 1, 0, 64, 256) == 1
+
+
+def _shape(**kw):
+    d = dict(batch=2, num_heads=16, d_latent=512, d_rope=64, page_size=64, max_pages_per_seq=4,
+             num_pages=8)
+    d.update(kw)
+    return mla._PagedShape(*[d[f] for f, _ in mla._PagedShape._fields_])
+
+
+def _attn(shape, S=1, dtype=mla.MLA_BF16, nulls=(), lse=True, scale=0.1):
+    p = [None if i in nulls else FAKE for i in range(6)]
+    return mla.lib.mla_decode_attn(p[0], p[1], p[2], p[3], p[4], ctypes.byref(shape), scale, S,
+                                   p[5], FAKE if lse else None, dtype, None)
+
+
+@pytest.mark.parametrize("null", range(6))
+def test_attn_rejects_null(null):
+    assert _attn(_shape(), nulls=(null,)) == mla.MLA_ERR_NULL
+    assert "NULL" in mla.mla_last_error_detail()
+
+
+@pytest.mark.parametrize("field,value", [("batch", 0), ("num_heads", 0), ("page_size", 40),
+                                         ("d_rope", 63), ("max_pages_per_seq", 0),
+                                         ("num_pages", 0), ("page_size", 0)])
+def test_attn_rejects_bad_shape(field, value):
+    assert _attn(_shape(**{field: value})) == mla.MLA_ERR_SHAPE
+
+
+def test_attn_rejects_bad_splits_and_scale():
+    assert _attn(_shape(), S=0) == mla.MLA_ERR_SHAPE
+    assert _attn(_shape(), S=5000) == mla.MLA_ERR_SHAPE
+    assert _attn(_shape(), S=4, lse=False) == mla.MLA_ERR_NULL
+    assert _attn(_shape(), scale=float("inf")) == mla.MLA_ERR_SHAPE
+    assert _attn(_shape(page_size=2 ** 20, max_pages_per_seq=2 ** 12)) == mla.MLA_ERR_SHAPE
+
+
+def test_attn_rejects_unsupported():
+    assert _attn(_shape(d_latent=256)) == mla.MLA_ERR_UNSUPPORTED
+    assert _attn(_shape(num_heads=129)) == mla.MLA_ERR_UNSUPPORTED
+    assert _attn(_shape(), dtype=mla.MLA_F32) == mla.MLA_ERR_UNSUPPORTED
+    assert _attn(_shape(d_latent=64, d_rope=16), dtype=mla.MLA_BF16) == mla.MLA_ERR_UNSUPPORTED
+    assert _attn(_shape(d_latent=64, d_rope=16, num_heads=65), dtype=mla.MLA_F32) == mla.MLA_ERR_UNSUPPORTED
+    assert _attn(_shape(), dtype=7) == mla.MLA_ERR_UNSUPPORTED
+
+
+def test_decode_rejects_small_workspace():
+    shp = _shape()
+    st = mla.lib.mla_decode(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(shp), 0.1, 4, FAKE, 100,
+                            FAKE, None, mla.MLA_BF16, None)
+    assert st == mla.MLA_ERR_WORKSPACE
+    st = mla.lib.mla_decode(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(shp), 0.1, 4, None, 10 ** 9,
+                            FAKE, None, mla.MLA_BF16, None)
+    assert st == mla.MLA_ERR_WORKSPACE
+    st = mla.lib.mla_decode(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(shp), 0.1, 4, FAKE + 4,
+                            10 ** 9, FAKE, None, mla.MLA_BF16, None)
+    assert st == mla.MLA_ERR_WORKSPACE
+
+
+def test_combine_validation():
+    L = mla.lib
+    assert L.mla_splitk_combine(None, FAKE, 1, 1, 2, 512, FAKE, None, None) == mla.MLA_ERR_NULL
+    assert L.mla_splitk_combine(FAKE, FAKE, 1, 1, 0, 512, FAKE, None, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_splitk_combine(FAKE, FAKE, 1, 1, 2, 510, FAKE, None, None) == mla.MLA_ERR_SHAPE
+
+
+def test_absorb_validation():
+    L = mla.lib
+    args = lambda **k: [k.get("q_c", FAKE), k.get("w", FAKE), k.get("q_r", FAKE),
+                        k.get("sl", FAKE), 10000.0, k.get("q_lat", FAKE), k.get("q_pe", FAKE),
+                        k.get("B", 2), 4, 32, 64, k.get("d_R", 16), k.get("wdt", 0), 0, None]
+    assert L.mla_absorb_q(*args(q_c=None)) == mla.MLA_ERR_NULL
+    assert L.mla_absorb_q(*args(q_pe=None)) == mla.MLA_ERR_NULL
+    assert L.mla_absorb_q(*args(sl=None)) == mla.MLA_ERR_NULL
+    assert L.mla_absorb_q(*args(d_R=15)) == mla.MLA_ERR_SHAPE
+    assert L.mla_absorb_q(*args(B=0)) == mla.MLA_ERR_SHAPE
+    assert L.mla_absorb_q(*args(wdt=3)) == mla.MLA_ERR_UNSUPPORTED
+
+
+def test_append_outproj_linear_validate_validation():
+    L = mla.lib
+    shp = _shape()
+    assert L.mla_kv_append(FAKE, FAKE, 0, FAKE, FAKE, FAKE, 1e4, ctypes.byref(shp), 1, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_kv_append(FAKE, None, 1, FAKE, FAKE, FAKE, 1e4, ctypes.byref(shp), 1, None) == mla.MLA_ERR_NULL
+    bad = _shape(page_size=20)
+    assert L.mla_kv_append(FAKE, FAKE, 1, FAKE, FAKE, FAKE, 1e4, ctypes.byref(bad), 1, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_out_proj(FAKE, FAKE, FAKE, 2, 4, 64, 32, 128, 0, FAKE, None, None) == mla.MLA_ERR_NULL
+    assert L.mla_out_proj(FAKE, FAKE, None, 0, 4, 64, 32, 0, 0, FAKE, None, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_linear(FAKE, 0, FAKE, 0, 0, 4, 4, FAKE, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_linear(FAKE, 2, FAKE, 0, 4, 4, 4, FAKE, None) == mla.MLA_ERR_UNSUPPORTED
+    assert L.mla_validate_indices(FAKE, FAKE, ctypes.byref(shp), None, None) == mla.MLA_ERR_NULL
+    assert L.mla_stream_read(FAKE, 100, FAKE, None) == mla.MLA_ERR_SHAPE
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(2, 4)
+    with pytest.raises(ValueError):
+        mla.mla_linear(x, torch.zeros(3, 4), torch.zeros(2, 3))
+
+
+def test_single_hip_runtime_in_process():
+    """The binding loads torch before libmla.so, so exactly one libamdhip64 is mapped
+    (two runtimes in one process do not share devices)."""
+    maps = open("/proc/self/maps").read()
+    libs = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
+    assert len(libs) == 1, libs

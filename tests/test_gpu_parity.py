@@ -1,0 +1,442 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the same seeded
+inputs.  Tolerances: fp32 max-abs <= 1e-5; bf16 max-abs <= 2e-2 and rel-L2 <= 5e-3;
+indexing (which tokens are read) bit-exact."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_util import assert_bf16, assert_fp32, dev, errors, host64, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import head_latent_attention_15_amd as m
+    return m
+
+
+def run_attention(mla, inp, S, lse=True):
+    """decode_attn (+ combine for S > 1) on device copies of a workloads problem."""
+    q_lat, q_pe, cache = dev(inp["q_lat"]), dev(inp["q_pe"]), dev(inp["cache"])
+    bt, sl = dev(inp["block_table"]), dev(inp["seq_lens"])
+    B, H, d_c = q_lat.shape
+    if S == 1:
+        out = torch.empty(B, H, d_c, device="cuda")
+        lse_t = torch.empty(B, H, device="cuda") if lse else None
+        mla.mla_decode_attn(q_lat, q_pe, cache, bt, sl, inp["scale"], 1, out, lse_t)
+    else:
+        o_part = torch.empty(B, H, S, d_c, device="cuda")
+        lse_part = torch.empty(B, H, S, device="cuda")
+        mla.mla_decode_attn(q_lat, q_pe, cache, bt, sl, inp["scale"], S, o_part, lse_part)
+        out = torch.empty(B, H, d_c, device="cuda")
+        lse_t = torch.empty(B, H, device="cuda")
+        mla.mla_splitk_combine(o_part, lse_part, out, lse_t)
+    torch.cuda.synchronize()
+    return out, lse_t
+
+
+def oracle_attention(inp, batch_index=None):
+    d_c = inp["shape"].d_c
+    P = inp["cache"].shape[1]
+    cache = inp["cache"]
+    bt = inp["block_table"].numpy()
+    sl = inp["seq_lens"].numpy()
+    idx = range(inp["q_lat"].shape[0]) if batch_index is None else batch_index
+    o, lse = [], []
+    for b in idx:
+        # gather only the pages this sequence references, then the oracle's paged gather
+        rows = oracle.gather_rows(W.to_f64(cache[torch.from_numpy(np.maximum(bt[b], 0)).long()]),
+                                  np.arange(bt.shape[1]), int(sl[b]), P)
+        att = oracle.latent_attention(W.to_f64(inp["q_lat"][b]), W.to_f64(inp["q_pe"][b]), rows,
+                                      d_c, inp["scale"])
+        o.append(att["o_lat"])
+        lse.append(att["lse"])
+    return np.stack(o), np.stack(lse)
+
+
+# ------------------------------------------------------------------ tiny fp32 end to end
+def test_tiny_fp32_chain(mla):
+    """Cache fill with RoPE, query absorption + RoPE, attention (1, 2, 4 splits), combine,
+    W^UV: every intermediate and the output against the oracle, max-abs <= 1e-5."""
+    x = W.tiny_fp32()
+    s = x["shape"]
+    B, H, T = s.B, s.H, x["T"]
+    say("tiny_fp32 chain")
+    pages = T // W.PAGE
+    cache = torch.zeros(pages, W.PAGE, s.d_c + s.d_R, device="cuda")
+    bt, before = dev(x["block_table"]), dev(x["seq_lens_before"])
+    mla.mla_kv_append(dev(x["c_kv"]), dev(x["k_r"]), before, bt, cache, x["rope_base"])
+    seq_lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    q_lat = torch.empty(B, H, s.d_c, device="cuda")
+    q_pe = torch.empty(B, H, s.d_R, device="cuda")
+    mla.mla_absorb_q(dev(x["q_c"]), dev(x["w_uk"]), dev(x["q_r"]), seq_lens, x["rope_base"],
+                     q_lat, q_pe)
+    torch.cuda.synchronize()
+
+    # oracle, expanded path with explicit RoPE at positions 0..T-1, query at T-1
+    c = W.to_f64(x["c_kv"][0])
+    k_pe = oracle.rope(W.to_f64(x["k_r"][0]), np.arange(T), x["rope_base"])
+    q_pe_ref = oracle.rope(W.to_f64(x["q_r"][0]), T - 1, x["rope_base"])
+    ref = oracle.expanded_decode(W.to_f64(x["q_c"][0]), q_pe_ref, c, k_pe, W.to_f64(x["w_uk"]),
+                                 W.to_f64(x["w_uv"]), x["scale"])
+    rows_ref = np.concatenate([c, k_pe], 1)
+    assert_fp32(host64(cache).reshape(T, -1), rows_ref, 1e-6, "cache rows")
+    assert_fp32(host64(q_lat)[0], oracle.absorb_query(W.to_f64(x["q_c"][0]), W.to_f64(x["w_uk"])),
+                1e-5, "q_lat")
+    assert_fp32(host64(q_pe)[0], q_pe_ref, 1e-6, "q_pe")
+
+    for S in (1, 2, 4):
+        inp = {"q_lat": q_lat, "q_pe": q_pe, "cache": cache, "block_table": bt,
+               "seq_lens": seq_lens, "scale": x["scale"]}
+        o_lat, lse = run_attention(mla, inp, S)
+        o_heads = torch.empty(B, H, s.d_h, device="cuda")
+        mla.mla_out_proj(o_lat, dev(x["w_uv"]), None, o_heads)
+        torch.cuda.synchronize()
+        assert_fp32(host64(o_heads)[0], ref["o"], 1e-5, f"o (S={S})")
+        assert_fp32(host64(lse)[0], ref["lse"], 1e-5, f"lse (S={S})")
+
+
+def test_worked_example_on_gpu(mla):
+    """kasblo.com/?p=4663 figure '説明用の数値例' zero-padded into the fp32 shapes:
+    c=(2,1), U=[[1,0],[0,1],[1,1]] as head 0's W^UK block, q=(1,2,1), scale 1, no RoPE part,
+    one cached token.  q~ = U^T q = (2, 3) exactly; lse = score = 7 exactly; o~ = c."""
+    say("worked example")
+    H, d_h, d_c, d_R = 4, 32, 64, 16
+    w_uk = torch.zeros(H * d_h, d_c)
+    w_uk[0:3, 0:2] = torch.tensor([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]])
+    q_c = torch.zeros(1, H, d_h)
+    q_c[0, 0, 0:3] = torch.tensor([1.0, 2.0, 1.0])
+    q_lat = torch.empty(1, H, d_c, device="cuda")
+    seq_lens = torch.ones(1, dtype=torch.int32, device="cuda")
+    mla.mla_absorb_q(dev(q_c), dev(w_uk), None, seq_lens, 10000.0, q_lat, None)
+    cache = torch.zeros(1, W.PAGE, d_c + d_R, device="cuda")
+    cache[0, 0, 0:2] = torch.tensor([2.0, 1.0])
+    q_pe = torch.zeros(1, H, d_R, device="cuda")
+    out = torch.empty(1, H, d_c, device="cuda")
+    lse = torch.empty(1, H, device="cuda")
+    bt = torch.zeros(1, 1, dtype=torch.int32, device="cuda")
+    mla.mla_decode_attn(q_lat, q_pe, cache, bt, seq_lens, 1.0, 1, out, lse)
+    torch.cuda.synchronize()
+    assert q_lat[0, 0, :2].tolist() == [2.0, 3.0]
+    assert torch.all(q_lat[0, 0, 2:] == 0) and torch.all(q_lat[0, 1:] == 0)
+    assert lse[0, 0].item() == 7.0
+    assert out[0, 0, :2].tolist() == [2.0, 1.0]
+
+
+# ------------------------------------------------------------------ bf16 latent parity
+@pytest.mark.parametrize("H", [128, 64, 16, 20])
+@pytest.mark.parametrize("S", [1, 3, 8])
+def test_latent_ragged_midsize(mla, H, S):
+    """Several pages, a ragged tail, a 1-token sequence, permuted pages."""
+    inp = W.paged_attention(100 + H, B=3, H=H, seq_lens=[1, 700, 1500])
+    say(f"ragged midsize H={H} S={S}")
+    out, lse = run_attention(mla, inp, S)
+    o_ref, lse_ref = oracle_attention(inp)
+    assert_bf16(host64(out), o_ref, f"o~ H={H} S={S}")
+    m, _ = errors(host64(lse), lse_ref)
+    assert m <= 2e-2, f"lse max-abs {m}"
+
+
+@pytest.mark.slow
+def test_dsv2_b32_t4k_full(mla):
+    """B=32, T=4096, H=128 (the headline shape), suggested splits, full output."""
+    inp = W.dsv2_b32_t4k()
+    S = mla.mla_suggest_num_splits(32, 4096, 0, 64, 256)
+    say(f"dsv2_b32_t4k S={S}")
+    out, lse = run_attention(mla, inp, S)
+    o_ref, lse_ref = oracle_attention(inp)
+    m, r = assert_bf16(host64(out), o_ref, "dsv2_b32_t4k")
+    print(f"dsv2_b32_t4k: max-abs {m:.3e} rel-L2 {r:.3e}")
+    assert errors(host64(lse), lse_ref)[0] <= 2e-2
+
+
+@pytest.mark.slow
+def test_long_b4_t32k_full(mla):
+    """B=4, T=32768 over a permuted pool, 64 splits, full output."""
+    inp = W.long_b4_t32k()
+    S = mla.mla_suggest_num_splits(4, 32768, 0, 64, 256)
+    say(f"long_b4_t32k S={S}")
+    out, lse = run_attention(mla, inp, S)
+    o_ref, lse_ref = oracle_attention(inp)
+    m, r = assert_bf16(host64(out), o_ref, "long_b4_t32k")
+    print(f"long_b4_t32k: max-abs {m:.3e} rel-L2 {r:.3e}")
+
+
+@pytest.mark.slow
+def test_ragged_b128_sampled(mla):
+    """B=128 ragged over a shared permuted pool: whole batch on the GPU, sampled
+    sequences (shortest, longest, and a seeded draw) against the oracle."""
+    inp = W.ragged_b128()
+    sl = inp["seq_lens"].tolist()
+    S = mla.mla_suggest_num_splits(128, max(sl), sum(sl), 64, 256)
+    say(f"ragged_b128 S={S}")
+    out, lse = run_attention(mla, inp, S)
+    rng = np.random.default_rng(0)
+    pick = sorted(set([int(np.argmin(sl)), int(np.argmax(sl))] + rng.choice(128, 10, replace=False).tolist()))
+    o_ref, _ = oracle_attention(inp, pick)
+    m, r = assert_bf16(host64(out)[pick], o_ref, "ragged_b128")
+    print(f"ragged_b128 sample {pick}: max-abs {m:.3e} rel-L2 {r:.3e}")
+
+
+# ------------------------------------------------------------------ indexing exactness
+def _spike_problem(B, H, seq_lens, spikes, seed=7):
+    """q~ = 0, q_pe = 64 e_0; the rope part of every row is 0 except row j* of each
+    sequence, whose k^R[0] = 64: its score is 4096*scale (~296) above all others, so its
+    softmax weight is 1 and every other weight underflows to exactly 0."""
+    inp = W.paged_attention(seed, B=B, H=H, seq_lens=seq_lens)
+    inp["cache"][:, :, 512:] = 0
+    inp["q_lat"].zero_()
+    inp["q_pe"].zero_()
+    inp["q_pe"][:, :, 0] = 64.0
+    bt = inp["block_table"]
+    for b, j in enumerate(spikes):
+        inp["cache"][int(bt[b, j // 64]), j % 64, 512] = 64.0
+    return inp
+
+
+@pytest.mark.parametrize("S", [1, 4])
+def test_spike_selects_exact_token(mla, S):
+    """o~ equals the selected latent bit-exactly on both sides of page boundaries."""
+    seq_lens = [64, 65, 128, 129, 300, 1000, 1000, 4096]
+    spikes = [63, 64, 127, 128, 0, 999, 511, 4095]
+    inp = _spike_problem(len(seq_lens), 32, seq_lens, spikes)
+    say(f"spike S={S}")
+    out, _ = run_attention(mla, inp, S)
+    out = out.cpu()
+    bt = inp["block_table"]
+    for b, j in enumerate(spikes):
+        want = inp["cache"][int(bt[b, j // 64]), j % 64, :512].float()
+        assert torch.equal(out[b], want.expand_as(out[b])), f"seq {b} token {j}"
+
+
+def test_single_token_bit_exact(mla):
+    """seq_len = 1: softmax weight exactly 1, o~ = c_0 bit-exactly."""
+    inp = W.paged_attention(8, B=4, H=128, seq_lens=[1, 1, 1, 1])
+    say("single token")
+    out, lse = run_attention(mla, inp, 1)
+    out = out.cpu()
+    bt = inp["block_table"]
+    for b in range(4):
+        want = inp["cache"][int(bt[b, 0]), 0, :512].float().expand_as(out[b])
+        bad = (out[b] != want).nonzero()
+        assert bad.numel() == 0, (f"seq {b}: {bad.shape[0]} mismatches, first at {bad[:4].tolist()}: "
+                                  f"{[(out[b][tuple(i)].item(), want[tuple(i)].item()) for i in bad[:4]]}")
+
+
+def test_page_permutation_bit_identical(mla):
+    """Moving pages in the pool (and the block table with them) changes nothing."""
+    inp = W.paged_attention(9, B=3, H=128, seq_lens=[333, 1024, 77], permute_pages=False)
+    say("page permutation")
+    a, la = run_attention(mla, inp, 2)
+    n = inp["cache"].shape[0]
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(1))
+    inp2 = dict(inp)
+    inp2["cache"] = torch.empty_like(inp["cache"])
+    inp2["cache"][perm] = inp["cache"]
+    bt = inp["block_table"].clone()
+    m = bt >= 0
+    bt[m] = perm[bt[m].long()].to(torch.int32)
+    inp2["block_table"] = bt
+    b, lb = run_attention(mla, inp2, 2)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_nan_poison_outside_context(mla):
+    """NaN in pages nobody references and in slots at or past seq_len is never read."""
+    inp = W.paged_attention(10, B=3, H=64, seq_lens=[70, 129, 500], extra_pages=3)
+    say("nan poison")
+    clean, lc = run_attention(mla, inp, 3)
+    pois = dict(inp)
+    cache = inp["cache"].clone()
+    bt = inp["block_table"]
+    used = set(int(v) for v in bt.flatten().tolist() if v >= 0)
+    for p in range(cache.shape[0]):
+        if p not in used:
+            cache[p] = float("nan")
+    for b, L in enumerate(inp["seq_lens"].tolist()):
+        last = int(bt[b, (L - 1) // 64])
+        cache[last, (L - 1) % 64 + 1:] = float("nan")
+    pois["cache"] = cache
+    dirty, ld = run_attention(mla, pois, 3)
+    assert torch.equal(clean, dirty) and torch.equal(lc, ld)
+
+
+def test_splits_agree_fp32_combine(mla):
+    """The split-K combine is exact up to fp32 rounding: with the fp32-math path (H=20 is
+    not tiled by the MFMA kernel), S = 1 and S in {2, 7, 64} agree to 1e-5, including
+    splits entirely past the end of short sequences."""
+    inp = W.paged_attention(11, B=4, H=20, seq_lens=[64, 100, 2000, 4096])
+    say("splits fp32")
+    ref, lref = run_attention(mla, inp, 1)
+    for S in (2, 7, 64):
+        out, lse = run_attention(mla, inp, S)
+        assert_fp32(host64(out), host64(ref), 1e-5, f"o S={S}")
+        assert_fp32(host64(lse), host64(lref), 1e-5, f"lse S={S}")
+
+
+def test_splits_mfma_vs_oracle(mla):
+    """MFMA path: every split count (including empty splits) meets the bf16 bar."""
+    inp = W.paged_attention(11, B=4, H=128, seq_lens=[64, 100, 2000, 4096])
+    o_ref, lse_ref = oracle_attention(inp)
+    for S in (1, 2, 7, 64):
+        say(f"splits mfma S={S}")
+        out, lse = run_attention(mla, inp, S)
+        assert_bf16(host64(out), o_ref, f"S={S}")
+        assert errors(host64(lse), lse_ref)[0] <= 2e-2
+        assert torch.isfinite(lse).all()
+
+
+def test_single_token_generic_path(mla):
+    """seq_len = 1 through the fp32-math path (H=20): o~ = c_0 bit-exactly."""
+    inp = W.paged_attention(8, B=3, H=20, seq_lens=[1, 1, 1])
+    say("single token generic")
+    out, lse = run_attention(mla, inp, 1)
+    out = out.cpu()
+    bt = inp["block_table"]
+    for b in range(3):
+        want = inp["cache"][int(bt[b, 0]), 0, :512].float().expand_as(out[b])
+        bad = (out[b] != want).nonzero()
+        assert bad.numel() == 0, (f"seq {b}: {bad.shape[0]} mismatches, first at {bad[:4].tolist()}: "
+                                  f"{[(out[b][tuple(i)].item(), want[tuple(i)].item()) for i in bad[:4]]}")
+
+
+def test_deterministic(mla):
+    inp = W.paged_attention(12, B=2, H=128, seq_lens=[3000, 1234])
+    say("determinism")
+    a, la = run_attention(mla, inp, 5)
+    b, lb = run_attention(mla, inp, 5)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_zero_query_and_ones_latent(mla):
+    """q = 0: every weight is 1/T, o~ = mean of the latents.  All-ones latents: o~ = 1."""
+    inp = W.paged_attention(13, B=2, H=32, seq_lens=[512, 1000])
+    inp["q_lat"].zero_()
+    inp["q_pe"].zero_()
+    say("zero query")
+    out, lse = run_attention(mla, inp, 2)
+    o_ref, lse_ref = oracle_attention(inp)
+    assert_fp32(host64(out), o_ref, 2e-5, "mean")
+    assert_fp32(host64(lse), lse_ref, 1e-5, "lse = ln T")
+    inp2 = W.paged_attention(14, B=2, H=32, seq_lens=[512, 1000])
+    inp2["cache"][:, :, :512] = 1.0
+    out, _ = run_attention(mla, inp2, 3)
+    assert_fp32(host64(out), np.ones(out.shape), 1e-5, "ones")
+
+
+def test_validate_indices(mla):
+    say("validate indices")
+    inp = W.paged_attention(15, B=3, H=16, seq_lens=[100, 64, 1])
+    bt, sl = dev(inp["block_table"]), dev(inp["seq_lens"])
+    cnt = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    n = inp["cache"].shape[0]
+    mla.mla_validate_indices(bt, sl, 64, n, cnt)
+    torch.cuda.synchronize()
+    assert cnt.item() == 0
+    bt[0, 1] = n          # out of the pool
+    sl[2] = 10 ** 6       # longer than the table allows
+    mla.mla_validate_indices(bt, sl, 64, n, cnt)
+    torch.cuda.synchronize()
+    assert cnt.item() == 2
+
+
+def test_stream_read_runs(mla):
+    say("stream read")
+    x = torch.ones(1 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4096, device="cuda")
+    mla.mla_stream_read(x, sink)
+    torch.cuda.synchronize()
+    assert torch.isfinite(sink).all()
+
+
+# ------------------------------------------------------------------ full decode layer
+def layer_on_gpu(mla, x, S):
+    """The whole decode layer through the C ABI: projections, cache append, absorption,
+    attention + combine, W^UV and W^O."""
+    s = x["shape"]
+    B, H, d_h, d_c, d_R, d = s.B, s.H, s.d_h, s.d_c, s.d_R, x["d"]
+    w = {k: dev(v) for k, v in x["weights"].items()}
+    h = dev(x["h"])
+    cache = dev(x["cache"])
+    bt, before = dev(x["block_table"]), dev(x["seq_lens_before"])
+    f32 = dict(device="cuda", dtype=torch.float32)
+    c_q = torch.empty(B, x["d_cq"], **f32)
+    q_c = torch.empty(B, H * d_h, **f32)
+    q_r = torch.empty(B, H * d_R, **f32)
+    c_kv = torch.empty(B, d_c, **f32)
+    k_r = torch.empty(B, d_R, **f32)
+    mla.mla_linear(h, w["w_dq"], c_q)
+    mla.mla_linear(c_q, w["w_uq"], q_c)
+    mla.mla_linear(c_q, w["w_qr"], q_r)
+    mla.mla_linear(h, w["w_dkv"], c_kv)
+    mla.mla_linear(h, w["w_kr"], k_r)
+    mla.mla_kv_append(c_kv.view(B, 1, d_c), k_r.view(B, 1, d_R), before, bt, cache, x["rope_base"])
+    seq_lens = before + 1
+    q_lat = torch.empty(B, H, d_c, device="cuda", dtype=torch.bfloat16)
+    q_pe = torch.empty(B, H, d_R, device="cuda", dtype=torch.bfloat16)
+    mla.mla_absorb_q(q_c.view(B, H, d_h), w["w_uk"], q_r.view(B, H, d_R), seq_lens,
+                     x["rope_base"], q_lat, q_pe)
+    ws = torch.empty(max(1, mla.mla_decode_workspace_bytes(B, H, d_c, S)), dtype=torch.uint8, device="cuda")
+    o_lat = torch.empty(B, H, d_c, **f32)
+    mla.mla_decode(q_lat, q_pe, cache, bt, seq_lens, x["scale"], S, ws, o_lat)
+    o_heads = torch.empty(B, H, d_h, **f32)
+    u = torch.empty(B, d, **f32)
+    mla.mla_out_proj(o_lat, w["w_uv"], w["w_o"], o_heads, u)
+    torch.cuda.synchronize()
+    return u, cache
+
+
+@pytest.mark.slow
+def test_full_layer_b64_t2k_sampled(mla):
+    """Full layer at d=5120, H=128, B=64, 2048 prior tokens + 1 appended: all 64 rows of
+    u on the GPU; sequences 0 and 37 through the oracle's expanded path."""
+    x = W.layer_b64_t2k()
+    say("layer_b64_t2k")
+    u, cache = layer_on_gpu(mla, x, S=4)
+    pick = [0, 37]
+    ref = oracle.decode_layer(W.to_f64(x["h"]), {k: W.to_f64(v) for k, v in x["weights"].items()},
+                              W.to_f64(x["cache"]), x["block_table"].numpy(),
+                              x["seq_lens_before"].numpy(), x["shape"].d_h, x["shape"].d_R,
+                              x["rope_base"], x["scale"], batch_index=pick)
+    m, r = assert_bf16(host64(u)[pick], ref["u"][pick], "layer u")
+    print(f"layer_b64_t2k u: max-abs {m:.3e} rel-L2 {r:.3e}")
+    # the appended rows: [c^KV ; RoPE(k^R, 2048)] rounded to bf16
+    bt = x["block_table"]
+    for b in pick:
+        row = host64(cache[int(bt[b, 2048 // 64]), 2048 % 64])
+        want = np.concatenate([ref["c_kv_new"][b], oracle.rope(ref["k_r_new"][b], 2048, 10000.0)])
+        assert_bf16(row, want, "appended row")
+
+
+def test_small_layer_chain(mla):
+    """A small layer (d=256, H=16, d_c=512, d_R=64, B=5, 100 prior tokens) end to end on all rows."""
+    x = W.layer_b64_t2k(seed=21, B=5, T=100, d=256, H=16, d_cq=96)
+    say("small layer")
+    u, _ = layer_on_gpu(mla, x, S=2)
+    ref = oracle.decode_layer(W.to_f64(x["h"]), {k: W.to_f64(v) for k, v in x["weights"].items()},
+                              W.to_f64(x["cache"]), x["block_table"].numpy(),
+                              x["seq_lens_before"].numpy(), x["shape"].d_h, x["shape"].d_R,
+                              x["rope_base"], x["scale"])
+    assert_bf16(host64(u), ref["u"], "small layer u")
+
+
+def test_linear_and_outproj_against_matmul(mla):
+    """Plain GEMMs against numpy fp64 matmul, including ragged tile edges."""
+    g = torch.Generator().manual_seed(3)
+    say("linear")
+    for (M, N, K) in [(1, 1, 1), (7, 130, 67), (64, 512, 5120), (65, 64, 33)]:
+        x = torch.randn(M, K, generator=g)
+        w = torch.randn(N, K, generator=g).to(torch.bfloat16)
+        y = torch.empty(M, N, device="cuda")
+        mla.mla_linear(dev(x), dev(w), y)
+        torch.cuda.synchronize()
+        ref = W.to_f64(x) @ W.to_f64(w).T
+        m, _ = errors(host64(y), ref)
+        assert m <= 1e-5 * math.sqrt(K) * 4, (M, N, K, m)
