@@ -41,6 +41,7 @@
 #include "launchers.h"
 
 #include <cstdlib>
+#include <type_traits>
 
 namespace mla {
 namespace {
@@ -53,6 +54,8 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 constexpr int DC = 512, DR = 64, ROW = DC + DR;
 constexpr int ROW_BYTES = ROW * 2;                  // 1152
@@ -61,27 +64,21 @@ constexpr int TILE = 32;                            // tokens per tile
 constexpr int TILE_CHUNKS = TILE * CHUNKS;          // 2304
 constexpr int TILE_WAVE_COPIES = TILE_CHUNKS / 64;  // 36 wave-wide 16-byte copies per tile
 constexpr int TILE_BYTES = TILE_CHUNKS * 16;        // 36864
-constexpr int NBUF = 3;                             // tile buffers
+constexpr int NBUF = 4;                             // tile buffers
 constexpr int KSTEPS = ROW / 32;                    // 18 k-steps of the score product
-constexpr int MAX_HEADS = 128;
-constexpr int P_STRIDE = 80;                        // bytes per head row of a P tile (64 + pad)
-constexpr int P_BYTES = MAX_HEADS * P_STRIDE;
-constexpr int MAX_SPLIT_PAGES = 2048;               // block-table entries of a split in LDS
-constexpr int OFF_P = NBUF * TILE_BYTES;
-constexpr int OFF_PAGES = OFF_P + 2 * P_BYTES;
-constexpr int OFF_L = OFF_PAGES + MAX_SPLIT_PAGES * 4;
-constexpr int OFF_FLAG = OFF_L + MAX_HEADS * 4;
-constexpr int LDS_BYTES = OFF_FLAG + 64;
+constexpr int LDS_BYTES = NBUF * TILE_BYTES;
 constexpr float HEADROOM = 32.0f;  // log2 units between a split's first-tile max and its reference
 constexpr float P_RANGE = 64.0f;   // a score this far above the reference takes the fallback
 constexpr float LN2 = 0.6931471805599453f;
 
-// 16-byte-chunk swizzle of tile row t (a permutation of the low three chunk bits):
-//  - ds_read_b128 of one chunk column by 8 consecutive rows hits 8 distinct 16-byte bank
-//    groups (the 72-chunk row pitch is a multiple of 8 chunks);
-//  - the transposing reads of 4 consecutive rows x 2 adjacent chunks (one 16-lane group)
-//    hit 8 distinct bank groups, because the 4 rows' swizzles differ in bits 1-2.
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+// 16-byte-chunk swizzle of tile row t (0..31): logical chunk c of the row is stored at
+// position c ^ swz(t).  Measured on gfx950, this map keeps conflict-free (full LDS read
+// rate) both the ds_read_b128 of the score operand (rows 8 (r >> 2) + 4 mt + (r & 3), one
+// chunk column per 16-lane group) and the transposing ds_read_b64_tr_b16 of the PV operand
+// (rows 8 g + 4 r + 0..3 x 2 adjacent chunks).
+__device__ __forceinline__ int swz(int t) {
+  return ((((t >> 3) & 3) ^ (t & 3)) << 1) | ((t >> 2) & 1);
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -123,6 +120,14 @@ __device__ __forceinline__ bf16x2_t to_bf16x2(float a, float b) {
   return __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
 }
 
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+
+// eight bf16 ones (0x3f80 each)
+__device__ __forceinline__ i32x4_t i16x4x2_ones() {
+  const int one2 = 0x3f803f80;
+  return i32x4_t{one2, one2, one2, one2};
+}
+
 __device__ __forceinline__ float from_bf16(__bf16 h) {
   return bf16_to_f32(__builtin_bit_cast(uint16_t, h));
 }
@@ -134,8 +139,8 @@ __device__ __forceinline__ float from_bf16(__bf16 h) {
 // l + 64k.
 __device__ void split_exact_fallback(const bf16raw* __restrict__ q_lat,
                                      const bf16raw* __restrict__ q_pe,
-                                     const bf16raw* __restrict__ cache, const int32_t* pages,
-                                     int first_page, int log2P, int j0, int j1, int b, int H,
+                                     const bf16raw* __restrict__ cache, const int32_t* bt_row,
+                                     int log2P, int j0, int j1, int b, int H,
                                      int S, int s, float scale_log2, float* __restrict__ o_part,
                                      float* __restrict__ lse_part, int h_begin, int n_heads,
                                      int lane) {
@@ -152,7 +157,7 @@ __device__ void split_exact_fallback(const bf16raw* __restrict__ q_lat,
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[k] = 0.f;
     for (int j = j0; j < j1; ++j) {
-      const int pg = pages[(j >> log2P) - first_page];
+      const int pg = bt_row[j >> log2P];
       const bf16raw* row = cache + ((static_cast<int64_t>(pg) << log2P) + (j & (P - 1))) * ROW;
       float part = 0.f;
 #pragma unroll
@@ -173,8 +178,15 @@ __device__ void split_exact_fallback(const bf16raw* __restrict__ q_lat,
   }
 }
 
-// NW wavefronts, H = 16 * NW heads.  Scores: 16 heads per wave.  PV: 512 / NW columns of
-// all H heads per wave (NHT = NW head tiles x NCT = 32 / NW column tiles = 32 tiles).
+// NW wavefronts, H = 16 * NW heads; wave w owns heads h0 = 16 w .. h0 + 15 for both
+// products, so a wave's softmax weights never leave its registers:
+//   scores: S^T = K_tile (32 x 576) * Q^T (576 x 16), Q resident in VGPRs for the split;
+//   PV:     O^T (512 x 16) += V^T (512 x 32) * P^T (32 x 16), 32 column tiles, the V^T
+//           operand read with the transposing ds_read_b64_tr_b16.
+// One barrier per tile: it publishes tile it (every wave's copies landed) and retires tile
+// it-1, whose buffer then receives the copies of tile it+2.  Between barriers the waves run
+// free, so the two waves sharing a SIMD overlap one's softmax arithmetic with the other's
+// matrix-core work.
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     const bf16raw* __restrict__ q_lat, const bf16raw* __restrict__ q_pe,
@@ -182,25 +194,25 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     const int32_t* __restrict__ seq_lens, int H, int log2P, int max_pages, int pages_per_split,
     int S, float scale_log2, float* __restrict__ o_part, float* __restrict__ lse_part) {
   constexpr int NT = NW * 64;
-  constexpr int NHT = NW;           // head tiles in the PV product
-  constexpr int NCT = 32 / NW;      // column tiles per wave in the PV product
-  constexpr int CW = 16 * NCT;      // columns per wave
-  constexpr int COPIES_LO = TILE_WAVE_COPIES / NW;
-  constexpr int COPIES_HI = (TILE_WAVE_COPIES + NW - 1) / NW;
-  static_assert(NW == 1 || NW == 2 || NW == 4 || NW == 8, "columns split evenly");
+  constexpr int NCT = DC / 16;                                    // PV column tiles
+  constexpr int STEPS = KSTEPS * 2;                               // score MFMA steps per tile
+  constexpr int COPIES = (TILE_WAVE_COPIES + NW - 1) / NW;        // tile copies per wave
+  constexpr int COPY_EVERY = STEPS / COPIES;                      // score steps between copies
+  static_assert(NW == 1 || NW == 2 || NW == 4 || NW == 8, "16 to 128 heads");
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
-  int32_t* pages = reinterpret_cast<int32_t*>(smem + OFF_PAGES);
-  float* l_lds = reinterpret_cast<float*>(smem + OFF_L);
-  int32_t* flag_lds = reinterpret_cast<int32_t*>(smem + OFF_FLAG);
-  const uint32_t smem_lds = static_cast<uint32_t>(reinterpret_cast<size_t>((lds_char_t*)smem));
+  lds_char_t* const lsm = (lds_char_t*)smem;  // 32-bit LDS addressing for the tile reads
+  const uint32_t smem_lds = static_cast<uint32_t>(reinterpret_cast<size_t>(lsm));
 
-  const int s = blockIdx.x, b = blockIdx.y;
+  // Consecutive workgroup ids go to the 8 XCDs in turn; with the sequence index in x, all
+  // splits of a sequence (ids b, b + B, ...) land on XCD b % 8 when B % 8 == 0, so the
+  // sequence's queries are fetched once into that XCD's L2.
+  const int b = blockIdx.x, s = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int P = 1 << log2P;
-  const int h0 = 16 * w;   // score heads of this wave
-  const int c0 = CW * w;   // PV columns of this wave
+  const int h0 = 16 * w;   // heads of this wave
+  const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_pages;
 
   const int L = seq_lens[b];
   const int j0 = s * pages_per_split * P;
@@ -216,14 +228,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     return;
   }
 
-  // stage the split's block-table entries in LDS
-  const int first_page = j0 >> log2P;
-  const int npg = ((j1 - 1) >> log2P) - first_page + 1;
-  for (int i = tid; i < npg; i += NT)
-    pages[i] = block_table[static_cast<int64_t>(b) * max_pages + first_page + i];
-
-  // resident query fragments: B operand of S^T = K Q^T (lane: head h0 + r16, features
-  // 32 kk + 8 g .. + 7)
+  // resident query fragments: B operand of S^T = K Q^T (lane (g, r16): head h0 + r16,
+  // features 32 kk + 8 g .. + 7)
   bf16x8_t qf[KSTEPS];
   {
     const bf16raw* qrow = q_lat + (static_cast<int64_t>(b) * H + h0 + r16) * DC + 8 * g;
@@ -234,81 +240,84 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     for (int kk = 0; kk < DR / 32; ++kk)
       qf[DC / 32 + kk] = *reinterpret_cast<const bf16x8_t*>(prow + 32 * kk);
   }
-  wait_vmcnt<0>();
-  __syncthreads();  // page table visible, query fragments landed
 
-  // this wave's share of a tile copy: wave-wide copies w, w + NW, ... (< 36)
-  const int n_copies = (TILE_WAVE_COPIES - w + NW - 1) / NW;
+  // Wave w issues copies q = w, w + NW, ... of each tile; lane l of copy q fills LDS chunk
+  // 64 q + l, i.e. row t, stored position p, which holds logical chunk p ^ swz(t) of the row.
+  // When 36 copies do not split evenly, a wave without a last copy repeats its first (same
+  // source, same LDS bytes), so every wave counts COPIES copies per tile.
   const char* cache_bytes = reinterpret_cast<const char*>(cache);
   // A tile starting at token tb lies inside one page (P % 32 == 0, tiles 32-aligned).
-  auto issue_tile = [&](int tb, int buf) {
-    const int pg = __builtin_amdgcn_readfirstlane(pages[(tb >> log2P) - first_page]);
-    const char* base =
-        cache_bytes + ((static_cast<int64_t>(pg) << log2P) + (tb & (P - 1))) * ROW_BYTES;
-    const int last = j1 - 1 - tb;  // rows past it repeat the last valid row
+  auto tile_base = [&](int tb) {
+    const int pg = __builtin_amdgcn_readfirstlane(bt_row[tb >> log2P]);
+    return cache_bytes + ((static_cast<int64_t>(pg) << log2P) + (tb & (P - 1))) * ROW_BYTES;
+  };
+  // copy r of this wave for the tile at token tb into buffer buf; rows past the split's end
+  // repeat its last valid row
+  auto issue_copy = [&](const char* base, int tb, int buf, int r) {
     int ln = lane;
-    asm volatile("" : "+v"(ln));  // recompute the chunk coordinates each tile
-#pragma unroll
-    for (int r = 0; r < COPIES_HI; ++r) {
-      const int q = w + NW * r;
-      if (r < COPIES_LO || q < TILE_WAVE_COPIES) {
-        const int chunk = 64 * q + ln;
-        const int t = chunk / CHUNKS;
-        const int c = (chunk - t * CHUNKS) ^ swz(t);
-        const uint32_t voff = static_cast<uint32_t>(min(t, last) * ROW_BYTES + c * 16);
-        dma16(base, voff, smem_lds + buf * TILE_BYTES + q * 64 * 16);
-      }
-    }
+    asm volatile("" : "+v"(ln));  // recompute the copy coordinates each time (no live ranges)
+    const int q = w + NW * r < TILE_WAVE_COPIES ? w + NW * r : w;
+    const int chunk = 64 * q + ln;
+    const int t = chunk / CHUNKS;
+    const int c = (chunk - t * CHUNKS) ^ swz(t);
+    const uint32_t voff = static_cast<uint32_t>(min(t, j1 - 1 - tb) * ROW_BYTES + c * 16);
+    dma16(base, voff, smem_lds + buf * TILE_BYTES + q * 64 * 16);
   };
-  auto wait_own_copies = [&](bool next_in_flight) {
-    if (!next_in_flight) {
-      wait_vmcnt<0>();
-    } else if (COPIES_LO == COPIES_HI || n_copies == COPIES_HI) {
-      wait_vmcnt<COPIES_HI>();
-    } else {
-      wait_vmcnt<COPIES_LO>();
-    }
+  auto issue_tile = [&](int tb, int buf) {
+    const char* base = tile_base(tb);
+#pragma unroll
+    for (int r = 0; r < COPIES; ++r) issue_copy(base, tb, buf, r);
   };
-
-  f32x4_t o[NHT][NCT];
-#pragma unroll
-  for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) o[ht][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // Reference maximum of head h0 + r16 (log2 units, same in its 4 lanes) and this lane's
-  // share of its softmax denominator.  The reference is fixed for the split: the first
-  // tile's maximum plus HEADROOM, so the accumulators are never rescaled.
-  float m_ref = -INFINITY, l_run = 0.f;
-  bool out_of_range = false;  // sticky: a score of this head block left the reference range
 
   const int ntiles = (j1 - j0 + TILE - 1) / TILE;
-  issue_tile(j0, 0);
-  if (ntiles > 1) issue_tile(j0 + TILE, 1);
-  for (int it = 0; it < ntiles; ++it) {
-    const int tb = j0 + it * TILE;
-    const int buf = it % NBUF;
-    wait_own_copies(it + 1 < ntiles);
-    block_barrier();  // tile it complete; every wave done with tile it-1 and P buffer it-1
-    if (it + 2 < ntiles) issue_tile(tb + 2 * TILE, (it + 2) % NBUF);
-    const char* tile = smem + buf * TILE_BYTES;
-    char* ptile = smem + OFF_P + (it & 1) * P_BYTES;
 
-    // ---- scores of heads h0..h0+15: S^T (2 token M-tiles x 16 heads, K = 576); the 36
-    //      K fragments stream through a 4-deep register ring
+  // O^T accumulators: o[ct] lane (g, r16) holds O[h0 + r16][16 ct + 4 g + i]
+  f32x4_t o[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) o[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // Reference maximum of head h0 + r16 (log2 units, same in its 4 lanes): the first tile's
+  // maximum plus HEADROOM, fixed for the split, so the accumulators are never rescaled.
+  // The softmax denominators accumulate on the matrix core as ones (16 x 32) * P^T
+  // (32 x 16): every entry of lane (g, r16) holds the sum of head h0 + r16, exactly over the
+  // bf16 weights the PV product consumes.
+  float m_ref = -INFINITY;
+  f32x4_t l_acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, i16x4x2_ones());
+  bool out_of_range = false;  // sticky: a score of this head block left the reference range
+
+  // Scores and softmax of tile it, returning this wave's P^T operand.  This wave's copies of
+  // tile it+2 are spread over the score steps.  Near the end of the split, where there is no
+  // tile it+2, the same copies re-fetch tile it (just read, so served by L2) into the retired
+  // buffer instead: every score step then issues the same copies and every wait counts
+  // alike.
+  auto score = [&](int it) {
+    const int tb = j0 + it * TILE;
+    const lds_char_t* tile = lsm + (it % NBUF) * TILE_BYTES;
+    const int tb2 = it + 2 < ntiles ? tb + 2 * TILE : tb;
+    const char* base2 = tile_base(tb2);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int gg = ln >> 4, rr = ln & 15;
+
+    // ---- scores S^T (2 token M-tiles x 16 heads, K = 576).  Row r of M-tile mt is token
+    //      8 (r >> 2) + 4 mt + (r & 3), so lane (gg, rr) ends up with tokens 8 gg .. 8 gg + 7
+    //      of head h0 + rr: after the softmax, exactly its P^T operand of the PV product.
+    //      The 36 K fragments stream through a 4-deep register ring.
+    f32x4_t sacc4[4];  // (M tile, k-step parity): four independent accumulation chains
     {
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int gg = ln >> 4, rr = ln & 15;
-      const int sk = swz(rr);
-      const int k0 = rr * ROW_BYTES + 16 * (gg ^ sk);        // chunk 8j + g
-      const int k1 = rr * ROW_BYTES + 16 * ((4 + gg) ^ sk);  // chunk 8j + 4 + g
-      f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-      constexpr int STEPS = KSTEPS * 2;
+      int kb[2][2];  // [M tile][k-step parity] byte offset of the fragment of k-step 0 / 1
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int t = 8 * (rr >> 2) + 4 * mt + (rr & 3);
+#pragma unroll
+        for (int par = 0; par < 2; ++par) kb[mt][par] = t * ROW_BYTES + 16 * ((4 * par + gg) ^ swz(t));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sacc4[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       constexpr int KRING = 4;
       auto k_frag = [&](int step) {
         const int kk = step >> 1, mt = step & 1;
-        const int off = ((kk & 1) ? k1 : k0) + (kk >> 1) * 128 + mt * 16 * ROW_BYTES;
-        return *reinterpret_cast<const bf16x8_t*>(tile + off);
+        return *(const lds_bf16x8_t*)(tile + kb[mt][kk & 1] + (kk >> 1) * 128);
       };
       bf16x8_t ka[KRING];
 #pragma unroll
@@ -317,109 +326,143 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
       for (int step = 0; step < STEPS; ++step) {
         if (step + KRING - 1 < STEPS) ka[(step + KRING - 1) % KRING] = k_frag(step + KRING - 1);
         const int kk = step >> 1, mt = step & 1;
-        sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step % KRING], qf[kk], sacc[mt], 0, 0, 0);
+        const int ch = mt * 2 + (kk & 1);
+        sacc4[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step % KRING], qf[kk], sacc4[ch], 0, 0, 0);
+        if (step % COPY_EVERY == 0 && step / COPY_EVERY < COPIES)
+          issue_copy(base2, tb2, (it + 2) % NBUF, step / COPY_EVERY);
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
 
-      // softmax (log2 domain): lane holds head h0 + rr, tokens 16 mt + 4 gg + i
-      float tmax = -INFINITY;
+    // ---- softmax (log2 domain) on the raw scores: lane holds head h0 + rr, tokens
+    //      8 gg + 4 mt + i.  The scale is positive, so the raw maximum orders like the
+    //      scaled one; each weight is 2^(s * scale - m_ref) with one rounding in the fma.
+    f32x4_t sc[2] = {sacc4[0] + sacc4[1], sacc4[2] + sacc4[3]};
+    if (tb + TILE > j1) {  // last tile of the split: tokens at or past j1 get weight 0
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = tb + 16 * mt + 4 * gg + i;
-          const float v = tok < j1 ? mul_rn(sacc[mt][i], scale_log2) : -INFINITY;
-          sacc[mt][i] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      if (it == 0) m_ref = tmax + HEADROOM;
-      out_of_range |= tmax > m_ref + P_RANGE;
-      float lsum = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x2_t p01 = to_bf16x2(__builtin_amdgcn_exp2f(sacc[mt][0] - m_ref),
-                                       __builtin_amdgcn_exp2f(sacc[mt][1] - m_ref));
-        const bf16x2_t p23 = to_bf16x2(__builtin_amdgcn_exp2f(sacc[mt][2] - m_ref),
-                                       __builtin_amdgcn_exp2f(sacc[mt][3] - m_ref));
-        lsum += (from_bf16(p01[0]) + from_bf16(p01[1])) + (from_bf16(p23[0]) + from_bf16(p23[1]));
-        const bf16x4_t p4 = __builtin_shufflevector(p01, p23, 0, 1, 2, 3);
-        *reinterpret_cast<bf16x4_t*>(ptile + (h0 + rr) * P_STRIDE + (16 * mt + 4 * gg) * 2) = p4;
-      }
-      l_run += lsum;
+        for (int i = 0; i < 4; ++i)
+          if (tb + 8 * gg + 4 * mt + i >= j1) sc[mt][i] = -INFINITY;
     }
-    block_barrier();  // P tile visible
-
-    // ---- O[all heads][c0 .. c0 + CW) += P (H x 32) * V (32 x CW)
-    {
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int gg = ln >> 4, rr = ln & 15;
-      bf16x8_t vb[NCT];
+    float tmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float tmax2 = mul_rn(tmax, scale_log2);
+    if (it == 0) m_ref = tmax2 + HEADROOM;
+    out_of_range |= tmax2 > m_ref + P_RANGE;
+    const float neg_m = -m_ref;
+    bf16x2_t pp[4];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf)
+        pp[2 * mt + hlf] =
+            to_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[mt][2 * hlf], scale_log2, neg_m)),
+                      __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mt][2 * hlf + 1], scale_log2, neg_m)));
+    const bf16x8_t pt = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                                __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
+                                                0, 1, 2, 3, 4, 5, 6, 7);
+    l_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pt, l_acc, 0, 0, 0);
+    return pt;
+  };
+
+  // PV of tile it with this wave's P^T operand pt.
+  auto pv = [&](int it, bf16x8_t pt) {
+    const lds_char_t* tile = lsm + (it % NBUF) * TILE_BYTES;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int gg = ln >> 4, rr = ln & 15;
+    // ---- V^T fragments (A operand): lane (gg, rr) holds column 16 ct + rr, tokens
+    //      8 gg .. 8 gg + 7, gathered by two transposing reads of 4 rows each.  Column tile ct
+    //      sits in chunks 2 ct, 2 ct + 1; with the row swizzle only the low three chunk bits
+    //      move, so 8 lane offsets (read r, ct & 3) plus the immediate 128 (ct >> 2) cover all.
+    {
+      int vb[2][4];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int t = 8 * gg + 4 * r + (rr >> 2);
+        const int e = (rr & 3) >> 1;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4)
+          vb[r][c4] = t * ROW_BYTES + 16 * ((2 * c4 + e) ^ swz(t)) + 8 * (rr & 1);
+      }
+      auto v_frag = [&](int ct) {
         i16x4_t half[2];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int t = 8 * gg + 4 * r + (rr >> 2);
-          const int chunk = (c0 + 16 * ct) / 8 + ((rr & 3) >> 1);
-          const char* p = tile + t * ROW_BYTES + 16 * (chunk ^ swz(t)) + 8 * (rr & 1);
-          half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
-        }
-        vb[ct] = __builtin_bit_cast(bf16x8_t,
-                                    __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-      constexpr int PRING = 3;
-      auto p_frag = [&](int ht) {
-        return *reinterpret_cast<const bf16x8_t*>(ptile + (16 * ht + rr) * P_STRIDE + 16 * gg);
+        for (int r = 0; r < 2; ++r)
+          half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4_t*)(tile + vb[r][ct & 3] + 128 * (ct >> 2)));
+        return __builtin_bit_cast(bf16x8_t,
+                                  __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      bf16x8_t pa[PRING];
+      constexpr int VRING = 4;
+      bf16x8_t va[VRING];
 #pragma unroll
-      for (int i = 0; i < PRING - 1 && i < NHT; ++i) pa[i] = p_frag(i);
+      for (int i = 0; i < VRING - 1; ++i) va[i] = v_frag(i);
 #pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) {
-        if (ht + PRING - 1 < NHT) pa[(ht + PRING - 1) % PRING] = p_frag(ht + PRING - 1);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          o[ht][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[ht % PRING], vb[ct], o[ht][ct], 0, 0, 0);
+      for (int ct = 0; ct < NCT; ++ct) {
+        if (ct + VRING - 1 < NCT) va[(ct + VRING - 1) % VRING] = v_frag(ct + VRING - 1);
+        o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ct % VRING], pt, o[ct], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+
+  // The query loads are complete before the first copy is issued: the copies are invisible
+  // to the compiler's own wait counting, so no compiler-inserted wait may fall after them.
+  wait_vmcnt<0>();
+  issue_tile(j0, 0);
+  if (ntiles > 1) issue_tile(j0 + TILE, 1);
+  // Waves 0 .. NW/2-1 (group 0) take each tile as scores then PV; waves NW/2 .. NW-1
+  // (group 1) run half a tile behind, as PV of the previous tile then scores.  A SIMD holds
+  // one wave of each group, so while one scores (K reads, softmax arithmetic) the other feeds
+  // the matrix core with its PV product.  Barrier it (before the work on tile it) publishes
+  // tile it, copied by every wave, and retires tile it-2, whose buffer the copies of tile it+2
+  // overwrite; both groups pass ntiles + 1 barriers.
+  auto tile_barrier = [&](int it) {
+    if (it < ntiles) wait_vmcnt<COPIES>();  // own copies of tile it landed
+    block_barrier();
+  };
+  if (NW == 1 || w < NW / 2) {
+    for (int it = 0; it < ntiles; ++it) {
+      tile_barrier(it);
+      const bf16x8_t pt = score(it);
+      pv(it, pt);
+    }
+    tile_barrier(ntiles);
+  } else {
+    tile_barrier(0);
+    bf16x8_t pt = score(0);
+    for (int it = 1; it < ntiles; ++it) {
+      tile_barrier(it);
+      pv(it - 1, pt);
+      pt = score(it);
+    }
+    tile_barrier(ntiles);
+    pv(ntiles - 1, pt);
   }
 
-  // ---- epilogue: denominators and fallback flags through LDS, then normalise and write
-  {
-    float lt = l_run + __shfl_xor(l_run, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    const bool fb = __any(out_of_range);
-    if (g == 0) l_lds[h0 + r16] = lt;
-    if (lane == 0) flag_lds[w] = fb ? 1 : 0;
-    if (!fb && lse_part != nullptr && g == 0)
-      lse_part[(static_cast<int64_t>(b) * H + h0 + r16) * S + s] = (m_ref + __log2f(lt)) * LN2;
+  // ---- epilogue: normalise and write four consecutive columns per lane; a head block
+  //      whose scores left the reference range is recomputed exactly
+  if (!__any(out_of_range)) {
+    const int64_t row = (static_cast<int64_t>(b) * H + h0 + r16) * S + s;
+    if (lse_part != nullptr && g == 0) lse_part[row] = (m_ref + __log2f(l_acc[0])) * LN2;
+    const float inv = 1.f / l_acc[0];
+    float* dst = o_part + row * DC + 4 * g;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) *reinterpret_cast<f32x4_t*>(dst + 16 * ct) = o[ct] * inv;
+  } else {
+    split_exact_fallback(q_lat, q_pe, cache, bt_row, log2P, j0, j1, b, H, S, s, scale_log2,
+                         o_part, lse_part, h0, 16, lane);
   }
-  __syncthreads();
-#pragma unroll
-  for (int ht = 0; ht < NHT; ++ht) {
-    if (flag_lds[ht]) continue;  // that head block is recomputed by its owner below
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 16 * ht + 4 * g + i;
-      const float inv = 1.f / l_lds[h];
-      float* dst = o_part + ((static_cast<int64_t>(b) * H + h) * S + s) * DC + c0 + r16;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) dst[16 * ct] = o[ht][ct][i] * inv;
-    }
-  }
-  if (flag_lds[w])
-    split_exact_fallback(q_lat, q_pe, cache, pages, first_page, log2P, j0, j1, b, H, S, s,
-                         scale_log2, o_part, lse_part, h0, 16, lane);
 }
 
 template <int NW>
 hipError_t launch_nw(const PagedArgs& a, hipStream_t st) {
   const float log2e = 1.4426950408889634f;
-  hipLaunchKernelGGL((attn_mfma_kernel<NW>), dim3(a.num_splits, a.B), dim3(NW * 64), 0, st,
+  hipLaunchKernelGGL((attn_mfma_kernel<NW>), dim3(a.B, a.num_splits), dim3(NW * 64), 0, st,
                      static_cast<const bf16raw*>(a.q_lat), static_cast<const bf16raw*>(a.q_pe),
                      static_cast<const bf16raw*>(a.cache), a.block_table, a.seq_lens, a.H,
                      __builtin_ctz(static_cast<unsigned>(a.page_size)), a.max_pages,
@@ -435,7 +478,7 @@ bool attn_mfma_supported(const PagedArgs& a) {
   const bool heads_ok = a.H == 16 || a.H == 32 || a.H == 64 || a.H == 128;
   const bool page_ok = a.page_size >= TILE && (a.page_size & (a.page_size - 1)) == 0;
   return a.d_c == DC && a.d_R == DR && heads_ok && page_ok &&
-         a.pages_per_split <= MAX_SPLIT_PAGES && a.B <= 65535 && aligned16(a.q_lat) &&
+         a.B <= 65535 && aligned16(a.q_lat) &&
          aligned16(a.q_pe) && aligned16(a.cache);
 }
 
