@@ -3,14 +3,17 @@
 
 One step = the decode hot path over one batch of the DeepSeek-V2-shaped workload
 (B=32 sequences, T=4096 cached tokens each, H=128 heads, d_c=512, d_R=64, bf16 cache and
-queries, 64-token pages): split-K attention over the paged latent cache followed by the
-log-sum-exp combine, both from libmla.  Inputs are seeded synthetic data, resident in HBM
-before timing starts.  Four copies of the 151 MB cache rotate between steps so the 256 MB
-Infinity Cache cannot serve a repeat.
+queries, 64-token pages): split-K attention over the paged latent cache (bf16 split
+partials) followed by the log-sum-exp combine, both from libmla.  Inputs are seeded
+synthetic data, resident in HBM before timing starts.  Four copies of the 151 MB cache
+rotate between steps so the 256 MB Infinity Cache cannot serve a repeat.
+
+Three timed regions, each bracketed by HIP events on the launch stream: whole steps (the
+headline value), the attention kernel alone back to back (its average launch duration,
+the roofline position), and the combine alone.
 
 Prints ONE JSON line: throughput (latent-cache GB/s), the attention kernel's roofline
-position (HIP-event time per launch on the launch stream), and the fp64 CPU oracle timed
-on the host cores as a baseline.
+position, and the fp64 CPU oracle timed on the host cores as a baseline.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
 """
@@ -58,8 +61,9 @@ def measured_traffic(launch_bytes_alg: float):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, n_seq: int):
-    """The fp64 oracle (unchanged) on the first n_seq sequences of the same workload."""
+def cpu_baseline(inp, n_seq: int, min_seconds: float = 10.0):
+    """The fp64 oracle (unchanged) on the first n_seq sequences of the same workload,
+    repeated until at least min_seconds of CPU work has been timed."""
     import numpy as np
     import oracle
     import workloads as W
@@ -73,17 +77,21 @@ def cpu_baseline(inp, n_seq: int):
     P = inp["cache"].shape[1]
     t0 = time.perf_counter()
     toks = 0
-    for b in range(n_seq):
-        rows = oracle.gather_rows(W.to_f64(inp["cache"][bt[b, :math.ceil(sl[b] / P)].astype(np.int64)]),
-                                  np.arange(math.ceil(sl[b] / P)), int(sl[b]), P)
-        oracle.latent_attention(W.to_f64(inp["q_lat"][b]), W.to_f64(inp["q_pe"][b]), rows, 512,
-                                inp["scale"])
-        toks += int(sl[b])
+    passes = 0
+    while passes == 0 or time.perf_counter() - t0 < min_seconds:
+        for b in range(n_seq):
+            rows = oracle.gather_rows(
+                W.to_f64(inp["cache"][bt[b, :math.ceil(sl[b] / P)].astype(np.int64)]),
+                np.arange(math.ceil(sl[b] / P)), int(sl[b]), P)
+            oracle.latent_attention(W.to_f64(inp["q_lat"][b]), W.to_f64(inp["q_pe"][b]), rows,
+                                    512, inp["scale"])
+            toks += int(sl[b])
+        passes += 1
     dt = time.perf_counter() - t0
     return {"value": round(toks * ROW_BYTES / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{n_seq} of 32 sequences x 4096 tokens (fp64 NumPy latent attention, "
-                      f"{dt:.1f} s)"}
+            "sample": f"{passes} passes over {n_seq} of 32 sequences x 4096 tokens (fp64 NumPy "
+                      f"latent attention incl. the paged gather, {dt:.1f} s)"}
 
 
 def main():
@@ -124,42 +132,39 @@ def main():
         caches.append(caches[0].clone())
     q_lat, q_pe = inp["q_lat"].to(dev), inp["q_pe"].to(dev)
     bt, sl = inp["block_table"].to(dev), inp["seq_lens"].to(dev)
-    o_part = torch.empty(B, H, S, 512, device=dev)
+    o_part = torch.empty(B, H, S, 512, device=dev, dtype=torch.bfloat16)
     lse_part = torch.empty(B, H, S, device=dev)
     out = torch.empty(B, H, 512, device=dev)
     lse = torch.empty(B, H, device=dev)
     scale = inp["scale"]
 
-    def step(k, ev=None):
-        if ev is not None:
-            ev[0].record()
+    def attn(k):
         mla.mla_decode_attn(q_lat, q_pe, caches[k % N_CACHE_COPIES], bt, sl, scale, S, o_part, lse_part)
-        if ev is not None:
-            ev[1].record()
+
+    def combine():
         mla.mla_splitk_combine(o_part, lse_part, out, lse)
-        if ev is not None:
-            ev[2].record()
+
+    def timed(fn, n):
+        """Average milliseconds of n back-to-back calls between two events."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for k in range(n):
+            fn(k)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
 
     log(f"warmup {args.warmup} steps, S={S}, {num_cus} CUs")
     for k in range(args.warmup):
-        step(k)
+        attn(k)
+        combine()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for k in range(args.steps):
-        step(k, evs[k])
-    stop.record()
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / args.steps
-    attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    comb_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    attn_avg = sum(attn_ms) / len(attn_ms)
-    comb_avg = sum(comb_ms) / len(comb_ms)
-    log(f"step {ms_step * 1e3:.1f} us; attention {attn_avg * 1e3:.1f} us (min {min(attn_ms) * 1e3:.1f}); "
-        f"combine {comb_avg * 1e3:.1f} us")
+    ms_step = timed(lambda k: (attn(k), combine()), args.steps)
+    attn_avg = timed(attn, args.steps)
+    comb_avg = timed(lambda k: combine(), args.steps)
+    log(f"step {ms_step * 1e3:.1f} us; attention {attn_avg * 1e3:.1f} us; combine {comb_avg * 1e3:.1f} us")
 
     # plain streaming read of one cache copy: the practical HBM read ceiling
     sink = torch.empty(4096, device=dev)
@@ -183,6 +188,7 @@ def main():
 
     tokens = B * T
     cache_bytes = tokens * ROW_BYTES
+    # cache + queries + block table + seq_lens read once; combined output written once
     step_alg_bytes = cache_bytes + B * H * 576 * 2 + B * H * 512 * 4 + bt.numel() * 4 + B * 4
     flops = tokens * H * FLOP_PER_TOKEN_HEAD
     attn_s = attn_avg * 1e-3
@@ -202,8 +208,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "dsv2_b32_t4k", "B": B, "T": T, "H": H, "d_c": 512, "d_R": 64,
-                   "page_size": 64, "num_splits": S, "cache_copies": N_CACHE_COPIES,
-                   "parallelism": "none"},
+                   "page_size": 64, "num_splits": S, "split_partials": "bf16",
+                   "cache_copies": N_CACHE_COPIES, "parallelism": "none"},
         "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "query_tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "step_bytes_algorithmic": step_alg_bytes,
@@ -215,7 +221,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "attn_mfma_kernel (8 waves x 16 heads)",
+                     "kernel": "attn_mfma_kernel<8, bf16 partials> (8 waves x 16 heads, 32-token tiles)",
                      "bytes_per_launch_algorithmic": cache_bytes},
     }
     if not args.no_cpu_baseline:

@@ -55,8 +55,8 @@ _SIGNATURES = {
     "mla_absorb_q": (_I32, [_P, _P, _P, _P, _F, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                             _I32, _P]),
     "mla_kv_append": (_I32, [_P, _P, _I32, _P, _P, _P, _F, _SP, _I32, _P]),
-    "mla_decode_attn": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _P, _I32, _P]),
-    "mla_splitk_combine": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    "mla_decode_attn": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _I32, _P, _I32, _P]),
+    "mla_splitk_combine": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "mla_decode": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _SZ, _P, _P, _I32, _P]),
     "mla_out_proj": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "mla_linear": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P]),
@@ -211,8 +211,9 @@ def mla_kv_append(c_kv, k_r, seq_lens_before, block_table, kv_cache, rope_base, 
 
 def mla_decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale, num_splits,
                     o_part, lse_part=None, stream=None):
-    """Split-K decode attention; o_part [B,H,S,d_c] (or [B,H,d_c] when S == 1),
-    lse_part [B,H,S] (or [B,H] / None when S == 1)."""
+    """Split-K decode attention; o_part [B,H,S,d_c] (or [B,H,d_c] when S == 1), float32 or
+    bfloat16 (the partial dtype follows the tensor), lse_part [B,H,S] (or [B,H] / None when
+    S == 1)."""
     torch = _torch()
     B, H, d_c = q_lat.shape
     _expect(q_pe.shape[0] == B and q_pe.shape[1] == H, "q_pe must be [B,H,d_R]")
@@ -230,11 +231,12 @@ def mla_decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale,
         _dev(q_lat, "q_lat", None, 3), _dev(q_pe, "q_pe", None, 3),
         _dev(kv_cache, "kv_cache", None, 3), _dev(block_table, "block_table", torch.int32, 2),
         _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), float(softmax_scale), S,
-        _dev(o_part, "o_part", torch.float32), _dev(lse_part, "lse_part", torch.float32),
+        _dev(o_part, "o_part"), _dtype_code(o_part), _dev(lse_part, "lse_part", torch.float32),
         _dtype_code(q_lat), _stream(stream)))
 
 
 def mla_splitk_combine(o_part, lse_part, out, lse_out=None, stream=None):
+    """Log-sum-exp combine of float32 or bfloat16 partials o_part [B,H,S,d_c] into out [B,H,d_c]."""
     torch = _torch()
     B, H, S, d_c = o_part.shape
     _expect(tuple(lse_part.shape) == (B, H, S), "lse_part must be [B,H,S]")
@@ -242,8 +244,8 @@ def mla_splitk_combine(o_part, lse_part, out, lse_out=None, stream=None):
     if lse_out is not None:
         _expect(tuple(lse_out.shape) == (B, H), "lse_out must be [B,H]")
     _check(lib.mla_splitk_combine(
-        _dev(o_part, "o_part", torch.float32, 4), _dev(lse_part, "lse_part", torch.float32, 3),
-        B, H, S, d_c, _dev(out, "out", torch.float32, 3),
+        _dev(o_part, "o_part", None, 4), _dtype_code(o_part),
+        _dev(lse_part, "lse_part", torch.float32, 3), B, H, S, d_c, _dev(out, "out", torch.float32, 3),
         _dev(lse_out, "lse_out", torch.float32, 2), _stream(stream)))
 
 

@@ -14,11 +14,11 @@
 
 namespace mla {
 
-template <typename T, int DC, int DR>
+template <typename T, typename OT, int DC, int DR>
 __global__ __launch_bounds__(64) void attn_generic_kernel(
     const T* __restrict__ q_lat, const T* __restrict__ q_pe, const T* __restrict__ cache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int H,
-    int P, int max_pages, int pages_per_split, int S, float scale_log2, float* __restrict__ o_part,
+    int P, int max_pages, int pages_per_split, int S, float scale_log2, OT* __restrict__ o_part,
     float* __restrict__ lse_part) {
   static_assert(DR <= 64, "rope part must fit one lane each");
   constexpr int ROW = DC + DR;
@@ -73,21 +73,27 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     const int idx = lane + 64 * k;
-    if (idx < DC) o_part[ob * DC + idx] = acc[k] * inv;
+    if (idx < DC) st(o_part + ob * DC + idx, acc[k] * inv);
   }
   if (lane == 0 && lse_part != nullptr)
     lse_part[ob] = l > 0.f ? (m + __log2f(l)) * 0.6931471805599453f : -INFINITY;
 }
 
-template <typename T, int DC, int DR>
-static hipError_t launch_generic(const PagedArgs& a, hipStream_t st) {
+template <typename T, typename OT, int DC, int DR>
+static hipError_t launch_generic_t(const PagedArgs& a, hipStream_t st) {
   dim3 grid(a.num_splits, a.H, a.B);
-  hipLaunchKernelGGL((attn_generic_kernel<T, DC, DR>), grid, dim3(64), 0, st,
+  hipLaunchKernelGGL((attn_generic_kernel<T, OT, DC, DR>), grid, dim3(64), 0, st,
                      static_cast<const T*>(a.q_lat), static_cast<const T*>(a.q_pe),
                      static_cast<const T*>(a.cache), a.block_table, a.seq_lens, a.H,
                      a.page_size, a.max_pages, a.pages_per_split, a.num_splits,
-                     a.scale * 1.4426950408889634f, a.o_part, a.lse_part);
+                     a.scale * 1.4426950408889634f, static_cast<OT*>(a.o_part), a.lse_part);
   return hipGetLastError();
+}
+
+template <typename T, int DC, int DR>
+static hipError_t launch_generic(const PagedArgs& a, hipStream_t st) {
+  return a.part_bf16 ? launch_generic_t<T, bf16raw, DC, DR>(a, st)
+                     : launch_generic_t<T, float, DC, DR>(a, st);
 }
 
 hipError_t launch_attn_generic_f32_64_16(const PagedArgs& a, hipStream_t s) {

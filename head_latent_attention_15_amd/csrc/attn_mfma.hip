@@ -137,11 +137,12 @@ __device__ __forceinline__ float from_bf16(__bf16 h) {
 // reading the rows straight from the paged cache.  One wavefront handles n_heads heads
 // starting at h_begin; lane l owns features 9l .. 9l+8 of the score and latent columns
 // l + 64k.
+template <typename OT>
 __device__ void split_exact_fallback(const bf16raw* __restrict__ q_lat,
                                      const bf16raw* __restrict__ q_pe,
                                      const bf16raw* __restrict__ cache, const int32_t* bt_row,
                                      int log2P, int j0, int j1, int b, int H,
-                                     int S, int s, float scale_log2, float* __restrict__ o_part,
+                                     int S, int s, float scale_log2, OT* __restrict__ o_part,
                                      float* __restrict__ lse_part, int h_begin, int n_heads,
                                      int lane) {
   const int P = 1 << log2P;
@@ -173,7 +174,7 @@ __device__ void split_exact_fallback(const bf16raw* __restrict__ q_lat,
     }
     const int64_t ob = (static_cast<int64_t>(b) * H + h) * S + s;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) o_part[ob * DC + lane + 64 * k] = acc[k] / l;
+    for (int k = 0; k < 8; ++k) st(o_part + ob * DC + lane + 64 * k, acc[k] / l);
     if (lane == 0 && lse_part != nullptr) lse_part[ob] = (m + __log2f(l)) * LN2;
   }
 }
@@ -187,18 +188,19 @@ __device__ void split_exact_fallback(const bf16raw* __restrict__ q_lat,
 // it-1, whose buffer then receives the copies of tile it+2.  Between barriers the waves run
 // free, so the two waves sharing a SIMD overlap one's softmax arithmetic with the other's
 // matrix-core work.
-template <int NW>
+template <int NW, typename OT>
 __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     const bf16raw* __restrict__ q_lat, const bf16raw* __restrict__ q_pe,
     const bf16raw* __restrict__ cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int H, int log2P, int max_pages, int pages_per_split,
-    int S, float scale_log2, float* __restrict__ o_part, float* __restrict__ lse_part) {
+    int S, float scale_log2, OT* __restrict__ o_part, float* __restrict__ lse_part) {
   constexpr int NT = NW * 64;
   constexpr int NCT = DC / 16;                                    // PV column tiles
   constexpr int STEPS = KSTEPS * 2;                               // score MFMA steps per tile
   constexpr int COPIES = (TILE_WAVE_COPIES + NW - 1) / NW;        // tile copies per wave
   constexpr int COPY_EVERY = STEPS / COPIES;                      // score steps between copies
   static_assert(NW == 1 || NW == 2 || NW == 4 || NW == 8, "16 to 128 heads");
+  static_assert(KSTEPS == 18, "query loader covers 512 + 64 features");
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   lds_char_t* const lsm = (lds_char_t*)smem;  // 32-bit LDS addressing for the tile reads
   const uint32_t smem_lds = static_cast<uint32_t>(reinterpret_cast<size_t>(lsm));
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   if (j0 >= j1) {  // empty split: o = 0, lse = -inf
     for (int e = tid; e < H * DC; e += NT) {
       const int h = e / DC, c = e % DC;
-      o_part[((static_cast<int64_t>(b) * H + h) * S + s) * DC + c] = 0.f;
+      st(o_part + ((static_cast<int64_t>(b) * H + h) * S + s) * DC + c, 0.f);
     }
     if (lse_part != nullptr)
       for (int h = tid; h < H; h += NT) lse_part[(static_cast<int64_t>(b) * H + h) * S + s] = -INFINITY;
@@ -229,17 +231,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   }
 
   // resident query fragments: B operand of S^T = K Q^T (lane (g, r16): head h0 + r16,
-  // features 32 kk + 8 g .. + 7)
+  // features 32 kk + 8 g .. + 7); loaded after the first tile's copies are issued
   bf16x8_t qf[KSTEPS];
-  {
-    const bf16raw* qrow = q_lat + (static_cast<int64_t>(b) * H + h0 + r16) * DC + 8 * g;
-    const bf16raw* prow = q_pe + (static_cast<int64_t>(b) * H + h0 + r16) * DR + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < DC / 32; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk);
-#pragma unroll
-    for (int kk = 0; kk < DR / 32; ++kk)
-      qf[DC / 32 + kk] = *reinterpret_cast<const bf16x8_t*>(prow + 32 * kk);
-  }
 
   // Wave w issues copies q = w, w + NW, ... of each tile; lane l of copy q fills LDS chunk
   // 64 q + l, i.e. row t, stored position p, which holds logical chunk p ^ swz(t) of the row.
@@ -257,10 +250,13 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     int ln = lane;
     asm volatile("" : "+v"(ln));  // recompute the copy coordinates each time (no live ranges)
     const int q = w + NW * r < TILE_WAVE_COPIES ? w + NW * r : w;
-    const int chunk = 64 * q + ln;
-    const int t = chunk / CHUNKS;
-    const int c = (chunk - t * CHUNKS) ^ swz(t);
-    const uint32_t voff = static_cast<uint32_t>(min(t, j1 - 1 - tb) * ROW_BYTES + c * 16);
+    const unsigned chunk = 64u * q + ln;  // < 2304
+    // chunk / 72 and the row offsets on the full-rate 24-bit multiplier:
+    // floor(chunk * 14564 / 2^20) equals chunk / 72 for every chunk below 2304
+    const unsigned t = __umul24(chunk, 14564u) >> 20;
+    const unsigned c = (chunk - __umul24(t, static_cast<unsigned>(CHUNKS))) ^ swz(t);
+    const unsigned trow = min(t, static_cast<unsigned>(j1 - 1 - tb));
+    const uint32_t voff = __umul24(trow, static_cast<unsigned>(ROW_BYTES)) + c * 16;
     dma16(base, voff, smem_lds + buf * TILE_BYTES + q * 64 * 16);
   };
   auto issue_tile = [&](int tb, int buf) {
@@ -410,10 +406,22 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     }
   };
 
-  // The query loads are complete before the first copy is issued: the copies are invisible
-  // to the compiler's own wait counting, so no compiler-inserted wait may fall after them.
-  wait_vmcnt<0>();
+  // The 18 query fragments of this wave in one assembly block that also waits for them
+  // (and, being issued after them, for this wave's copies of the first tile), so the two
+  // latencies overlap and no compiler-inserted wait falls after a later copy.
+  auto load_query = [&]() {
+    const bf16raw* qrow = q_lat + (static_cast<int64_t>(b) * H + h0 + r16) * DC + 8 * g;
+    const bf16raw* prow = q_pe + (static_cast<int64_t>(b) * H + h0 + r16) * DR + 8 * g;
+    i32x4_t r[KSTEPS];
+    asm volatile("global_load_dwordx4 %0, %18, off\n\tglobal_load_dwordx4 %1, %18, off offset:64\n\tglobal_load_dwordx4 %2, %18, off offset:128\n\tglobal_load_dwordx4 %3, %18, off offset:192\n\tglobal_load_dwordx4 %4, %18, off offset:256\n\tglobal_load_dwordx4 %5, %18, off offset:320\n\tglobal_load_dwordx4 %6, %18, off offset:384\n\tglobal_load_dwordx4 %7, %18, off offset:448\n\tglobal_load_dwordx4 %8, %18, off offset:512\n\tglobal_load_dwordx4 %9, %18, off offset:576\n\tglobal_load_dwordx4 %10, %18, off offset:640\n\tglobal_load_dwordx4 %11, %18, off offset:704\n\tglobal_load_dwordx4 %12, %18, off offset:768\n\tglobal_load_dwordx4 %13, %18, off offset:832\n\tglobal_load_dwordx4 %14, %18, off offset:896\n\tglobal_load_dwordx4 %15, %18, off offset:960\n\tglobal_load_dwordx4 %16, %19, off\n\tglobal_load_dwordx4 %17, %19, off offset:64\n\ts_waitcnt vmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15]), "=&v"(r[16]), "=&v"(r[17])
+                 : "v"(qrow), "v"(prow)
+                 : "memory");
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = __builtin_bit_cast(bf16x8_t, r[kk]);
+  };
   issue_tile(j0, 0);
+  load_query();
   if (ntiles > 1) issue_tile(j0 + TILE, 1);
   // Waves 0 .. NW/2-1 (group 0) take each tile as scores then PV; waves NW/2 .. NW-1
   // (group 1) run half a tile behind, as PV of the previous tile then scores.  A SIMD holds
@@ -450,24 +458,53 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     const int64_t row = (static_cast<int64_t>(b) * H + h0 + r16) * S + s;
     if (lse_part != nullptr && g == 0) lse_part[row] = (m_ref + __log2f(l_acc[0])) * LN2;
     const float inv = 1.f / l_acc[0];
-    float* dst = o_part + row * DC + 4 * g;
+    if constexpr (std::is_same<OT, float>::value) {
+      float* dst = o_part + row * DC + 4 * g;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) *reinterpret_cast<f32x4_t*>(dst + 16 * ct) = o[ct] * inv;
+      for (int ct = 0; ct < NCT; ++ct) *reinterpret_cast<f32x4_t*>(dst + 16 * ct) = o[ct] * inv;
+    } else {
+      // bf16 (round to nearest even), 16 bytes per lane and store: for column tiles 2m and
+      // 2m + 1 a lane pair (g, g ^ 1) trades halves, so even g writes columns
+      // 32 m + 4 g .. + 7 and odd g writes 32 m + 4 g + 12 .. + 7 (half the store
+      // instructions of four-column stores)
+      const bool odd = (g & 1) != 0;
+      bf16raw* dst = o_part + row * DC + 4 * g + (odd ? 12 : 0);
+#pragma unroll
+      for (int m = 0; m < NCT / 2; ++m) {
+        const f32x4_t a = o[2 * m] * inv, c = o[2 * m + 1] * inv;
+        const bf16x4_t pa = __builtin_shufflevector(to_bf16x2(a[0], a[1]), to_bf16x2(a[2], a[3]), 0, 1, 2, 3);
+        const bf16x4_t pc = __builtin_shufflevector(to_bf16x2(c[0], c[1]), to_bf16x2(c[2], c[3]), 0, 1, 2, 3);
+        const uint2 send = __builtin_bit_cast(uint2, odd ? pa : pc);
+        uint2 recv;
+        recv.x = __shfl_xor(send.x, 16, 64);
+        recv.y = __shfl_xor(send.y, 16, 64);
+        const bf16x4_t pr = __builtin_bit_cast(bf16x4_t, recv);
+        const bf16x8_t v8 = odd ? __builtin_shufflevector(pr, pc, 0, 1, 2, 3, 4, 5, 6, 7)
+                                : __builtin_shufflevector(pa, pr, 0, 1, 2, 3, 4, 5, 6, 7);
+        *reinterpret_cast<bf16x8_t*>(dst + 32 * m) = v8;
+      }
+    }
   } else {
     split_exact_fallback(q_lat, q_pe, cache, bt_row, log2P, j0, j1, b, H, S, s, scale_log2,
                          o_part, lse_part, h0, 16, lane);
   }
 }
 
-template <int NW>
-hipError_t launch_nw(const PagedArgs& a, hipStream_t st) {
+template <int NW, typename OT>
+hipError_t launch_nw_t(const PagedArgs& a, hipStream_t st) {
   const float log2e = 1.4426950408889634f;
-  hipLaunchKernelGGL((attn_mfma_kernel<NW>), dim3(a.B, a.num_splits), dim3(NW * 64), 0, st,
+  hipLaunchKernelGGL((attn_mfma_kernel<NW, OT>), dim3(a.B, a.num_splits), dim3(NW * 64), 0, st,
                      static_cast<const bf16raw*>(a.q_lat), static_cast<const bf16raw*>(a.q_pe),
                      static_cast<const bf16raw*>(a.cache), a.block_table, a.seq_lens, a.H,
                      __builtin_ctz(static_cast<unsigned>(a.page_size)), a.max_pages,
-                     a.pages_per_split, a.num_splits, a.scale * log2e, a.o_part, a.lse_part);
+                     a.pages_per_split, a.num_splits, a.scale * log2e,
+                     static_cast<OT*>(a.o_part), a.lse_part);
   return hipGetLastError();
+}
+
+template <int NW>
+hipError_t launch_nw(const PagedArgs& a, hipStream_t st) {
+  return a.part_bf16 ? launch_nw_t<NW, bf16raw>(a, st) : launch_nw_t<NW, float>(a, st);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }

@@ -6,8 +6,8 @@
 // softmax denominator is a sum over the tokens (qiita.com/joule "Attention 計算").
 //
 // One workgroup per (sequence, head); each thread owns 4 consecutive latent columns
-// (one 16-byte load per split), the weights live in LDS.  Deterministic: fixed summation
-// order, no atomics.
+// (one 16-byte load per split for fp32 partials, 8 bytes for bf16), the weights live in
+// LDS.  Deterministic: fixed summation order, no atomics.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -15,8 +15,20 @@ namespace mla {
 
 constexpr int kCombineThreads = 128;
 
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned short u16x4_t;
+
+__device__ __forceinline__ f32x4_t load4(const float* p) {
+  return *reinterpret_cast<const f32x4_t*>(p);
+}
+__device__ __forceinline__ f32x4_t load4(const bf16raw* p) {
+  const u16x4_t v = *reinterpret_cast<const u16x4_t*>(p);
+  return f32x4_t{bf16_to_f32(v[0]), bf16_to_f32(v[1]), bf16_to_f32(v[2]), bf16_to_f32(v[3])};
+}
+
+template <typename PT>
 __global__ __launch_bounds__(kCombineThreads) void splitk_combine_kernel(
-    const float* __restrict__ o_part, const float* __restrict__ lse_part, int S, int d_c,
+    const PT* __restrict__ o_part, const float* __restrict__ lse_part, int S, int d_c,
     float* __restrict__ out, float* __restrict__ lse_out) {
   extern __shared__ float w_lds[];  // S weights
   __shared__ float red[kCombineThreads / 64];
@@ -50,13 +62,13 @@ __global__ __launch_bounds__(kCombineThreads) void splitk_combine_kernel(
   for (int w = 0; w < kCombineThreads / 64; ++w) den += red[w];
   const float inv = den > 0.f ? 1.f / den : 0.f;
 
-  const float* base = o_part + static_cast<int64_t>(bh) * S * d_c;
+  const PT* base = o_part + static_cast<int64_t>(bh) * S * d_c;
   for (int c = tid * 4; c < d_c; c += kCombineThreads * 4) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < S; ++s) {
       const float w = w_lds[s];
       if (w != 0.f) {
-        const float4 v = *reinterpret_cast<const float4*>(base + static_cast<int64_t>(s) * d_c + c);
+        const f32x4_t v = load4(base + static_cast<int64_t>(s) * d_c + c);
         acc.x += w * v.x;
         acc.y += w * v.y;
         acc.z += w * v.z;
@@ -64,16 +76,20 @@ __global__ __launch_bounds__(kCombineThreads) void splitk_combine_kernel(
       }
     }
     acc.x *= inv; acc.y *= inv; acc.z *= inv; acc.w *= inv;
-    *reinterpret_cast<float4*>(out + static_cast<int64_t>(bh) * d_c + c) = acc;
+    *reinterpret_cast<f32x4_t*>(out + static_cast<int64_t>(bh) * d_c + c) = acc;
   }
   if (tid == 0 && lse_out != nullptr) lse_out[bh] = den > 0.f ? msafe + logf(den) : -INFINITY;
 }
 
-hipError_t launch_splitk_combine(const float* o_part, const float* lse_part, int B, int H,
-                                 int S, int d_c, float* out, float* lse_out, hipStream_t st) {
+hipError_t launch_splitk_combine(const void* o_part, int part_bf16, const float* lse_part, int B,
+                                 int H, int S, int d_c, float* out, float* lse_out, hipStream_t st) {
   const size_t lds = static_cast<size_t>(S) * sizeof(float);
-  hipLaunchKernelGGL(splitk_combine_kernel, dim3(B * H), dim3(kCombineThreads), lds, st,
-                     o_part, lse_part, S, d_c, out, lse_out);
+  if (part_bf16)
+    hipLaunchKernelGGL(splitk_combine_kernel<bf16raw>, dim3(B * H), dim3(kCombineThreads), lds,
+                       st, static_cast<const bf16raw*>(o_part), lse_part, S, d_c, out, lse_out);
+  else
+    hipLaunchKernelGGL(splitk_combine_kernel<float>, dim3(B * H), dim3(kCombineThreads), lds, st,
+                       static_cast<const float*>(o_part), lse_part, S, d_c, out, lse_out);
   return hipGetLastError();
 }
 

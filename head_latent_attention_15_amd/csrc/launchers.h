@@ -18,7 +18,8 @@ struct PagedArgs {
   float scale;
   int32_t num_splits;
   int32_t pages_per_split;
-  float* o_part;
+  void* o_part;      // fp32 or bf16 (part_bf16), [B][H][S][d_c]
+  int part_bf16;     // 1: o_part elements are bf16 (round to nearest even)
   float* lse_part;
 };
 
@@ -29,8 +30,8 @@ hipError_t launch_attn_generic_bf16_512_64(const PagedArgs& a, hipStream_t s);
 hipError_t launch_attn_mfma_bf16_512_64(const PagedArgs& a, hipStream_t s);
 bool attn_mfma_supported(const PagedArgs& a);
 
-hipError_t launch_splitk_combine(const float* o_part, const float* lse_part, int B, int H,
-                                 int S, int d_c, float* out, float* lse_out, hipStream_t s);
+hipError_t launch_splitk_combine(const void* o_part, int part_bf16, const float* lse_part, int B,
+                                 int H, int S, int d_c, float* out, float* lse_out, hipStream_t s);
 
 // Batched small-M GEMM: y[z][m][n] = sum_k x[z][m][k] * W_z(n, k), with
 // W_z(n, k) = w[z*sw + n*ldw + k] when w_nk, else w[z*sw + k*ldw + n].

@@ -118,8 +118,8 @@ int32_t mla_suggest_num_splits(int32_t B, int32_t max_seq_len, int64_t total_tok
 mla_status_t mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_cache,
                              const int32_t* block_table, const int32_t* seq_lens,
                              const mla_paged_shape_t* shape, float softmax_scale,
-                             int32_t num_splits, float* o_part, float* lse_part,
-                             mla_dtype_t dtype, void* stream) {
+                             int32_t num_splits, void* o_part, mla_dtype_t part_dtype,
+                             float* lse_part, mla_dtype_t dtype, void* stream) {
   if (!q_lat || !q_pe || !kv_cache || !block_table || !seq_lens || !o_part)
     return fail(MLA_ERR_NULL, "mla_decode_attn: a required pointer is NULL");
   mla_status_t st = check_paged_shape(shape);
@@ -131,6 +131,8 @@ mla_status_t mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv
   if (!std::isfinite(softmax_scale))
     return fail(MLA_ERR_SHAPE, "softmax_scale is not finite");
   if (!is_dtype(dtype)) return fail(MLA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (!is_dtype(part_dtype))
+    return fail(MLA_ERR_UNSUPPORTED, "unknown partial dtype %d", part_dtype);
 
   mla::PagedArgs a;
   a.q_lat = q_lat;
@@ -149,6 +151,7 @@ mla_status_t mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv
   a.num_splits = num_splits;
   a.pages_per_split = pages_per_split(shape->max_pages_per_seq, num_splits);
   a.o_part = o_part;
+  a.part_bf16 = part_dtype == MLA_BF16;
   a.lse_part = lse_part;
   hipStream_t s = as_stream(stream);
 
@@ -165,17 +168,19 @@ mla_status_t mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv
               a.d_c, a.d_R, a.H, dtype);
 }
 
-mla_status_t mla_splitk_combine(const float* o_part, const float* lse_part, int32_t B,
-                                int32_t H, int32_t num_splits, int32_t d_c, float* out,
-                                float* lse_out, void* stream) {
+mla_status_t mla_splitk_combine(const void* o_part, mla_dtype_t part_dtype,
+                                const float* lse_part, int32_t B, int32_t H, int32_t num_splits,
+                                int32_t d_c, float* out, float* lse_out, void* stream) {
   if (!o_part || !lse_part || !out)
     return fail(MLA_ERR_NULL, "mla_splitk_combine: a required pointer is NULL");
   if (B < 1 || H < 1 || d_c < 1 || num_splits < 1 || num_splits > kMaxSplits)
     return fail(MLA_ERR_SHAPE, "mla_splitk_combine: bad sizes B=%d H=%d S=%d d_c=%d", B, H,
                 num_splits, d_c);
   if (d_c % 4 != 0) return fail(MLA_ERR_SHAPE, "mla_splitk_combine: d_c %d %% 4 != 0", d_c);
-  return launched(mla::launch_splitk_combine(o_part, lse_part, B, H, num_splits, d_c, out,
-                                             lse_out, as_stream(stream)),
+  if (!is_dtype(part_dtype))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_splitk_combine: unknown partial dtype %d", part_dtype);
+  return launched(mla::launch_splitk_combine(o_part, part_dtype == MLA_BF16, lse_part, B, H,
+                                             num_splits, d_c, out, lse_out, as_stream(stream)),
                   "split-K combine");
 }
 
@@ -186,7 +191,7 @@ mla_status_t mla_decode(const void* q_lat, const void* q_pe, const void* kv_cach
                         float* out, float* lse_out, mla_dtype_t dtype, void* stream) {
   if (num_splits == 1)
     return mla_decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, shape, softmax_scale,
-                           1, out, lse_out, dtype, stream);
+                           1, out, MLA_F32, lse_out, dtype, stream);
   mla_status_t st = check_paged_shape(shape);
   if (st != MLA_OK) return st;
   if (num_splits < 1 || num_splits > kMaxSplits)
@@ -198,15 +203,17 @@ mla_status_t mla_decode(const void* q_lat, const void* q_pe, const void* kv_cach
                 workspace ? workspace_bytes : static_cast<size_t>(0), need);
   if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
     return fail(MLA_ERR_WORKSPACE, "mla_decode: workspace is not 16-byte aligned");
+  // partials in the input precision: bf16 for bf16 caches, fp32 otherwise
+  const mla_dtype_t part_dtype = dtype == MLA_BF16 ? MLA_BF16 : MLA_F32;
   const size_t rows = static_cast<size_t>(shape->batch) * shape->num_heads * num_splits;
-  float* o_part = static_cast<float*>(workspace);
+  void* o_part = workspace;
   float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                              align256(rows * shape->d_latent * sizeof(float)));
   st = mla_decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, shape, softmax_scale,
-                       num_splits, o_part, lse_part, dtype, stream);
+                       num_splits, o_part, part_dtype, lse_part, dtype, stream);
   if (st != MLA_OK) return st;
-  return mla_splitk_combine(o_part, lse_part, shape->batch, shape->num_heads, num_splits,
-                            shape->d_latent, out, lse_out, stream);
+  return mla_splitk_combine(o_part, part_dtype, lse_part, shape->batch, shape->num_heads,
+                            num_splits, shape->d_latent, out, lse_out, stream);
 }
 
 mla_status_t mla_absorb_q(const float* q_c, const void* w_uk, const float* q_r,

@@ -78,8 +78,9 @@ typedef struct {
 size_t mla_cache_bytes(int64_t B, int64_t T, int64_t layers, int32_t d_c, int32_t d_R,
                        int32_t elem_bytes);
 
-/* Bytes of workspace mla_decode needs for num_splits > 1: the fp32 split partials
- * o_part [B][H][S][d_c] followed by lse_part [B][H][S] (256-byte aligned). */
+/* Bytes of workspace mla_decode needs for num_splits > 1: room for fp32 split partials
+ * o_part [B][H][S][d_c] followed by lse_part [B][H][S] (256-byte aligned); enough for
+ * the bf16 partials mla_decode uses with bf16 caches. */
 size_t mla_decode_workspace_bytes(int32_t B, int32_t H, int32_t d_c, int32_t num_splits);
 
 /* A split count for mla_decode_attn: enough (sequence, split) work items to cover
@@ -135,7 +136,9 @@ mla_status_t mla_kv_append(const float* c_kv, const float* k_r, int32_t n_new,
  * A split with no tokens writes o = 0 and lse = -inf.
  *   q_lat [B][H][d_latent], q_pe [B][H][d_rope]: `dtype` (q_pe already rotated)
  *   kv_cache: `dtype`;  block_table [B][max_pages_per_seq], seq_lens [B]: int32, device
- *   o_part [B][H][S][d_latent] fp32;  lse_part [B][H][S] fp32.
+ *   o_part [B][H][S][d_latent] in part_dtype (F32, or BF16 rounded to nearest even: half
+ *   the partial traffic; the softmax sums and the PV accumulation stay fp32);
+ *   lse_part [B][H][S] fp32.
  *   With num_splits == 1, o_part is the final o~ [B][H][d_latent] and lse_part may be NULL.
  * softmax_scale is normally 1/sqrt(d_h + d_R) (1/sqrt(192) at DeepSeek-V2 shape).
  * Supported: (d_latent, d_rope, dtype) = (512, 64, BF16) with H <= 128, or
@@ -145,24 +148,25 @@ mla_status_t mla_kv_append(const float* c_kv, const float* k_r, int32_t n_new,
 mla_status_t mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_cache,
                              const int32_t* block_table, const int32_t* seq_lens,
                              const mla_paged_shape_t* shape, float softmax_scale,
-                             int32_t num_splits, float* o_part, float* lse_part,
-                             mla_dtype_t dtype, void* stream);
+                             int32_t num_splits, void* o_part, mla_dtype_t part_dtype,
+                             float* lse_part, mla_dtype_t dtype, void* stream);
 
 /* Log-sum-exp combine of split partials (exact re-assembly of one softmax whose sum
  * over tokens was cut into disjoint ranges; qiita "Attention 計算").
  *   M = max_s lse_s; w_s = e^{lse_s - M} (0 for lse_s = -inf)
  *   out[b][i][:] = sum_s w_s o_part[b][i][s][:] / sum_s w_s;  lse_out = M + ln sum_s w_s
  * All splits empty: out = 0, lse_out = -inf.
- *   o_part [B][H][S][d_c], lse_part [B][H][S] fp32;  out [B][H][d_c] fp32;
- *   lse_out [B][H] fp32 or NULL.
- * Errors: NULL, SHAPE (sizes < 1, d_c % 4). */
-mla_status_t mla_splitk_combine(const float* o_part, const float* lse_part, int32_t B,
-                                int32_t H, int32_t num_splits, int32_t d_c, float* out,
-                                float* lse_out, void* stream);
+ *   o_part [B][H][S][d_c] in part_dtype (F32 or BF16), lse_part [B][H][S] fp32;
+ *   out [B][H][d_c] fp32 (fp32 weights and sums);  lse_out [B][H] fp32 or NULL.
+ * Errors: NULL, SHAPE (sizes < 1, d_c % 4), UNSUPPORTED (part_dtype). */
+mla_status_t mla_splitk_combine(const void* o_part, mla_dtype_t part_dtype,
+                                const float* lse_part, int32_t B, int32_t H, int32_t num_splits,
+                                int32_t d_c, float* out, float* lse_out, void* stream);
 
 /* mla_decode_attn followed by mla_splitk_combine, with the split partials in a caller
  * workspace of at least mla_decode_workspace_bytes(B, H, d_latent, num_splits) bytes
- * (unused when num_splits == 1).  out [B][H][d_latent] fp32; lse_out [B][H] or NULL.
+ * (unused when num_splits == 1); the partials take the cache dtype (BF16 caches: bf16
+ * partials).  out [B][H][d_latent] fp32; lse_out [B][H] or NULL.
  * Errors: as the two calls, plus WORKSPACE when the workspace is NULL or too small. */
 mla_status_t mla_decode(const void* q_lat, const void* q_pe, const void* kv_cache,
                         const int32_t* block_table, const int32_t* seq_lens,

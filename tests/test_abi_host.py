@@ -61,10 +61,10 @@ def _shape(**kw):
     return mla._PagedShape(*[d[f] for f, _ in mla._PagedShape._fields_])
 
 
-def _attn(shape, S=1, dtype=mla.MLA_BF16, nulls=(), lse=True, scale=0.1):
+def _attn(shape, S=1, dtype=mla.MLA_BF16, nulls=(), lse=True, scale=0.1, part=mla.MLA_F32):
     p = [None if i in nulls else FAKE for i in range(6)]
     return mla.lib.mla_decode_attn(p[0], p[1], p[2], p[3], p[4], ctypes.byref(shape), scale, S,
-                                   p[5], FAKE if lse else None, dtype, None)
+                                   p[5], part, FAKE if lse else None, dtype, None)
 
 
 @pytest.mark.parametrize("null", range(6))
@@ -112,9 +112,15 @@ def test_decode_rejects_small_workspace():
 
 def test_combine_validation():
     L = mla.lib
-    assert L.mla_splitk_combine(None, FAKE, 1, 1, 2, 512, FAKE, None, None) == mla.MLA_ERR_NULL
-    assert L.mla_splitk_combine(FAKE, FAKE, 1, 1, 0, 512, FAKE, None, None) == mla.MLA_ERR_SHAPE
-    assert L.mla_splitk_combine(FAKE, FAKE, 1, 1, 2, 510, FAKE, None, None) == mla.MLA_ERR_SHAPE
+    F32, BF16 = mla.MLA_F32, mla.MLA_BF16
+    assert L.mla_splitk_combine(None, F32, FAKE, 1, 1, 2, 512, FAKE, None, None) == mla.MLA_ERR_NULL
+    assert L.mla_splitk_combine(FAKE, BF16, FAKE, 1, 1, 0, 512, FAKE, None, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_splitk_combine(FAKE, F32, FAKE, 1, 1, 2, 510, FAKE, None, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_splitk_combine(FAKE, 7, FAKE, 1, 1, 2, 512, FAKE, None, None) == mla.MLA_ERR_UNSUPPORTED
+
+
+def test_attn_rejects_unknown_partial_dtype():
+    assert _attn(_shape(), part=7) == mla.MLA_ERR_UNSUPPORTED
 
 
 def test_absorb_validation():

@@ -22,8 +22,9 @@ def mla():
     return m
 
 
-def run_attention(mla, inp, S, lse=True):
-    """decode_attn (+ combine for S > 1) on device copies of a workloads problem."""
+def run_attention(mla, inp, S, lse=True, part=torch.float32):
+    """decode_attn (+ combine for S > 1) on device copies of a workloads problem; `part` is
+    the dtype of the split partials (float32 or bfloat16)."""
     q_lat, q_pe, cache = dev(inp["q_lat"]), dev(inp["q_pe"]), dev(inp["cache"])
     bt, sl = dev(inp["block_table"]), dev(inp["seq_lens"])
     B, H, d_c = q_lat.shape
@@ -32,7 +33,7 @@ def run_attention(mla, inp, S, lse=True):
         lse_t = torch.empty(B, H, device="cuda") if lse else None
         mla.mla_decode_attn(q_lat, q_pe, cache, bt, sl, inp["scale"], 1, out, lse_t)
     else:
-        o_part = torch.empty(B, H, S, d_c, device="cuda")
+        o_part = torch.empty(B, H, S, d_c, device="cuda", dtype=part)
         lse_part = torch.empty(B, H, S, device="cuda")
         mla.mla_decode_attn(q_lat, q_pe, cache, bt, sl, inp["scale"], S, o_part, lse_part)
         out = torch.empty(B, H, d_c, device="cuda")
@@ -145,15 +146,17 @@ def test_latent_ragged_midsize(mla, H, S):
 
 
 @pytest.mark.slow
-def test_dsv2_b32_t4k_full(mla):
-    """B=32, T=4096, H=128 (the headline shape), suggested splits, full output."""
+@pytest.mark.parametrize("part", [torch.float32, torch.bfloat16], ids=["f32part", "bf16part"])
+def test_dsv2_b32_t4k_full(mla, part):
+    """B=32, T=4096, H=128 (the headline shape), suggested splits, full output; with
+    bf16 partials this is the launch configuration the benchmark times."""
     inp = W.dsv2_b32_t4k()
     S = mla.mla_suggest_num_splits(32, 4096, 0, 64, 256)
-    say(f"dsv2_b32_t4k S={S}")
-    out, lse = run_attention(mla, inp, S)
+    say(f"dsv2_b32_t4k S={S} part={part}")
+    out, lse = run_attention(mla, inp, S, part=part)
     o_ref, lse_ref = oracle_attention(inp)
     m, r = assert_bf16(host64(out), o_ref, "dsv2_b32_t4k")
-    print(f"dsv2_b32_t4k: max-abs {m:.3e} rel-L2 {r:.3e}")
+    print(f"dsv2_b32_t4k ({part}): max-abs {m:.3e} rel-L2 {r:.3e}")
     assert errors(host64(lse), lse_ref)[0] <= 2e-2
 
 
@@ -281,16 +284,33 @@ def test_splits_agree_fp32_combine(mla):
         assert_fp32(host64(lse), host64(lref), 1e-5, f"lse S={S}")
 
 
-def test_splits_mfma_vs_oracle(mla):
-    """MFMA path: every split count (including empty splits) meets the bf16 bar."""
+@pytest.mark.parametrize("part", [torch.float32, torch.bfloat16], ids=["f32part", "bf16part"])
+def test_splits_mfma_vs_oracle(mla, part):
+    """MFMA path: every split count (including empty splits) meets the bf16 bar, with
+    fp32 and with bf16 split partials."""
     inp = W.paged_attention(11, B=4, H=128, seq_lens=[64, 100, 2000, 4096])
     o_ref, lse_ref = oracle_attention(inp)
     for S in (1, 2, 7, 64):
-        say(f"splits mfma S={S}")
-        out, lse = run_attention(mla, inp, S)
+        say(f"splits mfma S={S} part={part}")
+        out, lse = run_attention(mla, inp, S, part=part)
         assert_bf16(host64(out), o_ref, f"S={S}")
         assert errors(host64(lse), lse_ref)[0] <= 2e-2
         assert torch.isfinite(lse).all()
+
+
+def test_bf16_partials_generic_path(mla):
+    """bf16 split partials through the VALU path (H=20): the combined output stays within
+    bf16 rounding of the fp32-partial result, which itself matches the oracle."""
+    inp = W.paged_attention(15, B=3, H=20, seq_lens=[70, 700, 3000])
+    o_ref, _ = oracle_attention(inp)
+    say("bf16 partials generic")
+    a, la = run_attention(mla, inp, 5)
+    b, lb = run_attention(mla, inp, 5, part=torch.bfloat16)
+    assert_bf16(host64(a), o_ref, "fp32 partials")
+    assert_bf16(host64(b), o_ref, "bf16 partials")
+    assert torch.equal(la, lb), "lse does not depend on the partial dtype"
+    d = (b - a).abs().max().item()
+    assert d <= 2.0 ** -8 * a.abs().max().item(), f"bf16 partial rounding {d}"
 
 
 def test_single_token_generic_path(mla):
