@@ -97,6 +97,50 @@ def _check(st: int) -> None:
         raise MLAError(st, lib.mla_last_error_detail().decode())
 
 
+_capture: list | None = None
+
+
+def _invoke(name: str, *args) -> None:
+    """Call lib.<name>(*args) and raise on a non-OK status; inside bind(), record instead."""
+    if _capture is not None:
+        _capture.append((name, args))
+        return
+    _check(getattr(lib, name)(*args))
+
+
+class Bound:
+    """A library call whose arguments were checked and marshalled once (see bind)."""
+
+    def __init__(self, name: str, args: tuple):
+        fn = getattr(lib, name)
+        conv = []
+        for a, t in zip(args, fn.argtypes):
+            # plain Python numbers become ctypes values once; pointers stay NULL or as given
+            conv.append(t(a) if isinstance(a, (int, float)) and not isinstance(a, bool) else a)
+        self.name, self._fn, self._args = name, fn, tuple(conv)
+
+    def __call__(self) -> None:
+        _check(self._fn(*self._args))
+
+
+def bind(fn, *args, **kwargs) -> Bound:
+    """Check and marshal the arguments of one hot-path wrapper now; return a callable that
+    repeats exactly that library call (same tensors, same stream) with no per-call Python
+    checks.  The tensors must stay alive and in place while the Bound is used."""
+    global _capture
+    if _capture is not None:
+        raise RuntimeError("bind() is not reentrant")
+    _capture = []
+    try:
+        fn(*args, **kwargs)
+        calls = _capture
+    finally:
+        _capture = None
+    if len(calls) != 1:
+        raise RuntimeError(f"{getattr(fn, '__name__', fn)} made {len(calls)} library calls")
+    return Bound(*calls[0])
+
+
 # ----------------------------------------------------------------------------- helpers
 def _torch():
     import torch
@@ -186,11 +230,11 @@ def mla_absorb_q(q_c, w_uk, q_r, seq_lens, rope_base, q_lat, q_pe, stream=None):
                 "q_r and q_pe must be [B,H,d_R]")
         _expect(q_pe.dtype == q_lat.dtype, "q_pe and q_lat must share a dtype")
         _expect(tuple(seq_lens.shape) == (B,), "seq_lens must be [B]")
-    _check(lib.mla_absorb_q(
+    _invoke("mla_absorb_q",
         _dev(q_c, "q_c", torch.float32, 3), _dev(w_uk, "w_uk", None, 2),
         _dev(q_r, "q_r", torch.float32, 3), _dev(seq_lens, "seq_lens", torch.int32, 1),
         float(rope_base), _dev(q_lat, "q_lat", None, 3), _dev(q_pe, "q_pe", None, 3),
-        B, H, d_h, d_c, d_R, _dtype_code(w_uk), _dtype_code(q_lat), _stream(stream)))
+        B, H, d_h, d_c, d_R, _dtype_code(w_uk), _dtype_code(q_lat), _stream(stream))
 
 
 def mla_kv_append(c_kv, k_r, seq_lens_before, block_table, kv_cache, rope_base, stream=None):
@@ -202,11 +246,11 @@ def mla_kv_append(c_kv, k_r, seq_lens_before, block_table, kv_cache, rope_base, 
     _expect(kv_cache.shape[2] == d_c + k_r.shape[2], "cache row must be d_c + d_R wide")
     _expect(block_table.shape[0] == B and tuple(seq_lens_before.shape) == (B,), "batch mismatch")
     shp = paged_shape(kv_cache, block_table, 1, d_c)
-    _check(lib.mla_kv_append(
+    _invoke("mla_kv_append",
         _dev(c_kv, "c_kv", torch.float32, 3), _dev(k_r, "k_r", torch.float32, 3), n,
         _dev(seq_lens_before, "seq_lens_before", torch.int32, 1),
         _dev(block_table, "block_table", torch.int32, 2), _dev(kv_cache, "kv_cache", None, 3),
-        float(rope_base), ctypes.byref(shp), _dtype_code(kv_cache), _stream(stream)))
+        float(rope_base), ctypes.byref(shp), _dtype_code(kv_cache), _stream(stream))
 
 
 def mla_decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale, num_splits,
@@ -227,12 +271,12 @@ def mla_decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale,
     if lse_part is not None:
         _expect(lse_part.numel() == B * H * S, "lse_part must hold B*H*S floats")
     shp = paged_shape(kv_cache, block_table, H, d_c)
-    _check(lib.mla_decode_attn(
+    _invoke("mla_decode_attn",
         _dev(q_lat, "q_lat", None, 3), _dev(q_pe, "q_pe", None, 3),
         _dev(kv_cache, "kv_cache", None, 3), _dev(block_table, "block_table", torch.int32, 2),
         _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), float(softmax_scale), S,
         _dev(o_part, "o_part"), _dtype_code(o_part), _dev(lse_part, "lse_part", torch.float32),
-        _dtype_code(q_lat), _stream(stream)))
+        _dtype_code(q_lat), _stream(stream))
 
 
 def mla_splitk_combine(o_part, lse_part, out, lse_out=None, stream=None):
@@ -243,10 +287,10 @@ def mla_splitk_combine(o_part, lse_part, out, lse_out=None, stream=None):
     _expect(tuple(out.shape) == (B, H, d_c), "out must be [B,H,d_c]")
     if lse_out is not None:
         _expect(tuple(lse_out.shape) == (B, H), "lse_out must be [B,H]")
-    _check(lib.mla_splitk_combine(
+    _invoke("mla_splitk_combine",
         _dev(o_part, "o_part", None, 4), _dtype_code(o_part),
         _dev(lse_part, "lse_part", torch.float32, 3), B, H, S, d_c, _dev(out, "out", torch.float32, 3),
-        _dev(lse_out, "lse_out", torch.float32, 2), _stream(stream)))
+        _dev(lse_out, "lse_out", torch.float32, 2), _stream(stream))
 
 
 def mla_decode(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale, num_splits,
@@ -260,12 +304,12 @@ def mla_decode(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale, num_
     shp = paged_shape(kv_cache, block_table, H, d_c)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.mla_decode(
+    _invoke("mla_decode",
         _dev(q_lat, "q_lat", None, 3), _dev(q_pe, "q_pe", None, 3),
         _dev(kv_cache, "kv_cache", None, 3), _dev(block_table, "block_table", torch.int32, 2),
         _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), float(softmax_scale),
         int(num_splits), ws_ptr, ws_bytes, _dev(out, "out", torch.float32, 3),
-        _dev(lse_out, "lse_out", torch.float32, 2), _dtype_code(q_lat), _stream(stream)))
+        _dev(lse_out, "lse_out", torch.float32, 2), _dtype_code(q_lat), _stream(stream))
 
 
 def mla_out_proj(o_lat, w_uv, w_o, o_heads, u=None, stream=None):
@@ -281,11 +325,11 @@ def mla_out_proj(o_lat, w_uv, w_o, o_heads, u=None, stream=None):
         _expect(tuple(w_o.shape) == (d_model, H * d_h), "w_o must be [d_model, H*d_h]")
         _expect(w_o.dtype == w_uv.dtype, "w_o and w_uv share a dtype")
         _expect(u is not None and tuple(u.shape) == (B, d_model), "u must be [B, d_model]")
-    _check(lib.mla_out_proj(
+    _invoke("mla_out_proj",
         _dev(o_lat, "o_lat", torch.float32, 3), _dev(w_uv, "w_uv", None, 2),
         _dev(w_o, "w_o", None, 2), B, H, d_c, d_h, d_model, _dtype_code(w_uv),
         _dev(o_heads, "o_heads", torch.float32, 3), _dev(u, "u", torch.float32, 2),
-        _stream(stream)))
+        _stream(stream))
 
 
 def mla_linear(x, w, y, stream=None):
@@ -294,22 +338,22 @@ def mla_linear(x, w, y, stream=None):
     M, K = x.shape
     N = w.shape[0]
     _expect(w.shape[1] == K and tuple(y.shape) == (M, N), "shapes must be x[M,K] w[N,K] y[M,N]")
-    _check(lib.mla_linear(_dev(x, "x", None, 2), _dtype_code(x), _dev(w, "w", None, 2),
+    _invoke("mla_linear", _dev(x, "x", None, 2), _dtype_code(x), _dev(w, "w", None, 2),
                           _dtype_code(w), M, N, K, _dev(y, "y", torch.float32, 2),
-                          _stream(stream)))
+                          _stream(stream))
 
 
 def mla_validate_indices(block_table, seq_lens, page_size, num_pages, dev_count, stream=None):
     torch = _torch()
     B, maxp = block_table.shape
     shp = _PagedShape(B, 1, 1, 2, page_size, maxp, num_pages)
-    _check(lib.mla_validate_indices(
+    _invoke("mla_validate_indices",
         _dev(block_table, "block_table", torch.int32, 2), _dev(seq_lens, "seq_lens", torch.int32, 1),
-        ctypes.byref(shp), _dev(dev_count, "dev_count", torch.int32), _stream(stream)))
+        ctypes.byref(shp), _dev(dev_count, "dev_count", torch.int32), _stream(stream))
 
 
 def mla_stream_read(src, sink, stream=None):
     torch = _torch()
     _expect(sink.numel() >= 4096, "sink must hold 4096 floats")
-    _check(lib.mla_stream_read(_dev(src, "src"), src.numel() * src.element_size(),
-                               _dev(sink, "sink", torch.float32), _stream(stream)))
+    _invoke("mla_stream_read", _dev(src, "src"), src.numel() * src.element_size(),
+                               _dev(sink, "sink", torch.float32), _stream(stream))

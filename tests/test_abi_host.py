@@ -164,3 +164,24 @@ def test_single_hip_runtime_in_process():
     maps = open("/proc/self/maps").read()
     libs = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
     assert len(libs) == 1, libs
+
+
+def test_bound_call_marshals_once_and_checks_status():
+    """A Bound repeats one library call with pre-converted arguments and still raises on a
+    non-OK status (here: a NULL dev_count, rejected before any GPU work)."""
+    shp = mla._PagedShape(1, 1, 1, 2, 64, 1, 1)
+    b = mla.Bound("mla_validate_indices", (FAKE, FAKE, ctypes.byref(shp), None, None))
+    assert all(not isinstance(a, int) for a in b._args if a is not None)
+    for _ in range(2):
+        with pytest.raises(mla.MLAError) as e:
+            b()
+        assert e.value.status == mla.MLA_ERR_NULL
+
+
+def test_bind_requires_exactly_one_library_call():
+    with pytest.raises(RuntimeError):
+        mla.bind(lambda: None)
+    import torch
+    with pytest.raises(ValueError):  # the wrapper's own checks still run at bind time
+        mla.bind(mla.mla_linear, torch.zeros(2, 4), torch.zeros(3, 4), torch.zeros(2, 3))
+    assert mla._capture is None

@@ -335,6 +335,30 @@ def test_deterministic(mla):
     assert torch.equal(a, b) and torch.equal(la, lb)
 
 
+def test_bound_calls_match_wrappers(mla):
+    """bind(): the pre-marshalled attention and combine calls produce bit-identical output
+    to the checked wrappers, on repeated calls."""
+    inp = W.paged_attention(14, B=3, H=128, seq_lens=[4096, 77, 1500])
+    say("bound calls")
+    ref, lref = run_attention(mla, inp, 4, part=torch.bfloat16)
+    q_lat, q_pe, cache = dev(inp["q_lat"]), dev(inp["q_pe"]), dev(inp["cache"])
+    bt, sl = dev(inp["block_table"]), dev(inp["seq_lens"])
+    B, H, d_c = q_lat.shape
+    o_part = torch.empty(B, H, 4, d_c, device="cuda", dtype=torch.bfloat16)
+    lse_part = torch.empty(B, H, 4, device="cuda")
+    out = torch.empty(B, H, d_c, device="cuda")
+    lse = torch.empty(B, H, device="cuda")
+    attn = mla.bind(mla.mla_decode_attn, q_lat, q_pe, cache, bt, sl, inp["scale"], 4, o_part,
+                    lse_part)
+    comb = mla.bind(mla.mla_splitk_combine, o_part, lse_part, out, lse)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        attn()
+        comb()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(lse, lref)
+
+
 def test_zero_query_and_ones_latent(mla):
     """q = 0: every weight is 1/T, o~ = mean of the latents.  All-ones latents: o~ = 1."""
     inp = W.paged_attention(13, B=2, H=32, seq_lens=[512, 1000])
