@@ -9,23 +9,27 @@
 // followed by the W^UV up-projection outside this kernel (kasblo.com/?p=4663,
 // "V側は、小さな表現の加重和を先に求める").
 //
-// Work decomposition.  One workgroup per (split, sequence) holds every head, so each cache
+// Work decomposition.  One workgroup per (sequence, split) holds every head, so each cache
 // byte crosses HBM once.  32-token tiles are copied HBM -> LDS with 16-byte
-// global_load_lds_dwordx4 (no VGPR round trip) into three buffers, so two tiles' copies are
-// in flight while one is consumed.  The copy is issued from inline assembly with explicit
-// vmcnt waits: it has no destination registers, and keeping it out of the compiler's view
-// stops the compiler from adding a full vmcnt(0) wait in front of every LDS read.
+// global_load_lds_dwordx4 (no VGPR round trip) into four buffers: while tile it is consumed,
+// the copies of tiles it+1 and it+2 are in flight.  The copy is issued from inline assembly
+// with explicit vmcnt waits: it has no destination registers, and keeping it out of the
+// compiler's view stops the compiler from adding a full vmcnt(0) wait in front of every LDS
+// read.  Each lane's source offset for each copy comes from a small LDS table written once
+// per workgroup.
 //
-// The two products are split differently over the NW wavefronts of the workgroup:
-//   scores: wave w owns 16 heads; S^T = K_tile (32 x 576) * Q^T (576 x 16) runs on
-//           v_mfma_f32_16x16x32_bf16 with Q resident in VGPRs for the whole split and the
-//           K operand read with ds_read_b128; the softmax weights P (bf16) go to LDS;
-//   PV:     wave w owns 512/NW latent columns of every head; O += P (H x 32) * V (32 x cols)
-//           reads P with ds_read_b128 and only its own V columns with the transposing
-//           ds_read_b64_tr_b16, whose throughput is about a quarter of ds_read_b128's.
-// Splitting PV by columns keeps the transposed reads to 1/NW of the tile per wave.
-// LDS rows carry a 16-byte-chunk XOR swizzle so the row-strided ds_read_b128 and the
-// transposed reads spread over the banks; P rows are padded to 80 bytes for the same reason.
+// Each of the NW wavefronts owns 16 heads for both products, so its softmax weights never
+// leave its registers:
+//   scores: S^T = K_tile (32 x 576) * Q^T (576 x 16) on v_mfma_f32_16x16x32_bf16, Q resident
+//           in VGPRs for the whole split, the K operand read with ds_read_b128;
+//   PV:     O^T (512 x 16) += V^T (512 x 32) * P^T (32 x 16), the V^T operand read with the
+//           transposing ds_read_b64_tr_b16.
+// Tokens are the M dimension of the score product, so the C layout of S^T is, up to a fixed
+// token permutation inside each tile, the B layout P^T needs in the PV product.  LDS rows
+// carry a 16-byte-chunk XOR swizzle that keeps both the row-strided ds_read_b128 of K and
+// the transposed reads of V conflict-free.  Half the wavefronts run the PV product of a
+// tile while the other half compute the next scores, so the two wavefronts sharing a SIMD
+// alternate between LDS-heavy and matrix-core-heavy work.
 //
 // Softmax reference: each split fixes one reference maximum per head from its first tile
 // (plus headroom) and never rescales the running output, which is only ever touched by
@@ -66,7 +70,8 @@ constexpr int TILE_WAVE_COPIES = TILE_CHUNKS / 64;  // 36 wave-wide 16-byte copi
 constexpr int TILE_BYTES = TILE_CHUNKS * 16;        // 36864
 constexpr int NBUF = 4;                             // tile buffers
 constexpr int KSTEPS = ROW / 32;                    // 18 k-steps of the score product
-constexpr int LDS_BYTES = NBUF * TILE_BYTES;
+constexpr int VOFF_TABLE = NBUF * TILE_BYTES;      // LDS offset of the copy offset table
+constexpr int LDS_BYTES = VOFF_TABLE + TILE_WAVE_COPIES * 64 * 4;  // tiles + 36 x 64 offsets
 constexpr float HEADROOM = 32.0f;  // log2 units between a split's first-tile max and its reference
 constexpr float P_RANGE = 64.0f;   // a score this far above the reference takes the fallback
 constexpr float LN2 = 0.6931471805599453f;
@@ -185,7 +190,7 @@ __device__ void split_exact_fallback(const bf16raw* __restrict__ q_lat,
 //   PV:     O^T (512 x 16) += V^T (512 x 32) * P^T (32 x 16), 32 column tiles, the V^T
 //           operand read with the transposing ds_read_b64_tr_b16.
 // One barrier per tile: it publishes tile it (every wave's copies landed) and retires tile
-// it-1, whose buffer then receives the copies of tile it+2.  Between barriers the waves run
+// it-2, whose buffer then receives the copies of tile it+2.  Between barriers the waves run
 // free, so the two waves sharing a SIMD overlap one's softmax arithmetic with the other's
 // matrix-core work.
 template <int NW, typename OT>
@@ -244,26 +249,44 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     const int pg = __builtin_amdgcn_readfirstlane(bt_row[tb >> log2P]);
     return cache_bytes + ((static_cast<int64_t>(pg) << log2P) + (tb & (P - 1))) * ROW_BYTES;
   };
-  // copy r of this wave for the tile at token tb into buffer buf; rows past the split's end
-  // repeat its last valid row
-  auto issue_copy = [&](const char* base, int tb, int buf, int r) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));  // recompute the copy coordinates each time (no live ranges)
-    const int q = w + NW * r < TILE_WAVE_COPIES ? w + NW * r : w;
-    const unsigned chunk = 64u * q + ln;  // < 2304
+  // Source offset (bytes from the tile's first row) of lane l of copy q: row t, stored
+  // position p of LDS chunk 64 q + l, which holds logical chunk p ^ swz(t); rows past the
+  // split's end (t > last) repeat its last valid row.
+  auto copy_voff = [&](int q, int l, unsigned last) {
+    const unsigned chunk = 64u * q + l;  // < 2304
     // chunk / 72 and the row offsets on the full-rate 24-bit multiplier:
     // floor(chunk * 14564 / 2^20) equals chunk / 72 for every chunk below 2304
     const unsigned t = __umul24(chunk, 14564u) >> 20;
     const unsigned c = (chunk - __umul24(t, static_cast<unsigned>(CHUNKS))) ^ swz(t);
-    const unsigned trow = min(t, static_cast<unsigned>(j1 - 1 - tb));
-    const uint32_t voff = __umul24(trow, static_cast<unsigned>(ROW_BYTES)) + c * 16;
-    dma16(base, voff, smem_lds + buf * TILE_BYTES + q * 64 * 16);
+    const unsigned trow = min(t, last);
+    return __umul24(trow, static_cast<unsigned>(ROW_BYTES)) + c * 16;
+  };
+  auto copy_index = [&](int r) { return w + NW * r < TILE_WAVE_COPIES ? w + NW * r : w; };
+  // copy r of this wave for the tile at token tb into buffer buf, offsets computed in place
+  // (the form that clamps rows at the split's end)
+  auto issue_copy = [&](const char* base, int tb, int buf, int r) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // recompute the copy coordinates each time (no live ranges)
+    const int q = copy_index(r);
+    dma16(base, copy_voff(q, ln, static_cast<unsigned>(j1 - 1 - tb)), smem_lds + buf * TILE_BYTES + q * 64 * 16);
   };
   auto issue_tile = [&](int tb, int buf) {
     const char* base = tile_base(tb);
 #pragma unroll
     for (int r = 0; r < COPIES; ++r) issue_copy(base, tb, buf, r);
   };
+  // The copy coordinates do not depend on the tile: the workgroup writes them once to an
+  // LDS table, row t << 16 | chunk byte offset, and a copy inside the loop reads its lane's
+  // entry there (one LDS read, then clamp and multiply) instead of recomputing them.
+  auto table_entry = [&](int r) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    return *((const __attribute__((address_space(3))) uint32_t*)(lsm + VOFF_TABLE) + copy_index(r) * 64 + ln);
+  };
+  auto entry_voff = [&](uint32_t e, unsigned last) {
+    return __umul24(min(e >> 16, last), static_cast<unsigned>(ROW_BYTES)) + (e & 0xffffu);
+  };
+
 
   const int ntiles = (j1 - j0 + TILE - 1) / TILE;
 
@@ -291,6 +314,10 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     const lds_char_t* tile = lsm + (it % NBUF) * TILE_BYTES;
     const int tb2 = it + 2 < ntiles ? tb + 2 * TILE : tb;
     const char* base2 = tile_base(tb2);
+    const unsigned last2 = static_cast<unsigned>(j1 - 1 - tb2);  // rows past it repeat it
+    // table reads this many score steps ahead of their copy (0: just before it)
+    constexpr int LEAD = COPY_EVERY > 3 ? 3 : COPY_EVERY - 1;
+    uint32_t enext = table_entry(0);
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int gg = ln >> 4, rr = ln & 15;
@@ -324,8 +351,14 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
         const int kk = step >> 1, mt = step & 1;
         const int ch = mt * 2 + (kk & 1);
         sacc4[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step % KRING], qf[kk], sacc4[ch], 0, 0, 0);
+        if (LEAD == 0 && step > 0 && step % COPY_EVERY == 0 && step / COPY_EVERY < COPIES)
+          enext = table_entry(step / COPY_EVERY);
         if (step % COPY_EVERY == 0 && step / COPY_EVERY < COPIES)
-          issue_copy(base2, tb2, (it + 2) % NBUF, step / COPY_EVERY);
+          dma16(base2, entry_voff(enext, last2),
+                smem_lds + ((it + 2) % NBUF) * TILE_BYTES + copy_index(step / COPY_EVERY) * 64 * 16);
+        if (LEAD > 0 && step + LEAD >= COPY_EVERY && (step + LEAD) % COPY_EVERY == 0 &&
+            (step + LEAD) / COPY_EVERY < COPIES)
+          enext = table_entry((step + LEAD) / COPY_EVERY);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -421,6 +454,12 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = __builtin_bit_cast(bf16x8_t, r[kk]);
   };
   issue_tile(j0, 0);
+  for (int e = tid; e < TILE_WAVE_COPIES * 64; e += NT) {
+    const unsigned chunk = static_cast<unsigned>(e);
+    const unsigned t = chunk / CHUNKS, c = (chunk % CHUNKS) ^ swz(t);
+    ((__attribute__((address_space(3))) uint32_t*)(lsm + VOFF_TABLE))[e] = (t << 16) | (c * 16);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // table written before barrier 0
   load_query();
   if (ntiles > 1) issue_tile(j0 + TILE, 1);
   // Waves 0 .. NW/2-1 (group 0) take each tile as scores then PV; waves NW/2 .. NW-1
@@ -431,6 +470,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   // overwrite; both groups pass ntiles + 1 barriers.
   auto tile_barrier = [&](int it) {
     if (it < ntiles) wait_vmcnt<COPIES>();  // own copies of tile it landed
+    else wait_vmcnt<0>();                   // no copy may still be writing LDS at the end
     block_barrier();
   };
   if (NW == 1 || w < NW / 2) {
@@ -530,3 +570,4 @@ hipError_t launch_attn_mfma_bf16_512_64(const PagedArgs& a, hipStream_t s) {
 }
 
 }  // namespace mla
+
