@@ -304,6 +304,18 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, i16x4x2_ones());
   bool out_of_range = false;  // sticky: a score of this head block left the reference range
 
+  // Lane offsets of the K fragments inside a tile buffer, the same for every tile (kept in
+  // registers):
+  //   kb[mt][par]: the K fragment of k-step par (0 / 1) for M tile mt: row
+  //     8 (r16 >> 2) + 4 mt + (r16 & 3), logical chunk 4 par + g; k-step kk adds 128 (kk >> 1);
+  int kb[2][2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int t = 8 * (r16 >> 2) + 4 * mt + (r16 & 3);
+#pragma unroll
+    for (int par = 0; par < 2; ++par) kb[mt][par] = t * ROW_BYTES + 16 * ((4 * par + g) ^ swz(t));
+  }
+
   // Scores and softmax of tile it, returning this wave's P^T operand.  This wave's copies of
   // tile it+2 are spread over the score steps.  Near the end of the split, where there is no
   // tile it+2, the same copies re-fetch tile it (just read, so served by L2) into the retired
@@ -318,25 +330,14 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     // table reads this many score steps ahead of their copy (0: just before it)
     constexpr int LEAD = COPY_EVERY > 3 ? 3 : COPY_EVERY - 1;
     uint32_t enext = table_entry(0);
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int gg = ln >> 4, rr = ln & 15;
 
     // ---- scores S^T (2 token M-tiles x 16 heads, K = 576).  Row r of M-tile mt is token
     //      8 (r >> 2) + 4 mt + (r & 3), so lane (gg, rr) ends up with tokens 8 gg .. 8 gg + 7
     //      of head h0 + rr: after the softmax, exactly its P^T operand of the PV product.
     //      The 36 K fragments stream through a 4-deep register ring.
-    f32x4_t sacc4[4];  // (M tile, k-step parity): four independent accumulation chains
+    f32x4_t sacc[2];  // one accumulation chain per M tile (dependent MFMAs issue back to back)
     {
-      int kb[2][2];  // [M tile][k-step parity] byte offset of the fragment of k-step 0 / 1
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int t = 8 * (rr >> 2) + 4 * mt + (rr & 3);
-#pragma unroll
-        for (int par = 0; par < 2; ++par) kb[mt][par] = t * ROW_BYTES + 16 * ((4 * par + gg) ^ swz(t));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sacc4[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      sacc[0] = sacc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       constexpr int KRING = 4;
       auto k_frag = [&](int step) {
         const int kk = step >> 1, mt = step & 1;
@@ -349,8 +350,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
       for (int step = 0; step < STEPS; ++step) {
         if (step + KRING - 1 < STEPS) ka[(step + KRING - 1) % KRING] = k_frag(step + KRING - 1);
         const int kk = step >> 1, mt = step & 1;
-        const int ch = mt * 2 + (kk & 1);
-        sacc4[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step % KRING], qf[kk], sacc4[ch], 0, 0, 0);
+        sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step % KRING], qf[kk], sacc[mt], 0, 0, 0);
         if (LEAD == 0 && step > 0 && step % COPY_EVERY == 0 && step / COPY_EVERY < COPIES)
           enext = table_entry(step / COPY_EVERY);
         if (step % COPY_EVERY == 0 && step / COPY_EVERY < COPIES)
@@ -366,30 +366,39 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     // ---- softmax (log2 domain) on the raw scores: lane holds head h0 + rr, tokens
     //      8 gg + 4 mt + i.  The scale is positive, so the raw maximum orders like the
     //      scaled one; each weight is 2^(s * scale - m_ref) with one rounding in the fma.
-    f32x4_t sc[2] = {sacc4[0] + sacc4[1], sacc4[2] + sacc4[3]};
+    f32x4_t sc[2] = {sacc[0], sacc[1]};
     if (tb + TILE > j1) {  // last tile of the split: tokens at or past j1 get weight 0
+      asm volatile("" ::: "memory");  // a real branch: the masking runs on one tile only
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (tb + 8 * gg + 4 * mt + i >= j1) sc[mt][i] = -INFINITY;
+          if (tb + 8 * g + 4 * mt + i >= j1) sc[mt][i] = -INFINITY;
     }
-    float tmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float tmax2 = mul_rn(tmax, scale_log2);
-    if (it == 0) m_ref = tmax2 + HEADROOM;
-    out_of_range |= tmax2 > m_ref + P_RANGE;
+    if (it == 0) {  // the first tile's maximum fixes the reference
+      asm volatile("" ::: "memory");
+      float tmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      m_ref = mul_rn(tmax, scale_log2) + HEADROOM;
+    }
     const float neg_m = -m_ref;
+    float e[2][4];  // exponents s * scale - m_ref
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[mt][i] = __builtin_fmaf(sc[mt][i], scale_log2, neg_m);
+    // a weight above 2^P_RANGE leaves the reference range
+    out_of_range |= fmaxf(fmaxf(fmaxf(e[0][0], e[0][1]), fmaxf(e[0][2], e[0][3])),
+                          fmaxf(fmaxf(e[1][0], e[1][1]), fmaxf(e[1][2], e[1][3]))) > P_RANGE;
     bf16x2_t pp[4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf)
-        pp[2 * mt + hlf] =
-            to_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[mt][2 * hlf], scale_log2, neg_m)),
-                      __builtin_amdgcn_exp2f(__builtin_fmaf(sc[mt][2 * hlf + 1], scale_log2, neg_m)));
+        pp[2 * mt + hlf] = to_bf16x2(__builtin_amdgcn_exp2f(e[mt][2 * hlf]),
+                                     __builtin_amdgcn_exp2f(e[mt][2 * hlf + 1]));
     const bf16x8_t pt = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
                                                 __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
                                                 0, 1, 2, 3, 4, 5, 6, 7);
@@ -401,7 +410,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   auto pv = [&](int it, bf16x8_t pt) {
     const lds_char_t* tile = lsm + (it % NBUF) * TILE_BYTES;
     int ln = lane;
-    asm volatile("" : "+v"(ln));
+    asm volatile("" : "+v"(ln));  // recomputed per tile (no long live ranges)
     const int gg = ln >> 4, rr = ln & 15;
     // ---- V^T fragments (A operand): lane (gg, rr) holds column 16 ct + rr, tokens
     //      8 gg .. 8 gg + 7, gathered by two transposing reads of 4 rows each.  Column tile ct
