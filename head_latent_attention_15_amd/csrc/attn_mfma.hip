@@ -71,7 +71,10 @@ constexpr int TILE_BYTES = TILE_CHUNKS * 16;        // 36864
 constexpr int NBUF = 4;                             // tile buffers
 constexpr int KSTEPS = ROW / 32;                    // 18 k-steps of the score product
 constexpr int VOFF_TABLE = NBUF * TILE_BYTES;      // LDS offset of the copy offset table
-constexpr int LDS_BYTES = VOFF_TABLE + TILE_WAVE_COPIES * 64 * 4;  // tiles + 36 x 64 offsets
+constexpr int PAGE_TABLE = VOFF_TABLE + TILE_WAVE_COPIES * 64 * 4;  // after 36 x 64 offsets
+constexpr int MAX_SPLIT_PAGES = 1024;               // block-table entries of one split in LDS
+constexpr int LDS_BYTES = PAGE_TABLE + MAX_SPLIT_PAGES * 4;
+static_assert(LDS_BYTES <= 163840, "LDS per workgroup");
 constexpr float HEADROOM = 32.0f;  // log2 units between a split's first-tile max and its reference
 constexpr float P_RANGE = 64.0f;   // a score this far above the reference takes the fallback
 constexpr float LN2 = 0.6931471805599453f;
@@ -245,10 +248,11 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   // source, same LDS bytes), so every wave counts COPIES copies per tile.
   const char* cache_bytes = reinterpret_cast<const char*>(cache);
   // A tile starting at token tb lies inside one page (P % 32 == 0, tiles 32-aligned).
-  auto tile_base = [&](int tb) {
-    const int pg = __builtin_amdgcn_readfirstlane(bt_row[tb >> log2P]);
+  auto tile_page = [&](int tb) { return __builtin_amdgcn_readfirstlane(bt_row[tb >> log2P]); };
+  auto page_base = [&](int pg, int tb) {
     return cache_bytes + ((static_cast<int64_t>(pg) << log2P) + (tb & (P - 1))) * ROW_BYTES;
   };
+  auto tile_base = [&](int tb) { return page_base(tile_page(tb), tb); };
   // Source offset (bytes from the tile's first row) of lane l of copy q: row t, stored
   // position p of LDS chunk 64 q + l, which holds logical chunk p ^ swz(t); rows past the
   // split's end (t > last) repeat its last valid row.
@@ -321,11 +325,20 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   // tile it+2, the same copies re-fetch tile it (just read, so served by L2) into the retired
   // buffer instead: every score step then issues the same copies and every wait counts
   // alike.
+  // the tile whose copies score(it) issues: it+2, or it itself near the end of the split
+  auto copy_tile = [&](int it) { return j0 + (it + 2 < ntiles ? it + 2 : min(it, ntiles - 1)) * TILE; };
+  // Inside the loop the block-table entries of the split come from an LDS copy: an LDS read
+  // keeps the in-order LDS wait counts, where a scalar load (same counter, out of order)
+  // would force a full wait in front of the next tile read.
+  auto split_page = [&](int tb) {
+    return __builtin_amdgcn_readfirstlane(
+        ((const __attribute__((address_space(3))) int32_t*)(lsm + PAGE_TABLE))[(tb - j0) >> log2P]);
+  };
   auto score = [&](int it) {
     const int tb = j0 + it * TILE;
     const lds_char_t* tile = lsm + (it % NBUF) * TILE_BYTES;
-    const int tb2 = it + 2 < ntiles ? tb + 2 * TILE : tb;
-    const char* base2 = tile_base(tb2);
+    const int tb2 = copy_tile(it);
+    const char* base2 = page_base(split_page(tb2), tb2);
     const unsigned last2 = static_cast<unsigned>(j1 - 1 - tb2);  // rows past it repeat it
     // table reads this many score steps ahead of their copy (0: just before it)
     constexpr int LEAD = COPY_EVERY > 3 ? 3 : COPY_EVERY - 1;
@@ -468,6 +481,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     const unsigned t = chunk / CHUNKS, c = (chunk % CHUNKS) ^ swz(t);
     ((__attribute__((address_space(3))) uint32_t*)(lsm + VOFF_TABLE))[e] = (t << 16) | (c * 16);
   }
+  for (int e = tid; e * P < j1 - j0; e += NT)  // the pages this split reads
+    ((__attribute__((address_space(3))) int32_t*)(lsm + PAGE_TABLE))[e] = bt_row[(j0 >> log2P) + e];
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // table written before barrier 0
   load_query();
   if (ntiles > 1) issue_tile(j0 + TILE, 1);
@@ -562,6 +577,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 bool attn_mfma_supported(const PagedArgs& a) {
   const bool heads_ok = a.H == 16 || a.H == 32 || a.H == 64 || a.H == 128;
+  if (a.pages_per_split > MAX_SPLIT_PAGES) return false;
   const bool page_ok = a.page_size >= TILE && (a.page_size & (a.page_size - 1)) == 0;
   return a.d_c == DC && a.d_R == DR && heads_ok && page_ok &&
          a.B <= 65535 && aligned16(a.q_lat) &&
