@@ -335,6 +335,10 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
         ((const __attribute__((address_space(3))) int32_t*)(lsm + PAGE_TABLE))[(tb - j0) >> log2P]);
   };
   auto score = [&](int it) {
+    // The two waves of a SIMD are in different phases; the sequencer favours the older
+    // wave, which left the other group behind at every barrier.  Giving the score phase
+    // (K reads, softmax arithmetic, copies) the higher issue priority balances them.
+    __builtin_amdgcn_s_setprio(1);
     const int tb = j0 + it * TILE;
     const lds_char_t* tile = lsm + (it % NBUF) * TILE_BYTES;
     const int tb2 = copy_tile(it);
@@ -421,6 +425,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
 
   // PV of tile it with this wave's P^T operand pt.
   auto pv = [&](int it, bf16x8_t pt) {
+    __builtin_amdgcn_s_setprio(0);
     const lds_char_t* tile = lsm + (it % NBUF) * TILE_BYTES;
     int ln = lane;
     asm volatile("" : "+v"(ln));  // recomputed per tile (no long live ranges)
