@@ -102,6 +102,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-seconds", type=float, default=0.5,
+                    help="keep warming up until this much time has passed (clocks settle)")
     ap.add_argument("--splits", type=int, default=0, help="split count (0: library suggestion)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32)
@@ -161,11 +163,18 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
-    log(f"warmup {args.warmup} steps, S={S}, {num_cus} CUs")
-    for k in range(args.warmup):
+    # at least W warmup steps, and at least --warmup-seconds of them: the first tens of
+    # milliseconds of back-to-back launches run at lower clocks than the steady state
+    t_w = time.perf_counter()
+    k = 0
+    while k < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
         attn(k)
         combine()
+        k += 1
+        if k % 32 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    log(f"warmup {k} steps ({time.perf_counter() - t_w:.2f} s), S={S}, {num_cus} CUs")
 
     ms_step = timed(lambda k: (attn(k), combine()), args.steps)
     # second and third regions: each kernel alone, back to back, events at the ends only

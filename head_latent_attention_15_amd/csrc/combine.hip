@@ -5,7 +5,10 @@
 // is recovered exactly by weighting each split with e^{lse_s - M} (M = max lse): the
 // softmax denominator is a sum over the tokens (qiita.com/joule "Attention 計算").
 //
-// One workgroup per (sequence, head); each thread owns 4 consecutive latent columns
+// One workgroup per (sequence, head), numbered sequence-fastest: consecutive workgroup ids
+// go to the 8 XCDs in turn, so (with B a multiple of 8) the workgroups of sequence b run on
+// XCD b % 8, the one whose attention workgroups wrote b's partials, and can find them in
+// that XCD's L2.  Each thread owns 4 consecutive latent columns
 // (one 16-byte load per split for fp32 partials, 8 bytes for bf16), the weights live in
 // LDS.  Deterministic: fixed summation order, no atomics.
 #include "device_common.h"
@@ -28,11 +31,11 @@ __device__ __forceinline__ f32x4_t load4(const bf16raw* p) {
 
 template <typename PT>
 __global__ __launch_bounds__(kCombineThreads) void splitk_combine_kernel(
-    const PT* __restrict__ o_part, const float* __restrict__ lse_part, int S, int d_c,
-    float* __restrict__ out, float* __restrict__ lse_out) {
+    const PT* __restrict__ o_part, const float* __restrict__ lse_part, int B, int H, int S,
+    int d_c, float* __restrict__ out, float* __restrict__ lse_out) {
   extern __shared__ float w_lds[];  // S weights
   __shared__ float red[kCombineThreads / 64];
-  const int bh = blockIdx.x;
+  const int bh = (blockIdx.x % B) * H + blockIdx.x / B;
   const int tid = threadIdx.x;
   const float* lse = lse_part + static_cast<int64_t>(bh) * S;
 
@@ -86,10 +89,10 @@ hipError_t launch_splitk_combine(const void* o_part, int part_bf16, const float*
   const size_t lds = static_cast<size_t>(S) * sizeof(float);
   if (part_bf16)
     hipLaunchKernelGGL(splitk_combine_kernel<bf16raw>, dim3(B * H), dim3(kCombineThreads), lds,
-                       st, static_cast<const bf16raw*>(o_part), lse_part, S, d_c, out, lse_out);
+                       st, static_cast<const bf16raw*>(o_part), lse_part, B, H, S, d_c, out, lse_out);
   else
     hipLaunchKernelGGL(splitk_combine_kernel<float>, dim3(B * H), dim3(kCombineThreads), lds, st,
-                       static_cast<const float*>(o_part), lse_part, S, d_c, out, lse_out);
+                       static_cast<const float*>(o_part), lse_part, B, H, S, d_c, out, lse_out);
   return hipGetLastError();
 }
 
