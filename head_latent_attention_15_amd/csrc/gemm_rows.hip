@@ -1,0 +1,253 @@
+// Weight-streaming GEMM for the projections around the attention, on bf16 MFMA:
+//   y[z][m][n] = sum_k x[z][m][k] * w[z][n][k]
+// with w in nn.Linear layout ([out, in], k contiguous): W^DQ, W^UQ, W^QR, W^DKV, W^KR
+// ("論文解説: DeepSeek-V2 …", "Low-Rank Key-Value Joint Compression" and the query
+// compression beside it), the per-head W^UV_i and W^O ("行列吸収トリック"; kasblo.com/?p=4663,
+// "V側は、小さな表現の加重和を先に求める").  M is the decode batch (a few tens of rows), so the
+// weights are the traffic: every weight byte is read once, from HBM straight into MFMA
+// B-operand registers (lane (g, r) takes w[n + r][k + 8 g .. + 7], 16 contiguous bytes).
+//
+// The activations x are small and shared by every workgroup; a workgroup stages them
+// through LDS in 128-wide k chunks as bf16, split as x = hi + lo (both bf16, lo the
+// rounding remainder) when x is fp32, so the products keep about 16 significant bits of x
+// and every product of a bf16 weight is exact in the fp32 accumulator.
+//
+// Work decomposition: 4 wavefronts, wave w owns TN column tiles of 16 (64 TN columns per
+// workgroup) and all four 16-row tiles of a 64-row block of x.  Long k ranges are split over
+// KS workgroups, which add their results into y with fp32 atomics (y is zeroed first), so
+// the sum order, and with it the last bits of y, can differ between runs.
+#include "device_common.h"
+#include "launchers.h"
+
+#include <algorithm>
+#include <type_traits>
+
+namespace mla {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+constexpr int KC = 128;                 // k per staged chunk (4 MFMA k-steps)
+constexpr int XROW = KC * 2 + 16;       // LDS bytes per staged row: bf16, padded (banks)
+constexpr int XPLANE = 64 * XROW;       // one plane (hi or lo) of 64 rows
+constexpr int GR_LDS = 2 * 2 * XPLANE;  // two chunk buffers x (hi, lo)
+
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+  return static_cast<unsigned>(f32_to_bf16(a)) | (static_cast<unsigned>(f32_to_bf16(b)) << 16);
+}
+
+template <typename XT, int TN>
+__global__ __launch_bounds__(256, 2) void gemm_rows_kernel(
+    const XT* __restrict__ x, int64_t ldx, int64_t sx, const bf16raw* __restrict__ w,
+    int64_t ldw, int64_t sw, float* __restrict__ y, int64_t ldy, int64_t sy, int M, int N,
+    int K, int KS, int kper, int atomic_out) {
+  constexpr bool SPLIT_X = std::is_same<XT, float>::value;  // fp32 x: hi + lo planes
+  __shared__ __attribute__((aligned(16))) char smem[GR_LDS];
+  lds_char_t* const lsm = (lds_char_t*)smem;
+
+  const int z = blockIdx.z / KS, ks = blockIdx.z % KS;
+  x += z * sx;
+  w += z * sw;
+  y += z * sy;
+  const int m0 = blockIdx.y * 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r = lane & 15;
+  const int n0 = blockIdx.x * 64 * TN + wv * 16 * TN;  // this wave's first column
+  const int kb = ks * kper;
+  const int nchunks = kper / KC;
+
+  // ---- staging of one 128-wide chunk of x: thread t converts row t / 4, columns
+  //      32 (t % 4) .. + 31 (rows past M are zero)
+  const int srow = tid >> 2, scol = (tid & 3) * 32;
+  const bool srow_ok = m0 + srow < M;
+  const XT* xsrc = x + static_cast<int64_t>(m0 + (srow_ok ? srow : 0)) * ldx + scol;
+  float xv[32];
+  auto stage_load = [&](int kc) {
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) {
+      if constexpr (SPLIT_X) {
+        const f32x4_t v = srow_ok ? *reinterpret_cast<const f32x4_t*>(xsrc + kc + i)
+                                  : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        xv[i] = v[0]; xv[i + 1] = v[1]; xv[i + 2] = v[2]; xv[i + 3] = v[3];
+      } else {
+        const uint2 v = srow_ok ? *reinterpret_cast<const uint2*>(xsrc + kc + i) : uint2{0u, 0u};
+        xv[i] = __uint_as_float(v.x << 16); xv[i + 1] = __uint_as_float(v.x & 0xffff0000u);
+        xv[i + 2] = __uint_as_float(v.y << 16); xv[i + 3] = __uint_as_float(v.y & 0xffff0000u);
+      }
+    }
+  };
+  auto stage_store = [&](int buf) {
+    lds_char_t* hi = lsm + buf * 2 * XPLANE + srow * XROW + scol * 2;
+#pragma unroll
+    for (int i = 0; i < 32; i += 8) {
+      u32x4_t h, l;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = xv[i + 2 * j], b = xv[i + 2 * j + 1];
+        h[j] = pack_bf16(a, b);
+        if constexpr (SPLIT_X) {
+          const float ah = __uint_as_float(h[j] << 16), bh = __uint_as_float(h[j] & 0xffff0000u);
+          l[j] = pack_bf16(a - ah, b - bh);
+        }
+      }
+      *(lds_u32x4_t*)(hi + 2 * i) = h;
+      if constexpr (SPLIT_X) *(lds_u32x4_t*)(hi + XPLANE + 2 * i) = l;
+    }
+  };
+
+  // ---- weight rows of this lane (clamped to N - 1; those columns are not stored)
+  const bf16raw* wrow[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int n = min(n0 + 16 * j + r, N - 1);
+    wrow[j] = w + static_cast<int64_t>(n) * ldw + kb + 8 * g;
+  }
+  const int nsteps = nchunks * 4;
+  auto w_frag = [&](int step, int j) {
+    return *reinterpret_cast<const bf16x8_t*>(wrow[j] + 32 * step);
+  };
+
+  f32x4_t acc[TN][4];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[j][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // W fragments of the next three k-steps in flight (ring of 4 k-steps)
+  bf16x8_t wf[4][TN];
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) wf[i][j] = i < nsteps ? w_frag(i, j) : bf16x8_t{};
+
+  stage_load(kb);
+  stage_store(0);
+  for (int c = 0; c < nchunks; ++c) {
+    __syncthreads();  // chunk c staged; the other buffer is free
+    const bool more = c + 1 < nchunks;
+    if (more) stage_load(kb + (c + 1) * KC);
+    const lds_char_t* xa = lsm + (c & 1) * 2 * XPLANE + r * XROW + g * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int step = 4 * c + i;
+      if (step + 3 < nsteps) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) wf[(i + 3) & 3][j] = w_frag(step + 3, j);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8_t ah = *(const lds_bf16x8_t*)(xa + mt * 16 * XROW + i * 64);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wf[i][j], acc[j][mt], 0, 0, 0);
+        if constexpr (SPLIT_X) {
+          const bf16x8_t al = *(const lds_bf16x8_t*)(xa + XPLANE + mt * 16 * XROW + i * 64);
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wf[i][j], acc[j][mt], 0, 0, 0);
+        }
+      }
+    }
+    if (more) stage_store((c + 1) & 1);
+  }
+
+  // ---- lane (g, r) of tile (j, mt) holds y[m0 + 16 mt + 4 g + i][n0 + 16 j + r]
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int n = n0 + 16 * j + r;
+    if (n >= N) continue;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 16 * mt + 4 * g + i;
+        if (m >= M) continue;
+        float* dst = y + static_cast<int64_t>(m) * ldy + n;
+        if (atomic_out) atomicAdd(dst, acc[j][mt][i]);
+        else *dst = acc[j][mt][i];
+      }
+  }
+}
+
+// zero y[z][m][n] for the atomic accumulation
+__global__ void zero_rows_kernel(float* __restrict__ y, int64_t ldy, int64_t sy, int M, int N,
+                                 int batch) {
+  const int64_t total = static_cast<int64_t>(batch) * M * N;
+  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t z = e / (static_cast<int64_t>(M) * N);
+    const int64_t rem = e % (static_cast<int64_t>(M) * N);
+    y[z * sy + (rem / N) * ldy + rem % N] = 0.f;
+  }
+}
+
+template <typename XT, int TN>
+hipError_t launch_t(const GemmArgs& g, int KS, hipStream_t s) {
+  const int kper = g.K / KS;
+  const int nb = (g.N + 64 * TN - 1) / (64 * TN), mb = (g.M + 63) / 64;
+  if (KS > 1) {
+    const int64_t total = static_cast<int64_t>(g.batch) * g.M * g.N;
+    const int blocks = static_cast<int>(std::min<int64_t>((total + 255) / 256, 4096));
+    hipLaunchKernelGGL(zero_rows_kernel, dim3(blocks), dim3(256), 0, s, static_cast<float*>(g.y),
+                       g.ldy, g.sy, g.M, g.N, g.batch);
+  }
+  hipLaunchKernelGGL((gemm_rows_kernel<XT, TN>), dim3(nb, mb, g.batch * KS), dim3(256), 0, s,
+                     static_cast<const XT*>(g.x), g.ldx, g.sx, static_cast<const bf16raw*>(g.w),
+                     g.ldw, g.sw, static_cast<float*>(g.y), g.ldy, g.sy, g.M, g.N, g.K, KS,
+                     kper, KS > 1 ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <typename XT>
+hipError_t launch_x(const GemmArgs& g, int TN, int KS, hipStream_t s) {
+  switch (TN) {
+    case 4: return launch_t<XT, 4>(g, KS, s);
+    case 2: return launch_t<XT, 2>(g, KS, s);
+    default: return launch_t<XT, 1>(g, KS, s);
+  }
+}
+
+}  // namespace
+
+bool gemm_rows_supported(const GemmArgs& g) {
+  return g.w_bf16 && g.w_nk && !g.y_bf16 && g.K % KC == 0 && g.K > 0 && g.M > 0 && g.N > 0 &&
+         g.batch > 0 && g.batch <= 65535 && (g.M + 63) / 64 <= 65535 &&
+         (reinterpret_cast<uintptr_t>(g.w) & 15) == 0 && (g.ldw % 8) == 0 && (g.sw % 8) == 0 &&
+         (reinterpret_cast<uintptr_t>(g.x) & 15) == 0 && (g.ldx % 8) == 0 && (g.sx % 8) == 0;
+}
+
+// Tile width and k split: the widest tile (fewer re-reads of x) whose grid, with the
+// smallest k split that divides the chunk count, still fills about 3/4 of the 256 CUs.
+void gemm_rows_plan(const GemmArgs& g, int* tn, int* ks) {
+  const int chunks = g.K / KC;
+  const int64_t mb = (g.M + 63) / 64;
+  for (int t : {4, 2, 1}) {
+    if (t > 1 && 64 * t > g.N) continue;
+    const int64_t nb = (g.N + 64 * t - 1) / (64 * t);
+    for (int d = 1; d <= chunks; ++d) {
+      if (chunks % d != 0 || nb * mb * g.batch * d < 192) continue;
+      if (static_cast<int64_t>(g.batch) * d > 65535) break;
+      *tn = t;
+      *ks = d;
+      return;
+    }
+  }
+  *tn = 1;
+  *ks = 1;
+  for (int d = chunks; d >= 1; --d)
+    if (chunks % d == 0 && static_cast<int64_t>(g.batch) * d <= 65535) { *ks = d; break; }
+}
+
+hipError_t launch_gemm_rows(const GemmArgs& g, hipStream_t s) {
+  int tn = 1, ks = 1;
+  gemm_rows_plan(g, &tn, &ks);
+  return g.x_bf16 ? launch_x<bf16raw>(g, tn, ks, s) : launch_x<float>(g, tn, ks, s);
+}
+
+}  // namespace mla

@@ -43,6 +43,11 @@ struct GemmArgs {
   int M, N, K, batch;
 };
 hipError_t launch_gemm_small(const GemmArgs& g, hipStream_t s);
+// Same product on bf16 MFMA for bf16 nn.Linear-layout weights (w_nk), fp32 y and K a
+// multiple of 128 (gemm_rows_supported); split-K results are added with fp32 atomics.
+bool gemm_rows_supported(const GemmArgs& g);
+void gemm_rows_plan(const GemmArgs& g, int* tn, int* ks);
+hipError_t launch_gemm_rows(const GemmArgs& g, hipStream_t s);
 
 hipError_t launch_rope_rows(const float* x, int64_t rows, int rows_per_seq, int d_R,
                             const int32_t* seq_lens, int pos_offset, float base, void* out,

@@ -58,6 +58,12 @@ mla_status_t check_paged_shape(const mla_paged_shape_t* shp) {
   return MLA_OK;
 }
 
+// Projections: bf16 MFMA weight streaming where it applies, the fp32 tile GEMM otherwise
+// (fp32 weights, bf16 output, k not a multiple of 128, weights stored [in, out]).
+hipError_t gemm(const mla::GemmArgs& g, hipStream_t s) {
+  return mla::gemm_rows_supported(g) ? mla::launch_gemm_rows(g, s) : mla::launch_gemm_small(g, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -279,7 +285,7 @@ mla_status_t mla_out_proj(const float* o_lat, const void* w_uv, const void* w_o,
   g.w_nk = true;
   g.y = o_heads; g.ldy = static_cast<int64_t>(H) * d_h; g.sy = d_h; g.y_bf16 = 0;
   g.M = B; g.N = d_h; g.K = d_c; g.batch = H;
-  mla_status_t st = launched(mla::launch_gemm_small(g, s), "W^UV GEMM");
+  mla_status_t st = launched(gemm(g, s), "W^UV GEMM");
   if (st != MLA_OK || !w_o) return st;
   mla::GemmArgs o;
   o.x = o_heads; o.ldx = static_cast<int64_t>(H) * d_h; o.sx = 0; o.x_bf16 = 0;
@@ -287,7 +293,7 @@ mla_status_t mla_out_proj(const float* o_lat, const void* w_uv, const void* w_o,
   o.w_nk = true;
   o.y = u; o.ldy = d_model; o.sy = 0; o.y_bf16 = 0;
   o.M = B; o.N = d_model; o.K = H * d_h; o.batch = 1;
-  return launched(mla::launch_gemm_small(o, s), "W^O GEMM");
+  return launched(gemm(o, s), "W^O GEMM");
 }
 
 mla_status_t mla_linear(const void* x, mla_dtype_t x_dtype, const void* w,
@@ -303,7 +309,7 @@ mla_status_t mla_linear(const void* x, mla_dtype_t x_dtype, const void* w,
   g.w = w; g.ldw = K; g.sw = 0; g.w_bf16 = w_dtype == MLA_BF16; g.w_nk = true;
   g.y = y; g.ldy = N; g.sy = 0; g.y_bf16 = 0;
   g.M = M; g.N = N; g.K = K; g.batch = 1;
-  return launched(mla::launch_gemm_small(g, as_stream(stream)), "linear GEMM");
+  return launched(gemm(g, as_stream(stream)), "linear GEMM");
 }
 
 mla_status_t mla_validate_indices(const int32_t* block_table, const int32_t* seq_lens,

@@ -484,3 +484,45 @@ def test_linear_and_outproj_against_matmul(mla):
         ref = W.to_f64(x) @ W.to_f64(w).T
         m, _ = errors(host64(y), ref)
         assert m <= 1e-5 * math.sqrt(K) * 4, (M, N, K, m)
+
+
+def test_weight_streaming_gemm_paths(mla):
+    """The bf16-weight MFMA GEMM (weights [out, in], k a multiple of 128) against numpy
+    fp64 matmul over its tile widths, k splits (atomic accumulation), ragged rows and
+    columns, bf16 activations and more than 64 rows.  x is fp32 (split hi + lo) or bf16."""
+    g = torch.Generator().manual_seed(31)
+    for (M, N, K, xdt) in [(64, 5120, 16384, torch.float32),   # wide tiles, 16-way k split
+                           (50, 1000, 1536, torch.float32),    # narrow tiles, ragged N
+                           (100, 300, 256, torch.bfloat16),    # two row blocks, bf16 x
+                           (3, 16, 128, torch.float32)]:       # one chunk
+        say(f"weight-streaming GEMM M={M} N={N} K={K} x={xdt}")
+        x = torch.randn(M, K, generator=g).to(xdt)
+        w = torch.randn(N, K, generator=g).to(torch.bfloat16)
+        y = torch.empty(M, N, device="cuda")
+        mla.mla_linear(dev(x), dev(w), y)
+        torch.cuda.synchronize()
+        ref = W.to_f64(x) @ W.to_f64(w).T
+        m, r = errors(host64(y), ref)
+        # x keeps ~16 significant bits (hi + lo), products are exact, sums are fp32
+        assert m <= 2e-5 * float(np.abs(ref).max()) + 1e-4, (M, N, K, m)
+        assert r <= 1e-5, (M, N, K, r)
+
+
+def test_out_proj_full_size(mla):
+    """W^UV per head (batched, strided) then W^O at the DeepSeek-V2 sizes, fp64 reference."""
+    g = torch.Generator().manual_seed(32)
+    B, H, d_h, d_c, d_model = 64, 128, 128, 512, 5120
+    say("out_proj full size")
+    o_lat = torch.randn(B, H, d_c, generator=g)
+    w_uv = (torch.randn(H * d_h, d_c, generator=g) / math.sqrt(d_c)).to(torch.bfloat16)
+    w_o = (torch.randn(d_model, H * d_h, generator=g) / math.sqrt(H * d_h)).to(torch.bfloat16)
+    o_heads = torch.empty(B, H, d_h, device="cuda")
+    u = torch.empty(B, d_model, device="cuda")
+    mla.mla_out_proj(dev(o_lat), dev(w_uv), dev(w_o), o_heads, u)
+    torch.cuda.synchronize()
+    ref_heads = np.stack([W.to_f64(o_lat[:, i]) @ W.to_f64(w_uv[i * d_h:(i + 1) * d_h]).T
+                          for i in range(H)], axis=1)
+    assert_fp32(host64(o_heads), ref_heads, 1e-4, "o_heads")
+    ref_u = ref_heads.reshape(B, H * d_h) @ W.to_f64(w_o).T
+    m, r = errors(host64(u), ref_u)
+    assert r <= 1e-5 and m <= 1e-4, (m, r)
