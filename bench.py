@@ -97,6 +97,97 @@ def cpu_baseline(inp, n_seq: int, min_seconds: float = 10.0):
                       f"latent attention incl. the paged gather, {dt:.1f} s)"}
 
 
+def layer_rows(mla, W, torch, oracle_seqs: int):
+    """Every step of the path on the full decode layer (DeepSeek-V2 sizes, B=64, 2048 cached
+    tokens + the new one): each library call timed alone (20 back-to-back calls after a
+    0.3 s warmup of the whole chain), its algorithmic bytes (weights, cache rows,
+    activations in and out at their stored dtypes) and its fraction of the 8 TB/s HBM
+    roofline (every step is HBM-bound at this batch); then the whole chain, and the fp64
+    oracle's layer on a few of the sequences."""
+    x = W.layer_b64_t2k()
+    s = x["shape"]
+    B, H, d_h, d_c, d_R, d, d_cq = s.B, s.H, s.d_h, s.d_c, s.d_R, x["d"], x["d_cq"]
+    cu = lambda t: t.to("cuda")
+    w = {k: cu(v) for k, v in x["weights"].items()}
+    h, cache, bt, before = cu(x["h"]), cu(x["cache"]), cu(x["block_table"]), cu(x["seq_lens_before"])
+    f32 = dict(device="cuda", dtype=torch.float32)
+    c_q, q_c, q_r = torch.empty(B, d_cq, **f32), torch.empty(B, H * d_h, **f32), torch.empty(B, H * d_R, **f32)
+    c_kv, k_r = torch.empty(B, d_c, **f32), torch.empty(B, d_R, **f32)
+    seq_lens = before + 1
+    q_lat = torch.empty(B, H, d_c, device="cuda", dtype=torch.bfloat16)
+    q_pe = torch.empty(B, H, d_R, device="cuda", dtype=torch.bfloat16)
+    S = mla.mla_suggest_num_splits(B, int(seq_lens.max()), 0, 64, 256)
+    ws = torch.empty(max(1, mla.mla_decode_workspace_bytes(B, H, d_c, S)), dtype=torch.uint8, device="cuda")
+    o_lat, o_heads, u = torch.empty(B, H, d_c, **f32), torch.empty(B, H, d_h, **f32), torch.empty(B, d, **f32)
+    nb = lambda t: t.numel() * t.element_size()
+    tokens = int(seq_lens.sum())
+    rows = [
+        ("7 mla_linear (W^DQ, W^UQ, W^QR, W^DKV, W^KR)",
+         [mla.bind(mla.mla_linear, h, w["w_dq"], c_q), mla.bind(mla.mla_linear, c_q, w["w_uq"], q_c),
+          mla.bind(mla.mla_linear, c_q, w["w_qr"], q_r), mla.bind(mla.mla_linear, h, w["w_dkv"], c_kv),
+          mla.bind(mla.mla_linear, h, w["w_kr"], k_r)],
+         sum(nb(w[k]) for k in ("w_dq", "w_uq", "w_qr", "w_dkv", "w_kr")) + 3 * nb(h) + 2 * nb(c_q)
+         + nb(c_q) + nb(q_c) + nb(q_r) + nb(c_kv) + nb(k_r)),
+        ("2 mla_kv_append", [mla.bind(mla.mla_kv_append, c_kv.view(B, 1, d_c), k_r.view(B, 1, d_R),
+                                      before, bt, cache, x["rope_base"])],
+         nb(c_kv) + nb(k_r) + B * (d_c + d_R) * 2),
+        ("1 mla_absorb_q", [mla.bind(mla.mla_absorb_q, q_c.view(B, H, d_h), w["w_uk"], q_r.view(B, H, d_R),
+                                     seq_lens, x["rope_base"], q_lat, q_pe)],
+         nb(w["w_uk"]) + nb(q_c) + nb(q_r) + nb(q_lat) + nb(q_pe)),
+        (f"3+4 mla_decode (attention + combine, {S} splits)",
+         [mla.bind(mla.mla_decode, q_lat, q_pe, cache, bt, seq_lens, x["scale"], S, ws, o_lat)],
+         tokens * (d_c + d_R) * 2 + nb(q_lat) + nb(q_pe) + nb(o_lat)),
+        ("5 mla_out_proj W^UV", [mla.bind(mla.mla_out_proj, o_lat, w["w_uv"], None, o_heads)],
+         nb(w["w_uv"]) + nb(o_lat) + nb(o_heads)),
+        ("6 W^O (mla_linear on the concatenated heads)",
+         [mla.bind(mla.mla_linear, o_heads.view(B, H * d_h), w["w_o"], u)],
+         nb(w["w_o"]) + nb(o_heads) + nb(u)),
+    ]
+    chain = [c for _, calls, _ in rows for c in calls]
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.3:
+        for c in chain:
+            c()
+        torch.cuda.synchronize()
+
+    def timed(fn, n=20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3  # us
+
+    out = {}
+    total_bytes = 0
+    for name, calls, byts in rows:
+        us = timed(lambda: [c() for c in calls])
+        gbps = byts / us / 1e3
+        out[name] = {"us": round(us, 2), "bytes_algorithmic": int(byts), "GBps": round(gbps, 1),
+                     "roofline_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+        total_bytes += byts
+    chain_us = timed(lambda: [c() for c in chain])
+    res = {"workload": "layer_b64_t2k (d=5120, H=128, d_h=128, d_c=512, d_c^Q=1536, d_R=64, "
+                       "B=64, 2048 cached tokens + 1, bf16 weights and cache)",
+           "steps": out, "chain_us": round(chain_us, 2), "chain_bytes_algorithmic": int(total_bytes),
+           "chain_GBps": round(total_bytes / chain_us / 1e3, 1),
+           "chain_roofline_frac": round(total_bytes / chain_us / 1e3 / HBM_PEAK_GBPS, 4),
+           "sequences_per_s": round(B / (chain_us * 1e-6), 1)}
+    if oracle_seqs > 0:
+        import oracle
+        wf = {k: W.to_f64(v) for k, v in x["weights"].items()}
+        hf, cf = W.to_f64(x["h"]), W.to_f64(x["cache"])
+        t0 = time.perf_counter()
+        oracle.decode_layer(hf, wf, cf, x["block_table"].numpy(), x["seq_lens_before"].numpy(), d_h, d_R,
+                            x["rope_base"], x["scale"], batch_index=list(range(oracle_seqs)))
+        dt = time.perf_counter() - t0
+        res["cpu_oracle"] = {"sequences_per_s": round(oracle_seqs / dt, 3), "kind": "oracle",
+                             "sample": f"{oracle_seqs} of 64 sequences (fp64 expanded layer, {dt:.1f} s)"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,6 +198,7 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="split count (0: library suggestion)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32)
+    ap.add_argument("--no-layer", action="store_true", help="skip the per-step layer measurement")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for --pmc runs)")
     args = ap.parse_args()
@@ -249,6 +341,9 @@ def main():
     if not args.no_cpu_baseline:
         log(f"timing the fp64 oracle on {args.cpu_seqs} sequences")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)
+    if not args.no_layer:
+        log("timing every step of the path on the full decode layer")
+        result["layer_b64_t2k"] = layer_rows(mla, W, torch, 0 if args.no_cpu_baseline else 4)
     print(json.dumps(result), flush=True)
 
 
