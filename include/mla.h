@@ -26,7 +26,10 @@
  *   - Block-table entries and seq_lens are read on the device and are NOT bounds-checked
  *     there: out-of-range values are undefined behaviour.  mla_validate_indices checks
  *     them on the device beforehand.
- *   - Results are deterministic for fixed inputs and arguments (no floating-point atomics).
+ *   - Results are deterministic for fixed inputs and arguments, except the projections
+ *     (mla_linear, mla_out_proj) with bf16 weights: their long reductions are split over
+ *     workgroups that add into the fp32 output atomically, so the last bits of y / u /
+ *     o_heads can differ between runs.
  *
  * Paged latent cache: kv_cache[num_pages][page_size][d_latent + d_rope]; a row is
  * [c^KV (d_latent) | RoPE(k^R) (d_rope)].  Token j (0-based) of sequence b lives at
@@ -180,6 +183,7 @@ mla_status_t mla_decode(const void* q_lat, const void* q_pe, const void* kv_cach
  * (kasblo "V側は…": up-project after the weighted sum; qiita "Attention 計算" for u.)
  *   o_lat [B][H][d_c] fp32;  w_uv [H*d_h][d_c] w_dtype;  w_o [d_model][H*d_h] w_dtype or NULL
  *   o_heads [B][H][d_h] fp32 (always written);  u [B][d_model] fp32 (NULL iff w_o NULL)
+ * Both products use the GEMM paths of mla_linear (bf16 MFMA for bf16 weights).
  * Errors: NULL, SHAPE, UNSUPPORTED (dtype). */
 mla_status_t mla_out_proj(const float* o_lat, const void* w_uv, const void* w_o, int32_t B,
                           int32_t H, int32_t d_c, int32_t d_h, int32_t d_model,
@@ -189,6 +193,9 @@ mla_status_t mla_out_proj(const float* o_lat, const void* w_uv, const void* w_o,
  * fp32 output.  Used for the projections c^Q = W^DQ h, q^C = W^UQ c^Q, q^R = W^QR c^Q,
  * c^KV = W^DKV h, k^R = W^KR h (qiita "Query の圧縮", "RoPE の扱い").
  *   x [M][K] x_dtype;  w [N][K] w_dtype;  y [M][N] fp32.
+ * With bf16 w, K a multiple of 128 and 16-byte aligned x, w: bf16 MFMA with x carried as
+ * two bf16 terms (about 16 significant bits), split-K partial sums added atomically (y is
+ * overwritten, not accumulated into); otherwise an fp32 VALU GEMM.
  * Errors: NULL, SHAPE (sizes < 1), UNSUPPORTED (dtype). */
 mla_status_t mla_linear(const void* x, mla_dtype_t x_dtype, const void* w,
                         mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K, float* y,
