@@ -84,8 +84,75 @@ __global__ __launch_bounds__(kCombineThreads) void splitk_combine_kernel(
   if (tid == 0 && lse_out != nullptr) lse_out[bh] = den > 0.f ? msafe + logf(den) : -INFINITY;
 }
 
+// d_c = 512, at most 64 splits: one wavefront per (sequence, head), lane l owns columns
+// 8 l .. 8 l + 7 (one 16-byte load per split for bf16 partials), lane s holds split s's lse
+// and weight; the weights reach every lane by shuffle, the S loads are issued back to back.
+__device__ __forceinline__ void load8(const bf16raw* p, float (&v)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
+  const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+}
+
+template <typename PT>
+__global__ __launch_bounds__(256) void combine512_kernel(
+    const PT* __restrict__ o_part, const float* __restrict__ lse_part, int B, int H, int S,
+    float* __restrict__ out, float* __restrict__ lse_out) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= B * H) return;
+  const int bh = (item % B) * H + item / B;  // sequence-fastest, as in splitk_combine_kernel
+  const float x = lane < S ? lse_part[static_cast<int64_t>(bh) * S + lane] : -INFINITY;
+  const float m = wave_max(x);
+  const float msafe = (m == -INFINITY) ? 0.f : m;
+  const float wl = (x == -INFINITY) ? 0.f : expf(x - msafe);
+  const float den = wave_sum(wl);
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const PT* base = o_part + static_cast<int64_t>(bh) * S * 512 + 8 * lane;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float v[8][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + j < S) load8(base + static_cast<int64_t>(s0 + j) * 512, v[j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (s0 + j >= S) break;
+      const float w = __shfl(wl, s0 + j, 64);
+      if (w != 0.f) {  // an empty split contributes nothing (and no NaN)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[j][i], acc[i]);
+      }
+    }
+  }
+  float* dst = out + static_cast<int64_t>(bh) * 512 + 8 * lane;
+  *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+  *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+  if (lane == 0 && lse_out != nullptr) lse_out[bh] = den > 0.f ? msafe + logf(den) : -INFINITY;
+}
+
 hipError_t launch_splitk_combine(const void* o_part, int part_bf16, const float* lse_part, int B,
                                  int H, int S, int d_c, float* out, float* lse_out, hipStream_t st) {
+  const bool aligned = ((reinterpret_cast<uintptr_t>(o_part) | reinterpret_cast<uintptr_t>(out)) & 15) == 0;
+  if (d_c == 512 && S <= 64 && aligned) {
+    const int items = B * H;
+    if (part_bf16)
+      hipLaunchKernelGGL(combine512_kernel<bf16raw>, dim3((items + 3) / 4), dim3(256), 0, st,
+                         static_cast<const bf16raw*>(o_part), lse_part, B, H, S, out, lse_out);
+    else
+      hipLaunchKernelGGL(combine512_kernel<float>, dim3((items + 3) / 4), dim3(256), 0, st,
+                         static_cast<const float*>(o_part), lse_part, B, H, S, out, lse_out);
+    return hipGetLastError();
+  }
   const size_t lds = static_cast<size_t>(S) * sizeof(float);
   if (part_bf16)
     hipLaunchKernelGGL(splitk_combine_kernel<bf16raw>, dim3(B * H), dim3(kCombineThreads), lds,
