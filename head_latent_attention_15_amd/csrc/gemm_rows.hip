@@ -72,11 +72,12 @@ __global__ __launch_bounds__(256, 2) void gemm_rows_kernel(
 #pragma unroll
     for (int i = 0; i < 32; i += 4) {
       if constexpr (SPLIT_X) {
-        const f32x4_t v = srow_ok ? *reinterpret_cast<const f32x4_t*>(xsrc + kc + i)
-                                  : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        f32x4_t v = *reinterpret_cast<const f32x4_t*>(xsrc + kc + i);
+        if (!srow_ok) v = f32x4_t{0.f, 0.f, 0.f, 0.f};
         xv[i] = v[0]; xv[i + 1] = v[1]; xv[i + 2] = v[2]; xv[i + 3] = v[3];
       } else {
-        const uint2 v = srow_ok ? *reinterpret_cast<const uint2*>(xsrc + kc + i) : uint2{0u, 0u};
+        uint2 v = *reinterpret_cast<const uint2*>(xsrc + kc + i);
+        if (!srow_ok) v = uint2{0u, 0u};
         xv[i] = __uint_as_float(v.x << 16); xv[i + 1] = __uint_as_float(v.x & 0xffff0000u);
         xv[i + 2] = __uint_as_float(v.y << 16); xv[i + 3] = __uint_as_float(v.y & 0xffff0000u);
       }
@@ -124,22 +125,20 @@ __global__ __launch_bounds__(256, 2) void gemm_rows_kernel(
 #pragma unroll
   for (int i = 0; i < 3; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) wf[i][j] = i < nsteps ? w_frag(i, j) : bf16x8_t{};
+    for (int j = 0; j < TN; ++j) wf[i][j] = w_frag(min(i, nsteps - 1), j);
 
   stage_load(kb);
   stage_store(0);
   for (int c = 0; c < nchunks; ++c) {
     __syncthreads();  // chunk c staged; the other buffer is free
     const bool more = c + 1 < nchunks;
-    if (more) stage_load(kb + (c + 1) * KC);
+    stage_load(kb + min(c + 1, nchunks - 1) * KC);
     const lds_char_t* xa = lsm + (c & 1) * 2 * XPLANE + r * XROW + g * 16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int step = 4 * c + i;
-      if (step + 3 < nsteps) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) wf[(i + 3) & 3][j] = w_frag(step + 3, j);
-      }
+      for (int j = 0; j < TN; ++j) wf[(i + 3) & 3][j] = w_frag(min(step + 3, nsteps - 1), j);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const bf16x8_t ah = *(const lds_bf16x8_t*)(xa + mt * 16 * XROW + i * 64);
@@ -153,6 +152,7 @@ __global__ __launch_bounds__(256, 2) void gemm_rows_kernel(
             acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wf[i][j], acc[j][mt], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (more) stage_store((c + 1) & 1);
   }
@@ -222,26 +222,23 @@ bool gemm_rows_supported(const GemmArgs& g) {
          (reinterpret_cast<uintptr_t>(g.x) & 15) == 0 && (g.ldx % 8) == 0 && (g.sx % 8) == 0;
 }
 
-// Tile width and k split: the widest tile (fewer re-reads of x) whose grid, with the
-// smallest k split that divides the chunk count, still fills about 3/4 of the 256 CUs.
+// Tile width and k split.  Wide tiles (fewer re-reads of x per weight byte) pay off when
+// both N and the k range are long; otherwise narrower tiles spread better.  The k split is
+// the smallest divisor of the chunk count whose grid fills about 3/4 of the 256 CUs.
+// (Chosen from measurements at the DeepSeek-V2 projection shapes with M = 64.)
 void gemm_rows_plan(const GemmArgs& g, int* tn, int* ks) {
   const int chunks = g.K / KC;
   const int64_t mb = (g.M + 63) / 64;
-  for (int t : {4, 2, 1}) {
-    if (t > 1 && 64 * t > g.N) continue;
-    const int64_t nb = (g.N + 64 * t - 1) / (64 * t);
-    for (int d = 1; d <= chunks; ++d) {
-      if (chunks % d != 0 || nb * mb * g.batch * d < 192) continue;
-      if (static_cast<int64_t>(g.batch) * d > 65535) break;
-      *tn = t;
-      *ks = d;
-      return;
-    }
-  }
-  *tn = 1;
+  const int t = (g.N >= 4096 && g.K >= 8192) ? 4 : (g.N >= 4096 ? 2 : 1);
+  const int64_t nb = (g.N + 64 * t - 1) / (64 * t);
+  *tn = t;
   *ks = 1;
-  for (int d = chunks; d >= 1; --d)
-    if (chunks % d == 0 && static_cast<int64_t>(g.batch) * d <= 65535) { *ks = d; break; }
+  for (int d = 1; d <= chunks; ++d) {
+    if (chunks % d != 0) continue;
+    if (static_cast<int64_t>(g.batch) * d > 65535) break;
+    *ks = d;
+    if (nb * mb * g.batch * d >= 192) break;
+  }
 }
 
 hipError_t launch_gemm_rows(const GemmArgs& g, hipStream_t s) {
