@@ -49,6 +49,12 @@ bool gemm_rows_supported(const GemmArgs& g);
 void gemm_rows_plan(const GemmArgs& g, int* tn, int* ks);
 hipError_t launch_gemm_rows(const GemmArgs& g, hipStream_t s);
 
+// Query absorption q~_i = W^UK_i^T q^C_i on bf16 MFMA (bf16 W^UK, bf16 q~, d_h = 128).
+bool absorb_mfma_supported(int B, int H, int d_h, int d_c, const void* q_c, const void* w_uk,
+                           const void* q_lat);
+hipError_t launch_absorb_mfma(const float* q_c, const void* w_uk, void* q_lat, int B, int H,
+                              int d_c, hipStream_t s);
+
 hipError_t launch_rope_rows(const float* x, int64_t rows, int rows_per_seq, int d_R,
                             const int32_t* seq_lens, int pos_offset, float base, void* out,
                             int out_bf16, hipStream_t s);

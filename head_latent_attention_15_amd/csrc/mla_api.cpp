@@ -243,7 +243,11 @@ mla_status_t mla_absorb_q(const float* q_c, const void* w_uk, const float* q_r,
   g.w_nk = false;
   g.y = q_lat; g.ldy = static_cast<int64_t>(H) * d_c; g.sy = d_c; g.y_bf16 = out_dtype == MLA_BF16;
   g.M = B; g.N = d_c; g.K = d_h; g.batch = H;
-  mla_status_t st = launched(mla::launch_gemm_small(g, s), "absorb GEMM");
+  const bool mfma = w_dtype == MLA_BF16 && out_dtype == MLA_BF16 &&
+                    mla::absorb_mfma_supported(B, H, d_h, d_c, q_c, w_uk, q_lat);
+  mla_status_t st = launched(mfma ? mla::launch_absorb_mfma(q_c, w_uk, q_lat, B, H, d_c, s)
+                                  : mla::launch_gemm_small(g, s),
+                             "absorb GEMM");
   if (st != MLA_OK || !q_r) return st;
   return launched(mla::launch_rope_rows(q_r, static_cast<int64_t>(B) * H, H, d_R, seq_lens, -1,
                                         rope_base, q_pe, out_dtype == MLA_BF16, s),

@@ -526,3 +526,23 @@ def test_out_proj_full_size(mla):
     ref_u = ref_heads.reshape(B, H * d_h) @ W.to_f64(w_o).T
     m, r = errors(host64(u), ref_u)
     assert r <= 1e-5 and m <= 1e-4, (m, r)
+
+
+def test_absorb_mfma_against_oracle(mla):
+    """Query absorption on the MFMA path (bf16 W^UK, bf16 q~, d_h = 128) against the
+    oracle's absorption in fp64: ragged batch (B = 70: a full and a partial 64-row block),
+    several 128-column blocks; q~ is rounded once to bf16."""
+    g = torch.Generator().manual_seed(33)
+    B, H, d_h, d_c = 70, 6, 128, 512
+    say("absorb mfma")
+    q_c = torch.randn(B, H, d_h, generator=g)
+    w_uk = (torch.randn(H * d_h, d_c, generator=g) / math.sqrt(d_h)).to(torch.bfloat16)
+    q_lat = torch.empty(B, H, d_c, device="cuda", dtype=torch.bfloat16)
+    seq_lens = torch.full((B,), 5, dtype=torch.int32, device="cuda")
+    mla.mla_absorb_q(dev(q_c), dev(w_uk), None, seq_lens, 10000.0, q_lat, None)
+    torch.cuda.synchronize()
+    ref = np.stack([oracle.absorb_query(W.to_f64(q_c[b]), W.to_f64(w_uk)) for b in range(B)])
+    assert_bf16(host64(q_lat), ref, "q~")
+    # the bf16 output is the only rounding: within half a bf16 ulp of the fp64 value
+    m, _ = errors(host64(q_lat), ref)
+    assert m <= float(np.abs(ref).max()) * 2.0 ** -8, m
