@@ -480,6 +480,40 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = __builtin_bit_cast(bf16x8_t, r[kk]);
   };
+  // With eight wavefronts (five copies per tile and wave) the copies of the second tile
+  // join the same block, issued after the query loads, and the block waits for everything
+  // but them: two tiles are then in flight while the queries arrive.  A one-tile split
+  // copies its tile again into the unused second buffer, so the wait counts stay alike.
+  auto load_query_tile1 = [&]() {
+    const bf16raw* qrow = q_lat + (static_cast<int64_t>(b) * H + h0 + r16) * DC + 8 * g;
+    const bf16raw* prow = q_pe + (static_cast<int64_t>(b) * H + h0 + r16) * DR + 8 * g;
+    const int tb1 = ntiles > 1 ? j0 + TILE : j0;
+    const unsigned last1 = static_cast<unsigned>(j1 - 1 - tb1);
+    const uint64_t b64 = reinterpret_cast<uint64_t>(tile_base(tb1));
+    const uint32_t blo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b64));
+    const uint32_t bhi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b64 >> 32));
+    const void* base1 = reinterpret_cast<const void*>((static_cast<uint64_t>(bhi) << 32) | blo);
+    uint32_t vo[5], la[5];  // called with COPIES == 5 only
+#pragma unroll
+    for (int c = 0; c < 5; ++c) {
+      vo[c] = copy_voff(copy_index(c), lane, last1);
+      la[c] = __builtin_amdgcn_readfirstlane(smem_lds + TILE_BYTES + copy_index(c) * 64 * 16);
+    }
+    i32x4_t r[KSTEPS];
+    asm volatile("global_load_dwordx4 %0, %18, off\n\tglobal_load_dwordx4 %1, %18, off offset:64\n\tglobal_load_dwordx4 %2, %18, off offset:128\n\tglobal_load_dwordx4 %3, %18, off offset:192\n\tglobal_load_dwordx4 %4, %18, off offset:256\n\tglobal_load_dwordx4 %5, %18, off offset:320\n\tglobal_load_dwordx4 %6, %18, off offset:384\n\tglobal_load_dwordx4 %7, %18, off offset:448\n\tglobal_load_dwordx4 %8, %18, off offset:512\n\tglobal_load_dwordx4 %9, %18, off offset:576\n\tglobal_load_dwordx4 %10, %18, off offset:640\n\tglobal_load_dwordx4 %11, %18, off offset:704\n\tglobal_load_dwordx4 %12, %18, off offset:768\n\tglobal_load_dwordx4 %13, %18, off offset:832\n\tglobal_load_dwordx4 %14, %18, off offset:896\n\tglobal_load_dwordx4 %15, %18, off offset:960\n\tglobal_load_dwordx4 %16, %19, off\n\tglobal_load_dwordx4 %17, %19, off offset:64\n\t"
+                 "s_mov_b32 m0, %25\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %20, %30\n\t"
+                 "s_mov_b32 m0, %26\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %21, %30\n\t"
+                 "s_mov_b32 m0, %27\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %22, %30\n\t"
+                 "s_mov_b32 m0, %28\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %23, %30\n\t"
+                 "s_mov_b32 m0, %29\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %24, %30\n\t"
+                 "s_waitcnt vmcnt(5)"
+                 : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15]), "=&v"(r[16]), "=&v"(r[17])
+                 : "v"(qrow), "v"(prow), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "v"(vo[4]),
+                   "s"(la[0]), "s"(la[1]), "s"(la[2]), "s"(la[3]), "s"(la[4]), "s"(base1)
+                 : "memory", "m0");
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = __builtin_bit_cast(bf16x8_t, r[kk]);
+  };
   issue_tile(j0, 0);
   for (int e = tid; e < TILE_WAVE_COPIES * 64; e += NT) {
     const unsigned chunk = static_cast<unsigned>(e);
@@ -489,8 +523,12 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   for (int e = tid; e * P < j1 - j0; e += NT)  // the pages this split reads
     ((__attribute__((address_space(3))) int32_t*)(lsm + PAGE_TABLE))[e] = bt_row[(j0 >> log2P) + e];
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // table written before barrier 0
-  load_query();
-  if (ntiles > 1) issue_tile(j0 + TILE, 1);
+  if constexpr (COPIES == 5) {
+    load_query_tile1();
+  } else {
+    load_query();
+    if (ntiles > 1) issue_tile(j0 + TILE, 1);
+  }
   // Waves 0 .. NW/2-1 (group 0) take each tile as scores then PV; waves NW/2 .. NW-1
   // (group 1) run half a tile behind, as PV of the previous tile then scores.  A SIMD holds
   // one wave of each group, so while one scores (K reads, softmax arithmetic) the other feeds
