@@ -29,8 +29,12 @@ constexpr int AB_W = 128 * AB_ROW;         // W^UK_i^T block: 128 columns c
 constexpr int AB_X = 64 * AB_ROW;          // one plane of q^C_i: 64 rows b
 constexpr int AB_LDS = AB_W + 2 * AB_X;
 
+// two floats to bf16 (round to nearest even) in one v_cvt_pk_bf16_f32, a in the low half;
+// branch-free, so the loops around it keep exact memory wait counts
 __device__ __forceinline__ unsigned pack2(float a, float b) {
-  return static_cast<unsigned>(f32_to_bf16(a)) | (static_cast<unsigned>(f32_to_bf16(b)) << 16);
+  typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 __global__ __launch_bounds__(256) void absorb_kernel(const float* __restrict__ q_c,

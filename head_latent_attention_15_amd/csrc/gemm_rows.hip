@@ -15,7 +15,10 @@
 // Work decomposition: 4 wavefronts, wave w owns TN column tiles of 16 (64 TN columns per
 // workgroup) and all four 16-row tiles of a 64-row block of x.  Long k ranges are split over
 // KS workgroups, which add their results into y with fp32 atomics (y is zeroed first), so
-// the sum order, and with it the last bits of y, can differ between runs.
+// the sum order, and with it the last bits of y, can differ between runs.  Each wave keeps
+// the weight fragments of the next R - 1 k-steps in flight: at these sizes the loaded HBM
+// latency is several microseconds, and the bytes outstanding across the chip, not the
+// access pattern, set the rate.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -37,11 +40,15 @@ constexpr int XROW = KC * 2 + 16;       // LDS bytes per staged row: bf16, padde
 constexpr int XPLANE = 64 * XROW;       // one plane (hi or lo) of 64 rows
 constexpr int GR_LDS = 2 * 2 * XPLANE;  // two chunk buffers x (hi, lo)
 
+// two floats to bf16 (round to nearest even) in one v_cvt_pk_bf16_f32, a in the low half;
+// branch-free, so the loops around it keep exact memory wait counts
 __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
-  return static_cast<unsigned>(f32_to_bf16(a)) | (static_cast<unsigned>(f32_to_bf16(b)) << 16);
+  typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
-template <typename XT, int TN>
+template <typename XT, int TN, int R>
 __global__ __launch_bounds__(256, 2) void gemm_rows_kernel(
     const XT* __restrict__ x, int64_t ldx, int64_t sx, const bf16raw* __restrict__ w,
     int64_t ldw, int64_t sw, float* __restrict__ y, int64_t ldy, int64_t sy, int M, int N,
@@ -120,41 +127,50 @@ __global__ __launch_bounds__(256, 2) void gemm_rows_kernel(
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[j][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // W fragments of the next three k-steps in flight (ring of 4 k-steps)
-  bf16x8_t wf[4][TN];
+  // W fragments of the next R - 1 k-steps in flight (ring of R k-steps, R a multiple of
+  // the 4 steps of a chunk).  Every step issues TN loads (clamped to the last step near the
+  // end), so the wait before each MFMA is an exact count.  The chunk loop is unrolled over
+  // one turn of the ring (R / 4 chunks; the plan makes the chunk count a multiple of it), so
+  // every ring slot is a fixed register.
+  static_assert(R % 4 == 0 && R >= 4, "ring of whole chunks");
+  constexpr int CPT = R / 4;  // chunks per turn of the ring
+  bf16x8_t wf[R][TN];
 #pragma unroll
-  for (int i = 0; i < 3; ++i)
+  for (int i = 0; i < R - 1; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) wf[i][j] = w_frag(min(i, nsteps - 1), j);
 
   stage_load(kb);
   stage_store(0);
-  for (int c = 0; c < nchunks; ++c) {
-    __syncthreads();  // chunk c staged; the other buffer is free
-    const bool more = c + 1 < nchunks;
-    stage_load(kb + min(c + 1, nchunks - 1) * KC);
-    const lds_char_t* xa = lsm + (c & 1) * 2 * XPLANE + r * XROW + g * 16;
+  for (int c0 = 0; c0 < nchunks; c0 += CPT) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int step = 4 * c + i;
+    for (int u = 0; u < CPT; ++u) {
+      const int c = c0 + u;
+      __syncthreads();  // chunk c staged; the other buffer is free
+      stage_load(kb + min(c + 1, nchunks - 1) * KC);
+      const lds_char_t* xa = lsm + (c & 1) * 2 * XPLANE + r * XROW + g * 16;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) wf[(i + 3) & 3][j] = w_frag(min(step + 3, nsteps - 1), j);
+      for (int i = 0; i < 4; ++i) {
+        const int step = 4 * c + i, slot = 4 * u + i;  // slot == step % R
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8_t ah = *(const lds_bf16x8_t*)(xa + mt * 16 * XROW + i * 64);
+        for (int j = 0; j < TN; ++j) wf[(slot + R - 1) % R][j] = w_frag(min(step + R - 1, nsteps - 1), j);
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wf[i][j], acc[j][mt], 0, 0, 0);
-        if constexpr (SPLIT_X) {
-          const bf16x8_t al = *(const lds_bf16x8_t*)(xa + XPLANE + mt * 16 * XROW + i * 64);
+        for (int mt = 0; mt < 4; ++mt) {
+          const bf16x8_t ah = *(const lds_bf16x8_t*)(xa + mt * 16 * XROW + i * 64);
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wf[i][j], acc[j][mt], 0, 0, 0);
+            acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wf[slot][j], acc[j][mt], 0, 0, 0);
+          if constexpr (SPLIT_X) {
+            const bf16x8_t al = *(const lds_bf16x8_t*)(xa + XPLANE + mt * 16 * XROW + i * 64);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wf[slot][j], acc[j][mt], 0, 0, 0);
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      if (c + 1 < nchunks) stage_store((c + 1) & 1);
     }
-    if (more) stage_store((c + 1) & 1);
   }
 
   // ---- lane (g, r) of tile (j, mt) holds y[m0 + 16 mt + 4 g + i][n0 + 16 j + r]
@@ -175,42 +191,69 @@ __global__ __launch_bounds__(256, 2) void gemm_rows_kernel(
   }
 }
 
-// zero y[z][m][n] for the atomic accumulation
-__global__ void zero_rows_kernel(float* __restrict__ y, int64_t ldy, int64_t sy, int M, int N,
-                                 int batch) {
-  const int64_t total = static_cast<int64_t>(batch) * M * N;
-  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < total;
-       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t z = e / (static_cast<int64_t>(M) * N);
-    const int64_t rem = e % (static_cast<int64_t>(M) * N);
-    y[z * sy + (rem / N) * ldy + rem % N] = 0.f;
+// zero y[z][m][n] for the atomic accumulation: rows (z, m) over grid.y, 16-byte stores
+// along n where the row is aligned
+__global__ __launch_bounds__(256) void zero_rows_kernel(float* __restrict__ y, int64_t ldy,
+                                                        int64_t sy, int M, int N, int batch) {
+  const int64_t rows = static_cast<int64_t>(M) * batch;
+  for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
+    const int64_t z = row / M, m = row - z * M;
+    float* p = y + z * sy + m * ldy;
+    const bool vec = (reinterpret_cast<uintptr_t>(p) & 15) == 0;
+    for (int n = (blockIdx.x * 256 + threadIdx.x) * 4; n < N; n += gridDim.x * 1024) {
+      if (vec && n + 4 <= N) {
+        *reinterpret_cast<float4*>(p + n) = make_float4(0.f, 0.f, 0.f, 0.f);
+      } else {
+        for (int k = n; k < min(n + 4, N); ++k) p[k] = 0.f;
+      }
+    }
   }
 }
 
-template <typename XT, int TN>
+template <typename XT, int TN, int R>
 hipError_t launch_t(const GemmArgs& g, int KS, hipStream_t s) {
   const int kper = g.K / KS;
   const int nb = (g.N + 64 * TN - 1) / (64 * TN), mb = (g.M + 63) / 64;
   if (KS > 1) {
-    const int64_t total = static_cast<int64_t>(g.batch) * g.M * g.N;
-    const int blocks = static_cast<int>(std::min<int64_t>((total + 255) / 256, 4096));
-    hipLaunchKernelGGL(zero_rows_kernel, dim3(blocks), dim3(256), 0, s, static_cast<float*>(g.y),
+    const int64_t rows = static_cast<int64_t>(g.batch) * g.M;
+    const int gx = static_cast<int>(std::min<int64_t>((g.N + 1023) / 1024, 64));
+    const int gy = static_cast<int>(std::min<int64_t>(rows, 4096));
+    hipLaunchKernelGGL(zero_rows_kernel, dim3(gx, gy), dim3(256), 0, s, static_cast<float*>(g.y),
                        g.ldy, g.sy, g.M, g.N, g.batch);
   }
-  hipLaunchKernelGGL((gemm_rows_kernel<XT, TN>), dim3(nb, mb, g.batch * KS), dim3(256), 0, s,
+  hipLaunchKernelGGL((gemm_rows_kernel<XT, TN, R>), dim3(nb, mb, g.batch * KS), dim3(256), 0, s,
                      static_cast<const XT*>(g.x), g.ldx, g.sx, static_cast<const bf16raw*>(g.w),
                      g.ldw, g.sw, static_cast<float*>(g.y), g.ldy, g.sy, g.M, g.N, g.K, KS,
                      kper, KS > 1 ? 1 : 0);
   return hipGetLastError();
 }
 
-template <typename XT>
-hipError_t launch_x(const GemmArgs& g, int TN, int KS, hipStream_t s) {
-  switch (TN) {
-    case 4: return launch_t<XT, 4>(g, KS, s);
-    case 2: return launch_t<XT, 2>(g, KS, s);
-    default: return launch_t<XT, 1>(g, KS, s);
+// ring depths compiled per tile width: the ring holds 4 R TN registers per lane
+template <typename XT, int TN>
+hipError_t launch_r(const GemmArgs& g, int KS, int R, hipStream_t s) {
+  switch (R) {
+    case 4: return launch_t<XT, TN, 4>(g, KS, s);
+    case 8: return launch_t<XT, TN, 8>(g, KS, s);
+    case 12: if constexpr (TN <= 2) return launch_t<XT, TN, 12>(g, KS, s); else break;
+    case 16: if constexpr (TN <= 2) return launch_t<XT, TN, 16>(g, KS, s); else break;
+    case 20: if constexpr (TN == 1) return launch_t<XT, TN, 20>(g, KS, s); else break;
+    default: break;
   }
+  return hipErrorInvalidValue;
+}
+
+template <typename XT>
+hipError_t launch_x(const GemmArgs& g, int TN, int KS, int R, hipStream_t s) {
+  switch (TN) {
+    case 4: return launch_r<XT, 4>(g, KS, R, s);
+    case 2: return launch_r<XT, 2>(g, KS, R, s);
+    case 1: return launch_r<XT, 1>(g, KS, R, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool ring_ok(int tn, int r) {
+  return r == 4 || r == 8 || ((r == 12 || r == 16) && tn <= 2) || (r == 20 && tn == 1);
 }
 
 }  // namespace
@@ -222,11 +265,15 @@ bool gemm_rows_supported(const GemmArgs& g) {
          (reinterpret_cast<uintptr_t>(g.x) & 15) == 0 && (g.ldx % 8) == 0 && (g.sx % 8) == 0;
 }
 
-// Tile width and k split.  Wide tiles (fewer re-reads of x per weight byte) pay off when
-// both N and the k range are long; otherwise narrower tiles spread better.  The k split is
-// the smallest divisor of the chunk count whose grid fills about 3/4 of the 256 CUs.
-// (Chosen from measurements at the DeepSeek-V2 projection shapes with M = 64.)
-void gemm_rows_plan(const GemmArgs& g, int* tn, int* ks) {
+// Tile width, k split and ring depth.  Wide tiles (fewer re-reads of x per weight byte)
+// pay off when both N and the k range are long; otherwise narrower tiles spread better.
+// The k split is the smallest divisor of the chunk count whose grid fills about 3/4 of the
+// 256 CUs.  The ring is the deepest compiled one that turns a whole number of times over a
+// workgroup's chunks: the weight bytes in flight per CU, not the access pattern, bound
+// these short streams (the fragment pattern itself streams at full HBM rate once enough
+// loads are outstanding).  (Chosen from measurements at the DeepSeek-V2 projection shapes
+// with M = 64.)
+void gemm_rows_plan(const GemmArgs& g, int* tn, int* ks, int* ring) {
   const int chunks = g.K / KC;
   const int64_t mb = (g.M + 63) / 64;
   const int t = (g.N >= 4096 && g.K >= 8192) ? 4 : (g.N >= 4096 ? 2 : 1);
@@ -239,12 +286,29 @@ void gemm_rows_plan(const GemmArgs& g, int* tn, int* ks) {
     *ks = d;
     if (nb * mb * g.batch * d >= 192) break;
   }
+  const int per = chunks / *ks;
+  *ring = 4;
+  if (t < 4)  // four-tile waves already hold 12 KB in flight per wave with the shallow ring
+    for (int r = 20; r > 4; r -= 4)
+      if (ring_ok(t, r) && per % (r / 4) == 0) { *ring = r; break; }
+}
+
+bool gemm_rows_plan_ok(const GemmArgs& g, int tn, int ks, int ring) {
+  const int chunks = g.K / KC;
+  return (tn == 1 || tn == 2 || tn == 4) && ks >= 1 && chunks % ks == 0 &&
+         static_cast<int64_t>(g.batch) * ks <= 65535 && ring_ok(tn, ring) &&
+         (chunks / ks) % (ring / 4) == 0;
+}
+
+hipError_t launch_gemm_rows_with(const GemmArgs& g, int tn, int ks, int ring, hipStream_t s) {
+  if (!gemm_rows_plan_ok(g, tn, ks, ring)) return hipErrorInvalidValue;
+  return g.x_bf16 ? launch_x<bf16raw>(g, tn, ks, ring, s) : launch_x<float>(g, tn, ks, ring, s);
 }
 
 hipError_t launch_gemm_rows(const GemmArgs& g, hipStream_t s) {
-  int tn = 1, ks = 1;
-  gemm_rows_plan(g, &tn, &ks);
-  return g.x_bf16 ? launch_x<bf16raw>(g, tn, ks, s) : launch_x<float>(g, tn, ks, s);
+  int tn = 1, ks = 1, ring = 4;
+  gemm_rows_plan(g, &tn, &ks, &ring);
+  return launch_gemm_rows_with(g, tn, ks, ring, s);
 }
 
 }  // namespace mla

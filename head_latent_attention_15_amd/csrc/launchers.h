@@ -45,8 +45,13 @@ struct GemmArgs {
 hipError_t launch_gemm_small(const GemmArgs& g, hipStream_t s);
 // Same product on bf16 MFMA for bf16 nn.Linear-layout weights (w_nk), fp32 y and K a
 // multiple of 128 (gemm_rows_supported); split-K results are added with fp32 atomics.
+// The plan picks the tile width (tn 16-column tiles per wavefront), the k split and the
+// depth of the weight ring; launch_gemm_rows_with takes them explicitly (checked by
+// gemm_rows_plan_ok).
 bool gemm_rows_supported(const GemmArgs& g);
-void gemm_rows_plan(const GemmArgs& g, int* tn, int* ks);
+void gemm_rows_plan(const GemmArgs& g, int* tn, int* ks, int* ring);
+bool gemm_rows_plan_ok(const GemmArgs& g, int tn, int ks, int ring);
+hipError_t launch_gemm_rows_with(const GemmArgs& g, int tn, int ks, int ring, hipStream_t s);
 hipError_t launch_gemm_rows(const GemmArgs& g, hipStream_t s);
 
 // Query absorption q~_i = W^UK_i^T q^C_i on bf16 MFMA (bf16 W^UK, bf16 q~, d_h = 128).
