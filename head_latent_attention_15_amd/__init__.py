@@ -60,6 +60,8 @@ _SIGNATURES = {
     "mla_decode": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _SZ, _P, _P, _I32, _P]),
     "mla_out_proj": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "mla_linear": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P]),
+    "mla_linear_planned": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _I32, _I32, _I32,
+                                  _I32, _P]),
     "mla_validate_indices": (_I32, [_P, _P, _SP, _P, _P]),
     "mla_stream_read": (_I32, [_P, _SZ, _P, _P]),
     "mla_status_string": (ctypes.c_char_p, [_I32]),
@@ -341,6 +343,17 @@ def mla_linear(x, w, y, stream=None):
     _invoke("mla_linear", _dev(x, "x", None, 2), _dtype_code(x), _dev(w, "w", None, 2),
                           _dtype_code(w), M, N, K, _dev(y, "y", torch.float32, 2),
                           _stream(stream))
+
+
+def mla_linear_planned(x, w, y, kernel, tile, split, ring, stream=None):
+    """mla_linear on an explicit kernel (0 tile grid, 1 persistent) and plan."""
+    torch = _torch()
+    M, K = x.shape
+    N = w.shape[0]
+    _expect(w.shape[1] == K and tuple(y.shape) == (M, N), "shapes must be x[M,K] w[N,K] y[M,N]")
+    _invoke("mla_linear_planned", _dev(x, "x", None, 2), _dtype_code(x), _dev(w, "w", None, 2),
+                                  _dtype_code(w), M, N, K, _dev(y, "y", torch.float32, 2),
+                                  kernel, tile, split, ring, _stream(stream))
 
 
 def mla_validate_indices(block_table, seq_lens, page_size, num_pages, dev_count, stream=None):

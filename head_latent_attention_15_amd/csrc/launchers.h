@@ -53,6 +53,14 @@ void gemm_rows_plan(const GemmArgs& g, int* tn, int* ks, int* ring);
 bool gemm_rows_plan_ok(const GemmArgs& g, int tn, int ks, int ring);
 hipError_t launch_gemm_rows_with(const GemmArgs& g, int tn, int ks, int ring, hipStream_t s);
 hipError_t launch_gemm_rows(const GemmArgs& g, hipStream_t s);
+// Persistent form of the same product for M <= 64 and N a multiple of 64: one workgroup per
+// CU, each streaming an equal run of (64 tn columns x 128 k) units with a continuous weight
+// ring (depth `ring` k-steps); partial tile sums added into y with fp32 atomics.
+bool gemm_stream_supported(const GemmArgs& g);
+void gemm_stream_plan(const GemmArgs& g, int* tn, int* grid, int* ring);
+bool gemm_stream_plan_ok(const GemmArgs& g, int tn, int grid, int ring);
+hipError_t launch_gemm_stream_with(const GemmArgs& g, int tn, int grid, int ring, hipStream_t s);
+hipError_t launch_gemm_stream(const GemmArgs& g, hipStream_t s);
 
 // Query absorption q~_i = W^UK_i^T q^C_i on bf16 MFMA (bf16 W^UK, bf16 q~, d_h = 128).
 bool absorb_mfma_supported(int B, int H, int d_h, int d_c, const void* q_c, const void* w_uk,

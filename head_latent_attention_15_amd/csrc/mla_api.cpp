@@ -59,8 +59,14 @@ mla_status_t check_paged_shape(const mla_paged_shape_t* shp) {
 }
 
 // Projections: bf16 MFMA weight streaming where it applies, the fp32 tile GEMM otherwise
-// (fp32 weights, bf16 output, k not a multiple of 128, weights stored [in, out]).
+// (fp32 weights, bf16 output, k not a multiple of 128, weights stored [in, out]).  Large
+// single products (8 MB of weights and up, 1024 output columns and up: W^DQ, W^UQ, W^QR,
+// W^O at the DeepSeek-V2 sizes) take the persistent one-workgroup-per-CU kernel, which
+// measured faster there; smaller and batched ones the tile-grid kernel.
 hipError_t gemm(const mla::GemmArgs& g, hipStream_t s) {
+  if (mla::gemm_stream_supported(g) && g.batch == 1 && g.N >= 1024 &&
+      static_cast<int64_t>(g.N) * g.K * 2 >= (int64_t{8} << 20))
+    return mla::launch_gemm_stream(g, s);
   return mla::gemm_rows_supported(g) ? mla::launch_gemm_rows(g, s) : mla::launch_gemm_small(g, s);
 }
 
@@ -314,6 +320,35 @@ mla_status_t mla_linear(const void* x, mla_dtype_t x_dtype, const void* w,
   g.y = y; g.ldy = N; g.sy = 0; g.y_bf16 = 0;
   g.M = M; g.N = N; g.K = K; g.batch = 1;
   return launched(gemm(g, as_stream(stream)), "linear GEMM");
+}
+
+mla_status_t mla_linear_planned(const void* x, mla_dtype_t x_dtype, const void* w,
+                                mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K, float* y,
+                                int32_t kernel, int32_t tile, int32_t split, int32_t ring,
+                                void* stream) {
+  if (!x || !w || !y) return fail(MLA_ERR_NULL, "mla_linear_planned: a required pointer is NULL");
+  if (M < 1 || N < 1 || K < 1) return fail(MLA_ERR_SHAPE, "mla_linear_planned: sizes must be >= 1");
+  if (!is_dtype(x_dtype) || w_dtype != MLA_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_linear_planned: bf16 weights required");
+  mla::GemmArgs g;
+  g.x = x; g.ldx = K; g.sx = 0; g.x_bf16 = x_dtype == MLA_BF16;
+  g.w = w; g.ldw = K; g.sw = 0; g.w_bf16 = 1; g.w_nk = true;
+  g.y = y; g.ldy = N; g.sy = 0; g.y_bf16 = 0;
+  g.M = M; g.N = N; g.K = K; g.batch = 1;
+  const hipStream_t s = as_stream(stream);
+  if (kernel == 0) {
+    if (!mla::gemm_rows_supported(g) || !mla::gemm_rows_plan_ok(g, tile, split, ring))
+      return fail(MLA_ERR_UNSUPPORTED, "mla_linear_planned: tile-grid plan (%d, %d, %d) not valid here",
+                  tile, split, ring);
+    return launched(mla::launch_gemm_rows_with(g, tile, split, ring, s), "linear GEMM");
+  }
+  if (kernel == 1) {
+    if (!mla::gemm_stream_supported(g) || !mla::gemm_stream_plan_ok(g, tile, split, ring))
+      return fail(MLA_ERR_UNSUPPORTED, "mla_linear_planned: persistent plan (%d, %d, %d) not valid here",
+                  tile, split, ring);
+    return launched(mla::launch_gemm_stream_with(g, tile, split, ring, s), "linear GEMM");
+  }
+  return fail(MLA_ERR_UNSUPPORTED, "mla_linear_planned: kernel %d unknown", kernel);
 }
 
 mla_status_t mla_validate_indices(const int32_t* block_table, const int32_t* seq_lens,

@@ -218,6 +218,19 @@ mla_status_t mla_validate_indices(const int32_t* block_table, const int32_t* seq
  * practical HBM read ceiling next to the attention kernel.  Errors: NULL, SHAPE. */
 mla_status_t mla_stream_read(const void* src, size_t bytes, float* sink, void* stream);
 
+/* mla_linear with an explicit kernel and plan, for measurement and for tests that cover
+ * each plan: kernel 0 is the tile-grid GEMM (tile = 16-column tiles per wavefront 1, 2 or
+ * 4; split = workgroups along k, dividing K / 128; ring = weight k-steps in flight, 4 to 20
+ * by 4, turning a whole number of times over a workgroup's chunks), kernel 1 the persistent
+ * GEMM (tile as above with N a multiple of 64 tile and M <= 64; split = workgroups, at most
+ * 256, dividing the unit count N / (64 tile) * K / 128; ring as above over a workgroup's
+ * units).  Same product, layouts and rounding as mla_linear; bf16 weights only.
+ * Errors: NULL, SHAPE, UNSUPPORTED (dtype, or a plan the kernel cannot take). */
+mla_status_t mla_linear_planned(const void* x, mla_dtype_t x_dtype, const void* w,
+                                mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K, float* y,
+                                int32_t kernel, int32_t tile, int32_t split, int32_t ring,
+                                void* stream);
+
 /* Static string for a status code. */
 const char* mla_status_string(mla_status_t status);
 

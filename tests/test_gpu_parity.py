@@ -508,6 +508,47 @@ def test_weight_streaming_gemm_paths(mla):
         assert r <= 1e-5, (M, N, K, r)
 
 
+def test_linear_planned_kernels(mla):
+    """Both weight-streaming kernels over explicit plans against numpy fp64 matmul: the
+    persistent kernel with k slices per XCD (grids that are multiples of 8) and without,
+    runs that cross column-tile boundaries, odd runs, ragged M, bf16 and fp32 x, every ring
+    depth; the tile-grid kernel over its tile widths, k splits and rings.  Invalid plans are
+    refused without launching."""
+    g = torch.Generator().manual_seed(34)
+    cases = [  # (M, N, K, x dtype, [(kernel, tile, split, ring), ...])
+        (64, 1536, 5120, torch.bfloat16, [(1, 1, 240, 16), (1, 2, 240, 8), (1, 4, 240, 4),
+                                          (1, 1, 160, 12), (0, 1, 8, 20), (0, 2, 4, 4)]),
+        (50, 1024, 1536, torch.float32, [(1, 2, 96, 4), (1, 1, 96, 8), (1, 4, 12, 4),
+                                         (1, 2, 48, 8), (0, 2, 2, 12), (0, 4, 3, 4)]),
+        (64, 512, 640, torch.float32, [(1, 1, 8, 4), (1, 1, 10, 16), (1, 1, 40, 4),
+                                       (1, 2, 20, 4), (0, 1, 5, 4)]),
+        (7, 128, 256, torch.bfloat16, [(1, 2, 2, 4), (1, 1, 4, 4), (1, 1, 1, 8), (0, 1, 2, 4)]),
+    ]
+    for (M, N, K, xdt, plans) in cases:
+        x = torch.randn(M, K, generator=g).to(xdt)
+        w = torch.randn(N, K, generator=g).to(torch.bfloat16)
+        ref = W.to_f64(x) @ W.to_f64(w).T
+        xd, wd = dev(x), dev(w)
+        for (kernel, tile, split, ring) in plans:
+            say(f"planned GEMM M={M} N={N} K={K} x={xdt} kernel={kernel} plan=({tile},{split},{ring})")
+            y = torch.full((M, N), float("nan"), device="cuda")
+            mla.mla_linear_planned(xd, wd, y, kernel, tile, split, ring)
+            torch.cuda.synchronize()
+            m, r = errors(host64(y), ref)
+            assert m <= 2e-5 * float(np.abs(ref).max()) + 1e-4, (M, N, K, kernel, tile, split, ring, m)
+            assert r <= 1e-5, (M, N, K, kernel, tile, split, ring, r)
+    # plans the kernels cannot take are refused (nothing launched, y untouched)
+    x = dev(torch.randn(64, 1536, generator=g))
+    w = dev(torch.randn(1024, 1536, generator=g).to(torch.bfloat16))
+    y = torch.zeros(64, 1024, device="cuda")
+    for bad in [(1, 4, 7, 4), (1, 2, 512, 4), (1, 4, 96, 8), (1, 3, 96, 4), (0, 2, 5, 4),
+                (0, 4, 2, 16), (2, 1, 1, 4)]:
+        with pytest.raises(mla.MLAError):
+            mla.mla_linear_planned(x, w, y, *bad)
+    torch.cuda.synchronize()
+    assert float(y.abs().max()) == 0.0
+
+
 def test_out_proj_full_size(mla):
     """W^UV per head (batched, strided) then W^O at the DeepSeek-V2 sizes, fp64 reference."""
     g = torch.Generator().manual_seed(32)
