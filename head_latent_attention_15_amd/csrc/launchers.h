@@ -61,6 +61,14 @@ void gemm_stream_plan(const GemmArgs& g, int* tn, int* grid, int* ring);
 bool gemm_stream_plan_ok(const GemmArgs& g, int tn, int grid, int ring);
 hipError_t launch_gemm_stream_with(const GemmArgs& g, int tn, int grid, int ring, hipStream_t s);
 hipError_t launch_gemm_stream(const GemmArgs& g, hipStream_t s);
+// Activation-stationary form for M <= 64, N a multiple of 128 and K of 256: a workgroup
+// stages one k slice (32 s values) of x in LDS once and streams the weights of a run of
+// 128 tn-column tiles in it.  The plan picks tn (1, 2), s (8, 12, 16, 20) and the grid.
+bool gemm_xs_supported(const GemmArgs& g);
+bool gemm_xs_plan(const GemmArgs& g, int* tn, int* s, int* grid);
+bool gemm_xs_plan_ok(const GemmArgs& g, int tn, int s, int grid);
+hipError_t launch_gemm_xs_with(const GemmArgs& g, int tn, int s, int grid, hipStream_t st);
+hipError_t launch_gemm_xs(const GemmArgs& g, hipStream_t st);
 
 // Query absorption q~_i = W^UK_i^T q^C_i on bf16 MFMA (bf16 W^UK, bf16 q~, d_h = 128).
 bool absorb_mfma_supported(int B, int H, int d_h, int d_c, const void* q_c, const void* w_uk,

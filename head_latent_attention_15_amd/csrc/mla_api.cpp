@@ -60,13 +60,19 @@ mla_status_t check_paged_shape(const mla_paged_shape_t* shp) {
 
 // Projections: bf16 MFMA weight streaming where it applies, the fp32 tile GEMM otherwise
 // (fp32 weights, bf16 output, k not a multiple of 128, weights stored [in, out]).  Large
-// single products (8 MB of weights and up, 1024 output columns and up: W^DQ, W^UQ, W^QR,
-// W^O at the DeepSeek-V2 sizes) take the persistent one-workgroup-per-CU kernel, which
-// measured faster there; smaller and batched ones the tile-grid kernel.
+// single products (8 MB of weights and up, 1024 output columns and up) take one of the
+// one-workgroup-per-CU kernels, which measured faster there: the activation-stationary
+// one for short k (up to 4096, 4096 columns and up: W^UQ, W^QR at the DeepSeek-V2 sizes),
+// the persistent one otherwise (W^DQ, W^O).  Smaller and batched products take the
+// tile-grid kernel.
 hipError_t gemm(const mla::GemmArgs& g, hipStream_t s) {
-  if (mla::gemm_stream_supported(g) && g.batch == 1 && g.N >= 1024 &&
-      static_cast<int64_t>(g.N) * g.K * 2 >= (int64_t{8} << 20))
-    return mla::launch_gemm_stream(g, s);
+  const bool large = g.batch == 1 && g.N >= 1024 &&
+                     static_cast<int64_t>(g.N) * g.K * 2 >= (int64_t{8} << 20);
+  int tn, sl, grid;
+  if (large && g.K <= 4096 && g.N >= 4096 && mla::gemm_xs_supported(g) &&
+      mla::gemm_xs_plan(g, &tn, &sl, &grid))
+    return mla::launch_gemm_xs_with(g, tn, sl, grid, s);
+  if (large && mla::gemm_stream_supported(g)) return mla::launch_gemm_stream(g, s);
   return mla::gemm_rows_supported(g) ? mla::launch_gemm_rows(g, s) : mla::launch_gemm_small(g, s);
 }
 
@@ -347,6 +353,13 @@ mla_status_t mla_linear_planned(const void* x, mla_dtype_t x_dtype, const void* 
       return fail(MLA_ERR_UNSUPPORTED, "mla_linear_planned: persistent plan (%d, %d, %d) not valid here",
                   tile, split, ring);
     return launched(mla::launch_gemm_stream_with(g, tile, split, ring, s), "linear GEMM");
+  }
+  if (kernel == 2) {
+    if (!mla::gemm_xs_supported(g) || !mla::gemm_xs_plan_ok(g, tile, ring, split))
+      return fail(MLA_ERR_UNSUPPORTED,
+                  "mla_linear_planned: activation-stationary plan (%d, %d, %d) not valid here",
+                  tile, split, ring);
+    return launched(mla::launch_gemm_xs_with(g, tile, ring, split, s), "linear GEMM");
   }
   return fail(MLA_ERR_UNSUPPORTED, "mla_linear_planned: kernel %d unknown", kernel);
 }

@@ -224,7 +224,11 @@ mla_status_t mla_stream_read(const void* src, size_t bytes, float* sink, void* s
  * by 4, turning a whole number of times over a workgroup's chunks), kernel 1 the persistent
  * GEMM (tile as above with N a multiple of 64 tile and M <= 64; split = workgroups, at most
  * 256, dividing the unit count N / (64 tile) * K / 128; ring as above over a workgroup's
- * units).  Same product, layouts and rounding as mla_linear; bf16 weights only.
+ * units); kernel 2 the activation-stationary GEMM (tile 1 or 2 = 128-column tiles of 8
+ * wavefronts, M <= 64, N a multiple of 128 tile; ring = k-steps per slice, the slice
+ * being 32 ring values of k: 8, 12 or 16 for fp32 x, 8, 16 or 20 for bf16 x (tile 2: 8 or
+ * 16); split = workgroups, at most 256, whose runs of tiles stay inside one slice).  Same
+ * product, layouts and rounding as mla_linear; bf16 weights only.
  * Errors: NULL, SHAPE, UNSUPPORTED (dtype, or a plan the kernel cannot take). */
 mla_status_t mla_linear_planned(const void* x, mla_dtype_t x_dtype, const void* w,
                                 mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K, float* y,

@@ -523,6 +523,12 @@ def test_linear_planned_kernels(mla):
         (64, 512, 640, torch.float32, [(1, 1, 8, 4), (1, 1, 10, 16), (1, 1, 40, 4),
                                        (1, 2, 20, 4), (0, 1, 5, 4)]),
         (7, 128, 256, torch.bfloat16, [(1, 2, 2, 4), (1, 1, 4, 4), (1, 1, 1, 8), (0, 1, 2, 4)]),
+        # activation-stationary: slices of 256 / 384 / 512 k, runs of 1 to 4 tiles, two-tile
+        # waves, ragged M, bf16 x with 640-wide slices (copies spanning two rows)
+        (64, 2048, 1536, torch.float32, [(2, 1, 64, 12), (2, 1, 32, 12), (2, 1, 48, 16),
+                                         (2, 2, 24, 8), (2, 2, 16, 12), (2, 1, 96, 8)]),
+        (33, 1024, 5120, torch.bfloat16, [(2, 1, 64, 20), (2, 1, 80, 16), (2, 2, 40, 8),
+                                          (2, 1, 8, 20)]),
     ]
     for (M, N, K, xdt, plans) in cases:
         x = torch.randn(M, K, generator=g).to(xdt)
@@ -542,7 +548,7 @@ def test_linear_planned_kernels(mla):
     w = dev(torch.randn(1024, 1536, generator=g).to(torch.bfloat16))
     y = torch.zeros(64, 1024, device="cuda")
     for bad in [(1, 4, 7, 4), (1, 2, 512, 4), (1, 4, 96, 8), (1, 3, 96, 4), (0, 2, 5, 4),
-                (0, 4, 2, 16), (2, 1, 1, 4)]:
+                (0, 4, 2, 16), (2, 1, 7, 12), (2, 1, 32, 20), (2, 4, 8, 8), (3, 1, 1, 4)]:
         with pytest.raises(mla.MLAError):
             mla.mla_linear_planned(x, w, y, *bad)
     torch.cuda.synchronize()
