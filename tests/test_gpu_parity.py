@@ -578,7 +578,8 @@ def test_out_proj_full_size(mla):
 def test_absorb_mfma_against_oracle(mla):
     """Query absorption on the MFMA path (bf16 W^UK, bf16 q~, d_h = 128) against the
     oracle's absorption in fp64: ragged batch (B = 70: a full and a partial 64-row block),
-    several 128-column blocks; q~ is rounded once to bf16."""
+    four 128-column blocks; q~ is rounded once to bf16.  Then with q^R, whose RoPE the same
+    call applies, against the oracle's RoPE at ragged positions."""
     g = torch.Generator().manual_seed(33)
     B, H, d_h, d_c = 70, 6, 128, 512
     say("absorb mfma")
@@ -593,3 +594,16 @@ def test_absorb_mfma_against_oracle(mla):
     # the bf16 output is the only rounding: within half a bf16 ulp of the fp64 value
     m, _ = errors(host64(q_lat), ref)
     assert m <= float(np.abs(ref).max()) * 2.0 ** -8, m
+    # with q^R: the same launch also rotates q_pe at position seq_len - 1 (ragged lengths)
+    d_R = 64
+    q_r = torch.randn(B, H, d_R, generator=g)
+    seq_lens = torch.randint(1, 5000, (B,), generator=g, dtype=torch.int32)
+    q_lat2 = torch.empty(B, H, d_c, device="cuda", dtype=torch.bfloat16)
+    q_pe = torch.empty(B, H, d_R, device="cuda", dtype=torch.bfloat16)
+    mla.mla_absorb_q(dev(q_c), dev(w_uk), dev(q_r), dev(seq_lens), 10000.0, q_lat2, q_pe)
+    torch.cuda.synchronize()
+    assert torch.equal(q_lat2.cpu(), q_lat.cpu())
+    ref_pe = np.stack([oracle.rope(W.to_f64(q_r[b]), int(seq_lens[b]) - 1) for b in range(B)])
+    assert_bf16(host64(q_pe), ref_pe, "q_pe")
+    m, _ = errors(host64(q_pe), ref_pe)
+    assert m <= float(np.abs(ref_pe).max()) * 2.0 ** -8, m
