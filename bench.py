@@ -188,6 +188,43 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     return res
 
 
+def multi_token_rows(mla, W, torch, caches, bt, sl, scale, num_cus, n_q: int = 2, steps: int = 20):
+    """Multi-token decode on the headline cache: the last n_q cached tokens of every
+    sequence are new queries (causal among themselves); attention + combine over B n_q
+    query rows.  The cache is counted once in the bytes: the n_q workgroups of a
+    (sequence, split) read the same tiles."""
+    B, H, T = 32, 128, 4096
+    q_lat, q_pe = (t.to("cuda") for t in W.multi_queries(6, B, n_q, H))
+    S = mla.mla_suggest_num_splits(B * n_q, T, 0, 64, num_cus)
+    o_part = torch.empty(B, n_q, H, S, 512, device="cuda", dtype=torch.bfloat16)
+    lse_part = torch.empty(B, n_q, H, S, device="cuda")
+    out = torch.empty(B * n_q, H, 512, device="cuda")
+    calls = [mla.bind(mla.mla_decode_attn_multi, q_lat, q_pe, c, bt, sl, scale, S, o_part, lse_part)
+             for c in caches]
+    combine = mla.bind(mla.mla_splitk_combine, o_part.view(B * n_q, H, S, 512),
+                       lse_part.view(B * n_q, H, S), out)
+    for k in range(8):
+        calls[k % len(calls)]()
+        combine()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(steps):
+        calls[k % len(calls)]()
+        combine()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    cache_bytes = B * T * ROW_BYTES
+    flops = B * n_q * T * H * FLOP_PER_TOKEN_HEAD
+    return {"workload": f"decode_nq{n_q}_b32_t4k (B=32, T=4096, H=128, {n_q} query tokens per "
+                        "sequence at positions T-n_q .. T-1, causal among them)",
+            "n_q": n_q, "num_splits": S, "us_per_step": round(us, 2),
+            "query_tokens_per_s": round(B * n_q / (us * 1e-6), 1),
+            "cache_GBps": round(cache_bytes / (us * 1e-6) / 1e9, 1),
+            "tflops": round(flops / (us * 1e-6) / 1e12, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +375,8 @@ def main():
                      "kernel": "attn_mfma_kernel<8, bf16 partials> (8 waves x 16 heads, 32-token tiles)",
                      "bytes_per_launch_algorithmic": attn_alg_bytes},
     }
+    log("timing multi-token decode (2 query tokens per sequence)")
+    result["multi_token"] = multi_token_rows(mla, W, torch, caches, bt, sl, scale, num_cus)
     if not args.no_cpu_baseline:
         log(f"timing the fp64 oracle on {args.cpu_seqs} sequences")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)

@@ -56,6 +56,8 @@ _SIGNATURES = {
                             _I32, _P]),
     "mla_kv_append": (_I32, [_P, _P, _I32, _P, _P, _P, _F, _SP, _I32, _P]),
     "mla_decode_attn": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _I32, _P, _I32, _P]),
+    "mla_decode_attn_multi": (_I32, [_P, _P, _P, _P, _P, _SP, _I32, _F, _I32, _P, _I32, _P, _I32,
+                                     _P]),
     "mla_splitk_combine": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "mla_decode": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _SZ, _P, _P, _I32, _P]),
     "mla_out_proj": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
@@ -280,6 +282,31 @@ def mla_decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale,
         _dev(o_part, "o_part"), _dtype_code(o_part), _dev(lse_part, "lse_part", torch.float32),
         _dtype_code(q_lat), _stream(stream))
 
+
+
+def mla_decode_attn_multi(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale,
+                          num_splits, o_part, lse_part=None, stream=None):
+    """Decode attention for n_q new tokens per sequence (causal among them): q_lat
+    [B,n_q,H,d_c], q_pe [B,n_q,H,d_R]; o_part [B,n_q,H,S,d_c] (or [B,n_q,H,d_c] when S == 1),
+    lse_part [B,n_q,H,S] (or None when S == 1)."""
+    torch = _torch()
+    B, n_q, H, d_c = q_lat.shape
+    _expect(tuple(q_pe.shape[:3]) == (B, n_q, H), "q_pe must be [B,n_q,H,d_R]")
+    _expect(q_pe.dtype == q_lat.dtype == kv_cache.dtype, "q_lat, q_pe, kv_cache share a dtype")
+    _expect(kv_cache.shape[2] == d_c + q_pe.shape[3], "cache row must be d_c + d_R wide")
+    _expect(block_table.shape[0] == B and tuple(seq_lens.shape) == (B,), "batch mismatch")
+    S = int(num_splits)
+    want = (B, n_q, H, d_c) if S == 1 else (B, n_q, H, S, d_c)
+    _expect(tuple(o_part.shape) == want, f"o_part must be {want}")
+    if lse_part is not None:
+        _expect(lse_part.numel() == B * n_q * H * S, "lse_part must hold B*n_q*H*S floats")
+    shp = paged_shape(kv_cache, block_table, H, d_c)
+    _invoke("mla_decode_attn_multi",
+        _dev(q_lat, "q_lat", None, 4), _dev(q_pe, "q_pe", None, 4),
+        _dev(kv_cache, "kv_cache", None, 3), _dev(block_table, "block_table", torch.int32, 2),
+        _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), n_q, float(softmax_scale),
+        S, _dev(o_part, "o_part"), _dtype_code(o_part), _dev(lse_part, "lse_part", torch.float32),
+        _dtype_code(q_lat), _stream(stream))
 
 def mla_splitk_combine(o_part, lse_part, out, lse_out=None, stream=None):
     """Log-sum-exp combine of float32 or bfloat16 partials o_part [B,H,S,d_c] into out [B,H,d_c]."""

@@ -19,22 +19,23 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(
     const T* __restrict__ q_lat, const T* __restrict__ q_pe, const T* __restrict__ cache,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int H,
     int P, int max_pages, int pages_per_split, int S, float scale_log2, OT* __restrict__ o_part,
-    float* __restrict__ lse_part) {
+    float* __restrict__ lse_part, int n_q) {
   static_assert(DR <= 64, "rope part must fit one lane each");
   constexpr int ROW = DC + DR;
   constexpr int NC = (DC + 63) / 64;
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // query row bq = b n_q + t: token t of sequence b, at position seq_len - n_q + t
+  const int s = blockIdx.x, h = blockIdx.y, bq = blockIdx.z, b = bq / n_q, t = bq - b * n_q;
   const int lane = threadIdx.x;
 
   float qc[NC];
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     const int idx = lane + 64 * k;
-    qc[k] = idx < DC ? ld(q_lat + (static_cast<int64_t>(b) * H + h) * DC + idx) : 0.f;
+    qc[k] = idx < DC ? ld(q_lat + (static_cast<int64_t>(bq) * H + h) * DC + idx) : 0.f;
   }
-  const float qr = lane < DR ? ld(q_pe + (static_cast<int64_t>(b) * H + h) * DR + lane) : 0.f;
+  const float qr = lane < DR ? ld(q_pe + (static_cast<int64_t>(bq) * H + h) * DR + lane) : 0.f;
 
-  const int L = seq_lens[b];
+  const int L = seq_lens[b] - (n_q - 1 - t);
   const int j0 = s * pages_per_split * P;
   const int j1 = min(L, (s + 1) * pages_per_split * P);
   const int32_t* bt = block_table + static_cast<int64_t>(b) * max_pages;
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(
     m = mn;
   }
 
-  const int64_t ob = (static_cast<int64_t>(b) * H + h) * S + s;
+  const int64_t ob = (static_cast<int64_t>(bq) * H + h) * S + s;
   const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
@@ -81,12 +82,13 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(
 
 template <typename T, typename OT, int DC, int DR>
 static hipError_t launch_generic_t(const PagedArgs& a, hipStream_t st) {
-  dim3 grid(a.num_splits, a.H, a.B);
+  dim3 grid(a.num_splits, a.H, a.B * a.n_q);
   hipLaunchKernelGGL((attn_generic_kernel<T, OT, DC, DR>), grid, dim3(64), 0, st,
                      static_cast<const T*>(a.q_lat), static_cast<const T*>(a.q_pe),
                      static_cast<const T*>(a.cache), a.block_table, a.seq_lens, a.H,
                      a.page_size, a.max_pages, a.pages_per_split, a.num_splits,
-                     a.scale * 1.4426950408889634f, static_cast<OT*>(a.o_part), a.lse_part);
+                     a.scale * 1.4426950408889634f, static_cast<OT*>(a.o_part), a.lse_part,
+                     a.n_q);
   return hipGetLastError();
 }
 

@@ -149,7 +149,7 @@ template <typename OT>
 __device__ void split_exact_fallback(const bf16raw* __restrict__ q_lat,
                                      const bf16raw* __restrict__ q_pe,
                                      const bf16raw* __restrict__ cache, const int32_t* bt_row,
-                                     int log2P, int j0, int j1, int b, int H,
+                                     int log2P, int j0, int j1, int bq, int H,
                                      int S, int s, float scale_log2, OT* __restrict__ o_part,
                                      float* __restrict__ lse_part, int h_begin, int n_heads,
                                      int lane) {
@@ -159,8 +159,8 @@ __device__ void split_exact_fallback(const bf16raw* __restrict__ q_lat,
 #pragma unroll
     for (int f = 0; f < 9; ++f) {
       const int k = 9 * lane + f;
-      q[f] = k < DC ? bf16_to_f32(q_lat[(static_cast<int64_t>(b) * H + h) * DC + k])
-                    : bf16_to_f32(q_pe[(static_cast<int64_t>(b) * H + h) * DR + (k - DC)]);
+      q[f] = k < DC ? bf16_to_f32(q_lat[(static_cast<int64_t>(bq) * H + h) * DC + k])
+                    : bf16_to_f32(q_pe[(static_cast<int64_t>(bq) * H + h) * DR + (k - DC)]);
     }
     float m = -INFINITY, l = 0.f, acc[8];
 #pragma unroll
@@ -180,7 +180,7 @@ __device__ void split_exact_fallback(const bf16raw* __restrict__ q_lat,
       for (int k = 0; k < 8; ++k) acc[k] = acc[k] * alpha + p * bf16_to_f32(row[lane + 64 * k]);
       m = mn;
     }
-    const int64_t ob = (static_cast<int64_t>(b) * H + h) * S + s;
+    const int64_t ob = (static_cast<int64_t>(bq) * H + h) * S + s;
 #pragma unroll
     for (int k = 0; k < 8; ++k) st(o_part + ob * DC + lane + 64 * k, acc[k] / l);
     if (lane == 0 && lse_part != nullptr) lse_part[ob] = (m + __log2f(l)) * LN2;
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     const bf16raw* __restrict__ q_lat, const bf16raw* __restrict__ q_pe,
     const bf16raw* __restrict__ cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int H, int log2P, int max_pages, int pages_per_split,
-    int S, float scale_log2, OT* __restrict__ o_part, float* __restrict__ lse_part) {
+    int S, float scale_log2, OT* __restrict__ o_part, float* __restrict__ lse_part, int n_q) {
   constexpr int NT = NW * 64;
   constexpr int NCT = DC / 16;                                    // PV column tiles
   constexpr int STEPS = KSTEPS * 2;                               // score MFMA steps per tile
@@ -216,7 +216,10 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   // Consecutive workgroup ids go to the 8 XCDs in turn; with the sequence index in x, all
   // splits of a sequence (ids b, b + B, ...) land on XCD b % 8 when B % 8 == 0, so the
   // sequence's queries are fetched once into that XCD's L2.
-  const int b = blockIdx.x, s = blockIdx.y;
+  // Several query tokens per sequence (n_q > 1): token t = blockIdx.z sits at position
+  // seq_len - n_q + t and sees the cache up to it; its queries and outputs are row
+  // bq = b n_q + t.  Its workgroups share the sequence's XCD and read the same tiles.
+  const int b = blockIdx.x, s = blockIdx.y, bq = b * n_q + blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
@@ -224,17 +227,17 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   const int h0 = 16 * w;   // heads of this wave
   const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_pages;
 
-  const int L = seq_lens[b];
+  const int L = seq_lens[b] - (n_q - 1 - static_cast<int>(blockIdx.z));
   const int j0 = s * pages_per_split * P;
   const int j1 = min(L, j0 + pages_per_split * P);
 
   if (j0 >= j1) {  // empty split: o = 0, lse = -inf
     for (int e = tid; e < H * DC; e += NT) {
       const int h = e / DC, c = e % DC;
-      st(o_part + ((static_cast<int64_t>(b) * H + h) * S + s) * DC + c, 0.f);
+      st(o_part + ((static_cast<int64_t>(bq) * H + h) * S + s) * DC + c, 0.f);
     }
     if (lse_part != nullptr)
-      for (int h = tid; h < H; h += NT) lse_part[(static_cast<int64_t>(b) * H + h) * S + s] = -INFINITY;
+      for (int h = tid; h < H; h += NT) lse_part[(static_cast<int64_t>(bq) * H + h) * S + s] = -INFINITY;
     return;
   }
 
@@ -470,8 +473,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   // (and, being issued after them, for this wave's copies of the first tile), so the two
   // latencies overlap and no compiler-inserted wait falls after a later copy.
   auto load_query = [&]() {
-    const bf16raw* qrow = q_lat + (static_cast<int64_t>(b) * H + h0 + r16) * DC + 8 * g;
-    const bf16raw* prow = q_pe + (static_cast<int64_t>(b) * H + h0 + r16) * DR + 8 * g;
+    const bf16raw* qrow = q_lat + (static_cast<int64_t>(bq) * H + h0 + r16) * DC + 8 * g;
+    const bf16raw* prow = q_pe + (static_cast<int64_t>(bq) * H + h0 + r16) * DR + 8 * g;
     i32x4_t r[KSTEPS];
     asm volatile("global_load_dwordx4 %0, %18, off\n\tglobal_load_dwordx4 %1, %18, off offset:64\n\tglobal_load_dwordx4 %2, %18, off offset:128\n\tglobal_load_dwordx4 %3, %18, off offset:192\n\tglobal_load_dwordx4 %4, %18, off offset:256\n\tglobal_load_dwordx4 %5, %18, off offset:320\n\tglobal_load_dwordx4 %6, %18, off offset:384\n\tglobal_load_dwordx4 %7, %18, off offset:448\n\tglobal_load_dwordx4 %8, %18, off offset:512\n\tglobal_load_dwordx4 %9, %18, off offset:576\n\tglobal_load_dwordx4 %10, %18, off offset:640\n\tglobal_load_dwordx4 %11, %18, off offset:704\n\tglobal_load_dwordx4 %12, %18, off offset:768\n\tglobal_load_dwordx4 %13, %18, off offset:832\n\tglobal_load_dwordx4 %14, %18, off offset:896\n\tglobal_load_dwordx4 %15, %18, off offset:960\n\tglobal_load_dwordx4 %16, %19, off\n\tglobal_load_dwordx4 %17, %19, off offset:64\n\ts_waitcnt vmcnt(0)"
                  : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15]), "=&v"(r[16]), "=&v"(r[17])
@@ -485,8 +488,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   // but them: two tiles are then in flight while the queries arrive.  A one-tile split
   // copies its tile again into the unused second buffer, so the wait counts stay alike.
   auto load_query_tile1 = [&]() {
-    const bf16raw* qrow = q_lat + (static_cast<int64_t>(b) * H + h0 + r16) * DC + 8 * g;
-    const bf16raw* prow = q_pe + (static_cast<int64_t>(b) * H + h0 + r16) * DR + 8 * g;
+    const bf16raw* qrow = q_lat + (static_cast<int64_t>(bq) * H + h0 + r16) * DC + 8 * g;
+    const bf16raw* prow = q_pe + (static_cast<int64_t>(bq) * H + h0 + r16) * DR + 8 * g;
     const int tb1 = ntiles > 1 ? j0 + TILE : j0;
     const unsigned last1 = static_cast<unsigned>(j1 - 1 - tb1);
     const uint64_t b64 = reinterpret_cast<uint64_t>(tile_base(tb1));
@@ -562,7 +565,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   // ---- epilogue: normalise and write four consecutive columns per lane; a head block
   //      whose scores left the reference range is recomputed exactly
   if (!__any(out_of_range)) {
-    const int64_t row = (static_cast<int64_t>(b) * H + h0 + r16) * S + s;
+    const int64_t row = (static_cast<int64_t>(bq) * H + h0 + r16) * S + s;
     if (lse_part != nullptr && g == 0) lse_part[row] = (m_ref + __log2f(l_acc[0])) * LN2;
     const float inv = 1.f / l_acc[0];
     if constexpr (std::is_same<OT, float>::value) {
@@ -592,7 +595,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
       }
     }
   } else {
-    split_exact_fallback(q_lat, q_pe, cache, bt_row, log2P, j0, j1, b, H, S, s, scale_log2,
+    split_exact_fallback(q_lat, q_pe, cache, bt_row, log2P, j0, j1, bq, H, S, s, scale_log2,
                          o_part, lse_part, h0, 16, lane);
   }
 }
@@ -600,12 +603,12 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
 template <int NW, typename OT>
 hipError_t launch_nw_t(const PagedArgs& a, hipStream_t st) {
   const float log2e = 1.4426950408889634f;
-  hipLaunchKernelGGL((attn_mfma_kernel<NW, OT>), dim3(a.B, a.num_splits), dim3(NW * 64), 0, st,
+  hipLaunchKernelGGL((attn_mfma_kernel<NW, OT>), dim3(a.B, a.num_splits, a.n_q), dim3(NW * 64), 0, st,
                      static_cast<const bf16raw*>(a.q_lat), static_cast<const bf16raw*>(a.q_pe),
                      static_cast<const bf16raw*>(a.cache), a.block_table, a.seq_lens, a.H,
                      __builtin_ctz(static_cast<unsigned>(a.page_size)), a.max_pages,
                      a.pages_per_split, a.num_splits, a.scale * log2e,
-                     static_cast<OT*>(a.o_part), a.lse_part);
+                     static_cast<OT*>(a.o_part), a.lse_part, a.n_q);
   return hipGetLastError();
 }
 
@@ -623,7 +626,7 @@ bool attn_mfma_supported(const PagedArgs& a) {
   if (a.pages_per_split > MAX_SPLIT_PAGES) return false;
   const bool page_ok = a.page_size >= TILE && (a.page_size & (a.page_size - 1)) == 0;
   return a.d_c == DC && a.d_R == DR && heads_ok && page_ok &&
-         a.B <= 65535 && aligned16(a.q_lat) &&
+         a.B <= 65535 && a.n_q >= 1 && a.n_q <= 65535 && aligned16(a.q_lat) &&
          aligned16(a.q_pe) && aligned16(a.cache);
 }
 

@@ -21,6 +21,7 @@ struct PagedArgs {
   void* o_part;      // fp32 or bf16 (part_bf16), [B][H][S][d_c]
   int part_bf16;     // 1: o_part elements are bf16 (round to nearest even)
   float* lse_part;
+  int32_t n_q;       // query tokens per sequence (rows b n_q + t of q and of the partials)
 };
 
 // Decode attention, one wavefront per (sequence, head, split), fp32 VALU math.

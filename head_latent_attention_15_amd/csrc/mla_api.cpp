@@ -133,11 +133,12 @@ int32_t mla_suggest_num_splits(int32_t B, int32_t max_seq_len, int64_t total_tok
   return static_cast<int32_t>(S);
 }
 
-mla_status_t mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_cache,
+// Decode attention for n_q query tokens per sequence (1 for plain decode).
+static mla_status_t decode_attn(const void* q_lat, const void* q_pe, const void* kv_cache,
                              const int32_t* block_table, const int32_t* seq_lens,
                              const mla_paged_shape_t* shape, float softmax_scale,
                              int32_t num_splits, void* o_part, mla_dtype_t part_dtype,
-                             float* lse_part, mla_dtype_t dtype, void* stream) {
+                             float* lse_part, mla_dtype_t dtype, int32_t n_q, void* stream) {
   if (!q_lat || !q_pe || !kv_cache || !block_table || !seq_lens || !o_part)
     return fail(MLA_ERR_NULL, "mla_decode_attn: a required pointer is NULL");
   mla_status_t st = check_paged_shape(shape);
@@ -151,6 +152,8 @@ mla_status_t mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv
   if (!is_dtype(dtype)) return fail(MLA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
   if (!is_dtype(part_dtype))
     return fail(MLA_ERR_UNSUPPORTED, "unknown partial dtype %d", part_dtype);
+  if (n_q < 1 || static_cast<int64_t>(shape->batch) * n_q > 65535)
+    return fail(MLA_ERR_SHAPE, "n_q %d outside [1, 65535 / batch]", n_q);
 
   mla::PagedArgs a;
   a.q_lat = q_lat;
@@ -171,6 +174,7 @@ mla_status_t mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv
   a.o_part = o_part;
   a.part_bf16 = part_dtype == MLA_BF16;
   a.lse_part = lse_part;
+  a.n_q = n_q;
   hipStream_t s = as_stream(stream);
 
   if (dtype == MLA_BF16 && a.d_c == 512 && a.d_R == 64 && a.H <= 128) {
@@ -184,6 +188,25 @@ mla_status_t mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv
               "mla_decode_attn: (d_latent=%d, d_rope=%d, H=%d, dtype=%d) is not compiled; "
               "supported: (512, 64, H<=128, BF16) and (64, 16, H<=64, F32)",
               a.d_c, a.d_R, a.H, dtype);
+}
+
+mla_status_t mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_cache,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const mla_paged_shape_t* shape, float softmax_scale,
+                             int32_t num_splits, void* o_part, mla_dtype_t part_dtype,
+                             float* lse_part, mla_dtype_t dtype, void* stream) {
+  return decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, shape, softmax_scale,
+                     num_splits, o_part, part_dtype, lse_part, dtype, 1, stream);
+}
+
+mla_status_t mla_decode_attn_multi(const void* q_lat, const void* q_pe, const void* kv_cache,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   const mla_paged_shape_t* shape, int32_t n_q,
+                                   float softmax_scale, int32_t num_splits, void* o_part,
+                                   mla_dtype_t part_dtype, float* lse_part, mla_dtype_t dtype,
+                                   void* stream) {
+  return decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, shape, softmax_scale,
+                     num_splits, o_part, part_dtype, lse_part, dtype, n_q, stream);
 }
 
 mla_status_t mla_splitk_combine(const void* o_part, mla_dtype_t part_dtype,

@@ -154,6 +154,27 @@ mla_status_t mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv
                              int32_t num_splits, void* o_part, mla_dtype_t part_dtype,
                              float* lse_part, mla_dtype_t dtype, void* stream);
 
+/* Decode attention for n_q new query tokens per sequence (speculative or multi-token
+ * decode), all already appended to the cache: token t (0..n_q-1) of sequence b sits at
+ * position seq_lens[b] - n_q + t and attends to the cached tokens 0 .. that position, so
+ * the new tokens see each other causally (qiita "Attention 計算": the sum over tokens runs
+ * up to the query's own position).  Each (b, t) is a decode query as in mla_decode_attn
+ * with seq_len seq_lens[b] - n_q + 1 + t; rows are numbered bq = b*n_q + t:
+ *   q_lat [B][n_q][H][d_latent], q_pe [B][n_q][H][d_rope]: `dtype`
+ *   o_part [B][n_q][H][S][d_latent] in part_dtype, lse_part [B][n_q][H][S] fp32
+ * so mla_splitk_combine with batch B*n_q merges the splits.  A token whose position is
+ * negative (seq_lens[b] < n_q - t) sees no tokens: o = 0, lse = -inf.  n_q = 1 is
+ * mla_decode_attn.  The n_q workgroups of one (sequence, split) read the same cache
+ * tiles at about the same time from the same XCD, so the extra tokens cost L2 reads,
+ * not HBM reads.
+ * Errors: as mla_decode_attn, plus SHAPE for n_q < 1 or B*n_q > 65535. */
+mla_status_t mla_decode_attn_multi(const void* q_lat, const void* q_pe, const void* kv_cache,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   const mla_paged_shape_t* shape, int32_t n_q,
+                                   float softmax_scale, int32_t num_splits, void* o_part,
+                                   mla_dtype_t part_dtype, float* lse_part, mla_dtype_t dtype,
+                                   void* stream);
+
 /* Log-sum-exp combine of split partials (exact re-assembly of one softmax whose sum
  * over tokens was cut into disjoint ranges; qiita "Attention 計算").
  *   M = max_s lse_s; w_s = e^{lse_s - M} (0 for lse_s = -inf)

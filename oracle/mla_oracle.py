@@ -299,6 +299,31 @@ def paged_decode(q_lat, q_pe, cache, block_table, seq_lens, d_c: int, scale):
     return o, lse
 
 
+def paged_decode_multi(q_lat, q_pe, cache, block_table, seq_lens, n_q: int, d_c: int, scale):
+    """Latent attention for n_q new query tokens per sequence, all already in the cache.
+    Query t of sequence b sits at position seq_lens[b] - n_q + t and attends to the cached
+    tokens 0 .. that position: the sum over tokens runs up to the query's own position
+    ([qiita] "Attention 計算"), so the new tokens see each other causally.
+    q_lat [B, n_q, H, d_c], q_pe [B, n_q, H, d_R].
+    Returns o_lat [B, n_q, H, d_c], lse [B, n_q, H] (no visible token: o = 0, lse = -inf)."""
+    q_lat, q_pe = _f64(q_lat), _f64(q_pe)
+    B, nq, H, _ = q_lat.shape
+    if nq != n_q:
+        raise ValueError("q_lat must hold n_q tokens per sequence")
+    P = np.asarray(cache).shape[1]
+    o = np.zeros((B, n_q, H, d_c), dtype=F64)
+    lse = np.full((B, n_q, H), -np.inf, dtype=F64)
+    for b in range(B):
+        for t in range(n_q):
+            visible = int(seq_lens[b]) - n_q + t + 1   # tokens 0 .. position of query t
+            if visible <= 0:
+                continue
+            rows = gather_rows(cache, block_table[b], visible, P)
+            att = latent_attention(q_lat[b, t], q_pe[b, t], rows, d_c, scale)
+            o[b, t], lse[b, t] = att["o_lat"], att["lse"]
+    return o, lse
+
+
 # --------------------------------------------------------------------------------------
 # Projections and the full decode layer
 # --------------------------------------------------------------------------------------

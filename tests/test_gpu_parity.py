@@ -188,6 +188,70 @@ def test_ragged_b128_sampled(mla):
     print(f"ragged_b128 sample {pick}: max-abs {m:.3e} rel-L2 {r:.3e}")
 
 
+# ------------------------------------------------------------------ multi-token decode
+def run_attention_multi(mla, inp, q_lat, q_pe, n_q, S, part=torch.float32):
+    """mla_decode_attn_multi (+ combine over B n_q rows for S > 1)."""
+    cache, bt, sl = dev(inp["cache"]), dev(inp["block_table"]), dev(inp["seq_lens"])
+    B, _, H, d_c = q_lat.shape
+    ql, qp = dev(q_lat), dev(q_pe)
+    if S == 1:
+        out = torch.empty(B, n_q, H, d_c, device="cuda")
+        mla.mla_decode_attn_multi(ql, qp, cache, bt, sl, inp["scale"], 1, out, None)
+    else:
+        o_part = torch.empty(B, n_q, H, S, d_c, device="cuda", dtype=part)
+        lse_part = torch.empty(B, n_q, H, S, device="cuda")
+        mla.mla_decode_attn_multi(ql, qp, cache, bt, sl, inp["scale"], S, o_part, lse_part)
+        out = torch.empty(B * n_q, H, d_c, device="cuda")
+        mla.mla_splitk_combine(o_part.view(B * n_q, H, S, d_c), lse_part.view(B * n_q, H, S), out)
+        out = out.view(B, n_q, H, d_c)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("H", [128, 20], ids=["mfma", "generic"])
+def test_multi_token_decode(mla, H):
+    """n_q new tokens per sequence, causal among them, against the oracle: ragged lengths
+    over permuted pages, one sequence shorter than n_q (its first query sees nothing and
+    returns exactly 0), split counts 1, 3 and 8 with fp32 and bf16 partials; n_q = 1 equals
+    mla_decode_attn bit for bit."""
+    n_q = 3
+    inp = W.paged_attention(40 + H, B=4, H=H, seq_lens=[2, 97, 700, 1537])
+    g = torch.Generator().manual_seed(41)
+    q_lat = torch.randn(4, n_q, H, 512, generator=g).to(torch.bfloat16)
+    q_pe = torch.randn(4, n_q, H, 64, generator=g).to(torch.bfloat16)
+    cache64 = W.to_f64(inp["cache"])
+    o_ref, _ = oracle.paged_decode_multi(W.to_f64(q_lat), W.to_f64(q_pe), cache64,
+                                         inp["block_table"].numpy(), inp["seq_lens"].numpy(),
+                                         n_q, 512, inp["scale"])
+    for S, part in [(1, torch.float32), (3, torch.float32), (8, torch.bfloat16)]:
+        say(f"multi-token decode H={H} n_q={n_q} S={S} part={part}")
+        out = run_attention_multi(mla, inp, q_lat, q_pe, n_q, S, part)
+        assert_bf16(host64(out), o_ref, f"S={S}")
+        assert float(out[0, 0].abs().max()) == 0.0  # position -1: no visible token
+    say(f"multi-token decode H={H} n_q=1 vs single")
+    one = run_attention_multi(mla, inp, q_lat[:, :1], q_pe[:, :1], 1, 4)
+    single = dict(inp, q_lat=q_lat[:, 0].contiguous(), q_pe=q_pe[:, 0].contiguous())
+    ref_one, _ = run_attention(mla, single, 4)
+    assert torch.equal(one[:, 0], ref_one)
+
+
+def test_multi_token_decode_fp32(mla):
+    """The fp32 shape (d_c = 64, d_R = 16, H = 4) with n_q = 4: max-abs <= 1e-5."""
+    n_q = 4
+    inp = W.paged_attention(42, B=2, H=4, seq_lens=[5, 300], d_c=64, d_R=16, d_h=32,
+                            dtype=torch.float32)
+    g = torch.Generator().manual_seed(43)
+    q_lat = torch.randn(2, n_q, 4, 64, generator=g)
+    q_pe = torch.randn(2, n_q, 4, 16, generator=g)
+    o_ref, _ = oracle.paged_decode_multi(W.to_f64(q_lat), W.to_f64(q_pe), W.to_f64(inp["cache"]),
+                                         inp["block_table"].numpy(), inp["seq_lens"].numpy(),
+                                         n_q, 64, inp["scale"])
+    for S in (1, 2):
+        say(f"multi-token decode fp32 n_q={n_q} S={S}")
+        out = run_attention_multi(mla, inp, q_lat, q_pe, n_q, S)
+        assert_fp32(host64(out), o_ref, what=f"S={S}")
+
+
 # ------------------------------------------------------------------ indexing exactness
 def _spike_problem(B, H, seq_lens, spikes, seed=7):
     """q~ = 0, q_pe = 64 e_0; the rope part of every row is 0 except row j* of each

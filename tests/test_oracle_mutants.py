@@ -31,6 +31,8 @@ PIN_TESTS = [
     pins.test_gather_permuted_pool_equals_contiguous,
     pins.test_append_then_gather,
     pins.test_paged_decode_matches_per_sequence_sdpa,
+    pins.test_multi_token_decode_is_causal_sdpa,
+    pins.test_multi_token_decode_reduces_to_single,
     pins.test_layer_single_token_closed_form,
     pins.test_layer_matches_sdpa_composition,
     pins.test_cache_sizes_from_pages,
@@ -111,6 +113,26 @@ def _absorb_no_transpose(q_c, w_uk):
     return out
 
 
+def _multi_decode(visible_of):
+    """paged_decode_multi with another rule for the tokens a query sees"""
+    def f(q_lat, q_pe, cache, block_table, seq_lens, n_q, d_c, scale):
+        q_lat, q_pe = np.asarray(q_lat, float), np.asarray(q_pe, float)
+        B, _, H, _ = q_lat.shape
+        P = np.asarray(cache).shape[1]
+        o = np.zeros((B, n_q, H, d_c))
+        lse = np.full((B, n_q, H), -np.inf)
+        for b in range(B):
+            for t in range(n_q):
+                v = visible_of(int(seq_lens[b]), n_q, t)
+                if v <= 0:
+                    continue
+                att = M.latent_attention(q_lat[b, t], q_pe[b, t],
+                                         M.gather_rows(cache, block_table[b], v, P), d_c, scale)
+                o[b, t], lse[b, t] = att["o_lat"], att["lse"]
+        return o, lse
+    return f
+
+
 M_rope_orig = M.rope
 M_softmax_orig = M.softmax
 M_lse_orig = M.logsumexp
@@ -127,6 +149,10 @@ MUTANTS = {
     "cache_bytes_k_and_v": ("cache_bytes", _cache_bytes_kv_twice),
     "lse_in_log2": ("logsumexp", _logsumexp_log2),
     "absorb_reversed_index": ("absorb_query", _absorb_no_transpose),
+    "multi_query_misses_itself": ("paged_decode_multi", _multi_decode(lambda L, n, t: L - n + t)),
+    "multi_query_not_causal": ("paged_decode_multi", _multi_decode(lambda L, n, t: L)),
+    "multi_query_tokens_reversed": ("paged_decode_multi",
+                                    _multi_decode(lambda L, n, t: L - t)),
 }
 
 

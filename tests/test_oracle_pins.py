@@ -291,6 +291,60 @@ def test_paged_decode_matches_per_sequence_sdpa():
         assert np.allclose(o[b], ref, atol=1e-13)
 
 
+def test_multi_token_decode_is_causal_sdpa():
+    """n_q new tokens per sequence: torch SDPA in fp64 with a boolean mask that lets query t
+    see the cached tokens up to its own position (seq_len - n_q + t), over the gathered
+    paged rows; pages permuted, one sequence shorter than n_q (its first query sees
+    nothing: o = 0, lse = -inf)."""
+    r = _rng(12)
+    P, d_c, d_R, H, n_q = 4, 6, 2, 3, 3
+    seq_lens = [7, 3, 2]
+    pool = r.standard_normal((6, P, d_c + d_R))
+    bt = np.array([[4, 0], [5, -1], [2, -1]])
+    q_lat, q_pe = r.standard_normal((3, n_q, H, d_c)), r.standard_normal((3, n_q, H, d_R))
+    o, lse = oracle.paged_decode_multi(q_lat, q_pe, pool, bt, seq_lens, n_q, d_c, 0.45)
+    for b, L in enumerate(seq_lens):
+        rows = np.concatenate([pool[bt[b, j // P], j % P][None] for j in range(L)])
+        for t in range(n_q):
+            pos = L - n_q + t
+            if pos < 0:
+                assert np.all(o[b, t] == 0) and np.all(lse[b, t] == -np.inf)
+                continue
+            q = torch.from_numpy(np.concatenate([q_lat[b, t], q_pe[b, t]], 1)[:, None])[None]
+            k = torch.from_numpy(np.broadcast_to(rows, (H, L, d_c + d_R)).copy())[None]
+            v = torch.from_numpy(np.broadcast_to(rows[:, :d_c], (H, L, d_c)).copy())[None]
+            mask = torch.arange(L)[None, :] <= pos          # [1, L]: keys up to the query
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q, k, v, attn_mask=mask, scale=0.45)[0, :, 0].numpy()
+            assert np.allclose(o[b, t], ref, rtol=0, atol=1e-13), (b, t)
+
+
+def test_multi_token_decode_reduces_to_single():
+    """n_q = 1 is paged_decode; the last of n_q tokens sees the whole sequence, so it equals
+    paged_decode at the same lengths exactly; rows past a query's position do not change it."""
+    r = _rng(13)
+    P, d_c, d_R, H = 4, 5, 2, 2
+    seq_lens = [9, 6]
+    pool = r.standard_normal((6, P, d_c + d_R))
+    bt = np.array([[3, 0, 5], [1, 4, -1]])
+    q1, p1 = r.standard_normal((2, 1, H, d_c)), r.standard_normal((2, 1, H, d_R))
+    o1, l1 = oracle.paged_decode_multi(q1, p1, pool, bt, seq_lens, 1, d_c, 0.5)
+    o_ref, l_ref = oracle.paged_decode(q1[:, 0], p1[:, 0], pool, bt, seq_lens, d_c, 0.5)
+    assert np.array_equal(o1[:, 0], o_ref) and np.array_equal(l1[:, 0], l_ref)
+    n_q = 4
+    q4, p4 = r.standard_normal((2, n_q, H, d_c)), r.standard_normal((2, n_q, H, d_R))
+    o4, l4 = oracle.paged_decode_multi(q4, p4, pool, bt, seq_lens, n_q, d_c, 0.5)
+    o_last, l_last = oracle.paged_decode(q4[:, -1], p4[:, -1], pool, bt, seq_lens, d_c, 0.5)
+    assert np.array_equal(o4[:, -1], o_last) and np.array_equal(l4[:, -1], l_last)
+    # overwrite the last cached token of sequence 0: only its last query may change
+    pool2 = pool.copy()
+    j = seq_lens[0] - 1
+    pool2[bt[0, j // P], j % P] = r.standard_normal(d_c + d_R) * 5
+    o5, _ = oracle.paged_decode_multi(q4, p4, pool2, bt, seq_lens, n_q, d_c, 0.5)
+    assert np.array_equal(o5[0, :-1], o4[0, :-1]) and not np.allclose(o5[0, -1], o4[0, -1])
+    assert np.array_equal(o5[1], o4[1])
+
+
 # ---------------------------------------------------------------- full layer
 def _tiny_layer(seed, B=2, d=12, H=2, d_h=3, d_c=5, d_cq=4, d_R=2, T=6, P=4):
     r = _rng(seed)

@@ -125,6 +125,14 @@ def dsv2_b32_t4k(seed: int = 2, B: int = 32, T: int = 4096, H: int = 128):
             "shape": Shape(B=B, H=H, d_c=512, d_R=64), "scale": 1.0 / math.sqrt(192)}
 
 
+def multi_queries(seed: int, B: int, n_q: int, H: int, d_c: int = 512, d_R: int = 64,
+                  dtype=torch.bfloat16):
+    """Absorbed queries for n_q new tokens per sequence (multi-token decode): q~
+    [B, n_q, H, d_c] and q_pe [B, n_q, H, d_R] ~ N(0,1), drawn in that order."""
+    g = _gen(seed)
+    return _normal(g, (B, n_q, H, d_c), dtype=dtype), _normal(g, (B, n_q, H, d_R), dtype=dtype)
+
+
 def long_b4_t32k(seed: int = 3, B: int = 4, T: int = 32768, H: int = 128):
     """Long context: seq b reads pages perm[512b .. 512b+511] of a 2048-page pool.
     Draw order: permutation, cache, q_lat, q_pe."""
