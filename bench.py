@@ -169,6 +169,29 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
                      "roofline_frac": round(gbps / HBM_PEAK_GBPS, 4)}
         total_bytes += byts
     chain_us = timed(lambda: [c() for c in chain])
+
+    # the survey's fourth next item, measured only: offline absorption folds W^UK_i^T into
+    # W^UQ_i ([H d_c, d_c^Q], 201 MB of bf16 weights, prepared once here in fp32 and rounded
+    # once), so q~ = W~ c^Q is one projection instead of W^UQ plus the absorption
+    wuk = w["w_uk"].float().view(H, d_h, d_c).transpose(1, 2).contiguous()
+    wuq = w["w_uq"].float().view(H, d_h, d_cq)
+    w_off = torch.bmm(wuk, wuq).to(torch.bfloat16).view(H * d_c, d_cq)
+    del wuk, wuq
+    q_off = torch.empty(B, H * d_c, **f32)
+    off_us = timed(lambda: mla.mla_linear(c_q, w_off, q_off))
+    rt_calls = [mla.bind(mla.mla_linear, c_q, w["w_uq"], q_c),
+                mla.bind(mla.mla_absorb_q, q_c.view(B, H, d_h), w["w_uk"], None, seq_lens,
+                         x["rope_base"], q_lat, None)]
+    rt_us = timed(lambda: [c() for c in rt_calls])
+    off_bytes = nb(w_off) + nb(c_q) + nb(q_off)
+    out["next-4 offline absorption (measure only)"] = {
+        "us": round(off_us, 2), "bytes_algorithmic": int(off_bytes),
+        "GBps": round(off_bytes / off_us / 1e3, 1),
+        "roofline_frac": round(off_bytes / off_us / 1e3 / HBM_PEAK_GBPS, 4),
+        "runtime_absorption_us": round(rt_us, 2),
+        "note": "q~ = (W^UK^T W^UQ) c^Q in one mla_linear; runtime_absorption_us = W^UQ + "
+                "mla_absorb_q on the same input"}
+    del w_off, q_off
     res = {"workload": "layer_b64_t2k (d=5120, H=128, d_h=128, d_c=512, d_c^Q=1536, d_R=64, "
                        "B=64, 2048 cached tokens + 1, bf16 weights and cache)",
            "steps": out, "chain_us": round(chain_us, 2), "chain_bytes_algorithmic": int(total_bytes),

@@ -619,6 +619,28 @@ def test_linear_planned_kernels(mla):
     assert float(y.abs().max()) == 0.0
 
 
+def test_offline_absorption_gemm(mla):
+    """Offline absorption (W~_i = W^UK_i^T W^UQ_i, prepared once in fp64 and rounded to
+    bf16) through mla_linear gives the absorbed query of the oracle (W^UK_i^T (W^UQ c^Q)_i
+    in fp64) within the bf16 bar: the weight is the only rounding."""
+    g = torch.Generator().manual_seed(35)
+    B, H, d_h, d_c, d_cq = 8, 4, 128, 512, 1536
+    say("offline absorption")
+    c_q = torch.randn(B, d_cq, generator=g)
+    w_uq = (torch.randn(H * d_h, d_cq, generator=g) / math.sqrt(d_cq)).to(torch.bfloat16)
+    w_uk = (torch.randn(H * d_h, d_c, generator=g) / math.sqrt(d_h)).to(torch.bfloat16)
+    wuk, wuq = W.to_f64(w_uk), W.to_f64(w_uq)
+    w_off = np.concatenate([wuk[i * d_h:(i + 1) * d_h].T @ wuq[i * d_h:(i + 1) * d_h]
+                            for i in range(H)])
+    w_off = torch.from_numpy(w_off).to(torch.bfloat16)
+    y = torch.empty(B, H * d_c, device="cuda")
+    mla.mla_linear(dev(c_q), dev(w_off), y)
+    torch.cuda.synchronize()
+    q_c = oracle.linear(W.to_f64(c_q), wuq).reshape(B, H, d_h)
+    ref = np.stack([oracle.absorb_query(q_c[b], wuk) for b in range(B)]).reshape(B, H * d_c)
+    assert_bf16(host64(y), ref, "offline q~")
+
+
 def test_out_proj_full_size(mla):
     """W^UV per head (batched, strided) then W^O at the DeepSeek-V2 sizes, fp64 reference."""
     g = torch.Generator().manual_seed(32)
