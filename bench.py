@@ -103,16 +103,24 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     0.3 s warmup of the whole chain), its algorithmic bytes (weights, cache rows,
     activations in and out at their stored dtypes) and its fraction of the 8 TB/s HBM
     roofline (every step is HBM-bound at this batch); then the whole chain, and the fp64
-    oracle's layer on a few of the sequences."""
+    oracle's layer on a few of the sequences.  The projections that share an input run as
+    one product over their stacked weights ([W^DQ; W^DKV; W^KR] h, [W^UQ; W^QR] c^Q; the
+    weights are stacked once at load time, outside the timing) and the append and the
+    absorption read their inputs in place; the chain of separate products is timed beside
+    it."""
     x = W.layer_b64_t2k()
     s = x["shape"]
     B, H, d_h, d_c, d_R, d, d_cq = s.B, s.H, s.d_h, s.d_c, s.d_R, x["d"], x["d_cq"]
     cu = lambda t: t.to("cuda")
     w = {k: cu(v) for k, v in x["weights"].items()}
+    w_a = torch.cat([w["w_dq"], w["w_dkv"], w["w_kr"]]).contiguous()
+    w_b = torch.cat([w["w_uq"], w["w_qr"]]).contiguous()
     h, cache, bt, before = cu(x["h"]), cu(x["cache"]), cu(x["block_table"]), cu(x["seq_lens_before"])
     f32 = dict(device="cuda", dtype=torch.float32)
-    c_q, q_c, q_r = torch.empty(B, d_cq, **f32), torch.empty(B, H * d_h, **f32), torch.empty(B, H * d_R, **f32)
-    c_kv, k_r = torch.empty(B, d_c, **f32), torch.empty(B, d_R, **f32)
+    y_a = torch.empty(B, d_cq + d_c + d_R, **f32)
+    y_b = torch.empty(B, H * (d_h + d_R), **f32)
+    c_q, c_kv, k_r = y_a[:, :d_cq], y_a[:, d_cq:d_cq + d_c], y_a[:, d_cq + d_c:]
+    q_c, q_r = y_b[:, :H * d_h].view(B, H, d_h), y_b[:, H * d_h:].view(B, H, d_R)
     seq_lens = before + 1
     q_lat = torch.empty(B, H, d_c, device="cuda", dtype=torch.bfloat16)
     q_pe = torch.empty(B, H, d_R, device="cuda", dtype=torch.bfloat16)
@@ -122,18 +130,16 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     nb = lambda t: t.numel() * t.element_size()
     tokens = int(seq_lens.sum())
     rows = [
-        ("7 mla_linear (W^DQ, W^UQ, W^QR, W^DKV, W^KR)",
-         [mla.bind(mla.mla_linear, h, w["w_dq"], c_q), mla.bind(mla.mla_linear, c_q, w["w_uq"], q_c),
-          mla.bind(mla.mla_linear, c_q, w["w_qr"], q_r), mla.bind(mla.mla_linear, h, w["w_dkv"], c_kv),
-          mla.bind(mla.mla_linear, h, w["w_kr"], k_r)],
-         sum(nb(w[k]) for k in ("w_dq", "w_uq", "w_qr", "w_dkv", "w_kr")) + 3 * nb(h) + 2 * nb(c_q)
-         + nb(c_q) + nb(q_c) + nb(q_r) + nb(c_kv) + nb(k_r)),
-        ("2 mla_kv_append", [mla.bind(mla.mla_kv_append, c_kv.view(B, 1, d_c), k_r.view(B, 1, d_R),
-                                      before, bt, cache, x["rope_base"])],
-         nb(c_kv) + nb(k_r) + B * (d_c + d_R) * 2),
-        ("1 mla_absorb_q", [mla.bind(mla.mla_absorb_q, q_c.view(B, H, d_h), w["w_uk"], q_r.view(B, H, d_R),
-                                     seq_lens, x["rope_base"], q_lat, q_pe)],
-         nb(w["w_uk"]) + nb(q_c) + nb(q_r) + nb(q_lat) + nb(q_pe)),
+        ("7 mla_linear [W^DQ; W^DKV; W^KR] h",
+         [mla.bind(mla.mla_linear, h, w_a, y_a)], nb(w_a) + nb(h) + nb(y_a)),
+        ("7 mla_linear_strided [W^UQ; W^QR] c^Q",
+         [mla.bind(mla.mla_linear_strided, c_q, w_b, y_b)], nb(w_b) + B * d_cq * 4 + nb(y_b)),
+        ("2 mla_kv_append_strided", [mla.bind(mla.mla_kv_append_strided, c_kv.unsqueeze(1),
+                                              k_r.unsqueeze(1), before, bt, cache, x["rope_base"])],
+         B * (d_c + d_R) * 4 + B * (d_c + d_R) * 2),
+        ("1 mla_absorb_q_strided", [mla.bind(mla.mla_absorb_q_strided, q_c, w["w_uk"], q_r, seq_lens,
+                                             x["rope_base"], q_lat, q_pe)],
+         nb(w["w_uk"]) + B * H * (d_h + d_R) * 4 + nb(q_lat) + nb(q_pe)),
         (f"3+4 mla_decode (attention + combine, {S} splits)",
          [mla.bind(mla.mla_decode, q_lat, q_pe, cache, bt, seq_lens, x["scale"], S, ws, o_lat)],
          tokens * (d_c + d_R) * 2 + nb(q_lat) + nb(q_pe) + nb(o_lat)),
@@ -143,10 +149,24 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
          [mla.bind(mla.mla_linear, o_heads.view(B, H * d_h), w["w_o"], u)],
          nb(w["w_o"]) + nb(o_heads) + nb(u)),
     ]
+    # the same layer with one product per weight and dense intermediates
+    sep = {k: torch.empty(B, n, **f32) for k, n in
+           (("c_q", d_cq), ("q_c", H * d_h), ("q_r", H * d_R), ("c_kv", d_c), ("k_r", d_R))}
+    separate = [
+        mla.bind(mla.mla_linear, h, w["w_dq"], sep["c_q"]),
+        mla.bind(mla.mla_linear, sep["c_q"], w["w_uq"], sep["q_c"]),
+        mla.bind(mla.mla_linear, sep["c_q"], w["w_qr"], sep["q_r"]),
+        mla.bind(mla.mla_linear, h, w["w_dkv"], sep["c_kv"]),
+        mla.bind(mla.mla_linear, h, w["w_kr"], sep["k_r"]),
+        mla.bind(mla.mla_kv_append, sep["c_kv"].view(B, 1, d_c), sep["k_r"].view(B, 1, d_R),
+                 before, bt, cache, x["rope_base"]),
+        mla.bind(mla.mla_absorb_q, sep["q_c"].view(B, H, d_h), w["w_uk"], sep["q_r"].view(B, H, d_R),
+                 seq_lens, x["rope_base"], q_lat, q_pe),
+    ] + [c for _, calls, _ in rows[4:] for c in calls]
     chain = [c for _, calls, _ in rows for c in calls]
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < 0.3:
-        for c in chain:
+        for c in chain + separate:
             c()
         torch.cuda.synchronize()
 
@@ -169,6 +189,7 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
                      "roofline_frac": round(gbps / HBM_PEAK_GBPS, 4)}
         total_bytes += byts
     chain_us = timed(lambda: [c() for c in chain])
+    separate_us = timed(lambda: [c() for c in separate])
 
     # the survey's fourth next item, measured only: offline absorption folds W^UK_i^T into
     # W^UQ_i ([H d_c, d_c^Q], 201 MB of bf16 weights, prepared once here in fp32 and rounded
@@ -178,12 +199,12 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     w_off = torch.bmm(wuk, wuq).to(torch.bfloat16).view(H * d_c, d_cq)
     del wuk, wuq
     q_off = torch.empty(B, H * d_c, **f32)
-    off_us = timed(lambda: mla.mla_linear(c_q, w_off, q_off))
-    rt_calls = [mla.bind(mla.mla_linear, c_q, w["w_uq"], q_c),
-                mla.bind(mla.mla_absorb_q, q_c.view(B, H, d_h), w["w_uk"], None, seq_lens,
+    off_us = timed(lambda: mla.mla_linear(sep["c_q"], w_off, q_off))
+    rt_calls = [mla.bind(mla.mla_linear, sep["c_q"], w["w_uq"], sep["q_c"]),
+                mla.bind(mla.mla_absorb_q, sep["q_c"].view(B, H, d_h), w["w_uk"], None, seq_lens,
                          x["rope_base"], q_lat, None)]
     rt_us = timed(lambda: [c() for c in rt_calls])
-    off_bytes = nb(w_off) + nb(c_q) + nb(q_off)
+    off_bytes = nb(w_off) + nb(sep["c_q"]) + nb(q_off)
     out["next-4 offline absorption (measure only)"] = {
         "us": round(off_us, 2), "bytes_algorithmic": int(off_bytes),
         "GBps": round(off_bytes / off_us / 1e3, 1),
@@ -197,7 +218,8 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
            "steps": out, "chain_us": round(chain_us, 2), "chain_bytes_algorithmic": int(total_bytes),
            "chain_GBps": round(total_bytes / chain_us / 1e3, 1),
            "chain_roofline_frac": round(total_bytes / chain_us / 1e3 / HBM_PEAK_GBPS, 4),
-           "sequences_per_s": round(B / (chain_us * 1e-6), 1)}
+           "sequences_per_s": round(B / (chain_us * 1e-6), 1),
+           "chain_separate_products_us": round(separate_us, 2)}
     if oracle_seqs > 0:
         import oracle
         wf = {k: W.to_f64(v) for k, v in x["weights"].items()}

@@ -54,7 +54,10 @@ _SIGNATURES = {
     "mla_suggest_num_splits": (_I32, [_I32, _I32, _I64, _I32, _I32]),
     "mla_absorb_q": (_I32, [_P, _P, _P, _P, _F, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                             _I32, _P]),
+    "mla_absorb_q_strided": (_I32, [_P, _I64, _P, _P, _I64, _P, _F, _P, _P, _I32, _I32, _I32,
+                                    _I32, _I32, _I32, _I32, _P]),
     "mla_kv_append": (_I32, [_P, _P, _I32, _P, _P, _P, _F, _SP, _I32, _P]),
+    "mla_kv_append_strided": (_I32, [_P, _I64, _P, _I64, _I32, _P, _P, _P, _F, _SP, _I32, _P]),
     "mla_decode_attn": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _I32, _P, _I32, _P]),
     "mla_decode_attn_multi": (_I32, [_P, _P, _P, _P, _P, _SP, _I32, _F, _I32, _P, _I32, _P, _I32,
                                      _P]),
@@ -62,6 +65,7 @@ _SIGNATURES = {
     "mla_decode": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _SZ, _P, _P, _I32, _P]),
     "mla_out_proj": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "mla_linear": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P]),
+    "mla_linear_strided": (_I32, [_P, _I32, _I64, _P, _I32, _I32, _I32, _I32, _P, _I64, _P]),
     "mla_linear_planned": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _I32, _I32, _I32,
                                   _I32, _P]),
     "mla_validate_indices": (_I32, [_P, _P, _SP, _P, _P]),
@@ -178,6 +182,40 @@ def _dev(t, name, dtype=None, ndim=None):
     return t.data_ptr()
 
 
+def _row_stride(shape, stride, lead, name="tensor") -> int:
+    """Row stride (elements) of a tensor whose first `lead` dims number rows at one common
+    stride and whose other dims are dense within a row; raises ValueError otherwise."""
+    width = 1
+    for i in range(len(shape) - 1, lead - 1, -1):
+        if shape[i] > 1 and stride[i] != width:
+            raise ValueError(f"{name} must be dense within a row (strides {tuple(stride)})")
+        width *= shape[i]
+    ld, span = None, 1
+    for i in range(lead - 1, -1, -1):
+        if shape[i] > 1:
+            if ld is None:
+                ld = stride[i] // span if stride[i] % span == 0 else -1
+            if ld <= 0 or stride[i] != ld * span:
+                raise ValueError(f"{name}: rows must be evenly spaced (strides {tuple(stride)})")
+        span *= shape[i]
+    return ld if ld is not None else width
+
+
+def _dev_rows(t, name, dtype, ndim, lead):
+    """Device pointer and row stride of a GPU tensor laid out as _row_stride describes (a
+    column range of a wider buffer, for instance)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t.data_ptr(), _row_stride(t.shape, t.stride(), lead, name)
+
+
 def _stream(stream):
     if stream is None:
         return _torch().cuda.current_stream().cuda_stream
@@ -241,6 +279,30 @@ def mla_absorb_q(q_c, w_uk, q_r, seq_lens, rope_base, q_lat, q_pe, stream=None):
         B, H, d_h, d_c, d_R, _dtype_code(w_uk), _dtype_code(q_lat), _stream(stream))
 
 
+def mla_absorb_q_strided(q_c, w_uk, q_r, seq_lens, rope_base, q_lat, q_pe, stream=None):
+    """mla_absorb_q reading q_c [B,H,d_h] and q_r [B,H,d_R] as row-strided views (each
+    row's heads contiguous), e.g. column ranges of the stacked [W^UQ; W^QR] projection."""
+    torch = _torch()
+    B, H, d_h = q_c.shape
+    d_c = w_uk.shape[1]
+    _expect(w_uk.shape[0] == H * d_h, "w_uk must be [H*d_h, d_c]")
+    _expect(tuple(q_lat.shape) == (B, H, d_c), "q_lat must be [B,H,d_c]")
+    qc_ptr, ld_qc = _dev_rows(q_c, "q_c", torch.float32, 3, 1)
+    qr_ptr, ld_qr, d_R = None, 0, 0
+    if q_r is not None:
+        d_R = q_r.shape[2]
+        _expect(tuple(q_r.shape) == (B, H, d_R) and tuple(q_pe.shape) == (B, H, d_R),
+                "q_r and q_pe must be [B,H,d_R]")
+        _expect(q_pe.dtype == q_lat.dtype, "q_pe and q_lat must share a dtype")
+        _expect(tuple(seq_lens.shape) == (B,), "seq_lens must be [B]")
+        qr_ptr, ld_qr = _dev_rows(q_r, "q_r", torch.float32, 3, 1)
+    _invoke("mla_absorb_q_strided",
+        qc_ptr, ld_qc, _dev(w_uk, "w_uk", None, 2), qr_ptr, ld_qr,
+        _dev(seq_lens, "seq_lens", torch.int32, 1), float(rope_base),
+        _dev(q_lat, "q_lat", None, 3), _dev(q_pe, "q_pe", None, 3),
+        B, H, d_h, d_c, d_R, _dtype_code(w_uk), _dtype_code(q_lat), _stream(stream))
+
+
 def mla_kv_append(c_kv, k_r, seq_lens_before, block_table, kv_cache, rope_base, stream=None):
     """Write [c_kv | RoPE(k_r, pos)] rows at positions seq_lens_before[b] + t.
     c_kv [B,n,d_c] f32, k_r [B,n,d_R] f32, kv_cache [pages, P, d_c + d_R]."""
@@ -252,6 +314,24 @@ def mla_kv_append(c_kv, k_r, seq_lens_before, block_table, kv_cache, rope_base, 
     shp = paged_shape(kv_cache, block_table, 1, d_c)
     _invoke("mla_kv_append",
         _dev(c_kv, "c_kv", torch.float32, 3), _dev(k_r, "k_r", torch.float32, 3), n,
+        _dev(seq_lens_before, "seq_lens_before", torch.int32, 1),
+        _dev(block_table, "block_table", torch.int32, 2), _dev(kv_cache, "kv_cache", None, 3),
+        float(rope_base), ctypes.byref(shp), _dtype_code(kv_cache), _stream(stream))
+
+
+def mla_kv_append_strided(c_kv, k_r, seq_lens_before, block_table, kv_cache, rope_base,
+                          stream=None):
+    """mla_kv_append reading c_kv [B,n,d_c] and k_r [B,n,d_R] as row-strided views (rows
+    b n + t evenly spaced), e.g. column ranges of the stacked [W^DQ; W^DKV; W^KR] projection."""
+    torch = _torch()
+    B, n, d_c = c_kv.shape
+    _expect(k_r.shape[0] == B and k_r.shape[1] == n, "k_r must be [B,n,d_R]")
+    _expect(kv_cache.shape[2] == d_c + k_r.shape[2], "cache row must be d_c + d_R wide")
+    _expect(block_table.shape[0] == B and tuple(seq_lens_before.shape) == (B,), "batch mismatch")
+    shp = paged_shape(kv_cache, block_table, 1, d_c)
+    c_ptr, ld_c = _dev_rows(c_kv, "c_kv", torch.float32, 3, 2)
+    k_ptr, ld_k = _dev_rows(k_r, "k_r", torch.float32, 3, 2)
+    _invoke("mla_kv_append_strided", c_ptr, ld_c, k_ptr, ld_k, n,
         _dev(seq_lens_before, "seq_lens_before", torch.int32, 1),
         _dev(block_table, "block_table", torch.int32, 2), _dev(kv_cache, "kv_cache", None, 3),
         float(rope_base), ctypes.byref(shp), _dtype_code(kv_cache), _stream(stream))
@@ -370,6 +450,19 @@ def mla_linear(x, w, y, stream=None):
     _invoke("mla_linear", _dev(x, "x", None, 2), _dtype_code(x), _dev(w, "w", None, 2),
                           _dtype_code(w), M, N, K, _dev(y, "y", torch.float32, 2),
                           _stream(stream))
+
+
+def mla_linear_strided(x, w, y, stream=None):
+    """y = x w^T on row-strided views: x [M,K], y [M,N] fp32 with unit column stride (e.g.
+    column ranges of wider buffers); w [N,K] dense (e.g. several nn.Linear weights stacked)."""
+    torch = _torch()
+    M, K = x.shape
+    N = w.shape[0]
+    _expect(w.shape[1] == K and tuple(y.shape) == (M, N), "shapes must be x[M,K] w[N,K] y[M,N]")
+    x_ptr, ldx = _dev_rows(x, "x", None, 2, 1)
+    y_ptr, ldy = _dev_rows(y, "y", torch.float32, 2, 1)
+    _invoke("mla_linear_strided", x_ptr, _dtype_code(x), ldx, _dev(w, "w", None, 2),
+                                  _dtype_code(w), M, N, K, y_ptr, ldy, _stream(stream))
 
 
 def mla_linear_planned(x, w, y, kernel, tile, split, ring, stream=None):

@@ -40,7 +40,7 @@ __device__ __forceinline__ unsigned pack2(float a, float b) {
 __global__ __launch_bounds__(256) void absorb_kernel(const float* __restrict__ q_c,
                                                      const bf16raw* __restrict__ w_uk,
                                                      bf16raw* __restrict__ q_lat, int B, int H,
-                                                     int d_c) {
+                                                     int d_c, int64_t ld_q) {
   __shared__ __attribute__((aligned(16))) char smem[AB_LDS];
   lds_char_t* const lsm = (lds_char_t*)smem;
   const int c0 = blockIdx.x * 128, b0 = blockIdx.y * 64, h = blockIdx.z;
@@ -61,7 +61,8 @@ __global__ __launch_bounds__(256) void absorb_kernel(const float* __restrict__ q
   //      row t / 4, columns 32 (t % 4) .. + 31
   const int xr = tid >> 2, xc = (tid & 3) * 32;
   const bool xr_ok = b0 + xr < B;
-  const float* xsrc = q_c + (static_cast<int64_t>(b0 + (xr_ok ? xr : 0)) * H + h) * AB_DH + xc;
+  const float* xsrc =
+      q_c + static_cast<int64_t>(b0 + (xr_ok ? xr : 0)) * ld_q + h * AB_DH + xc;
   f32x4_t xv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -134,18 +135,19 @@ __global__ __launch_bounds__(256) void absorb_kernel(const float* __restrict__ q
 
 }  // namespace
 
-bool absorb_mfma_supported(int B, int H, int d_h, int d_c, const void* q_c, const void* w_uk,
-                           const void* q_lat) {
+bool absorb_mfma_supported(int B, int H, int d_h, int d_c, const void* q_c, int64_t ld_q,
+                           const void* w_uk, const void* q_lat) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(q_c) | reinterpret_cast<uintptr_t>(w_uk) |
                       reinterpret_cast<uintptr_t>(q_lat);
   return d_h == AB_DH && d_c % 128 == 0 && B >= 1 && (B + 63) / 64 <= 65535 && H <= 65535 &&
-         (a & 15) == 0;
+         (a & 15) == 0 && ld_q % 4 == 0;
 }
 
-hipError_t launch_absorb_mfma(const float* q_c, const void* w_uk, void* q_lat, int B, int H,
-                              int d_c, hipStream_t s) {
+hipError_t launch_absorb_mfma(const float* q_c, int64_t ld_q, const void* w_uk, void* q_lat,
+                              int B, int H, int d_c, hipStream_t s) {
   hipLaunchKernelGGL(absorb_kernel, dim3(d_c / 128, (B + 63) / 64, H), dim3(256), 0, s, q_c,
-                     static_cast<const bf16raw*>(w_uk), static_cast<bf16raw*>(q_lat), B, H, d_c);
+                     static_cast<const bf16raw*>(w_uk), static_cast<bf16raw*>(q_lat), B, H, d_c,
+                     ld_q);
   return hipGetLastError();
 }
 

@@ -10,10 +10,13 @@
 
 namespace mla {
 
-// out[r][:] = RoPE(x[r][:], seq_lens[r / rows_per_seq] + pos_offset)
+// out[r][:] = RoPE(x row r, seq_lens[r / rows_per_seq] + pos_offset), where row r of x starts
+// at x + (r / rows_per_seq) ld_seq + (r % rows_per_seq) d_R (rows of one sequence contiguous,
+// sequences ld_seq elements apart) and out is dense [rows][d_R]
 template <typename OT>
 __global__ __launch_bounds__(256) void rope_rows_kernel(const float* __restrict__ x,
                                                         int64_t rows, int rows_per_seq, int d_R,
+                                                        int64_t ld_seq,
                                                         const int32_t* __restrict__ seq_lens,
                                                         int pos_offset, float base,
                                                         OT* __restrict__ out) {
@@ -23,43 +26,48 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(const float* __restrict_
        e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int64_t r = e / half;
     const int k = static_cast<int>(e % half);
-    const int64_t pos = static_cast<int64_t>(seq_lens[r / rows_per_seq]) + pos_offset;
+    const int64_t sq = r / rows_per_seq;
+    const int64_t pos = static_cast<int64_t>(seq_lens[sq]) + pos_offset;
+    const float* xr = x + sq * ld_seq + (r - sq * rows_per_seq) * d_R;
     float y0, y1;
-    rope_pair(x[r * d_R + 2 * k], x[r * d_R + 2 * k + 1], pos, k, d_R, base, &y0, &y1);
+    rope_pair(xr[2 * k], xr[2 * k + 1], pos, k, d_R, base, &y0, &y1);
     st(out + r * d_R + 2 * k, y0);
     st(out + r * d_R + 2 * k + 1, y1);
   }
 }
 
 hipError_t launch_rope_rows(const float* x, int64_t rows, int rows_per_seq, int d_R,
-                            const int32_t* seq_lens, int pos_offset, float base, void* out,
-                            int out_bf16, hipStream_t s) {
+                            int64_t ld_seq, const int32_t* seq_lens, int pos_offset, float base,
+                            void* out, int out_bf16, hipStream_t s) {
   const int64_t total = rows * (d_R / 2);
   const int blocks = static_cast<int>(total < 256 * 1024 ? (total + 255) / 256 : 1024);
   if (out_bf16) {
     hipLaunchKernelGGL(rope_rows_kernel<bf16raw>, dim3(blocks), dim3(256), 0, s, x, rows,
-                       rows_per_seq, d_R, seq_lens, pos_offset, base,
+                       rows_per_seq, d_R, ld_seq, seq_lens, pos_offset, base,
                        static_cast<bf16raw*>(out));
   } else {
     hipLaunchKernelGGL(rope_rows_kernel<float>, dim3(blocks), dim3(256), 0, s, x, rows,
-                       rows_per_seq, d_R, seq_lens, pos_offset, base, static_cast<float*>(out));
+                       rows_per_seq, d_R, ld_seq, seq_lens, pos_offset, base,
+                       static_cast<float*>(out));
   }
   return hipGetLastError();
 }
 
-// One workgroup per appended token: row [c^KV | RoPE(k^R, pos)] at its page and slot.
+// One workgroup per appended token: row [c^KV | RoPE(k^R, pos)] at its page and slot.  The
+// inputs of token t of sequence b are rows b n_new + t of c_kv and k_r, ld_c and ld_k
+// elements apart.
 template <typename CT>
 __global__ __launch_bounds__(256) void kv_append_kernel(
-    const float* __restrict__ c_kv, const float* __restrict__ k_r, int n_new,
-    const int32_t* __restrict__ seq_lens_before, const int32_t* __restrict__ block_table,
+    const float* __restrict__ c_kv, int64_t ld_c, const float* __restrict__ k_r, int64_t ld_k,
+    int n_new, const int32_t* __restrict__ seq_lens_before, const int32_t* __restrict__ block_table,
     CT* __restrict__ cache, float base, int d_c, int d_R, int P, int max_pages) {
   const int t = blockIdx.x, b = blockIdx.y;
   const int pos = seq_lens_before[b] + t;
   const int page = block_table[static_cast<int64_t>(b) * max_pages + pos / P];
   CT* row = cache + (static_cast<int64_t>(page) * P + pos % P) * (d_c + d_R);
-  const float* c = c_kv + (static_cast<int64_t>(b) * n_new + t) * d_c;
+  const float* c = c_kv + (static_cast<int64_t>(b) * n_new + t) * ld_c;
   for (int i = threadIdx.x; i < d_c; i += blockDim.x) st(row + i, c[i]);
-  const float* kr = k_r + (static_cast<int64_t>(b) * n_new + t) * d_R;
+  const float* kr = k_r + (static_cast<int64_t>(b) * n_new + t) * ld_k;
   for (int k = threadIdx.x; k < d_R / 2; k += blockDim.x) {
     float y0, y1;
     rope_pair(kr[2 * k], kr[2 * k + 1], pos, k, d_R, base, &y0, &y1);
@@ -68,19 +76,19 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
   }
 }
 
-hipError_t launch_kv_append(const float* c_kv, const float* k_r, int n_new,
-                            const int32_t* seq_lens_before, const int32_t* block_table,
+hipError_t launch_kv_append(const float* c_kv, int64_t ld_c, const float* k_r, int64_t ld_k,
+                            int n_new, const int32_t* seq_lens_before, const int32_t* block_table,
                             void* cache, int cache_bf16, float base, int B, int d_c, int d_R,
                             int page_size, int max_pages, hipStream_t s) {
   dim3 grid(n_new, B);
   if (cache_bf16) {
-    hipLaunchKernelGGL(kv_append_kernel<bf16raw>, grid, dim3(256), 0, s, c_kv, k_r, n_new,
-                       seq_lens_before, block_table, static_cast<bf16raw*>(cache), base, d_c,
-                       d_R, page_size, max_pages);
+    hipLaunchKernelGGL(kv_append_kernel<bf16raw>, grid, dim3(256), 0, s, c_kv, ld_c, k_r, ld_k,
+                       n_new, seq_lens_before, block_table, static_cast<bf16raw*>(cache), base,
+                       d_c, d_R, page_size, max_pages);
   } else {
-    hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(256), 0, s, c_kv, k_r, n_new,
-                       seq_lens_before, block_table, static_cast<float*>(cache), base, d_c,
-                       d_R, page_size, max_pages);
+    hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(256), 0, s, c_kv, ld_c, k_r, ld_k,
+                       n_new, seq_lens_before, block_table, static_cast<float*>(cache), base,
+                       d_c, d_R, page_size, max_pages);
   }
   return hipGetLastError();
 }

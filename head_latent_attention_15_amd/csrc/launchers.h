@@ -71,18 +71,19 @@ bool gemm_xs_plan_ok(const GemmArgs& g, int tn, int s, int grid);
 hipError_t launch_gemm_xs_with(const GemmArgs& g, int tn, int s, int grid, hipStream_t st);
 hipError_t launch_gemm_xs(const GemmArgs& g, hipStream_t st);
 
-// Query absorption q~_i = W^UK_i^T q^C_i on bf16 MFMA (bf16 W^UK, bf16 q~, d_h = 128).
-bool absorb_mfma_supported(int B, int H, int d_h, int d_c, const void* q_c, const void* w_uk,
-                           const void* q_lat);
-hipError_t launch_absorb_mfma(const float* q_c, const void* w_uk, void* q_lat, int B, int H,
-                              int d_c, hipStream_t s);
+// Query absorption q~_i = W^UK_i^T q^C_i on bf16 MFMA (bf16 W^UK, bf16 q~, d_h = 128);
+// row b of q_c starts at q_c + b ld_q, its heads d_h apart.
+bool absorb_mfma_supported(int B, int H, int d_h, int d_c, const void* q_c, int64_t ld_q,
+                           const void* w_uk, const void* q_lat);
+hipError_t launch_absorb_mfma(const float* q_c, int64_t ld_q, const void* w_uk, void* q_lat,
+                              int B, int H, int d_c, hipStream_t s);
 
 hipError_t launch_rope_rows(const float* x, int64_t rows, int rows_per_seq, int d_R,
-                            const int32_t* seq_lens, int pos_offset, float base, void* out,
-                            int out_bf16, hipStream_t s);
+                            int64_t ld_seq, const int32_t* seq_lens, int pos_offset, float base,
+                            void* out, int out_bf16, hipStream_t s);
 
-hipError_t launch_kv_append(const float* c_kv, const float* k_r, int n_new,
-                            const int32_t* seq_lens_before, const int32_t* block_table,
+hipError_t launch_kv_append(const float* c_kv, int64_t ld_c, const float* k_r, int64_t ld_k,
+                            int n_new, const int32_t* seq_lens_before, const int32_t* block_table,
                             void* cache, int cache_bf16, float base, int B, int d_c, int d_R,
                             int page_size, int max_pages, hipStream_t s);
 

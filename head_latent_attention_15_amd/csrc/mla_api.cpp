@@ -257,55 +257,99 @@ mla_status_t mla_decode(const void* q_lat, const void* q_pe, const void* kv_cach
                             num_splits, shape->d_latent, out, lse_out, stream);
 }
 
-mla_status_t mla_absorb_q(const float* q_c, const void* w_uk, const float* q_r,
-                          const int32_t* seq_lens, float rope_base, void* q_lat, void* q_pe,
-                          int32_t B, int32_t H, int32_t d_h, int32_t d_c, int32_t d_R,
-                          mla_dtype_t w_dtype, mla_dtype_t out_dtype, void* stream) {
-  if (!q_c || !w_uk || !q_lat) return fail(MLA_ERR_NULL, "mla_absorb_q: NULL q_c/w_uk/q_lat");
+static mla_status_t absorb_q(const char* fn, const float* q_c, int64_t ld_qc, const void* w_uk,
+                             const float* q_r, int64_t ld_qr, const int32_t* seq_lens,
+                             float rope_base, void* q_lat, void* q_pe, int32_t B, int32_t H,
+                             int32_t d_h, int32_t d_c, int32_t d_R, mla_dtype_t w_dtype,
+                             mla_dtype_t out_dtype, void* stream) {
+  if (!q_c || !w_uk || !q_lat) return fail(MLA_ERR_NULL, "%s: NULL q_c/w_uk/q_lat", fn);
   if (q_r && (!q_pe || !seq_lens))
-    return fail(MLA_ERR_NULL, "mla_absorb_q: q_r given but q_pe or seq_lens is NULL");
+    return fail(MLA_ERR_NULL, "%s: q_r given but q_pe or seq_lens is NULL", fn);
   if (B < 1 || H < 1 || d_h < 1 || d_c < 1 || (q_r && d_R < 1))
-    return fail(MLA_ERR_SHAPE, "mla_absorb_q: sizes must be >= 1");
-  if (q_r && d_R % 2) return fail(MLA_ERR_SHAPE, "mla_absorb_q: d_R %d is odd", d_R);
+    return fail(MLA_ERR_SHAPE, "%s: sizes must be >= 1", fn);
+  if (q_r && d_R % 2) return fail(MLA_ERR_SHAPE, "%s: d_R %d is odd", fn, d_R);
+  if (ld_qc < static_cast<int64_t>(H) * d_h || (q_r && ld_qr < static_cast<int64_t>(H) * d_R))
+    return fail(MLA_ERR_SHAPE, "%s: row strides %lld / %lld below H*d_h / H*d_R", fn,
+                static_cast<long long>(ld_qc), static_cast<long long>(ld_qr));
   if (!is_dtype(w_dtype) || !is_dtype(out_dtype))
-    return fail(MLA_ERR_UNSUPPORTED, "mla_absorb_q: unknown dtype");
-  if (q_r && !std::isfinite(rope_base))
-    return fail(MLA_ERR_SHAPE, "mla_absorb_q: rope_base not finite");
+    return fail(MLA_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  if (q_r && !std::isfinite(rope_base)) return fail(MLA_ERR_SHAPE, "%s: rope_base not finite", fn);
   hipStream_t s = as_stream(stream);
   mla::GemmArgs g;
-  g.x = q_c; g.ldx = static_cast<int64_t>(H) * d_h; g.sx = d_h; g.x_bf16 = 0;
+  g.x = q_c; g.ldx = ld_qc; g.sx = d_h; g.x_bf16 = 0;
   g.w = w_uk; g.ldw = d_c; g.sw = static_cast<int64_t>(d_h) * d_c; g.w_bf16 = w_dtype == MLA_BF16;
   g.w_nk = false;
   g.y = q_lat; g.ldy = static_cast<int64_t>(H) * d_c; g.sy = d_c; g.y_bf16 = out_dtype == MLA_BF16;
   g.M = B; g.N = d_c; g.K = d_h; g.batch = H;
   const bool mfma = w_dtype == MLA_BF16 && out_dtype == MLA_BF16 &&
-                    mla::absorb_mfma_supported(B, H, d_h, d_c, q_c, w_uk, q_lat);
-  mla_status_t st = launched(mfma ? mla::launch_absorb_mfma(q_c, w_uk, q_lat, B, H, d_c, s)
+                    mla::absorb_mfma_supported(B, H, d_h, d_c, q_c, ld_qc, w_uk, q_lat);
+  mla_status_t st = launched(mfma ? mla::launch_absorb_mfma(q_c, ld_qc, w_uk, q_lat, B, H, d_c, s)
                                   : mla::launch_gemm_small(g, s),
                              "absorb GEMM");
   if (st != MLA_OK || !q_r) return st;
-  return launched(mla::launch_rope_rows(q_r, static_cast<int64_t>(B) * H, H, d_R, seq_lens, -1,
-                                        rope_base, q_pe, out_dtype == MLA_BF16, s),
+  return launched(mla::launch_rope_rows(q_r, static_cast<int64_t>(B) * H, H, d_R, ld_qr, seq_lens,
+                                        -1, rope_base, q_pe, out_dtype == MLA_BF16, s),
                   "query RoPE");
+}
+
+mla_status_t mla_absorb_q(const float* q_c, const void* w_uk, const float* q_r,
+                          const int32_t* seq_lens, float rope_base, void* q_lat, void* q_pe,
+                          int32_t B, int32_t H, int32_t d_h, int32_t d_c, int32_t d_R,
+                          mla_dtype_t w_dtype, mla_dtype_t out_dtype, void* stream) {
+  return absorb_q("mla_absorb_q", q_c, static_cast<int64_t>(H) * d_h, w_uk, q_r,
+                  static_cast<int64_t>(H) * d_R, seq_lens, rope_base, q_lat, q_pe, B, H, d_h,
+                  d_c, d_R, w_dtype, out_dtype, stream);
+}
+
+mla_status_t mla_absorb_q_strided(const float* q_c, int64_t ld_qc, const void* w_uk,
+                                  const float* q_r, int64_t ld_qr, const int32_t* seq_lens,
+                                  float rope_base, void* q_lat, void* q_pe, int32_t B, int32_t H,
+                                  int32_t d_h, int32_t d_c, int32_t d_R, mla_dtype_t w_dtype,
+                                  mla_dtype_t out_dtype, void* stream) {
+  return absorb_q("mla_absorb_q_strided", q_c, ld_qc, w_uk, q_r, ld_qr, seq_lens, rope_base,
+                  q_lat, q_pe, B, H, d_h, d_c, d_R, w_dtype, out_dtype, stream);
+}
+
+static mla_status_t kv_append(const char* fn, const float* c_kv, int64_t ld_ckv,
+                              const float* k_r, int64_t ld_kr, int32_t n_new,
+                              const int32_t* seq_lens_before, const int32_t* block_table,
+                              void* kv_cache, float rope_base, const mla_paged_shape_t* shape,
+                              mla_dtype_t cache_dtype, void* stream) {
+  if (!c_kv || !k_r || !seq_lens_before || !block_table || !kv_cache)
+    return fail(MLA_ERR_NULL, "%s: a required pointer is NULL", fn);
+  mla_status_t st = check_paged_shape(shape);
+  if (st != MLA_OK) return st;
+  if (n_new < 1) return fail(MLA_ERR_SHAPE, "%s: n_new %d < 1", fn, n_new);
+  if (n_new > 65535) return fail(MLA_ERR_SHAPE, "%s: n_new %d > 65535", fn, n_new);
+  if (ld_ckv < shape->d_latent || ld_kr < shape->d_rope)
+    return fail(MLA_ERR_SHAPE, "%s: row strides %lld / %lld below d_latent / d_rope", fn,
+                static_cast<long long>(ld_ckv), static_cast<long long>(ld_kr));
+  if (!is_dtype(cache_dtype)) return fail(MLA_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  if (!std::isfinite(rope_base)) return fail(MLA_ERR_SHAPE, "%s: rope_base", fn);
+  return launched(mla::launch_kv_append(c_kv, ld_ckv, k_r, ld_kr, n_new, seq_lens_before,
+                                        block_table, kv_cache, cache_dtype == MLA_BF16, rope_base,
+                                        shape->batch, shape->d_latent, shape->d_rope,
+                                        shape->page_size, shape->max_pages_per_seq,
+                                        as_stream(stream)),
+                  "cache append");
 }
 
 mla_status_t mla_kv_append(const float* c_kv, const float* k_r, int32_t n_new,
                            const int32_t* seq_lens_before, const int32_t* block_table,
                            void* kv_cache, float rope_base, const mla_paged_shape_t* shape,
                            mla_dtype_t cache_dtype, void* stream) {
-  if (!c_kv || !k_r || !seq_lens_before || !block_table || !kv_cache)
-    return fail(MLA_ERR_NULL, "mla_kv_append: a required pointer is NULL");
-  mla_status_t st = check_paged_shape(shape);
-  if (st != MLA_OK) return st;
-  if (n_new < 1) return fail(MLA_ERR_SHAPE, "mla_kv_append: n_new %d < 1", n_new);
-  if (n_new > 65535) return fail(MLA_ERR_SHAPE, "mla_kv_append: n_new %d > 65535", n_new);
-  if (!is_dtype(cache_dtype)) return fail(MLA_ERR_UNSUPPORTED, "mla_kv_append: unknown dtype");
-  if (!std::isfinite(rope_base)) return fail(MLA_ERR_SHAPE, "mla_kv_append: rope_base");
-  return launched(mla::launch_kv_append(c_kv, k_r, n_new, seq_lens_before, block_table, kv_cache,
-                                        cache_dtype == MLA_BF16, rope_base, shape->batch,
-                                        shape->d_latent, shape->d_rope, shape->page_size,
-                                        shape->max_pages_per_seq, as_stream(stream)),
-                  "cache append");
+  if (!shape) return fail(MLA_ERR_NULL, "shape is NULL");
+  return kv_append("mla_kv_append", c_kv, shape->d_latent, k_r, shape->d_rope, n_new,
+                   seq_lens_before, block_table, kv_cache, rope_base, shape, cache_dtype, stream);
+}
+
+mla_status_t mla_kv_append_strided(const float* c_kv, int64_t ld_ckv, const float* k_r,
+                                   int64_t ld_kr, int32_t n_new, const int32_t* seq_lens_before,
+                                   const int32_t* block_table, void* kv_cache, float rope_base,
+                                   const mla_paged_shape_t* shape, mla_dtype_t cache_dtype,
+                                   void* stream) {
+  return kv_append("mla_kv_append_strided", c_kv, ld_ckv, k_r, ld_kr, n_new, seq_lens_before,
+                   block_table, kv_cache, rope_base, shape, cache_dtype, stream);
 }
 
 mla_status_t mla_out_proj(const float* o_lat, const void* w_uv, const void* w_o, int32_t B,
@@ -335,20 +379,35 @@ mla_status_t mla_out_proj(const float* o_lat, const void* w_uv, const void* w_o,
   return launched(gemm(o, s), "W^O GEMM");
 }
 
+static mla_status_t linear(const char* fn, const void* x, mla_dtype_t x_dtype, int64_t ldx,
+                           const void* w, mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K,
+                           float* y, int64_t ldy, void* stream) {
+  if (!x || !w || !y) return fail(MLA_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (M < 1 || N < 1 || K < 1) return fail(MLA_ERR_SHAPE, "%s: sizes must be >= 1", fn);
+  if (M > 65535 * 64) return fail(MLA_ERR_SHAPE, "%s: M %d too large", fn, M);
+  if (ldx < K || ldy < N)
+    return fail(MLA_ERR_SHAPE, "%s: row strides ldx %lld < K or ldy %lld < N", fn,
+                static_cast<long long>(ldx), static_cast<long long>(ldy));
+  if (!is_dtype(x_dtype) || !is_dtype(w_dtype))
+    return fail(MLA_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  mla::GemmArgs g;
+  g.x = x; g.ldx = ldx; g.sx = 0; g.x_bf16 = x_dtype == MLA_BF16;
+  g.w = w; g.ldw = K; g.sw = 0; g.w_bf16 = w_dtype == MLA_BF16; g.w_nk = true;
+  g.y = y; g.ldy = ldy; g.sy = 0; g.y_bf16 = 0;
+  g.M = M; g.N = N; g.K = K; g.batch = 1;
+  return launched(gemm(g, as_stream(stream)), "linear GEMM");
+}
+
 mla_status_t mla_linear(const void* x, mla_dtype_t x_dtype, const void* w,
                         mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K, float* y,
                         void* stream) {
-  if (!x || !w || !y) return fail(MLA_ERR_NULL, "mla_linear: a required pointer is NULL");
-  if (M < 1 || N < 1 || K < 1) return fail(MLA_ERR_SHAPE, "mla_linear: sizes must be >= 1");
-  if (M > 65535 * 64) return fail(MLA_ERR_SHAPE, "mla_linear: M %d too large", M);
-  if (!is_dtype(x_dtype) || !is_dtype(w_dtype))
-    return fail(MLA_ERR_UNSUPPORTED, "mla_linear: unknown dtype");
-  mla::GemmArgs g;
-  g.x = x; g.ldx = K; g.sx = 0; g.x_bf16 = x_dtype == MLA_BF16;
-  g.w = w; g.ldw = K; g.sw = 0; g.w_bf16 = w_dtype == MLA_BF16; g.w_nk = true;
-  g.y = y; g.ldy = N; g.sy = 0; g.y_bf16 = 0;
-  g.M = M; g.N = N; g.K = K; g.batch = 1;
-  return launched(gemm(g, as_stream(stream)), "linear GEMM");
+  return linear("mla_linear", x, x_dtype, K, w, w_dtype, M, N, K, y, N, stream);
+}
+
+mla_status_t mla_linear_strided(const void* x, mla_dtype_t x_dtype, int64_t ldx, const void* w,
+                                mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K, float* y,
+                                int64_t ldy, void* stream) {
+  return linear("mla_linear_strided", x, x_dtype, ldx, w, w_dtype, M, N, K, y, ldy, stream);
 }
 
 mla_status_t mla_linear_planned(const void* x, mla_dtype_t x_dtype, const void* w,

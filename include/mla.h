@@ -15,7 +15,8 @@
  *
  * Conventions for every entry point
  *   - Tensor pointers are DEVICE pointers owned by the caller; every tensor is dense,
- *     row-major, in the shape given.  The library never allocates, frees or synchronises;
+ *     row-major, in the shape given (the _strided entry points take row strides for the
+ *     inputs they name).  The library never allocates, frees or synchronises;
  *     it enqueues kernels on `stream` (a hipStream_t passed as void*; NULL = the null
  *     stream) and returns.  Structs of sizes (mla_paged_shape_t) are HOST pointers.
  *   - All arguments are validated on the host before anything is launched; on any
@@ -27,7 +28,7 @@
  *     there: out-of-range values are undefined behaviour.  mla_validate_indices checks
  *     them on the device beforehand.
  *   - Results are deterministic for fixed inputs and arguments, except the projections
- *     (mla_linear, mla_out_proj) with bf16 weights: their long reductions are split over
+ *     (mla_linear*, mla_out_proj) with bf16 weights: their long reductions are split over
  *     workgroups that add into the fp32 output atomically, so the last bits of y / u /
  *     o_heads can differ between runs.
  *
@@ -113,6 +114,18 @@ mla_status_t mla_absorb_q(const float* q_c, const void* w_uk, const float* q_r,
                           int32_t B, int32_t H, int32_t d_h, int32_t d_c, int32_t d_R,
                           mla_dtype_t w_dtype, mla_dtype_t out_dtype, void* stream);
 
+/* mla_absorb_q on row-strided inputs: row b of q_c starts at q_c + b * ld_qc and row b of
+ * q_r at q_r + b * ld_qr (elements; the heads of a row stay contiguous, d_h and d_R apart).
+ * This reads q^C and q^R in place from one stacked projection y = [W^UQ; W^QR] c^Q, whose
+ * rows hold q^C_b followed by q^R_b (ld_qc = ld_qr = H*(d_h + d_R), q_r = q_c + H*d_h).
+ * The products and roundings are those of mla_absorb_q.  q_lat and q_pe stay dense.
+ * Errors: as mla_absorb_q, and SHAPE for ld_qc < H*d_h or (q_r given) ld_qr < H*d_R. */
+mla_status_t mla_absorb_q_strided(const float* q_c, int64_t ld_qc, const void* w_uk,
+                                  const float* q_r, int64_t ld_qr, const int32_t* seq_lens,
+                                  float rope_base, void* q_lat, void* q_pe, int32_t B, int32_t H,
+                                  int32_t d_h, int32_t d_c, int32_t d_R, mla_dtype_t w_dtype,
+                                  mla_dtype_t out_dtype, void* stream);
+
 /* Append n_new tokens per sequence to the paged cache.
  * Token t of sequence b goes to position pos = seq_lens_before[b] + t and its row is
  * [c_kv[b][t][:] | RoPE(k_r[b][t][:], pos)] converted to cache_dtype
@@ -127,6 +140,17 @@ mla_status_t mla_kv_append(const float* c_kv, const float* k_r, int32_t n_new,
                            const int32_t* seq_lens_before, const int32_t* block_table,
                            void* kv_cache, float rope_base, const mla_paged_shape_t* shape,
                            mla_dtype_t cache_dtype, void* stream);
+
+/* mla_kv_append on row-strided inputs: the inputs of token t of sequence b are read at
+ * c_kv + (b*n_new + t) * ld_ckv and k_r + (b*n_new + t) * ld_kr (elements).  This reads
+ * c^KV and k^R in place from one stacked projection y = [W^DQ; W^DKV; W^KR] h (row stride
+ * d_c^Q + d_latent + d_rope).  Same rows written as mla_kv_append.
+ * Errors: as mla_kv_append, and SHAPE for ld_ckv < d_latent or ld_kr < d_rope. */
+mla_status_t mla_kv_append_strided(const float* c_kv, int64_t ld_ckv, const float* k_r,
+                                   int64_t ld_kr, int32_t n_new, const int32_t* seq_lens_before,
+                                   const int32_t* block_table, void* kv_cache, float rope_base,
+                                   const mla_paged_shape_t* shape, mla_dtype_t cache_dtype,
+                                   void* stream);
 
 /* Decode attention over the paged latent cache, split over tokens.
  * For every sequence b, head i and split s (s = 0..num_splits-1), with
@@ -214,13 +238,28 @@ mla_status_t mla_out_proj(const float* o_lat, const void* w_uv, const void* w_o,
  * fp32 output.  Used for the projections c^Q = W^DQ h, q^C = W^UQ c^Q, q^R = W^QR c^Q,
  * c^KV = W^DKV h, k^R = W^KR h (qiita "Query の圧縮", "RoPE の扱い").
  *   x [M][K] x_dtype;  w [N][K] w_dtype;  y [M][N] fp32.
- * With bf16 w, K a multiple of 128 and 16-byte aligned x, w: bf16 MFMA with x carried as
- * two bf16 terms (about 16 significant bits), split-K partial sums added atomically (y is
- * overwritten, not accumulated into); otherwise an fp32 VALU GEMM.
+ * With bf16 w, K a multiple of 128 and 16-byte aligned x, w: bf16 MFMA (fp32 x carried as
+ * two bf16 terms, about 16 significant bits; bf16 x as is), split-K partial sums added
+ * atomically (y is overwritten, not accumulated into).  Which MFMA kernel runs depends on
+ * the shape: for one product of 8 MB of weights or more with N >= 1024 and M <= 64, an
+ * activation-stationary kernel (K <= 4096, N >= 4096) or a persistent weight-streaming
+ * kernel, one workgroup per CU; otherwise a tile-grid kernel.  All give the same products
+ * and roundings up to the order of the fp32 additions.  Without MFMA: an fp32 VALU GEMM.
  * Errors: NULL, SHAPE (sizes < 1), UNSUPPORTED (dtype). */
 mla_status_t mla_linear(const void* x, mla_dtype_t x_dtype, const void* w,
                         mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K, float* y,
                         void* stream);
+
+/* mla_linear with row strides: x row m at x + m * ldx, y row m at y + m * ldy (elements,
+ * ldx >= K, ldy >= N; only columns 0 .. N-1 of each y row are written).  Projections that
+ * read the same input can then run as one product over their stacked weights, e.g.
+ * [W^DQ; W^DKV; W^KR] h (one launch instead of three, the three results side by side in
+ * each row of y), and the next product can read its input columns in place, e.g. c^Q as
+ * the first d_c^Q columns of that y.  x and y must not overlap.
+ * Errors: as mla_linear, and SHAPE for ldx < K or ldy < N. */
+mla_status_t mla_linear_strided(const void* x, mla_dtype_t x_dtype, int64_t ldx, const void* w,
+                                mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K, float* y,
+                                int64_t ldy, void* stream);
 
 /* Device-side check of the paging indices: counts sequences whose seq_len is negative or
  * exceeds max_pages_per_seq*page_size, and referenced block-table entries outside

@@ -185,3 +185,49 @@ def test_bind_requires_exactly_one_library_call():
     with pytest.raises(ValueError):  # the wrapper's own checks still run at bind time
         mla.bind(mla.mla_linear, torch.zeros(2, 4), torch.zeros(3, 4), torch.zeros(2, 3))
     assert mla._capture is None
+
+
+def test_strided_validation():
+    """The row-strided entry points reject strides shorter than a row before launching."""
+    L = mla.lib
+    shp = _shape()
+    assert L.mla_linear_strided(FAKE, 0, 3, FAKE, 1, 4, 4, 4, FAKE, 4, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_linear_strided(FAKE, 0, 4, FAKE, 1, 4, 4, 4, FAKE, 3, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_linear_strided(None, 0, 4, FAKE, 1, 4, 4, 4, FAKE, 4, None) == mla.MLA_ERR_NULL
+    d_c, d_R = shp.d_latent, shp.d_rope
+    assert L.mla_kv_append_strided(FAKE, d_c - 1, FAKE, d_R, 1, FAKE, FAKE, FAKE, 1e4,
+                                   ctypes.byref(shp), 1, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_kv_append_strided(FAKE, d_c, FAKE, d_R - 1, 1, FAKE, FAKE, FAKE, 1e4,
+                                   ctypes.byref(shp), 1, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_kv_append_strided(FAKE, d_c, FAKE, d_R, 1, FAKE, FAKE, FAKE, 1e4,
+                                   None, 1, None) == mla.MLA_ERR_NULL
+    # B=2, H=4, d_h=32, d_c=64, d_R=16: ld_qc >= 128, ld_qr >= 64
+    args = lambda ldq, ldr: [FAKE, ldq, FAKE, FAKE, ldr, FAKE, 1e4, FAKE, FAKE, 2, 4, 32, 64,
+                             16, 1, 1, None]
+    assert L.mla_absorb_q_strided(*args(127, 64)) == mla.MLA_ERR_SHAPE
+    assert L.mla_absorb_q_strided(*args(128, 63)) == mla.MLA_ERR_SHAPE
+
+
+@pytest.mark.parametrize("shape,stride,lead,ld", [
+    ((4, 6), (6, 1), 1, 6),                   # dense
+    ((4, 6), (10, 1), 1, 10),                 # column range of a [4, 10] buffer
+    ((1, 6), (99, 1), 1, 6),                  # one row: the row width
+    ((5, 4, 8), (40, 8, 1), 1, 40),           # [B, H, d] dense
+    ((5, 4, 8), (50, 8, 1), 1, 50),           # heads dense, rows 50 apart
+    ((3, 2, 8), (20, 10, 1), 2, 10),          # [B, n, d]: rows b n + t, 10 apart
+    ((3, 1, 8), (2112, 8, 1), 2, 2112),       # n = 1: the batch stride
+    ((1, 1, 8), (8, 8, 1), 2, 8),             # a single row
+])
+def test_row_stride(shape, stride, lead, ld):
+    assert mla._row_stride(shape, stride, lead) == ld
+
+
+@pytest.mark.parametrize("shape,stride,lead", [
+    ((4, 6), (6, 2), 1),                      # columns not unit-strided
+    ((5, 4, 8), (50, 9, 1), 1),               # heads not dense within a row
+    ((3, 2, 8), (25, 10, 1), 2),              # rows b n + t not evenly spaced
+    ((3, 2, 8), (20, 0, 1), 2),               # broadcast rows
+])
+def test_row_stride_rejects(shape, stride, lead):
+    with pytest.raises(ValueError):
+        mla._row_stride(shape, stride, lead)

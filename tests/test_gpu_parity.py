@@ -465,32 +465,50 @@ def test_stream_read_runs(mla):
 
 
 # ------------------------------------------------------------------ full decode layer
-def layer_on_gpu(mla, x, S):
+def layer_on_gpu(mla, x, S, stacked=False):
     """The whole decode layer through the C ABI: projections, cache append, absorption,
-    attention + combine, W^UV and W^O."""
+    attention + combine, W^UV and W^O.  stacked: the projections that share an input run as
+    one product over their stacked weights ([W^DQ; W^DKV; W^KR] h, then [W^UQ; W^QR] c^Q
+    with c^Q read in place), and the append and absorption read their inputs in place from
+    those outputs through the row-strided entry points."""
     s = x["shape"]
-    B, H, d_h, d_c, d_R, d = s.B, s.H, s.d_h, s.d_c, s.d_R, x["d"]
+    B, H, d_h, d_c, d_R, d, d_cq = s.B, s.H, s.d_h, s.d_c, s.d_R, x["d"], x["d_cq"]
     w = {k: dev(v) for k, v in x["weights"].items()}
     h = dev(x["h"])
     cache = dev(x["cache"])
     bt, before = dev(x["block_table"]), dev(x["seq_lens_before"])
-    f32 = dict(device="cuda", dtype=torch.float32)
-    c_q = torch.empty(B, x["d_cq"], **f32)
-    q_c = torch.empty(B, H * d_h, **f32)
-    q_r = torch.empty(B, H * d_R, **f32)
-    c_kv = torch.empty(B, d_c, **f32)
-    k_r = torch.empty(B, d_R, **f32)
-    mla.mla_linear(h, w["w_dq"], c_q)
-    mla.mla_linear(c_q, w["w_uq"], q_c)
-    mla.mla_linear(c_q, w["w_qr"], q_r)
-    mla.mla_linear(h, w["w_dkv"], c_kv)
-    mla.mla_linear(h, w["w_kr"], k_r)
-    mla.mla_kv_append(c_kv.view(B, 1, d_c), k_r.view(B, 1, d_R), before, bt, cache, x["rope_base"])
     seq_lens = before + 1
+    f32 = dict(device="cuda", dtype=torch.float32)
     q_lat = torch.empty(B, H, d_c, device="cuda", dtype=torch.bfloat16)
     q_pe = torch.empty(B, H, d_R, device="cuda", dtype=torch.bfloat16)
-    mla.mla_absorb_q(q_c.view(B, H, d_h), w["w_uk"], q_r.view(B, H, d_R), seq_lens,
-                     x["rope_base"], q_lat, q_pe)
+    if stacked:
+        w_a = torch.cat([w["w_dq"], w["w_dkv"], w["w_kr"]]).contiguous()
+        w_b = torch.cat([w["w_uq"], w["w_qr"]]).contiguous()
+        y_a = torch.empty(B, d_cq + d_c + d_R, **f32)
+        y_b = torch.empty(B, H * (d_h + d_R), **f32)
+        mla.mla_linear(h, w_a, y_a)
+        mla.mla_linear_strided(y_a[:, :d_cq], w_b, y_b)
+        mla.mla_kv_append_strided(y_a[:, d_cq:d_cq + d_c].unsqueeze(1),
+                                  y_a[:, d_cq + d_c:].unsqueeze(1), before, bt, cache,
+                                  x["rope_base"])
+        mla.mla_absorb_q_strided(y_b[:, :H * d_h].view(B, H, d_h), w["w_uk"],
+                                 y_b[:, H * d_h:].view(B, H, d_R), seq_lens, x["rope_base"],
+                                 q_lat, q_pe)
+    else:
+        c_q = torch.empty(B, d_cq, **f32)
+        q_c = torch.empty(B, H * d_h, **f32)
+        q_r = torch.empty(B, H * d_R, **f32)
+        c_kv = torch.empty(B, d_c, **f32)
+        k_r = torch.empty(B, d_R, **f32)
+        mla.mla_linear(h, w["w_dq"], c_q)
+        mla.mla_linear(c_q, w["w_uq"], q_c)
+        mla.mla_linear(c_q, w["w_qr"], q_r)
+        mla.mla_linear(h, w["w_dkv"], c_kv)
+        mla.mla_linear(h, w["w_kr"], k_r)
+        mla.mla_kv_append(c_kv.view(B, 1, d_c), k_r.view(B, 1, d_R), before, bt, cache,
+                          x["rope_base"])
+        mla.mla_absorb_q(q_c.view(B, H, d_h), w["w_uk"], q_r.view(B, H, d_R), seq_lens,
+                         x["rope_base"], q_lat, q_pe)
     ws = torch.empty(max(1, mla.mla_decode_workspace_bytes(B, H, d_c, S)), dtype=torch.uint8, device="cuda")
     o_lat = torch.empty(B, H, d_c, **f32)
     mla.mla_decode(q_lat, q_pe, cache, bt, seq_lens, x["scale"], S, ws, o_lat)
@@ -502,12 +520,13 @@ def layer_on_gpu(mla, x, S):
 
 
 @pytest.mark.slow
-def test_full_layer_b64_t2k_sampled(mla):
+@pytest.mark.parametrize("stacked", [False, True], ids=["separate", "stacked"])
+def test_full_layer_b64_t2k_sampled(mla, stacked):
     """Full layer at d=5120, H=128, B=64, 2048 prior tokens + 1 appended: all 64 rows of
     u on the GPU; sequences 0 and 37 through the oracle's expanded path."""
     x = W.layer_b64_t2k()
-    say("layer_b64_t2k")
-    u, cache = layer_on_gpu(mla, x, S=4)
+    say(f"layer_b64_t2k stacked={stacked}")
+    u, cache = layer_on_gpu(mla, x, S=4, stacked=stacked)
     pick = [0, 37]
     ref = oracle.decode_layer(W.to_f64(x["h"]), {k: W.to_f64(v) for k, v in x["weights"].items()},
                               W.to_f64(x["cache"]), x["block_table"].numpy(),
@@ -523,11 +542,12 @@ def test_full_layer_b64_t2k_sampled(mla):
         assert_bf16(row, want, "appended row")
 
 
-def test_small_layer_chain(mla):
+@pytest.mark.parametrize("stacked", [False, True], ids=["separate", "stacked"])
+def test_small_layer_chain(mla, stacked):
     """A small layer (d=256, H=16, d_c=512, d_R=64, B=5, 100 prior tokens) end to end on all rows."""
     x = W.layer_b64_t2k(seed=21, B=5, T=100, d=256, H=16, d_cq=96)
-    say("small layer")
-    u, _ = layer_on_gpu(mla, x, S=2)
+    say(f"small layer stacked={stacked}")
+    u, _ = layer_on_gpu(mla, x, S=2, stacked=stacked)
     ref = oracle.decode_layer(W.to_f64(x["h"]), {k: W.to_f64(v) for k, v in x["weights"].items()},
                               W.to_f64(x["cache"]), x["block_table"].numpy(),
                               x["seq_lens_before"].numpy(), x["shape"].d_h, x["shape"].d_R,
@@ -693,3 +713,69 @@ def test_absorb_mfma_against_oracle(mla):
     assert_bf16(host64(q_pe), ref_pe, "q_pe")
     m, _ = errors(host64(q_pe), ref_pe)
     assert m <= float(np.abs(ref_pe).max()) * 2.0 ** -8, m
+
+
+def test_strided_entry_points(mla):
+    """The row-strided entry points on views into wider buffers.  mla_linear_strided
+    against numpy fp64 matmul on each kernel family (persistent, activation-stationary,
+    tile-grid, fp32 VALU), with the columns of y's buffer outside the view left untouched;
+    mla_kv_append_strided and mla_absorb_q_strided bit-identical to their dense forms on
+    the same values (same kernels, same arithmetic), and the absorption with a row stride
+    the MFMA path cannot take (not a multiple of 4) against the oracle."""
+    g = torch.Generator().manual_seed(77)
+    for (M, N, K, xdt) in [(64, 2112, 5120, torch.float32),    # [W^DQ; W^DKV; W^KR] shape
+                           (64, 24576, 1536, torch.float32),   # [W^UQ; W^QR] shape
+                           (5, 192, 256, torch.bfloat16),
+                           (3, 70, 33, torch.float32)]:
+        say(f"linear strided M={M} N={N} K={K} x={xdt}")
+        xb = torch.randn(M, K + 24, generator=g).to(xdt)
+        w = (torch.randn(N, K, generator=g) / math.sqrt(K)).to(torch.bfloat16)
+        yb = torch.full((M, N + 40), 7.0, device="cuda")
+        mla.mla_linear_strided(dev(xb)[:, 8:8 + K], dev(w), yb[:, 16:16 + N])
+        torch.cuda.synchronize()
+        ref = W.to_f64(xb[:, 8:8 + K]) @ W.to_f64(w).T
+        m, r = errors(host64(yb[:, 16:16 + N]), ref)
+        assert m <= 2e-5 * float(np.abs(ref).max()) + 1e-4 and r <= 1e-5, (M, N, K, m, r)
+        assert bool((yb[:, :16] == 7.0).all()) and bool((yb[:, 16 + N:] == 7.0).all())
+
+    # cache append: c^KV and k^R as column ranges of one [B, n, 1536 + 576 + 8] buffer
+    B, n, d_c, d_R, P = 6, 3, 512, 64, 16
+    say("kv_append strided")
+    src = torch.randn(B, n, 1536 + d_c + d_R + 8, generator=g)
+    before = torch.tensor([0, 5, 16, 29, 47, 60], dtype=torch.int32)
+    bt = torch.randperm(B * 5, generator=g).to(torch.int32).view(B, 5)
+    caches = [torch.zeros(B * 5, P, d_c + d_R, device="cuda", dtype=torch.bfloat16) for _ in range(2)]
+    s_dev = dev(src)
+    mla.mla_kv_append_strided(s_dev[:, :, 1536:1536 + d_c], s_dev[:, :, 1536 + d_c:1536 + d_c + d_R],
+                              dev(before), dev(bt), caches[0], 10000.0)
+    mla.mla_kv_append(dev(src[:, :, 1536:1536 + d_c]), dev(src[:, :, 1536 + d_c:1536 + d_c + d_R]),
+                      dev(before), dev(bt), caches[1], 10000.0)
+    torch.cuda.synchronize()
+    assert torch.equal(caches[0].cpu(), caches[1].cpu())
+    assert int((caches[0] != 0).any(-1).sum()) == B * n
+
+    # absorption: q^C and q^R as the two column ranges of one [B, H (d_h + d_R) + pad] buffer
+    B, H, d_h = 70, 6, 128
+    w_uk = (torch.randn(H * d_h, d_c, generator=g) / math.sqrt(d_h)).to(torch.bfloat16)
+    seq_lens = torch.randint(1, 5000, (B,), generator=g, dtype=torch.int32)
+    for pad, out_dt in [(8, torch.bfloat16), (8, torch.float32), (2, torch.bfloat16)]:
+        say(f"absorb strided pad={pad} out={out_dt}")
+        yb = torch.randn(B, H * (d_h + d_R) + pad, generator=g)
+        yd = dev(yb)
+        q_c, q_r = yd[:, :H * d_h].view(B, H, d_h), yd[:, H * d_h:H * (d_h + d_R)].view(B, H, d_R)
+        outs = [(torch.empty(B, H, d_c, device="cuda", dtype=out_dt),
+                 torch.empty(B, H, d_R, device="cuda", dtype=out_dt)) for _ in range(2)]
+        mla.mla_absorb_q_strided(q_c, dev(w_uk), q_r, dev(seq_lens), 10000.0, *outs[0])
+        torch.cuda.synchronize()
+        ref_pe = np.stack([oracle.rope(W.to_f64(q_r[b].cpu()), int(seq_lens[b]) - 1)
+                           for b in range(B)])
+        if pad % 4 == 0:
+            mla.mla_absorb_q(q_c.contiguous(), dev(w_uk), q_r.contiguous(), dev(seq_lens), 10000.0,
+                             *outs[1])
+            torch.cuda.synchronize()
+            assert torch.equal(outs[0][0].cpu(), outs[1][0].cpu())
+            assert torch.equal(outs[0][1].cpu(), outs[1][1].cpu())
+        ref = np.stack([oracle.absorb_query(W.to_f64(q_c[b].cpu()), W.to_f64(w_uk))
+                        for b in range(B)])
+        assert_bf16(host64(outs[0][0]), ref, "q~ strided")
+        assert_bf16(host64(outs[0][1]), ref_pe, "q_pe strided")
