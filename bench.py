@@ -105,9 +105,10 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     roofline (every step is HBM-bound at this batch); then the whole chain, and the fp64
     oracle's layer on a few of the sequences.  The projections that share an input run as
     one product over their stacked weights ([W^DQ; W^DKV; W^KR] h, [W^UQ; W^QR] c^Q; the
-    weights are stacked once at load time, outside the timing) and the append and the
-    absorption read their inputs in place; the chain of separate products is timed beside
-    it."""
+    weights are stacked once at load time, outside the timing), the append and the
+    absorption read their inputs in place, and in the timed chain the products accumulate
+    into outputs cleared by one fill at its start.  The chain with dense outputs (each
+    product zeroing its own) and the chain of separate products are timed beside it."""
     x = W.layer_b64_t2k()
     s = x["shape"]
     B, H, d_h, d_c, d_R, d, d_cq = s.B, s.H, s.d_h, s.d_c, s.d_R, x["d"], x["d_cq"]
@@ -117,8 +118,10 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     w_b = torch.cat([w["w_uq"], w["w_qr"]]).contiguous()
     h, cache, bt, before = cu(x["h"]), cu(x["cache"]), cu(x["block_table"]), cu(x["seq_lens_before"])
     f32 = dict(device="cuda", dtype=torch.float32)
-    y_a = torch.empty(B, d_cq + d_c + d_R, **f32)
-    y_b = torch.empty(B, H * (d_h + d_R), **f32)
+    n_a, n_b = d_cq + d_c + d_R, H * (d_h + d_R)
+    outs = torch.empty(B * (n_a + n_b + d), **f32)  # y_a, y_b and u, cleared by one fill
+    y_a, y_b = outs[:B * n_a].view(B, n_a), outs[B * n_a:B * (n_a + n_b)].view(B, n_b)
+    u = outs[B * (n_a + n_b):].view(B, d)
     c_q, c_kv, k_r = y_a[:, :d_cq], y_a[:, d_cq:d_cq + d_c], y_a[:, d_cq + d_c:]
     q_c, q_r = y_b[:, :H * d_h].view(B, H, d_h), y_b[:, H * d_h:].view(B, H, d_R)
     seq_lens = before + 1
@@ -126,7 +129,7 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     q_pe = torch.empty(B, H, d_R, device="cuda", dtype=torch.bfloat16)
     S = mla.mla_suggest_num_splits(B, int(seq_lens.max()), 0, 64, 256)
     ws = torch.empty(max(1, mla.mla_decode_workspace_bytes(B, H, d_c, S)), dtype=torch.uint8, device="cuda")
-    o_lat, o_heads, u = torch.empty(B, H, d_c, **f32), torch.empty(B, H, d_h, **f32), torch.empty(B, d, **f32)
+    o_lat, o_heads = torch.empty(B, H, d_c, **f32), torch.empty(B, H, d_h, **f32)
     nb = lambda t: t.numel() * t.element_size()
     tokens = int(seq_lens.sum())
     rows = [
@@ -164,10 +167,33 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
                  seq_lens, x["rope_base"], q_lat, q_pe),
     ] + [c for _, calls, _ in rows[4:] for c in calls]
     chain = [c for _, calls, _ in rows for c in calls]
+
+    # the same calls with the products accumulating into outputs cleared together by one
+    # fill at the start of the layer (y_a, y_b and u share one buffer), so the split-k kernels
+    # launch no zero fills of their own: two kernels fewer on the one stream
+    acc_chain = ([mla.bind(mla.mla_linear_strided, h, w_a, y_a, accumulate=True),
+                  mla.bind(mla.mla_linear_strided, c_q, w_b, y_b, accumulate=True)]
+                 + [rows[i][1][0] for i in (2, 3, 4, 5)]
+                 + [mla.bind(mla.mla_linear_strided, o_heads.view(B, H * d_h), w["w_o"], u,
+                             accumulate=True)])
+
+    def accumulate_chain():
+        outs.zero_()
+        for c in acc_chain:
+            c()
+
+    for c in chain:
+        c()
+    torch.cuda.synchronize()
+    u_dense = u.clone()
+    accumulate_chain()
+    torch.cuda.synchronize()
+    acc_vs_dense = float((u - u_dense).abs().max() / u_dense.abs().max())
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < 0.3:
         for c in chain + separate:
             c()
+        accumulate_chain()
         torch.cuda.synchronize()
 
     def timed(fn, n=20):
@@ -188,8 +214,9 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
         out[name] = {"us": round(us, 2), "bytes_algorithmic": int(byts), "GBps": round(gbps, 1),
                      "roofline_frac": round(gbps / HBM_PEAK_GBPS, 4)}
         total_bytes += byts
-    chain_us = timed(lambda: [c() for c in chain])
+    dense_us = timed(lambda: [c() for c in chain])
     separate_us = timed(lambda: [c() for c in separate])
+    chain_us = timed(accumulate_chain)
 
     # the survey's fourth next item, measured only: offline absorption folds W^UK_i^T into
     # W^UQ_i ([H d_c, d_c^Q], 201 MB of bf16 weights, prepared once here in fp32 and rounded
@@ -219,7 +246,11 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
            "chain_GBps": round(total_bytes / chain_us / 1e3, 1),
            "chain_roofline_frac": round(total_bytes / chain_us / 1e3 / HBM_PEAK_GBPS, 4),
            "sequences_per_s": round(B / (chain_us * 1e-6), 1),
-           "chain_separate_products_us": round(separate_us, 2)}
+           "chain_schedule": "one stream; stacked products accumulating into outputs cleared "
+                             "by one fill at the start",
+           "chain_dense_outputs_us": round(dense_us, 2),
+           "chain_separate_products_us": round(separate_us, 2),
+           "accumulate_vs_dense_max_rel_diff": round(acc_vs_dense, 6)}
     if oracle_seqs > 0:
         import oracle
         wf = {k: W.to_f64(v) for k, v in x["weights"].items()}

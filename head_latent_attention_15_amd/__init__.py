@@ -65,7 +65,8 @@ _SIGNATURES = {
     "mla_decode": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _SZ, _P, _P, _I32, _P]),
     "mla_out_proj": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "mla_linear": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P]),
-    "mla_linear_strided": (_I32, [_P, _I32, _I64, _P, _I32, _I32, _I32, _I32, _P, _I64, _P]),
+    "mla_linear_strided": (_I32, [_P, _I32, _I64, _P, _I32, _I32, _I32, _I32, _P, _I64, _I32,
+                                  _P]),
     "mla_linear_planned": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _I32, _I32, _I32,
                                   _I32, _P]),
     "mla_validate_indices": (_I32, [_P, _P, _SP, _P, _P]),
@@ -452,9 +453,10 @@ def mla_linear(x, w, y, stream=None):
                           _stream(stream))
 
 
-def mla_linear_strided(x, w, y, stream=None):
-    """y = x w^T on row-strided views: x [M,K], y [M,N] fp32 with unit column stride (e.g.
-    column ranges of wider buffers); w [N,K] dense (e.g. several nn.Linear weights stacked)."""
+def mla_linear_strided(x, w, y, accumulate=False, stream=None):
+    """y = x w^T (accumulate: y += x w^T) on row-strided views: x [M,K], y [M,N] fp32 with
+    unit column stride (e.g. column ranges of wider buffers); w [N,K] dense (e.g. several
+    nn.Linear weights stacked)."""
     torch = _torch()
     M, K = x.shape
     N = w.shape[0]
@@ -462,7 +464,8 @@ def mla_linear_strided(x, w, y, stream=None):
     x_ptr, ldx = _dev_rows(x, "x", None, 2, 1)
     y_ptr, ldy = _dev_rows(y, "y", torch.float32, 2, 1)
     _invoke("mla_linear_strided", x_ptr, _dtype_code(x), ldx, _dev(w, "w", None, 2),
-                                  _dtype_code(w), M, N, K, y_ptr, ldy, _stream(stream))
+                                  _dtype_code(w), M, N, K, y_ptr, ldy, int(bool(accumulate)),
+                                  _stream(stream))
 
 
 def mla_linear_planned(x, w, y, kernel, tile, split, ring, stream=None):

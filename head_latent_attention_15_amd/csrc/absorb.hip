@@ -8,7 +8,9 @@
 // (x = hi + lo, about 16 significant bits of the fp32 input; every product with a bf16
 // weight is exact in fp32), then computes the 128 x 64 block of q~^T on
 // v_mfma_f32_16x16x32_bf16: A = W^UK_i^T (c x j), B = q^C_i^T (j x b).  Each lane's C
-// entries are four consecutive c of one b, written as one 8-byte bf16 store.
+// entries are four consecutive c of one b, written as one 8-byte bf16 store.  At the
+// DeepSeek-V2 sizes the same launch also rotates the query's RoPE part (qiita.com/joule,
+// "RoPE の扱い"), so the absorption step is one kernel.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -37,16 +39,46 @@ __device__ __forceinline__ unsigned pack2(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+// The query RoPE rides along when ROPE: for d_c = 512 (four column blocks) and d_R = 64,
+// column block x of (row block, head) rotates q^R rows b0 + 16 x .. + 15, two pairs per
+// thread; their loads go out before the weight and q^C loads and the fp64 rotation runs
+// while those are in flight.
+struct AbsorbRope {
+  const float* q_r;
+  int64_t ld_r;
+  const int32_t* seq_lens;
+  float base;
+  bf16raw* q_pe;
+};
+constexpr int AB_DR = 64;
+
+template <bool ROPE>
 __global__ __launch_bounds__(256) void absorb_kernel(const float* __restrict__ q_c,
                                                      const bf16raw* __restrict__ w_uk,
                                                      bf16raw* __restrict__ q_lat, int B, int H,
-                                                     int d_c, int64_t ld_q) {
+                                                     int d_c, int64_t ld_q, AbsorbRope rp) {
   __shared__ __attribute__((aligned(16))) char smem[AB_LDS];
   lds_char_t* const lsm = (lds_char_t*)smem;
   const int c0 = blockIdx.x * 128, b0 = blockIdx.y * 64, h = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
+
+  // ---- RoPE inputs: pair e = tid + 256 p is row b0 + 16 blockIdx.x + e / 32, pair e % 32
+  //      (rows past B load row B - 1 and store nothing: unconditional loads keep the wait
+  //      for them apart from the weight loads issued next)
+  float2 rv[2] = {};
+  int rpos[2] = {};
+  if constexpr (ROPE) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int e = tid + 256 * p, k = e & 31;
+      const int b = min(b0 + 16 * static_cast<int>(blockIdx.x) + (e >> 5), B - 1);
+      rv[p] = *reinterpret_cast<const float2*>(rp.q_r + static_cast<int64_t>(b) * rp.ld_r +
+                                               h * AB_DR + 2 * k);
+      rpos[p] = rp.seq_lens[b] - 1;
+    }
+  }
 
   // ---- W^UK_i rows j, columns c0 .. c0 + 127 -> LDS [c][j]: thread t moves 16-byte
   //      pieces q = t + 256 e (row j = q / 16, columns 8 (q % 16) .. + 7)
@@ -68,6 +100,20 @@ __global__ __launch_bounds__(256) void absorb_kernel(const float* __restrict__ q
   for (int i = 0; i < 8; ++i) {
     xv[i] = *reinterpret_cast<const f32x4_t*>(xsrc + 4 * i);
     if (!xr_ok) xv[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // ---- RoPE while the weight and q^C loads are in flight (the scheduling barrier keeps
+  //      its arithmetic, and so its wait, below the last load)
+  if constexpr (ROPE) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int e = tid + 256 * p, b = b0 + 16 * blockIdx.x + (e >> 5), k = e & 31;
+      float y0, y1;
+      rope_pair(rv[p].x, rv[p].y, rpos[p], k, AB_DR, rp.base, &y0, &y1);
+      if (b < B)
+        *reinterpret_cast<unsigned*>(rp.q_pe + (static_cast<int64_t>(b) * H + h) * AB_DR +
+                                     2 * k) = pack2(y0, y1);
+    }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -143,11 +189,25 @@ bool absorb_mfma_supported(int B, int H, int d_h, int d_c, const void* q_c, int6
          (a & 15) == 0 && ld_q % 4 == 0;
 }
 
+bool absorb_rope_fusable(int d_c, int d_R, const float* q_r, int64_t ld_r, const void* q_pe) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(q_r) | reinterpret_cast<uintptr_t>(q_pe);
+  return d_c == 4 * 128 && d_R == AB_DR && (a & 7) == 0 && ld_r % 2 == 0;
+}
+
 hipError_t launch_absorb_mfma(const float* q_c, int64_t ld_q, const void* w_uk, void* q_lat,
-                              int B, int H, int d_c, hipStream_t s) {
-  hipLaunchKernelGGL(absorb_kernel, dim3(d_c / 128, (B + 63) / 64, H), dim3(256), 0, s, q_c,
-                     static_cast<const bf16raw*>(w_uk), static_cast<bf16raw*>(q_lat), B, H, d_c,
-                     ld_q);
+                              int B, int H, int d_c, const float* q_r, int64_t ld_r,
+                              const int32_t* seq_lens, float rope_base, void* q_pe,
+                              hipStream_t s) {
+  const dim3 grid(d_c / 128, (B + 63) / 64, H);
+  const AbsorbRope rp{q_r, ld_r, seq_lens, rope_base, static_cast<bf16raw*>(q_pe)};
+  if (q_r)
+    hipLaunchKernelGGL(absorb_kernel<true>, grid, dim3(256), 0, s, q_c,
+                       static_cast<const bf16raw*>(w_uk), static_cast<bf16raw*>(q_lat), B, H,
+                       d_c, ld_q, rp);
+  else
+    hipLaunchKernelGGL(absorb_kernel<false>, grid, dim3(256), 0, s, q_c,
+                       static_cast<const bf16raw*>(w_uk), static_cast<bf16raw*>(q_lat), B, H,
+                       d_c, ld_q, rp);
   return hipGetLastError();
 }
 

@@ -214,7 +214,7 @@ template <typename XT, int TN, int R>
 hipError_t launch_t(const GemmArgs& g, int KS, hipStream_t s) {
   const int kper = g.K / KS;
   const int nb = (g.N + 64 * TN - 1) / (64 * TN), mb = (g.M + 63) / 64;
-  if (KS > 1) {
+  if (KS > 1 && !g.accumulate) {
     const int64_t rows = static_cast<int64_t>(g.batch) * g.M;
     const int gx = static_cast<int>(std::min<int64_t>((g.N + 1023) / 1024, 64));
     const int gy = static_cast<int>(std::min<int64_t>(rows, 4096));
@@ -224,7 +224,7 @@ hipError_t launch_t(const GemmArgs& g, int KS, hipStream_t s) {
   hipLaunchKernelGGL((gemm_rows_kernel<XT, TN, R>), dim3(nb, mb, g.batch * KS), dim3(256), 0, s,
                      static_cast<const XT*>(g.x), g.ldx, g.sx, static_cast<const bf16raw*>(g.w),
                      g.ldw, g.sw, static_cast<float*>(g.y), g.ldy, g.sy, g.M, g.N, g.K, KS,
-                     kper, KS > 1 ? 1 : 0);
+                     kper, KS > 1 || g.accumulate ? 1 : 0);
   return hipGetLastError();
 }
 

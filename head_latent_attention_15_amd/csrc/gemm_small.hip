@@ -17,7 +17,8 @@ constexpr int GT_M = 64, GT_N = 64, GT_K = 32;
 template <typename XT, typename WT, typename YT, bool W_NK>
 __global__ __launch_bounds__(256) void gemm_small_kernel(
     const XT* __restrict__ x, int64_t ldx, int64_t sx, const WT* __restrict__ w, int64_t ldw,
-    int64_t sw, YT* __restrict__ y, int64_t ldy, int64_t sy, int M, int N, int K) {
+    int64_t sw, YT* __restrict__ y, int64_t ldy, int64_t sy, int M, int N, int K,
+    int accumulate) {
   __shared__ float xs[GT_K][GT_M + 4];
   __shared__ float ws[GT_K][GT_N + 4];
   const int z = blockIdx.z;
@@ -75,7 +76,9 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int gn = n0 + tn + j;
-      if (gn < N) st(y + gm * ldy + gn, acc[i][j]);
+      if (gn >= N) continue;
+      YT* dst = y + gm * ldy + gn;
+      st(dst, accumulate ? acc[i][j] + ld(dst) : acc[i][j]);
     }
   }
 }
@@ -86,11 +89,13 @@ static hipError_t launch3(const GemmArgs& g, hipStream_t s) {
   if (g.w_nk) {
     hipLaunchKernelGGL((gemm_small_kernel<XT, WT, YT, true>), grid, dim3(256), 0, s,
                        static_cast<const XT*>(g.x), g.ldx, g.sx, static_cast<const WT*>(g.w),
-                       g.ldw, g.sw, static_cast<YT*>(g.y), g.ldy, g.sy, g.M, g.N, g.K);
+                       g.ldw, g.sw, static_cast<YT*>(g.y), g.ldy, g.sy, g.M, g.N, g.K,
+                       g.accumulate);
   } else {
     hipLaunchKernelGGL((gemm_small_kernel<XT, WT, YT, false>), grid, dim3(256), 0, s,
                        static_cast<const XT*>(g.x), g.ldx, g.sx, static_cast<const WT*>(g.w),
-                       g.ldw, g.sw, static_cast<YT*>(g.y), g.ldy, g.sy, g.M, g.N, g.K);
+                       g.ldw, g.sw, static_cast<YT*>(g.y), g.ldy, g.sy, g.M, g.N, g.K,
+                       g.accumulate);
   }
   return hipGetLastError();
 }

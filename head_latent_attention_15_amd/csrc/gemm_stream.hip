@@ -336,8 +336,9 @@ hipError_t launch_t(const GemmArgs& g, const StreamArgs& a, int grid, hipStream_
   const int64_t rows = static_cast<int64_t>(g.batch) * g.M;
   const int gx = static_cast<int>(std::min<int64_t>((g.N + 1023) / 1024, 64));
   const int gy = static_cast<int>(std::min<int64_t>(rows, 4096));
-  hipLaunchKernelGGL(zero_rows_stream, dim3(gx, gy), dim3(256), 0, s, static_cast<float*>(g.y),
-                     g.ldy, g.sy, g.M, g.N, g.batch);
+  if (!g.accumulate)
+    hipLaunchKernelGGL(zero_rows_stream, dim3(gx, gy), dim3(256), 0, s,
+                       static_cast<float*>(g.y), g.ldy, g.sy, g.M, g.N, g.batch);
   hipLaunchKernelGGL((gemm_stream_kernel<XT, TN, R>), dim3(grid), dim3(512), 0, s,
                      static_cast<const XT*>(g.x), static_cast<const bf16raw*>(g.w),
                      static_cast<float*>(g.y), a);

@@ -267,8 +267,9 @@ __global__ __launch_bounds__(256) void zero_rows_xs(float* __restrict__ y, int64
 template <typename XT, int TN, int S>
 hipError_t launch_t(const GemmArgs& g, const XsArgs& a, int grid, hipStream_t s) {
   const int gx = std::min((g.N + 1023) / 1024, 64);
-  hipLaunchKernelGGL(zero_rows_xs, dim3(gx, std::min(g.M, 4096)), dim3(256), 0, s,
-                     static_cast<float*>(g.y), g.ldy, g.M, g.N);
+  if (!g.accumulate)
+    hipLaunchKernelGGL(zero_rows_xs, dim3(gx, std::min(g.M, 4096)), dim3(256), 0, s,
+                       static_cast<float*>(g.y), g.ldy, g.M, g.N);
   hipLaunchKernelGGL((gemm_xs_kernel<XT, TN, S>), dim3(grid), dim3(512), 0, s,
                      static_cast<const XT*>(g.x), static_cast<const bf16raw*>(g.w),
                      static_cast<float*>(g.y), a);

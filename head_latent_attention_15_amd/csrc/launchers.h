@@ -37,11 +37,13 @@ hipError_t launch_splitk_combine(const void* o_part, int part_bf16, const float*
 // Batched small-M GEMM: y[z][m][n] = sum_k x[z][m][k] * W_z(n, k), with
 // W_z(n, k) = w[z*sw + n*ldw + k] when w_nk, else w[z*sw + k*ldw + n].
 // x/w dtype: 0 = fp32, 1 = bf16; y dtype likewise.
+// accumulate: y += the product (y holds its prior values; fp32 y only) instead of y = it.
 struct GemmArgs {
   const void* x; int64_t ldx, sx; int x_bf16;
   const void* w; int64_t ldw, sw; int w_bf16; bool w_nk;
   void* y; int64_t ldy, sy; int y_bf16;
   int M, N, K, batch;
+  int accumulate = 0;
 };
 hipError_t launch_gemm_small(const GemmArgs& g, hipStream_t s);
 // Same product on bf16 MFMA for bf16 nn.Linear-layout weights (w_nk), fp32 y and K a
@@ -72,11 +74,15 @@ hipError_t launch_gemm_xs_with(const GemmArgs& g, int tn, int s, int grid, hipSt
 hipError_t launch_gemm_xs(const GemmArgs& g, hipStream_t st);
 
 // Query absorption q~_i = W^UK_i^T q^C_i on bf16 MFMA (bf16 W^UK, bf16 q~, d_h = 128);
-// row b of q_c starts at q_c + b ld_q, its heads d_h apart.
+// row b of q_c starts at q_c + b ld_q, its heads d_h apart.  With q_r non-NULL (only where
+// absorb_rope_fusable) the same launch writes q_pe = RoPE(q_r, seq_lens - 1) in bf16.
 bool absorb_mfma_supported(int B, int H, int d_h, int d_c, const void* q_c, int64_t ld_q,
                            const void* w_uk, const void* q_lat);
+bool absorb_rope_fusable(int d_c, int d_R, const float* q_r, int64_t ld_r, const void* q_pe);
 hipError_t launch_absorb_mfma(const float* q_c, int64_t ld_q, const void* w_uk, void* q_lat,
-                              int B, int H, int d_c, hipStream_t s);
+                              int B, int H, int d_c, const float* q_r, int64_t ld_r,
+                              const int32_t* seq_lens, float rope_base, void* q_pe,
+                              hipStream_t s);
 
 hipError_t launch_rope_rows(const float* x, int64_t rows, int rows_per_seq, int d_R,
                             int64_t ld_seq, const int32_t* seq_lens, int pos_offset, float base,

@@ -283,10 +283,14 @@ static mla_status_t absorb_q(const char* fn, const float* q_c, int64_t ld_qc, co
   g.M = B; g.N = d_c; g.K = d_h; g.batch = H;
   const bool mfma = w_dtype == MLA_BF16 && out_dtype == MLA_BF16 &&
                     mla::absorb_mfma_supported(B, H, d_h, d_c, q_c, ld_qc, w_uk, q_lat);
-  mla_status_t st = launched(mfma ? mla::launch_absorb_mfma(q_c, ld_qc, w_uk, q_lat, B, H, d_c, s)
-                                  : mla::launch_gemm_small(g, s),
-                             "absorb GEMM");
-  if (st != MLA_OK || !q_r) return st;
+  // the MFMA kernel also applies the query RoPE where the shape allows (one launch)
+  const bool fused = mfma && q_r && mla::absorb_rope_fusable(d_c, d_R, q_r, ld_qr, q_pe);
+  mla_status_t st = launched(
+      mfma ? mla::launch_absorb_mfma(q_c, ld_qc, w_uk, q_lat, B, H, d_c, fused ? q_r : nullptr,
+                                     ld_qr, seq_lens, rope_base, q_pe, s)
+           : mla::launch_gemm_small(g, s),
+      "absorb GEMM");
+  if (st != MLA_OK || !q_r || fused) return st;
   return launched(mla::launch_rope_rows(q_r, static_cast<int64_t>(B) * H, H, d_R, ld_qr, seq_lens,
                                         -1, rope_base, q_pe, out_dtype == MLA_BF16, s),
                   "query RoPE");
@@ -381,7 +385,7 @@ mla_status_t mla_out_proj(const float* o_lat, const void* w_uv, const void* w_o,
 
 static mla_status_t linear(const char* fn, const void* x, mla_dtype_t x_dtype, int64_t ldx,
                            const void* w, mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K,
-                           float* y, int64_t ldy, void* stream) {
+                           float* y, int64_t ldy, int32_t accumulate, void* stream) {
   if (!x || !w || !y) return fail(MLA_ERR_NULL, "%s: a required pointer is NULL", fn);
   if (M < 1 || N < 1 || K < 1) return fail(MLA_ERR_SHAPE, "%s: sizes must be >= 1", fn);
   if (M > 65535 * 64) return fail(MLA_ERR_SHAPE, "%s: M %d too large", fn, M);
@@ -395,19 +399,21 @@ static mla_status_t linear(const char* fn, const void* x, mla_dtype_t x_dtype, i
   g.w = w; g.ldw = K; g.sw = 0; g.w_bf16 = w_dtype == MLA_BF16; g.w_nk = true;
   g.y = y; g.ldy = ldy; g.sy = 0; g.y_bf16 = 0;
   g.M = M; g.N = N; g.K = K; g.batch = 1;
+  g.accumulate = accumulate != 0;
   return launched(gemm(g, as_stream(stream)), "linear GEMM");
 }
 
 mla_status_t mla_linear(const void* x, mla_dtype_t x_dtype, const void* w,
                         mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K, float* y,
                         void* stream) {
-  return linear("mla_linear", x, x_dtype, K, w, w_dtype, M, N, K, y, N, stream);
+  return linear("mla_linear", x, x_dtype, K, w, w_dtype, M, N, K, y, N, 0, stream);
 }
 
 mla_status_t mla_linear_strided(const void* x, mla_dtype_t x_dtype, int64_t ldx, const void* w,
                                 mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K, float* y,
-                                int64_t ldy, void* stream) {
-  return linear("mla_linear_strided", x, x_dtype, ldx, w, w_dtype, M, N, K, y, ldy, stream);
+                                int64_t ldy, int32_t accumulate, void* stream) {
+  return linear("mla_linear_strided", x, x_dtype, ldx, w, w_dtype, M, N, K, y, ldy, accumulate,
+                stream);
 }
 
 mla_status_t mla_linear_planned(const void* x, mla_dtype_t x_dtype, const void* w,

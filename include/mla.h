@@ -250,16 +250,20 @@ mla_status_t mla_linear(const void* x, mla_dtype_t x_dtype, const void* w,
                         mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K, float* y,
                         void* stream);
 
-/* mla_linear with row strides: x row m at x + m * ldx, y row m at y + m * ldy (elements,
- * ldx >= K, ldy >= N; only columns 0 .. N-1 of each y row are written).  Projections that
- * read the same input can then run as one product over their stacked weights, e.g.
- * [W^DQ; W^DKV; W^KR] h (one launch instead of three, the three results side by side in
- * each row of y), and the next product can read its input columns in place, e.g. c^Q as
- * the first d_c^Q columns of that y.  x and y must not overlap.
+/* mla_linear with row strides and an accumulate option: x row m at x + m * ldx, y row m at
+ * y + m * ldy (elements, ldx >= K, ldy >= N; only columns 0 .. N-1 of each y row are
+ * touched).  accumulate = 0: y = x w^T, as mla_linear.  accumulate != 0: y += x w^T, y
+ * holding its prior values (with y zeroed beforehand this is the same product; the split-k
+ * kernels then launch no zero fill of their own, so a caller can clear y earlier, on
+ * another stream, off the critical path).  Projections that read the same input can run as
+ * one product over their stacked weights, e.g. [W^DQ; W^DKV; W^KR] h (one launch instead
+ * of three, the three results side by side in each row of y), and the next product can
+ * read its input columns in place, e.g. c^Q as the first d_c^Q columns of that y.  x and y
+ * must not overlap.
  * Errors: as mla_linear, and SHAPE for ldx < K or ldy < N. */
 mla_status_t mla_linear_strided(const void* x, mla_dtype_t x_dtype, int64_t ldx, const void* w,
                                 mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K, float* y,
-                                int64_t ldy, void* stream);
+                                int64_t ldy, int32_t accumulate, void* stream);
 
 /* Device-side check of the paging indices: counts sequences whose seq_len is negative or
  * exceeds max_pages_per_seq*page_size, and referenced block-table entries outside

@@ -191,9 +191,9 @@ def test_strided_validation():
     """The row-strided entry points reject strides shorter than a row before launching."""
     L = mla.lib
     shp = _shape()
-    assert L.mla_linear_strided(FAKE, 0, 3, FAKE, 1, 4, 4, 4, FAKE, 4, None) == mla.MLA_ERR_SHAPE
-    assert L.mla_linear_strided(FAKE, 0, 4, FAKE, 1, 4, 4, 4, FAKE, 3, None) == mla.MLA_ERR_SHAPE
-    assert L.mla_linear_strided(None, 0, 4, FAKE, 1, 4, 4, 4, FAKE, 4, None) == mla.MLA_ERR_NULL
+    assert L.mla_linear_strided(FAKE, 0, 3, FAKE, 1, 4, 4, 4, FAKE, 4, 0, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_linear_strided(FAKE, 0, 4, FAKE, 1, 4, 4, 4, FAKE, 3, 1, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_linear_strided(None, 0, 4, FAKE, 1, 4, 4, 4, FAKE, 4, 0, None) == mla.MLA_ERR_NULL
     d_c, d_R = shp.d_latent, shp.d_rope
     assert L.mla_kv_append_strided(FAKE, d_c - 1, FAKE, d_R, 1, FAKE, FAKE, FAKE, 1e4,
                                    ctypes.byref(shp), 1, None) == mla.MLA_ERR_SHAPE

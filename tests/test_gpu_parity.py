@@ -718,9 +718,11 @@ def test_absorb_mfma_against_oracle(mla):
 def test_strided_entry_points(mla):
     """The row-strided entry points on views into wider buffers.  mla_linear_strided
     against numpy fp64 matmul on each kernel family (persistent, activation-stationary,
-    tile-grid, fp32 VALU), with the columns of y's buffer outside the view left untouched;
+    tile-grid, fp32 VALU), then again with accumulate on top of that result, with the
+    columns of y's buffer outside the view left untouched;
     mla_kv_append_strided and mla_absorb_q_strided bit-identical to their dense forms on
-    the same values (same kernels, same arithmetic), and the absorption with a row stride
+    the same values (same kernels, same arithmetic), the query RoPE done inside the
+    absorption kernel bit-identical to the RoPE kernel, and the absorption with a row stride
     the MFMA path cannot take (not a multiple of 4) against the oracle."""
     g = torch.Generator().manual_seed(77)
     for (M, N, K, xdt) in [(64, 2112, 5120, torch.float32),    # [W^DQ; W^DKV; W^KR] shape
@@ -736,6 +738,12 @@ def test_strided_entry_points(mla):
         ref = W.to_f64(xb[:, 8:8 + K]) @ W.to_f64(w).T
         m, r = errors(host64(yb[:, 16:16 + N]), ref)
         assert m <= 2e-5 * float(np.abs(ref).max()) + 1e-4 and r <= 1e-5, (M, N, K, m, r)
+        assert bool((yb[:, :16] == 7.0).all()) and bool((yb[:, 16 + N:] == 7.0).all())
+        # accumulate: y += x w^T on top of the first result (no zero fill), so y = 2 x w^T
+        mla.mla_linear_strided(dev(xb)[:, 8:8 + K], dev(w), yb[:, 16:16 + N], accumulate=True)
+        torch.cuda.synchronize()
+        m, r = errors(host64(yb[:, 16:16 + N]), 2 * ref)
+        assert m <= 4e-5 * float(np.abs(ref).max()) + 2e-4 and r <= 1e-5, ("acc", M, N, K, m, r)
         assert bool((yb[:, :16] == 7.0).all()) and bool((yb[:, 16 + N:] == 7.0).all())
 
     # cache append: c^KV and k^R as column ranges of one [B, n, 1536 + 576 + 8] buffer
@@ -775,6 +783,17 @@ def test_strided_entry_points(mla):
             torch.cuda.synchronize()
             assert torch.equal(outs[0][0].cpu(), outs[1][0].cpu())
             assert torch.equal(outs[0][1].cpu(), outs[1][1].cpu())
+        if pad == 8 and out_dt == torch.bfloat16:
+            # q^R at an odd row stride cannot ride along in the absorption kernel: the RoPE
+            # then runs as its own kernel and must give the same bits as the fused one
+            odd = torch.empty(B, H * d_R + 1, device="cuda")
+            odd[:, :H * d_R] = q_r.reshape(B, H * d_R)
+            sep = torch.empty(B, H, d_R, device="cuda", dtype=out_dt)
+            mla.mla_absorb_q_strided(q_c, dev(w_uk), odd[:, :H * d_R].view(B, H, d_R),
+                                     dev(seq_lens), 10000.0, outs[1][0], sep)
+            torch.cuda.synchronize()
+            assert torch.equal(sep.cpu(), outs[0][1].cpu())
+            assert torch.equal(outs[1][0].cpu(), outs[0][0].cpu())
         ref = np.stack([oracle.absorb_query(W.to_f64(q_c[b].cpu()), W.to_f64(w_uk))
                         for b in range(B)])
         assert_bf16(host64(outs[0][0]), ref, "q~ strided")
