@@ -106,9 +106,12 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     oracle's layer on a few of the sequences.  The projections that share an input run as
     one product over their stacked weights ([W^DQ; W^DKV; W^KR] h, [W^UQ; W^QR] c^Q; the
     weights are stacked once at load time, outside the timing), the append and the
-    absorption read their inputs in place, and in the timed chain the products accumulate
-    into outputs cleared by one fill at its start.  The chain with dense outputs (each
-    product zeroing its own) and the chain of separate products are timed beside it."""
+    absorption read their inputs in place, the split-K combine is fused with W^UV, and in
+    the timed chain the products accumulate into outputs cleared by one fill at its start.
+    Timed beside it: the chain with dense outputs (each product zeroing its own), the chain
+    with the combine and W^UV as two launches, and the chain of separate products.  The
+    fused step's algorithmic bytes are W^UV and its output: the combined latent is never
+    stored."""
     x = W.layer_b64_t2k()
     s = x["shape"]
     B, H, d_h, d_c, d_R, d, d_cq = s.B, s.H, s.d_h, s.d_c, s.d_R, x["d"], x["d_cq"]
@@ -129,6 +132,8 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     q_pe = torch.empty(B, H, d_R, device="cuda", dtype=torch.bfloat16)
     S = mla.mla_suggest_num_splits(B, int(seq_lens.max()), 0, 64, 256)
     ws = torch.empty(max(1, mla.mla_decode_workspace_bytes(B, H, d_c, S)), dtype=torch.uint8, device="cuda")
+    o_part = torch.empty(B, H, S, d_c, device="cuda", dtype=torch.bfloat16)
+    lse_part = torch.empty(B, H, S, **f32)
     o_lat, o_heads = torch.empty(B, H, d_c, **f32), torch.empty(B, H, d_h, **f32)
     nb = lambda t: t.numel() * t.element_size()
     tokens = int(seq_lens.sum())
@@ -143,15 +148,22 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
         ("1 mla_absorb_q_strided", [mla.bind(mla.mla_absorb_q_strided, q_c, w["w_uk"], q_r, seq_lens,
                                              x["rope_base"], q_lat, q_pe)],
          nb(w["w_uk"]) + B * H * (d_h + d_R) * 4 + nb(q_lat) + nb(q_pe)),
-        (f"3+4 mla_decode (attention + combine, {S} splits)",
-         [mla.bind(mla.mla_decode, q_lat, q_pe, cache, bt, seq_lens, x["scale"], S, ws, o_lat)],
-         tokens * (d_c + d_R) * 2 + nb(q_lat) + nb(q_pe) + nb(o_lat)),
-        ("5 mla_out_proj W^UV", [mla.bind(mla.mla_out_proj, o_lat, w["w_uv"], None, o_heads)],
-         nb(w["w_uv"]) + nb(o_lat) + nb(o_heads)),
+        (f"3 mla_decode_attn ({S} splits, bf16 partials)",
+         [mla.bind(mla.mla_decode_attn, q_lat, q_pe, cache, bt, seq_lens, x["scale"], S, o_part,
+                   lse_part)],
+         tokens * (d_c + d_R) * 2 + nb(q_lat) + nb(q_pe)),
+        ("4+5 mla_combine_out_proj (combine fused with W^UV)",
+         [mla.bind(mla.mla_combine_out_proj, o_part, lse_part, w["w_uv"], o_heads)],
+         nb(w["w_uv"]) + nb(o_heads)),
         ("6 W^O (mla_linear on the concatenated heads)",
          [mla.bind(mla.mla_linear, o_heads.view(B, H * d_h), w["w_o"], u)],
          nb(w["w_o"]) + nb(o_heads) + nb(u)),
     ]
+    # attention + combine (o~ written to HBM), then W^UV on it, then W^O
+    unfused_back = [
+        mla.bind(mla.mla_decode, q_lat, q_pe, cache, bt, seq_lens, x["scale"], S, ws, o_lat),
+        mla.bind(mla.mla_out_proj, o_lat, w["w_uv"], None, o_heads),
+        rows[6][1][0]]
     # the same layer with one product per weight and dense intermediates
     sep = {k: torch.empty(B, n, **f32) for k, n in
            (("c_q", d_cq), ("q_c", H * d_h), ("q_r", H * d_R), ("c_kv", d_c), ("k_r", d_R))}
@@ -165,7 +177,7 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
                  before, bt, cache, x["rope_base"]),
         mla.bind(mla.mla_absorb_q, sep["q_c"].view(B, H, d_h), w["w_uk"], sep["q_r"].view(B, H, d_R),
                  seq_lens, x["rope_base"], q_lat, q_pe),
-    ] + [c for _, calls, _ in rows[4:] for c in calls]
+    ] + unfused_back
     chain = [c for _, calls, _ in rows for c in calls]
 
     # the same calls with the products accumulating into outputs cleared together by one
@@ -182,6 +194,13 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
         for c in acc_chain:
             c()
 
+    unfused_chain = acc_chain[:4] + unfused_back[:2] + acc_chain[6:]
+
+    def accumulate_unfused():
+        outs.zero_()
+        for c in unfused_chain:
+            c()
+
     for c in chain:
         c()
     torch.cuda.synchronize()
@@ -194,6 +213,7 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
         for c in chain + separate:
             c()
         accumulate_chain()
+        accumulate_unfused()
         torch.cuda.synchronize()
 
     def timed(fn, n=20):
@@ -217,6 +237,7 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     dense_us = timed(lambda: [c() for c in chain])
     separate_us = timed(lambda: [c() for c in separate])
     chain_us = timed(accumulate_chain)
+    unfused_us = timed(accumulate_unfused)
 
     # the survey's fourth next item, measured only: offline absorption folds W^UK_i^T into
     # W^UQ_i ([H d_c, d_c^Q], 201 MB of bf16 weights, prepared once here in fp32 and rounded
@@ -247,8 +268,9 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
            "chain_roofline_frac": round(total_bytes / chain_us / 1e3 / HBM_PEAK_GBPS, 4),
            "sequences_per_s": round(B / (chain_us * 1e-6), 1),
            "chain_schedule": "one stream; stacked products accumulating into outputs cleared "
-                             "by one fill at the start",
+                             "by one fill at the start; combine fused with W^UV",
            "chain_dense_outputs_us": round(dense_us, 2),
+           "chain_unfused_combine_us": round(unfused_us, 2),
            "chain_separate_products_us": round(separate_us, 2),
            "accumulate_vs_dense_max_rel_diff": round(acc_vs_dense, 6)}
     if oracle_seqs > 0:

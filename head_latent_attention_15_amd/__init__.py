@@ -62,6 +62,8 @@ _SIGNATURES = {
     "mla_decode_attn_multi": (_I32, [_P, _P, _P, _P, _P, _SP, _I32, _F, _I32, _P, _I32, _P, _I32,
                                      _P]),
     "mla_splitk_combine": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    "mla_combine_out_proj": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _I32, _I32, _P,
+                                    _P]),
     "mla_decode": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _SZ, _P, _P, _I32, _P]),
     "mla_out_proj": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "mla_linear": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P]),
@@ -401,6 +403,22 @@ def mla_splitk_combine(o_part, lse_part, out, lse_out=None, stream=None):
         _dev(o_part, "o_part", None, 4), _dtype_code(o_part),
         _dev(lse_part, "lse_part", torch.float32, 3), B, H, S, d_c, _dev(out, "out", torch.float32, 3),
         _dev(lse_out, "lse_out", torch.float32, 2), _stream(stream))
+
+
+def mla_combine_out_proj(o_part, lse_part, w_uv, o_heads, stream=None):
+    """o_heads = W^UV_i (combine of the split partials) per head, in one kernel.
+    o_part [B,H,S,d_c] f32/bf16, lse_part [B,H,S] f32, w_uv [H*d_h, d_c] bf16,
+    o_heads [B,H,d_h] f32."""
+    torch = _torch()
+    B, H, S, d_c = o_part.shape
+    d_h = o_heads.shape[2]
+    _expect(tuple(lse_part.shape) == (B, H, S), "lse_part must be [B,H,S]")
+    _expect(tuple(w_uv.shape) == (H * d_h, d_c), "w_uv must be [H*d_h, d_c]")
+    _expect(tuple(o_heads.shape) == (B, H, d_h), "o_heads must be [B,H,d_h]")
+    _invoke("mla_combine_out_proj", _dev(o_part, "o_part", None, 4), _dtype_code(o_part),
+            _dev(lse_part, "lse_part", torch.float32, 3), B, H, S, d_c,
+            _dev(w_uv, "w_uv", None, 2), _dtype_code(w_uv), d_h,
+            _dev(o_heads, "o_heads", torch.float32, 3), _stream(stream))
 
 
 def mla_decode(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale, num_splits,

@@ -31,6 +31,14 @@ hipError_t launch_attn_generic_bf16_512_64(const PagedArgs& a, hipStream_t s);
 hipError_t launch_attn_mfma_bf16_512_64(const PagedArgs& a, hipStream_t s);
 bool attn_mfma_supported(const PagedArgs& a);
 
+// Split-K combine fused with the W^UV up-projection (d_c = 512, d_h = 128, S <= 64, bf16
+// W^UV): o_heads[b][i] = W^UV_i combine_s(o_part[b][i][s], lse_part[b][i][s]).
+bool combine_uv_supported(int H, int S, int d_c, int d_h, const void* o_part, const void* w_uv,
+                          int B);
+hipError_t launch_combine_uv(const void* o_part, int part_bf16, const float* lse_part,
+                             const void* w_uv, float* o_heads, int B, int H, int S,
+                             hipStream_t s);
+
 hipError_t launch_splitk_combine(const void* o_part, int part_bf16, const float* lse_part, int B,
                                  int H, int S, int d_c, float* out, float* lse_out, hipStream_t s);
 

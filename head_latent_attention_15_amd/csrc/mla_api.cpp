@@ -225,6 +225,25 @@ mla_status_t mla_splitk_combine(const void* o_part, mla_dtype_t part_dtype,
                   "split-K combine");
 }
 
+mla_status_t mla_combine_out_proj(const void* o_part, mla_dtype_t part_dtype,
+                                  const float* lse_part, int32_t B, int32_t H, int32_t num_splits,
+                                  int32_t d_c, const void* w_uv, mla_dtype_t w_dtype, int32_t d_h,
+                                  float* o_heads, void* stream) {
+  if (!o_part || !lse_part || !w_uv || !o_heads)
+    return fail(MLA_ERR_NULL, "mla_combine_out_proj: a required pointer is NULL");
+  if (B < 1 || H < 1 || num_splits < 1 || d_c < 1 || d_h < 1)
+    return fail(MLA_ERR_SHAPE, "mla_combine_out_proj: sizes must be >= 1");
+  if (!is_dtype(part_dtype) || w_dtype != MLA_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_combine_out_proj: partials F32/BF16, w_uv BF16 only");
+  if (!mla::combine_uv_supported(H, num_splits, d_c, d_h, o_part, w_uv, B))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "mla_combine_out_proj: compiled for d_c = 512, d_h = 128, at most 64 splits and "
+                "16-byte aligned o_part / w_uv (got d_c=%d d_h=%d S=%d)", d_c, d_h, num_splits);
+  return launched(mla::launch_combine_uv(o_part, part_dtype == MLA_BF16, lse_part, w_uv, o_heads,
+                                         B, H, num_splits, as_stream(stream)),
+                  "combine + W^UV");
+}
+
 mla_status_t mla_decode(const void* q_lat, const void* q_pe, const void* kv_cache,
                         const int32_t* block_table, const int32_t* seq_lens,
                         const mla_paged_shape_t* shape, float softmax_scale,

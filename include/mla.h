@@ -211,6 +211,24 @@ mla_status_t mla_splitk_combine(const void* o_part, mla_dtype_t part_dtype,
                                 const float* lse_part, int32_t B, int32_t H, int32_t num_splits,
                                 int32_t d_c, float* out, float* lse_out, void* stream);
 
+/* mla_splitk_combine fused with the W^UV up-projection, in one kernel (the combined latent
+ * stays on the chip: it is neither written nor read back):
+ *   o~[b][i][:] = combine of o_part[b][i][:][:] with lse_part[b][i][:], as mla_splitk_combine
+ *   o_heads[b][i][j] = sum_c w_uv[i*d_h + j][c] * o~[b][i][c]
+ * ("論文解説: DeepSeek-V2 …", "行列吸収トリック"; kasblo.com/?p=4663, "V側は、小さな表現の
+ * 加重和を先に求める": the weighted sum of latents first, W^UV_i after it.)
+ *   o_part [B][H][S][d_c] part_dtype (F32 or BF16);  lse_part [B][H][S] fp32;
+ *   w_uv [H*d_h][d_c] bf16 (nn.Linear weight, head i = row block i);  o_heads [B][H][d_h] fp32.
+ * o~ is formed in fp32 and enters the product as two bf16 terms (about 16 significant bits,
+ * as mla_out_proj carries its fp32 input), fp32 accumulation.  Compiled for d_c = 512,
+ * d_h = 128, num_splits <= 64, 16-byte aligned o_part and w_uv; other shapes take
+ * mla_splitk_combine followed by mla_out_proj.  Deterministic (no atomics).
+ * Errors: NULL, SHAPE (sizes < 1), UNSUPPORTED (dtypes, or a shape not compiled). */
+mla_status_t mla_combine_out_proj(const void* o_part, mla_dtype_t part_dtype,
+                                  const float* lse_part, int32_t B, int32_t H, int32_t num_splits,
+                                  int32_t d_c, const void* w_uv, mla_dtype_t w_dtype, int32_t d_h,
+                                  float* o_heads, void* stream);
+
 /* mla_decode_attn followed by mla_splitk_combine, with the split partials in a caller
  * workspace of at least mla_decode_workspace_bytes(B, H, d_latent, num_splits) bytes
  * (unused when num_splits == 1); the partials take the cache dtype (BF16 caches: bf16

@@ -231,3 +231,18 @@ def test_row_stride(shape, stride, lead, ld):
 def test_row_stride_rejects(shape, stride, lead):
     with pytest.raises(ValueError):
         mla._row_stride(shape, stride, lead)
+
+
+def test_combine_out_proj_validation():
+    """Shapes the fused combine + W^UV kernel is not compiled for are refused, not run."""
+    L = mla.lib
+    args = lambda **k: [k.get("o", FAKE), k.get("pdt", 1), FAKE, 2, 8, k.get("S", 4),
+                        k.get("d_c", 512), FAKE, k.get("wdt", 1), k.get("d_h", 128), FAKE, None]
+    assert L.mla_combine_out_proj(*args(o=None)) == mla.MLA_ERR_NULL
+    assert L.mla_combine_out_proj(*args(S=0)) == mla.MLA_ERR_SHAPE
+    assert L.mla_combine_out_proj(*args(S=65)) == mla.MLA_ERR_UNSUPPORTED
+    assert L.mla_combine_out_proj(*args(d_h=64)) == mla.MLA_ERR_UNSUPPORTED
+    assert L.mla_combine_out_proj(*args(d_c=256)) == mla.MLA_ERR_UNSUPPORTED
+    assert L.mla_combine_out_proj(*args(wdt=0)) == mla.MLA_ERR_UNSUPPORTED
+    assert L.mla_combine_out_proj(*args(pdt=5)) == mla.MLA_ERR_UNSUPPORTED
+    assert L.mla_combine_out_proj(*args(o=FAKE + 8)) == mla.MLA_ERR_UNSUPPORTED

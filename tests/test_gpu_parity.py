@@ -465,7 +465,7 @@ def test_stream_read_runs(mla):
 
 
 # ------------------------------------------------------------------ full decode layer
-def layer_on_gpu(mla, x, S, stacked=False):
+def layer_on_gpu(mla, x, S, stacked=False, fused=False):
     """The whole decode layer through the C ABI: projections, cache append, absorption,
     attention + combine, W^UV and W^O.  stacked: the projections that share an input run as
     one product over their stacked weights ([W^DQ; W^DKV; W^KR] h, then [W^UQ; W^QR] c^Q
@@ -509,24 +509,33 @@ def layer_on_gpu(mla, x, S, stacked=False):
                           x["rope_base"])
         mla.mla_absorb_q(q_c.view(B, H, d_h), w["w_uk"], q_r.view(B, H, d_R), seq_lens,
                          x["rope_base"], q_lat, q_pe)
-    ws = torch.empty(max(1, mla.mla_decode_workspace_bytes(B, H, d_c, S)), dtype=torch.uint8, device="cuda")
-    o_lat = torch.empty(B, H, d_c, **f32)
-    mla.mla_decode(q_lat, q_pe, cache, bt, seq_lens, x["scale"], S, ws, o_lat)
     o_heads = torch.empty(B, H, d_h, **f32)
     u = torch.empty(B, d, **f32)
-    mla.mla_out_proj(o_lat, w["w_uv"], w["w_o"], o_heads, u)
+    if fused:  # attention, then the combine fused with W^UV, then W^O
+        o_part = torch.empty(B, H, S, d_c, device="cuda", dtype=torch.bfloat16)
+        lse_part = torch.empty(B, H, S, **f32)
+        mla.mla_decode_attn(q_lat, q_pe, cache, bt, seq_lens, x["scale"], S, o_part, lse_part)
+        mla.mla_combine_out_proj(o_part, lse_part, w["w_uv"], o_heads)
+        mla.mla_linear(o_heads.view(B, H * d_h), w["w_o"], u)
+    else:
+        ws = torch.empty(max(1, mla.mla_decode_workspace_bytes(B, H, d_c, S)), dtype=torch.uint8,
+                         device="cuda")
+        o_lat = torch.empty(B, H, d_c, **f32)
+        mla.mla_decode(q_lat, q_pe, cache, bt, seq_lens, x["scale"], S, ws, o_lat)
+        mla.mla_out_proj(o_lat, w["w_uv"], w["w_o"], o_heads, u)
     torch.cuda.synchronize()
     return u, cache
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("stacked", [False, True], ids=["separate", "stacked"])
-def test_full_layer_b64_t2k_sampled(mla, stacked):
+@pytest.mark.parametrize("stacked,fused", [(False, False), (True, False), (True, True)],
+                         ids=["separate", "stacked", "stacked-fused"])
+def test_full_layer_b64_t2k_sampled(mla, stacked, fused):
     """Full layer at d=5120, H=128, B=64, 2048 prior tokens + 1 appended: all 64 rows of
     u on the GPU; sequences 0 and 37 through the oracle's expanded path."""
     x = W.layer_b64_t2k()
-    say(f"layer_b64_t2k stacked={stacked}")
-    u, cache = layer_on_gpu(mla, x, S=4, stacked=stacked)
+    say(f"layer_b64_t2k stacked={stacked} fused={fused}")
+    u, cache = layer_on_gpu(mla, x, S=4, stacked=stacked, fused=fused)
     pick = [0, 37]
     ref = oracle.decode_layer(W.to_f64(x["h"]), {k: W.to_f64(v) for k, v in x["weights"].items()},
                               W.to_f64(x["cache"]), x["block_table"].numpy(),
@@ -542,12 +551,13 @@ def test_full_layer_b64_t2k_sampled(mla, stacked):
         assert_bf16(row, want, "appended row")
 
 
-@pytest.mark.parametrize("stacked", [False, True], ids=["separate", "stacked"])
-def test_small_layer_chain(mla, stacked):
+@pytest.mark.parametrize("stacked,fused", [(False, False), (True, False), (True, True)],
+                         ids=["separate", "stacked", "stacked-fused"])
+def test_small_layer_chain(mla, stacked, fused):
     """A small layer (d=256, H=16, d_c=512, d_R=64, B=5, 100 prior tokens) end to end on all rows."""
     x = W.layer_b64_t2k(seed=21, B=5, T=100, d=256, H=16, d_cq=96)
-    say(f"small layer stacked={stacked}")
-    u, _ = layer_on_gpu(mla, x, S=2, stacked=stacked)
+    say(f"small layer stacked={stacked} fused={fused}")
+    u, _ = layer_on_gpu(mla, x, S=2, stacked=stacked, fused=fused)
     ref = oracle.decode_layer(W.to_f64(x["h"]), {k: W.to_f64(v) for k, v in x["weights"].items()},
                               W.to_f64(x["cache"]), x["block_table"].numpy(),
                               x["seq_lens_before"].numpy(), x["shape"].d_h, x["shape"].d_R,
@@ -798,3 +808,49 @@ def test_strided_entry_points(mla):
                         for b in range(B)])
         assert_bf16(host64(outs[0][0]), ref, "q~ strided")
         assert_bf16(host64(outs[0][1]), ref_pe, "q_pe strided")
+
+
+@pytest.mark.parametrize("B,H,S,pdt", [(37, 8, 5, torch.bfloat16),   # ragged blocks, 2 chunks
+                                       (20, 6, 64, torch.float32),   # H % 8 != 0, most splits
+                                       (64, 16, 4, torch.bfloat16),  # the layer's shape class
+                                       (1, 8, 1, torch.bfloat16)])   # one row, one split
+def test_combine_out_proj(mla, B, H, S, pdt):
+    """The combine fused with W^UV against the oracle's combine and up-projection in fp64 on
+    seeded partials: ragged sequence blocks, both head numberings, 1 to 64 splits, empty
+    splits (lse = -inf) holding NaN that must not leak, and one (sequence, head) with no
+    tokens at all (o = 0).  Then against the unfused pair (mla_splitk_combine, mla_out_proj)
+    on the same inputs."""
+    g = torch.Generator().manual_seed(90 + S)
+    d_c, d_h = 512, 128
+    say(f"combine_out_proj B={B} H={H} S={S} {pdt}")
+    o_part = torch.randn(B, H, S, d_c, generator=g)
+    lse = torch.randn(B, H, S, generator=g) * 3
+    empty = torch.rand(B, H, S, generator=g) < 0.2
+    if B > 1:
+        empty[1, 2, :] = True
+    lse[empty] = -math.inf
+    o_part = o_part.to(pdt)
+    w_uv = (torch.randn(H * d_h, d_c, generator=g) / math.sqrt(d_c)).to(torch.bfloat16)
+    # weight-0 splits do not enter the sum: the oracle gets zeros there, the GPU gets NaN
+    o_ref = W.to_f64(o_part)
+    o_ref[empty.numpy()] = 0.0
+    o_gpu = o_part.clone()
+    o_gpu[empty] = float("nan")
+    o_comb, _ = oracle.combine_splits(np.moveaxis(o_ref, 2, 0), np.moveaxis(W.to_f64(lse), 2, 0))
+    ref = oracle.up_project_values(o_comb, W.to_f64(w_uv))
+    out = torch.empty(B, H, d_h, device="cuda")
+    mla.mla_combine_out_proj(dev(o_gpu), dev(lse), dev(w_uv), out)
+    torch.cuda.synchronize()
+    m, r = errors(host64(out), ref)
+    # o~ carried as hi + lo bf16 (about 16 bits), exact products, fp32 sums over 512
+    assert r <= 1e-5 and m <= 1e-5 * float(np.abs(ref).max()) + 1e-6, (m, r)
+    if B > 1:
+        assert bool((out[1, 2] == 0).all())
+    # the unfused pair on the same partials
+    o_lat = torch.empty(B, H, d_c, device="cuda")
+    o_h2 = torch.empty(B, H, d_h, device="cuda")
+    mla.mla_splitk_combine(dev(o_gpu), dev(lse), o_lat)
+    mla.mla_out_proj(o_lat, dev(w_uv), None, o_h2)
+    torch.cuda.synchronize()
+    m2, r2 = errors(host64(out), host64(o_h2))
+    assert r2 <= 1e-5, (m2, r2)
