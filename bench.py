@@ -334,6 +334,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32)
     ap.add_argument("--no-layer", action="store_true", help="skip the per-step layer measurement")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="run only the full-layer measurement and print its JSON (for profiling "
+                         "the layer's kernels)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for --pmc runs)")
     args = ap.parse_args()
@@ -354,6 +357,10 @@ def main():
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
     num_cus = props.multi_processor_count
+    if args.layer_only:
+        log("layer_b64_t2k only")
+        print(json.dumps({"layer_b64_t2k": layer_rows(mla, W, torch, 0)}), flush=True)
+        return
 
     log("generating dsv2_b32_t4k inputs")
     inp = W.dsv2_b32_t4k()

@@ -381,33 +381,35 @@ bool gemm_stream_plan_ok(const GemmArgs& g, int tn, int grid, int ring) {
   return (units / grid) % (ring / 4) == 0;
 }
 
-// Tile width, workgroups and ring depth.  For each tile width: the largest divisor of the
-// unit count up to one workgroup per CU, then the deepest compiled ring that turns a whole
-// number of times over a run.  The score is the workgroups times the weight fragments each
-// wave keeps in flight (capped where more stops paying); a narrower tile, which re-stages x
-// more often per weight byte, must beat a wider one by a twentieth.
-static int ring_for(int tn, int64_t nu) {
-  for (int r = 20; r > 4; r -= 4)
-    if (ring_ok(tn, r) && nu % (r / 4) == 0) return r;
-  return 4;
-}
-
+// Tile width, workgroups and ring depth.  For each tile width the workgroup count is the
+// largest divisor of the unit count up to one per CU (a multiple of 8 if one is close).
+// Measured at the DeepSeek-V2 shapes (W^O: 64 x 5120 x 16384; [W^DQ; W^DKV; W^KR]:
+// 64 x 2112 x 5120) with the weights streaming from HBM: the shallowest ring (4 k-steps,
+// three in flight per wave) beats the deeper ones by 2-6 %, and 128-column tiles beat 256-
+// and 64-column ones; so tile 2 is preferred, then 4, then 1, as long as its workgroup
+// count is within 7/8 of the best.
 void gemm_stream_plan(const GemmArgs& g, int* tn, int* grid, int* ring) {
-  int64_t best = -1;
-  for (int t : {4, 2, 1}) {
+  int gds[3] = {0, 0, 0};
+  const int order[3] = {2, 4, 1};
+  int best_gd = 0;
+  for (int i = 0; i < 3; ++i) {
+    const int t = order[i];
     if (g.N % (64 * t) != 0) continue;
     const int64_t units = static_cast<int64_t>(g.batch) * (g.N / (64 * t)) * (g.K / KC);
-    int gd = 1;  // largest divisor up to the CU count, a multiple of 8 if one is close
+    int gd = 1;
     for (int d = static_cast<int>(std::min<int64_t>(units, GS_CUS)); d >= 1; --d)
       if (units % d == 0) { gd = d; break; }
     for (int d = gd - gd % 8; d >= 8 && d * 8 >= gd * 7; d -= 8)
       if (units % d == 0) { gd = d; break; }
-    const int r = ring_for(t, units / gd);
-    const int64_t score = static_cast<int64_t>(gd) * std::min((r - 1) * t, 16);
-    if (best < 0 || score * 20 > best * 21) {
-      best = score; *tn = t; *grid = gd; *ring = r;
-    }
+    gds[i] = gd;
+    best_gd = std::max(best_gd, gd);
   }
+  for (int i = 0; i < 3; ++i)
+    if (gds[i] > 0 && gds[i] * 8 >= best_gd * 7) {
+      *tn = order[i]; *grid = gds[i]; *ring = 4;
+      return;
+    }
+  *tn = 1; *grid = 1; *ring = 4;
 }
 
 hipError_t launch_gemm_stream_with(const GemmArgs& g, int tn, int grid, int ring, hipStream_t s) {
