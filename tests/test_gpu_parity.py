@@ -813,10 +813,13 @@ def test_strided_entry_points(mla):
 @pytest.mark.parametrize("B,H,S,pdt", [(37, 8, 5, torch.bfloat16),   # ragged blocks, 2 chunks
                                        (20, 6, 64, torch.float32),   # H % 8 != 0, most splits
                                        (64, 16, 4, torch.bfloat16),  # the layer's shape class
-                                       (1, 8, 1, torch.bfloat16)])   # one row, one split
+                                       (1, 8, 1, torch.bfloat16),    # one row, one split
+                                       (70, 64, 6, torch.bfloat16),  # 32-row blocks, ragged
+                                       (40, 128, 3, torch.float32)]) # 32-row blocks, fp32
 def test_combine_out_proj(mla, B, H, S, pdt):
     """The combine fused with W^UV against the oracle's combine and up-projection in fp64 on
-    seeded partials: ragged sequence blocks, both head numberings, 1 to 64 splits, empty
+    seeded partials: ragged sequence blocks of 16 and of 32 (the kernel takes 32 once 16-row
+    blocks would exceed one workgroup per CU), both head numberings, 1 to 64 splits, empty
     splits (lse = -inf) holding NaN that must not leak, and one (sequence, head) with no
     tokens at all (o = 0).  Then against the unfused pair (mla_splitk_combine, mla_out_proj)
     on the same inputs."""
