@@ -738,6 +738,7 @@ def test_strided_entry_points(mla):
     for (M, N, K, xdt) in [(64, 2112, 5120, torch.float32),    # [W^DQ; W^DKV; W^KR] shape
                            (64, 24576, 1536, torch.float32),   # [W^UQ; W^QR] shape
                            (5, 192, 256, torch.bfloat16),
+                           (100, 320, 384, torch.float32),    # two row blocks
                            (3, 70, 33, torch.float32)]:
         say(f"linear strided M={M} N={N} K={K} x={xdt}")
         xb = torch.randn(M, K + 24, generator=g).to(xdt)
