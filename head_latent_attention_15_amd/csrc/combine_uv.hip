@@ -7,12 +7,13 @@
 // kasblo.com/?p=4663, "V側は、小さな表現の加重和を先に求める").  Fusing the two keeps o~ on
 // the chip: it is never written to HBM and read back.
 //
-// One workgroup (8 wavefronts) per (head, block of 16 sequences).  Phase 1: thread t
-// combines row t / 32 of the block over 16 latent columns (two 16-byte bf16 loads per
-// split), with the split weights computed once per row across its 32 lanes and passed
-// around by shuffle; the result is stored in LDS as two bf16 planes (hi + rounding
-// remainder: about 16 significant bits, so every product with a bf16 weight is exact in
-// fp32).  Phase 2: wavefront w computes output columns 16 w .. 16 w + 15 of all 16 rows on
+// One workgroup (8 wavefronts) per (head, block of ROWS = 16 or 32 sequences; 32 once
+// 16-row blocks would need more than one workgroup per CU).  Phase 1: the 512 / ROWS lanes
+// of a sequence each merge ROWS latent columns (16-byte loads per split), with the split
+// weights computed once per sequence across those lanes and passed around by shuffle; the
+// result is stored in LDS as two bf16 planes (hi + rounding remainder: about 16
+// significant bits, so every product with a bf16 weight is exact in fp32).  Phase 2:
+// wavefront w computes output columns 16 w .. 16 w + 15 of all ROWS sequences on
 // v_mfma_f32_16x16x32_bf16 (A = o~ from LDS, B = W^UV_i rows straight from HBM into
 // registers, 16 contiguous bytes per lane and k-step); those loads go out right after the
 // partial loads, so they are in flight during the combine.
