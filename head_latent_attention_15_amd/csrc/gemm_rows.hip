@@ -14,8 +14,9 @@
 //
 // Work decomposition: 4 wavefronts, wave w owns TN column tiles of 16 (64 TN columns per
 // workgroup) and all four 16-row tiles of a 64-row block of x.  Long k ranges are split over
-// KS workgroups, which add their results into y with fp32 atomics (y is zeroed first), so
-// the sum order, and with it the last bits of y, can differ between runs.  Each wave keeps
+// KS workgroups, which add their results into y with fp32 atomics (y is zeroed first,
+// unless the caller accumulates into its prior contents), so the sum order, and with it
+// the last bits of y, can differ between runs.  Each wave keeps
 // the weight fragments of the next R - 1 k-steps in flight: at these sizes the loaded HBM
 // latency is several microseconds, and the bytes outstanding across the chip, not the
 // access pattern, set the rate.

@@ -10,7 +10,8 @@
 // column tile (64 TN output columns) by 128 k, numbered tile-major, and each workgroup (one
 // per CU) takes an equal run of consecutive units.  Its weight stream never restarts: the
 // ring of weight fragments runs on across unit and tile boundaries, and the partial sums of
-// a tile are flushed into y (fp32 atomics, y zeroed first) when the run leaves the tile.
+// a tile are flushed into y (fp32 atomics; y zeroed first unless the caller accumulates)
+// when the run leaves the tile.
 //
 // A workgroup has two roles.  Waves 0-3 (consumers) own TN column tiles of 16 each and all
 // four 16-row tiles of x; the bf16 weight rows go from HBM straight into MFMA B-operand

@@ -12,8 +12,9 @@
 // weight rows go from HBM straight into MFMA B-operand registers (lane (g, r): row n + r,
 // 16 contiguous bytes), one tile's S k-steps ahead, so the ring runs on across tiles and
 // never restarts.  After each tile the partial sums are added into y (fp32 atomics, y
-// zeroed first; the slices of one tile add up there).  The loop issues no other global
-// loads and has no barrier: every wait is the exact count of the fragment it needs.
+// zeroed first unless the caller accumulates; the slices of one tile add up there).  The
+// loop issues no other global loads and has no barrier: every wait is the exact count of
+// the fragment it needs.
 #include "device_common.h"
 #include "launchers.h"
 
