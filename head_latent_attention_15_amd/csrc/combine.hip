@@ -86,22 +86,28 @@ __global__ __launch_bounds__(kCombineThreads) void splitk_combine_kernel(
 
 // d_c = 512, at most 64 splits: one wavefront per (sequence, head), lane l owns columns
 // 8 l .. 8 l + 7 (one 16-byte load per split for bf16 partials), lane s holds split s's lse
-// and weight; the weights reach every lane by shuffle, the S loads are issued back to back.
-__device__ __forceinline__ void load8(const bf16raw* p, float (&v)[8]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  const unsigned w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+// and weight.  Every load of a chunk of 8 splits goes out before anything waits (split
+// indices past S re-read split S - 1 and get weight 0, so the loads carry no branch that
+// would make each wait for its own data), and the weights reach the lanes by readlane.
+template <typename PT> struct Part8;
+template <> struct Part8<bf16raw> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16raw* p) {
+    u = *reinterpret_cast<const uint4*>(p);
   }
-}
-__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
-  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
-  const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
-}
+  __device__ __forceinline__ float at(int i) const {
+    const unsigned w = (i >> 1) == 0 ? u.x : (i >> 1) == 1 ? u.y : (i >> 1) == 2 ? u.z : u.w;
+    return (i & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+  }
+};
+template <> struct Part8<float> {
+  f32x4_t a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4_t*>(p);
+    b = *reinterpret_cast<const f32x4_t*>(p + 4);
+  }
+  __device__ __forceinline__ float at(int i) const { return i < 4 ? a[i] : b[i - 4]; }
+};
 
 template <typename PT>
 __global__ __launch_bounds__(256) void combine512_kernel(
@@ -111,28 +117,34 @@ __global__ __launch_bounds__(256) void combine512_kernel(
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= B * H) return;
   const int bh = (item % B) * H + item / B;  // sequence-fastest, as in splitk_combine_kernel
-  const float x = lane < S ? lse_part[static_cast<int64_t>(bh) * S + lane] : -INFINITY;
+  const float xraw = lse_part[static_cast<int64_t>(bh) * S + min(lane, S - 1)];
+  const PT* base = o_part + static_cast<int64_t>(bh) * S * 512 + 8 * lane;
+  Part8<PT> v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j].load(base + static_cast<int64_t>(min(j, S - 1)) * 512);
+  __builtin_amdgcn_sched_barrier(0);
+
+  const float x = lane < S ? xraw : -INFINITY;
   const float m = wave_max(x);
   const float msafe = (m == -INFINITY) ? 0.f : m;
-  const float wl = (x == -INFINITY) ? 0.f : expf(x - msafe);
+  const float wl = (x == -INFINITY) ? 0.f : expf(x - msafe);  // 0 for lanes >= S
   const float den = wave_sum(wl);
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  const PT* base = o_part + static_cast<int64_t>(bh) * S * 512 + 8 * lane;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float v[8][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (s0 + j < S) load8(base + static_cast<int64_t>(s0 + j) * 512, v[j]);
+  for (int s0 = 0;;) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (s0 + j >= S) break;
-      const float w = __shfl(wl, s0 + j, 64);
-      if (w != 0.f) {  // an empty split contributes nothing (and no NaN)
+      const float w = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s0 + j));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[j][i], acc[i]);
-      }
+      for (int i = 0; i < 8; ++i)  // an empty split adds exactly 0 (and no NaN)
+        acc[i] = fmaf(w, w != 0.f ? v[j].at(i) : 0.f, acc[i]);
     }
+    s0 += 8;
+    if (s0 >= S) break;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j].load(base + static_cast<int64_t>(min(s0 + j, S - 1)) * 512);
   }
   float* dst = out + static_cast<int64_t>(bh) * 512 + 8 * lane;
   *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
