@@ -133,10 +133,13 @@ __global__ __launch_bounds__(512) void gemm_xs_kernel(const XT* x, const bf16raw
 #pragma unroll
   for (int j = 0; j < TN; ++j)
     wlane[j] = w + static_cast<int64_t>(16 * (TN * wave + j) + r) * a.ldw + k0 + 8 * g;
-  // step s of the run: tile tile0 + s / S (the last tile again past the run), k-step s % S
+  // step s of the run: tile tile0 + s / S, k-step s % S.  Past the run the ring still loads
+  // (so every wait count stays the same) but from one lane-uniform 16-byte address, the
+  // first bytes of w: a broadcast of one line instead of 16 rows of the last tile again.
   auto w_frag = [&](int tl, int ks, int j) {
-    const int tt = tile0 + min(tl, ntl - 1);
-    return *reinterpret_cast<const bf16x8_t*>(wlane[j] + static_cast<int64_t>(tt) * CW * a.ldw + 32 * ks);
+    const bf16raw* p =
+        tl < ntl ? wlane[j] + static_cast<int64_t>(tile0 + tl) * CW * a.ldw + 32 * ks : w;
+    return *reinterpret_cast<const bf16x8_t*>(p);
   };
   bf16x8_t wf[R][TN];
 #pragma unroll
