@@ -41,7 +41,7 @@ ROW_BYTES = 576 * 2             # one cached token: c^KV (512) + k^R (64), bf16
 FLOP_PER_TOKEN_HEAD = 2 * (576 + 512)
 N_CACHE_COPIES = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_dsv2_b32_t4k_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "head_latent_attention_15_amd", "csrc", "attn_mfma.hip")
+KERNEL_SRC = os.path.join(ROOT, "head_latent_attention_15_amd", "csrc", "attn_cols.hip")
 
 
 def log(*a):
@@ -66,7 +66,8 @@ def measured_traffic():
 
 def cpu_baseline(inp, n_seq: int, min_seconds: float = 10.0):
     """The fp64 oracle (unchanged) on the first n_seq sequences of the same workload,
-    repeated until at least min_seconds of CPU work has been timed."""
+    repeated until at least min_seconds of CPU work has been timed, with the BLAS thread
+    count the process was started with."""
     import numpy as np
     import oracle
     import workloads as W
@@ -95,6 +96,22 @@ def cpu_baseline(inp, n_seq: int, min_seconds: float = 10.0):
             "kind": "oracle",
             "sample": f"{passes} passes over {n_seq} of 32 sequences x 4096 tokens (fp64 NumPy "
                       f"latent attention incl. the paged gather, {dt:.1f} s)"}
+
+
+def cpu_baseline_child(n_seq: int, threads: int):
+    """The same measurement in a child process whose BLAS and OpenMP pools are limited to
+    `threads` (set before NumPy loads); returns its cpu_baseline dict."""
+    import subprocess
+    env = dict(os.environ)
+    for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+        env[k] = str(threads)
+    env["HIP_VISIBLE_DEVICES"] = ""  # the child never touches the GPU
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-only",
+                        "--cpu-seqs", str(n_seq)], env=env, capture_output=True, text=True,
+                       timeout=600)
+    if r.returncode != 0:
+        return {"error": r.stderr[-400:]}
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 def layer_rows(mla, W, torch, oracle_seqs: int):
@@ -323,6 +340,63 @@ def multi_token_rows(mla, W, torch, caches, bt, sl, scale, num_cus, n_q: int = 2
             "tflops": round(flops / (us * 1e-6) / 1e12, 1)}
 
 
+def config_row(mla, torch, inp, name, num_cus, steps, n_copies, kernel="auto"):
+    """One attention workload beside the headline: the whole step (attention + combine,
+    bf16 partials) and the attention alone, back to back over n_copies rotating caches,
+    with algorithmic bytes (cache rows of every sequence, queries, tables; the combined
+    output for the step) and the fraction of the 8 TB/s HBM roofline."""
+    dev = torch.device("cuda:0")
+    B, H, d_c = inp["q_lat"].shape
+    sl = inp["seq_lens"]
+    S = mla.mla_suggest_num_splits(B, int(sl.max()), int(sl.sum()), 64, num_cus)
+    caches = [inp["cache"].to(dev)]
+    for _ in range(n_copies - 1):
+        caches.append(caches[0].clone())
+    q_lat, q_pe = inp["q_lat"].to(dev), inp["q_pe"].to(dev)
+    bt, sld = inp["block_table"].to(dev), sl.to(dev)
+    o_part = torch.empty(B, H, S, d_c, device=dev, dtype=torch.bfloat16)
+    lse_part = torch.empty(B, H, S, device=dev)
+    out = torch.empty(B, H, d_c, device=dev)
+    lse = torch.empty(B, H, device=dev)
+    calls = [mla.bind(mla.mla_decode_attn_planned, q_lat, q_pe, c, bt, sld, inp["scale"], S,
+                      o_part, lse_part, kernel=kernel) for c in caches]
+    combine = mla.bind(mla.mla_splitk_combine, o_part, lse_part, out, lse)
+    t0 = time.perf_counter()
+    k = 0
+    while time.perf_counter() - t0 < 0.3:
+        calls[k % n_copies]()
+        combine()
+        k += 1
+        if k % 32 == 0:
+            torch.cuda.synchronize()
+    step_ms = timed_ms(torch, lambda k: (calls[k % n_copies](), combine()), steps)
+    attn_ms = timed_ms(torch, lambda k: calls[k % n_copies](), steps)
+    tokens = int(sl.sum())
+    attn_bytes = tokens * ROW_BYTES + B * H * 576 * 2 + bt.numel() * 4 + B * 4
+    step_bytes = attn_bytes + B * H * 512 * 4
+    del caches
+    return {"workload": name, "B": B, "H": H, "tokens": tokens, "num_splits": S,
+            "us_per_step": round(step_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
+            "cache_GBps_step": round(tokens * ROW_BYTES / (step_ms * 1e-3) / 1e9, 1),
+            "step_frac": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "attn_GBps": round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1),
+            "attn_frac": round(attn_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "query_tokens_per_s": round(B / (step_ms * 1e-3), 1)}
+
+
+def timed_ms(torch, fn, n):
+    """Average milliseconds of n back-to-back calls fn(0..n-1) between two HIP events on the
+    current stream (the stream the library launches on)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for k in range(n):
+        fn(k)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -331,9 +405,15 @@ def main():
     ap.add_argument("--warmup-seconds", type=float, default=0.5,
                     help="keep warming up until this much time has passed (clocks settle)")
     ap.add_argument("--splits", type=int, default=0, help="split count (0: library suggestion)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "cols", "heads"],
+                    help="attention kernel of the headline step (auto: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32)
+    ap.add_argument("--cpu-baseline-only", action="store_true",
+                    help="(internal) time only the oracle on the host and print its JSON")
     ap.add_argument("--no-layer", action="store_true", help="skip the per-step layer measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the long-context and ragged-batch attention lines")
     ap.add_argument("--layer-only", action="store_true",
                     help="run only the full-layer measurement and print its JSON (for profiling "
                          "the layer's kernels)")
@@ -346,6 +426,11 @@ def main():
               "(sequences shard across GPUs with no communication); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.cpu_baseline_only:
+        import workloads as W
+        print(json.dumps(cpu_baseline(W.dsv2_b32_t4k(), args.cpu_seqs)), flush=True)
+        return
 
     import torch
     import head_latent_attention_15_amd as mla
@@ -379,23 +464,16 @@ def main():
 
     # arguments checked and marshalled once per cache copy, so the host issues each launch
     # in a few microseconds and the timed regions measure the GPU, not Python
-    attn_calls = [mla.bind(mla.mla_decode_attn, q_lat, q_pe, c, bt, sl, scale, S, o_part, lse_part)
-                  for c in caches]
+    def attn_calls_for(kernel):
+        return [mla.bind(mla.mla_decode_attn_planned, q_lat, q_pe, c, bt, sl, scale, S, o_part,
+                         lse_part, kernel=kernel) for c in caches]
+    attn_calls = attn_calls_for(args.kernel)
+    other = "heads" if args.kernel in ("auto", "cols") else "cols"
+    other_calls = attn_calls_for(other)
     combine = mla.bind(mla.mla_splitk_combine, o_part, lse_part, out, lse)
 
     def attn(k):
         attn_calls[k % N_CACHE_COPIES]()
-
-    def timed(fn, n):
-        """Average milliseconds of n back-to-back calls between two events."""
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for k in range(n):
-            fn(k)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
 
     # at least W warmup steps, and at least --warmup-seconds of them: the first tens of
     # milliseconds of back-to-back launches run at lower clocks than the steady state
@@ -404,33 +482,36 @@ def main():
     while k < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
         attn(k)
         combine()
+        other_calls[k % N_CACHE_COPIES]()
         k += 1
         if k % 32 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     log(f"warmup {k} steps ({time.perf_counter() - t_w:.2f} s), S={S}, {num_cus} CUs")
 
-    ms_step = timed(lambda k: (attn(k), combine()), args.steps)
+    ms_step = timed_ms(torch, lambda k: (attn(k), combine()), args.steps)
     # second and third regions: each kernel alone, back to back, events at the ends only
     # (an event recorded between two kernels stalls the queue for several microseconds,
     # so per-kernel events would time the stall with the kernel)
-    attn_avg = timed(attn, args.steps)
-    comb_avg = timed(lambda k: combine(), args.steps)
-    log(f"step {ms_step * 1e3:.1f} us; attention alone {attn_avg * 1e3:.1f} us; "
-        f"combine alone {comb_avg * 1e3:.1f} us")
+    attn_avg = timed_ms(torch, attn, args.steps)
+    comb_avg = timed_ms(torch, lambda k: combine(), args.steps)
+    other_avg = timed_ms(torch, lambda k: other_calls[k % N_CACHE_COPIES](), args.steps)
+    log(f"step {ms_step * 1e3:.1f} us; attention alone {attn_avg * 1e3:.1f} us "
+        f"({other} kernel {other_avg * 1e3:.1f} us); combine alone {comb_avg * 1e3:.1f} us")
 
-    # plain streaming read of one cache copy: the practical HBM read ceiling
+    # streaming reads of the cache copies: the practical HBM read ceilings, with plain
+    # vector loads and with the LDS DMA copy the attention kernels stage tiles with
     sink = torch.empty(4096, device=dev)
-    for _ in range(3):
-        mla.mla_stream_read(caches[1], sink)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 10
-    e0.record()
-    for k in range(reps):
-        mla.mla_stream_read(caches[k % N_CACHE_COPIES], sink)
-    e1.record()
-    torch.cuda.synchronize()
-    stream_gbps = caches[0].numel() * 2 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    cache_nbytes = caches[0].numel() * 2
+
+    def stream_gbps(fn):
+        for j in range(3):
+            fn(caches[j % N_CACHE_COPIES], sink)
+        reps = 12
+        ms = timed_ms(torch, lambda k: fn(caches[k % N_CACHE_COPIES], sink), reps)
+        return cache_nbytes / (ms * 1e-3) / 1e9
+    stream_gbps_plain = stream_gbps(mla.mla_stream_read)
+    stream_gbps_lds = stream_gbps(mla.mla_stream_read_lds)
 
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -450,6 +531,7 @@ def main():
     attn_alg_bytes = cache_bytes + B * H * 576 * 2 + bt.numel() * 4 + B * 4
     achieved = attn_alg_bytes / attn_s / 1e9
     traffic = measured_traffic()
+    kname = {"auto": "cols", "cols": "cols", "heads": "heads"}[args.kernel]
     result = {
         "metric": METRIC,
         "value": round(cache_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -465,26 +547,49 @@ def main():
         "data": "synthetic",
         "config": {"workload": "dsv2_b32_t4k", "B": B, "T": T, "H": H, "d_c": 512, "d_R": 64,
                    "page_size": 64, "num_splits": S, "split_partials": "bf16",
-                   "cache_copies": N_CACHE_COPIES, "parallelism": "none"},
+                   "attention_kernel": kname, "cache_copies": N_CACHE_COPIES,
+                   "parallelism": "none"},
         "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "query_tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "step_bytes_algorithmic": step_alg_bytes,
+        # the whole step (attention + combine) against the HBM roofline: the figure the
+        # headline value is; roofline.frac below is the attention kernel alone
+        "step_frac": round(step_alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "attn_us": round(attn_avg * 1e3, 2),
         "combine_us": round(comb_avg * 1e3, 2),
+        f"attn_us_{other}_kernel": round(other_avg * 1e3, 2),
         "attn_tflops": round(flops / attn_s / 1e12, 2),
         "mfma_frac_of_peak": round(flops / attn_s / 1e12 / BF16_PEAK_TFLOPS, 4),
-        "stream_read_GBps": round(stream_gbps, 1),
+        "stream_read_GBps": round(stream_gbps_plain, 1),
+        "stream_read_lds_dma_GBps": round(stream_gbps_lds, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "attn_mfma_kernel<8, bf16 partials> (8 waves x 16 heads, 32-token tiles)",
+                     "frac_of_lds_dma_ceiling": round(achieved / stream_gbps_lds, 4),
+                     "kernel": ("attn_cols_kernel<bf16 partials> (8 waves: scores by 32-head "
+                                "groups x k parity, latent product by 64-column blocks)"
+                                if kname == "cols" else
+                                "attn_mfma_kernel<8, bf16 partials> (8 waves x 16 heads)"),
                      "bytes_per_launch_algorithmic": attn_alg_bytes},
     }
+    del caches
+    if not args.no_configs:
+        log("timing long_b4_t32k and ragged_b128")
+        result["long_b4_t32k"] = config_row(mla, torch, W.long_b4_t32k(), "long_b4_t32k", num_cus,
+                                            args.steps, N_CACHE_COPIES)
+        result["ragged_b128"] = config_row(mla, torch, W.ragged_b128(), "ragged_b128", num_cus,
+                                           args.steps, 2)
     log("timing multi-token decode (2 query tokens per sequence)")
+    caches = [inp["cache"].to(dev)]
+    for _ in range(N_CACHE_COPIES - 1):
+        caches.append(caches[0].clone())
     result["multi_token"] = multi_token_rows(mla, W, torch, caches, bt, sl, scale, num_cus)
+    del caches
     if not args.no_cpu_baseline:
-        log(f"timing the fp64 oracle on {args.cpu_seqs} sequences")
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seqs)
+        log(f"timing the fp64 oracle on {args.cpu_seqs} sequences (all cores, then 1 thread)")
+        cb = cpu_baseline(inp, args.cpu_seqs)
+        cb["single_thread"] = cpu_baseline_child(args.cpu_seqs, 1)
+        result["cpu_baseline"] = cb
     if not args.no_layer:
         log("timing every step of the path on the full decode layer")
         result["layer_b64_t2k"] = layer_rows(mla, W, torch, 0 if args.no_cpu_baseline else 4)

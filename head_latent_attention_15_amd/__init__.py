@@ -61,6 +61,8 @@ _SIGNATURES = {
     "mla_decode_attn": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _I32, _P, _I32, _P]),
     "mla_decode_attn_multi": (_I32, [_P, _P, _P, _P, _P, _SP, _I32, _F, _I32, _P, _I32, _P, _I32,
                                      _P]),
+    "mla_decode_attn_planned": (_I32, [_P, _P, _P, _P, _P, _SP, _I32, _F, _I32, _P, _I32, _P,
+                                       _I32, _I32, _P]),
     "mla_splitk_combine": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "mla_combine_out_proj": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _I32, _I32, _P,
                                     _P]),
@@ -73,6 +75,7 @@ _SIGNATURES = {
                                   _I32, _P]),
     "mla_validate_indices": (_I32, [_P, _P, _SP, _P, _P]),
     "mla_stream_read": (_I32, [_P, _SZ, _P, _P]),
+    "mla_stream_read_lds": (_I32, [_P, _SZ, _P, _P]),
     "mla_status_string": (ctypes.c_char_p, [_I32]),
     "mla_last_error_detail": (ctypes.c_char_p, []),
 }
@@ -391,6 +394,38 @@ def mla_decode_attn_multi(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_
         S, _dev(o_part, "o_part"), _dtype_code(o_part), _dev(lse_part, "lse_part", torch.float32),
         _dtype_code(q_lat), _stream(stream))
 
+ATTN_KERNELS = {"auto": 0, "heads": 1, "cols": 2, "generic": 3}
+
+
+def mla_decode_attn_planned(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale,
+                            num_splits, o_part, lse_part=None, kernel="auto", stream=None):
+    """mla_decode_attn (q_lat [B,H,d_c]) or mla_decode_attn_multi (q_lat [B,n_q,H,d_c]) on an
+    explicit kernel: "auto", "heads" (16 heads per wavefront), "cols" (column-partitioned,
+    H = 128) or "generic" (VALU), or the integer code."""
+    torch = _torch()
+    if q_lat.dim() == 3:
+        B, H, d_c = q_lat.shape
+        n_q = 1
+    else:
+        B, n_q, H, d_c = q_lat.shape
+    _expect(tuple(q_pe.shape[:-1]) == tuple(q_lat.shape[:-1]), "q_pe must match q_lat but the last dim")
+    _expect(q_pe.dtype == q_lat.dtype == kv_cache.dtype, "q_lat, q_pe, kv_cache share a dtype")
+    _expect(kv_cache.shape[2] == d_c + q_pe.shape[-1], "cache row must be d_c + d_R wide")
+    _expect(block_table.shape[0] == B and tuple(seq_lens.shape) == (B,), "batch mismatch")
+    S = int(num_splits)
+    _expect(o_part.numel() == B * n_q * H * S * d_c, "o_part must hold B*n_q*H*S*d_c elements")
+    if lse_part is not None:
+        _expect(lse_part.numel() == B * n_q * H * S, "lse_part must hold B*n_q*H*S floats")
+    k = ATTN_KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    shp = paged_shape(kv_cache, block_table, H, d_c)
+    _invoke("mla_decode_attn_planned",
+        _dev(q_lat, "q_lat"), _dev(q_pe, "q_pe"),
+        _dev(kv_cache, "kv_cache", None, 3), _dev(block_table, "block_table", torch.int32, 2),
+        _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), n_q, float(softmax_scale),
+        S, _dev(o_part, "o_part"), _dtype_code(o_part), _dev(lse_part, "lse_part", torch.float32),
+        _dtype_code(q_lat), k, _stream(stream))
+
+
 def mla_splitk_combine(o_part, lse_part, out, lse_out=None, stream=None):
     """Log-sum-exp combine of float32 or bfloat16 partials o_part [B,H,S,d_c] into out [B,H,d_c]."""
     torch = _torch()
@@ -511,3 +546,11 @@ def mla_stream_read(src, sink, stream=None):
     _expect(sink.numel() >= 4096, "sink must hold 4096 floats")
     _invoke("mla_stream_read", _dev(src, "src"), src.numel() * src.element_size(),
                                _dev(sink, "sink", torch.float32), _stream(stream))
+
+
+def mla_stream_read_lds(src, sink, stream=None):
+    torch = _torch()
+    cus = torch.cuda.get_device_properties(src.device).multi_processor_count
+    _expect(sink.numel() >= cus, f"sink must hold {cus} floats (one per compute unit)")
+    _invoke("mla_stream_read_lds", _dev(src, "src"), src.numel() * src.element_size(),
+                                   _dev(sink, "sink", torch.float32), _stream(stream))

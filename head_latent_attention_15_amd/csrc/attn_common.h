@@ -1,0 +1,154 @@
+// Pieces shared by the two bf16 MFMA attention kernels (attn_mfma.hip, attn_cols.hip):
+// the cache-tile geometry in LDS, its 16-byte-chunk swizzle, the HBM -> LDS copy issued
+// from inline assembly and the explicit wait counts that go with it.
+#pragma once
+
+#include "device_common.h"
+
+namespace mla {
+namespace attn {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+typedef __attribute__((address_space(3))) f32x4_t lds_f32x4_t;
+typedef __attribute__((address_space(3))) float lds_f32_t;
+typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
+typedef __attribute__((address_space(3))) int32_t lds_i32_t;
+
+constexpr int DC = 512, DR = 64, ROW = DC + DR;
+constexpr int ROW_BYTES = ROW * 2;                  // 1152
+constexpr int CHUNKS = ROW_BYTES / 16;              // 72 sixteen-byte chunks per row
+constexpr int TILE = 32;                            // tokens per tile
+constexpr int TILE_CHUNKS = TILE * CHUNKS;          // 2304
+constexpr int TILE_WAVE_COPIES = TILE_CHUNKS / 64;  // 36 wave-wide 16-byte copies per tile
+constexpr int TILE_BYTES = TILE_CHUNKS * 16;        // 36864
+constexpr int KSTEPS = ROW / 32;                    // 18 k-steps of the score product
+constexpr float LN2 = 0.6931471805599453f;
+
+// 16-byte-chunk swizzle of tile row t (0..31): logical chunk c of the row is stored at
+// position c ^ swz(t).  Measured on gfx950, this map keeps conflict-free (full LDS read
+// rate) both the ds_read_b128 of the score operand (rows 8 (r >> 2) + 4 mt + (r & 3), one
+// chunk column per 16-lane group) and the transposing ds_read_b64_tr_b16 of the PV operand
+// (rows 8 g + 4 r + 0..3 x 2 adjacent chunks).
+__device__ __forceinline__ int swz(int t) {
+  return ((((t >> 3) & 3) ^ (t & 3)) << 1) | ((t >> 2) & 1);
+}
+
+// Source offset (bytes from the tile's first row) of LDS chunk `chunk` (0..2303) of a tile:
+// row t = chunk / 72, stored position p = chunk % 72, which holds logical chunk p ^ swz(t);
+// rows past `last` repeat row `last`.
+__device__ __forceinline__ uint32_t tile_chunk_voff(unsigned chunk, unsigned last) {
+  // chunk / 72 on the full-rate 24-bit multiplier: floor(chunk * 14564 / 2^20) equals
+  // chunk / 72 for every chunk below 2304
+  const unsigned t = __umul24(chunk, 14564u) >> 20;
+  const unsigned c = (chunk - __umul24(t, static_cast<unsigned>(CHUNKS))) ^ swz(t);
+  const unsigned trow = min(t, last);
+  return __umul24(trow, static_cast<unsigned>(ROW_BYTES)) + c * 16;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+__device__ __forceinline__ void block_barrier() {
+  compiler_fence();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
+// 16 bytes per lane from base + voff (global) to LDS address lds_addr + 16 * lane.
+// lds_addr and base are wave-uniform.  M0 carries the LDS address; the s_nop covers the
+// M0-write to LDS-DMA hazard.  The copy has no destination registers and is kept out of
+// the compiler's view, so the compiler adds no vmcnt(0) wait in front of LDS reads; the
+// kernels wait for their copies with explicit counts.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
+  const uint64_t b64 = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b64));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b64 >> 32));
+  const void* ubase = reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  const uint32_t ulds = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(ulds), "v"(voff), "s"(ubase)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// round-to-nearest-even pack of two floats (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ bf16x2_t to_bf16x2(float a, float b) {
+  return __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
+}
+
+// eight bf16 ones (0x3f80 each)
+__device__ __forceinline__ i32x4_t i16x4x2_ones() {
+  const int one2 = 0x3f803f80;
+  return i32x4_t{one2, one2, one2, one2};
+}
+
+// Exact fallback for a head block whose scores jump far above the split's fixed softmax
+// reference: plain online softmax in fp32 per head (the running maximum moves every token),
+// reading the rows straight from the paged cache.  One wavefront handles n_heads heads
+// starting at h_begin; lane l owns features 9l .. 9l+8 of the score and latent columns
+// l + 64k.
+template <typename OT>
+__device__ void split_exact_fallback(const bf16raw* __restrict__ q_lat,
+                                     const bf16raw* __restrict__ q_pe,
+                                     const bf16raw* __restrict__ cache, const int32_t* bt_row,
+                                     int log2P, int j0, int j1, int bq, int H,
+                                     int S, int s, float scale_log2, OT* __restrict__ o_part,
+                                     float* __restrict__ lse_part, int h_begin, int n_heads,
+                                     int lane) {
+  const int P = 1 << log2P;
+  for (int h = h_begin; h < h_begin + n_heads; ++h) {
+    float q[9];
+#pragma unroll
+    for (int f = 0; f < 9; ++f) {
+      const int k = 9 * lane + f;
+      q[f] = k < DC ? bf16_to_f32(q_lat[(static_cast<int64_t>(bq) * H + h) * DC + k])
+                    : bf16_to_f32(q_pe[(static_cast<int64_t>(bq) * H + h) * DR + (k - DC)]);
+    }
+    float m = -INFINITY, l = 0.f, acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+    for (int j = j0; j < j1; ++j) {
+      const int pg = bt_row[j >> log2P];
+      const bf16raw* row = cache + ((static_cast<int64_t>(pg) << log2P) + (j & (P - 1))) * ROW;
+      float part = 0.f;
+#pragma unroll
+      for (int f = 0; f < 9; ++f) part += q[f] * bf16_to_f32(row[9 * lane + f]);
+      const float sc = mul_rn(wave_sum(part), scale_log2);
+      const float mn = fmaxf(m, sc);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      const float p = __builtin_amdgcn_exp2f(sc - mn);
+      l = l * alpha + p;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = acc[k] * alpha + p * bf16_to_f32(row[lane + 64 * k]);
+      m = mn;
+    }
+    const int64_t ob = (static_cast<int64_t>(bq) * H + h) * S + s;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) st(o_part + ob * DC + lane + 64 * k, acc[k] / l);
+    if (lane == 0 && lse_part != nullptr) lse_part[ob] = (m + __log2f(l)) * LN2;
+  }
+}
+
+}  // namespace attn
+}  // namespace mla

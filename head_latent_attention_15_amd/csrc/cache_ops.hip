@@ -1,11 +1,12 @@
-// Cache-side kernels: query RoPE, latent-cache append, paging-index validation, and a
-// plain streaming-read kernel used as the measured HBM read ceiling.
+// Cache-side kernels: query RoPE, latent-cache append, paging-index validation, and two
+// streaming-read kernels (plain vector loads; LDS DMA) used as measured HBM read ceilings.
 //
 // RoPE ("kasblo.com/?p=4663", "分離したRoPE"; qiita.com/joule "RoPE の扱い"): pair
 // (x[2k], x[2k+1]) turns by pos * base^(-2k/d_R); the decoupled key k^R is shared by all
 // heads and cached after rotation next to the latent c^KV ("論文解説: DeepSeek-V2 …",
 // "Decoupled RoPE": 576 elements per token per layer).
 #include "device_common.h"
+#include "attn_common.h"
 #include "launchers.h"
 
 namespace mla {
@@ -151,6 +152,38 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
   if (threadIdx.x == 0) sink[blockIdx.x] = static_cast<float>(acc & 0xffff);
+}
+
+// Streaming read through LDS DMA, the copy instruction the attention kernels stage their
+// cache tiles with: 8 wavefronts per workgroup, each copying 1 KB units (16 bytes per lane,
+// global_load_lds_dwordx4) grid-stride into a 16-slot LDS ring with up to 15 copies in
+// flight, so the chip holds ~128 KB of reads in flight per CU.  Nothing computes on the
+// data; after the last copy each workgroup writes one word of its LDS to the sink.
+constexpr int kDmaSlots = 16;
+
+__global__ __launch_bounds__(512) void stream_read_lds_kernel(const char* __restrict__ src,
+                                                              int64_t units,
+                                                              float* __restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) char ring[8 * kDmaSlots * 1024];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const uint32_t base = static_cast<uint32_t>(
+      reinterpret_cast<size_t>((__attribute__((address_space(3))) char*)ring)) + w * kDmaSlots * 1024;
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * 8;
+  int k = 0;
+  for (int64_t u = blockIdx.x * 8 + w; u < units; u += nw, ++k) {
+    if (k >= kDmaSlots) attn::wait_vmcnt<kDmaSlots - 1>();  // the slot's previous copy landed
+    attn::dma16(src + u * 1024, static_cast<uint32_t>(lane) * 16u, base + (k % kDmaSlots) * 1024);
+  }
+  attn::wait_vmcnt<0>();
+  attn::block_barrier();
+  if (threadIdx.x == 0) sink[blockIdx.x] = static_cast<float>(*reinterpret_cast<volatile int*>(ring) & 0xffff);
+}
+
+hipError_t launch_stream_read_lds(const void* src, size_t bytes, float* sink, int grid,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(stream_read_lds_kernel, dim3(grid), dim3(512), 0, s,
+                     static_cast<const char*>(src), static_cast<int64_t>(bytes / 1024), sink);
+  return hipGetLastError();
 }
 
 hipError_t launch_stream_read(const void* src, size_t bytes, float* sink, hipStream_t s) {

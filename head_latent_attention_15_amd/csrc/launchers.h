@@ -30,6 +30,10 @@ hipError_t launch_attn_generic_bf16_512_64(const PagedArgs& a, hipStream_t s);
 // Decode attention on bf16 MFMA, all heads of a (sequence, split) per workgroup.
 hipError_t launch_attn_mfma_bf16_512_64(const PagedArgs& a, hipStream_t s);
 bool attn_mfma_supported(const PagedArgs& a);
+// The same product for 128 heads with the latent product partitioned by columns across the
+// wavefronts (each LDS fragment read feeds several MFMAs).
+hipError_t launch_attn_cols_bf16_512_64(const PagedArgs& a, hipStream_t s);
+bool attn_cols_supported(const PagedArgs& a);
 
 // Split-K combine fused with the W^UV up-projection (d_c = 512, d_h = 128, S <= 64, bf16
 // W^UV): o_heads[b][i] = W^UV_i combine_s(o_part[b][i][s], lse_part[b][i][s]).
@@ -106,5 +110,8 @@ hipError_t launch_validate_indices(const int32_t* block_table, const int32_t* se
                                    hipStream_t s);
 
 hipError_t launch_stream_read(const void* src, size_t bytes, float* sink, hipStream_t s);
+
+hipError_t launch_stream_read_lds(const void* src, size_t bytes, float* sink, int grid,
+                                  hipStream_t s);
 
 }  // namespace mla

@@ -138,7 +138,8 @@ static mla_status_t decode_attn(const void* q_lat, const void* q_pe, const void*
                              const int32_t* block_table, const int32_t* seq_lens,
                              const mla_paged_shape_t* shape, float softmax_scale,
                              int32_t num_splits, void* o_part, mla_dtype_t part_dtype,
-                             float* lse_part, mla_dtype_t dtype, int32_t n_q, void* stream) {
+                             float* lse_part, mla_dtype_t dtype, int32_t n_q, int32_t kernel,
+                             void* stream) {
   if (!q_lat || !q_pe || !kv_cache || !block_table || !seq_lens || !o_part)
     return fail(MLA_ERR_NULL, "mla_decode_attn: a required pointer is NULL");
   mla_status_t st = check_paged_shape(shape);
@@ -177,11 +178,22 @@ static mla_status_t decode_attn(const void* q_lat, const void* q_pe, const void*
   a.n_q = n_q;
   hipStream_t s = as_stream(stream);
 
+  if (kernel < 0 || kernel > 3) return fail(MLA_ERR_UNSUPPORTED, "attention kernel %d unknown", kernel);
   if (dtype == MLA_BF16 && a.d_c == 512 && a.d_R == 64 && a.H <= 128) {
-    if (mla::attn_mfma_supported(a))
-      return launched(mla::launch_attn_mfma_bf16_512_64(a, s), "attention (bf16 MFMA)");
+    const bool cols = mla::attn_cols_supported(a), heads = mla::attn_mfma_supported(a);
+    if (kernel == 0) kernel = cols ? 2 : heads ? 1 : 3;
+    if (kernel == 2 && !cols)
+      return fail(MLA_ERR_UNSUPPORTED, "attention kernel 2 needs H = 128, pages of >= 32 tokens "
+                  "(a power of two), <= 1024 pages per split and 16-byte aligned tensors");
+    if (kernel == 1 && !heads)
+      return fail(MLA_ERR_UNSUPPORTED, "attention kernel 1 needs H in {16, 32, 64, 128}, pages of "
+                  ">= 32 tokens (a power of two), <= 1024 pages per split, aligned tensors");
+    if (kernel == 2) return launched(mla::launch_attn_cols_bf16_512_64(a, s), "attention (bf16 MFMA, column-partitioned)");
+    if (kernel == 1) return launched(mla::launch_attn_mfma_bf16_512_64(a, s), "attention (bf16 MFMA)");
     return launched(mla::launch_attn_generic_bf16_512_64(a, s), "attention (bf16 generic)");
   }
+  if (kernel == 1 || kernel == 2)
+    return fail(MLA_ERR_UNSUPPORTED, "attention kernels 1 and 2 need d_latent 512, d_rope 64, BF16");
   if (dtype == MLA_F32 && a.d_c == 64 && a.d_R == 16 && a.H <= 64)
     return launched(mla::launch_attn_generic_f32_64_16(a, s), "attention (fp32)");
   return fail(MLA_ERR_UNSUPPORTED,
@@ -196,7 +208,17 @@ mla_status_t mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv
                              int32_t num_splits, void* o_part, mla_dtype_t part_dtype,
                              float* lse_part, mla_dtype_t dtype, void* stream) {
   return decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, shape, softmax_scale,
-                     num_splits, o_part, part_dtype, lse_part, dtype, 1, stream);
+                     num_splits, o_part, part_dtype, lse_part, dtype, 1, 0, stream);
+}
+
+mla_status_t mla_decode_attn_planned(const void* q_lat, const void* q_pe, const void* kv_cache,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     const mla_paged_shape_t* shape, int32_t n_q,
+                                     float softmax_scale, int32_t num_splits, void* o_part,
+                                     mla_dtype_t part_dtype, float* lse_part, mla_dtype_t dtype,
+                                     int32_t kernel, void* stream) {
+  return decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, shape, softmax_scale,
+                     num_splits, o_part, part_dtype, lse_part, dtype, n_q, kernel, stream);
 }
 
 mla_status_t mla_decode_attn_multi(const void* q_lat, const void* q_pe, const void* kv_cache,
@@ -206,7 +228,7 @@ mla_status_t mla_decode_attn_multi(const void* q_lat, const void* q_pe, const vo
                                    mla_dtype_t part_dtype, float* lse_part, mla_dtype_t dtype,
                                    void* stream) {
   return decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, shape, softmax_scale,
-                     num_splits, o_part, part_dtype, lse_part, dtype, n_q, stream);
+                     num_splits, o_part, part_dtype, lse_part, dtype, n_q, 0, stream);
 }
 
 mla_status_t mla_splitk_combine(const void* o_part, mla_dtype_t part_dtype,
@@ -489,6 +511,21 @@ mla_status_t mla_stream_read(const void* src, size_t bytes, float* sink, void* s
   if (bytes == 0 || bytes % 16 != 0)
     return fail(MLA_ERR_SHAPE, "mla_stream_read: bytes %zu must be a positive multiple of 16", bytes);
   return launched(mla::launch_stream_read(src, bytes, sink, as_stream(stream)), "stream read");
+}
+
+mla_status_t mla_stream_read_lds(const void* src, size_t bytes, float* sink, void* stream) {
+  if (!src || !sink) return fail(MLA_ERR_NULL, "mla_stream_read_lds: NULL pointer");
+  if (bytes == 0 || bytes % 1024 != 0)
+    return fail(MLA_ERR_SHAPE, "mla_stream_read_lds: bytes %zu must be a positive multiple of 1024",
+                bytes);
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0)
+    return fail(MLA_ERR_SHAPE, "mla_stream_read_lds: src is not 16-byte aligned");
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return fail(MLA_ERR_LAUNCH, "mla_stream_read_lds: cannot query the compute-unit count");
+  return launched(mla::launch_stream_read_lds(src, bytes, sink, cus, as_stream(stream)),
+                  "stream read (LDS DMA)");
 }
 
 }  // extern "C"

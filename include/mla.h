@@ -199,6 +199,22 @@ mla_status_t mla_decode_attn_multi(const void* q_lat, const void* q_pe, const vo
                                    mla_dtype_t part_dtype, float* lse_part, mla_dtype_t dtype,
                                    void* stream);
 
+/* mla_decode_attn_multi with an explicit attention kernel, for measurement and for tests
+ * that cover each kernel: 0 = the library's choice (as mla_decode_attn_multi), 1 = the
+ * head-partitioned MFMA kernel (16 heads per wavefront; H in {16, 32, 64, 128}), 2 = the
+ * column-partitioned MFMA kernel (H = 128; each wavefront owns 64 latent columns of the
+ * weighted sum), 3 = the generic VALU kernel.  Kernels 1 and 2 need d_latent 512,
+ * d_rope 64, BF16, pages of >= 32 tokens (a power of two), at most 1024 pages per split
+ * and 16-byte aligned q_lat, q_pe, kv_cache (and o_part for 2).  Same results, within
+ * rounding order, as mla_decode_attn_multi.
+ * Errors: as mla_decode_attn_multi, plus UNSUPPORTED for a kernel the shape cannot take. */
+mla_status_t mla_decode_attn_planned(const void* q_lat, const void* q_pe, const void* kv_cache,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     const mla_paged_shape_t* shape, int32_t n_q,
+                                     float softmax_scale, int32_t num_splits, void* o_part,
+                                     mla_dtype_t part_dtype, float* lse_part, mla_dtype_t dtype,
+                                     int32_t kernel, void* stream);
+
 /* Log-sum-exp combine of split partials (exact re-assembly of one softmax whose sum
  * over tokens was cut into disjoint ranges; qiita "Attention 計算").
  *   M = max_s lse_s; w_s = e^{lse_s - M} (0 for lse_s = -inf)
@@ -299,6 +315,14 @@ mla_status_t mla_validate_indices(const int32_t* block_table, const int32_t* seq
  * sink[0 .. 4095] so the reads cannot be elided: a plain read kernel giving the
  * practical HBM read ceiling next to the attention kernel.  Errors: NULL, SHAPE. */
 mla_status_t mla_stream_read(const void* src, size_t bytes, float* sink, void* stream);
+
+/* The same measurement with the copy instruction the attention kernels stage cache tiles
+ * with (LDS DMA, global_load_lds_dwordx4): one workgroup of 8 wavefronts per compute unit,
+ * each wavefront keeping up to 15 one-kilobyte copies in flight; nothing computes on the
+ * data.  Writes one float per workgroup to sink[0 .. CUs-1] (the caller provides at least
+ * as many floats as the device has compute units).  `bytes` a multiple of 1024, src
+ * 16-byte aligned.  Errors: NULL, SHAPE, LAUNCH (device query). */
+mla_status_t mla_stream_read_lds(const void* src, size_t bytes, float* sink, void* stream);
 
 /* mla_linear with an explicit kernel and plan, for measurement and for tests that cover
  * each plan: kernel 0 is the tile-grid GEMM (tile = 16-column tiles per wavefront 1, 2 or
