@@ -67,6 +67,7 @@ _SIGNATURES = {
     "mla_combine_out_proj": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _I32, _I32, _P,
                                     _P]),
     "mla_decode": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _SZ, _P, _P, _I32, _P]),
+    "mla_decode_noalloc": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _P, _I32, _P]),
     "mla_out_proj": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "mla_linear": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P]),
     "mla_linear_strided": (_I32, [_P, _I32, _I64, _P, _I32, _I32, _I32, _I32, _P, _I64, _I32,
@@ -472,6 +473,23 @@ def mla_decode(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale, num_
         _dev(kv_cache, "kv_cache", None, 3), _dev(block_table, "block_table", torch.int32, 2),
         _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), float(softmax_scale),
         int(num_splits), ws_ptr, ws_bytes, _dev(out, "out", torch.float32, 3),
+        _dev(lse_out, "lse_out", torch.float32, 2), _dtype_code(q_lat), _stream(stream))
+
+
+def mla_decode_noalloc(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale,
+                       num_splits, out, lse_out=None, stream=None):
+    """mla_decode with the split partials in the library's fixed device scratch (48 MiB):
+    the call allocates no device memory."""
+    torch = _torch()
+    B, H, d_c = q_lat.shape
+    _expect(q_pe.dtype == q_lat.dtype == kv_cache.dtype, "q_lat, q_pe, kv_cache share a dtype")
+    _expect(tuple(out.shape) == (B, H, d_c), "out must be [B,H,d_c]")
+    shp = paged_shape(kv_cache, block_table, H, d_c)
+    _invoke("mla_decode_noalloc",
+        _dev(q_lat, "q_lat", None, 3), _dev(q_pe, "q_pe", None, 3),
+        _dev(kv_cache, "kv_cache", None, 3), _dev(block_table, "block_table", torch.int32, 2),
+        _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), float(softmax_scale),
+        int(num_splits), _dev(out, "out", torch.float32, 3),
         _dev(lse_out, "lse_out", torch.float32, 2), _dtype_code(q_lat), _stream(stream))
 
 

@@ -111,6 +111,10 @@ hipError_t launch_validate_indices(const int32_t* block_table, const int32_t* se
 
 hipError_t launch_stream_read(const void* src, size_t bytes, float* sink, hipStream_t s);
 
+// The fixed device scratch of the entry point that allocates nothing: its size, and the
+// current device's copy (looked up with hipGetSymbolAddress on a device's first use).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** out);
 hipError_t launch_stream_read_lds(const void* src, size_t bytes, float* sink, int grid,
                                   hipStream_t s);
 

@@ -298,6 +298,34 @@ mla_status_t mla_decode(const void* q_lat, const void* q_pe, const void* kv_cach
                             num_splits, shape->d_latent, out, lse_out, stream);
 }
 
+mla_status_t mla_decode_noalloc(const void* q_lat, const void* q_pe, const void* kv_cache,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                const mla_paged_shape_t* shape, float softmax_scale,
+                                int32_t num_splits, float* out, float* lse_out, mla_dtype_t dtype,
+                                void* stream) {
+  mla_status_t st = check_paged_shape(shape);
+  if (st != MLA_OK) return st;
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(MLA_ERR_SHAPE, "num_splits %d outside [1, %d]", num_splits, kMaxSplits);
+  if (num_splits == 1)  // no partials: the attention writes out directly
+    return mla_decode(q_lat, q_pe, kv_cache, block_table, seq_lens, shape, softmax_scale, 1,
+                      nullptr, 0, out, lse_out, dtype, stream);
+  const size_t need =
+      mla_decode_workspace_bytes(shape->batch, shape->num_heads, shape->d_latent, num_splits);
+  const size_t cap = mla::noalloc_scratch_bytes();
+  if (need > cap)
+    return fail(MLA_ERR_WORKSPACE,
+                "mla_decode_noalloc: %zu bytes of split partials (B=%d H=%d d_latent=%d S=%d) "
+                "exceed the %zu-byte device scratch; use fewer splits or mla_decode",
+                need, shape->batch, shape->num_heads, shape->d_latent, num_splits, cap);
+  void* ws = nullptr;
+  const hipError_t e = mla::noalloc_scratch(&ws);
+  if (e != hipSuccess)
+    return fail(MLA_ERR_LAUNCH, "mla_decode_noalloc: device scratch lookup: %s", hipGetErrorString(e));
+  return mla_decode(q_lat, q_pe, kv_cache, block_table, seq_lens, shape, softmax_scale,
+                    num_splits, ws, cap, out, lse_out, dtype, stream);
+}
+
 static mla_status_t absorb_q(const char* fn, const float* q_c, int64_t ld_qc, const void* w_uk,
                              const float* q_r, int64_t ld_qr, const int32_t* seq_lens,
                              float rope_base, void* q_lat, void* q_pe, int32_t B, int32_t H,

@@ -256,6 +256,23 @@ mla_status_t mla_decode(const void* q_lat, const void* q_pe, const void* kv_cach
                         int32_t num_splits, void* workspace, size_t workspace_bytes,
                         float* out, float* lse_out, mla_dtype_t dtype, void* stream);
 
+/* mla_decode for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the split partials go to a fixed
+ * device scratch array of 48 MiB that the library holds on every GPU it runs on until the
+ * process ends, instead of a caller workspace.  The call itself allocates nothing: no
+ * hipMalloc, no hipFree, no allocating library routine.  Same kernels, partial dtype and
+ * results (bit for bit) as mla_decode with the same num_splits.  Every call on one GPU
+ * shares that GPU's scratch and leaves its partials there; each call overwrites every
+ * partial it reads, so nothing needs clearing, but calls that overlap on one GPU (two
+ * streams, or two host threads) race and must be serialised by the caller.
+ * Errors: as mla_decode, plus WORKSPACE when mla_decode_workspace_bytes(B, H, d_latent,
+ * num_splits) exceeds 48 MiB (nothing is launched), LAUNCH if the scratch cannot be found. */
+mla_status_t mla_decode_noalloc(const void* q_lat, const void* q_pe, const void* kv_cache,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                const mla_paged_shape_t* shape, float softmax_scale,
+                                int32_t num_splits, float* out, float* lse_out, mla_dtype_t dtype,
+                                void* stream);
+
 /* Value up-projection and output projection.
  *   o_heads[b][i][d] = sum_c w_uv[i*d_h + d][c] * o_lat[b][i][c]    (o_i = W^UV_i o~_i)
  *   u[b][n] = sum_k w_o[n][k] * o_heads[b][k]   (k over H*d_h; u = W^O [o_1;...;o_H])
