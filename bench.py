@@ -41,7 +41,7 @@ ROW_BYTES = 576 * 2             # one cached token: c^KV (512) + k^R (64), bf16
 FLOP_PER_TOKEN_HEAD = 2 * (576 + 512)
 N_CACHE_COPIES = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_dsv2_b32_t4k_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "head_latent_attention_15_amd", "csrc", "attn_cols.hip")
+KERNEL_SRC = os.path.join(ROOT, "head_latent_attention_15_amd", "csrc", "attn_mfma.hip")
 
 
 def log(*a):
@@ -341,10 +341,11 @@ def multi_token_rows(mla, W, torch, caches, bt, sl, scale, num_cus, n_q: int = 2
 
 
 def config_row(mla, torch, inp, name, num_cus, steps, n_copies, kernel="auto"):
-    """One attention workload beside the headline: the whole step (attention + combine,
-    bf16 partials) and the attention alone, back to back over n_copies rotating caches,
-    with algorithmic bytes (cache rows of every sequence, queries, tables; the combined
-    output for the step) and the fraction of the 8 TB/s HBM roofline."""
+    """One attention workload beside the headline: the whole step (attention + combine, bf16
+    partials), the attention alone and mla_decode_fused (one launch that merges its splits
+    when the grid fits the device at once), back to back over n_copies rotating caches, with
+    algorithmic bytes (cache rows of every sequence, queries, tables; the combined output
+    for the step) and the fraction of the 8 TB/s HBM roofline."""
     dev = torch.device("cuda:0")
     B, H, d_c = inp["q_lat"].shape
     sl = inp["seq_lens"]
@@ -358,25 +359,33 @@ def config_row(mla, torch, inp, name, num_cus, steps, n_copies, kernel="auto"):
     lse_part = torch.empty(B, H, S, device=dev)
     out = torch.empty(B, H, d_c, device=dev)
     lse = torch.empty(B, H, device=dev)
+    counters = mla.merge_counters(B)
     calls = [mla.bind(mla.mla_decode_attn_planned, q_lat, q_pe, c, bt, sld, inp["scale"], S,
                       o_part, lse_part, kernel=kernel) for c in caches]
     combine = mla.bind(mla.mla_splitk_combine, o_part, lse_part, out, lse)
+    fused = [mla.bind(mla.mla_decode_fused, q_lat, q_pe, c, bt, sld, inp["scale"], S, o_part,
+                      lse_part, counters, out, lse) for c in caches]
     t0 = time.perf_counter()
     k = 0
     while time.perf_counter() - t0 < 0.3:
         calls[k % n_copies]()
         combine()
+        fused[k % n_copies]()
         k += 1
         if k % 32 == 0:
             torch.cuda.synchronize()
     step_ms = timed_ms(torch, lambda k: (calls[k % n_copies](), combine()), steps)
     attn_ms = timed_ms(torch, lambda k: calls[k % n_copies](), steps)
+    fused_ms = timed_ms(torch, lambda k: fused[k % n_copies](), steps)
     tokens = int(sl.sum())
     attn_bytes = tokens * ROW_BYTES + B * H * 576 * 2 + bt.numel() * 4 + B * 4
     step_bytes = attn_bytes + B * H * 512 * 4
+    single = bool(mla.mla_decode_fused_single_launch(mla.paged_shape(inp["cache"], inp["block_table"], H, d_c),
+                                                     1, S))
     del caches
     return {"workload": name, "B": B, "H": H, "tokens": tokens, "num_splits": S,
             "us_per_step": round(step_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
+            "us_one_launch_merge": round(fused_ms * 1e3, 2) if single else None,
             "cache_GBps_step": round(tokens * ROW_BYTES / (step_ms * 1e-3) / 1e9, 1),
             "step_frac": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "attn_GBps": round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1),
@@ -406,7 +415,8 @@ def main():
                     help="keep warming up until this much time has passed (clocks settle)")
     ap.add_argument("--splits", type=int, default=0, help="split count (0: library suggestion)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "cols", "heads"],
-                    help="attention kernel of the headline step (auto: the library's choice)")
+                    help="attention kernel timed alone beside the step (auto: the library's "
+                         "choice, the head-partitioned kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32)
     ap.add_argument("--cpu-baseline-only", action="store_true",
@@ -457,20 +467,32 @@ def main():
     q_lat, q_pe = inp["q_lat"].to(dev), inp["q_pe"].to(dev)
     bt, sl = inp["block_table"].to(dev), inp["seq_lens"].to(dev)
     o_part = torch.empty(B, H, S, 512, device=dev, dtype=torch.bfloat16)
+    o_part_f32 = torch.empty(B, H, S, 512, device=dev)
     lse_part = torch.empty(B, H, S, device=dev)
     out = torch.empty(B, H, 512, device=dev)
     lse = torch.empty(B, H, device=dev)
+    counters = mla.merge_counters(B)
     scale = inp["scale"]
 
     # arguments checked and marshalled once per cache copy, so the host issues each launch
     # in a few microseconds and the timed regions measure the GPU, not Python
-    def attn_calls_for(kernel):
-        return [mla.bind(mla.mla_decode_attn_planned, q_lat, q_pe, c, bt, sl, scale, S, o_part,
+    def attn_calls_for(kernel, part):
+        return [mla.bind(mla.mla_decode_attn_planned, q_lat, q_pe, c, bt, sl, scale, S, part,
                          lse_part, kernel=kernel) for c in caches]
-    attn_calls = attn_calls_for(args.kernel)
-    other = "heads" if args.kernel in ("auto", "cols") else "cols"
-    other_calls = attn_calls_for(other)
+
+    def fused_calls_for(part):
+        return [mla.bind(mla.mla_decode_fused, q_lat, q_pe, c, bt, sl, scale, S, part, lse_part,
+                         counters, out, lse) for c in caches]
+    attn_calls = attn_calls_for(args.kernel, o_part)          # the step: attention + combine
     combine = mla.bind(mla.mla_splitk_combine, o_part, lse_part, out, lse)
+    attn_f32_calls = attn_calls_for(args.kernel, o_part_f32)  # the same with fp32 partials
+    combine_f32 = mla.bind(mla.mla_splitk_combine, o_part_f32, lse_part, out, lse)
+    fused_calls = fused_calls_for(o_part)  # one launch that merges the splits itself
+    other = "heads" if args.kernel == "cols" else "cols"
+    other_calls = attn_calls_for(other, o_part)
+
+    def step_fused(k):
+        fused_calls[k % N_CACHE_COPIES]()
 
     def attn(k):
         attn_calls[k % N_CACHE_COPIES]()
@@ -482,6 +504,9 @@ def main():
     while k < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
         attn(k)
         combine()
+        attn_f32_calls[k % N_CACHE_COPIES]()
+        combine_f32()
+        step_fused(k)
         other_calls[k % N_CACHE_COPIES]()
         k += 1
         if k % 32 == 0:
@@ -490,13 +515,21 @@ def main():
     log(f"warmup {k} steps ({time.perf_counter() - t_w:.2f} s), S={S}, {num_cus} CUs")
 
     ms_step = timed_ms(torch, lambda k: (attn(k), combine()), args.steps)
-    # second and third regions: each kernel alone, back to back, events at the ends only
-    # (an event recorded between two kernels stalls the queue for several microseconds,
-    # so per-kernel events would time the stall with the kernel)
+    # the other timed regions, each back to back with events at the ends only (an event
+    # recorded between two kernels stalls the queue for several microseconds, so
+    # per-kernel events would time the stall with the kernel)
+    ms_step_f32 = timed_ms(torch, lambda k: (attn_f32_calls[k % N_CACHE_COPIES](), combine_f32()),
+                           args.steps)
+    ms_fused = timed_ms(torch, step_fused, args.steps)
     attn_avg = timed_ms(torch, attn, args.steps)
     comb_avg = timed_ms(torch, lambda k: combine(), args.steps)
     other_avg = timed_ms(torch, lambda k: other_calls[k % N_CACHE_COPIES](), args.steps)
-    log(f"step {ms_step * 1e3:.1f} us; attention alone {attn_avg * 1e3:.1f} us "
+    c = counters.cpu()
+    if int(c[-1]) != 0 or int(c[:-1].abs().sum()) != 0 or not bool(torch.isfinite(out).all()):
+        raise RuntimeError("in-launch merge left its counters set or a non-finite output")
+    log(f"step (attention + combine) {ms_step * 1e3:.1f} us, fp32 partials "
+        f"{ms_step_f32 * 1e3:.1f} us; one launch merging its splits {ms_fused * 1e3:.1f} us; "
+        f"attention alone {attn_avg * 1e3:.1f} us "
         f"({other} kernel {other_avg * 1e3:.1f} us); combine alone {comb_avg * 1e3:.1f} us")
 
     # streaming reads of the cache copies: the practical HBM read ceilings, with plain
@@ -526,12 +559,13 @@ def main():
     step_alg_bytes = cache_bytes + B * H * 576 * 2 + B * H * 512 * 4 + bt.numel() * 4 + B * 4
     flops = tokens * H * FLOP_PER_TOKEN_HEAD
     attn_s = attn_avg * 1e-3
-    # what one attention launch must move: the cache rows, the queries, the block table and
+    # what the attention alone must move: the cache rows, the queries, the block table and
     # the lengths (split partials are an implementation choice and are not counted)
     attn_alg_bytes = cache_bytes + B * H * 576 * 2 + bt.numel() * 4 + B * 4
+    # the dominant kernel of the step is the attention: its algorithmic bytes per launch
+    # over its average back-to-back launch duration
     achieved = attn_alg_bytes / attn_s / 1e9
     traffic = measured_traffic()
-    kname = {"auto": "cols", "cols": "cols", "heads": "heads"}[args.kernel]
     result = {
         "metric": METRIC,
         "value": round(cache_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -547,14 +581,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": "dsv2_b32_t4k", "B": B, "T": T, "H": H, "d_c": 512, "d_R": 64,
                    "page_size": 64, "num_splits": S, "split_partials": "bf16",
-                   "attention_kernel": kname, "cache_copies": N_CACHE_COPIES,
-                   "parallelism": "none"},
+                   "split_merge": "combine kernel (mla_splitk_combine)",
+                   "attention_kernel": "heads" if args.kernel != "cols" else "cols",
+                   "cache_copies": N_CACHE_COPIES, "parallelism": "none"},
         "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "query_tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "step_bytes_algorithmic": step_alg_bytes,
-        # the whole step (attention + combine) against the HBM roofline: the figure the
-        # headline value is; roofline.frac below is the attention kernel alone
         "step_frac": round(step_alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        # the whole step against the HBM roofline: the figure the headline value is;
+        # roofline.frac below is the attention kernel alone
+        "step_us_f32_partials": round(ms_step_f32 * 1e3, 2),
+        "step_us_one_launch_merge": round(ms_fused * 1e3, 2),
         "attn_us": round(attn_avg * 1e3, 2),
         "combine_us": round(comb_avg * 1e3, 2),
         f"attn_us_{other}_kernel": round(other_avg * 1e3, 2),
@@ -566,10 +603,9 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
                      "frac_of_lds_dma_ceiling": round(achieved / stream_gbps_lds, 4),
-                     "kernel": ("attn_cols_kernel<bf16 partials> (8 waves: scores by 32-head "
-                                "groups x k parity, latent product by 64-column blocks)"
-                                if kname == "cols" else
-                                "attn_mfma_kernel<8, bf16 partials> (8 waves x 16 heads)"),
+                     "kernel": ("attn_cols_kernel<bf16 partials> (8 waves: scores by 16-head "
+                                "blocks, latent product by 64-column blocks)" if args.kernel == "cols"
+                                else "attn_mfma_kernel<8, bf16 partials> (8 waves x 16 heads)"),
                      "bytes_per_launch_algorithmic": attn_alg_bytes},
     }
     del caches

@@ -63,6 +63,9 @@ _SIGNATURES = {
                                      _P]),
     "mla_decode_attn_planned": (_I32, [_P, _P, _P, _P, _P, _SP, _I32, _F, _I32, _P, _I32, _P,
                                        _I32, _I32, _P]),
+    "mla_decode_fused": (_I32, [_P, _P, _P, _P, _P, _SP, _I32, _F, _I32, _P, _I32, _P, _P, _P,
+                                _P, _I32, _P]),
+    "mla_decode_fused_single_launch": (_I32, [_SP, _I32, _I32]),
     "mla_splitk_combine": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "mla_combine_out_proj": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _I32, _I32, _P,
                                     _P]),
@@ -425,6 +428,59 @@ def mla_decode_attn_planned(q_lat, q_pe, kv_cache, block_table, seq_lens, softma
         _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), n_q, float(softmax_scale),
         S, _dev(o_part, "o_part"), _dtype_code(o_part), _dev(lse_part, "lse_part", torch.float32),
         _dtype_code(q_lat), k, _stream(stream))
+
+
+def merge_counters(rows, device=None):
+    """A zeroed int32 counter array for mla_decode_fused with `rows` = B * n_q query rows
+    (2 counters per row and the error word); every call leaves it zeroed for the next."""
+    torch = _torch()
+    return torch.zeros(2 * int(rows) + 1, dtype=torch.int32, device=device or "cuda")
+
+
+def mla_decode_fused(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale, num_splits,
+                     o_part, lse_part, counters, out, lse_out=None, stream=None):
+    """Attention and split combine in one launch (q_lat [B,H,d_c] or [B,n_q,H,d_c]); o_part
+    [rows,H,S,d_c] (fp32 or bf16) and lse_part [rows,H,S] are scratch, counters from
+    merge_counters(rows), out [rows,H,d_c] fp32."""
+    torch = _torch()
+    if q_lat.dim() == 3:
+        B, H, d_c = q_lat.shape
+        n_q = 1
+    else:
+        B, n_q, H, d_c = q_lat.shape
+    rows = B * n_q
+    _expect(tuple(q_pe.shape[:-1]) == tuple(q_lat.shape[:-1]), "q_pe must match q_lat but the last dim")
+    _expect(q_pe.dtype == q_lat.dtype == kv_cache.dtype, "q_lat, q_pe, kv_cache share a dtype")
+    _expect(kv_cache.shape[2] == d_c + q_pe.shape[-1], "cache row must be d_c + d_R wide")
+    _expect(block_table.shape[0] == B and tuple(seq_lens.shape) == (B,), "batch mismatch")
+    S = int(num_splits)
+    _expect(out.numel() == rows * H * d_c, "out must hold B*n_q*H*d_c floats")
+    if lse_out is not None:
+        _expect(lse_out.numel() == rows * H, "lse_out must hold B*n_q*H floats")
+    if S > 1:
+        _expect(o_part is not None and o_part.numel() == rows * H * S * d_c,
+                "o_part must hold B*n_q*H*S*d_c elements")
+        _expect(lse_part is not None and lse_part.numel() == rows * H * S,
+                "lse_part must hold B*n_q*H*S floats")
+        _expect(counters is not None and counters.numel() >= 2 * rows + 1,
+                "counters must hold 2*B*n_q + 1 int32 (merge_counters)")
+    shp = paged_shape(kv_cache, block_table, H, d_c)
+    _invoke("mla_decode_fused",
+        _dev(q_lat, "q_lat"), _dev(q_pe, "q_pe"),
+        _dev(kv_cache, "kv_cache", None, 3), _dev(block_table, "block_table", torch.int32, 2),
+        _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), n_q, float(softmax_scale),
+        S, _dev(o_part, "o_part") if S > 1 else None,
+        _dtype_code(o_part) if S > 1 else MLA_F32,
+        _dev(lse_part, "lse_part", torch.float32) if S > 1 else None,
+        _dev(counters, "counters", torch.int32, 1) if S > 1 else None,
+        _dev(out, "out", torch.float32), _dev(lse_out, "lse_out", torch.float32),
+        _dtype_code(q_lat), _stream(stream))
+
+
+def mla_decode_fused_single_launch(shape, n_q, num_splits) -> int:
+    """1 if mla_decode_fused merges inside the attention launch for this paged shape
+    (paged_shape(...)), n_q and split count on the current device; else 0."""
+    return int(lib.mla_decode_fused_single_launch(ctypes.byref(shape), int(n_q), int(num_splits)))
 
 
 def mla_splitk_combine(o_part, lse_part, out, lse_out=None, stream=None):

@@ -12,30 +12,28 @@
 //
 // One workgroup of 8 wavefronts per (sequence, split) holds all 128 heads, so each cache
 // byte crosses HBM once; 32-token tiles go HBM -> LDS with LDS DMA (attn_common.h) into
-// three buffers.  The point of this kernel is how few LDS bytes each matrix-core operation
-// needs.  Giving every wavefront 16 heads for both products (attn_mfma.hip) makes all eight
-// read the whole tile twice, ~15x the staged bytes.  Here:
+// three buffers.  Wave w has two jobs per tile:
+//   scores: the 16 heads of block w (heads 16 w .. 16 w + 15) against the whole tile,
+//           S^T = K (32 x 576) Q^T (576 x 16) with the queries resident in VGPRs, then
+//           their softmax; the weights P^T go to LDS (1 KB per block, double-buffered);
+//   PV:     latent columns 64 w .. 64 w + 63 of all 128 heads,
+//           O^T (64 x 128) += V^T (64 x 32) P^T (32 x 128): 4 V^T fragments (transposing
+//           reads) x 8 P^T fragments = 32 MFMAs, so the V part of the tile is read from LDS
+//           exactly once and each V fragment feeds eight MFMAs.
+// The score product needs one K fragment read per MFMA, so a wavefront's score phase is
+// bound by LDS latency while its PV phase is bound by the matrix core.  The two
+// wavefronts sharing a SIMD (w and w + 4) therefore run the phases in opposite order:
+// waves 0..3 do PV(it-1) then the scores and softmax of tile it, waves 4..7 the scores
+// and softmax then PV(it-1), so one's MFMA-dense PV fills the other's LDS waits.
 //
-//   scores: wave w = (head group hg = w & 3, k parity fh = w >> 2) multiplies the tile by
-//           the queries of 32 heads (heads 32 hg .. 32 hg + 31) over the k-steps of parity
-//           fh (9 of the 18 32-wide steps), so each K fragment read from LDS feeds two
-//           MFMAs and the queries stay resident without duplication (72 VGPRs).  The two
-//           waves of a head group then trade the partial scores of each other's 16-head
-//           block through LDS (2 KB per wave); each ends with the full scores of its own
-//           block hb = 2 hg + fh, 32 tokens x 16 heads, and runs their softmax;
-//   PV:     the weights P^T of the 8 head blocks go to LDS (8 KB per tile) and wave w
-//           accumulates O^T for latent columns 64 w .. 64 w + 63 of all 128 heads:
-//           4 V^T fragments (transposing reads) x 8 P^T fragments = 32 MFMAs, so the V part
-//           of the tile is read from LDS exactly once.
+// The tile sits in LDS as 9 column blocks (32 rows x 128 bytes; blocks 0..7 the latent, 8
+// the RoPE part), so the only reader of block w in the PV product is wave w: as soon as its
+// V fragments of tile it-1 are in registers, wave w refills block w with tile it+2 (waves
+// 0..3 also one quarter of the RoPE block each) while its MFMAs run.  The copies never
+// queue up behind a barrier.
 //
-// LDS bytes read per tile: 144 KB of K fragments, 64 KB of P, 32 KB of V and 16 KB of
-// exchanged scores, against ~550 KB when every wave reads the whole tile twice.
-//
-// Per tile, two barriers:  A(it) publishes tile it and P(it-1); between A(it) and B(it)
-// each wave runs PV(it-1) and the scores of tile it and stores its partner's partial;
-// B(it) publishes the partials and retires tile it-1, whose buffer receives the copies of
-// tile it+2; between B(it) and A(it+1) each wave adds the partner's partial, runs the
-// softmax of its block and stores its P^T fragment.
+// One barrier per tile, A(it): it publishes tile it (every wave's copies landed) and
+// P(it-1).
 //
 // Softmax reference (as in attn_mfma.hip): each split fixes one reference per head from its
 // first tile (plus headroom) and never rescales the accumulators; the final normalisation
@@ -59,15 +57,33 @@ using namespace attn;
 constexpr int NW = 8;                                // wavefronts per workgroup
 constexpr int NH = 128;                              // heads: 8 blocks of 16
 constexpr int NBUF = 3;                              // tile buffers
-constexpr int XCH = NBUF * TILE_BYTES;               // partial scores, 2 KB per wave
-constexpr int PBUF = XCH + NW * 2048;                // P^T fragments, 1 KB per head block
-constexpr int STATS = PBUF + 8 * 1024;               // denominators (128 floats), block flags (8)
+constexpr int BLOCK_BYTES = TILE * 128;              // one column block of a tile: 4 KB
+constexpr int PBUF = NBUF * TILE_BYTES;              // P^T fragments, 2 x (8 blocks x 1 KB)
+constexpr int STATS = PBUF + 2 * 8 * 1024;           // denominators (128 floats), block flags (8)
 constexpr int PAGE_TABLE = STATS + 1024;             // block-table entries of the split
-constexpr int MAX_SPLIT_PAGES = 1024;                // block-table entries of one split in LDS
+constexpr int MAX_SPLIT_PAGES = 1024;
 constexpr int LDS_BYTES = PAGE_TABLE + MAX_SPLIT_PAGES * 4;
 static_assert(LDS_BYTES <= 163840, "LDS per workgroup");
 constexpr float HEADROOM = 32.0f;  // log2 units between a split's first-tile max and its reference
 constexpr float P_RANGE = 64.0f;   // a score this far above the reference takes the fallback
+
+// LDS offset of 16-byte chunk c (0..71) of tile row t (0..31): column block c >> 3, row t,
+// slot (c & 7) ^ swz(t).  The 128-byte row stride maps rows onto the same banks as the
+// 1152-byte rows of a row-major tile (1152 = 128 mod 256), so the swizzle keeps the score
+// and transposing PV reads conflict-free as it does there.
+__device__ __forceinline__ int chunk_offset(int t, int c) {
+  return (c >> 3) * BLOCK_BYTES + t * 128 + 16 * ((c & 7) ^ swz(t));
+}
+
+// Source offset (bytes from the tile's first row) of lane l of copy q (0..35): the copy
+// fills LDS bytes 1024 q .. 1024 q + 1023 of the tile, i.e. column block q >> 2, rows
+// 8 (q & 3) .. + 7; lane l writes row 8 (q & 3) + (l >> 3), slot l & 7, which holds
+// logical chunk 8 (q >> 2) + ((l & 7) ^ swz(row)).  Rows past `last` repeat row `last`.
+__device__ __forceinline__ uint32_t block_copy_voff(int q, int l, unsigned last) {
+  const unsigned t = 8 * (q & 3) + (l >> 3);
+  const unsigned c = 8 * (q >> 2) + ((l & 7) ^ swz(t));
+  return __umul24(min(t, last), static_cast<unsigned>(ROW_BYTES)) + c * 16;
+}
 
 // LDS stores must land before a barrier publishes them (gfx950 has no implicit wait there).
 __device__ __forceinline__ void publish_barrier() {
@@ -82,8 +98,6 @@ __global__ __launch_bounds__(NW * 64) void attn_cols_kernel(
     const int32_t* __restrict__ seq_lens, int log2P, int max_pages, int pages_per_split,
     int S, float scale_log2, OT* __restrict__ o_part, float* __restrict__ lse_part, int n_q) {
   constexpr int NT = NW * 64;
-  constexpr int COPIES = (TILE_WAVE_COPIES + NW - 1) / NW;  // 5 tile copies per wave
-  constexpr int HALF = KSTEPS / 2;                           // 9 score k-steps per wave
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   lds_char_t* const lsm = (lds_char_t*)smem;  // 32-bit LDS addressing
   const uint32_t smem_lds = static_cast<uint32_t>(reinterpret_cast<size_t>(lsm));
@@ -98,9 +112,6 @@ __global__ __launch_bounds__(NW * 64) void attn_cols_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int P = 1 << log2P;
-  const int hg = w & 3, fh = w >> 2;       // score roles: head group, k-step parity
-  const int hb = 2 * hg + fh;              // own softmax block: heads 16 hb .. 16 hb + 15
-  const int hx = 2 * hg + (fh ^ 1);        // the partner's block
   const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_pages;
 
   const int L = seq_lens[b] - (n_q - 1 - static_cast<int>(blockIdx.z));
@@ -118,32 +129,27 @@ __global__ __launch_bounds__(NW * 64) void attn_cols_kernel(
   }
   const int ntiles = (j1 - j0 + TILE - 1) / TILE;
 
-  // ---- tile copies: wave w issues copies q = w, w + 8, ... of each tile (36 in all); a
-  //      wave without a fifth copy repeats its first (same source, same LDS bytes), so every
-  //      wave counts COPIES copies per tile.
+  // ---- tile copies.  Wave w owns copies 4 w .. 4 w + 3 (column block w) and waves 0..3
+  //      also copy 32 + w (a quarter of the RoPE block): 5 or 4 copies per wave and tile.
+  const int ncopies = w < 4 ? 5 : 4;
   const char* cache_bytes = reinterpret_cast<const char*>(cache);
   // A tile starting at token tb lies inside one page (P % 32 == 0, tiles 32-aligned).
   auto page_base = [&](int pg, int tb) {
     return cache_bytes + ((static_cast<int64_t>(pg) << log2P) + (tb & (P - 1))) * ROW_BYTES;
   };
-  auto copy_index = [&](int r) { return w + NW * r < TILE_WAVE_COPIES ? w + NW * r : w; };
-  // Inside the loop the block-table entries of the split come from an LDS copy, read ahead
-  // of the barrier that precedes the copies: an LDS read keeps the in-order LDS wait
-  // counts, where a scalar load would force full waits.  Each copy's source offsets are
-  // computed in place (a few VALU operations, no memory round trip).
+  auto copy_q = [&](int r) { return r < 4 ? 4 * w + r : 32 + w; };
+  // Inside the loop the block-table entries of the split come from an LDS copy: an LDS
+  // read keeps the in-order LDS wait counts, where a scalar load would force full waits.
   auto split_page = [&](int tb) {
     return __builtin_amdgcn_readfirstlane(((const lds_i32_t*)(lsm + PAGE_TABLE))[(tb - j0) >> log2P]);
   };
-  auto issue_tile = [&](int it, int page) {
-    const int tb = j0 + it * TILE;
-    const char* base = page_base(page, tb);
-    const unsigned last = static_cast<unsigned>(j1 - 1 - tb);  // rows past it repeat it
-    const uint32_t dst = smem_lds + (it % NBUF) * TILE_BYTES;
+  // copy r of this wave for tile it (buffer it % 3), whose rows come from `base`
+  auto issue_copy = [&](const char* base, int it, int r) {
     int ln = lane;
-    asm volatile("" : "+v"(ln));  // recomputed per tile (no long live ranges)
-#pragma unroll
-    for (int r = 0; r < COPIES; ++r)
-      dma16(base, tile_chunk_voff(64u * copy_index(r) + ln, last), dst + copy_index(r) * 64 * 16);
+    asm volatile("" : "+v"(ln));  // recomputed per copy (no long live ranges)
+    const unsigned last = static_cast<unsigned>(j1 - 1 - (j0 + it * TILE));  // rows past it repeat it
+    const int q = copy_q(r);
+    dma16(base, block_copy_voff(q, ln, last), smem_lds + (it % NBUF) * TILE_BYTES + q * 1024);
   };
 
   // ---- prologue: the split's block-table entries go to LDS first (one memory latency);
@@ -156,116 +162,71 @@ __global__ __launch_bounds__(NW * 64) void attn_cols_kernel(
   const int page1 = __builtin_amdgcn_readfirstlane(bt_row[tb1 >> log2P]);
   {
     const char* base = page_base(page0, j0);
-    const unsigned last = static_cast<unsigned>(j1 - 1 - j0);
-#pragma unroll
-    for (int r = 0; r < COPIES; ++r)
-      dma16(base, tile_chunk_voff(64u * copy_index(r) + lane, last),
-            smem_lds + copy_index(r) * 64 * 16);
+    for (int r = 0; r < ncopies; ++r) issue_copy(base, 0, r);
   }
 
-  // ---- resident query fragments (B operand of the score product): qo for the own block
-  //      hb, qx for the partner's block hx; fragment i is k-step 2 i + fh, lane (g, r16)
-  //      holding features 32 (2 i + fh) + 8 g .. + 7 of head 16 blk + r16 (i = 8: the RoPE
-  //      part).  Loaded in one assembly block together with the copies of tile 1, which
-  //      waits for everything but those copies: two tiles are in flight while the
-  //      queries arrive, and no compiler-inserted wait falls after a copy.
-  bf16x8_t qo[HALF], qx[HALF];
+  // ---- resident query fragments (B operand of S^T = K Q^T): lane (g, r16) holds head
+  //      16 w + r16, features 32 kk + 8 g .. + 7 (kk = 16, 17: the RoPE part).  Loaded in
+  //      one assembly block together with the copies of tile 1, which waits for everything
+  //      but those copies: two tiles are in flight while the queries arrive, and no
+  //      compiler-inserted wait falls after a copy.  Here every wave issues five copies of
+  //      tile 1 (waves 4..7 copy their first one twice: same source, same LDS bytes), so
+  //      one wait count serves all.
+  bf16x8_t qf[KSTEPS];
   {
-    const int64_t rowo = static_cast<int64_t>(bq) * NH + 16 * hb + r16;
-    const int64_t rowx = static_cast<int64_t>(bq) * NH + 16 * hx + r16;
-    const bf16raw* qrow_o = q_lat + rowo * DC + 32 * fh + 8 * g;
-    const bf16raw* qrow_x = q_lat + rowx * DC + 32 * fh + 8 * g;
-    const bf16raw* prow_o = q_pe + rowo * DR + 32 * fh + 8 * g;
-    const bf16raw* prow_x = q_pe + rowx * DR + 32 * fh + 8 * g;
+    const int64_t row = static_cast<int64_t>(bq) * NH + 16 * w + r16;
+    const bf16raw* qrow = q_lat + row * DC + 8 * g;
+    const bf16raw* prow = q_pe + row * DR + 8 * g;
     const unsigned last1 = static_cast<unsigned>(j1 - 1 - tb1);
     const uint64_t b64 = reinterpret_cast<uint64_t>(page_base(page1, tb1));
     const uint32_t blo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b64));
     const uint32_t bhi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b64 >> 32));
     const void* base1 = reinterpret_cast<const void*>((static_cast<uint64_t>(bhi) << 32) | blo);
-    static_assert(COPIES == 5, "the assembly block issues five copies");
     uint32_t vo[5], la[5];
 #pragma unroll
     for (int c = 0; c < 5; ++c) {
-      vo[c] = tile_chunk_voff(64u * copy_index(c) + lane, last1);
-      la[c] = __builtin_amdgcn_readfirstlane(smem_lds + TILE_BYTES + copy_index(c) * 64 * 16);
+      const int q = copy_q(c < ncopies ? c : 0);
+      vo[c] = block_copy_voff(q, lane, last1);
+      la[c] = __builtin_amdgcn_readfirstlane(smem_lds + TILE_BYTES + q * 1024);
     }
-    i32x4_t r[2 * HALF];
+    i32x4_t r[KSTEPS];
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
     asm volatile(
         "global_load_dwordx4 %0, %18, off\n\t"
-        "global_load_dwordx4 %1, %18, off offset:128\n\t"
-        "global_load_dwordx4 %2, %18, off offset:256\n\t"
-        "global_load_dwordx4 %3, %18, off offset:384\n\t"
-        "global_load_dwordx4 %4, %18, off offset:512\n\t"
-        "global_load_dwordx4 %5, %18, off offset:640\n\t"
-        "global_load_dwordx4 %6, %18, off offset:768\n\t"
-        "global_load_dwordx4 %7, %18, off offset:896\n\t"
-        "global_load_dwordx4 %8, %20, off\n\t"
-        "global_load_dwordx4 %9, %19, off\n\t"
-        "global_load_dwordx4 %10, %19, off offset:128\n\t"
-        "global_load_dwordx4 %11, %19, off offset:256\n\t"
-        "global_load_dwordx4 %12, %19, off offset:384\n\t"
-        "global_load_dwordx4 %13, %19, off offset:512\n\t"
-        "global_load_dwordx4 %14, %19, off offset:640\n\t"
-        "global_load_dwordx4 %15, %19, off offset:768\n\t"
-        "global_load_dwordx4 %16, %19, off offset:896\n\t"
-        "global_load_dwordx4 %17, %21, off\n\t"
-        "s_mov_b32 m0, %27\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %22, %32\n\t"
-        "s_mov_b32 m0, %28\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %23, %32\n\t"
-        "s_mov_b32 m0, %29\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %24, %32\n\t"
-        "s_mov_b32 m0, %30\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %25, %32\n\t"
-        "s_mov_b32 m0, %31\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %26, %32\n\t"
+        "global_load_dwordx4 %1, %18, off offset:64\n\t"
+        "global_load_dwordx4 %2, %18, off offset:128\n\t"
+        "global_load_dwordx4 %3, %18, off offset:192\n\t"
+        "global_load_dwordx4 %4, %18, off offset:256\n\t"
+        "global_load_dwordx4 %5, %18, off offset:320\n\t"
+        "global_load_dwordx4 %6, %18, off offset:384\n\t"
+        "global_load_dwordx4 %7, %18, off offset:448\n\t"
+        "global_load_dwordx4 %8, %18, off offset:512\n\t"
+        "global_load_dwordx4 %9, %18, off offset:576\n\t"
+        "global_load_dwordx4 %10, %18, off offset:640\n\t"
+        "global_load_dwordx4 %11, %18, off offset:704\n\t"
+        "global_load_dwordx4 %12, %18, off offset:768\n\t"
+        "global_load_dwordx4 %13, %18, off offset:832\n\t"
+        "global_load_dwordx4 %14, %18, off offset:896\n\t"
+        "global_load_dwordx4 %15, %18, off offset:960\n\t"
+        "global_load_dwordx4 %16, %19, off\n\t"
+        "global_load_dwordx4 %17, %19, off offset:64\n\t"
+        "s_mov_b32 m0, %25\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %20, %30\n\t"
+        "s_mov_b32 m0, %26\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %21, %30\n\t"
+        "s_mov_b32 m0, %27\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %22, %30\n\t"
+        "s_mov_b32 m0, %28\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %23, %30\n\t"
+        "s_mov_b32 m0, %29\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %24, %30\n\t"
         "s_waitcnt vmcnt(5)"
         : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
           "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
           "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15]), "=&v"(r[16]), "=&v"(r[17])
-        : "v"(qrow_o), "v"(qrow_x), "v"(prow_o), "v"(prow_x), "v"(vo[0]), "v"(vo[1]),
-          "v"(vo[2]), "v"(vo[3]), "v"(vo[4]), "s"(la[0]), "s"(la[1]), "s"(la[2]), "s"(la[3]),
-          "s"(la[4]), "s"(base1)
+        : "v"(qrow), "v"(prow), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "v"(vo[4]),
+          "s"(la[0]), "s"(la[1]), "s"(la[2]), "s"(la[3]), "s"(la[4]), "s"(base1)
         : "memory", "m0");
 #pragma clang diagnostic pop
 #pragma unroll
-    for (int i = 0; i < HALF; ++i) {
-      qo[i] = __builtin_bit_cast(bf16x8_t, r[i]);
-      qx[i] = __builtin_bit_cast(bf16x8_t, r[HALF + i]);
-    }
+    for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = __builtin_bit_cast(bf16x8_t, r[kk]);
   }
-
-  // K fragment lane offsets (the same for every tile): M tile mt, row
-  // t = 8 (r16 >> 2) + 4 mt + (r16 & 3), logical chunk 4 fh + g of each 128-byte group;
-  // k-step 2 i + fh adds 128 i.
-  int kb[2];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int t = 8 * (r16 >> 2) + 4 * mt + (r16 & 3);
-    kb[mt] = t * ROW_BYTES + 16 * ((4 * fh + g) ^ swz(t));
-  }
-
-  // Partial scores of tile it over this wave's k-steps: so = own block, sx = partner's
-  // block; row r of M tile mt is token 8 (r >> 2) + 4 mt + (r & 3), so lane (g, r16) ends
-  // with tokens 8 g .. 8 g + 7 of head r16 of the block: after the softmax, exactly the
-  // P^T operand of the PV product.  The 18 K fragments stream through a register ring.
-  auto score = [&](int it, f32x4_t (&so)[2], f32x4_t (&sx)[2]) {
-    const lds_char_t* tile = lsm + (it % NBUF) * TILE_BYTES;
-    so[0] = so[1] = sx[0] = sx[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    constexpr int STEPS = 2 * HALF;  // step = 2 i + mt
-    constexpr int KRING = 3;
-    auto k_frag = [&](int step) {
-      return *(const lds_bf16x8_t*)(tile + kb[step & 1] + 128 * (step >> 1));
-    };
-    bf16x8_t ka[KRING];
-#pragma unroll
-    for (int i = 0; i < KRING - 1; ++i) ka[i] = k_frag(i);
-#pragma unroll
-    for (int step = 0; step < STEPS; ++step) {
-      if (step + KRING - 1 < STEPS) ka[(step + KRING - 1) % KRING] = k_frag(step + KRING - 1);
-      const int mt = step & 1, i = step >> 1;
-      so[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step % KRING], qo[i], so[mt], 0, 0, 0);
-      sx[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step % KRING], qx[i], sx[mt], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
 
   // O^T accumulators: o[ct][hb2] lane (g, r16) holds O[16 hb2 + r16][64 w + 16 ct + 4 g + i]
   f32x4_t o[4][8];
@@ -276,13 +237,36 @@ __global__ __launch_bounds__(NW * 64) void attn_cols_kernel(
 
   // PV of tile it for this wave's 64 columns and all 8 head blocks.  V^T fragments (A
   // operand): lane (gg, rr) holds column 64 w + 16 ct + rr, tokens 8 gg .. 8 gg + 7,
-  // gathered by two transposing reads of 4 rows each (column tile 4 w + ct sits in chunks
-  // 8 w + 2 ct, + 1; the row swizzle moves only the low three chunk bits).
-  auto pv = [&](int it) {
-    const lds_char_t* tile = lsm + (it % NBUF) * TILE_BYTES + 128 * w;
+  // gathered by two transposing reads of 4 rows each from column block w.  Once they are
+  // in registers the block is free, and with `copies` set this wave's copies of tile it+3
+  // (the next tile of this buffer, rows from base3) go out between the MFMAs.
+  auto pv = [&](int it, bool copies, const char* base3) {
+    const lds_char_t* blk = lsm + (it % NBUF) * TILE_BYTES + w * BLOCK_BYTES;
     int ln = lane;
     asm volatile("" : "+v"(ln));  // recomputed per tile (no long live ranges)
     const int gg = ln >> 4, rr = ln & 15;
+    // Copy r of block w fills rows 8 r + x (x = lane >> 3) of the block, and since
+    // swz(8 r + x) = swz(x) ^ 2 r its source chunk is 8 w + (cx ^ 2 r), cx = (lane & 7) ^ swz(x);
+    // the RoPE quarter (waves 0..3) is rows 8 w + x, chunk 64 + (cx ^ 2 w).
+    const unsigned cx = static_cast<unsigned>((ln & 7) ^ swz(ln >> 3));
+    const unsigned xr = static_cast<unsigned>(ln >> 3);
+    const unsigned last3 = static_cast<unsigned>(j1 - 1 - (j0 + (it + 3) * TILE));
+    const uint32_t dst3 = smem_lds + ((it + 3) % NBUF) * TILE_BYTES;
+    auto copy = [&](int r) {
+      if (r < 4)
+        dma16(base3, __umul24(min(8u * r + xr, last3), static_cast<unsigned>(ROW_BYTES)) +
+                         16u * (8u * w + (cx ^ (2u * r))),
+              dst3 + (4 * w + r) * 1024);
+      else
+        dma16(base3, __umul24(min(8u * w + xr, last3), static_cast<unsigned>(ROW_BYTES)) +
+                         16u * (64u + (cx ^ (2u * w))),
+              dst3 + (32 + w) * 1024);
+    };
+    // P^T fragments of the 8 head blocks, 1 KB each, lane-contiguous
+    const lds_char_t* pb = lsm + PBUF + (it & 1) * 8192 + 16 * ln;
+    constexpr int PRING = 2;
+    bf16x8_t pf[PRING];
+    pf[0] = *(const lds_bf16x8_t*)(pb);
     bf16x8_t va[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -292,35 +276,74 @@ __global__ __launch_bounds__(NW * 64) void attn_cols_kernel(
         const int t = 8 * gg + 4 * r + (rr >> 2);
         const int e = (rr & 3) >> 1;
         half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(tile + t * ROW_BYTES + 16 * ((2 * ct + e) ^ swz(t)) + 8 * (rr & 1)));
+            (lds_i16x4_t*)(blk + t * 128 + 16 * ((2 * ct + e) ^ swz(t)) + 8 * (rr & 1)));
       }
       va[ct] = __builtin_bit_cast(bf16x8_t,
                                   __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
     }
-    // P^T fragments of the 8 head blocks, 1 KB each, lane-contiguous
-    const lds_char_t* pb = lsm + PBUF + 16 * ln;
-    constexpr int PRING = 2;
-    bf16x8_t pf[PRING];
-    pf[0] = *(const lds_bf16x8_t*)(pb);
+    // the V reads have returned before any copy may overwrite their block
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int h2 = 0; h2 < 8; ++h2) {
       if (h2 + 1 < 8) pf[(h2 + 1) % PRING] = *(const lds_bf16x8_t*)(pb + 1024 * (h2 + 1));
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+      for (int ct = 0; ct < 4; ++ct) {
         o[ct][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ct], pf[h2 % PRING], o[ct][h2], 0, 0, 0);
+        if (ct == 1 && h2 < 5) {  // a copy between two MFMAs runs in their shadow
+          __builtin_amdgcn_sched_barrier(0);
+          if (copies && h2 < ncopies) copy(h2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Reference maximum of head 16 hb + r16 (log2 units, same in its 4 lanes): the first
-  // tile's maximum plus HEADROOM, fixed for the split.  The denominators accumulate on the
-  // matrix core as ones (16 x 32) * P^T (32 x 16): every entry of lane (g, r16) holds the
-  // sum of head 16 hb + r16, exactly over the bf16 weights the PV product consumes.
+  // Reference maximum of head 16 w + r16 (log2 units, same in its 4 lanes): the first
+  // tile's maximum plus HEADROOM, fixed for the split.  Lane (g, r16) sums the bf16-rounded
+  // weights it hands to the PV product (tokens 8 g .. 8 g + 7 of every tile); the four
+  // lanes of a head are added at the end.
   float m_ref = -INFINITY;
-  f32x4_t l_acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float l_part = 0.f;
   bool out_of_range = false;  // sticky: a score of this head block left the reference range
 
-  // softmax of tile it on the full scores of the own block; stores its P^T fragment
+  // Scores of tile it for head block w (S^T: 2 token M tiles x 16 heads, k over 576; row r
+  // of M tile mt is token 8 (r >> 2) + 4 mt + (r & 3), so lane (g, r16) ends with tokens
+  // 8 g .. 8 g + 7 of head r16: after the softmax, exactly its P^T fragment).  The 36 K
+  // fragments stream through a register ring.
+  auto score = [&](int it, f32x4_t (&sacc)[2]) {
+    const lds_char_t* tile = lsm + (it % NBUF) * TILE_BYTES;
+    sacc[0] = sacc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // K fragment lane offsets: M tile mt, row t = 8 (r16 >> 2) + 4 mt + (r16 & 3), logical
+    // chunk 4 (kk & 1) + g of column block kk >> 1 (recomputed per tile: no long live ranges)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    int kb[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int t = 8 * ((ln & 15) >> 2) + 4 * mt + (ln & 3);
+#pragma unroll
+      for (int par = 0; par < 2; ++par) kb[mt][par] = chunk_offset(t, 4 * par + (ln >> 4));
+    }
+    constexpr int STEPS = 2 * KSTEPS;  // step = 2 kk + mt
+    constexpr int KRING = 3;
+    auto k_frag = [&](int step) {
+      const int kk = step >> 1, mt = step & 1;
+      return *(const lds_bf16x8_t*)(tile + kb[mt][kk & 1] + BLOCK_BYTES * (kk >> 1));
+    };
+    bf16x8_t ka[KRING];
+#pragma unroll
+    for (int i = 0; i < KRING - 1; ++i) ka[i] = k_frag(i);
+#pragma unroll
+    for (int step = 0; step < STEPS; ++step) {
+      if (step + KRING - 1 < STEPS) ka[(step + KRING - 1) % KRING] = k_frag(step + KRING - 1);
+      const int kk = step >> 1, mt = step & 1;
+      sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step % KRING], qf[kk], sacc[mt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // softmax of tile it on the scores of the own block; stores its P^T fragment
   auto softmax = [&](int it, const f32x4_t (&so)[2]) {
     const int tb = j0 + it * TILE;
     f32x4_t sc[2] = {so[0], so[1]};
@@ -360,37 +383,60 @@ __global__ __launch_bounds__(NW * 64) void attn_cols_kernel(
     const bf16x8_t pt = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
                                                 __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
                                                 0, 1, 2, 3, 4, 5, 6, 7);
-    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, i16x4x2_ones());
-    l_acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pt, l_acc, 0, 0, 0);
-    *(lds_bf16x8_t*)(lsm + PBUF + hb * 1024 + 16 * lane) = pt;
+    *(lds_bf16x8_t*)(lsm + PBUF + (it & 1) * 8192 + w * 1024 + 16 * lane) = pt;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) l_part += static_cast<float>(pt[i]);
   };
 
-  publish_barrier();  // A(0): tile 0 and the tables
-  for (int it = 0; it < ntiles; ++it) {
-    if (it > 0) pv(it - 1);
-    f32x4_t so[2], sx[2];
-    score(it, so, sx);
-    *(lds_f32x4_t*)(lsm + XCH + w * 2048 + 16 * lane) = sx[0];
-    *(lds_f32x4_t*)(lsm + XCH + w * 2048 + 1024 + 16 * lane) = sx[1];
-    const int page2 = it + 2 < ntiles ? split_page(j0 + (it + 2) * TILE) : 0;  // read ahead
-    publish_barrier();  // B(it)
-    if (it + 2 < ntiles) issue_tile(it + 2, page2);
-    {
-      const lds_char_t* xp = lsm + XCH + (w ^ 4) * 2048 + 16 * lane;
-      so[0] += *(const lds_f32x4_t*)(xp);
-      so[1] += *(const lds_f32x4_t*)(xp + 1024);
-    }
-    softmax(it, so);
+  // Phase it (between barriers A(it) and A(it+1)): PV(it-1) (which refills the wave's part
+  // of buffer (it-1) % 3 with tile it+2), the scores and softmax of tile it, in the
+  // wave group's order.  Tile 2 has no PV before it, so phase 0 requests it up front.
+  publish_barrier();  // A(0): tile 0 and the page table
+  if (ntiles > 2) {
+    const char* base2 = page_base(split_page(j0 + 2 * TILE), j0 + 2 * TILE);
+    for (int r = 0; r < ncopies; ++r) issue_copy(base2, 2, r);
+  }
+  // The two orders run as two separate loops: with the branch outside the tile loop each
+  // loop body is straight-line code, which the register allocator fits in 256 VGPRs.
+  auto phase_end = [&](int it, bool copies) {
     if (it == ntiles - 1) {  // the block's denominators and range flag for the epilogue
       const bool block_out = __any(out_of_range);  // a vote of the whole wavefront
-      if (g == 0) ((lds_f32_t*)(lsm + STATS))[16 * hb + r16] = l_acc[0];
-      if (lane == 0) ((lds_i32_t*)(lsm + STATS + 512))[hb] = block_out ? 1 : 0;
+      l_part += __shfl_xor(l_part, 16, 64);
+      l_part += __shfl_xor(l_part, 32, 64);
+      if (g == 0) ((lds_f32_t*)(lsm + STATS))[16 * w + r16] = l_part;
+      if (lane == 0) ((lds_i32_t*)(lsm + STATS + 512))[w] = block_out ? 1 : 0;
     }
-    if (it + 2 < ntiles) wait_vmcnt<COPIES>();  // own copies of tile it+1 landed
-    else wait_vmcnt<0>();
+    // own copies of tile it+1 landed (those of tile it+2 may still be in flight)
+    if (copies) {
+      if (w < 4) wait_vmcnt<5>();
+      else wait_vmcnt<4>();
+    } else {
+      wait_vmcnt<0>();
+    }
     publish_barrier();  // A(it+1)
+  };
+  if (w < 4) {  // PV first
+    for (int it = 0; it < ntiles; ++it) {
+      const bool copies = it + 2 < ntiles;  // tile it+2 is (being) requested in this phase
+      const int tb2 = j0 + (it + 2) * TILE;
+      if (it > 0) pv(it - 1, copies, page_base(copies ? split_page(tb2) : page0, tb2));
+      f32x4_t sacc[2];
+      score(it, sacc);
+      softmax(it, sacc);
+      phase_end(it, copies);
+    }
+  } else {      // scores first
+    for (int it = 0; it < ntiles; ++it) {
+      const bool copies = it + 2 < ntiles;
+      const int tb2 = j0 + (it + 2) * TILE;
+      f32x4_t sacc[2];
+      score(it, sacc);
+      softmax(it, sacc);
+      if (it > 0) pv(it - 1, copies, page_base(copies ? split_page(tb2) : page0, tb2));
+      phase_end(it, copies);
+    }
   }
-  pv(ntiles - 1);
+  pv(ntiles - 1, false, nullptr);
 
   // ---- epilogue: normalise and write this wave's 64 columns of every head; the lse of the
   //      own block; a block whose scores left the reference range is recomputed exactly
@@ -430,12 +476,12 @@ __global__ __launch_bounds__(NW * 64) void attn_cols_kernel(
       }
     }
   }
-  if (!(flags & (1 << hb))) {
+  if (!(flags & (1 << w))) {
     if (lse_part != nullptr && g == 0)
-      lse_part[(static_cast<int64_t>(bq) * NH + 16 * hb + r16) * S + s] = (m_ref + __log2f(l_acc[0])) * LN2;
+      lse_part[(static_cast<int64_t>(bq) * NH + 16 * w + r16) * S + s] = (m_ref + __log2f(l_part)) * LN2;
   } else {
     split_exact_fallback(q_lat, q_pe, cache, bt_row, log2P, j0, j1, bq, NH, S, s, scale_log2,
-                         o_part, lse_part, 16 * hb, 16, lane);
+                         o_part, lse_part, 16 * w, 16, lane);
   }
 }
 

@@ -42,6 +42,7 @@
 // are filled from the last valid token of the split, so no memory outside the referenced
 // pages is read and P = 0 meets finite values.
 #include "attn_common.h"
+#include "combine_row.h"
 #include "launchers.h"
 
 #include <cstdlib>
@@ -61,6 +62,58 @@ static_assert(LDS_BYTES <= 163840, "LDS per workgroup");
 constexpr float HEADROOM = 32.0f;  // log2 units between a split's first-tile max and its reference
 constexpr float P_RANGE = 64.0f;   // a score this far above the reference takes the fallback
 
+// In-launch merge of the S splits of query row bq, after this workgroup (split s) wrote
+// its partial: the workgroup counts its arrival in merge_cnt[2 bq], waits until all S
+// splits of the row have arrived, then combines heads s, s + S, s + 2 S, ... of the row
+// (one wavefront per head, combine_row.h) into out / lse_out.  The second counter
+// merge_cnt[2 bq + 1] counts the workgroups past the wait; the last one clears both, so
+// the counters are zero again for the next launch.  Workgroups wait for each other here,
+// so the launcher only asks for the merge when the whole grid is resident at once; the
+// wait is bounded all the same, and a wait that runs out sets *merge_err.
+constexpr int MERGE_SPIN_LIMIT = 1 << 20;
+
+template <int NW, typename OT>
+__device__ void merge_splits(const OT* __restrict__ o_part, const float* __restrict__ lse_part,
+                             int H, int S, int s, int bq, int* __restrict__ merge_cnt,
+                             int* __restrict__ merge_err, float* __restrict__ out,
+                             float* __restrict__ lse_out, int tid) {
+  int* const arrived = merge_cnt + 2 * bq;
+  int* const passed = arrived + 1;
+  // Each wavefront waits for its partial stores to complete (reach L2), then the barrier
+  // orders them all before thread 0's device-scope release.  That fence (an L2 write-back)
+  // and the acquire after the wait (an L2 and L1 invalidate) are cache-wide, so one thread
+  // issues each for the whole workgroup: the same fences issued by every wavefront cost
+  // about as much again as the attention.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_fetch_add(arrived, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int n = 0;
+    // polled without acquire (an acquire per poll would invalidate the caches every time)
+    while (__hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < S) {
+      if (++n == MERGE_SPIN_LIMIT) {
+        __hip_atomic_store(merge_err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  const int lane = tid & 63, w = tid >> 6;
+  for (int h = s + S * w; h < H; h += S * NW) {
+    const int64_t row = static_cast<int64_t>(bq) * H + h;
+    combine512_wave(o_part + row * S * DC, lse_part + row * S, S, out + row * DC,
+                    lse_out != nullptr ? lse_out + row : nullptr, lane);
+  }
+  if (tid == 0 &&
+      __hip_atomic_fetch_add(passed, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1) {
+    __hip_atomic_store(arrived, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(passed, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // NW wavefronts, H = 16 * NW heads; wave w owns heads h0 = 16 w .. h0 + 15 for both
 // products, so a wave's softmax weights never leave its registers:
 //   scores: S^T = K_tile (32 x 576) * Q^T (576 x 16), Q resident in VGPRs for the split;
@@ -75,7 +128,9 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     const bf16raw* __restrict__ q_lat, const bf16raw* __restrict__ q_pe,
     const bf16raw* __restrict__ cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int H, int log2P, int max_pages, int pages_per_split,
-    int S, float scale_log2, OT* __restrict__ o_part, float* __restrict__ lse_part, int n_q) {
+    int S, float scale_log2, OT* __restrict__ o_part, float* __restrict__ lse_part, int n_q,
+    int* __restrict__ merge_cnt, int* __restrict__ merge_err, float* __restrict__ out,
+    float* __restrict__ lse_out) {
   constexpr int NT = NW * 64;
   constexpr int NCT = DC / 16;                                    // PV column tiles
   constexpr int STEPS = KSTEPS * 2;                               // score MFMA steps per tile
@@ -112,6 +167,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     }
     if (lse_part != nullptr)
       for (int h = tid; h < H; h += NT) lse_part[(static_cast<int64_t>(bq) * H + h) * S + s] = -INFINITY;
+    if (merge_cnt != nullptr)
+      merge_splits<NW>(o_part, lse_part, H, S, s, bq, merge_cnt, merge_err, out, lse_out, tid);
     return;
   }
 
@@ -465,6 +522,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     split_exact_fallback(q_lat, q_pe, cache, bt_row, log2P, j0, j1, bq, H, S, s, scale_log2,
                          o_part, lse_part, h0, 16, lane);
   }
+  if (merge_cnt != nullptr)
+    merge_splits<NW>(o_part, lse_part, H, S, s, bq, merge_cnt, merge_err, out, lse_out, tid);
 }
 
 template <int NW, typename OT>
@@ -475,7 +534,9 @@ hipError_t launch_nw_t(const PagedArgs& a, hipStream_t st) {
                      static_cast<const bf16raw*>(a.cache), a.block_table, a.seq_lens, a.H,
                      __builtin_ctz(static_cast<unsigned>(a.page_size)), a.max_pages,
                      a.pages_per_split, a.num_splits, a.scale * log2e,
-                     static_cast<OT*>(a.o_part), a.lse_part, a.n_q);
+                     static_cast<OT*>(a.o_part), a.lse_part, a.n_q, a.merge_cnt,
+                     a.merge_cnt != nullptr ? a.merge_cnt + 2 * a.B * a.n_q : nullptr, a.out,
+                     a.lse_out);
   return hipGetLastError();
 }
 
@@ -495,6 +556,23 @@ bool attn_mfma_supported(const PagedArgs& a) {
   return a.d_c == DC && a.d_R == DR && heads_ok && page_ok &&
          a.B <= 65535 && a.n_q >= 1 && a.n_q <= 65535 && aligned16(a.q_lat) &&
          aligned16(a.q_pe) && aligned16(a.cache);
+}
+
+bool attn_mfma_grid_resident(const PagedArgs& a) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return false;
+  hipError_t e = hipErrorInvalidValue;
+  switch (a.H) {
+    case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_kernel<1, float>, 64, 0); break;
+    case 32: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_kernel<2, float>, 128, 0); break;
+    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_kernel<4, float>, 256, 0); break;
+    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_mfma_kernel<8, float>, 512, 0); break;
+    default: break;
+  }
+  if (e != hipSuccess) return false;
+  return static_cast<int64_t>(a.B) * a.num_splits * a.n_q <= static_cast<int64_t>(cus) * per_cu;
 }
 
 hipError_t launch_attn_mfma_bf16_512_64(const PagedArgs& a, hipStream_t s) {

@@ -11,6 +11,7 @@
 // that XCD's L2.  Each thread owns 4 consecutive latent columns
 // (one 16-byte load per split for fp32 partials, 8 bytes for bf16), the weights live in
 // LDS.  Deterministic: fixed summation order, no atomics.
+#include "combine_row.h"
 #include "device_common.h"
 #include "launchers.h"
 
@@ -84,31 +85,7 @@ __global__ __launch_bounds__(kCombineThreads) void splitk_combine_kernel(
   if (tid == 0 && lse_out != nullptr) lse_out[bh] = den > 0.f ? msafe + logf(den) : -INFINITY;
 }
 
-// d_c = 512, at most 64 splits: one wavefront per (sequence, head), lane l owns columns
-// 8 l .. 8 l + 7 (one 16-byte load per split for bf16 partials), lane s holds split s's lse
-// and weight.  Every load of a chunk of 8 splits goes out before anything waits (split
-// indices past S re-read split S - 1 and get weight 0, so the loads carry no branch that
-// would make each wait for its own data), and the weights reach the lanes by readlane.
-template <typename PT> struct Part8;
-template <> struct Part8<bf16raw> {
-  uint4 u;
-  __device__ __forceinline__ void load(const bf16raw* p) {
-    u = *reinterpret_cast<const uint4*>(p);
-  }
-  __device__ __forceinline__ float at(int i) const {
-    const unsigned w = (i >> 1) == 0 ? u.x : (i >> 1) == 1 ? u.y : (i >> 1) == 2 ? u.z : u.w;
-    return (i & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
-  }
-};
-template <> struct Part8<float> {
-  f32x4_t a, b;
-  __device__ __forceinline__ void load(const float* p) {
-    a = *reinterpret_cast<const f32x4_t*>(p);
-    b = *reinterpret_cast<const f32x4_t*>(p + 4);
-  }
-  __device__ __forceinline__ float at(int i) const { return i < 4 ? a[i] : b[i - 4]; }
-};
-
+// d_c = 512, at most 64 splits: one wavefront per (sequence, head) (combine_row.h).
 template <typename PT>
 __global__ __launch_bounds__(256) void combine512_kernel(
     const PT* __restrict__ o_part, const float* __restrict__ lse_part, int B, int H, int S,
@@ -117,39 +94,9 @@ __global__ __launch_bounds__(256) void combine512_kernel(
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= B * H) return;
   const int bh = (item % B) * H + item / B;  // sequence-fastest, as in splitk_combine_kernel
-  const float xraw = lse_part[static_cast<int64_t>(bh) * S + min(lane, S - 1)];
-  const PT* base = o_part + static_cast<int64_t>(bh) * S * 512 + 8 * lane;
-  Part8<PT> v[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j].load(base + static_cast<int64_t>(min(j, S - 1)) * 512);
-  __builtin_amdgcn_sched_barrier(0);
-
-  const float x = lane < S ? xraw : -INFINITY;
-  const float m = wave_max(x);
-  const float msafe = (m == -INFINITY) ? 0.f : m;
-  const float wl = (x == -INFINITY) ? 0.f : expf(x - msafe);  // 0 for lanes >= S
-  const float den = wave_sum(wl);
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0;;) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float w = __builtin_bit_cast(
-          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s0 + j));
-#pragma unroll
-      for (int i = 0; i < 8; ++i)  // an empty split adds exactly 0 (and no NaN)
-        acc[i] = fmaf(w, w != 0.f ? v[j].at(i) : 0.f, acc[i]);
-    }
-    s0 += 8;
-    if (s0 >= S) break;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      v[j].load(base + static_cast<int64_t>(min(s0 + j, S - 1)) * 512);
-  }
-  float* dst = out + static_cast<int64_t>(bh) * 512 + 8 * lane;
-  *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-  *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
-  if (lane == 0 && lse_out != nullptr) lse_out[bh] = den > 0.f ? msafe + logf(den) : -INFINITY;
+  combine512_wave(o_part + static_cast<int64_t>(bh) * S * 512, lse_part + static_cast<int64_t>(bh) * S,
+                  S, out + static_cast<int64_t>(bh) * 512, lse_out != nullptr ? lse_out + bh : nullptr,
+                  lane);
 }
 
 hipError_t launch_splitk_combine(const void* o_part, int part_bf16, const float* lse_part, int B,

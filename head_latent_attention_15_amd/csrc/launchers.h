@@ -22,6 +22,12 @@ struct PagedArgs {
   int part_bf16;     // 1: o_part elements are bf16 (round to nearest even)
   float* lse_part;
   int32_t n_q;       // query tokens per sequence (rows b n_q + t of q and of the partials)
+  // In-launch merge of the splits (attn_mfma only; merge_cnt NULL = none): two counters per
+  // query row (zero on entry, left zero), then one error word; out [rows][H][d_c] fp32 and
+  // lse_out [rows][H] (or NULL) receive the combined result.
+  int* merge_cnt = nullptr;
+  float* out = nullptr;
+  float* lse_out = nullptr;
 };
 
 // Decode attention, one wavefront per (sequence, head, split), fp32 VALU math.
@@ -30,6 +36,9 @@ hipError_t launch_attn_generic_bf16_512_64(const PagedArgs& a, hipStream_t s);
 // Decode attention on bf16 MFMA, all heads of a (sequence, split) per workgroup.
 hipError_t launch_attn_mfma_bf16_512_64(const PagedArgs& a, hipStream_t s);
 bool attn_mfma_supported(const PagedArgs& a);
+// Whole grid of the head-partitioned kernel resident at once on the current device (the
+// condition for its in-launch merge, whose workgroups wait for each other).
+bool attn_mfma_grid_resident(const PagedArgs& a);
 // The same product for 128 heads with the latent product partitioned by columns across the
 // wavefronts (each LDS fragment read feeds several MFMAs).
 hipError_t launch_attn_cols_bf16_512_64(const PagedArgs& a, hipStream_t s);

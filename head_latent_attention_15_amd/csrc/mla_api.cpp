@@ -133,13 +133,23 @@ int32_t mla_suggest_num_splits(int32_t B, int32_t max_seq_len, int64_t total_tok
   return static_cast<int32_t>(S);
 }
 
-// Decode attention for n_q query tokens per sequence (1 for plain decode).
+// Where the combined result of a decode that also merges its splits goes.
+struct MergeReq {
+  int32_t* counters;  // 2 per query row + 1 error word, zero on entry, left zero
+  float* out;
+  float* lse_out;
+};
+
+// Decode attention for n_q query tokens per sequence (1 for plain decode).  With `merge`
+// (num_splits > 1) the split partials are also combined into merge->out: inside the
+// attention launch when the head-partitioned kernel runs with its whole grid resident,
+// else by the combine kernel right after it.
 static mla_status_t decode_attn(const void* q_lat, const void* q_pe, const void* kv_cache,
                              const int32_t* block_table, const int32_t* seq_lens,
                              const mla_paged_shape_t* shape, float softmax_scale,
                              int32_t num_splits, void* o_part, mla_dtype_t part_dtype,
                              float* lse_part, mla_dtype_t dtype, int32_t n_q, int32_t kernel,
-                             void* stream) {
+                             void* stream, const MergeReq* merge = nullptr) {
   if (!q_lat || !q_pe || !kv_cache || !block_table || !seq_lens || !o_part)
     return fail(MLA_ERR_NULL, "mla_decode_attn: a required pointer is NULL");
   mla_status_t st = check_paged_shape(shape);
@@ -181,17 +191,32 @@ static mla_status_t decode_attn(const void* q_lat, const void* q_pe, const void*
   if (kernel < 0 || kernel > 3) return fail(MLA_ERR_UNSUPPORTED, "attention kernel %d unknown", kernel);
   if (dtype == MLA_BF16 && a.d_c == 512 && a.d_R == 64 && a.H <= 128) {
     const bool cols = mla::attn_cols_supported(a), heads = mla::attn_mfma_supported(a);
-    if (kernel == 0) kernel = cols ? 2 : heads ? 1 : 3;
+    if (kernel == 0) kernel = heads ? 1 : cols ? 2 : 3;
     if (kernel == 2 && !cols)
       return fail(MLA_ERR_UNSUPPORTED, "attention kernel 2 needs H = 128, pages of >= 32 tokens "
                   "(a power of two), <= 1024 pages per split and 16-byte aligned tensors");
     if (kernel == 1 && !heads)
       return fail(MLA_ERR_UNSUPPORTED, "attention kernel 1 needs H in {16, 32, 64, 128}, pages of "
                   ">= 32 tokens (a power of two), <= 1024 pages per split, aligned tensors");
-    if (kernel == 2) return launched(mla::launch_attn_cols_bf16_512_64(a, s), "attention (bf16 MFMA, column-partitioned)");
-    if (kernel == 1) return launched(mla::launch_attn_mfma_bf16_512_64(a, s), "attention (bf16 MFMA)");
-    return launched(mla::launch_attn_generic_bf16_512_64(a, s), "attention (bf16 generic)");
+    const bool merging = merge != nullptr && num_splits > 1;
+    if (merging && kernel == 1 && num_splits <= 64 && mla::attn_mfma_grid_resident(a)) {
+      a.merge_cnt = merge->counters;
+      a.out = merge->out;
+      a.lse_out = merge->lse_out;
+      return launched(mla::launch_attn_mfma_bf16_512_64(a, s), "attention (bf16 MFMA, merged splits)");
+    }
+    mla_status_t st2;
+    if (kernel == 2) st2 = launched(mla::launch_attn_cols_bf16_512_64(a, s), "attention (bf16 MFMA, column-partitioned)");
+    else if (kernel == 1) st2 = launched(mla::launch_attn_mfma_bf16_512_64(a, s), "attention (bf16 MFMA)");
+    else st2 = launched(mla::launch_attn_generic_bf16_512_64(a, s), "attention (bf16 generic)");
+    if (st2 != MLA_OK || !merging) return st2;
+    return launched(mla::launch_splitk_combine(o_part, part_dtype == MLA_BF16, lse_part,
+                                               a.B * n_q, a.H, num_splits, a.d_c, merge->out,
+                                               merge->lse_out, s),
+                    "split-K combine");
   }
+  if (merge != nullptr)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_fused: d_latent 512, d_rope 64, BF16 only");
   if (kernel == 1 || kernel == 2)
     return fail(MLA_ERR_UNSUPPORTED, "attention kernels 1 and 2 need d_latent 512, d_rope 64, BF16");
   if (dtype == MLA_F32 && a.d_c == 64 && a.d_R == 16 && a.H <= 64)
@@ -229,6 +254,46 @@ mla_status_t mla_decode_attn_multi(const void* q_lat, const void* q_pe, const vo
                                    void* stream) {
   return decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, shape, softmax_scale,
                      num_splits, o_part, part_dtype, lse_part, dtype, n_q, 0, stream);
+}
+
+mla_status_t mla_decode_fused(const void* q_lat, const void* q_pe, const void* kv_cache,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              const mla_paged_shape_t* shape, int32_t n_q, float softmax_scale,
+                              int32_t num_splits, void* o_part, mla_dtype_t part_dtype,
+                              float* lse_part, int32_t* counters, float* out, float* lse_out,
+                              mla_dtype_t dtype, void* stream) {
+  if (!out) return fail(MLA_ERR_NULL, "mla_decode_fused: out is NULL");
+  if (num_splits == 1)  // nothing to merge: the attention writes out directly
+    return decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, shape, softmax_scale, 1,
+                       out, MLA_F32, lse_out, dtype, n_q, 0, stream);
+  if (!counters) return fail(MLA_ERR_NULL, "mla_decode_fused: counters is NULL");
+  if (((reinterpret_cast<uintptr_t>(o_part) | reinterpret_cast<uintptr_t>(out)) & 15) != 0)
+    return fail(MLA_ERR_SHAPE, "mla_decode_fused: o_part and out must be 16-byte aligned");
+  if (num_splits > 64)
+    return fail(MLA_ERR_SHAPE, "mla_decode_fused: num_splits %d > 64", num_splits);
+  const MergeReq m{counters, out, lse_out};
+  return decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, shape, softmax_scale,
+                     num_splits, o_part, part_dtype, lse_part, dtype, n_q, 0, stream, &m);
+}
+
+int32_t mla_decode_fused_single_launch(const mla_paged_shape_t* shape, int32_t n_q,
+                                       int32_t num_splits) {
+  if (shape == nullptr || check_paged_shape(shape) != MLA_OK) return 0;
+  if (num_splits < 2 || num_splits > 64 || n_q < 1) return 0;
+  mla::PagedArgs a{};
+  a.B = shape->batch;
+  a.H = shape->num_heads;
+  a.d_c = shape->d_latent;
+  a.d_R = shape->d_rope;
+  a.page_size = shape->page_size;
+  a.max_pages = shape->max_pages_per_seq;
+  a.num_pages = shape->num_pages;
+  a.num_splits = num_splits;
+  a.pages_per_split = pages_per_split(shape->max_pages_per_seq, num_splits);
+  a.n_q = n_q;
+  // stand-in aligned pointers: the alignment rule is stated for the caller's tensors
+  a.q_lat = a.q_pe = a.cache = reinterpret_cast<const void*>(static_cast<uintptr_t>(256));
+  return mla::attn_mfma_supported(a) && mla::attn_mfma_grid_resident(a) ? 1 : 0;
 }
 
 mla_status_t mla_splitk_combine(const void* o_part, mla_dtype_t part_dtype,

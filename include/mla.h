@@ -245,6 +245,42 @@ mla_status_t mla_combine_out_proj(const void* o_part, mla_dtype_t part_dtype,
                                   int32_t d_c, const void* w_uv, mla_dtype_t w_dtype, int32_t d_h,
                                   float* o_heads, void* stream);
 
+/* Decode attention and split-K combine in one launch.  The workgroups of a query row merge
+ * its splits themselves once all of them have written their partials (workgroup s combines
+ * heads s, s + S, s + 2S, ... with the combine's per-row arithmetic), so no combine kernel
+ * and no second launch follow.  The splits are exact pieces of one softmax whose
+ * denominator is a sum over the tokens (qiita.com/joule/items/57d9b3f4fc27959eaa0d,
+ * "Attention 計算"), as for mla_splitk_combine.
+ * The in-launch merge needs the head-partitioned MFMA kernel (d_latent 512, d_rope 64,
+ * BF16, H in {16, 32, 64, 128}) with its whole grid (B * n_q * num_splits workgroups)
+ * resident on the device at once, since its workgroups wait for each other; otherwise the
+ * call runs the attention and then mla_splitk_combine's kernel on the same stream.  Either
+ * way out / lse_out hold the same bits as mla_decode_attn_multi + mla_splitk_combine with
+ * the same num_splits and partial dtype.
+ *   q_lat .. n_q, softmax_scale, num_splits, dtype: as mla_decode_attn_multi (BF16 only)
+ *   o_part     [B n_q][H][S][d_latent] part_dtype, lse_part [B n_q][H][S] fp32: scratch the
+ *              call overwrites (unused when num_splits == 1); 16-byte aligned
+ *   counters   int32 [2 B n_q + 1], caller-owned, ZERO before the first call; every call
+ *              leaves the first 2 B n_q words zero again.  The last word is an error flag:
+ *              set to 1 if a merge wait ran out (only possible when other work kept part of
+ *              the grid off the device for about a second); the call's out is then invalid.
+ *   out        [B n_q][H][d_latent] fp32 (16-byte aligned); lse_out [B n_q][H] or NULL
+ * Calls that share `counters` must not overlap (one stream, or caller-serialised).
+ * Errors: as mla_decode_attn_multi, plus NULL (out, or counters with num_splits > 1),
+ * SHAPE (num_splits > 64, misaligned o_part / out). */
+mla_status_t mla_decode_fused(const void* q_lat, const void* q_pe, const void* kv_cache,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              const mla_paged_shape_t* shape, int32_t n_q, float softmax_scale,
+                              int32_t num_splits, void* o_part, mla_dtype_t part_dtype,
+                              float* lse_part, int32_t* counters, float* out, float* lse_out,
+                              mla_dtype_t dtype, void* stream);
+
+/* 1 if mla_decode_fused with this shape, n_q and num_splits (and 16-byte aligned BF16
+ * tensors) merges its splits inside the attention launch on the current device, 0 if it
+ * runs the attention and the combine kernel (or the arguments are invalid).  Host-only. */
+int32_t mla_decode_fused_single_launch(const mla_paged_shape_t* shape, int32_t n_q,
+                                       int32_t num_splits);
+
 /* mla_decode_attn followed by mla_splitk_combine, with the split partials in a caller
  * workspace of at least mla_decode_workspace_bytes(B, H, d_latent, num_splits) bytes
  * (unused when num_splits == 1); the partials take the cache dtype (BF16 caches: bf16
