@@ -340,12 +340,14 @@ def multi_token_rows(mla, W, torch, caches, bt, sl, scale, num_cus, n_q: int = 2
             "tflops": round(flops / (us * 1e-6) / 1e12, 1)}
 
 
-def config_row(mla, torch, inp, name, num_cus, steps, n_copies, kernel="auto"):
-    """One attention workload beside the headline: the whole step (attention + combine, bf16
-    partials), the attention alone and mla_decode_fused (one launch that merges its splits
-    when the grid fits the device at once), back to back over n_copies rotating caches, with
-    algorithmic bytes (cache rows of every sequence, queries, tables; the combined output
-    for the step) and the fraction of the 8 TB/s HBM roofline."""
+def config_row(mla, torch, inp, name, num_cus, steps, n_copies, kernel="auto", flattened=False):
+    """One attention workload beside the headline, back to back over n_copies rotating
+    caches: the split-grid step (attention + combine, bf16 partials), its attention alone,
+    mla_decode_fused (one launch that merges its splits, when the grid fits the device at
+    once) and mla_decode_ragged (the flattened work list: one equal page range per compute
+    unit, then the combine).  us_per_step is the flattened list's when `flattened`, else the
+    split grid's.  Algorithmic bytes: cache rows of every sequence, queries, tables, and the
+    combined output for the step; fractions of the 8 TB/s HBM roofline."""
     dev = torch.device("cuda:0")
     B, H, d_c = inp["q_lat"].shape
     sl = inp["seq_lens"]
@@ -374,9 +376,19 @@ def config_row(mla, torch, inp, name, num_cus, steps, n_copies, kernel="auto"):
         k += 1
         if k % 32 == 0:
             torch.cuda.synchronize()
-    step_ms = timed_ms(torch, lambda k: (calls[k % n_copies](), combine()), steps)
+    split_ms = timed_ms(torch, lambda k: (calls[k % n_copies](), combine()), steps)
     attn_ms = timed_ms(torch, lambda k: calls[k % n_copies](), steps)
     fused_ms = timed_ms(torch, lambda k: fused[k % n_copies](), steps)
+    # the flattened work list: one equal page range per compute unit
+    ws = torch.empty(mla.mla_decode_ragged_workspace_bytes(caches[0], bt, H, d_c), dtype=torch.uint8,
+                     device=dev)
+    flat = [mla.bind(mla.mla_decode_ragged, q_lat, q_pe, c, bt, sld, inp["scale"], ws, out, lse)
+            for c in caches]
+    for k in range(2 * n_copies):
+        flat[k % n_copies]()
+    torch.cuda.synchronize()
+    flat_ms = timed_ms(torch, lambda k: flat[k % n_copies](), steps)
+    step_ms = flat_ms if flattened else split_ms
     tokens = int(sl.sum())
     attn_bytes = tokens * ROW_BYTES + B * H * 576 * 2 + bt.numel() * 4 + B * 4
     step_bytes = attn_bytes + B * H * 512 * 4
@@ -384,7 +396,10 @@ def config_row(mla, torch, inp, name, num_cus, steps, n_copies, kernel="auto"):
                                                      1, S))
     del caches
     return {"workload": name, "B": B, "H": H, "tokens": tokens, "num_splits": S,
+            "path": "mla_decode_ragged (flattened work list)" if flattened
+                    else "mla_decode (split grid: attention + combine)",
             "us_per_step": round(step_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
+            "us_split_grid": round(split_ms * 1e3, 2), "us_flattened": round(flat_ms * 1e3, 2),
             "us_one_launch_merge": round(fused_ms * 1e3, 2) if single else None,
             "cache_GBps_step": round(tokens * ROW_BYTES / (step_ms * 1e-3) / 1e9, 1),
             "step_frac": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -614,7 +629,7 @@ def main():
         result["long_b4_t32k"] = config_row(mla, torch, W.long_b4_t32k(), "long_b4_t32k", num_cus,
                                             args.steps, N_CACHE_COPIES)
         result["ragged_b128"] = config_row(mla, torch, W.ragged_b128(), "ragged_b128", num_cus,
-                                           args.steps, 2)
+                                           args.steps, 2, flattened=True)
     log("timing multi-token decode (2 query tokens per sequence)")
     caches = [inp["cache"].to(dev)]
     for _ in range(N_CACHE_COPIES - 1):

@@ -66,6 +66,8 @@ _SIGNATURES = {
     "mla_decode_fused": (_I32, [_P, _P, _P, _P, _P, _SP, _I32, _F, _I32, _P, _I32, _P, _P, _P,
                                 _P, _I32, _P]),
     "mla_decode_fused_single_launch": (_I32, [_SP, _I32, _I32]),
+    "mla_decode_ragged_workspace_bytes": (_SZ, [_SP]),
+    "mla_decode_ragged": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _P, _SZ, _P, _P, _I32, _P]),
     "mla_splitk_combine": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "mla_combine_out_proj": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _I32, _I32, _P,
                                     _P]),
@@ -481,6 +483,37 @@ def mla_decode_fused_single_launch(shape, n_q, num_splits) -> int:
     """1 if mla_decode_fused merges inside the attention launch for this paged shape
     (paged_shape(...)), n_q and split count on the current device; else 0."""
     return int(lib.mla_decode_fused_single_launch(ctypes.byref(shape), int(n_q), int(num_splits)))
+
+
+def mla_decode_ragged_workspace_bytes(kv_cache, block_table, num_heads, d_latent) -> int:
+    """Workspace bytes of mla_decode_ragged for this cache pool and batch."""
+    return int(lib.mla_decode_ragged_workspace_bytes(
+        ctypes.byref(paged_shape(kv_cache, block_table, num_heads, d_latent))))
+
+
+def mla_decode_ragged(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale, workspace,
+                      out, lse_out=None, stream=None):
+    """Decode of a ragged batch over the flattened work list: out [B,H,d_c] fp32; workspace a
+    uint8 tensor of >= mla_decode_ragged_workspace_bytes(kv_cache, block_table, H, d_c)
+    bytes."""
+    torch = _torch()
+    B, H, d_c = q_lat.shape
+    _expect(tuple(q_pe.shape[:-1]) == (B, H), "q_pe must be [B,H,d_R]")
+    _expect(q_pe.dtype == q_lat.dtype == kv_cache.dtype, "q_lat, q_pe, kv_cache share a dtype")
+    _expect(kv_cache.shape[2] == d_c + q_pe.shape[-1], "cache row must be d_c + d_R wide")
+    _expect(block_table.shape[0] == B and tuple(seq_lens.shape) == (B,), "batch mismatch")
+    _expect(tuple(out.shape) == (B, H, d_c), "out must be [B,H,d_c]")
+    if lse_out is not None:
+        _expect(tuple(lse_out.shape) == (B, H), "lse_out must be [B,H]")
+    _expect(workspace.dtype == torch.uint8, "workspace must be a uint8 tensor")
+    shp = paged_shape(kv_cache, block_table, H, d_c)
+    _invoke("mla_decode_ragged",
+        _dev(q_lat, "q_lat"), _dev(q_pe, "q_pe"),
+        _dev(kv_cache, "kv_cache", None, 3), _dev(block_table, "block_table", torch.int32, 2),
+        _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), float(softmax_scale),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _dev(out, "out", torch.float32, 3), _dev(lse_out, "lse_out", torch.float32, 2),
+        _dtype_code(q_lat), _stream(stream))
 
 
 def mla_splitk_combine(o_part, lse_part, out, lse_out=None, stream=None):

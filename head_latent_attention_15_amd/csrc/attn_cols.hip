@@ -480,7 +480,8 @@ __global__ __launch_bounds__(NW * 64) void attn_cols_kernel(
     if (lse_part != nullptr && g == 0)
       lse_part[(static_cast<int64_t>(bq) * NH + 16 * w + r16) * S + s] = (m_ref + __log2f(l_part)) * LN2;
   } else {
-    split_exact_fallback(q_lat, q_pe, cache, bt_row, log2P, j0, j1, bq, NH, S, s, scale_log2,
+    split_exact_fallback(q_lat, q_pe, cache, bt_row, log2P, j0, j1, bq, NH,
+                         static_cast<int64_t>(bq) * NH * S + s, S, scale_log2,
                          o_part, lse_part, 16 * w, 16, lane);
   }
 }

@@ -108,14 +108,15 @@ __device__ __forceinline__ i32x4_t i16x4x2_ones() {
 // reading the rows straight from the paged cache.  One wavefront handles n_heads heads
 // starting at h_begin; lane l owns features 9l .. 9l+8 of the score and latent columns
 // l + 64k.
+// The partial of head h goes to row prow0 + h * hstride of o_part / lse_part.
 template <typename OT>
 __device__ void split_exact_fallback(const bf16raw* __restrict__ q_lat,
                                      const bf16raw* __restrict__ q_pe,
                                      const bf16raw* __restrict__ cache, const int32_t* bt_row,
                                      int log2P, int j0, int j1, int bq, int H,
-                                     int S, int s, float scale_log2, OT* __restrict__ o_part,
-                                     float* __restrict__ lse_part, int h_begin, int n_heads,
-                                     int lane) {
+                                     int64_t prow0, int hstride, float scale_log2,
+                                     OT* __restrict__ o_part, float* __restrict__ lse_part,
+                                     int h_begin, int n_heads, int lane) {
   const int P = 1 << log2P;
   for (int h = h_begin; h < h_begin + n_heads; ++h) {
     float q[9];
@@ -143,7 +144,7 @@ __device__ void split_exact_fallback(const bf16raw* __restrict__ q_lat,
       for (int k = 0; k < 8; ++k) acc[k] = acc[k] * alpha + p * bf16_to_f32(row[lane + 64 * k]);
       m = mn;
     }
-    const int64_t ob = (static_cast<int64_t>(bq) * H + h) * S + s;
+    const int64_t ob = prow0 + static_cast<int64_t>(h) * hstride;
 #pragma unroll
     for (int k = 0; k < 8; ++k) st(o_part + ob * DC + lane + 64 * k, acc[k] / l);
     if (lane == 0 && lse_part != nullptr) lse_part[ob] = (m + __log2f(l)) * LN2;

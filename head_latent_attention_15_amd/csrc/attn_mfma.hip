@@ -123,14 +123,16 @@ __device__ void merge_splits(const OT* __restrict__ o_part, const float* __restr
 // it-2, whose buffer then receives the copies of tile it+2.  Between barriers the waves run
 // free, so the two waves sharing a SIMD overlap one's softmax arithmetic with the other's
 // matrix-core work.
+//
+// attn_split runs this for tokens j0 .. j1-1 of sequence b with the queries of row bq and
+// writes the split's partial of head h to row prow0 + h * hstride of o_part / lse_part;
+// every thread of the workgroup calls it with the same arguments.
 template <int NW, typename OT>
-__global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
+__device__ __forceinline__ void attn_split(
     const bf16raw* __restrict__ q_lat, const bf16raw* __restrict__ q_pe,
-    const bf16raw* __restrict__ cache, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ seq_lens, int H, int log2P, int max_pages, int pages_per_split,
-    int S, float scale_log2, OT* __restrict__ o_part, float* __restrict__ lse_part, int n_q,
-    int* __restrict__ merge_cnt, int* __restrict__ merge_err, float* __restrict__ out,
-    float* __restrict__ lse_out) {
+    const bf16raw* __restrict__ cache, const int32_t* __restrict__ block_table, int H,
+    int log2P, int max_pages, float scale_log2, OT* __restrict__ o_part,
+    float* __restrict__ lse_part, int b, int bq, int j0, int j1, int64_t prow0, int hstride) {
   constexpr int NT = NW * 64;
   constexpr int NCT = DC / 16;                                    // PV column tiles
   constexpr int STEPS = KSTEPS * 2;                               // score MFMA steps per tile
@@ -142,33 +144,24 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   lds_char_t* const lsm = (lds_char_t*)smem;  // 32-bit LDS addressing for the tile reads
   const uint32_t smem_lds = static_cast<uint32_t>(reinterpret_cast<size_t>(lsm));
 
-  // Consecutive workgroup ids go to the 8 XCDs in turn; with the sequence index in x, all
-  // splits of a sequence (ids b, b + B, ...) land on XCD b % 8 when B % 8 == 0, so the
-  // sequence's queries are fetched once into that XCD's L2.
-  // Several query tokens per sequence (n_q > 1): token t = blockIdx.z sits at position
-  // seq_len - n_q + t and sees the cache up to it; its queries and outputs are row
-  // bq = b n_q + t.  Its workgroups share the sequence's XCD and read the same tiles.
-  const int b = blockIdx.x, s = blockIdx.y, bq = b * n_q + blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63;
+  // the thread index is made opaque here, so that when this runs in a loop over pieces
+  // nothing derived from it is hoisted out of the loop and kept live across the pieces
+  int tid_opaque = threadIdx.x;
+  asm volatile("" : "+v"(tid_opaque));
+  const int tid = tid_opaque, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int P = 1 << log2P;
   const int h0 = 16 * w;   // heads of this wave
   const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_pages;
 
-  const int L = seq_lens[b] - (n_q - 1 - static_cast<int>(blockIdx.z));
-  const int j0 = s * pages_per_split * P;
-  const int j1 = min(L, j0 + pages_per_split * P);
-
   if (j0 >= j1) {  // empty split: o = 0, lse = -inf
     for (int e = tid; e < H * DC; e += NT) {
       const int h = e / DC, c = e % DC;
-      st(o_part + ((static_cast<int64_t>(bq) * H + h) * S + s) * DC + c, 0.f);
+      st(o_part + (prow0 + static_cast<int64_t>(h) * hstride) * DC + c, 0.f);
     }
     if (lse_part != nullptr)
-      for (int h = tid; h < H; h += NT) lse_part[(static_cast<int64_t>(bq) * H + h) * S + s] = -INFINITY;
-    if (merge_cnt != nullptr)
-      merge_splits<NW>(o_part, lse_part, H, S, s, bq, merge_cnt, merge_err, out, lse_out, tid);
+      for (int h = tid; h < H; h += NT) lse_part[prow0 + static_cast<int64_t>(h) * hstride] = -INFINITY;
     return;
   }
 
@@ -489,7 +482,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   // ---- epilogue: normalise and write four consecutive columns per lane; a head block
   //      whose scores left the reference range is recomputed exactly
   if (!__any(out_of_range)) {
-    const int64_t row = (static_cast<int64_t>(bq) * H + h0 + r16) * S + s;
+    const int64_t row = prow0 + static_cast<int64_t>(h0 + r16) * hstride;
     if (lse_part != nullptr && g == 0) lse_part[row] = (m_ref + __log2f(l_acc[0])) * LN2;
     const float inv = 1.f / l_acc[0];
     if constexpr (std::is_same<OT, float>::value) {
@@ -519,11 +512,244 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
       }
     }
   } else {
-    split_exact_fallback(q_lat, q_pe, cache, bt_row, log2P, j0, j1, bq, H, S, s, scale_log2,
-                         o_part, lse_part, h0, 16, lane);
+    split_exact_fallback(q_lat, q_pe, cache, bt_row, log2P, j0, j1, bq, H, prow0, hstride,
+                         scale_log2, o_part, lse_part, h0, 16, lane);
   }
+}
+
+// One workgroup per (sequence, split) (blockIdx.x, blockIdx.y), and per query token
+// (blockIdx.z) when n_q > 1.  Consecutive workgroup ids go to the 8 XCDs in turn; with the
+// sequence index in x, all splits of a sequence (ids b, b + B, ...) land on XCD b % 8 when
+// B % 8 == 0, so the sequence's queries are fetched once into that XCD's L2.  Token t of n_q
+// sits at position seq_len - n_q + t and sees the cache up to it; its queries and outputs are
+// row bq = b n_q + t, and its workgroups share the sequence's XCD and read the same tiles.
+template <int NW, typename OT>
+__global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
+    const bf16raw* __restrict__ q_lat, const bf16raw* __restrict__ q_pe,
+    const bf16raw* __restrict__ cache, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, int H, int log2P, int max_pages, int pages_per_split,
+    int S, float scale_log2, OT* __restrict__ o_part, float* __restrict__ lse_part, int n_q,
+    int* __restrict__ merge_cnt, int* __restrict__ merge_err, float* __restrict__ out,
+    float* __restrict__ lse_out) {
+  const int b = blockIdx.x, s = blockIdx.y, bq = b * n_q + blockIdx.z;
+  const int L = seq_lens[b] - (n_q - 1 - static_cast<int>(blockIdx.z));
+  const int j0 = s * (pages_per_split << log2P);
+  const int j1 = min(L, j0 + (pages_per_split << log2P));
+  attn_split<NW, OT>(q_lat, q_pe, cache, block_table, H, log2P, max_pages, scale_log2, o_part,
+                     lse_part, b, bq, j0, j1, static_cast<int64_t>(bq) * H * S + s, S);
   if (merge_cnt != nullptr)
-    merge_splits<NW>(o_part, lse_part, H, S, s, bq, merge_cnt, merge_err, out, lse_out, tid);
+    merge_splits<NW>(o_part, lse_part, H, S, s, bq, merge_cnt, merge_err, out, lse_out,
+                     static_cast<int>(threadIdx.x));
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// exclusive prefix sum over the 64 lanes
+__device__ __forceinline__ int wave_excl_scan_i(int v, int lane) {
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x - v;
+}
+
+// Flattened work list for ragged batches (one query token per sequence).  The cached pages
+// of all sequences, concatenated in sequence order (tot pages), are cut into gridDim.x
+// ranges of W = ceil(tot / gridDim.x) pages, widened to ceil(max_b pages_b / 63) if that
+// cut left some sequence in more than 64 ranges; range r goes to one workgroup, which runs attn_split
+// on each piece of a sequence inside it.  Every workgroup is busy for the same number of
+// pages (but the last), whatever the mix of lengths, and no workgroup is launched empty.
+// Sequence b is cut into count_b pieces (ranges floor(off_b / W) ..
+// floor((off_b + pages_b - 1) / W)); with first_b the number of pieces of the sequences
+// before b (at most gridDim.x + B pieces in all), the partial of head h from piece i is row
+// first_b H + h count_b + i of o_part [.][512] / lse_part: a sequence's pieces of one head
+// are consecutive rows, as the splits in the split-grid layout.  Each
+// workgroup computes this plan from seq_lens with wave scans (every wave alike, so the loop
+// over pieces is uniform); range 0's workgroup also writes (first_b, count_b) to seq_slots
+// for the combine.  Workgroup ids go to the 8 XCDs in turn, so range r = (id % 8)(G / 8) +
+// id / 8 gives each XCD a contiguous eighth of the tokens: a sequence's pieces and its
+// queries mostly share one L2.
+// Piece k (0-based, in sequence order) of range r = [lo, hi) under range width W, or
+// false past the range's last piece.  A piece is the part of one sequence inside the range:
+// sequence b, tokens j0 .. j1-1, and its partials' place (the sequence's first piece over
+// the whole batch, its piece count, and this piece's index among them).  A fresh scan over
+// seq_lens for every piece keeps no per-lane state alive across the pieces, whose split
+// body needs nearly every register.
+struct Piece {
+  int b, j0, j1, first, count, index;
+};
+
+__device__ __forceinline__ bool ragged_piece(const int32_t* __restrict__ seq_lens, int B,
+                                             int log2P, int W, int r, int lo, int hi, int k,
+                                             Piece* pc) {
+  const int lane = threadIdx.x & 63;
+  const int P = 1 << log2P;
+  int off_run = 0, first_run = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int bb = base + lane;
+    const int len = bb < B ? seq_lens[bb] : 0;
+    const int pg = (len + P - 1) >> log2P;
+    const int off = off_run + wave_excl_scan_i(pg, lane);
+    const int cnt = pg > 0 ? (off + pg - 1) / W - off / W + 1 : 0;
+    const bool in = cnt > 0 && off < hi && off + pg > lo;
+    const uint64_t mask = __ballot(in);
+    const int n = __builtin_popcountll(mask);
+    if (k < n) {
+      const int first = first_run + wave_excl_scan_i(cnt, lane);
+      // the k-th lane of the mask: the one with k mask lanes below it
+      const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
+      const int l = __builtin_ctzll(__ballot(in && below == k));
+      const int off_b = __builtin_amdgcn_readlane(off, l);
+      const int pg_b = __builtin_amdgcn_readlane(pg, l);
+      const int p0 = max(off_b, lo) - off_b, p1 = min(off_b + pg_b, hi) - off_b;
+      // (integer division runs on the vector unit: readfirstlane keeps the fields scalar)
+      pc->b = base + l;
+      pc->j0 = p0 << log2P;
+      pc->j1 = min(__builtin_amdgcn_readlane(len, l), p1 << log2P);
+      pc->first = __builtin_amdgcn_readlane(first, l);
+      pc->count = __builtin_amdgcn_readlane(cnt, l);
+      pc->index = __builtin_amdgcn_readfirstlane(r - off_b / W);
+      return true;
+    }
+    k -= n;
+    off_run = __builtin_amdgcn_readfirstlane(off_run + wave_sum_i(pg));
+    first_run = __builtin_amdgcn_readfirstlane(first_run + wave_sum_i(cnt));
+  }
+  return false;
+}
+
+// Flattened work list for ragged batches (one query token per sequence).  The cached pages
+// of all sequences, concatenated in sequence order (tot pages), are cut into gridDim.x
+// ranges of W = ceil(tot / gridDim.x) pages, widened to ceil(max_b pages_b / 63) if that
+// cut left some sequence in more than 64 ranges; range r goes to one workgroup, which runs
+// attn_split on each piece of a sequence inside it.  Every workgroup is busy for the same
+// number of pages (but the last), whatever the mix of lengths, and none is launched empty.
+// Sequence b is cut into count_b pieces (ranges floor(off_b / W) ..
+// floor((off_b + pages_b - 1) / W)); with first_b the number of pieces of the sequences
+// before b (at most gridDim.x + B pieces in all), the partial of head h from piece i is row
+// first_b H + h count_b + i of o_part [.][512] / lse_part: a sequence's pieces of one head
+// are consecutive rows, as the splits in the split-grid layout.  Each workgroup computes
+// the plan from seq_lens with wave scans (every wave alike, so the loop over pieces is
+// uniform); range 0's workgroup also writes (first_b, count_b) to seq_slots for the
+// combine.  Workgroup ids go to the 8 XCDs in turn, so range r = (id % 8)(G / 8) + id / 8
+// gives each XCD a contiguous eighth of the tokens: a sequence's pieces and its queries
+// mostly share one L2.
+template <int NW, typename OT>
+__global__ __launch_bounds__(NW * 64) void attn_mfma_ragged_kernel(
+    const bf16raw* __restrict__ q_lat, const bf16raw* __restrict__ q_pe,
+    const bf16raw* __restrict__ cache, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, int B, int H, int log2P, int max_pages,
+    float scale_log2, OT* __restrict__ o_part, float* __restrict__ lse_part,
+    int* __restrict__ seq_slots, int* __restrict__ err) {
+  const int G = gridDim.x, id = blockIdx.x;
+  const int r = __builtin_amdgcn_readfirstlane((G % 8 == 0) ? (id % 8) * (G / 8) + id / 8 : id);
+  const int lane = threadIdx.x & 63;
+  const int P = 1 << log2P;
+  int tot = 0, mx = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int bb = base + lane;
+    const int pg = bb < B ? (seq_lens[bb] + P - 1) >> log2P : 0;
+    tot += wave_sum_i(pg);
+    mx = max(mx, wave_max_i(pg));
+  }
+  tot = __builtin_amdgcn_readfirstlane(tot);
+  mx = __builtin_amdgcn_readfirstlane(mx);
+  // the even split, unless it cuts some sequence into more than 64 pieces (then a width of
+  // ceil(max pages / 63) bounds every count by 64)
+  int W = __builtin_amdgcn_readfirstlane(max((tot + G - 1) / G, 1));
+  {
+    int off_run = 0, most = 0;
+    for (int base = 0; base < B; base += 64) {
+      const int bb = base + lane;
+      const int pg = bb < B ? (seq_lens[bb] + P - 1) >> log2P : 0;
+      const int off = off_run + wave_excl_scan_i(pg, lane);
+      most = max(most, wave_max_i(pg > 0 ? (off + pg - 1) / W - off / W + 1 : 0));
+      off_run = __builtin_amdgcn_readfirstlane(off_run + wave_sum_i(pg));
+    }
+    if (__builtin_amdgcn_readfirstlane(most) > 64)
+      W = __builtin_amdgcn_readfirstlane(max(W, (mx + 62) / 63));
+  }
+  const bool too_long = W > MAX_SPLIT_PAGES;  // a range's block-table entries must fit LDS
+  if (r == 0 && threadIdx.x < 64) {
+    int off_run = 0, first_run = 0;
+    for (int base = 0; base < B; base += 64) {
+      const int bb = base + lane;
+      const int pg = bb < B ? (seq_lens[bb] + P - 1) >> log2P : 0;
+      const int off = off_run + wave_excl_scan_i(pg, lane);
+      const int cnt = pg > 0 && !too_long ? (off + pg - 1) / W - off / W + 1 : 0;
+      if (bb < B) {
+        seq_slots[2 * bb] = first_run + wave_excl_scan_i(cnt, lane);
+        seq_slots[2 * bb + 1] = cnt;
+      } else {
+        wave_excl_scan_i(cnt, lane);  // every lane takes part in the shuffles
+      }
+      off_run = __builtin_amdgcn_readfirstlane(off_run + wave_sum_i(pg));
+      first_run = __builtin_amdgcn_readfirstlane(first_run + wave_sum_i(cnt));
+    }
+    if (threadIdx.x == 0) *err = too_long ? 1 : 0;
+  }
+  if (too_long) return;
+  // The plan's scalars wait in LDS between pieces: kept in registers across the split body
+  // they push it over the register file (scratch spills inside the tile loop).
+  __shared__ int plan[2];
+  if (threadIdx.x == 0) {
+    plan[0] = W;
+    plan[1] = tot;
+  }
+  __syncthreads();
+  for (int k = 0;; ++k) {
+    const int Wk = __builtin_amdgcn_readfirstlane(
+        *static_cast<volatile __attribute__((address_space(3))) int*>(
+            (__attribute__((address_space(3))) int*)plan));
+    const int tk = __builtin_amdgcn_readfirstlane(
+        *static_cast<volatile __attribute__((address_space(3))) int*>(
+            (__attribute__((address_space(3))) int*)plan + 1));
+    const int rk = __builtin_amdgcn_readfirstlane(
+        (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x);
+    const int lo = rk * Wk, hi = min(lo + Wk, tk);
+    Piece pc;
+    if (!ragged_piece(seq_lens, B, log2P, Wk, rk, lo, hi, k, &pc)) break;
+    // The previous piece's partial stores leave the vector-memory counter (the prologue's
+    // explicit waits count only its own loads and copies), and its last LDS reads are done
+    // before this piece's copies overwrite the buffers.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    attn_split<NW, OT>(q_lat, q_pe, cache, block_table, H, log2P, max_pages, scale_log2,
+                       o_part, lse_part, pc.b, pc.b, pc.j0, pc.j1,
+                       static_cast<int64_t>(pc.first) * H + pc.index, pc.count);
+  }
+}
+
+template <int NW, typename OT>
+hipError_t launch_ragged_nw_t(const PagedArgs& a, int grid, int* seq_slots, int* err,
+                              hipStream_t st) {
+  const float log2e = 1.4426950408889634f;
+  hipLaunchKernelGGL((attn_mfma_ragged_kernel<NW, OT>), dim3(grid), dim3(NW * 64), 0, st,
+                     static_cast<const bf16raw*>(a.q_lat), static_cast<const bf16raw*>(a.q_pe),
+                     static_cast<const bf16raw*>(a.cache), a.block_table, a.seq_lens, a.B, a.H,
+                     __builtin_ctz(static_cast<unsigned>(a.page_size)), a.max_pages,
+                     a.scale * log2e, static_cast<OT*>(a.o_part), a.lse_part, seq_slots, err);
+  return hipGetLastError();
+}
+
+template <int NW>
+hipError_t launch_ragged_nw(const PagedArgs& a, int grid, int* seq_slots, int* err,
+                            hipStream_t st) {
+  return a.part_bf16 ? launch_ragged_nw_t<NW, bf16raw>(a, grid, seq_slots, err, st)
+                     : launch_ragged_nw_t<NW, float>(a, grid, seq_slots, err, st);
 }
 
 template <int NW, typename OT>
@@ -573,6 +799,19 @@ bool attn_mfma_grid_resident(const PagedArgs& a) {
   }
   if (e != hipSuccess) return false;
   return static_cast<int64_t>(a.B) * a.num_splits * a.n_q <= static_cast<int64_t>(cus) * per_cu;
+}
+
+int attn_mfma_ragged_max_range_pages() { return MAX_SPLIT_PAGES; }
+
+hipError_t launch_attn_mfma_ragged(const PagedArgs& a, int grid, int* seq_slots, int* err,
+                                   hipStream_t s) {
+  switch (a.H) {
+    case 16: return launch_ragged_nw<1>(a, grid, seq_slots, err, s);
+    case 32: return launch_ragged_nw<2>(a, grid, seq_slots, err, s);
+    case 64: return launch_ragged_nw<4>(a, grid, seq_slots, err, s);
+    case 128: return launch_ragged_nw<8>(a, grid, seq_slots, err, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_attn_mfma_bf16_512_64(const PagedArgs& a, hipStream_t s) {

@@ -99,6 +99,46 @@ __global__ __launch_bounds__(256) void combine512_kernel(
                   lane);
 }
 
+// Combine for the flattened work list of ragged batches: the count_b <= 64 partials of
+// sequence b, head h are rows first_b H + h count_b + i (i < count_b) of o_part [.][512] /
+// lse_part, with (first_b, count_b) = (seq_slots[2b], seq_slots[2b + 1]).  One wavefront
+// per (sequence, head); a sequence without tokens gets o = 0, lse = -inf.
+template <typename PT>
+__global__ __launch_bounds__(256) void combine512_slots_kernel(
+    const PT* __restrict__ o_part, const float* __restrict__ lse_part,
+    const int* __restrict__ seq_slots, int B, int H, float* __restrict__ out,
+    float* __restrict__ lse_out) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= B * H) return;
+  const int b = item / H, h = item % H;
+  const int first = seq_slots[2 * b], count = seq_slots[2 * b + 1];
+  if (count == 0) {
+    float* dst = out + static_cast<int64_t>(item) * 512 + 8 * lane;
+    *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (lane == 0 && lse_out != nullptr) lse_out[item] = -INFINITY;
+    return;
+  }
+  const int64_t row0 = static_cast<int64_t>(first) * H + static_cast<int64_t>(h) * count;
+  combine512_wave(o_part + row0 * 512, lse_part + row0, count,
+                  out + static_cast<int64_t>(item) * 512,
+                  lse_out != nullptr ? lse_out + item : nullptr, lane);
+}
+
+hipError_t launch_combine_slots(const void* o_part, int part_bf16, const float* lse_part,
+                                const int* seq_slots, int B, int H, float* out, float* lse_out,
+                                hipStream_t st) {
+  const int items = B * H;
+  if (part_bf16)
+    hipLaunchKernelGGL(combine512_slots_kernel<bf16raw>, dim3((items + 3) / 4), dim3(256), 0, st,
+                       static_cast<const bf16raw*>(o_part), lse_part, seq_slots, B, H, out, lse_out);
+  else
+    hipLaunchKernelGGL(combine512_slots_kernel<float>, dim3((items + 3) / 4), dim3(256), 0, st,
+                       static_cast<const float*>(o_part), lse_part, seq_slots, B, H, out, lse_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_splitk_combine(const void* o_part, int part_bf16, const float* lse_part, int B,
                                  int H, int S, int d_c, float* out, float* lse_out, hipStream_t st) {
   const bool aligned = ((reinterpret_cast<uintptr_t>(o_part) | reinterpret_cast<uintptr_t>(out)) & 15) == 0;

@@ -35,8 +35,9 @@ template <> struct Part8<float> {
   __device__ __forceinline__ float at(int i) const { return i < 4 ? a[i] : b[i - 4]; }
 };
 
-// part: the row's partials [S][512] (16-byte aligned); lse: its S lses; out: 512 fp32
-// (16-byte aligned); lse_out: one float or NULL.  1 <= S <= 64.  Lane l owns columns
+// part: the row's S partials of 512 values, part_stride elements apart (16-byte aligned);
+// lse: its S lses, lse_stride apart; out: 512 fp32 (16-byte aligned); lse_out: one float or
+// NULL.  1 <= S <= 64.  Lane l owns columns
 // 8 l .. 8 l + 7 (one 16-byte load per split for bf16 partials), lane s holds split s's lse
 // and weight.  Every load of a chunk of 8 splits goes out before anything waits (split
 // indices past S re-read split S - 1 and get weight 0, so the loads carry no branch that
@@ -45,12 +46,13 @@ template <typename PT>
 __device__ __forceinline__ void combine512_wave(const PT* __restrict__ part,
                                                 const float* __restrict__ lse, int S,
                                                 float* __restrict__ out,
-                                                float* __restrict__ lse_out, int lane) {
-  const float xraw = lse[min(lane, S - 1)];
+                                                float* __restrict__ lse_out, int lane,
+                                                int64_t part_stride = 512, int lse_stride = 1) {
+  const float xraw = lse[static_cast<int64_t>(min(lane, S - 1)) * lse_stride];
   const PT* base = part + 8 * lane;
   Part8<PT> v[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j].load(base + static_cast<int64_t>(min(j, S - 1)) * 512);
+  for (int j = 0; j < 8; ++j) v[j].load(base + min(j, S - 1) * part_stride);
   __builtin_amdgcn_sched_barrier(0);
 
   const float x = lane < S ? xraw : -INFINITY;
@@ -72,7 +74,7 @@ __device__ __forceinline__ void combine512_wave(const PT* __restrict__ part,
     s0 += 8;
     if (s0 >= S) break;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j].load(base + static_cast<int64_t>(min(s0 + j, S - 1)) * 512);
+    for (int j = 0; j < 8; ++j) v[j].load(base + min(s0 + j, S - 1) * part_stride);
   }
   float* dst = out + 8 * lane;
   *reinterpret_cast<cr_f32x4_t*>(dst) = cr_f32x4_t{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};

@@ -54,6 +54,20 @@ hipError_t launch_combine_uv(const void* o_part, int part_bf16, const float* lse
 
 hipError_t launch_splitk_combine(const void* o_part, int part_bf16, const float* lse_part, int B,
                                  int H, int S, int d_c, float* out, float* lse_out, hipStream_t s);
+// Combine of the flattened work list's partials (d_c = 512): with (first, count) =
+// (seq_slots[2b], seq_slots[2b + 1]), head h of sequence b has rows first H + h count + i,
+// i < count, of o_part [.][512] and lse_part.
+hipError_t launch_combine_slots(const void* o_part, int part_bf16, const float* lse_part,
+                                const int* seq_slots, int B, int H, float* out, float* lse_out,
+                                hipStream_t s);
+// Decode attention of a ragged batch over the flattened work list (n_q = 1): `grid`
+// workgroups each take an equal page range of the batch's concatenated cached pages;
+// room for (grid + B) H partial rows of 512 (o_part, part_bf16) and lse values (lse_part);
+// seq_slots [2B] receives (first piece, piece count) per sequence; *err is set to 1 (and
+// every count to 0) when a range would exceed 1024 pages, else to 0.
+hipError_t launch_attn_mfma_ragged(const PagedArgs& a, int grid, int* seq_slots, int* err,
+                                   hipStream_t s);
+int attn_mfma_ragged_max_range_pages();
 
 // Batched small-M GEMM: y[z][m][n] = sum_k x[z][m][k] * W_z(n, k), with
 // W_z(n, k) = w[z*sw + n*ldw + k] when w_nk, else w[z*sw + k*ldw + n].

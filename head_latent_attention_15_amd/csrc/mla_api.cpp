@@ -2,6 +2,7 @@
 // Every check runs before any HIP call, so a rejected call touches no device state.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -294,6 +295,96 @@ int32_t mla_decode_fused_single_launch(const mla_paged_shape_t* shape, int32_t n
   // stand-in aligned pointers: the alignment rule is stated for the caller's tensors
   a.q_lat = a.q_pe = a.cache = reinterpret_cast<const void*>(static_cast<uintptr_t>(256));
   return mla::attn_mfma_supported(a) && mla::attn_mfma_grid_resident(a) ? 1 : 0;
+}
+
+// Workgroups of the flattened ragged launch: one per compute unit of the current device,
+// or more when the pool holds over 1024 pages per compute unit (a workgroup's range of
+// pages must fit its LDS block table).
+static int ragged_grid(int32_t num_pages) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  const int per = mla::attn_mfma_ragged_max_range_pages();
+  return std::max(cus, (num_pages + per - 1) / per);
+}
+
+struct RaggedLayout {
+  size_t slots_off, lse_off, part_off, total;
+};
+
+static RaggedLayout ragged_layout(int32_t B, int32_t H, int32_t d_c, int grid) {
+  RaggedLayout l;
+  const size_t slots = static_cast<size_t>(grid) + B;
+  l.slots_off = 0;
+  l.lse_off = align256((2 * static_cast<size_t>(B) + 1) * sizeof(int32_t));
+  l.part_off = l.lse_off + align256(slots * H * sizeof(float));
+  l.total = l.part_off + align256(slots * H * d_c * sizeof(uint16_t));
+  return l;
+}
+
+size_t mla_decode_ragged_workspace_bytes(const mla_paged_shape_t* shape) {
+  if (shape == nullptr || shape->batch < 1 || shape->num_heads < 1 || shape->d_latent < 1 ||
+      shape->num_pages < 1)
+    return 0;
+  return ragged_layout(shape->batch, shape->num_heads, shape->d_latent,
+                       ragged_grid(shape->num_pages)).total;
+}
+
+mla_status_t mla_decode_ragged(const void* q_lat, const void* q_pe, const void* kv_cache,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               const mla_paged_shape_t* shape, float softmax_scale,
+                               void* workspace, size_t workspace_bytes, float* out,
+                               float* lse_out, mla_dtype_t dtype, void* stream) {
+  if (!q_lat || !q_pe || !kv_cache || !block_table || !seq_lens || !out)
+    return fail(MLA_ERR_NULL, "mla_decode_ragged: a required pointer is NULL");
+  mla_status_t st = check_paged_shape(shape);
+  if (st != MLA_OK) return st;
+  if (!std::isfinite(softmax_scale))
+    return fail(MLA_ERR_SHAPE, "mla_decode_ragged: softmax_scale is not finite");
+  mla::PagedArgs a{};
+  a.q_lat = q_lat;
+  a.q_pe = q_pe;
+  a.cache = kv_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.B = shape->batch;
+  a.H = shape->num_heads;
+  a.d_c = shape->d_latent;
+  a.d_R = shape->d_rope;
+  a.page_size = shape->page_size;
+  a.max_pages = shape->max_pages_per_seq;
+  a.num_pages = shape->num_pages;
+  a.scale = softmax_scale;
+  a.num_splits = 1;
+  a.pages_per_split = 1;
+  a.n_q = 1;
+  if (dtype != MLA_BF16 || !mla::attn_mfma_supported(a))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_ragged: needs BF16, d_latent 512, d_rope 64, "
+                "H in {16, 32, 64, 128}, pages of >= 32 tokens (a power of two) and 16-byte "
+                "aligned tensors");
+  if ((reinterpret_cast<uintptr_t>(out) & 15) != 0)
+    return fail(MLA_ERR_SHAPE, "mla_decode_ragged: out is not 16-byte aligned");
+  const int grid = ragged_grid(a.num_pages);
+  const RaggedLayout l = ragged_layout(a.B, a.H, a.d_c, grid);
+  if (workspace == nullptr || workspace_bytes < l.total)
+    return fail(MLA_ERR_WORKSPACE, "mla_decode_ragged: workspace %zu bytes, need %zu",
+                workspace ? workspace_bytes : static_cast<size_t>(0), l.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(MLA_ERR_WORKSPACE, "mla_decode_ragged: workspace is not 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  int32_t* seq_slots = reinterpret_cast<int32_t*>(ws + l.slots_off);
+  a.lse_part = reinterpret_cast<float*>(ws + l.lse_off);
+  a.o_part = ws + l.part_off;
+  a.part_bf16 = 1;
+  hipStream_t s = as_stream(stream);
+  st = launched(mla::launch_attn_mfma_ragged(a, grid, seq_slots, seq_slots + 2 * a.B, s),
+                "attention (flattened ragged work list)");
+  if (st != MLA_OK) return st;
+  return launched(mla::launch_combine_slots(a.o_part, 1, a.lse_part, seq_slots, a.B, a.H, out,
+                                            lse_out, s),
+                  "ragged combine");
 }
 
 mla_status_t mla_splitk_combine(const void* o_part, mla_dtype_t part_dtype,

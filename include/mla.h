@@ -281,6 +281,37 @@ mla_status_t mla_decode_fused(const void* q_lat, const void* q_pe, const void* k
 int32_t mla_decode_fused_single_launch(const mla_paged_shape_t* shape, int32_t n_q,
                                        int32_t num_splits);
 
+/* Bytes of workspace mla_decode_ragged needs for this paged shape (HOST pointer) on the
+ * current device.  Its launch has G = max(compute units, ceil(num_pages / 1024))
+ * workgroups; the workspace holds the per-sequence slot table, then (G + batch) fp32 lse
+ * rows of num_heads and bf16 partials of num_heads x d_latent, each part 256-byte aligned.
+ * Returns 0 for a NULL shape or a size below 1. */
+size_t mla_decode_ragged_workspace_bytes(const mla_paged_shape_t* shape);
+
+/* Decode for ragged batches (one query token per sequence, lengths free, BF16,
+ * d_latent 512, d_rope 64, H in {16, 32, 64, 128}): the same result as mla_decode, with the
+ * work cut for the device instead of per sequence.  The cached pages of the whole batch,
+ * concatenated in sequence order, are divided into one equal range per compute unit, so
+ * every workgroup streams the same number of pages whatever the mix of lengths; a range
+ * writes one bf16 partial per sequence piece inside it, and a combine kernel merges each
+ * sequence's pieces (the softmax denominator is a sum over the tokens:
+ * qiita.com/joule/items/57d9b3f4fc27959eaa0d, "Attention 計算").  The plan is computed on
+ * the device from seq_lens: no host synchronisation, two launches.
+ *   q_lat .. dtype: as mla_decode (n_q = 1)
+ *   workspace  >= mla_decode_ragged_workspace_bytes(shape) bytes, 256-byte aligned,
+ *              overwritten; its int32 word 2B is set to 1 when a workgroup's range would
+ *              exceed 1024 pages (more than 1024 x G cached pages in the batch, which takes
+ *              pages shared between sequences, or one sequence of more than 64 x 1024
+ *              pages); every output is then 0 / -inf.  Otherwise it is set to 0.
+ *   out [B][H][d_latent] fp32 (16-byte aligned); lse_out [B][H] or NULL.
+ * A sequence with seq_len 0 gives o = 0 and lse = -inf.
+ * Errors: NULL, SHAPE, UNSUPPORTED (shape or dtype), WORKSPACE (NULL, too small, misaligned). */
+mla_status_t mla_decode_ragged(const void* q_lat, const void* q_pe, const void* kv_cache,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               const mla_paged_shape_t* shape, float softmax_scale,
+                               void* workspace, size_t workspace_bytes, float* out,
+                               float* lse_out, mla_dtype_t dtype, void* stream);
+
 /* mla_decode_attn followed by mla_splitk_combine, with the split partials in a caller
  * workspace of at least mla_decode_workspace_bytes(B, H, d_latent, num_splits) bytes
  * (unused when num_splits == 1); the partials take the cache dtype (BF16 caches: bf16
