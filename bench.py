@@ -256,13 +256,12 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     chain_us = timed(accumulate_chain)
     unfused_us = timed(accumulate_unfused)
 
-    # the survey's fourth next item, measured only: offline absorption folds W^UK_i^T into
-    # W^UQ_i ([H d_c, d_c^Q], 201 MB of bf16 weights, prepared once here in fp32 and rounded
-    # once), so q~ = W~ c^Q is one projection instead of W^UQ plus the absorption
-    wuk = w["w_uk"].float().view(H, d_h, d_c).transpose(1, 2).contiguous()
-    wuq = w["w_uq"].float().view(H, d_h, d_cq)
-    w_off = torch.bmm(wuk, wuq).to(torch.bfloat16).view(H * d_c, d_cq)
-    del wuk, wuq
+    # Offline folds, measured only, with the weights prepared once by the library outside the
+    # timing.  W~ = W^UK^T W^UQ ([H d_c, d_c^Q], 201 MB of bf16) makes q~ = W~ c^Q one
+    # projection instead of W^UQ plus the absorption; W_fold = W^O W^UV ([d, H d_c], 671 MB)
+    # makes u = W_fold [o~_1; ...] one projection instead of W^UV plus W^O.
+    w_off = torch.empty(H * d_c, d_cq, device="cuda", dtype=torch.bfloat16)
+    mla.mla_fold_uq(w["w_uk"], w["w_uq"], H, w_off)
     q_off = torch.empty(B, H * d_c, **f32)
     off_us = timed(lambda: mla.mla_linear(sep["c_q"], w_off, q_off))
     rt_calls = [mla.bind(mla.mla_linear, sep["c_q"], w["w_uq"], sep["q_c"]),
@@ -270,14 +269,31 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
                          x["rope_base"], q_lat, None)]
     rt_us = timed(lambda: [c() for c in rt_calls])
     off_bytes = nb(w_off) + nb(sep["c_q"]) + nb(q_off)
-    out["next-4 offline absorption (measure only)"] = {
+    out["next-4 offline absorption W^UK^T W^UQ (measure only)"] = {
         "us": round(off_us, 2), "bytes_algorithmic": int(off_bytes),
         "GBps": round(off_bytes / off_us / 1e3, 1),
         "roofline_frac": round(off_bytes / off_us / 1e3 / HBM_PEAK_GBPS, 4),
-        "runtime_absorption_us": round(rt_us, 2),
-        "note": "q~ = (W^UK^T W^UQ) c^Q in one mla_linear; runtime_absorption_us = W^UQ + "
-                "mla_absorb_q on the same input"}
+        "runtime_path_us": round(rt_us, 2),
+        "note": "q~ = (W^UK^T W^UQ) c^Q in one mla_linear (fold by mla_fold_uq); "
+                "runtime_path_us = W^UQ + mla_absorb_q on the same input"}
     del w_off, q_off
+    w_fold = torch.empty(d, H * d_c, device="cuda", dtype=torch.bfloat16)
+    mla.mla_fold_o_uv(w["w_o"], w["w_uv"], H, w_fold)
+    u_fold = torch.empty(B, d, **f32)
+    fold_us = timed(lambda: mla.mla_linear(o_lat.view(B, H * d_c), w_fold, u_fold))
+    rt2 = [mla.bind(mla.mla_out_proj, o_lat, w["w_uv"], None, o_heads),
+           mla.bind(mla.mla_linear, o_heads.view(B, H * d_h), w["w_o"], u)]
+    rt2_us = timed(lambda: [c() for c in rt2])
+    fold_bytes = nb(w_fold) + nb(o_lat) + nb(u_fold)
+    out["next-4 offline fold W^O W^UV (measure only)"] = {
+        "us": round(fold_us, 2), "bytes_algorithmic": int(fold_bytes),
+        "GBps": round(fold_bytes / fold_us / 1e3, 1),
+        "roofline_frac": round(fold_bytes / fold_us / 1e3 / HBM_PEAK_GBPS, 4),
+        "runtime_path_us": round(rt2_us, 2),
+        "note": "u = (W^O W^UV) [o~_1; ...; o~_H] in one mla_linear (fold by mla_fold_o_uv, "
+                "d_c/d_h = 4x the bytes of W^O); runtime_path_us = W^UV (mla_out_proj) + W^O "
+                "on the same combined latent"}
+    del w_fold, u_fold
     res = {"workload": "layer_b64_t2k (d=5120, H=128, d_h=128, d_c=512, d_c^Q=1536, d_R=64, "
                        "B=64, 2048 cached tokens + 1, bf16 weights and cache)",
            "steps": out, "chain_us": round(chain_us, 2), "chain_bytes_algorithmic": int(total_bytes),

@@ -69,6 +69,8 @@ _SIGNATURES = {
     "mla_decode_ragged_workspace_bytes": (_SZ, [_SP]),
     "mla_decode_ragged": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _P, _SZ, _P, _P, _I32, _P]),
     "mla_splitk_combine": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    "mla_fold_uq": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P]),
+    "mla_fold_o_uv": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P]),
     "mla_combine_out_proj": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _I32, _I32, _P,
                                     _P]),
     "mla_decode": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _SZ, _P, _P, _I32, _P]),
@@ -514,6 +516,35 @@ def mla_decode_ragged(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scal
         _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         _dev(out, "out", torch.float32, 3), _dev(lse_out, "lse_out", torch.float32, 2),
         _dtype_code(q_lat), _stream(stream))
+
+
+def mla_fold_uq(w_uk, w_uq, num_heads, w_out, stream=None):
+    """W~ [H*d_c, d_cq]: head i rows = W^UK_i^T W^UQ_i (w_uk [H*d_h, d_c], w_uq [H*d_h, d_cq])."""
+    H = int(num_heads)
+    _expect(w_uk.dim() == 2 and w_uq.dim() == 2 and w_uk.shape[0] == w_uq.shape[0],
+            "w_uk and w_uq must be [H*d_h, .] with the same rows")
+    _expect(w_uk.shape[0] % H == 0, "rows of w_uk must be H*d_h")
+    d_h, d_c, d_cq = w_uk.shape[0] // H, w_uk.shape[1], w_uq.shape[1]
+    _expect(tuple(w_out.shape) == (H * d_c, d_cq), "w_out must be [H*d_c, d_cq]")
+    _expect(w_uk.dtype == w_uq.dtype, "w_uk and w_uq share a dtype")
+    _invoke("mla_fold_uq", _dev(w_uk, "w_uk", None, 2), _dev(w_uq, "w_uq", None, 2), H, d_h, d_c,
+            d_cq, _dtype_code(w_uk), _dev(w_out, "w_out", None, 2), _dtype_code(w_out),
+            _stream(stream))
+
+
+def mla_fold_o_uv(w_o, w_uv, num_heads, w_out, stream=None):
+    """W_fold [d_model, H*d_c]: head i columns = W^O_i W^UV_i (w_o [d_model, H*d_h],
+    w_uv [H*d_h, d_c])."""
+    H = int(num_heads)
+    _expect(w_o.dim() == 2 and w_uv.dim() == 2 and w_o.shape[1] == w_uv.shape[0],
+            "w_o must be [d_model, H*d_h] and w_uv [H*d_h, d_c]")
+    _expect(w_uv.shape[0] % H == 0, "rows of w_uv must be H*d_h")
+    d_h, d_c, d_model = w_uv.shape[0] // H, w_uv.shape[1], w_o.shape[0]
+    _expect(tuple(w_out.shape) == (d_model, H * d_c), "w_out must be [d_model, H*d_c]")
+    _expect(w_o.dtype == w_uv.dtype, "w_o and w_uv share a dtype")
+    _invoke("mla_fold_o_uv", _dev(w_o, "w_o", None, 2), _dev(w_uv, "w_uv", None, 2), H, d_h, d_c,
+            d_model, _dtype_code(w_o), _dev(w_out, "w_out", None, 2), _dtype_code(w_out),
+            _stream(stream))
 
 
 def mla_splitk_combine(o_part, lse_part, out, lse_out=None, stream=None):

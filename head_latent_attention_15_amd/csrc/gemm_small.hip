@@ -1,5 +1,8 @@
-// Batched small GEMM with fp32 accumulation, for the projections around the attention:
+// Batched small GEMM with fp32 accumulation, for the projections around the attention and
+// the offline weight folds:
 //   y[z][m][n] = sum_k x[z][m][k] * W_z(n, k)
+// x[z][m][k] is x[z*sx + m*ldx + k], or x[z*sx + k*ldx + m] with x_km (a weight read
+// transposed, as W^UK_i^T in the fold W^UK_i^T W^UQ_i).
 // W_z(n, k) is w[z*sw + n*ldw + k] for nn.Linear-layout weights ([out, in], used by
 // y = x W^T: W^DQ, W^UQ, W^QR, W^DKV, W^KR, W^UV_i, W^O) and w[z*sw + k*ldw + n] for the
 // query absorption q~_i = W^UK_i^T q^C_i ("論文解説: DeepSeek-V2 …", "行列吸収トリック").
@@ -18,7 +21,7 @@ template <typename XT, typename WT, typename YT, bool W_NK>
 __global__ __launch_bounds__(256) void gemm_small_kernel(
     const XT* __restrict__ x, int64_t ldx, int64_t sx, const WT* __restrict__ w, int64_t ldw,
     int64_t sw, YT* __restrict__ y, int64_t ldy, int64_t sy, int M, int N, int K,
-    int accumulate) {
+    int accumulate, int x_km) {
   __shared__ float xs[GT_K][GT_M + 4];
   __shared__ float ws[GT_K][GT_N + 4];
   const int z = blockIdx.z;
@@ -38,7 +41,7 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(
     for (int e = tid; e < GT_M * GT_K; e += 256) {
       const int mm = e / GT_K, kk = e % GT_K;
       const int gm = m0 + mm, gk = k0 + kk;
-      xs[kk][mm] = (gm < M && gk < K) ? ld(x + gm * ldx + gk) : 0.f;
+      xs[kk][mm] = (gm < M && gk < K) ? ld(x + (x_km ? gk * ldx + gm : gm * ldx + gk)) : 0.f;
     }
     for (int e = tid; e < GT_N * GT_K; e += 256) {
       int nn, kk;
@@ -90,12 +93,12 @@ static hipError_t launch3(const GemmArgs& g, hipStream_t s) {
     hipLaunchKernelGGL((gemm_small_kernel<XT, WT, YT, true>), grid, dim3(256), 0, s,
                        static_cast<const XT*>(g.x), g.ldx, g.sx, static_cast<const WT*>(g.w),
                        g.ldw, g.sw, static_cast<YT*>(g.y), g.ldy, g.sy, g.M, g.N, g.K,
-                       g.accumulate);
+                       g.accumulate, g.x_km);
   } else {
     hipLaunchKernelGGL((gemm_small_kernel<XT, WT, YT, false>), grid, dim3(256), 0, s,
                        static_cast<const XT*>(g.x), g.ldx, g.sx, static_cast<const WT*>(g.w),
                        g.ldw, g.sw, static_cast<YT*>(g.y), g.ldy, g.sy, g.M, g.N, g.K,
-                       g.accumulate);
+                       g.accumulate, g.x_km);
   }
   return hipGetLastError();
 }

@@ -79,6 +79,7 @@ struct GemmArgs {
   void* y; int64_t ldy, sy; int y_bf16;
   int M, N, K, batch;
   int accumulate = 0;
+  int x_km = 0;  // x[z][m][k] at x[z*sx + k*ldx + m] (launch_gemm_small only)
 };
 hipError_t launch_gemm_small(const GemmArgs& g, hipStream_t s);
 // Same product on bf16 MFMA for bf16 nn.Linear-layout weights (w_nk), fp32 y and K a

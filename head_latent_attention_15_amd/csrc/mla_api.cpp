@@ -581,6 +581,43 @@ mla_status_t mla_kv_append_strided(const float* c_kv, int64_t ld_ckv, const floa
                    block_table, kv_cache, rope_base, shape, cache_dtype, stream);
 }
 
+mla_status_t mla_fold_uq(const void* w_uk, const void* w_uq, int32_t H, int32_t d_h,
+                         int32_t d_c, int32_t d_cq, mla_dtype_t w_dtype, void* w_out,
+                         mla_dtype_t out_dtype, void* stream) {
+  if (!w_uk || !w_uq || !w_out) return fail(MLA_ERR_NULL, "mla_fold_uq: a pointer is NULL");
+  if (H < 1 || d_h < 1 || d_c < 1 || d_cq < 1)
+    return fail(MLA_ERR_SHAPE, "mla_fold_uq: sizes must be >= 1");
+  if (!is_dtype(w_dtype) || !is_dtype(out_dtype))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_fold_uq: unknown dtype");
+  // head i: y[i][m][n] = sum_d w_uk[i d_h + d][m] w_uq[i d_h + d][n], rows i d_c + m of w_out
+  mla::GemmArgs g;
+  g.x = w_uk; g.ldx = d_c; g.sx = static_cast<int64_t>(d_h) * d_c; g.x_bf16 = w_dtype == MLA_BF16;
+  g.x_km = 1;
+  g.w = w_uq; g.ldw = d_cq; g.sw = static_cast<int64_t>(d_h) * d_cq; g.w_bf16 = w_dtype == MLA_BF16;
+  g.w_nk = false;
+  g.y = w_out; g.ldy = d_cq; g.sy = static_cast<int64_t>(d_c) * d_cq; g.y_bf16 = out_dtype == MLA_BF16;
+  g.M = d_c; g.N = d_cq; g.K = d_h; g.batch = H;
+  return launched(mla::launch_gemm_small(g, as_stream(stream)), "W^UK^T W^UQ fold");
+}
+
+mla_status_t mla_fold_o_uv(const void* w_o, const void* w_uv, int32_t H, int32_t d_h,
+                           int32_t d_c, int32_t d_model, mla_dtype_t w_dtype, void* w_out,
+                           mla_dtype_t out_dtype, void* stream) {
+  if (!w_o || !w_uv || !w_out) return fail(MLA_ERR_NULL, "mla_fold_o_uv: a pointer is NULL");
+  if (H < 1 || d_h < 1 || d_c < 1 || d_model < 1)
+    return fail(MLA_ERR_SHAPE, "mla_fold_o_uv: sizes must be >= 1");
+  if (!is_dtype(w_dtype) || !is_dtype(out_dtype))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_fold_o_uv: unknown dtype");
+  // head i: y[i][n][c] = sum_d w_o[n][i d_h + d] w_uv[i d_h + d][c], columns i d_c + c of w_out
+  mla::GemmArgs g;
+  g.x = w_o; g.ldx = static_cast<int64_t>(H) * d_h; g.sx = d_h; g.x_bf16 = w_dtype == MLA_BF16;
+  g.w = w_uv; g.ldw = d_c; g.sw = static_cast<int64_t>(d_h) * d_c; g.w_bf16 = w_dtype == MLA_BF16;
+  g.w_nk = false;
+  g.y = w_out; g.ldy = static_cast<int64_t>(H) * d_c; g.sy = d_c; g.y_bf16 = out_dtype == MLA_BF16;
+  g.M = d_model; g.N = d_c; g.K = d_h; g.batch = H;
+  return launched(mla::launch_gemm_small(g, as_stream(stream)), "W^O W^UV fold");
+}
+
 mla_status_t mla_out_proj(const float* o_lat, const void* w_uv, const void* w_o, int32_t B,
                           int32_t H, int32_t d_c, int32_t d_h, int32_t d_model,
                           mla_dtype_t w_dtype, float* o_heads, float* u, void* stream) {

@@ -340,6 +340,29 @@ mla_status_t mla_decode_noalloc(const void* q_lat, const void* q_pe, const void*
                                 int32_t num_splits, float* out, float* lse_out, mla_dtype_t dtype,
                                 void* stream);
 
+/* Offline absorption of W^UK into W^UQ: the weight of q~ = W~ c^Q in one projection
+ * ("論文解説: DeepSeek-V2 …", "行列吸収トリック"; qiita.com/joule/items/57d9b3f4fc27959eaa0d,
+ * "Absorption Trick"):
+ *   w_out[i*d_c + m][n] = sum_d w_uk[i*d_h + d][m] * w_uq[i*d_h + d][n]   (W~_i = W^UK_i^T W^UQ_i)
+ *   w_uk [H*d_h][d_c], w_uq [H*d_h][d_cq] (nn.Linear weights), w_dtype; w_out [H*d_c][d_cq]
+ *   out_dtype (written; bf16 rounded once from the fp32 sum).  A one-time preparation
+ *   (a VALU batched GEMM), not a hot-path call.  Errors: NULL, SHAPE, UNSUPPORTED. */
+mla_status_t mla_fold_uq(const void* w_uk, const void* w_uq, int32_t H, int32_t d_h,
+                         int32_t d_c, int32_t d_cq, mla_dtype_t w_dtype, void* w_out,
+                         mla_dtype_t out_dtype, void* stream);
+
+/* Offline fold of W^UV into W^O: u = W_fold [o~_1; ...; o~_H] replaces o_i = W^UV_i o~_i
+ * followed by u = W^O [o_1; ...; o_H] (qiita.com/joule/items/57d9b3f4fc27959eaa0d,
+ * "Absorption Trick": W_UV folds into W_O):
+ *   w_out[n][i*d_c + c] = sum_d w_o[n][i*d_h + d] * w_uv[i*d_h + d][c]
+ *   w_o [d_model][H*d_h], w_uv [H*d_h][d_c] (nn.Linear weights), w_dtype;
+ *   w_out [d_model][H*d_c] out_dtype (written).  At decode the folded weight is d_c / d_h
+ *   times the size of W^O.  One-time preparation, as mla_fold_uq.
+ * Errors: NULL, SHAPE, UNSUPPORTED. */
+mla_status_t mla_fold_o_uv(const void* w_o, const void* w_uv, int32_t H, int32_t d_h,
+                           int32_t d_c, int32_t d_model, mla_dtype_t w_dtype, void* w_out,
+                           mla_dtype_t out_dtype, void* stream);
+
 /* Value up-projection and output projection.
  *   o_heads[b][i][d] = sum_c w_uv[i*d_h + d][c] * o_lat[b][i][c]    (o_i = W^UV_i o~_i)
  *   u[b][n] = sum_k w_o[n][k] * o_heads[b][k]   (k over H*d_h; u = W^O [o_1;...;o_H])
