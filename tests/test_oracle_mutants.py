@@ -168,3 +168,77 @@ def test_mutant_is_caught(name, monkeypatch):
         except Exception:  # an assertion or a shape error: the pin noticed
             failures += 1
     assert failures > 0, f"planted mistake {name} passed every pin"
+
+
+# ---- the fp8 latent-cache oracle ------------------------------------------------------
+from oracle import fp8_cache as F8  # noqa: E402
+from tests import test_oracle_fp8 as fp8_pins  # noqa: E402
+
+FP8_PIN_TESTS = [
+    fp8_pins.test_decode_every_code_matches_torch,
+    fp8_pins.test_encode_matches_torch_including_ties,
+    fp8_pins.test_encode_saturates_and_keeps_signed_zero,
+    fp8_pins.test_codes_of_representable_values_round_trip,
+    fp8_pins.test_golden_example,
+    fp8_pins.test_scale_is_the_smallest_power_of_two,
+    fp8_pins.test_round_trip_error_bound,
+    fp8_pins.test_values_the_format_holds_are_exact,
+    fp8_pins.test_row_layout,
+]
+
+F8_scale_orig = F8.block_scale
+F8_encode_orig = F8.e4m3_encode
+F8_value_orig = F8.e4m3_value
+
+
+def _scale_one_binade_high(block):
+    return 2.0 * F8_scale_orig(block)
+
+
+def _encode_ties_away(x):
+    """round half away from zero instead of to the even code"""
+    x = np.asarray(x, dtype=float)
+    out = F8_encode_orig(x)
+    vals = np.sort(F8.e4m3_decode(np.arange(0x7F, dtype=np.uint8)))
+    mids = set(((vals[:-1] + vals[1:]) / 2).tolist())
+    flat, res = x.reshape(-1), out.reshape(-1)
+    for n, v in enumerate(flat):
+        if abs(v) in mids:
+            res[n] = F8_encode_orig(np.array([math.copysign(np.nextafter(abs(v), np.inf), v)]))[0]
+    return out
+
+
+def _value_bias_8(code):
+    code = int(code) & 0xFF
+    e, m = (code >> 3) & 0xF, code & 7
+    if e == 0xF and m == 7:
+        return math.nan
+    sign = -1.0 if code & 0x80 else 1.0
+    return sign * ((m / 8.0) * 2.0 ** -7 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 8))
+
+
+def _encode_flush_subnormals(x):
+    out = F8_encode_orig(x)
+    out[(out & 0x78) == 0] &= 0x80
+    return out
+
+
+FP8_MUTANTS = {
+    "fp8_scale_one_binade_high": ("block_scale", _scale_one_binade_high),
+    "fp8_ties_away_from_zero": ("e4m3_encode", _encode_ties_away),
+    "fp8_exponent_bias_8": ("e4m3_value", _value_bias_8),
+    "fp8_flush_subnormals": ("e4m3_encode", _encode_flush_subnormals),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_fp8_mutant_is_caught(name, monkeypatch):
+    attr, fn = FP8_MUTANTS[name]
+    monkeypatch.setattr(F8, attr, fn)
+    failures = 0
+    for t in FP8_PIN_TESTS:
+        try:
+            t()
+        except Exception:
+            failures += 1
+    assert failures > 0, f"planted mistake {name} passed every fp8 pin"
