@@ -3,22 +3,27 @@
 
 One step = the decode hot path over one batch of the DeepSeek-V2-shaped workload
 (B=32 sequences, T=4096 cached tokens each, H=128 heads, d_c=512, d_R=64, bf16 cache and
-queries, 64-token pages): split-K attention over the paged latent cache (bf16 split
-partials) followed by the log-sum-exp combine, both from libmla.  Inputs are seeded
-synthetic data, resident in HBM before timing starts.  Four copies of the 151 MB cache
-rotate between steps so the 256 MB Infinity Cache cannot serve a repeat.
+queries, 64-token pages): split-K attention over the paged latent cache (the library's
+kernel for 128 heads, bf16 split partials) followed by the log-sum-exp combine, both from
+libmla.  Inputs are seeded synthetic data, resident in HBM before timing starts.  Four
+copies of the 151 MB cache rotate between steps so the 256 MB Infinity Cache cannot serve
+a repeat.
 
-Three timed regions on the launch stream, each bracketed by HIP events at its ends only:
-K whole steps (the headline value), K attention launches back to back (the attention
-kernel's average launch duration, its roofline position), and K combine launches.  Back
-to back, the attention kernel runs a little slower than between two combines (the
-kernel trace shows both), so its roofline figure is the conservative one.  Every launch is
-a pre-marshalled library call (head_latent_attention_15_amd.bind), so the host stays ahead of the GPU.
+Timed regions on the launch stream, each bracketed by HIP events at its ends only: K whole
+steps (the headline value); the same steps with fp32 partials; K single launches that
+merge their own splits (mla_decode_fused); K attention launches back to back (the
+attention kernel's average launch duration: its roofline position); K combines; and K
+launches of the other attention kernel.  Every launch is a pre-marshalled library call
+(head_latent_attention_15_amd.bind), so the host stays ahead of the GPU.  Beside the
+headline: the long-context and ragged workloads (split grid, flattened work list, single
+launch), the headline over fp8 latent rows, multi-token decode, the plain and LDS-DMA
+stream-read ceilings, the full decode layer with every step's roofline fraction and the
+offline folds, and the fp64 CPU oracle on all host cores and on one thread.
 
-Prints ONE JSON line: throughput (latent-cache GB/s), the attention kernel's roofline
-position, and the fp64 CPU oracle timed on the host cores as a baseline.
+Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline] [--no-layer]
+                    [--no-configs] [--headline-only]
 """
 from __future__ import annotations
 
@@ -356,6 +361,53 @@ def multi_token_rows(mla, W, torch, caches, bt, sl, scale, num_cus, n_q: int = 2
             "tflops": round(flops / (us * 1e-6) / 1e12, 1)}
 
 
+def fp8_rows(mla, torch, inp, num_cus, steps, n_copies):
+    """The headline workload over fp8 latent rows (MLA_FP8: 656 bytes per token against
+    1152): the bf16 cache quantised once on the GPU (outside the timing), then attention +
+    combine (bf16 partials) and the attention alone, back to back over rotating copies.
+    GB/s count the fp8 bytes actually stored; the bf16-equivalent rate counts 1152 bytes per
+    token for comparison with the bf16 step."""
+    dev = torch.device("cuda:0")
+    B, H, T = 32, 128, 4096
+    S = mla.mla_suggest_num_splits(B, T, 0, 64, num_cus)
+    src = inp["cache"].to(dev)
+    caches = [torch.empty(src.shape[:-1] + (656,), dtype=torch.uint8, device=dev)]
+    mla.mla_quantize_cache(src, caches[0])
+    del src
+    for _ in range(n_copies - 1):
+        caches.append(caches[0].clone())
+    q_lat, q_pe = inp["q_lat"].to(dev), inp["q_pe"].to(dev)
+    bt, sl = inp["block_table"].to(dev), inp["seq_lens"].to(dev)
+    o_part = torch.empty(B, H, S, 512, device=dev, dtype=torch.bfloat16)
+    lse_part = torch.empty(B, H, S, device=dev)
+    out = torch.empty(B, H, 512, device=dev)
+    lse = torch.empty(B, H, device=dev)
+    calls = [mla.bind(mla.mla_decode_attn_planned, q_lat, q_pe, c, bt, sl, inp["scale"], S, o_part,
+                      lse_part) for c in caches]
+    combine = mla.bind(mla.mla_splitk_combine, o_part, lse_part, out, lse)
+    t0 = time.perf_counter()
+    k = 0
+    while time.perf_counter() - t0 < 0.3:
+        calls[k % n_copies]()
+        combine()
+        k += 1
+        if k % 32 == 0:
+            torch.cuda.synchronize()
+    step_ms = timed_ms(torch, lambda k: (calls[k % n_copies](), combine()), steps)
+    attn_ms = timed_ms(torch, lambda k: calls[k % n_copies](), steps)
+    tokens = B * T
+    fp8_bytes = tokens * 656
+    attn_bytes = fp8_bytes + B * H * 576 * 2 + bt.numel() * 4 + B * 4
+    del caches
+    return {"workload": "dsv2_b32_t4k over fp8 latent rows (MLA_FP8, 656 B per token)",
+            "num_splits": S, "us_per_step": round(step_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
+            "cache_bytes": fp8_bytes, "cache_GBps_step": round(fp8_bytes / (step_ms * 1e-3) / 1e9, 1),
+            "attn_GBps": round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1),
+            "attn_frac": round(attn_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "bf16_equivalent_GBps_step": round(tokens * ROW_BYTES / (step_ms * 1e-3) / 1e9, 1),
+            "query_tokens_per_s": round(B / (step_ms * 1e-3), 1)}
+
+
 def config_row(mla, torch, inp, name, num_cus, steps, n_copies, kernel="auto", flattened=False):
     """One attention workload beside the headline, back to back over n_copies rotating
     caches: the split-grid step (attention + combine, bf16 partials), its attention alone,
@@ -424,6 +476,11 @@ def config_row(mla, torch, inp, name, num_cus, steps, n_copies, kernel="auto", f
             "query_tokens_per_s": round(B / (step_ms * 1e-3), 1)}
 
 
+def _us(ms):
+    """milliseconds -> microseconds rounded, None for a region not timed (NaN)"""
+    return None if ms != ms else round(ms * 1e3, 2)
+
+
 def timed_ms(torch, fn, n):
     """Average milliseconds of n back-to-back calls fn(0..n-1) between two HIP events on the
     current stream (the stream the library launches on)."""
@@ -458,6 +515,9 @@ def main():
     ap.add_argument("--layer-only", action="store_true",
                     help="run only the full-layer measurement and print its JSON (for profiling "
                          "the layer's kernels)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline step and its attention alone (for a kernel "
+                         "trace of exactly those launches)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for --pmc runs)")
     args = ap.parse_args()
@@ -535,10 +595,11 @@ def main():
     while k < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
         attn(k)
         combine()
-        attn_f32_calls[k % N_CACHE_COPIES]()
-        combine_f32()
-        step_fused(k)
-        other_calls[k % N_CACHE_COPIES]()
+        if not args.headline_only:
+            attn_f32_calls[k % N_CACHE_COPIES]()
+            combine_f32()
+            step_fused(k)
+            other_calls[k % N_CACHE_COPIES]()
         k += 1
         if k % 32 == 0:
             torch.cuda.synchronize()
@@ -549,12 +610,16 @@ def main():
     # the other timed regions, each back to back with events at the ends only (an event
     # recorded between two kernels stalls the queue for several microseconds, so
     # per-kernel events would time the stall with the kernel)
-    ms_step_f32 = timed_ms(torch, lambda k: (attn_f32_calls[k % N_CACHE_COPIES](), combine_f32()),
-                           args.steps)
-    ms_fused = timed_ms(torch, step_fused, args.steps)
+    if args.headline_only:
+        ms_step_f32 = ms_fused = other_avg = float("nan")
+    else:
+        ms_step_f32 = timed_ms(torch, lambda k: (attn_f32_calls[k % N_CACHE_COPIES](), combine_f32()),
+                               args.steps)
+        ms_fused = timed_ms(torch, step_fused, args.steps)
     attn_avg = timed_ms(torch, attn, args.steps)
     comb_avg = timed_ms(torch, lambda k: combine(), args.steps)
-    other_avg = timed_ms(torch, lambda k: other_calls[k % N_CACHE_COPIES](), args.steps)
+    if not args.headline_only:
+        other_avg = timed_ms(torch, lambda k: other_calls[k % N_CACHE_COPIES](), args.steps)
     c = counters.cpu()
     if int(c[-1]) != 0 or int(c[:-1].abs().sum()) != 0 or not bool(torch.isfinite(out).all()):
         raise RuntimeError("in-launch merge left its counters set or a non-finite output")
@@ -621,11 +686,11 @@ def main():
         "step_frac": round(step_alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         # the whole step against the HBM roofline: the figure the headline value is;
         # roofline.frac below is the attention kernel alone
-        "step_us_f32_partials": round(ms_step_f32 * 1e3, 2),
-        "step_us_one_launch_merge": round(ms_fused * 1e3, 2),
+        "step_us_f32_partials": _us(ms_step_f32),
+        "step_us_one_launch_merge": _us(ms_fused),
         "attn_us": round(attn_avg * 1e3, 2),
         "combine_us": round(comb_avg * 1e3, 2),
-        f"attn_us_{other}_kernel": round(other_avg * 1e3, 2),
+        f"attn_us_{other}_kernel": _us(other_avg),
         "attn_tflops": round(flops / attn_s / 1e12, 2),
         "mfma_frac_of_peak": round(flops / attn_s / 1e12 / BF16_PEAK_TFLOPS, 4),
         "stream_read_GBps": round(stream_gbps_plain, 1),
@@ -640,12 +705,17 @@ def main():
                      "bytes_per_launch_algorithmic": attn_alg_bytes},
     }
     del caches
+    if args.headline_only:
+        print(json.dumps(result), flush=True)
+        return
     if not args.no_configs:
         log("timing long_b4_t32k and ragged_b128")
         result["long_b4_t32k"] = config_row(mla, torch, W.long_b4_t32k(), "long_b4_t32k", num_cus,
                                             args.steps, N_CACHE_COPIES)
         result["ragged_b128"] = config_row(mla, torch, W.ragged_b128(), "ragged_b128", num_cus,
                                            args.steps, 2, flattened=True)
+    log("timing the headline workload over fp8 latent rows")
+    result["fp8_cache"] = fp8_rows(mla, torch, inp, num_cus, args.steps, N_CACHE_COPIES)
     log("timing multi-token decode (2 query tokens per sequence)")
     caches = [inp["cache"].to(dev)]
     for _ in range(N_CACHE_COPIES - 1):

@@ -24,7 +24,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "mla.h")
 
 MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED = 0, 1, 2, 3
 MLA_ERR_WORKSPACE, MLA_ERR_LAUNCH, MLA_ERR_INDEX = 4, 5, 6
-MLA_F32, MLA_BF16 = 0, 1
+MLA_F32, MLA_BF16, MLA_FP8 = 0, 1, 2
 
 
 class MLAError(RuntimeError):
@@ -70,6 +70,7 @@ _SIGNATURES = {
     "mla_decode_ragged": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _P, _SZ, _P, _P, _I32, _P]),
     "mla_splitk_combine": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "mla_fold_uq": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P]),
+    "mla_quantize_cache": (_I32, [_P, _I32, _I64, _I64, _P, _P]),
     "mla_fold_o_uv": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P]),
     "mla_combine_out_proj": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _I32, _I32, _P,
                                     _P]),
@@ -243,10 +244,42 @@ def _expect(cond, msg):
         raise ValueError(msg)
 
 
+FP8_ROW_BYTES = 656  # MLA_FP8 cache rows: 512 E4M3 codes, 64 bf16 k^R, 4 fp32 scales
+
+
+def is_fp8_cache(kv_cache) -> bool:
+    """A uint8 cache of 656-byte rows (the MLA_FP8 format)."""
+    torch = _torch()
+    return kv_cache.dtype == torch.uint8 and kv_cache.shape[-1] == FP8_ROW_BYTES
+
+
+def _cache_code(kv_cache) -> int:
+    return MLA_FP8 if is_fp8_cache(kv_cache) else _dtype_code(kv_cache)
+
+
+def _attn_code(q_lat, q_pe, kv_cache) -> int:
+    """dtype code of an attention call: the shared dtype, or MLA_FP8 for bf16 queries over
+    fp8 rows."""
+    torch = _torch()
+    if is_fp8_cache(kv_cache):
+        _expect(q_lat.dtype == q_pe.dtype == torch.bfloat16, "fp8 rows take bf16 queries")
+        return MLA_FP8
+    _expect(q_pe.dtype == q_lat.dtype == kv_cache.dtype, "q_lat, q_pe, kv_cache share a dtype")
+    return _dtype_code(q_lat)
+
+
+def _check_row(kv_cache, d_c, d_R):
+    if is_fp8_cache(kv_cache):
+        _expect(d_c == 512 and d_R == 64, "fp8 rows hold d_c = 512 and d_R = 64")
+    else:
+        _expect(kv_cache.shape[2] == d_c + d_R, "cache row must be d_c + d_R wide")
+
+
 def paged_shape(kv_cache, block_table, num_heads: int, d_latent: int) -> _PagedShape:
     pages, P, row = kv_cache.shape
     B, maxp = block_table.shape
-    return _PagedShape(B, num_heads, d_latent, row - d_latent, P, maxp, pages)
+    d_rope = 64 if is_fp8_cache(kv_cache) else row - d_latent
+    return _PagedShape(B, num_heads, d_latent, d_rope, P, maxp, pages)
 
 
 # ----------------------------------------------------------------------------- sizes
@@ -323,14 +356,14 @@ def mla_kv_append(c_kv, k_r, seq_lens_before, block_table, kv_cache, rope_base, 
     torch = _torch()
     B, n, d_c = c_kv.shape
     _expect(k_r.shape[0] == B and k_r.shape[1] == n, "k_r must be [B,n,d_R]")
-    _expect(kv_cache.shape[2] == d_c + k_r.shape[2], "cache row must be d_c + d_R wide")
+    _check_row(kv_cache, d_c, k_r.shape[2])
     _expect(block_table.shape[0] == B and tuple(seq_lens_before.shape) == (B,), "batch mismatch")
     shp = paged_shape(kv_cache, block_table, 1, d_c)
     _invoke("mla_kv_append",
         _dev(c_kv, "c_kv", torch.float32, 3), _dev(k_r, "k_r", torch.float32, 3), n,
         _dev(seq_lens_before, "seq_lens_before", torch.int32, 1),
         _dev(block_table, "block_table", torch.int32, 2), _dev(kv_cache, "kv_cache", None, 3),
-        float(rope_base), ctypes.byref(shp), _dtype_code(kv_cache), _stream(stream))
+        float(rope_base), ctypes.byref(shp), _cache_code(kv_cache), _stream(stream))
 
 
 def mla_kv_append_strided(c_kv, k_r, seq_lens_before, block_table, kv_cache, rope_base,
@@ -340,7 +373,7 @@ def mla_kv_append_strided(c_kv, k_r, seq_lens_before, block_table, kv_cache, rop
     torch = _torch()
     B, n, d_c = c_kv.shape
     _expect(k_r.shape[0] == B and k_r.shape[1] == n, "k_r must be [B,n,d_R]")
-    _expect(kv_cache.shape[2] == d_c + k_r.shape[2], "cache row must be d_c + d_R wide")
+    _check_row(kv_cache, d_c, k_r.shape[2])
     _expect(block_table.shape[0] == B and tuple(seq_lens_before.shape) == (B,), "batch mismatch")
     shp = paged_shape(kv_cache, block_table, 1, d_c)
     c_ptr, ld_c = _dev_rows(c_kv, "c_kv", torch.float32, 3, 2)
@@ -348,7 +381,7 @@ def mla_kv_append_strided(c_kv, k_r, seq_lens_before, block_table, kv_cache, rop
     _invoke("mla_kv_append_strided", c_ptr, ld_c, k_ptr, ld_k, n,
         _dev(seq_lens_before, "seq_lens_before", torch.int32, 1),
         _dev(block_table, "block_table", torch.int32, 2), _dev(kv_cache, "kv_cache", None, 3),
-        float(rope_base), ctypes.byref(shp), _dtype_code(kv_cache), _stream(stream))
+        float(rope_base), ctypes.byref(shp), _cache_code(kv_cache), _stream(stream))
 
 
 def mla_decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale, num_splits,
@@ -359,8 +392,8 @@ def mla_decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale,
     torch = _torch()
     B, H, d_c = q_lat.shape
     _expect(q_pe.shape[0] == B and q_pe.shape[1] == H, "q_pe must be [B,H,d_R]")
-    _expect(q_pe.dtype == q_lat.dtype == kv_cache.dtype, "q_lat, q_pe, kv_cache share a dtype")
-    _expect(kv_cache.shape[2] == d_c + q_pe.shape[2], "cache row must be d_c + d_R wide")
+    code = _attn_code(q_lat, q_pe, kv_cache)
+    _check_row(kv_cache, d_c, q_pe.shape[2])
     _expect(block_table.shape[0] == B and tuple(seq_lens.shape) == (B,), "batch mismatch")
     S = int(num_splits)
     want = (B, H, d_c) if S == 1 else (B, H, S, d_c)
@@ -374,7 +407,7 @@ def mla_decode_attn(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale,
         _dev(kv_cache, "kv_cache", None, 3), _dev(block_table, "block_table", torch.int32, 2),
         _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), float(softmax_scale), S,
         _dev(o_part, "o_part"), _dtype_code(o_part), _dev(lse_part, "lse_part", torch.float32),
-        _dtype_code(q_lat), _stream(stream))
+        code, _stream(stream))
 
 
 
@@ -386,8 +419,8 @@ def mla_decode_attn_multi(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_
     torch = _torch()
     B, n_q, H, d_c = q_lat.shape
     _expect(tuple(q_pe.shape[:3]) == (B, n_q, H), "q_pe must be [B,n_q,H,d_R]")
-    _expect(q_pe.dtype == q_lat.dtype == kv_cache.dtype, "q_lat, q_pe, kv_cache share a dtype")
-    _expect(kv_cache.shape[2] == d_c + q_pe.shape[3], "cache row must be d_c + d_R wide")
+    code = _attn_code(q_lat, q_pe, kv_cache)
+    _check_row(kv_cache, d_c, q_pe.shape[3])
     _expect(block_table.shape[0] == B and tuple(seq_lens.shape) == (B,), "batch mismatch")
     S = int(num_splits)
     want = (B, n_q, H, d_c) if S == 1 else (B, n_q, H, S, d_c)
@@ -400,7 +433,7 @@ def mla_decode_attn_multi(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_
         _dev(kv_cache, "kv_cache", None, 3), _dev(block_table, "block_table", torch.int32, 2),
         _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), n_q, float(softmax_scale),
         S, _dev(o_part, "o_part"), _dtype_code(o_part), _dev(lse_part, "lse_part", torch.float32),
-        _dtype_code(q_lat), _stream(stream))
+        code, _stream(stream))
 
 ATTN_KERNELS = {"auto": 0, "heads": 1, "cols": 2, "generic": 3}
 
@@ -417,8 +450,8 @@ def mla_decode_attn_planned(q_lat, q_pe, kv_cache, block_table, seq_lens, softma
     else:
         B, n_q, H, d_c = q_lat.shape
     _expect(tuple(q_pe.shape[:-1]) == tuple(q_lat.shape[:-1]), "q_pe must match q_lat but the last dim")
-    _expect(q_pe.dtype == q_lat.dtype == kv_cache.dtype, "q_lat, q_pe, kv_cache share a dtype")
-    _expect(kv_cache.shape[2] == d_c + q_pe.shape[-1], "cache row must be d_c + d_R wide")
+    code = _attn_code(q_lat, q_pe, kv_cache)
+    _check_row(kv_cache, d_c, q_pe.shape[-1])
     _expect(block_table.shape[0] == B and tuple(seq_lens.shape) == (B,), "batch mismatch")
     S = int(num_splits)
     _expect(o_part.numel() == B * n_q * H * S * d_c, "o_part must hold B*n_q*H*S*d_c elements")
@@ -431,7 +464,7 @@ def mla_decode_attn_planned(q_lat, q_pe, kv_cache, block_table, seq_lens, softma
         _dev(kv_cache, "kv_cache", None, 3), _dev(block_table, "block_table", torch.int32, 2),
         _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), n_q, float(softmax_scale),
         S, _dev(o_part, "o_part"), _dtype_code(o_part), _dev(lse_part, "lse_part", torch.float32),
-        _dtype_code(q_lat), k, _stream(stream))
+        code, k, _stream(stream))
 
 
 def merge_counters(rows, device=None):
@@ -454,8 +487,8 @@ def mla_decode_fused(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale
         B, n_q, H, d_c = q_lat.shape
     rows = B * n_q
     _expect(tuple(q_pe.shape[:-1]) == tuple(q_lat.shape[:-1]), "q_pe must match q_lat but the last dim")
-    _expect(q_pe.dtype == q_lat.dtype == kv_cache.dtype, "q_lat, q_pe, kv_cache share a dtype")
-    _expect(kv_cache.shape[2] == d_c + q_pe.shape[-1], "cache row must be d_c + d_R wide")
+    code = _attn_code(q_lat, q_pe, kv_cache)
+    _check_row(kv_cache, d_c, q_pe.shape[-1])
     _expect(block_table.shape[0] == B and tuple(seq_lens.shape) == (B,), "batch mismatch")
     S = int(num_splits)
     _expect(out.numel() == rows * H * d_c, "out must hold B*n_q*H*d_c floats")
@@ -478,7 +511,7 @@ def mla_decode_fused(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale
         _dev(lse_part, "lse_part", torch.float32) if S > 1 else None,
         _dev(counters, "counters", torch.int32, 1) if S > 1 else None,
         _dev(out, "out", torch.float32), _dev(lse_out, "lse_out", torch.float32),
-        _dtype_code(q_lat), _stream(stream))
+        code, _stream(stream))
 
 
 def mla_decode_fused_single_launch(shape, n_q, num_splits) -> int:
@@ -501,8 +534,8 @@ def mla_decode_ragged(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scal
     torch = _torch()
     B, H, d_c = q_lat.shape
     _expect(tuple(q_pe.shape[:-1]) == (B, H), "q_pe must be [B,H,d_R]")
-    _expect(q_pe.dtype == q_lat.dtype == kv_cache.dtype, "q_lat, q_pe, kv_cache share a dtype")
-    _expect(kv_cache.shape[2] == d_c + q_pe.shape[-1], "cache row must be d_c + d_R wide")
+    code = _attn_code(q_lat, q_pe, kv_cache)
+    _check_row(kv_cache, d_c, q_pe.shape[-1])
     _expect(block_table.shape[0] == B and tuple(seq_lens.shape) == (B,), "batch mismatch")
     _expect(tuple(out.shape) == (B, H, d_c), "out must be [B,H,d_c]")
     if lse_out is not None:
@@ -515,7 +548,7 @@ def mla_decode_ragged(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scal
         _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), float(softmax_scale),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         _dev(out, "out", torch.float32, 3), _dev(lse_out, "lse_out", torch.float32, 2),
-        _dtype_code(q_lat), _stream(stream))
+        code, _stream(stream))
 
 
 def mla_fold_uq(w_uk, w_uq, num_heads, w_out, stream=None):
@@ -545,6 +578,19 @@ def mla_fold_o_uv(w_o, w_uv, num_heads, w_out, stream=None):
     _invoke("mla_fold_o_uv", _dev(w_o, "w_o", None, 2), _dev(w_uv, "w_uv", None, 2), H, d_h, d_c,
             d_model, _dtype_code(w_o), _dev(w_out, "w_out", None, 2), _dtype_code(w_out),
             _stream(stream))
+
+
+def mla_quantize_cache(src, dst, stream=None):
+    """fp8 rows dst [..., 656] (uint8) from rows src [..., 576] (fp32 or bf16, rows contiguous
+    in memory with stride src.stride(-2) elements)."""
+    torch = _torch()
+    _expect(src.shape[-1] == 576 and dst.shape[-1] == FP8_ROW_BYTES, "rows of 576 -> 656 bytes")
+    _expect(dst.dtype == torch.uint8, "dst must be uint8")
+    rows = src.numel() // 576
+    _expect(dst.numel() == rows * FP8_ROW_BYTES, "dst must hold one row per source row")
+    _expect(src.is_contiguous(), "src must be contiguous")
+    _invoke("mla_quantize_cache", _dev(src, "src"), _dtype_code(src), 576, rows,
+            _dev(dst, "dst", torch.uint8), _stream(stream))
 
 
 def mla_splitk_combine(o_part, lse_part, out, lse_out=None, stream=None):
@@ -583,7 +629,7 @@ def mla_decode(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale, num_
     least mla_decode_workspace_bytes bytes; may be None when num_splits == 1)."""
     torch = _torch()
     B, H, d_c = q_lat.shape
-    _expect(q_pe.dtype == q_lat.dtype == kv_cache.dtype, "q_lat, q_pe, kv_cache share a dtype")
+    code = _attn_code(q_lat, q_pe, kv_cache)
     _expect(tuple(out.shape) == (B, H, d_c), "out must be [B,H,d_c]")
     shp = paged_shape(kv_cache, block_table, H, d_c)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
@@ -593,7 +639,7 @@ def mla_decode(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale, num_
         _dev(kv_cache, "kv_cache", None, 3), _dev(block_table, "block_table", torch.int32, 2),
         _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), float(softmax_scale),
         int(num_splits), ws_ptr, ws_bytes, _dev(out, "out", torch.float32, 3),
-        _dev(lse_out, "lse_out", torch.float32, 2), _dtype_code(q_lat), _stream(stream))
+        _dev(lse_out, "lse_out", torch.float32, 2), code, _stream(stream))
 
 
 def mla_decode_noalloc(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale,
@@ -602,7 +648,7 @@ def mla_decode_noalloc(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_sca
     the call allocates no device memory."""
     torch = _torch()
     B, H, d_c = q_lat.shape
-    _expect(q_pe.dtype == q_lat.dtype == kv_cache.dtype, "q_lat, q_pe, kv_cache share a dtype")
+    code = _attn_code(q_lat, q_pe, kv_cache)
     _expect(tuple(out.shape) == (B, H, d_c), "out must be [B,H,d_c]")
     shp = paged_shape(kv_cache, block_table, H, d_c)
     _invoke("mla_decode_noalloc",
@@ -610,7 +656,7 @@ def mla_decode_noalloc(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_sca
         _dev(kv_cache, "kv_cache", None, 3), _dev(block_table, "block_table", torch.int32, 2),
         _dev(seq_lens, "seq_lens", torch.int32, 1), ctypes.byref(shp), float(softmax_scale),
         int(num_splits), _dev(out, "out", torch.float32, 3),
-        _dev(lse_out, "lse_out", torch.float32, 2), _dtype_code(q_lat), _stream(stream))
+        _dev(lse_out, "lse_out", torch.float32, 2), code, _stream(stream))
 
 
 def mla_out_proj(o_lat, w_uv, w_o, o_heads, u=None, stream=None):

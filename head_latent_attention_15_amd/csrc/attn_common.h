@@ -108,8 +108,21 @@ __device__ __forceinline__ i32x4_t i16x4x2_ones() {
 // reading the rows straight from the paged cache.  One wavefront handles n_heads heads
 // starting at h_begin; lane l owns features 9l .. 9l+8 of the score and latent columns
 // l + 64k.
+// Element k of a cache row: bf16 rows of 576 values, or (FP8) 656-byte rows of 512 E4M3
+// codes, 64 bf16 values and 4 fp32 block scales (code times its block's scale).
+template <bool FP8>
+__device__ __forceinline__ float row_elem(const unsigned char* row, int k) {
+  if constexpr (FP8) {
+    if (k >= DC) return bf16_to_f32(reinterpret_cast<const bf16raw*>(row + DC)[k - DC]);
+    const float sc = reinterpret_cast<const float*>(row + DC + 2 * DR)[k >> 7];
+    return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(row[k]), 0) * sc;
+  } else {
+    return bf16_to_f32(reinterpret_cast<const bf16raw*>(row)[k]);
+  }
+}
+
 // The partial of head h goes to row prow0 + h * hstride of o_part / lse_part.
-template <typename OT>
+template <typename OT, bool FP8 = false>
 __device__ void split_exact_fallback(const bf16raw* __restrict__ q_lat,
                                      const bf16raw* __restrict__ q_pe,
                                      const bf16raw* __restrict__ cache, const int32_t* bt_row,
@@ -118,6 +131,7 @@ __device__ void split_exact_fallback(const bf16raw* __restrict__ q_lat,
                                      OT* __restrict__ o_part, float* __restrict__ lse_part,
                                      int h_begin, int n_heads, int lane) {
   const int P = 1 << log2P;
+  constexpr int RB = FP8 ? 656 : ROW_BYTES;
   for (int h = h_begin; h < h_begin + n_heads; ++h) {
     float q[9];
 #pragma unroll
@@ -131,17 +145,18 @@ __device__ void split_exact_fallback(const bf16raw* __restrict__ q_lat,
     for (int k = 0; k < 8; ++k) acc[k] = 0.f;
     for (int j = j0; j < j1; ++j) {
       const int pg = bt_row[j >> log2P];
-      const bf16raw* row = cache + ((static_cast<int64_t>(pg) << log2P) + (j & (P - 1))) * ROW;
+      const unsigned char* row = reinterpret_cast<const unsigned char*>(cache) +
+                                 ((static_cast<int64_t>(pg) << log2P) + (j & (P - 1))) * RB;
       float part = 0.f;
 #pragma unroll
-      for (int f = 0; f < 9; ++f) part += q[f] * bf16_to_f32(row[9 * lane + f]);
+      for (int f = 0; f < 9; ++f) part += q[f] * row_elem<FP8>(row, 9 * lane + f);
       const float sc = mul_rn(wave_sum(part), scale_log2);
       const float mn = fmaxf(m, sc);
       const float alpha = __builtin_amdgcn_exp2f(m - mn);
       const float p = __builtin_amdgcn_exp2f(sc - mn);
       l = l * alpha + p;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = acc[k] * alpha + p * bf16_to_f32(row[lane + 64 * k]);
+      for (int k = 0; k < 8; ++k) acc[k] = acc[k] * alpha + p * row_elem<FP8>(row, lane + 64 * k);
       m = mn;
     }
     const int64_t ob = prow0 + static_cast<int64_t>(h) * hstride;

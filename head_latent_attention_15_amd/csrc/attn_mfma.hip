@@ -59,6 +59,20 @@ constexpr int PAGE_TABLE = VOFF_TABLE + TILE_WAVE_COPIES * 64 * 4;  // after 36 
 constexpr int MAX_SPLIT_PAGES = 1024;               // block-table entries of one split in LDS
 constexpr int LDS_BYTES = PAGE_TABLE + MAX_SPLIT_PAGES * 4;
 static_assert(LDS_BYTES <= 163840, "LDS per workgroup");
+// fp8 latent rows (656 bytes: 512 E4M3 codes, 64 bf16 k^R, 4 fp32 block scales) are
+// staged raw and converted into the same bf16 tile buffers: three of those, two staging
+// buffers (a tile of rows is 41 chunks of 16 bytes x 32 rows, copied as 21 wave-wide copies
+// of 1 KB), then the block table.
+constexpr int FP8_ROW_BYTES = 656;
+constexpr int FP8_ROW_CHUNKS = FP8_ROW_BYTES / 16;                  // 41
+constexpr int FP8_TILE_CHUNKS = TILE * FP8_ROW_CHUNKS;               // 1312
+constexpr int FP8_COPIES = (FP8_TILE_CHUNKS + 63) / 64;              // 21 wave copies
+constexpr int FP8_STAGE_BYTES = FP8_COPIES * 1024;                   // 21504
+constexpr int FP8_NBUF = 3;
+constexpr int FP8_STAGE = FP8_NBUF * TILE_BYTES;
+constexpr int FP8_PAGE_TABLE = FP8_STAGE + 2 * FP8_STAGE_BYTES;
+constexpr int FP8_LDS_BYTES = FP8_PAGE_TABLE + MAX_SPLIT_PAGES * 4;
+static_assert(FP8_LDS_BYTES <= 163840, "LDS per workgroup");
 constexpr float HEADROOM = 32.0f;  // log2 units between a split's first-tile max and its reference
 constexpr float P_RANGE = 64.0f;   // a score this far above the reference takes the fallback
 
@@ -127,7 +141,12 @@ __device__ void merge_splits(const OT* __restrict__ o_part, const float* __restr
 // attn_split runs this for tokens j0 .. j1-1 of sequence b with the queries of row bq and
 // writes the split's partial of head h to row prow0 + h * hstride of o_part / lse_part;
 // every thread of the workgroup calls it with the same arguments.
-template <int NW, typename OT>
+//
+// With FP8 the cache holds fp8 latent rows: each tile is copied raw into a staging buffer
+// one tile ahead and, during the previous tile, converted by every wavefront into the bf16
+// tile buffer the products read (E4M3 code times its block's power-of-two scale is exact in
+// bf16), so the score and PV steps are the bf16 ones.
+template <int NW, typename OT, bool FP8 = false>
 __device__ __forceinline__ void attn_split(
     const bf16raw* __restrict__ q_lat, const bf16raw* __restrict__ q_pe,
     const bf16raw* __restrict__ cache, const int32_t* __restrict__ block_table, int H,
@@ -136,11 +155,16 @@ __device__ __forceinline__ void attn_split(
   constexpr int NT = NW * 64;
   constexpr int NCT = DC / 16;                                    // PV column tiles
   constexpr int STEPS = KSTEPS * 2;                               // score MFMA steps per tile
-  constexpr int COPIES = (TILE_WAVE_COPIES + NW - 1) / NW;        // tile copies per wave
+  constexpr int COPIES = FP8 ? (FP8_COPIES + NW - 1) / NW          // tile copies per wave
+                             : (TILE_WAVE_COPIES + NW - 1) / NW;
   constexpr int COPY_EVERY = STEPS / COPIES;                      // score steps between copies
+  constexpr int NB = FP8 ? FP8_NBUF : NBUF;                       // bf16 tile buffers
+  constexpr int PTAB = FP8 ? FP8_PAGE_TABLE : PAGE_TABLE;         // LDS block table
+  constexpr int SRC_ROW = FP8 ? FP8_ROW_BYTES : ROW_BYTES;        // cache row bytes
   static_assert(NW == 1 || NW == 2 || NW == 4 || NW == 8, "16 to 128 heads");
   static_assert(KSTEPS == 18, "query loader covers 512 + 64 features");
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  static_assert(!FP8 || NW == 8, "fp8 rows: 128 heads");
+  __shared__ __attribute__((aligned(16))) char smem[FP8 ? FP8_LDS_BYTES : LDS_BYTES];
   lds_char_t* const lsm = (lds_char_t*)smem;  // 32-bit LDS addressing for the tile reads
   const uint32_t smem_lds = static_cast<uint32_t>(reinterpret_cast<size_t>(lsm));
 
@@ -177,7 +201,7 @@ __device__ __forceinline__ void attn_split(
   // A tile starting at token tb lies inside one page (P % 32 == 0, tiles 32-aligned).
   auto tile_page = [&](int tb) { return __builtin_amdgcn_readfirstlane(bt_row[tb >> log2P]); };
   auto page_base = [&](int pg, int tb) {
-    return cache_bytes + ((static_cast<int64_t>(pg) << log2P) + (tb & (P - 1))) * ROW_BYTES;
+    return cache_bytes + ((static_cast<int64_t>(pg) << log2P) + (tb & (P - 1))) * SRC_ROW;
   };
   auto tile_base = [&](int tb) { return page_base(tile_page(tb), tb); };
   // source offset of lane l of copy q (LDS chunk 64 q + l); rows past the split's end
@@ -199,13 +223,69 @@ __device__ __forceinline__ void attn_split(
 #pragma unroll
     for (int r = 0; r < COPIES; ++r) issue_copy(base, tb, buf, r);
   };
+  // fp8 rows: copy r of this wave moves chunks n = 64 q + lane (q = w + NW r, copies past
+  // the 21st repeat the 21st: same source, same bytes) of the tile's raw rows, chunk n being
+  // row n / 41, bytes 16 (n % 41) .. of it, to staging byte 16 n; the lanes past the tile's
+  // 1312 chunks re-read its last chunk into the buffer's tail.  Rows past the split's end
+  // repeat its last valid row.
+  auto fp8_copy = [&](const char* base, int tb, int stage, int r) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const unsigned q = min(static_cast<unsigned>(w + NW * r), static_cast<unsigned>(FP8_COPIES - 1));
+    const unsigned n = min(64u * q + ln, static_cast<unsigned>(FP8_TILE_CHUNKS - 1));
+    const unsigned t = __umul24(n, 3197u) >> 17;  // n / 41 for n < 1312
+    const unsigned c = n - __umul24(t, static_cast<unsigned>(FP8_ROW_CHUNKS));
+    const unsigned row = min(t, static_cast<unsigned>(j1 - 1 - tb));
+    dma16(base, __umul24(row, static_cast<unsigned>(FP8_ROW_BYTES)) + 16u * c,
+          smem_lds + FP8_STAGE + stage * FP8_STAGE_BYTES + q * 1024);
+  };
+  auto fp8_issue_tile = [&](int tb, int stage) {
+    const char* base = tile_base(tb);
+#pragma unroll
+    for (int r = 0; r < COPIES; ++r) fp8_copy(base, tb, stage, r);
+  };
+  // Converts the staged raw rows of a tile into bf16 buffer buf: chunk e (0 .. 2303) of the
+  // bf16 tile is row t = e / 72, logical chunk c = e % 72, stored at position c ^ swz(t);
+  // c < 64 holds latent values 8 c .. 8 c + 7 (8 codes of block c / 16 times that block's
+  // scale), c >= 64 the k^R bytes 16 (c - 64) .. as they are.  Thread tid takes chunks
+  // tid, tid + NT, ...
+  constexpr int CONV = (TILE_CHUNKS + NT - 1) / NT;  // chunks per thread and tile
+  auto fp8_convert_chunk = [&](int stage, int buf, int i) {
+    const lds_char_t* src = lsm + FP8_STAGE + stage * FP8_STAGE_BYTES;
+    lds_char_t* dst = lsm + buf * TILE_BYTES;
+    {
+      int e = tid + NT * i;
+      asm volatile("" : "+v"(e));
+      if (TILE_CHUNKS % NT != 0 && e >= TILE_CHUNKS) return;
+      const unsigned t = __umul24(static_cast<unsigned>(e), 7282u) >> 19;  // e / 72
+      const unsigned c = static_cast<unsigned>(e) - __umul24(t, static_cast<unsigned>(CHUNKS));
+      const lds_char_t* row = src + __umul24(t, static_cast<unsigned>(FP8_ROW_BYTES));
+      i32x4_t v;
+      if (c < 64) {
+        typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+        const u32x2_t codes = *(const __attribute__((address_space(3))) u32x2_t*)(row + 8 * c);
+        const float sc = *(const lds_f32_t*)(row + 640 + 4 * (c >> 4));
+        v[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], sc, false));
+        v[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], sc, true));
+        v[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], sc, false));
+        v[3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], sc, true));
+      } else {
+        v = *(const __attribute__((address_space(3))) i32x4_t*)(row + 512 + 16 * (c - 64));
+      }
+      *(__attribute__((address_space(3))) i32x4_t*)(dst + t * ROW_BYTES + 16 * (c ^ swz(t))) = v;
+    }
+  };
+  auto fp8_convert = [&](int stage, int buf) {
+#pragma unroll
+    for (int i = 0; i < CONV; ++i) fp8_convert_chunk(stage, buf, i);
+  };
   // The copy coordinates do not depend on the tile: the workgroup writes them once to an
   // LDS table, row t << 16 | chunk byte offset, and a copy inside the loop reads its lane's
   // entry there (one LDS read, then clamp and multiply) instead of recomputing them.
   auto table_entry = [&](int r) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    return *((const __attribute__((address_space(3))) uint32_t*)(lsm + VOFF_TABLE) + copy_index(r) * 64 + ln);
+    return FP8 ? 0u : *((const __attribute__((address_space(3))) uint32_t*)(lsm + VOFF_TABLE) + copy_index(r) * 64 + ln);
   };
   auto entry_voff = [&](uint32_t e, unsigned last) {
     return __umul24(min(e >> 16, last), static_cast<unsigned>(ROW_BYTES)) + (e & 0xffffu);
@@ -252,7 +332,7 @@ __device__ __forceinline__ void attn_split(
   // would force a full wait in front of the next tile read.
   auto split_page = [&](int tb) {
     return __builtin_amdgcn_readfirstlane(
-        ((const __attribute__((address_space(3))) int32_t*)(lsm + PAGE_TABLE))[(tb - j0) >> log2P]);
+        ((const __attribute__((address_space(3))) int32_t*)(lsm + PTAB))[(tb - j0) >> log2P]);
   };
   auto score = [&](int it) {
     // The two waves of a SIMD are in different phases; the sequencer favours the older
@@ -260,8 +340,9 @@ __device__ __forceinline__ void attn_split(
     // (K reads, softmax arithmetic, copies) the higher issue priority balances them.
     __builtin_amdgcn_s_setprio(1);
     const int tb = j0 + it * TILE;
-    const lds_char_t* tile = lsm + (it % NBUF) * TILE_BYTES;
+    const lds_char_t* tile = lsm + (it % NB) * TILE_BYTES;
     const int tb2 = copy_tile(it);
+    const bool copy_fp8 = FP8 && it + 2 < ntiles;  // fp8: only real tiles, into staging
     const char* base2 = page_base(split_page(tb2), tb2);
     const unsigned last2 = static_cast<unsigned>(j1 - 1 - tb2);  // rows past it repeat it
     // table reads this many score steps ahead of their copy (0: just before it)
@@ -290,9 +371,13 @@ __device__ __forceinline__ void attn_split(
         sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[step % KRING], qf[kk], sacc[mt], 0, 0, 0);
         if (LEAD == 0 && step > 0 && step % COPY_EVERY == 0 && step / COPY_EVERY < COPIES)
           enext = table_entry(step / COPY_EVERY);
-        if (step % COPY_EVERY == 0 && step / COPY_EVERY < COPIES)
+        if constexpr (FP8) {
+          if (copy_fp8 && step % COPY_EVERY == 0 && step / COPY_EVERY < COPIES)
+            fp8_copy(base2, tb2, (it + 2) & 1, step / COPY_EVERY);
+        } else if (step % COPY_EVERY == 0 && step / COPY_EVERY < COPIES) {
           dma16(base2, entry_voff(enext, last2),
-                smem_lds + ((it + 2) % NBUF) * TILE_BYTES + copy_index(step / COPY_EVERY) * 64 * 16);
+                smem_lds + ((it + 2) % NB) * TILE_BYTES + copy_index(step / COPY_EVERY) * 64 * 16);
+        }
         if (LEAD > 0 && step + LEAD >= COPY_EVERY && (step + LEAD) % COPY_EVERY == 0 &&
             (step + LEAD) / COPY_EVERY < COPIES)
           enext = table_entry((step + LEAD) / COPY_EVERY);
@@ -346,7 +431,7 @@ __device__ __forceinline__ void attn_split(
   // PV of tile it with this wave's P^T operand pt.
   auto pv = [&](int it, bf16x8_t pt) {
     __builtin_amdgcn_s_setprio(0);
-    const lds_char_t* tile = lsm + (it % NBUF) * TILE_BYTES;
+    const lds_char_t* tile = lsm + (it % NB) * TILE_BYTES;
     int ln = lane;
     asm volatile("" : "+v"(ln));  // recomputed per tile (no long live ranges)
     const int gg = ln >> 4, rr = ln & 15;
@@ -434,20 +519,33 @@ __device__ __forceinline__ void attn_split(
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = __builtin_bit_cast(bf16x8_t, r[kk]);
   };
-  issue_tile(j0, 0);
-  for (int e = tid; e < TILE_WAVE_COPIES * 64; e += NT) {
-    const unsigned chunk = static_cast<unsigned>(e);
-    const unsigned t = chunk / CHUNKS, c = (chunk % CHUNKS) ^ swz(t);
-    ((__attribute__((address_space(3))) uint32_t*)(lsm + VOFF_TABLE))[e] = (t << 16) | (c * 16);
-  }
-  for (int e = tid; e * P < j1 - j0; e += NT)  // the pages this split reads
-    ((__attribute__((address_space(3))) int32_t*)(lsm + PAGE_TABLE))[e] = bt_row[(j0 >> log2P) + e];
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // table written before barrier 0
-  if constexpr (COPIES == 5) {
-    load_query_tile1();
-  } else {
+  if constexpr (FP8) {
+    // raw tiles 0 and 1 into the two staging buffers, the block table, the queries (whose
+    // wait covers the copies too); then tile 0 converted before barrier 0
+    fp8_issue_tile(j0, 0);
+    if (ntiles > 1) fp8_issue_tile(j0 + TILE, 1);
+    for (int e = tid; e * P < j1 - j0; e += NT)  // the pages this split reads
+      ((__attribute__((address_space(3))) int32_t*)(lsm + PTAB))[e] = bt_row[(j0 >> log2P) + e];
     load_query();
-    if (ntiles > 1) issue_tile(j0 + TILE, 1);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    block_barrier();
+    fp8_convert(0, 0);
+  } else {
+    issue_tile(j0, 0);
+    for (int e = tid; e < TILE_WAVE_COPIES * 64; e += NT) {
+      const unsigned chunk = static_cast<unsigned>(e);
+      const unsigned t = chunk / CHUNKS, c = (chunk % CHUNKS) ^ swz(t);
+      ((__attribute__((address_space(3))) uint32_t*)(lsm + VOFF_TABLE))[e] = (t << 16) | (c * 16);
+    }
+    for (int e = tid; e * P < j1 - j0; e += NT)  // the pages this split reads
+      ((__attribute__((address_space(3))) int32_t*)(lsm + PTAB))[e] = bt_row[(j0 >> log2P) + e];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // table written before barrier 0
+    if constexpr (COPIES == 5) {
+      load_query_tile1();
+    } else {
+      load_query();
+      if (ntiles > 1) issue_tile(j0 + TILE, 1);
+    }
   }
   // Waves 0 .. NW/2-1 (group 0) take each tile as scores then PV; waves NW/2 .. NW-1
   // (group 1) run half a tile behind, as PV of the previous tile then scores.  A SIMD holds
@@ -456,9 +554,20 @@ __device__ __forceinline__ void attn_split(
   // tile it, copied by every wave, and retires tile it-2, whose buffer the copies of tile it+2
   // overwrite; both groups pass ntiles + 1 barriers.
   auto tile_barrier = [&](int it) {
-    if (it < ntiles) wait_vmcnt<COPIES>();  // own copies of tile it landed
-    else wait_vmcnt<0>();                   // no copy may still be writing LDS at the end
-    block_barrier();
+    if constexpr (FP8) {
+      // the raw tile it+1 (copied during tile it-1) has landed, and the conversion of tile
+      // it (during tile it-1) is in LDS: barrier it publishes both; then this wave converts
+      // its share of tile it+1 (spread over the score steps instead, it costs spills inside
+      // the loop and runs slower)
+      wait_vmcnt<0>();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      block_barrier();
+      if (it + 1 < ntiles) fp8_convert((it + 1) & 1, (it + 1) % NB);
+    } else {
+      if (it < ntiles) wait_vmcnt<COPIES>();  // own copies of tile it landed
+      else wait_vmcnt<0>();                   // no copy may still be writing LDS at the end
+      block_barrier();
+    }
   };
   if (NW == 1 || w < NW / 2) {
     for (int it = 0; it < ntiles; ++it) {
@@ -512,8 +621,8 @@ __device__ __forceinline__ void attn_split(
       }
     }
   } else {
-    split_exact_fallback(q_lat, q_pe, cache, bt_row, log2P, j0, j1, bq, H, prow0, hstride,
-                         scale_log2, o_part, lse_part, h0, 16, lane);
+    split_exact_fallback<OT, FP8>(q_lat, q_pe, cache, bt_row, log2P, j0, j1, bq, H, prow0,
+                                  hstride, scale_log2, o_part, lse_part, h0, 16, lane);
   }
 }
 
@@ -523,7 +632,7 @@ __device__ __forceinline__ void attn_split(
 // B % 8 == 0, so the sequence's queries are fetched once into that XCD's L2.  Token t of n_q
 // sits at position seq_len - n_q + t and sees the cache up to it; its queries and outputs are
 // row bq = b n_q + t, and its workgroups share the sequence's XCD and read the same tiles.
-template <int NW, typename OT>
+template <int NW, typename OT, bool FP8 = false>
 __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
     const bf16raw* __restrict__ q_lat, const bf16raw* __restrict__ q_pe,
     const bf16raw* __restrict__ cache, const int32_t* __restrict__ block_table,
@@ -535,8 +644,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(
   const int L = seq_lens[b] - (n_q - 1 - static_cast<int>(blockIdx.z));
   const int j0 = s * (pages_per_split << log2P);
   const int j1 = min(L, j0 + (pages_per_split << log2P));
-  attn_split<NW, OT>(q_lat, q_pe, cache, block_table, H, log2P, max_pages, scale_log2, o_part,
-                     lse_part, b, bq, j0, j1, static_cast<int64_t>(bq) * H * S + s, S);
+  attn_split<NW, OT, FP8>(q_lat, q_pe, cache, block_table, H, log2P, max_pages, scale_log2,
+                          o_part, lse_part, b, bq, j0, j1, static_cast<int64_t>(bq) * H * S + s, S);
   if (merge_cnt != nullptr)
     merge_splits<NW>(o_part, lse_part, H, S, s, bq, merge_cnt, merge_err, out, lse_out,
                      static_cast<int>(threadIdx.x));
@@ -752,10 +861,10 @@ hipError_t launch_ragged_nw(const PagedArgs& a, int grid, int* seq_slots, int* e
                      : launch_ragged_nw_t<NW, float>(a, grid, seq_slots, err, st);
 }
 
-template <int NW, typename OT>
+template <int NW, typename OT, bool FP8 = false>
 hipError_t launch_nw_t(const PagedArgs& a, hipStream_t st) {
   const float log2e = 1.4426950408889634f;
-  hipLaunchKernelGGL((attn_mfma_kernel<NW, OT>), dim3(a.B, a.num_splits, a.n_q), dim3(NW * 64), 0, st,
+  hipLaunchKernelGGL((attn_mfma_kernel<NW, OT, FP8>), dim3(a.B, a.num_splits, a.n_q), dim3(NW * 64), 0, st,
                      static_cast<const bf16raw*>(a.q_lat), static_cast<const bf16raw*>(a.q_pe),
                      static_cast<const bf16raw*>(a.cache), a.block_table, a.seq_lens, a.H,
                      __builtin_ctz(static_cast<unsigned>(a.page_size)), a.max_pages,
@@ -812,6 +921,13 @@ hipError_t launch_attn_mfma_ragged(const PagedArgs& a, int grid, int* seq_slots,
     case 128: return launch_ragged_nw<8>(a, grid, seq_slots, err, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+bool attn_mfma_fp8_supported(const PagedArgs& a) { return a.H == 128 && attn_mfma_supported(a); }
+
+hipError_t launch_attn_mfma_fp8(const PagedArgs& a, hipStream_t s) {
+  if (a.H != 128) return hipErrorInvalidValue;
+  return a.part_bf16 ? launch_nw_t<8, bf16raw, true>(a, s) : launch_nw_t<8, float, true>(a, s);
 }
 
 hipError_t launch_attn_mfma_bf16_512_64(const PagedArgs& a, hipStream_t s) {

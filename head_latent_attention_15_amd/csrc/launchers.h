@@ -36,6 +36,18 @@ hipError_t launch_attn_generic_bf16_512_64(const PagedArgs& a, hipStream_t s);
 // Decode attention on bf16 MFMA, all heads of a (sequence, split) per workgroup.
 hipError_t launch_attn_mfma_bf16_512_64(const PagedArgs& a, hipStream_t s);
 bool attn_mfma_supported(const PagedArgs& a);
+// The same kernel over fp8 latent rows (656 bytes: 512 E4M3 codes, 64 bf16 k^R, 4 fp32
+// block scales; 128 heads), bf16 queries.
+bool attn_mfma_fp8_supported(const PagedArgs& a);
+hipError_t launch_attn_mfma_fp8(const PagedArgs& a, hipStream_t s);
+// fp8 latent rows: rows of 576 values (bf16 or fp32, row stride src_ld) quantised into
+// 656-byte rows, and the append of new tokens (c^KV quantised, k^R rotated, bf16).
+hipError_t launch_quantize_rows_fp8(const void* src, int src_bf16, int64_t src_ld, int64_t rows,
+                                    void* dst, hipStream_t s);
+hipError_t launch_kv_append_fp8(const float* c_kv, int64_t ld_c, const float* k_r, int64_t ld_k,
+                                int n_new, const int32_t* seq_lens_before,
+                                const int32_t* block_table, void* cache, float base, int B,
+                                int page_size, int max_pages, hipStream_t s);
 // Whole grid of the head-partitioned kernel resident at once on the current device (the
 // condition for its in-launch merge, whose workgroups wait for each other).
 bool attn_mfma_grid_resident(const PagedArgs& a);

@@ -161,7 +161,8 @@ static mla_status_t decode_attn(const void* q_lat, const void* q_pe, const void*
     return fail(MLA_ERR_NULL, "lse_part is NULL with num_splits %d > 1", num_splits);
   if (!std::isfinite(softmax_scale))
     return fail(MLA_ERR_SHAPE, "softmax_scale is not finite");
-  if (!is_dtype(dtype)) return fail(MLA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (!is_dtype(dtype) && dtype != MLA_FP8)
+    return fail(MLA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
   if (!is_dtype(part_dtype))
     return fail(MLA_ERR_UNSUPPORTED, "unknown partial dtype %d", part_dtype);
   if (n_q < 1 || static_cast<int64_t>(shape->batch) * n_q > 65535)
@@ -190,6 +191,18 @@ static mla_status_t decode_attn(const void* q_lat, const void* q_pe, const void*
   hipStream_t s = as_stream(stream);
 
   if (kernel < 0 || kernel > 3) return fail(MLA_ERR_UNSUPPORTED, "attention kernel %d unknown", kernel);
+  if (dtype == MLA_FP8) {
+    if (a.d_c != 512 || a.d_R != 64 || !mla::attn_mfma_fp8_supported(a) || (kernel != 0 && kernel != 1))
+      return fail(MLA_ERR_UNSUPPORTED, "fp8 cache: d_latent 512, d_rope 64, H = 128, pages of "
+                  ">= 32 tokens (a power of two), <= 1024 pages per split, aligned tensors, "
+                  "kernel 0 or 1");
+    const mla_status_t st2 = launched(mla::launch_attn_mfma_fp8(a, s), "attention (fp8 cache)");
+    if (st2 != MLA_OK || merge == nullptr || num_splits == 1) return st2;
+    return launched(mla::launch_splitk_combine(o_part, part_dtype == MLA_BF16, lse_part,
+                                               a.B * n_q, a.H, num_splits, a.d_c, merge->out,
+                                               merge->lse_out, s),
+                    "split-K combine");
+  }
   if (dtype == MLA_BF16 && a.d_c == 512 && a.d_R == 64 && a.H <= 128) {
     const bool cols = mla::attn_cols_supported(a), heads = mla::attn_mfma_supported(a);
     if (kernel == 0) kernel = heads ? 1 : cols ? 2 : 3;
@@ -553,8 +566,18 @@ static mla_status_t kv_append(const char* fn, const float* c_kv, int64_t ld_ckv,
   if (ld_ckv < shape->d_latent || ld_kr < shape->d_rope)
     return fail(MLA_ERR_SHAPE, "%s: row strides %lld / %lld below d_latent / d_rope", fn,
                 static_cast<long long>(ld_ckv), static_cast<long long>(ld_kr));
-  if (!is_dtype(cache_dtype)) return fail(MLA_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  if (!is_dtype(cache_dtype) && cache_dtype != MLA_FP8)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
   if (!std::isfinite(rope_base)) return fail(MLA_ERR_SHAPE, "%s: rope_base", fn);
+  if (cache_dtype == MLA_FP8) {
+    if (shape->d_latent != 512 || shape->d_rope != 64)
+      return fail(MLA_ERR_UNSUPPORTED, "%s: fp8 rows need d_latent 512, d_rope 64", fn);
+    return launched(mla::launch_kv_append_fp8(c_kv, ld_ckv, k_r, ld_kr, n_new, seq_lens_before,
+                                              block_table, kv_cache, rope_base, shape->batch,
+                                              shape->page_size, shape->max_pages_per_seq,
+                                              as_stream(stream)),
+                    "cache append (fp8 rows)");
+  }
   return launched(mla::launch_kv_append(c_kv, ld_ckv, k_r, ld_kr, n_new, seq_lens_before,
                                         block_table, kv_cache, cache_dtype == MLA_BF16, rope_base,
                                         shape->batch, shape->d_latent, shape->d_rope,
@@ -579,6 +602,21 @@ mla_status_t mla_kv_append_strided(const float* c_kv, int64_t ld_ckv, const floa
                                    void* stream) {
   return kv_append("mla_kv_append_strided", c_kv, ld_ckv, k_r, ld_kr, n_new, seq_lens_before,
                    block_table, kv_cache, rope_base, shape, cache_dtype, stream);
+}
+
+mla_status_t mla_quantize_cache(const void* src, mla_dtype_t src_dtype, int64_t src_ld,
+                                int64_t rows, void* dst, void* stream) {
+  if (!src || !dst) return fail(MLA_ERR_NULL, "mla_quantize_cache: a pointer is NULL");
+  if (rows < 1 || src_ld < 576)
+    return fail(MLA_ERR_SHAPE, "mla_quantize_cache: rows %lld < 1 or src_ld %lld < 576",
+                static_cast<long long>(rows), static_cast<long long>(src_ld));
+  if (rows > (static_cast<int64_t>(1) << 33))
+    return fail(MLA_ERR_SHAPE, "mla_quantize_cache: %lld rows", static_cast<long long>(rows));
+  if (!is_dtype(src_dtype))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_quantize_cache: source dtype F32 or BF16");
+  return launched(mla::launch_quantize_rows_fp8(src, src_dtype == MLA_BF16, src_ld, rows, dst,
+                                                as_stream(stream)),
+                  "fp8 row quantisation");
 }
 
 mla_status_t mla_fold_uq(const void* w_uk, const void* w_uq, int32_t H, int32_t d_h,

@@ -60,7 +60,17 @@ typedef enum {
   MLA_ERR_INDEX = 6        /* reserved for index errors found on the host              */
 } mla_status_t;
 
-typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype_t;
+/* MLA_FP8 names a cache format, not an element type: 656-byte rows holding the 512 latent
+ * values as OCP FP8 E4M3 codes (bytes 0..511), the 64 rotated k^R values in bf16 (bytes
+ * 512..639) and four fp32 power-of-two scales, one per 128-value latent block (bytes
+ * 640..655); the value of a code is its E4M3 value times its block's scale.  Block b's
+ * scale is the smallest 2^k with max|x| <= 448 * 2^k (1 for an all-zero block) and a code
+ * the E4M3 value nearest to x / 2^k, ties to the even code.  The pages name KV-cache
+ * quantisation alongside MLA but fix no format (kasblo.com/?p=4663, "GQA・量子化・
+ * FlashAttentionとは何が違うのか"); this one makes dequantisation exact in bf16.  Accepted as
+ * the cache dtype of mla_kv_append*, mla_quantize_cache and mla_decode_attn* (with BF16
+ * queries, 128 heads, d_latent 512, d_rope 64). */
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_FP8 = 2 } mla_dtype_t;
 
 typedef struct {
   int32_t batch;             /* B: sequences                                        */
@@ -152,6 +162,14 @@ mla_status_t mla_kv_append_strided(const float* c_kv, int64_t ld_ckv, const floa
                                    const mla_paged_shape_t* shape, mla_dtype_t cache_dtype,
                                    void* stream);
 
+/* fp8 latent rows (MLA_FP8) from rows of 576 values: dst row r = the quantised row r of
+ * src (src + r * src_ld, src_dtype F32 or BF16; latent then k^R).  The latent is quantised
+ * as MLA_FP8 describes; k^R is rounded to bf16 (exact for BF16 input).  rows >= 1; src_ld
+ * >= 576.  The codes follow from the values alone (every step is exact in fp32).
+ * Errors: NULL, SHAPE, UNSUPPORTED (src_dtype). */
+mla_status_t mla_quantize_cache(const void* src, mla_dtype_t src_dtype, int64_t src_ld,
+                                int64_t rows, void* dst, void* stream);
+
 /* Decode attention over the paged latent cache, split over tokens.
  * For every sequence b, head i and split s (s = 0..num_splits-1), with
  * cps = ceil(max_pages_per_seq / num_splits) pages per split, split s covers the cached
@@ -161,15 +179,18 @@ mla_status_t mla_kv_append_strided(const float* c_kv, int64_t ld_ckv, const floa
  *   lse_part[b][i][s]  = ln sum_j e^{score_j}
  * (qiita "Attention 計算" in the absorbed order; kasblo "V側は…" for the latent sum).
  * A split with no tokens writes o = 0 and lse = -inf.
- *   q_lat [B][H][d_latent], q_pe [B][H][d_rope]: `dtype` (q_pe already rotated)
- *   kv_cache: `dtype`;  block_table [B][max_pages_per_seq], seq_lens [B]: int32, device
+ *   q_lat [B][H][d_latent], q_pe [B][H][d_rope]: `dtype` (q_pe already rotated), BF16
+ *   when dtype is MLA_FP8
+ *   kv_cache: `dtype` (MLA_FP8: 656-byte rows, the values dequantised exactly);
+ *   block_table [B][max_pages_per_seq], seq_lens [B]: int32, device
  *   o_part [B][H][S][d_latent] in part_dtype (F32, or BF16 rounded to nearest even: half
  *   the partial traffic; the softmax sums and the PV accumulation stay fp32);
  *   lse_part [B][H][S] fp32.
  *   With num_splits == 1, o_part is the final o~ [B][H][d_latent] and lse_part may be NULL.
  * softmax_scale is normally 1/sqrt(d_h + d_R) (1/sqrt(192) at DeepSeek-V2 shape).
- * Supported: (d_latent, d_rope, dtype) = (512, 64, BF16) with H <= 128, or
- * (64, 16, F32) with H <= 64; otherwise UNSUPPORTED.
+ * Supported: (d_latent, d_rope, dtype) = (512, 64, BF16) with H <= 128, (512, 64, FP8)
+ * with H = 128 (the head-partitioned kernel, staging raw rows and converting them to bf16
+ * in LDS), or (64, 16, F32) with H <= 64; otherwise UNSUPPORTED.
  * Errors: NULL, SHAPE (sizes < 1, page_size % 16, odd d_rope, num_splits < 1,
  * seq_lens bound max_pages_per_seq*page_size does not fit int32), UNSUPPORTED. */
 mla_status_t mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_cache,

@@ -52,31 +52,27 @@ def e4m3_value(code: int) -> float:
 
 
 def e4m3_decode(codes) -> np.ndarray:
+    """Values of E4M3 codes: e4m3_value looked up per code."""
     codes = np.asarray(codes, dtype=np.uint8)
-    return np.vectorize(e4m3_value, otypes=[F64])(codes) if codes.size else codes.astype(F64)
-
-
-# the 127 non-negative finite values, codes 0x00 .. 0x7E, in increasing order
-_POS_CODES = np.arange(0x7F, dtype=np.uint8)
-_POS_VALUES = np.array([e4m3_value(c) for c in _POS_CODES], dtype=F64)
+    table = np.array([e4m3_value(c) for c in range(256)], dtype=F64)
+    return table[codes]
 
 
 def e4m3_encode(x) -> np.ndarray:
     """Nearest E4M3 code to each value (ties to the even code), magnitudes past 448
-    saturating to +-448, NaN to 0x7F.  Brute force over the non-negative grid."""
+    saturating to +-448, NaN to 0x7F.  The two grid neighbours of |x| among the 127
+    non-negative finite values (codes 0x00 .. 0x7E, increasing with the code) are compared."""
+    grid = e4m3_decode(np.arange(0x7F, dtype=np.uint8))
     x = np.asarray(x, dtype=F64)
-    out = np.empty(x.shape, dtype=np.uint8)
-    flat, res = x.reshape(-1), out.reshape(-1)
-    for n, v in enumerate(flat):
-        if math.isnan(v):
-            res[n] = 0x7F
-            continue
-        a = min(abs(v), E4M3_MAX)
-        d = np.abs(_POS_VALUES - a)
-        best = np.flatnonzero(d == d.min())
-        code = int(best[0]) if len(best) == 1 else int(best[best % 2 == 0][0])
-        res[n] = code | (0x80 if math.copysign(1.0, v) < 0 else 0)
-    return out
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    a = np.where(np.isnan(x), 0.0, a)
+    hi = np.clip(np.searchsorted(grid, a, side="left"), 0, 0x7E)  # first grid value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - grid[lo], grid[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
 
 
 def block_scale(block) -> float:
@@ -98,11 +94,9 @@ def quantize_latent(latent):
     lead = latent.shape[:-1]
     blocks = latent.reshape(lead + (LATENT // BLOCK, BLOCK))
     scales = np.empty(lead + (LATENT // BLOCK,), dtype=F64)
-    codes = np.empty(blocks.shape, dtype=np.uint8)
     for idx in np.ndindex(*blocks.shape[:-1]):
-        s = block_scale(blocks[idx])
-        scales[idx] = s
-        codes[idx] = e4m3_encode(blocks[idx] / s)
+        scales[idx] = block_scale(blocks[idx])
+    codes = e4m3_encode(blocks / scales[..., None])
     return codes.reshape(lead + (LATENT,)), scales
 
 
