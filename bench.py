@@ -515,6 +515,8 @@ def main():
     ap.add_argument("--layer-only", action="store_true",
                     help="run only the full-layer measurement and print its JSON (for profiling "
                          "the layer's kernels)")
+    ap.add_argument("--config", choices=["long_b4_t32k", "ragged_b128"], default=None,
+                    help="run only this workload line and print its JSON (for a kernel trace)")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline step and its attention alone (for a kernel "
                          "trace of exactly those launches)")
@@ -543,6 +545,14 @@ def main():
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
     num_cus = props.multi_processor_count
+    if args.config is not None:
+        log(f"{args.config} only")
+        gen = {"long_b4_t32k": (W.long_b4_t32k, N_CACHE_COPIES, False),
+               "ragged_b128": (W.ragged_b128, 2, True)}[args.config]
+        row = config_row(mla, torch, gen[0](), args.config, num_cus, args.steps, gen[1],
+                         flattened=gen[2])
+        print(json.dumps({args.config: row}), flush=True)
+        return
     if args.layer_only:
         log("layer_b64_t2k only")
         print(json.dumps({"layer_b64_t2k": layer_rows(mla, W, torch, 0)}), flush=True)

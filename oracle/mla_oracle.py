@@ -139,6 +139,45 @@ def expanded_decode(q_c, q_pe, c_kv, k_pe, w_uk, w_uv, scale, w_o=None):
     return out
 
 
+def causal_attention(q, k, v, scale):
+    """Causal softmax attention for a prompt, per head ([qiita] "Attention 計算": the sum for
+    query t runs over j <= t, o_t = sum_j softmax_j(q_t . k_j * scale) v_j).
+
+    q [T, H, d_qk], k [T, H, d_qk], v [T, H, d_v] -> (o [T, H, d_v], lse [T, H]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, H, _ = q.shape
+    o = np.empty((T, H, v.shape[-1]), dtype=F64)
+    lse = np.empty((T, H), dtype=F64)
+    visible = np.tril(np.ones((T, T), dtype=bool))   # [t, j]: j <= t
+    for i in range(H):
+        s = (q[:, i] @ k[:, i].T) * scale              # [T, T]
+        s = np.where(visible, s, -np.inf)
+        o[:, i] = softmax(s, axis=-1) @ v[:, i]
+        lse[:, i] = logsumexp(s, axis=-1)
+    return o, lse
+
+
+def expanded_prefill(q_c, q_pe, c_kv, k_pe, w_uk, w_uv, scale):
+    """A prompt of T tokens through the expanded path, causal ([perforder]
+    "極限最適化の代償" and [kasblo] "「キャッシュを減らせた」と「その割合だけ速い」は別の評価":
+    for many query tokens the up-projected keys and values are the natural order).
+
+    q_c [T, H, d_h], q_pe [T, H, d_R] (rotated), c_kv [T, d_c], k_pe [T, d_R] (rotated),
+    w_uk, w_uv [H*d_h, d_c] -> (o [T, H, d_h], lse [T, H]).
+    """
+    q_c, q_pe = _f64(q_c), _f64(q_pe)
+    T, H, d_h = q_c.shape
+    k = np.empty((T, H, d_h + q_pe.shape[-1]), dtype=F64)
+    v = np.empty((T, H, d_h), dtype=F64)
+    for i in range(H):
+        k[:, i, :d_h] = _f64(c_kv) @ head_block(w_uk, i, d_h).T
+        k[:, i, d_h:] = _f64(k_pe)
+        v[:, i] = _f64(c_kv) @ head_block(w_uv, i, d_h).T
+    q = np.concatenate([q_c, q_pe], axis=-1)
+    return causal_attention(q, k, v, scale)
+
+
 # --------------------------------------------------------------------------------------
 # Absorbed form, fp64 (used only to check that absorption changes nothing)
 # --------------------------------------------------------------------------------------

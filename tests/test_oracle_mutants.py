@@ -37,6 +37,8 @@ PIN_TESTS = [
     pins.test_layer_matches_sdpa_composition,
     pins.test_cache_sizes_from_pages,
     pins.test_default_scale,
+    pins.test_causal_attention_is_masked_sdpa,
+    pins.test_expanded_prefill_rows_are_decodes,
 ]
 
 
@@ -137,6 +139,30 @@ M_rope_orig = M.rope
 M_softmax_orig = M.softmax
 M_lse_orig = M.logsumexp
 
+M_causal_orig = M.causal_attention
+
+
+def _causal_misses_itself(q, k, v, scale):
+    """each query sees only the tokens strictly before it (and the first one itself)"""
+    q, k, v = (np.asarray(a, float) for a in (q, k, v))
+    T, H, _ = q.shape
+    o = np.empty((T, H, v.shape[-1]))
+    lse = np.empty((T, H))
+    vis = np.tril(np.ones((T, T), dtype=bool), -1)
+    vis[0, 0] = True
+    for i in range(H):
+        s = np.where(vis, (q[:, i] @ k[:, i].T) * scale, -np.inf)
+        o[:, i] = M.softmax(s, axis=-1) @ v[:, i]
+        lse[:, i] = M.logsumexp(s, axis=-1)
+    return o, lse
+
+
+def _causal_future(q, k, v, scale):
+    """mask transposed: each query sees the tokens at and after it"""
+    o, lse = M_causal_orig(np.asarray(q)[::-1], np.asarray(k)[::-1], np.asarray(v)[::-1], scale)
+    return o[::-1], lse[::-1]
+
+
 MUTANTS = {
     "rope_clockwise": ("rope", _rope_clockwise),
     "rope_wrong_frequency": ("rope", _rope_wrong_freq),
@@ -153,6 +179,8 @@ MUTANTS = {
     "multi_query_not_causal": ("paged_decode_multi", _multi_decode(lambda L, n, t: L)),
     "multi_query_tokens_reversed": ("paged_decode_multi",
                                     _multi_decode(lambda L, n, t: L - t)),
+    "causal_misses_itself": ("causal_attention", _causal_misses_itself),
+    "causal_sees_future": ("causal_attention", _causal_future),
 }
 
 

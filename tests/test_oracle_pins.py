@@ -412,3 +412,41 @@ def test_default_scale():
     """1/sqrt(d_h + d_R): 1/sqrt(192) at DeepSeek-V2 shape, not 1/sqrt(576)."""
     assert oracle.default_scale(128, 64) == 1 / math.sqrt(192)
     assert oracle.default_scale(32, 16) == 1 / math.sqrt(48)
+
+
+# ---- prefill in the expanded form -----------------------------------------------------
+
+def test_causal_attention_is_masked_sdpa():
+    """causal_attention equals torch's SDPA with its causal mask, in fp64 (library routine)."""
+    rng = np.random.default_rng(40)
+    T, H = 37, 5
+    q = rng.standard_normal((T, H, 24))
+    k = rng.standard_normal((T, H, 24))
+    v = rng.standard_normal((T, H, 7))
+    o, lse = oracle.causal_attention(q, k, v, 0.25)
+    t = lambda a: torch.from_numpy(a).transpose(0, 1)
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=True,
+                                                           scale=0.25).transpose(0, 1).numpy()
+    assert np.max(np.abs(o - ref)) <= 1e-12
+    # lse of the visible scores: row 0 sees only itself
+    assert np.allclose(lse[0], np.einsum("hd,hd->h", q[0], k[0]) * 0.25, atol=1e-12)
+
+
+def test_expanded_prefill_rows_are_decodes():
+    """Query t of a prompt is the decode of the prompt's first t + 1 tokens: every row of
+    expanded_prefill equals expanded_decode over that prefix."""
+    rng = np.random.default_rng(41)
+    T, H, d_h, d_c, d_R = 11, 3, 8, 16, 4
+    q_c = rng.standard_normal((T, H, d_h))
+    q_pe = rng.standard_normal((T, H, d_R))
+    c_kv = rng.standard_normal((T, d_c))
+    k_pe = rng.standard_normal((T, d_R))
+    w_uk = rng.standard_normal((H * d_h, d_c)) / 4
+    w_uv = rng.standard_normal((H * d_h, d_c)) / 4
+    o, lse = oracle.expanded_prefill(q_c, q_pe, c_kv, k_pe, w_uk, w_uv, 0.3)
+    for t in (0, 1, 5, T - 1):
+        dec = oracle.expanded_decode(q_c[t], q_pe[t], c_kv[:t + 1], k_pe[:t + 1], w_uk, w_uv, 0.3)
+        assert np.max(np.abs(o[t] - dec["o"])) <= 1e-12
+        assert np.max(np.abs(lse[t] - dec["lse"])) <= 1e-12
+    # the first token sees only itself: its values
+    assert np.allclose(o[0], np.stack([c_kv[0] @ w_uv[i * d_h:(i + 1) * d_h].T for i in range(H)]))
