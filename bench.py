@@ -408,6 +408,31 @@ def fp8_rows(mla, torch, inp, num_cus, steps, n_copies):
             "query_tokens_per_s": round(B / (step_ms * 1e-3), 1)}
 
 
+def prefill_row(mla, torch, steps, T=4096, H=128):
+    """Prefill attention in the expanded form (mla_prefill_attn) over one prompt of T tokens
+    with H heads: q^C, k^C, v^C [T, H, 128], q_pe [T, H, 64], k_pe [T, 64], seeded bf16, resident
+    in HBM.  Matrix-core bound: causal flops = H * T (T + 1) / 2 * (192 + 128) * 2, reported
+    against the 2.5 PF bf16 dense peak."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(7)
+    mk = lambda *shape: torch.randn(*shape, generator=g).to(torch.bfloat16).to(dev)
+    q_c, q_pe, k_c, v_c = mk(1, T, H, 128), mk(1, T, H, 64), mk(1, T, H, 128), mk(1, T, H, 128)
+    k_pe = mk(1, T, 64)
+    out = torch.empty(1, T, H, 128, device=dev)
+    call = mla.bind(mla.mla_prefill_attn, q_c, q_pe, k_c, k_pe, v_c, 1.0 / math.sqrt(192), out)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.3:
+        call()
+        torch.cuda.synchronize()
+    ms = timed_ms(torch, lambda k: call(), max(5, steps // 5))
+    flops = H * T * (T + 1) / 2 * (192 + 128) * 2
+    return {"workload": f"prefill_t{T}_h{H} (one prompt, expanded form, causal)",
+            "T": T, "H": H, "us": round(ms * 1e3, 1),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac_of_peak": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "prompt_tokens_per_s": round(T / (ms * 1e-3), 1)}
+
+
 def config_row(mla, torch, inp, name, num_cus, steps, n_copies, kernel="auto", flattened=False):
     """One attention workload beside the headline, back to back over n_copies rotating
     caches: the split-grid step (attention + combine, bf16 partials), its attention alone,
@@ -726,6 +751,8 @@ def main():
                                            args.steps, 2, flattened=True)
     log("timing the headline workload over fp8 latent rows")
     result["fp8_cache"] = fp8_rows(mla, torch, inp, num_cus, args.steps, N_CACHE_COPIES)
+    log("timing prefill attention (expanded form, T=4096, H=128)")
+    result["prefill"] = prefill_row(mla, torch, args.steps)
     log("timing multi-token decode (2 query tokens per sequence)")
     caches = [inp["cache"].to(dev)]
     for _ in range(N_CACHE_COPIES - 1):

@@ -71,6 +71,8 @@ _SIGNATURES = {
     "mla_splitk_combine": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "mla_fold_uq": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P]),
     "mla_quantize_cache": (_I32, [_P, _I32, _I64, _I64, _P, _P]),
+    "mla_prefill_attn": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F, _P, _P, _I32,
+                                _P]),
     "mla_fold_o_uv": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P]),
     "mla_combine_out_proj": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _I32, _I32, _P,
                                     _P]),
@@ -591,6 +593,27 @@ def mla_quantize_cache(src, dst, stream=None):
     _expect(src.is_contiguous(), "src must be contiguous")
     _invoke("mla_quantize_cache", _dev(src, "src"), _dtype_code(src), 576, rows,
             _dev(dst, "dst", torch.uint8), _stream(stream))
+
+
+def mla_prefill_attn(q_c, q_pe, k_c, k_pe, v_c, softmax_scale, out, lse_out=None, stream=None):
+    """Causal prefill attention, expanded form: q_c, k_c, v_c [B,T,H,d_h], q_pe [B,T,H,d_R],
+    k_pe [B,T,d_R] (bf16); out [B,T,H,d_h] fp32, lse_out [B,T,H] or None."""
+    torch = _torch()
+    B, T, H, d_h = q_c.shape
+    d_R = q_pe.shape[-1]
+    _expect(tuple(q_pe.shape) == (B, T, H, d_R), "q_pe must be [B,T,H,d_R]")
+    _expect(tuple(k_c.shape) == (B, T, H, d_h) and tuple(v_c.shape) == (B, T, H, d_h),
+            "k_c and v_c must be [B,T,H,d_h]")
+    _expect(tuple(k_pe.shape) == (B, T, d_R), "k_pe must be [B,T,d_R]")
+    _expect(tuple(out.shape) == (B, T, H, d_h), "out must be [B,T,H,d_h]")
+    if lse_out is not None:
+        _expect(tuple(lse_out.shape) == (B, T, H), "lse_out must be [B,T,H]")
+    for t in (q_pe, k_c, k_pe, v_c):
+        _expect(t.dtype == q_c.dtype, "inputs share a dtype")
+    _invoke("mla_prefill_attn", _dev(q_c, "q_c"), _dev(q_pe, "q_pe"), _dev(k_c, "k_c"),
+            _dev(k_pe, "k_pe"), _dev(v_c, "v_c"), B, T, H, d_h, d_R, float(softmax_scale),
+            _dev(out, "out", torch.float32), _dev(lse_out, "lse_out", torch.float32),
+            _dtype_code(q_c), _stream(stream))
 
 
 def mla_splitk_combine(o_part, lse_part, out, lse_out=None, stream=None):

@@ -48,6 +48,13 @@ hipError_t launch_kv_append_fp8(const float* c_kv, int64_t ld_c, const float* k_
                                 int n_new, const int32_t* seq_lens_before,
                                 const int32_t* block_table, void* cache, float base, int B,
                                 int page_size, int max_pages, hipStream_t s);
+// Causal prefill attention in the expanded form (d_h = 128, d_R = 64, bf16 inputs):
+// q_c [B][T][H][128], q_pe [B][T][H][64], k_c [B][T][H][128], k_pe [B][T][64] (shared by the
+// heads), v_c [B][T][H][128]; out [B][T][H][128] fp32, lse_out [B][T][H] or NULL.
+bool attn_prefill_supported(int d_h, int d_R);
+hipError_t launch_attn_prefill(const void* q_c, const void* q_pe, const void* k_c,
+                               const void* k_pe, const void* v_c, int B, int T, int H,
+                               float scale, float* out, float* lse_out, hipStream_t s);
 // Whole grid of the head-partitioned kernel resident at once on the current device (the
 // condition for its in-launch merge, whose workgroups wait for each other).
 bool attn_mfma_grid_resident(const PagedArgs& a);

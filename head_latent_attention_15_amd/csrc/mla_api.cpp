@@ -604,6 +604,29 @@ mla_status_t mla_kv_append_strided(const float* c_kv, int64_t ld_ckv, const floa
                    block_table, kv_cache, rope_base, shape, cache_dtype, stream);
 }
 
+mla_status_t mla_prefill_attn(const void* q_c, const void* q_pe, const void* k_c,
+                              const void* k_pe, const void* v_c, int32_t B, int32_t T,
+                              int32_t H, int32_t d_h, int32_t d_R, float softmax_scale,
+                              float* out, float* lse_out, mla_dtype_t dtype, void* stream) {
+  if (!q_c || !q_pe || !k_c || !k_pe || !v_c || !out)
+    return fail(MLA_ERR_NULL, "mla_prefill_attn: a required pointer is NULL");
+  if (B < 1 || T < 1 || H < 1 || d_h < 1 || d_R < 1)
+    return fail(MLA_ERR_SHAPE, "mla_prefill_attn: sizes must be >= 1");
+  if (B > 65535 || H > 65535 || static_cast<int64_t>(B) * T * H * d_h > (static_cast<int64_t>(1) << 40))
+    return fail(MLA_ERR_SHAPE, "mla_prefill_attn: B %d, H %d or the prompt is too large", B, H);
+  if (!std::isfinite(softmax_scale))
+    return fail(MLA_ERR_SHAPE, "mla_prefill_attn: softmax_scale is not finite");
+  if (dtype != MLA_BF16 || !mla::attn_prefill_supported(d_h, d_R))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_attn: BF16 inputs, d_h 128, d_R 64");
+  const uintptr_t any = reinterpret_cast<uintptr_t>(q_c) | reinterpret_cast<uintptr_t>(q_pe) |
+                        reinterpret_cast<uintptr_t>(k_c) | reinterpret_cast<uintptr_t>(k_pe) |
+                        reinterpret_cast<uintptr_t>(v_c) | reinterpret_cast<uintptr_t>(out);
+  if (any & 15) return fail(MLA_ERR_SHAPE, "mla_prefill_attn: tensors must be 16-byte aligned");
+  return launched(mla::launch_attn_prefill(q_c, q_pe, k_c, k_pe, v_c, B, T, H, softmax_scale,
+                                           out, lse_out, as_stream(stream)),
+                  "prefill attention");
+}
+
 mla_status_t mla_quantize_cache(const void* src, mla_dtype_t src_dtype, int64_t src_ld,
                                 int64_t rows, void* dst, void* stream) {
   if (!src || !dst) return fail(MLA_ERR_NULL, "mla_quantize_cache: a pointer is NULL");

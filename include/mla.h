@@ -162,6 +162,27 @@ mla_status_t mla_kv_append_strided(const float* c_kv, int64_t ld_ckv, const floa
                                    const mla_paged_shape_t* shape, mla_dtype_t cache_dtype,
                                    void* stream);
 
+/* Prefill attention in the expanded form: T prompt tokens per sequence attend causally to
+ * the prompt through the up-projected keys and values (for many query tokens the pages give
+ * the naive order: [perforder] "極限最適化の代償：MLA特有の学習負荷と独自Tritonカーネルという
+ * 障壁"; kasblo.com/?p=4663, "「キャッシュを減らせた」と「その割合だけ速い」は別の評価").
+ * With k^C_{j,i} = W^UK_i c_j and v^C_{j,i} = W^UV_i c_j computed over the prompt (two
+ * mla_linear products), for every sequence b, query t and head i:
+ *   s_tj = softmax_scale * ([q_c; q_pe][b][t][i] . [k_c[b][j][i]; k_pe[b][j]]),  j <= t
+ *   out[b][t][i][:] = sum_j softmax_j(s_tj) v_c[b][j][i][:];  lse_out[b][t][i] = ln sum_j e^s
+ * (qiita.com/joule/items/57d9b3f4fc27959eaa0d, "Attention 計算": the sum runs to the query's
+ * own position; "論文解説: DeepSeek-V2 …", "Decoupled RoPE": k^R is shared by the heads).
+ *   q_c [B][T][H][d_h], q_pe [B][T][H][d_R] (rotated), k_c [B][T][H][d_h],
+ *   k_pe [B][T][d_R] (rotated), v_c [B][T][H][d_h]: BF16, 16-byte aligned
+ *   out [B][T][H][d_h] fp32 (16-byte aligned); lse_out [B][T][H] fp32 or NULL
+ * Supported: d_h = 128, d_R = 64, BF16 (bf16 MFMA; the weights P are rounded to bf16 for
+ * the value product and the denominators sum those rounded weights).
+ * Errors: NULL, SHAPE, UNSUPPORTED. */
+mla_status_t mla_prefill_attn(const void* q_c, const void* q_pe, const void* k_c,
+                              const void* k_pe, const void* v_c, int32_t B, int32_t T,
+                              int32_t H, int32_t d_h, int32_t d_R, float softmax_scale,
+                              float* out, float* lse_out, mla_dtype_t dtype, void* stream);
+
 /* fp8 latent rows (MLA_FP8) from rows of 576 values: dst row r = the quantised row r of
  * src (src + r * src_ld, src_dtype F32 or BF16; latent then k^R).  The latent is quantised
  * as MLA_FP8 describes; k^R is rounded to bf16 (exact for BF16 input).  rows >= 1; src_ld
