@@ -127,13 +127,14 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     roofline (every step is HBM-bound at this batch); then the whole chain, and the fp64
     oracle's layer on a few of the sequences.  The projections that share an input run as
     one product over their stacked weights ([W^DQ; W^DKV; W^KR] h, [W^UQ; W^QR] c^Q; the
-    weights are stacked once at load time, outside the timing), the append and the
-    absorption read their inputs in place, the split-K combine is fused with W^UV, and in
-    the timed chain the products accumulate into outputs cleared by one fill at its start.
-    Timed beside it: the chain with dense outputs (each product zeroing its own), the chain
-    with the combine and W^UV as two launches, and the chain of separate products.  The
-    fused step's algorithmic bytes are W^UV and its output: the combined latent is never
-    stored."""
+    weights are stacked once at load time, outside the timing), the append reads its inputs
+    in place, the query side ([W^UQ; W^QR] c^Q, RoPE, absorption) is one launch reading c^Q in
+    place (its weights packed once at load time, outside the timing), the split-K combine is fused with W^UV, and in the timed chain the products
+    accumulate into outputs cleared by one fill at its start.  Timed beside it: the chain
+    with the query side as two launches (the stacked product, then the absorption), with
+    dense outputs (each product zeroing its own), with the combine and W^UV as two
+    launches, and the chain of separate products.  The fused steps' algorithmic bytes are
+    their weights, inputs and outputs: q^C, q^R and the combined latent are never stored."""
     x = W.layer_b64_t2k()
     s = x["shape"]
     B, H, d_h, d_c, d_R, d, d_cq = s.B, s.H, s.d_h, s.d_c, s.d_R, x["d"], x["d_cq"]
@@ -141,12 +142,13 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     w = {k: cu(v) for k, v in x["weights"].items()}
     w_a = torch.cat([w["w_dq"], w["w_dkv"], w["w_kr"]]).contiguous()
     w_b = torch.cat([w["w_uq"], w["w_qr"]]).contiguous()
+    w_pack = mla.mla_pack_query_weights(w["w_uq"], w["w_qr"], H)  # load-time packing
     h, cache, bt, before = cu(x["h"]), cu(x["cache"]), cu(x["block_table"]), cu(x["seq_lens_before"])
     f32 = dict(device="cuda", dtype=torch.float32)
     n_a, n_b = d_cq + d_c + d_R, H * (d_h + d_R)
-    outs = torch.empty(B * (n_a + n_b + d), **f32)  # y_a, y_b and u, cleared by one fill
-    y_a, y_b = outs[:B * n_a].view(B, n_a), outs[B * n_a:B * (n_a + n_b)].view(B, n_b)
-    u = outs[B * (n_a + n_b):].view(B, d)
+    outs = torch.empty(B * (n_a + d), **f32)  # y_a and u, cleared by one fill
+    y_a, u = outs[:B * n_a].view(B, n_a), outs[B * n_a:].view(B, d)
+    y_b = torch.empty(B, n_b, **f32)            # q^C | q^R of the two-launch query side
     c_q, c_kv, k_r = y_a[:, :d_cq], y_a[:, d_cq:d_cq + d_c], y_a[:, d_cq + d_c:]
     q_c, q_r = y_b[:, :H * d_h].view(B, H, d_h), y_b[:, H * d_h:].view(B, H, d_R)
     seq_lens = before + 1
@@ -162,14 +164,13 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     rows = [
         ("7 mla_linear [W^DQ; W^DKV; W^KR] h",
          [mla.bind(mla.mla_linear, h, w_a, y_a)], nb(w_a) + nb(h) + nb(y_a)),
-        ("7 mla_linear_strided [W^UQ; W^QR] c^Q",
-         [mla.bind(mla.mla_linear_strided, c_q, w_b, y_b)], nb(w_b) + B * d_cq * 4 + nb(y_b)),
         ("2 mla_kv_append_strided", [mla.bind(mla.mla_kv_append_strided, c_kv.unsqueeze(1),
                                               k_r.unsqueeze(1), before, bt, cache, x["rope_base"])],
          B * (d_c + d_R) * 4 + B * (d_c + d_R) * 2),
-        ("1 mla_absorb_q_strided", [mla.bind(mla.mla_absorb_q_strided, q_c, w["w_uk"], q_r, seq_lens,
-                                             x["rope_base"], q_lat, q_pe)],
-         nb(w["w_uk"]) + B * H * (d_h + d_R) * 4 + nb(q_lat) + nb(q_pe)),
+        ("7+1 mla_query_path (W^UQ, W^QR, RoPE, absorption in one launch)",
+         [mla.bind(mla.mla_query_path, c_q, w_pack, w["w_uk"], seq_lens, x["rope_base"],
+                   q_lat, q_pe)],
+         nb(w_b) + nb(w["w_uk"]) + B * d_cq * 4 + nb(q_lat) + nb(q_pe)),
         (f"3 mla_decode_attn ({S} splits, bf16 partials)",
          [mla.bind(mla.mla_decode_attn, q_lat, q_pe, cache, bt, seq_lens, x["scale"], S, o_part,
                    lse_part)],
@@ -181,11 +182,19 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
          [mla.bind(mla.mla_linear, o_heads.view(B, H * d_h), w["w_o"], u)],
          nb(w["w_o"]) + nb(o_heads) + nb(u)),
     ]
+    # the query side as two launches: the stacked product [W^UQ; W^QR] c^Q, then the
+    # absorption (with the RoPE) reading q^C and q^R in place
+    two_launch_query = [
+        ("7 mla_linear_strided [W^UQ; W^QR] c^Q",
+         mla.bind(mla.mla_linear_strided, c_q, w_b, y_b), nb(w_b) + B * d_cq * 4 + nb(y_b)),
+        ("1 mla_absorb_q_strided",
+         mla.bind(mla.mla_absorb_q_strided, q_c, w["w_uk"], q_r, seq_lens, x["rope_base"], q_lat,
+                  q_pe), nb(w["w_uk"]) + B * H * (d_h + d_R) * 4 + nb(q_lat) + nb(q_pe))]
     # attention + combine (o~ written to HBM), then W^UV on it, then W^O
     unfused_back = [
         mla.bind(mla.mla_decode, q_lat, q_pe, cache, bt, seq_lens, x["scale"], S, ws, o_lat),
         mla.bind(mla.mla_out_proj, o_lat, w["w_uv"], None, o_heads),
-        rows[6][1][0]]
+        rows[5][1][0]]
     # the same layer with one product per weight and dense intermediates
     sep = {k: torch.empty(B, n, **f32) for k, n in
            (("c_q", d_cq), ("q_c", H * d_h), ("q_r", H * d_R), ("c_kv", d_c), ("k_r", d_R))}
@@ -205,23 +214,24 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     # the same calls with the products accumulating into outputs cleared together by one
     # fill at the start of the layer (y_a, y_b and u share one buffer), so the split-k kernels
     # launch no zero fills of their own: two kernels fewer on the one stream
-    acc_chain = ([mla.bind(mla.mla_linear_strided, h, w_a, y_a, accumulate=True),
-                  mla.bind(mla.mla_linear_strided, c_q, w_b, y_b, accumulate=True)]
-                 + [rows[i][1][0] for i in (2, 3, 4, 5)]
+    acc_chain = ([mla.bind(mla.mla_linear_strided, h, w_a, y_a, accumulate=True)]
+                 + [rows[i][1][0] for i in (1, 2, 3, 4)]
                  + [mla.bind(mla.mla_linear_strided, o_heads.view(B, H * d_h), w["w_o"], u,
                              accumulate=True)])
 
-    def accumulate_chain():
-        outs.zero_()
-        for c in acc_chain:
-            c()
+    def run_with_fill(calls):
+        def go():
+            outs.zero_()
+            for c in calls:
+                c()
+        return go
 
-    unfused_chain = acc_chain[:4] + unfused_back[:2] + acc_chain[6:]
-
-    def accumulate_unfused():
-        outs.zero_()
-        for c in unfused_chain:
-            c()
+    accumulate_chain = run_with_fill(acc_chain)
+    # attention + combine, then W^UV: two launches in place of the fused one
+    accumulate_unfused = run_with_fill(acc_chain[:3] + unfused_back[:2] + acc_chain[5:])
+    # the query side as two launches in place of mla_query_path
+    accumulate_two_launch = run_with_fill(acc_chain[:2] + [c for _, c, _ in two_launch_query]
+                                          + acc_chain[3:])
 
     for c in chain:
         c()
@@ -230,12 +240,16 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     accumulate_chain()
     torch.cuda.synchronize()
     acc_vs_dense = float((u - u_dense).abs().max() / u_dense.abs().max())
+    accumulate_two_launch()
+    torch.cuda.synchronize()
+    two_vs_one = float((u - u_dense).abs().max() / u_dense.abs().max())
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < 0.3:
         for c in chain + separate:
             c()
         accumulate_chain()
         accumulate_unfused()
+        accumulate_two_launch()
         torch.cuda.synchronize()
 
     def timed(fn, n=20):
@@ -256,10 +270,19 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
         out[name] = {"us": round(us, 2), "bytes_algorithmic": int(byts), "GBps": round(gbps, 1),
                      "roofline_frac": round(gbps / HBM_PEAK_GBPS, 4)}
         total_bytes += byts
+    two_us = 0.0
+    for name, call, byts in two_launch_query:
+        us = timed(call)
+        two_us += us
+        gbps = byts / us / 1e3
+        out[name + " (the query side as two launches; not in the chain)"] = {
+            "us": round(us, 2), "bytes_algorithmic": int(byts), "GBps": round(gbps, 1),
+            "roofline_frac": round(gbps / HBM_PEAK_GBPS, 4)}
     dense_us = timed(lambda: [c() for c in chain])
     separate_us = timed(lambda: [c() for c in separate])
     chain_us = timed(accumulate_chain)
     unfused_us = timed(accumulate_unfused)
+    two_launch_us = timed(accumulate_two_launch)
 
     # Offline folds, measured only, with the weights prepared once by the library outside the
     # timing.  W~ = W^UK^T W^UQ ([H d_c, d_c^Q], 201 MB of bf16) makes q~ = W~ c^Q one
@@ -306,7 +329,10 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
            "chain_roofline_frac": round(total_bytes / chain_us / 1e3 / HBM_PEAK_GBPS, 4),
            "sequences_per_s": round(B / (chain_us * 1e-6), 1),
            "chain_schedule": "one stream; stacked products accumulating into outputs cleared "
-                             "by one fill at the start; combine fused with W^UV",
+                             "by one fill at the start; the query side in one launch; combine "
+                             "fused with W^UV",
+           "chain_two_launch_query_us": round(two_launch_us, 2),
+           "two_launch_query_vs_one_max_rel_diff_u": round(two_vs_one, 6),
            "chain_dense_outputs_us": round(dense_us, 2),
            "chain_unfused_combine_us": round(unfused_us, 2),
            "chain_separate_products_us": round(separate_us, 2),

@@ -465,12 +465,13 @@ def test_stream_read_runs(mla):
 
 
 # ------------------------------------------------------------------ full decode layer
-def layer_on_gpu(mla, x, S, stacked=False, fused=False):
+def layer_on_gpu(mla, x, S, stacked=False, fused=False, qpath=False):
     """The whole decode layer through the C ABI: projections, cache append, absorption,
     attention + combine, W^UV and W^O.  stacked: the projections that share an input run as
     one product over their stacked weights ([W^DQ; W^DKV; W^KR] h, then [W^UQ; W^QR] c^Q
     with c^Q read in place), and the append and absorption read their inputs in place from
-    those outputs through the row-strided entry points."""
+    those outputs through the row-strided entry points.  qpath (with stacked): the query
+    side (W^UQ, W^QR, RoPE, absorption) is one mla_query_path launch instead."""
     s = x["shape"]
     B, H, d_h, d_c, d_R, d, d_cq = s.B, s.H, s.d_h, s.d_c, s.d_R, x["d"], x["d_cq"]
     w = {k: dev(v) for k, v in x["weights"].items()}
@@ -487,13 +488,18 @@ def layer_on_gpu(mla, x, S, stacked=False, fused=False):
         y_a = torch.empty(B, d_cq + d_c + d_R, **f32)
         y_b = torch.empty(B, H * (d_h + d_R), **f32)
         mla.mla_linear(h, w_a, y_a)
-        mla.mla_linear_strided(y_a[:, :d_cq], w_b, y_b)
         mla.mla_kv_append_strided(y_a[:, d_cq:d_cq + d_c].unsqueeze(1),
                                   y_a[:, d_cq + d_c:].unsqueeze(1), before, bt, cache,
                                   x["rope_base"])
-        mla.mla_absorb_q_strided(y_b[:, :H * d_h].view(B, H, d_h), w["w_uk"],
-                                 y_b[:, H * d_h:].view(B, H, d_R), seq_lens, x["rope_base"],
-                                 q_lat, q_pe)
+        if qpath:  # the query side in one launch, c^Q read in place
+            w_pack = mla.mla_pack_query_weights(w["w_uq"], w["w_qr"], H)
+            mla.mla_query_path(y_a[:, :d_cq], w_pack, w["w_uk"], seq_lens, x["rope_base"],
+                               q_lat, q_pe)
+        else:
+            mla.mla_linear_strided(y_a[:, :d_cq], w_b, y_b)
+            mla.mla_absorb_q_strided(y_b[:, :H * d_h].view(B, H, d_h), w["w_uk"],
+                                     y_b[:, H * d_h:].view(B, H, d_R), seq_lens, x["rope_base"],
+                                     q_lat, q_pe)
     else:
         c_q = torch.empty(B, d_cq, **f32)
         q_c = torch.empty(B, H * d_h, **f32)
@@ -528,14 +534,15 @@ def layer_on_gpu(mla, x, S, stacked=False, fused=False):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("stacked,fused", [(False, False), (True, False), (True, True)],
-                         ids=["separate", "stacked", "stacked-fused"])
-def test_full_layer_b64_t2k_sampled(mla, stacked, fused):
+@pytest.mark.parametrize("stacked,fused,qpath", [(False, False, False), (True, False, False),
+                                                (True, True, False), (True, True, True)],
+                         ids=["separate", "stacked", "stacked-fused", "stacked-fused-qpath"])
+def test_full_layer_b64_t2k_sampled(mla, stacked, fused, qpath):
     """Full layer at d=5120, H=128, B=64, 2048 prior tokens + 1 appended: all 64 rows of
     u on the GPU; sequences 0 and 37 through the oracle's expanded path."""
     x = W.layer_b64_t2k()
-    say(f"layer_b64_t2k stacked={stacked} fused={fused}")
-    u, cache = layer_on_gpu(mla, x, S=4, stacked=stacked, fused=fused)
+    say(f"layer_b64_t2k stacked={stacked} fused={fused} qpath={qpath}")
+    u, cache = layer_on_gpu(mla, x, S=4, stacked=stacked, fused=fused, qpath=qpath)
     pick = [0, 37]
     ref = oracle.decode_layer(W.to_f64(x["h"]), {k: W.to_f64(v) for k, v in x["weights"].items()},
                               W.to_f64(x["cache"]), x["block_table"].numpy(),
@@ -551,13 +558,15 @@ def test_full_layer_b64_t2k_sampled(mla, stacked, fused):
         assert_bf16(row, want, "appended row")
 
 
-@pytest.mark.parametrize("stacked,fused", [(False, False), (True, False), (True, True)],
-                         ids=["separate", "stacked", "stacked-fused"])
-def test_small_layer_chain(mla, stacked, fused):
-    """A small layer (d=256, H=16, d_c=512, d_R=64, B=5, 100 prior tokens) end to end on all rows."""
-    x = W.layer_b64_t2k(seed=21, B=5, T=100, d=256, H=16, d_cq=96)
-    say(f"small layer stacked={stacked} fused={fused}")
-    u, _ = layer_on_gpu(mla, x, S=2, stacked=stacked, fused=fused)
+@pytest.mark.parametrize("stacked,fused,qpath", [(False, False, False), (True, False, False),
+                                                (True, True, False), (True, True, True)],
+                         ids=["separate", "stacked", "stacked-fused", "stacked-fused-qpath"])
+def test_small_layer_chain(mla, stacked, fused, qpath):
+    """A small layer (d=256, H=16, d_c=512, d_R=64, B=5, 100 prior tokens) end to end on all
+    rows (d_c^Q = 384 where the one-launch query side runs, which needs a multiple of 384)."""
+    x = W.layer_b64_t2k(seed=21, B=5, T=100, d=256, H=16, d_cq=384 if qpath else 96)
+    say(f"small layer stacked={stacked} fused={fused} qpath={qpath}")
+    u, _ = layer_on_gpu(mla, x, S=2, stacked=stacked, fused=fused, qpath=qpath)
     ref = oracle.decode_layer(W.to_f64(x["h"]), {k: W.to_f64(v) for k, v in x["weights"].items()},
                               W.to_f64(x["cache"]), x["block_table"].numpy(),
                               x["seq_lens_before"].numpy(), x["shape"].d_h, x["shape"].d_R,
