@@ -142,7 +142,7 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     w = {k: cu(v) for k, v in x["weights"].items()}
     w_a = torch.cat([w["w_dq"], w["w_dkv"], w["w_kr"]]).contiguous()
     w_b = torch.cat([w["w_uq"], w["w_qr"]]).contiguous()
-    w_pack = mla.mla_pack_query_weights(w["w_uq"], w["w_qr"], H)  # load-time packing
+    w_pack = mla.mla_pack_query_weights(w["w_uq"], w["w_qr"], w["w_uk"], H)  # load-time packing
     h, cache, bt, before = cu(x["h"]), cu(x["cache"]), cu(x["block_table"]), cu(x["seq_lens_before"])
     f32 = dict(device="cuda", dtype=torch.float32)
     n_a, n_b = d_cq + d_c + d_R, H * (d_h + d_R)
@@ -168,8 +168,7 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
                                               k_r.unsqueeze(1), before, bt, cache, x["rope_base"])],
          B * (d_c + d_R) * 4 + B * (d_c + d_R) * 2),
         ("7+1 mla_query_path (W^UQ, W^QR, RoPE, absorption in one launch)",
-         [mla.bind(mla.mla_query_path, c_q, w_pack, w["w_uk"], seq_lens, x["rope_base"],
-                   q_lat, q_pe)],
+         [mla.bind(mla.mla_query_path, c_q, w_pack, seq_lens, x["rope_base"], q_lat, q_pe)],
          nb(w_b) + nb(w["w_uk"]) + B * d_cq * 4 + nb(q_lat) + nb(q_pe)),
         (f"3 mla_decode_attn ({S} splits, bf16 partials)",
          [mla.bind(mla.mla_decode_attn, q_lat, q_pe, cache, bt, seq_lens, x["scale"], S, o_part,

@@ -56,9 +56,9 @@ _SIGNATURES = {
                             _I32, _P]),
     "mla_absorb_q_strided": (_I32, [_P, _I64, _P, _P, _I64, _P, _F, _P, _P, _I32, _I32, _I32,
                                     _I32, _I32, _I32, _I32, _P]),
-    "mla_pack_query_weights": (_I32, [_P, _P, _I32, _I32, _P, _P]),
-    "mla_query_path": (_I32, [_P, _I64, _P, _P, _P, _F, _P, _P, _I32, _I32, _I32, _I32, _I32,
-                              _I32, _P]),
+    "mla_pack_query_weights": (_I32, [_P, _P, _P, _I32, _I32, _P, _P]),
+    "mla_query_path": (_I32, [_P, _I64, _P, _P, _F, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                              _P]),
     "mla_kv_append": (_I32, [_P, _P, _I32, _P, _P, _P, _F, _SP, _I32, _P]),
     "mla_kv_append_strided": (_I32, [_P, _I64, _P, _I64, _I32, _P, _P, _P, _F, _SP, _I32, _P]),
     "mla_decode_attn": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _I32, _P, _I32, _P]),
@@ -355,42 +355,49 @@ def mla_absorb_q_strided(q_c, w_uk, q_r, seq_lens, rope_base, q_lat, q_pe, strea
         B, H, d_h, d_c, d_R, _dtype_code(w_uk), _dtype_code(q_lat), _stream(stream))
 
 
-def mla_pack_query_weights(w_uq, w_qr, H, w_pack=None, stream=None):
-    """Pack [W^UQ; W^QR] (bf16 [H*128, d_cq] and [H*64, d_cq]) into the layout mla_query_path
-    reads; returns w_pack (a new bf16 tensor of H*192*d_cq elements unless one is given)."""
+def query_pack_elems(H, d_cq, d_h=128, d_R=64, d_c=512):
+    """bf16 elements of the packed query-side weights (mla_pack_query_weights)."""
+    return H * ((d_h + d_R) * d_cq + d_h * d_c)
+
+
+def mla_pack_query_weights(w_uq, w_qr, w_uk, H, w_pack=None, stream=None):
+    """Pack W^UQ [H*128, d_cq], W^QR [H*64, d_cq] and W^UK [H*128, 512] (bf16) into the
+    layout mla_query_path reads; returns w_pack (a new bf16 tensor unless one is given)."""
     torch = _torch()
     d_cq = w_uq.shape[1]
     _expect(tuple(w_uq.shape) == (H * 128, d_cq) and tuple(w_qr.shape) == (H * 64, d_cq),
             "w_uq must be [H*128, d_cq] and w_qr [H*64, d_cq]")
+    _expect(tuple(w_uk.shape) == (H * 128, 512), "w_uk must be [H*128, 512]")
+    n = query_pack_elems(H, d_cq)
     if w_pack is None:
-        w_pack = torch.empty(H * 192 * d_cq, device=w_uq.device, dtype=torch.bfloat16)
-    _expect(w_pack.numel() == H * 192 * d_cq, "w_pack must hold H*192*d_cq elements")
+        w_pack = torch.empty(n, device=w_uq.device, dtype=torch.bfloat16)
+    _expect(w_pack.numel() == n, f"w_pack must hold {n} elements")
     _invoke("mla_pack_query_weights",
-        _dev(w_uq, "w_uq", torch.bfloat16, 2), _dev(w_qr, "w_qr", torch.bfloat16, 2), H, d_cq,
-        _dev(w_pack, "w_pack", torch.bfloat16), _stream(stream))
+        _dev(w_uq, "w_uq", torch.bfloat16, 2), _dev(w_qr, "w_qr", torch.bfloat16, 2),
+        _dev(w_uk, "w_uk", torch.bfloat16, 2), H, d_cq, _dev(w_pack, "w_pack", torch.bfloat16),
+        _stream(stream))
     return w_pack
 
 
-def mla_query_path(c_q, w_pack, w_uk, seq_lens, rope_base, q_lat, q_pe, stream=None):
+def mla_query_path(c_q, w_pack, seq_lens, rope_base, q_lat, q_pe, stream=None):
     """The query side in one launch: q~_i = W^UK_i^T (W^UQ_i c^Q) into q_lat and
     RoPE(W^QR_i c^Q, seq_lens - 1) into q_pe.  c_q [B, d_cq] f32 (rows may be a column
-    range of a wider buffer), w_pack from mla_pack_query_weights, w_uk [H*d_h, d_c] bf16;
-    q_lat [B,H,d_c], q_pe [B,H,d_R] bf16."""
+    range of a wider buffer), w_pack from mla_pack_query_weights; q_lat [B,H,512],
+    q_pe [B,H,64] bf16."""
     torch = _torch()
     B, d_cq = c_q.shape
     B2, H, d_c = q_lat.shape
     d_R = q_pe.shape[2]
     _expect(B2 == B and tuple(q_pe.shape) == (B, H, d_R), "q_lat / q_pe must be [B,H,*]")
-    _expect(w_uk.shape[0] % H == 0 and w_uk.shape[1] == d_c, "w_uk must be [H*d_h, d_c]")
-    d_h = w_uk.shape[0] // H
-    _expect(w_pack.numel() == H * (d_h + d_R) * d_cq, "w_pack must hold H*(d_h + d_R)*d_cq elements")
+    _expect(w_pack.numel() == query_pack_elems(H, d_cq, 128, d_R, d_c),
+            "w_pack does not hold the packed weights of these sizes")
     _expect(tuple(seq_lens.shape) == (B,), "seq_lens must be [B]")
     cq_ptr, ld_cq = _dev_rows(c_q, "c_q", torch.float32, 2, 1)
     _invoke("mla_query_path",
-        cq_ptr, ld_cq, _dev(w_pack, "w_pack", torch.bfloat16), _dev(w_uk, "w_uk", torch.bfloat16, 2),
+        cq_ptr, ld_cq, _dev(w_pack, "w_pack", torch.bfloat16),
         _dev(seq_lens, "seq_lens", torch.int32, 1), float(rope_base),
         _dev(q_lat, "q_lat", torch.bfloat16, 3), _dev(q_pe, "q_pe", torch.bfloat16, 3),
-        B, H, d_h, d_R, d_c, d_cq, _stream(stream))
+        B, H, 128, d_R, d_c, d_cq, _stream(stream))
 
 
 def mla_kv_append(c_kv, k_r, seq_lens_before, block_table, kv_cache, rope_base, stream=None):

@@ -140,13 +140,14 @@ hipError_t launch_absorb_mfma(const float* q_c, int64_t ld_q, const void* w_uk, 
                               hipStream_t s);
 
 // The query side in one launch per 64-row block (qpath.hip): q^C_i and q^R_i from c^Q,
-// RoPE, and q~_i = W^UK_i^T q^C_i, bf16 weights ([W^UQ; W^QR] packed by launch_qpath_pack)
-// and outputs.
+// RoPE, and q~_i = W^UK_i^T q^C_i, bf16 weights (packed by launch_qpath_pack into
+// qpath_pack_elems bf16) and outputs.
 bool qpath_supported(int H, int d_h, int d_R, int d_c, int d_cq, int64_t ld_q, const void* c_q,
-                     const void* w_pack, const void* w_uk, const void* q_lat, const void* q_pe);
-hipError_t launch_qpath_pack(const void* w_uq, const void* w_qr, int H, int d_cq, void* out,
-                             hipStream_t s);
-hipError_t launch_qpath(const float* c_q, int64_t ld_q, const void* w_pack, const void* w_uk,
+                     const void* w_pack, const void* q_lat, const void* q_pe);
+int64_t qpath_pack_elems(int H, int d_cq);
+hipError_t launch_qpath_pack(const void* w_uq, const void* w_qr, const void* w_uk, int H,
+                             int d_cq, void* out, hipStream_t s);
+hipError_t launch_qpath(const float* c_q, int64_t ld_q, const void* w_pack,
                         const int32_t* seq_lens, float rope_base, int B, int H, int d_cq,
                         void* q_lat, void* q_pe, hipStream_t s);
 

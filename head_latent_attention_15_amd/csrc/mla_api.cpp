@@ -552,25 +552,26 @@ mla_status_t mla_absorb_q_strided(const float* q_c, int64_t ld_qc, const void* w
                   q_lat, q_pe, B, H, d_h, d_c, d_R, w_dtype, out_dtype, stream);
 }
 
-mla_status_t mla_pack_query_weights(const void* w_uq, const void* w_qr, int32_t H, int32_t d_cq,
-                                    void* w_pack, void* stream) {
+mla_status_t mla_pack_query_weights(const void* w_uq, const void* w_qr, const void* w_uk,
+                                    int32_t H, int32_t d_cq, void* w_pack, void* stream) {
   const char* fn = "mla_pack_query_weights";
-  if (!w_uq || !w_qr || !w_pack) return fail(MLA_ERR_NULL, "%s: a required pointer is NULL", fn);
-  if (H < 1 || d_cq < 32 || d_cq % 32)
-    return fail(MLA_ERR_SHAPE, "%s: H %d, d_cq %d (a positive multiple of 32)", fn, H, d_cq);
+  if (!w_uq || !w_qr || !w_uk || !w_pack)
+    return fail(MLA_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (H < 1 || d_cq < 384 || d_cq % 384)
+    return fail(MLA_ERR_SHAPE, "%s: H %d, d_cq %d (a positive multiple of 384)", fn, H, d_cq);
   if ((reinterpret_cast<uintptr_t>(w_uq) | reinterpret_cast<uintptr_t>(w_qr) |
-       reinterpret_cast<uintptr_t>(w_pack)) & 15)
+       reinterpret_cast<uintptr_t>(w_uk) | reinterpret_cast<uintptr_t>(w_pack)) & 15)
     return fail(MLA_ERR_UNSUPPORTED, "%s: pointers must be 16-byte aligned", fn);
-  return launched(mla::launch_qpath_pack(w_uq, w_qr, H, d_cq, w_pack, as_stream(stream)),
+  return launched(mla::launch_qpath_pack(w_uq, w_qr, w_uk, H, d_cq, w_pack, as_stream(stream)),
                   "query weight packing");
 }
 
-mla_status_t mla_query_path(const float* c_q, int64_t ld_cq, const void* w_pack, const void* w_uk,
+mla_status_t mla_query_path(const float* c_q, int64_t ld_cq, const void* w_pack,
                             const int32_t* seq_lens, float rope_base, void* q_lat, void* q_pe,
                             int32_t B, int32_t H, int32_t d_h, int32_t d_R, int32_t d_c,
                             int32_t d_cq, void* stream) {
   const char* fn = "mla_query_path";
-  if (!c_q || !w_pack || !w_uk || !seq_lens || !q_lat || !q_pe)
+  if (!c_q || !w_pack || !seq_lens || !q_lat || !q_pe)
     return fail(MLA_ERR_NULL, "%s: a required pointer is NULL", fn);
   if (B < 1 || H < 1 || d_h < 1 || d_R < 1 || d_c < 1 || d_cq < 1)
     return fail(MLA_ERR_SHAPE, "%s: sizes must be >= 1", fn);
@@ -578,13 +579,13 @@ mla_status_t mla_query_path(const float* c_q, int64_t ld_cq, const void* w_pack,
     return fail(MLA_ERR_SHAPE, "%s: row stride %lld below d_cq %d", fn,
                 static_cast<long long>(ld_cq), d_cq);
   if (!std::isfinite(rope_base)) return fail(MLA_ERR_SHAPE, "%s: rope_base not finite", fn);
-  if (!mla::qpath_supported(H, d_h, d_R, d_c, d_cq, ld_cq, c_q, w_pack, w_uk, q_lat, q_pe))
+  if (!mla::qpath_supported(H, d_h, d_R, d_c, d_cq, ld_cq, c_q, w_pack, q_lat, q_pe))
     return fail(MLA_ERR_UNSUPPORTED,
                 "%s: needs d_h 128, d_R 64, d_c 512, d_cq %% 384 == 0, ld_cq %% 4 == 0 and "
                 "16-byte aligned pointers (got d_h %d, d_R %d, d_c %d, d_cq %d)",
                 fn, d_h, d_R, d_c, d_cq);
-  return launched(mla::launch_qpath(c_q, ld_cq, w_pack, w_uk, seq_lens, rope_base, B, H, d_cq,
-                                    q_lat, q_pe, as_stream(stream)),
+  return launched(mla::launch_qpath(c_q, ld_cq, w_pack, seq_lens, rope_base, B, H, d_cq, q_lat,
+                                    q_pe, as_stream(stream)),
                   "query path");
 }
 

@@ -8,12 +8,16 @@
 // to HBM, and no k range is split over workgroups, so there are no atomics and every
 // result is the same on every run.
 //
-// The weights come packed once at load time (qpath_pack_kernel): for head i, the 192 rows
-// [W^UQ_i; W^QR_i] as 12 tiles of 16 rows, each tile as its d_c^Q / 32 k-steps in order,
-// each k-step one 1 KB MFMA operand fragment (lane 16 g + n: row n, k 8 g .. 8 g + 7).  A
-// wavefront then streams whole 1 KB fragments, and the two waves of a tile together read
-// 4 KB in sequence per chunk; row-major weights would be read 256 bytes per row per chunk
-// across 160 rows, which the DRAM serves far more slowly.
+// The weights come packed once at load time (qpath_pack_kernel).  [W^UQ_i; W^QR_i] (192 rows)
+// is cut into 12 tiles of 16 rows and d_c^Q / 32 k-steps; each (tile, k-step) is one 1 KB
+// MFMA operand fragment (lane 16 g + n: row n, k 8 g .. 8 g + 7), and the fragments are
+// ordered 128-wide chunk of k, head, tile, k-step within the chunk: everything a head needs
+// for one chunk is one contiguous 48 KB block, read in full by the head's two workgroups
+// together, and the blocks all heads read at about the same time form one contiguous
+// region, spread over every HBM channel.  Row-major weights would be read 256 bytes per row
+// per chunk across 160 rows, which the DRAM serves far more slowly.  W^UK_i follows as two 64 KB images, one per
+// half, laid out exactly as the workgroup keeps it in LDS, so it is copied in linear 1 KB
+// blocks.
 //
 // Workgroup (head i, half hf) of 12 wavefronts, 64 rows b (one block of the batch):
 // hf = blockIdx.x / H, so the two halves of a head run on one XCD (consecutive ids go to
@@ -93,35 +97,37 @@ __device__ __forceinline__ unsigned qp_pack2(float a, float b) {
 
 __global__ __launch_bounds__(QP_NT) void qpath_kernel(
     const float* __restrict__ c_q, int64_t ld_q, const bf16raw* __restrict__ w_pack,
-    const bf16raw* __restrict__ w_uk, const int32_t* __restrict__ seq_lens, float rope_base,
-    int B, int H, int d_cq, bf16raw* __restrict__ q_lat, bf16raw* __restrict__ q_pe) {
+    const int32_t* __restrict__ seq_lens, float rope_base, int B, int H, int d_cq,
+    bf16raw* __restrict__ q_lat, bf16raw* __restrict__ q_pe) {
   __shared__ __attribute__((aligned(16))) char smem[QP_LDS];
   lds_char_t* const lsm = (lds_char_t*)smem;
   const int h = blockIdx.x % H, hf = blockIdx.x / H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
-  const int nsteps = d_cq / 32, nchunks = d_cq / QP_KC;
+  const int nchunks = d_cq / QP_KC;
   // phase 2 puts q^C_i in the chunk buffer the last chunk does not read
   lds_char_t* const qc = lsm + (nchunks & 1) * QP_CHUNK;
 
   if (w >= QP_NC) {
     // ---- c^Q staging: thread p = tid - 640 moves row p / 2, k 64 (p % 2) .. + 63 of each
     //      chunk (rows past B read row B - 1: their products land in rows never stored).
-    //      Chunk ch + 1 is loaded while chunk ch is being used, converted and stored after
-    //      the barrier that ends chunk ch - 1, and the last chunk is loaded and stored once
-    //      more (into a buffer nobody reads before it is rewritten after a barrier): no
-    //      branch around the loads, so each wait is the exact one
+    //      Two chunks are in flight: chunk ch + 1, loaded two barriers earlier, is converted
+    //      and stored after the barrier that ends chunk ch - 1's reads, then chunk ch + 3 is
+    //      loaded into the registers it leaves.  Past the end the last chunk is loaded and
+    //      stored again (into a buffer nobody reads before it is rewritten after a
+    //      barrier): no branch around the loads, so each wait is the exact one
     const int p = tid - QP_CT, xrow = p >> 1;
     const float* xsrc = c_q + static_cast<int64_t>(min(xrow, B - 1)) * ld_q + 64 * (p & 1);
     lds_char_t* const xdst = lsm + xrow * QP_ROW + 128 * (p & 1);
-    f32x4_t xv[QP_XLOADS];
-    auto load_x = [&](int ch) {
+    f32x4_t xa[QP_XLOADS], xb[QP_XLOADS];
+    auto load_x = [&](f32x4_t (&xv)[QP_XLOADS], int ch) {
+      ch = min(ch, nchunks - 1);
 #pragma unroll
       for (int i = 0; i < QP_XLOADS; ++i)
         xv[i] = *reinterpret_cast<const f32x4_t*>(xsrc + ch * QP_KC + 4 * i);
     };
-    auto store_x = [&](int buf) {
+    auto store_x = [&](const f32x4_t (&xv)[QP_XLOADS], int buf) {
 #pragma unroll
       for (int i = 0; i < QP_XLOADS; i += 2) {
         u32x4_t hi, lo;
@@ -134,16 +140,28 @@ __global__ __launch_bounds__(QP_NT) void qpath_kernel(
         }
         *(lds_u32x4_t*)(xdst + buf * QP_CHUNK + 8 * i) = hi;
         *(lds_u32x4_t*)(xdst + buf * QP_CHUNK + QP_PLANE + 8 * i) = lo;
+        // one group of eight values at a time: with two chunks in flight, converting the
+        // whole chunk ahead of its stores would not fit in the registers
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
-    load_x(0);
-    store_x(0);
-    load_x(min(1, nchunks - 1));
+    load_x(xa, 0);
+    load_x(xb, 1);
+    store_x(xa, 0);
+    load_x(xa, 2);
     __syncthreads();
-    for (int ch = 0; ch < nchunks; ++ch) {
-      // buffer (ch + 1) & 1 was last read in chunk ch - 1, before the previous barrier
-      store_x((ch + 1) & 1);
-      load_x(min(ch + 2, nchunks - 1));
+    // buffer (ch + 1) & 1 was last read in chunk ch - 1, before the previous barrier
+    int ch = 0;
+    for (; ch + 1 < nchunks; ch += 2) {
+      store_x(xb, (ch + 1) & 1);  // chunk ch + 1
+      load_x(xb, ch + 3);
+      __syncthreads();
+      store_x(xa, (ch + 2) & 1);  // chunk ch + 2
+      load_x(xa, ch + 4);
+      __syncthreads();
+    }
+    if (ch < nchunks) {
+      store_x(xb, (ch + 1) & 1);
       __syncthreads();
     }
     __syncthreads();  // the k-half exchange (below) writes
@@ -158,22 +176,24 @@ __global__ __launch_bounds__(QP_NT) void qpath_kernel(
 #pragma unroll
     for (int q = 0; q < 2; ++q)
       pos[q] = seq_lens[min((tid + QP_CT * q) >> 4, B - 1)] - 1;
+    __builtin_amdgcn_sched_barrier(0);  // both go out before the weight loads
 
     // ---- packed tiles 2 pr + tt of this half: q^C tiles 0..7 of head i, then q^R tiles
     //      8 + 2 hf, 9 + 2 hf.  Ring fragment n: chunk n / 4, k-step 2 kh + (n % 4) / 2 of
-    //      the chunk, tile n % 2
+    //      the chunk, tile n % 2; a (chunk, head) block holds 12 tiles x 4 k-steps of 512 bf16
     const bf16raw* fbase[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int t = 2 * pr + tt, pt = t < 8 ? t : t + 2 * hf;
-      fbase[tt] = w_pack + ((static_cast<int64_t>(h) * 12 + pt) * nsteps + 2 * kh) * 512 + 8 * lane;
+      fbase[tt] = w_pack + ((static_cast<int64_t>(h) * 12 + pt) * 4 + 2 * kh) * 512 + 8 * lane;
     }
+    const int64_t chunk_stride = static_cast<int64_t>(H) * 48 * 512;
     auto frag_src = [&](int n) {
-      return reinterpret_cast<const bf16x8_t*>(fbase[n & 1] + 512 * (4 * (n >> 2) + ((n >> 1) & 1)));
+      return reinterpret_cast<const bf16x8_t*>(fbase[n & 1] + chunk_stride * (n >> 2) + 512 * ((n >> 1) & 1));
     };
     bf16x8_t wf[QP_RING];
 #pragma unroll
-    for (int n = 0; n < QP_RING - 1; ++n) wf[n] = *frag_src(n);
+    for (int n = 0; n < QP_RING - 2; ++n) wf[n] = *frag_src(n);
 
     // ---- RoPE table while the loads are in flight: entry e = row b, pair k = 16 hf + e % 16
     //      (angle pos * base^(-2k/d_R) and its sine and cosine in fp64)
@@ -192,14 +212,15 @@ __global__ __launch_bounds__(QP_NT) void qpath_kernel(
     __syncthreads();
 
     // ---- W^UK_i rows j, columns 256 hf .. + 255 -> LDS [j][c], chunk c of row j at position
-    //      c ^ qp_uswz(j): copy i moves rows 2 i, 2 i + 1, lane l to position l % 32 of row
-    //      2 i + l / 32.  Wave w issues copy w + 10 (ch - 1) in chunk ch = 1 .. 7, after the
-    //      first weight loads have gone out; copies a short d_c^Q leaves over go after the loop
-    const bf16raw* ubase = w_uk + (static_cast<int64_t>(h) * QP_DH) * QP_DC + 256 * hf;
+    //      c ^ qp_uswz(j), from its packed image (the same bytes in the same order): copy i
+    //      moves 1 KB, rows 2 i and 2 i + 1.  Wave w issues copy w + 10 (ch - 1) in chunk
+    //      ch = 1 .. 7, after the first weight loads have gone out; copies a short d_c^Q
+    //      leaves over go after the loop
+    const bf16raw* ubase = w_pack + static_cast<int64_t>(H) * 192 * d_cq +
+                           static_cast<int64_t>(2 * h + hf) * QP_DH * 256;
     const uint32_t ulds = static_cast<uint32_t>(reinterpret_cast<size_t>(lsm)) + QP_WUK;
     auto copy_uk = [&](int i) {
-      const int j = 2 * i + (lane >> 5), c = (lane & 31) ^ qp_uswz(j);
-      attn::dma16(ubase, static_cast<uint32_t>((j * QP_DC + 8 * c) * 2), ulds + i * 1024);
+      attn::dma16(ubase, static_cast<uint32_t>(i * 1024 + 16 * lane), ulds + i * 1024);
     };
     const int uk_chunks = min(7, nchunks - 1);
 
@@ -210,38 +231,55 @@ __global__ __launch_bounds__(QP_NT) void qpath_kernel(
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) acc[tt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // chunk ch (cu = ch % 3): fragment n = 4 ch + q sits in slot 4 cu + q; before using it
-    // the wave loads fragment n + 11 into the slot fragment n - 1 freed.  In the last turn
-    // only the first of those loads is a fragment that exists
+    // A fragments of one k-step: plane pl, row tile mt of k-step sl of chunk ch (this wave's
+    // k half).  They are read one k-step ahead, each right after the last product that uses
+    // the registers it replaces, so the LDS reads run under the products; the barrier of
+    // chunk ch sits between its two k-steps: every read of chunk ch is done by then (its
+    // buffer can be refilled) and chunk ch + 1, written during chunk ch - 1's second half and
+    // chunk ch's first, is complete
+    auto a_src = [&](int ch, int sl, int pl, int mt) {
+      return (const lds_bf16x8_t*)(lsm + (ch & 1) * QP_CHUNK + (16 * mt + r) * QP_ROW +
+                                   64 * (2 * kh + sl) + 16 * g + pl * QP_PLANE);
+    };
+    bf16x8_t xf[2][4];
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) xf[pl][mt] = *a_src(0, 0, pl, mt);
+    // chunk ch (cu = ch % 3): weight fragment n = 4 ch + q sits in slot 4 cu + q.  Before
+    // k-step sl uses fragments n = 4 ch + 2 sl and n + 1, the wave loads fragments n + 10 and
+    // n + 11 into the slots that fragments n - 2 and n - 1 (the previous k-step) freed.  In
+    // the last turn only the first k-step's loads are fragments that exist
     auto chunk = [&](int ch, auto cu_c, auto tail_c) {
       constexpr int cu = decltype(cu_c)::value;
       constexpr bool tail = decltype(tail_c)::value;
-      const lds_char_t* xa = lsm + (ch & 1) * QP_CHUNK + r * QP_ROW + 64 * (2 * kh) + 16 * g;
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl) {
-        bf16x8_t xf[2][4];
+        if (!tail || (cu == 0 && sl == 0)) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+            wf[(4 * cu + 2 * sl + tt + QP_RING - 2) % QP_RING] =
+                *frag_src(4 * ch + 2 * sl + tt + QP_RING - 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // issued here, not sunk below the products
+        if (sl == 0 && ch >= 1 && ch <= uk_chunks && w + QP_NC * (ch - 1) < QP_UCOPIES)
+          copy_uk(w + QP_NC * (ch - 1));
+        const bf16x8_t wk0 = wf[(4 * cu + 2 * sl) % QP_RING];
+        const bf16x8_t wk1 = wf[(4 * cu + 2 * sl + 1) % QP_RING];
+        const bool next = sl == 0 || !(tail && cu == QP_UNROLL - 1);  // a k-step follows
 #pragma unroll
         for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-            xf[pl][mt] = *(const lds_bf16x8_t*)(xa + mt * 16 * QP_ROW + 64 * sl + pl * QP_PLANE);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int q = 2 * sl + tt;
-          if (!tail || (cu == 0 && q == 0))
-            wf[(4 * cu + q + QP_RING - 1) % QP_RING] = *frag_src(4 * ch + q + QP_RING - 1);
-          __builtin_amdgcn_sched_barrier(0);  // issued here, not sunk below the products
-          if (q == 0 && ch >= 1 && ch <= uk_chunks && w + QP_NC * (ch - 1) < QP_UCOPIES)
-            copy_uk(w + QP_NC * (ch - 1));
-          const bf16x8_t wk = wf[(4 * cu + q) % QP_RING];
-#pragma unroll
-          for (int pl = 0; pl < 2; ++pl)
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-              acc[tt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[pl][mt], wk, acc[tt][mt], 0, 0, 0);
+          for (int mt = 0; mt < 4; ++mt) {
+            acc[0][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[pl][mt], wk0, acc[0][mt], 0, 0, 0);
+            acc[1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[pl][mt], wk1, acc[1][mt], 0, 0, 0);
+            if (next) xf[pl][mt] = *a_src(sl == 0 ? ch : ch + 1, sl ^ 1, pl, mt);
+          }
+        if (sl == 0) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // k-step 1 of chunk ch is read
+          __syncthreads();
         }
       }
-      __syncthreads();
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -259,7 +297,8 @@ __global__ __launch_bounds__(QP_NT) void qpath_kernel(
     static_assert(QP_UNROLL == 3, "the turn above is written out for three chunks");
     for (int i = w + QP_NC * uk_chunks; i < QP_UCOPIES; i += QP_NC) copy_uk(i);
 
-    // ---- k-half exchange through the chunk buffers (free after the last chunk): wave w
+    // ---- k-half exchange through the chunk buffers (no wave reads them after the last
+    //      chunk's barrier; the staging waves' last, unused copy went in before it): wave w
     //      sends its partial of the tile it does not finish (4 KB) and adds the partner's
     //      partial of the tile it finishes, tile 2 pr + kh: k half 0's sum plus k half 1's
     //      (float addition is commutative: one result in both waves)
@@ -380,25 +419,36 @@ __global__ __launch_bounds__(QP_NT) void qpath_kernel(
     }
 }
 
-// Packing of [W^UQ; W^QR] for qpath_kernel: fragment (i, tile, s) of 512 bf16 at
-// ((i * 12 + tile) * (d_cq / 32) + s) * 512, element 8 l + e = row 16 tile + l % 16 of head i's
-// [W^UQ_i; W^QR_i], k = 32 s + 8 (l / 16) + e.  One thread per 16 bytes.
+// Packing for qpath_kernel, one thread per 16 bytes.
+//   fragments: q = (((c * H + i) * 12 + tile) * 4 + s4) * 64 + l holds row 16 tile + l % 16
+//     of head i's [W^UQ_i; W^QR_i] at k = 32 (4 c + s4) + 8 (l / 16) .. + 7
+//   W^UK images, after H * 192 * d_cq elements: u = ((2 i + hf) * 128 + j) * 32 + pos holds
+//     W^UK row i * 128 + j, columns 256 hf + 8 (pos ^ qp_uswz(j)) .. + 7
 __global__ __launch_bounds__(256) void qpath_pack_kernel(const bf16raw* __restrict__ w_uq,
                                                          const bf16raw* __restrict__ w_qr,
+                                                         const bf16raw* __restrict__ w_uk,
                                                          int H, int d_cq,
                                                          bf16raw* __restrict__ out) {
-  const int nsteps = d_cq / 32;
-  const int64_t total = static_cast<int64_t>(H) * 12 * nsteps * 64;
+  const int nchunks = d_cq / QP_KC;
+  const int64_t nfrag = static_cast<int64_t>(H) * nchunks * 48 * 64;
+  const int64_t total = nfrag + static_cast<int64_t>(H) * 2 * QP_DH * 32;
   for (int64_t q = blockIdx.x * 256ll + threadIdx.x; q < total; q += static_cast<int64_t>(gridDim.x) * 256) {
-    const int l = static_cast<int>(q & 63);
-    const int64_t f = q >> 6;  // fragment
-    const int s = static_cast<int>(f % nsteps);
-    const int64_t it = f / nsteps;
-    const int tile = static_cast<int>(it % 12), i = static_cast<int>(it / 12);
-    const int row = 16 * tile + (l & 15), k = 32 * s + 8 * (l >> 4);
-    const bf16raw* src = row < QP_DH
-                             ? w_uq + (static_cast<int64_t>(i) * QP_DH + row) * d_cq + k
-                             : w_qr + (static_cast<int64_t>(i) * QP_DR + row - QP_DH) * d_cq + k;
+    const bf16raw* src;
+    if (q < nfrag) {
+      const int l = static_cast<int>(q & 63);
+      const int64_t f = q >> 6;  // fragment
+      const int s4 = static_cast<int>(f & 3), tile = static_cast<int>((f >> 2) % 12);
+      const int64_t ci = (f >> 2) / 12;
+      const int i = static_cast<int>(ci % H), c = static_cast<int>(ci / H);
+      const int row = 16 * tile + (l & 15), k = 32 * (4 * c + s4) + 8 * (l >> 4);
+      src = row < QP_DH ? w_uq + (static_cast<int64_t>(i) * QP_DH + row) * d_cq + k
+                        : w_qr + (static_cast<int64_t>(i) * QP_DR + row - QP_DH) * d_cq + k;
+    } else {
+      const int64_t u = q - nfrag;
+      const int pos = static_cast<int>(u & 31), j = static_cast<int>((u >> 5) & 127);
+      const int hf = static_cast<int>((u >> 12) & 1), i = static_cast<int>(u >> 13);
+      src = w_uk + (static_cast<int64_t>(i) * QP_DH + j) * QP_DC + 256 * hf + 8 * (pos ^ qp_uswz(j));
+    }
     *reinterpret_cast<uint4*>(out + q * 8) = *reinterpret_cast<const uint4*>(src);
   }
 }
@@ -406,33 +456,36 @@ __global__ __launch_bounds__(256) void qpath_pack_kernel(const bf16raw* __restri
 }  // namespace
 
 bool qpath_supported(int H, int d_h, int d_R, int d_c, int d_cq, int64_t ld_q, const void* c_q,
-                     const void* w_pack, const void* w_uk, const void* q_lat, const void* q_pe) {
+                     const void* w_pack, const void* q_lat, const void* q_pe) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(c_q) | reinterpret_cast<uintptr_t>(w_pack) |
-                      reinterpret_cast<uintptr_t>(w_uk) | reinterpret_cast<uintptr_t>(q_lat) |
-                      reinterpret_cast<uintptr_t>(q_pe);
+                      reinterpret_cast<uintptr_t>(q_lat) | reinterpret_cast<uintptr_t>(q_pe);
   return H >= 1 && H <= 32767 && d_h == QP_DH && d_R == QP_DR && d_c == QP_DC &&
          d_cq >= QP_KC * QP_UNROLL && d_cq % (QP_KC * QP_UNROLL) == 0 && ld_q >= d_cq &&
          ld_q % 4 == 0 && (a & 15) == 0;
 }
 
-hipError_t launch_qpath_pack(const void* w_uq, const void* w_qr, int H, int d_cq, void* out,
-                             hipStream_t s) {
-  const int64_t total = static_cast<int64_t>(H) * 12 * (d_cq / 32) * 64;
+int64_t qpath_pack_elems(int H, int d_cq) {
+  return static_cast<int64_t>(H) * (192 * static_cast<int64_t>(d_cq) + QP_DH * QP_DC);
+}
+
+hipError_t launch_qpath_pack(const void* w_uq, const void* w_qr, const void* w_uk, int H,
+                             int d_cq, void* out, hipStream_t s) {
+  const int64_t total = qpath_pack_elems(H, d_cq) / 8;
   const int grid = static_cast<int>(std::min<int64_t>((total + 255) / 256, 65535));
   hipLaunchKernelGGL(qpath_pack_kernel, dim3(grid), dim3(256), 0, s,
-                     static_cast<const bf16raw*>(w_uq), static_cast<const bf16raw*>(w_qr), H,
-                     d_cq, static_cast<bf16raw*>(out));
+                     static_cast<const bf16raw*>(w_uq), static_cast<const bf16raw*>(w_qr),
+                     static_cast<const bf16raw*>(w_uk), H, d_cq, static_cast<bf16raw*>(out));
   return hipGetLastError();
 }
 
-hipError_t launch_qpath(const float* c_q, int64_t ld_q, const void* w_pack, const void* w_uk,
+hipError_t launch_qpath(const float* c_q, int64_t ld_q, const void* w_pack,
                         const int32_t* seq_lens, float rope_base, int B, int H, int d_cq,
                         void* q_lat, void* q_pe, hipStream_t s) {
   // one launch per block of 64 rows b (each block reads the weights again)
   for (int b0 = 0; b0 < B; b0 += QP_M) {
     hipLaunchKernelGGL(qpath_kernel, dim3(2 * H), dim3(QP_NT), 0, s, c_q + b0 * ld_q, ld_q,
-                       static_cast<const bf16raw*>(w_pack), static_cast<const bf16raw*>(w_uk),
-                       seq_lens + b0, rope_base, min(QP_M, B - b0), H, d_cq,
+                       static_cast<const bf16raw*>(w_pack), seq_lens + b0, rope_base,
+                       min(QP_M, B - b0), H, d_cq,
                        static_cast<bf16raw*>(q_lat) + static_cast<int64_t>(b0) * H * QP_DC,
                        static_cast<bf16raw*>(q_pe) + static_cast<int64_t>(b0) * H * QP_DR);
     const hipError_t e = hipGetLastError();

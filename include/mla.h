@@ -136,28 +136,32 @@ mla_status_t mla_absorb_q_strided(const float* q_c, int64_t ld_qc, const void* w
                                   int32_t d_h, int32_t d_c, int32_t d_R, mla_dtype_t w_dtype,
                                   mla_dtype_t out_dtype, void* stream);
 
-/* Packing of the query up-projections for mla_query_path, done once at load time (the
- * product itself is a permutation copy).  For head i, the 192 rows [W^UQ_i; W^QR_i] form 12
- * tiles of 16 rows; tile tl is stored as its d_cq / 32 k-steps s in order, each step one
- * fragment of 512 bf16:
- *   w_pack[((i * 12 + tl) * (d_cq / 32) + s) * 512 + 8 * l + e]
- *     = row 16 tl + l % 16 of [W^UQ_i; W^QR_i] at k = 32 s + 8 (l / 16) + e,  l < 64, e < 8
- * (rows 0..127: W^UQ rows i*128 + row; rows 128..191: W^QR rows i*64 + row - 128).
- *   w_uq [H*128][d_cq], w_qr [H*64][d_cq] bf16 (nn.Linear weights); w_pack [H*192*d_cq] bf16
- *   (written; caller-owned, 16-byte aligned)
- * Errors: NULL, SHAPE (H < 1, d_cq not a positive multiple of 32), UNSUPPORTED (unaligned). */
-mla_status_t mla_pack_query_weights(const void* w_uq, const void* w_qr, int32_t H, int32_t d_cq,
-                                    void* w_pack, void* stream);
+/* Packing of the query-side weights for mla_query_path, done once at load time (a
+ * permutation copy).  w_pack holds H * (192 * d_cq + 128 * 512) bf16:
+ *  - W^UQ and W^QR as 1 KB MFMA operand fragments.  For head i, the 192 rows
+ *    [W^UQ_i; W^QR_i] form 12 tiles of 16 rows; fragment (i, c, tl, s4), for the 128-wide
+ *    k chunk c, tile tl and k-step s4 < 4 of the chunk, starts at element
+ *    (((c * H + i) * 12 + tl) * 4 + s4) * 512, and its element 8 l + e (l < 64,
+ *    e < 8) is row 16 tl + l % 16 of [W^UQ_i; W^QR_i] at k = 32 (4 c + s4) + 8 (l / 16) + e
+ *    (rows 0..127: W^UQ row i*128 + row; rows 128..191: W^QR row i*64 + row - 128).
+ *  - Then W^UK: for head i and half hf (columns 256 hf .. + 255), 128 rows j of 32
+ *    16-byte pieces; piece pos of row j, at element H*192*d_cq + (((2 i + hf) * 128 + j) * 32
+ *    + pos) * 8, holds W^UK[i*128 + j][256 hf + 8 (pos ^ f(j)) .. + 7] with
+ *    f(j) = 2 (j % 4) + 8 ((j / 8) % 2).
+ *   w_uq [H*128][d_cq], w_qr [H*64][d_cq], w_uk [H*128][512] bf16 (nn.Linear weights);
+ *   w_pack caller-owned, 16-byte aligned (written)
+ * Errors: NULL, SHAPE (H < 1, d_cq not a positive multiple of 384), UNSUPPORTED (unaligned). */
+mla_status_t mla_pack_query_weights(const void* w_uq, const void* w_qr, const void* w_uk,
+                                    int32_t H, int32_t d_cq, void* w_pack, void* stream);
 
 /* The whole query side of a decode step in one launch: up-projection, query RoPE and
  * absorption, head by head, without writing q^C or q^R to memory.
  *   q^C_i = W^UQ_i c^Q,  q^R_i = W^QR_i c^Q         (qiita.com/joule/items/57d9b3f4fc27959eaa0d,
  *                                                     "Query の圧縮", "RoPE の扱い")
  *   q_pe[b][i][:]  = RoPE(q^R_i of row b, pos = seq_lens[b] - 1)
- *   q_lat[b][i][c] = sum_d w_uk[i*d_h + d][c] * q^C_i[d]   (same page, "Absorption Trick")
+ *   q_lat[b][i][c] = sum_d W^UK[i*d_h + d][c] * q^C_i[d]   (same page, "Absorption Trick")
  *   c_q      [B] rows of d_cq fp32, row b at c_q + b * ld_cq (ld_cq >= d_cq, % 4 == 0)
- *   w_pack   W^UQ and W^QR as packed by mla_pack_query_weights (bf16)
- *   w_uk     [H*d_h][d_c]  bf16 (nn.Linear weight of W^UK)
+ *   w_pack   W^UQ, W^QR and W^UK as packed by mla_pack_query_weights (bf16)
  *   seq_lens [B] int32, context length INCLUDING the query token (>= 1)
  *   q_lat    [B][H][d_c] bf16, q_pe [B][H][d_R] bf16 (written)
  * Products: bf16 MFMA with fp32 accumulation, c^Q carried as two bf16 terms (about 16
@@ -168,7 +172,7 @@ mla_status_t mla_pack_query_weights(const void* w_uq, const void* w_qr, int32_t 
  * d_cq a multiple of 384 and 16-byte aligned pointers, else UNSUPPORTED (mla_linear_strided
  * followed by mla_absorb_q_strided computes the same).  The caller owns every buffer.
  * Errors: NULL, SHAPE (sizes < 1, ld_cq < d_cq, rope_base not finite), UNSUPPORTED. */
-mla_status_t mla_query_path(const float* c_q, int64_t ld_cq, const void* w_pack, const void* w_uk,
+mla_status_t mla_query_path(const float* c_q, int64_t ld_cq, const void* w_pack,
                             const int32_t* seq_lens, float rope_base, void* q_lat, void* q_pe,
                             int32_t B, int32_t H, int32_t d_h, int32_t d_R, int32_t d_c,
                             int32_t d_cq, void* stream);

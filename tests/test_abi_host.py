@@ -212,8 +212,8 @@ def test_query_path_validation():
     """mla_query_path and its weight packing refuse what the kernels are not built for
     before launching."""
     L = mla.lib
-    # c_q, ld_cq, w_pack, w_uk, seq_lens, base, q_lat, q_pe, B, H, d_h, d_R, d_c, d_cq
-    args = lambda **k: [k.get("c_q", FAKE), k.get("ld", 1536), FAKE, FAKE, FAKE,
+    # c_q, ld_cq, w_pack, seq_lens, base, q_lat, q_pe, B, H, d_h, d_R, d_c, d_cq
+    args = lambda **k: [k.get("c_q", FAKE), k.get("ld", 1536), FAKE, FAKE,
                         k.get("base", 1e4), FAKE, FAKE, k.get("B", 2), 8, k.get("d_h", 128),
                         64, 512, k.get("d_cq", 1536), None]
     assert L.mla_query_path(*args(c_q=None)) == mla.MLA_ERR_NULL
@@ -223,10 +223,11 @@ def test_query_path_validation():
     assert L.mla_query_path(*args(d_h=64)) == mla.MLA_ERR_UNSUPPORTED
     assert L.mla_query_path(*args(d_cq=1280, ld=1280)) == mla.MLA_ERR_UNSUPPORTED
     assert L.mla_query_path(*args(ld=1538)) == mla.MLA_ERR_UNSUPPORTED  # rows not 16-byte apart
-    assert L.mla_pack_query_weights(None, FAKE, 8, 1536, FAKE, None) == mla.MLA_ERR_NULL
-    assert L.mla_pack_query_weights(FAKE, FAKE, 8, 1537, FAKE, None) == mla.MLA_ERR_SHAPE
-    assert L.mla_pack_query_weights(FAKE, FAKE, 0, 1536, FAKE, None) == mla.MLA_ERR_SHAPE
-    assert L.mla_pack_query_weights(FAKE, FAKE + 2, 8, 1536, FAKE, None) == mla.MLA_ERR_UNSUPPORTED
+    assert L.mla_pack_query_weights(None, FAKE, FAKE, 8, 1536, FAKE, None) == mla.MLA_ERR_NULL
+    assert L.mla_pack_query_weights(FAKE, FAKE, FAKE, 8, 1280, FAKE, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_pack_query_weights(FAKE, FAKE, FAKE, 0, 1536, FAKE, None) == mla.MLA_ERR_SHAPE
+    assert (L.mla_pack_query_weights(FAKE, FAKE + 2, FAKE, 8, 1536, FAKE, None)
+            == mla.MLA_ERR_UNSUPPORTED)
 
 
 @pytest.mark.parametrize("shape,stride,lead,ld", [

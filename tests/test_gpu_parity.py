@@ -492,9 +492,8 @@ def layer_on_gpu(mla, x, S, stacked=False, fused=False, qpath=False):
                                   y_a[:, d_cq + d_c:].unsqueeze(1), before, bt, cache,
                                   x["rope_base"])
         if qpath:  # the query side in one launch, c^Q read in place
-            w_pack = mla.mla_pack_query_weights(w["w_uq"], w["w_qr"], H)
-            mla.mla_query_path(y_a[:, :d_cq], w_pack, w["w_uk"], seq_lens, x["rope_base"],
-                               q_lat, q_pe)
+            w_pack = mla.mla_pack_query_weights(w["w_uq"], w["w_qr"], w["w_uk"], H)
+            mla.mla_query_path(y_a[:, :d_cq], w_pack, seq_lens, x["rope_base"], q_lat, q_pe)
         else:
             mla.mla_linear_strided(y_a[:, :d_cq], w_b, y_b)
             mla.mla_absorb_q_strided(y_b[:, :H * d_h].view(B, H, d_h), w["w_uk"],

@@ -33,32 +33,42 @@ def run(mla, c_q, wts, seq_lens, base=10000.0):
     """c_q: a CUDA tensor [B, d_cq] (may be a column range); the weights are packed on the GPU
     first.  Returns (q_lat, q_pe) on the GPU."""
     B, H = c_q.shape[0], wts["w_qr"].shape[0] // 64
-    w_pack = mla.mla_pack_query_weights(dev(wts["w_uq"]), dev(wts["w_qr"]), H)
+    w_pack = mla.mla_pack_query_weights(dev(wts["w_uq"]), dev(wts["w_qr"]), dev(wts["w_uk"]), H)
     q_lat = torch.full((B, H, 512), float("nan"), device="cuda", dtype=torch.bfloat16)
     q_pe = torch.full((B, H, 64), float("nan"), device="cuda", dtype=torch.bfloat16)
-    mla.mla_query_path(c_q, w_pack, dev(wts["w_uk"]), dev(seq_lens), base, q_lat, q_pe)
+    mla.mla_query_path(c_q, w_pack, dev(seq_lens), base, q_lat, q_pe)
     torch.cuda.synchronize()
     return q_lat, q_pe
 
 
 def test_pack_query_weights_layout(mla):
-    """The packed layout, element by element: fragment (i, tile, s), lane l, element e holds
-    row 16 tile + l % 16 of [W^UQ_i; W^QR_i] at k = 32 s + 8 (l / 16) + e."""
-    H, d_cq = 3, 96
+    """The packed layout, element by element, rebuilt from its definition: fragment
+    (c, i, tile, s4), lane l, element e holds row 16 tile + l % 16 of [W^UQ_i; W^QR_i] at
+    k = 32 (4 c + s4) + 8 (l / 16) + e; then W^UK piece (i, hf, j, pos) holds
+    W^UK[i*128 + j][256 hf + 8 (pos ^ f(j)) ..], f(j) = 2 (j % 4) + 8 ((j / 8) % 2)."""
+    H, d_cq = 2, 768
     g = torch.Generator().manual_seed(99)
     w_uq = torch.randn(H * 128, d_cq, generator=g).to(torch.bfloat16)
     w_qr = torch.randn(H * 64, d_cq, generator=g).to(torch.bfloat16)
+    w_uk = torch.randn(H * 128, 512, generator=g).to(torch.bfloat16)
     say("pack query weights")
-    got = mla.mla_pack_query_weights(dev(w_uq), dev(w_qr), H).cpu()
+    got = mla.mla_pack_query_weights(dev(w_uq), dev(w_qr), dev(w_uk), H).cpu()
     rows = torch.cat([w_uq.view(H, 128, d_cq), w_qr.view(H, 64, d_cq)], dim=1)  # [H, 192, d_cq]
-    want = torch.empty(H, 12, d_cq // 32, 64, 8, dtype=torch.bfloat16)
+    nc = d_cq // 128
+    # [H, 192, nc, 4, 4, 8] (row, chunk, step, k group, element) -> [H, nc, 12, 4, 64 lanes, 8]
+    r6 = rows.view(H, 12, 16, nc, 4, 4, 8)              # i, tile, n, c, s4, g, e
+    frags = r6.permute(3, 0, 1, 4, 5, 2, 6).reshape(-1)  # c, i, tile, s4, (g, n), e
+    f = lambda j: 2 * (j % 4) + 8 * ((j // 8) % 2)
+    uk = torch.empty(H, 2, 128, 32, 8, dtype=torch.bfloat16)
     for i in range(H):
-        for tl in range(12):
-            for s_ in range(d_cq // 32):
-                for l in range(64):
-                    k = 32 * s_ + 8 * (l // 16)
-                    want[i, tl, s_, l] = rows[i, 16 * tl + l % 16, k:k + 8]
-    assert torch.equal(got, want.reshape(-1))
+        for hf in range(2):
+            for j in range(128):
+                for pos in range(32):
+                    c0 = 256 * hf + 8 * (pos ^ f(j))
+                    uk[i, hf, j, pos] = w_uk[i * 128 + j, c0:c0 + 8]
+    assert got.numel() == mla.query_pack_elems(H, d_cq)
+    assert torch.equal(got[:frags.numel()], frags)
+    assert torch.equal(got[frags.numel():], uk.reshape(-1))
 
 
 def reference(c_q, wts, seq_lens, base=10000.0):
