@@ -125,16 +125,16 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     0.3 s warmup of the whole chain), its algorithmic bytes (weights, cache rows,
     activations in and out at their stored dtypes) and its fraction of the 8 TB/s HBM
     roofline (every step is HBM-bound at this batch); then the whole chain, and the fp64
-    oracle's layer on a few of the sequences.  The projections that share an input run as
-    one product over their stacked weights ([W^DQ; W^DKV; W^KR] h, [W^UQ; W^QR] c^Q; the
-    weights are stacked once at load time, outside the timing), the append reads its inputs
+    oracle's layer on a few of the sequences.  In the chain every result is the same from
+    run to run (checked: two runs, u bit for bit): [W^DQ; W^DKV; W^KR] h and W^O are split-k
+    products summed in a fixed order (mla_linear_deterministic), the append reads its inputs
     in place, the query side ([W^UQ; W^QR] c^Q, RoPE, absorption) is one launch reading c^Q in
-    place (its weights packed once at load time, outside the timing), the split-K combine is fused with W^UV, and in the timed chain the products
-    accumulate into outputs cleared by one fill at its start.  Timed beside it: the chain
-    with the query side as two launches (the stacked product, then the absorption), with
-    dense outputs (each product zeroing its own), with the combine and W^UV as two
-    launches, and the chain of separate products.  The fused steps' algorithmic bytes are
-    their weights, inputs and outputs: q^C, q^R and the combined latent are never stored."""
+    place (its weights packed once at load time, outside the timing), and the split-K combine
+    is fused with W^UV.  Timed beside it: the chain with fp32-atomic projections
+    accumulating into outputs cleared by one fill, with the query side as two launches (the
+    stacked product, then the absorption), with the combine and W^UV as two launches, and
+    the chain of separate products.  The fused steps' algorithmic bytes are their weights,
+    inputs and outputs: q^C, q^R and the combined latent are never stored."""
     x = W.layer_b64_t2k()
     s = x["shape"]
     B, H, d_h, d_c, d_R, d, d_cq = s.B, s.H, s.d_h, s.d_c, s.d_R, x["d"], x["d_cq"]
@@ -146,7 +146,7 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     h, cache, bt, before = cu(x["h"]), cu(x["cache"]), cu(x["block_table"]), cu(x["seq_lens_before"])
     f32 = dict(device="cuda", dtype=torch.float32)
     n_a, n_b = d_cq + d_c + d_R, H * (d_h + d_R)
-    outs = torch.empty(B * (n_a + d), **f32)  # y_a and u, cleared by one fill
+    outs = torch.empty(B * (n_a + d), **f32)  # y_a and u (cleared by one fill where accumulated)
     y_a, u = outs[:B * n_a].view(B, n_a), outs[B * n_a:].view(B, d)
     y_b = torch.empty(B, n_b, **f32)            # q^C | q^R of the two-launch query side
     c_q, c_kv, k_r = y_a[:, :d_cq], y_a[:, d_cq:d_cq + d_c], y_a[:, d_cq + d_c:]
@@ -161,9 +161,14 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     o_lat, o_heads = torch.empty(B, H, d_c, **f32), torch.empty(B, H, d_h, **f32)
     nb = lambda t: t.numel() * t.element_size()
     tokens = int(seq_lens.sum())
+    # the projections run with a fixed summation order (split-k partials summed in order):
+    # one workspace serves both, since they run one after the other on the stream
+    ws_lin = torch.empty(max(mla.mla_linear_deterministic_workspace_bytes(B, n_a, d),
+                             mla.mla_linear_deterministic_workspace_bytes(B, d, H * d_h)),
+                         dtype=torch.uint8, device="cuda")
     rows = [
-        ("7 mla_linear [W^DQ; W^DKV; W^KR] h",
-         [mla.bind(mla.mla_linear, h, w_a, y_a)], nb(w_a) + nb(h) + nb(y_a)),
+        ("7 mla_linear_deterministic [W^DQ; W^DKV; W^KR] h",
+         [mla.bind(mla.mla_linear_deterministic, h, w_a, y_a, ws_lin)], nb(w_a) + nb(h) + nb(y_a)),
         ("2 mla_kv_append_strided", [mla.bind(mla.mla_kv_append_strided, c_kv.unsqueeze(1),
                                               k_r.unsqueeze(1), before, bt, cache, x["rope_base"])],
          B * (d_c + d_R) * 4 + B * (d_c + d_R) * 2),
@@ -177,10 +182,16 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
         ("4+5 mla_combine_out_proj (combine fused with W^UV)",
          [mla.bind(mla.mla_combine_out_proj, o_part, lse_part, w["w_uv"], o_heads)],
          nb(w["w_uv"]) + nb(o_heads)),
-        ("6 W^O (mla_linear on the concatenated heads)",
-         [mla.bind(mla.mla_linear, o_heads.view(B, H * d_h), w["w_o"], u)],
+        ("6 W^O (mla_linear_deterministic on the concatenated heads)",
+         [mla.bind(mla.mla_linear_deterministic, o_heads.view(B, H * d_h), w["w_o"], u, ws_lin)],
          nb(w["w_o"]) + nb(o_heads) + nb(u)),
     ]
+    # the same two products with fp32 atomic split-k (not in the main chain)
+    atomic_rows = [
+        ("7 mla_linear [W^DQ; W^DKV; W^KR] h",
+         mla.bind(mla.mla_linear, h, w_a, y_a), nb(w_a) + nb(h) + nb(y_a)),
+        ("6 W^O (mla_linear)", mla.bind(mla.mla_linear, o_heads.view(B, H * d_h), w["w_o"], u),
+         nb(w["w_o"]) + nb(o_heads) + nb(u))]
     # the query side as two launches: the stacked product [W^UQ; W^QR] c^Q, then the
     # absorption (with the RoPE) reading q^C and q^R in place
     two_launch_query = [
@@ -208,47 +219,49 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
         mla.bind(mla.mla_absorb_q, sep["q_c"].view(B, H, d_h), w["w_uk"], sep["q_r"].view(B, H, d_R),
                  seq_lens, x["rope_base"], q_lat, q_pe),
     ] + unfused_back
+    # the main chain: every step's result is the same from run to run
     chain = [c for _, calls, _ in rows for c in calls]
 
-    # the same calls with the products accumulating into outputs cleared together by one
-    # fill at the start of the layer (y_a, y_b and u share one buffer), so the split-k kernels
-    # launch no zero fills of their own: two kernels fewer on the one stream
-    acc_chain = ([mla.bind(mla.mla_linear_strided, h, w_a, y_a, accumulate=True)]
-                 + [rows[i][1][0] for i in (1, 2, 3, 4)]
-                 + [mla.bind(mla.mla_linear_strided, o_heads.view(B, H * d_h), w["w_o"], u,
-                             accumulate=True)])
-
-    def run_with_fill(calls):
+    def run_calls(calls, fill=False):
         def go():
-            outs.zero_()
+            if fill:
+                outs.zero_()
             for c in calls:
                 c()
         return go
 
-    accumulate_chain = run_with_fill(acc_chain)
+    main_chain = run_calls(chain)
+    # the atomic split-k products accumulating into outputs cleared together by one fill at
+    # the start of the layer (y_a and u share one buffer), so they launch no zero fills
+    acc_chain = ([mla.bind(mla.mla_linear_strided, h, w_a, y_a, accumulate=True)] + chain[1:5]
+                 + [mla.bind(mla.mla_linear_strided, o_heads.view(B, H * d_h), w["w_o"], u,
+                             accumulate=True)])
+    atomic_chain = run_calls(acc_chain, fill=True)
     # attention + combine, then W^UV: two launches in place of the fused one
-    accumulate_unfused = run_with_fill(acc_chain[:3] + unfused_back[:2] + acc_chain[5:])
+    unfused_chain = run_calls(chain[:3] + unfused_back[:2] + chain[5:])
     # the query side as two launches in place of mla_query_path
-    accumulate_two_launch = run_with_fill(acc_chain[:2] + [c for _, c, _ in two_launch_query]
-                                          + acc_chain[3:])
+    two_launch_chain = run_calls(chain[:2] + [c for _, c, _ in two_launch_query] + chain[3:])
 
-    for c in chain:
-        c()
+    main_chain()
     torch.cuda.synchronize()
-    u_dense = u.clone()
-    accumulate_chain()
+    u_det = u.clone()
+    main_chain()
     torch.cuda.synchronize()
-    acc_vs_dense = float((u - u_dense).abs().max() / u_dense.abs().max())
-    accumulate_two_launch()
+    rerun_identical = bool(torch.equal(u, u_det))
+    atomic_chain()
     torch.cuda.synchronize()
-    two_vs_one = float((u - u_dense).abs().max() / u_dense.abs().max())
+    atomic_vs_det = float((u - u_det).abs().max() / u_det.abs().max())
+    two_launch_chain()
+    torch.cuda.synchronize()
+    two_vs_one = float((u - u_det).abs().max() / u_det.abs().max())
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < 0.3:
-        for c in chain + separate:
+        for c in separate:
             c()
-        accumulate_chain()
-        accumulate_unfused()
-        accumulate_two_launch()
+        main_chain()
+        atomic_chain()
+        unfused_chain()
+        two_launch_chain()
         torch.cuda.synchronize()
 
     def timed(fn, n=20):
@@ -269,6 +282,12 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
         out[name] = {"us": round(us, 2), "bytes_algorithmic": int(byts), "GBps": round(gbps, 1),
                      "roofline_frac": round(gbps / HBM_PEAK_GBPS, 4)}
         total_bytes += byts
+    for name, call, byts in atomic_rows:
+        us = timed(call)
+        gbps = byts / us / 1e3
+        out[name + " (atomic split-k; not in the chain)"] = {
+            "us": round(us, 2), "bytes_algorithmic": int(byts), "GBps": round(gbps, 1),
+            "roofline_frac": round(gbps / HBM_PEAK_GBPS, 4)}
     two_us = 0.0
     for name, call, byts in two_launch_query:
         us = timed(call)
@@ -277,11 +296,11 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
         out[name + " (the query side as two launches; not in the chain)"] = {
             "us": round(us, 2), "bytes_algorithmic": int(byts), "GBps": round(gbps, 1),
             "roofline_frac": round(gbps / HBM_PEAK_GBPS, 4)}
-    dense_us = timed(lambda: [c() for c in chain])
     separate_us = timed(lambda: [c() for c in separate])
-    chain_us = timed(accumulate_chain)
-    unfused_us = timed(accumulate_unfused)
-    two_launch_us = timed(accumulate_two_launch)
+    chain_us = timed(main_chain)
+    atomic_us = timed(atomic_chain)
+    unfused_us = timed(unfused_chain)
+    two_launch_us = timed(two_launch_chain)
 
     # Offline folds, measured only, with the weights prepared once by the library outside the
     # timing.  W~ = W^UK^T W^UQ ([H d_c, d_c^Q], 201 MB of bf16) makes q~ = W~ c^Q one
@@ -327,15 +346,15 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
            "chain_GBps": round(total_bytes / chain_us / 1e3, 1),
            "chain_roofline_frac": round(total_bytes / chain_us / 1e3 / HBM_PEAK_GBPS, 4),
            "sequences_per_s": round(B / (chain_us * 1e-6), 1),
-           "chain_schedule": "one stream; stacked products accumulating into outputs cleared "
-                             "by one fill at the start; the query side in one launch; combine "
-                             "fused with W^UV",
+           "chain_schedule": "one stream; stacked projections with a fixed summation order; "
+                             "the query side in one launch; combine fused with W^UV",
+           "chain_bit_identical_reruns": rerun_identical,
+           "chain_atomic_projections_us": round(atomic_us, 2),
+           "atomic_vs_deterministic_max_rel_diff_u": round(atomic_vs_det, 6),
            "chain_two_launch_query_us": round(two_launch_us, 2),
            "two_launch_query_vs_one_max_rel_diff_u": round(two_vs_one, 6),
-           "chain_dense_outputs_us": round(dense_us, 2),
            "chain_unfused_combine_us": round(unfused_us, 2),
-           "chain_separate_products_us": round(separate_us, 2),
-           "accumulate_vs_dense_max_rel_diff": round(acc_vs_dense, 6)}
+           "chain_separate_products_us": round(separate_us, 2)}
     if oracle_seqs > 0:
         import oracle
         wf = {k: W.to_f64(v) for k, v in x["weights"].items()}

@@ -83,6 +83,9 @@ _SIGNATURES = {
     "mla_decode_noalloc": (_I32, [_P, _P, _P, _P, _P, _SP, _F, _I32, _P, _P, _I32, _P]),
     "mla_out_proj": (_I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "mla_linear": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _P]),
+    "mla_linear_deterministic_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "mla_linear_deterministic": (_I32, [_P, _I32, _I64, _P, _I32, _I32, _I32, _I32, _P, _I64,
+                                        _I32, _P, _SZ, _P]),
     "mla_linear_strided": (_I32, [_P, _I32, _I64, _P, _I32, _I32, _I32, _I32, _P, _I64, _I32,
                                   _P]),
     "mla_linear_planned": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _I32, _I32, _I32,
@@ -774,6 +777,27 @@ def mla_linear_strided(x, w, y, accumulate=False, stream=None):
     _invoke("mla_linear_strided", x_ptr, _dtype_code(x), ldx, _dev(w, "w", None, 2),
                                   _dtype_code(w), M, N, K, y_ptr, ldy, int(bool(accumulate)),
                                   _stream(stream))
+
+
+def mla_linear_deterministic_workspace_bytes(M, N, K):
+    """Workspace bytes mla_linear_deterministic needs for an [M,K] x [N,K]^T product (0: the
+    shape is not supported)."""
+    return int(lib.mla_linear_deterministic_workspace_bytes(int(M), int(N), int(K)))
+
+
+def mla_linear_deterministic(x, w, y, workspace, accumulate=False, stream=None):
+    """mla_linear_strided with a fixed summation order (bit-identical reruns): split-k partial
+    tiles go to `workspace` (a uint8 GPU tensor of at least
+    mla_linear_deterministic_workspace_bytes(M, N, K) bytes) and are summed in order into y."""
+    torch = _torch()
+    M, K = x.shape
+    N = w.shape[0]
+    _expect(w.shape[1] == K and tuple(y.shape) == (M, N), "shapes must be x[M,K] w[N,K] y[M,N]")
+    x_ptr, ldx = _dev_rows(x, "x", None, 2, 1)
+    y_ptr, ldy = _dev_rows(y, "y", torch.float32, 2, 1)
+    _invoke("mla_linear_deterministic", x_ptr, _dtype_code(x), ldx, _dev(w, "w", None, 2),
+            _dtype_code(w), M, N, K, y_ptr, ldy, int(bool(accumulate)),
+            _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
 
 
 def mla_linear_planned(x, w, y, kernel, tile, split, ring, stream=None):

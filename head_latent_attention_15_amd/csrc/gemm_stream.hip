@@ -10,8 +10,10 @@
 // column tile (64 TN output columns) by 128 k, numbered tile-major, and each workgroup (one
 // per CU) takes an equal run of consecutive units.  Its weight stream never restarts: the
 // ring of weight fragments runs on across unit and tile boundaries, and the partial sums of
-// a tile are flushed into y (fp32 atomics; y zeroed first unless the caller accumulates)
-// when the run leaves the tile.
+// a tile are flushed when the run leaves the tile: into y with fp32 atomics (y zeroed first
+// unless the caller accumulates), or, in the deterministic form, with plain stores into the
+// tile's own slot of a caller workspace, which gemm_stream_reduce then sums in one fixed
+// order (slice, then run) into y.
 //
 // A workgroup has two roles.  Waves 0-3 (consumers) own TN column tiles of 16 each and all
 // four 16-row tiles of x; the bf16 weight rows go from HBM straight into MFMA B-operand
@@ -95,6 +97,10 @@ struct StreamArgs {
   int NCH;  // units (128-wide k chunks) per tile
   int nu;   // units per workgroup
   int ksl;  // k slices (1, 2, 4 or 8): workgroup g works in slice (g % 8) % ksl
+  // deterministic form (part != nullptr): the partial tile of run q of slice sl for tile t
+  // goes to slot (sl * ntiles + t) * jmax + q - (t * cps) / nu, M rows of 64 TN floats
+  float* part;
+  int ntiles, jmax;
 };
 
 // Work units.  Workgroups go to the 8 XCDs in turn (g -> XCD g % 8).  The k chunks are cut
@@ -106,10 +112,10 @@ struct Unit {
   bool tile_end;  // last unit of its tile inside the slice
 };
 struct UnitMap {
-  int slice, cps, v0, nu, NB;
+  int slice, cps, run, v0, nu, NB;
   __device__ UnitMap(const StreamArgs& a, int g)
-      : slice((g & 7) % a.ksl), cps(a.NCH / a.ksl),
-        v0(((g >> 3) * (8 / a.ksl) + (g & 7) / a.ksl) * a.nu), nu(a.nu), NB(a.NB) {}
+      : slice((g & 7) % a.ksl), cps(a.NCH / a.ksl), run((g >> 3) * (8 / a.ksl) + (g & 7) / a.ksl),
+        v0(run * a.nu), nu(a.nu), NB(a.NB) {}
   // unit i of the run; past the run it repeats the last unit
   __device__ Unit operator()(int i) const {
     const int v = v0 + min(i, nu - 1);
@@ -124,7 +130,7 @@ struct UnitMap {
 // (they end with a full wait on their own memory operations: the compiler lays the role
 // split out with a path from the end of this code into the producers', and would otherwise
 // merge this role's outstanding loads into the producers' wait counts)
-template <typename XT, int TN, int R>
+template <typename XT, int TN, int R, bool DET>
 __device__ __forceinline__ void consume(const XT* x, const bf16raw* w, float* y,
                                         const StreamArgs& a, lds_char_t* lsm, int wave, int g,
                                         int r, int nu, const UnitMap& unit_of) {
@@ -201,20 +207,38 @@ __device__ __forceinline__ void consume(const XT* x, const bf16raw* w, float* y,
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // the run leaves this tile after unit i: add its partial sums into y
+      // the run leaves this tile after unit i: add its partial sums into y, or store them
+      // in the tile's slot of the workspace
       const Unit u = unit_of(i);
       if (i == nu - 1 || u.tile_end) {
-        float* yt = y + u.z * a.sy + static_cast<int64_t>(u.cb) * CW + col;
+        if constexpr (DET) {
+          const int t = u.z * a.NB + u.cb;
+          const int q = unit_of.run - (t * unit_of.cps) / nu;
+          float* pt = a.part +
+                      ((static_cast<int64_t>(unit_of.slice) * a.ntiles + t) * a.jmax + q) * a.M * CW + col;
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+          for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int m = 16 * mt + 4 * g + e;
-              if (m < a.M) atomicAdd(yt + static_cast<int64_t>(m) * a.ldy + 16 * j, acc[j][mt][e]);
-              acc[j][mt][e] = 0.f;
-            }
+              for (int e = 0; e < 4; ++e) {
+                const int m = 16 * mt + 4 * g + e;
+                if (m < a.M) pt[m * CW + 16 * j] = acc[j][mt][e];
+                acc[j][mt][e] = 0.f;
+              }
+        } else {
+          float* yt = y + u.z * a.sy + static_cast<int64_t>(u.cb) * CW + col;
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int m = 16 * mt + 4 * g + e;
+                if (m < a.M) atomicAdd(yt + static_cast<int64_t>(m) * a.ldy + 16 * j, acc[j][mt][e]);
+                acc[j][mt][e] = 0.f;
+              }
+        }
       }
       __syncthreads();
     }
@@ -222,7 +246,7 @@ __device__ __forceinline__ void consume(const XT* x, const bf16raw* w, float* y,
   wait_vmcnt<0>();
 }
 
-template <typename XT, int TN, int R>
+template <typename XT, int TN, int R, bool DET>
 __global__ __launch_bounds__(512) void gemm_stream_kernel(const XT* x, const bf16raw* w,
                                                           float* y, StreamArgs a) {
   constexpr bool SPLIT_X = std::is_same<XT, float>::value;  // fp32 x: hi + lo planes
@@ -242,7 +266,7 @@ __global__ __launch_bounds__(512) void gemm_stream_kernel(const XT* x, const bf1
   const uint32_t smem_lds = static_cast<uint32_t>(reinterpret_cast<size_t>(lsm));
 
   if (wave < 4) {
-    consume<XT, TN, R>(x, w, y, a, lsm, wave, g, r, nu, unit_of);
+    consume<XT, TN, R, DET>(x, w, y, a, lsm, wave, g, r, nu, unit_of);
   } else {
     // ---------------- producers: x of unit i -> plane buffer i % NPL ----------------
     // Wave p stages rows 16 p .. 16 p + 15 with LDS DMA copies of 1 KB (its only global
@@ -332,28 +356,63 @@ __global__ __launch_bounds__(256) void zero_rows_stream(float* __restrict__ y, i
   }
 }
 
-template <typename XT, int TN, int R>
+// Deterministic form, second pass: y[z][m][n] (+)= the partial tiles of column tile
+// t = z * NB + n / CW summed slice by slice, run by run (runs q0 .. q1 of each slice cover
+// the tile's units t * cps .. (t + 1) * cps - 1).  One thread per 4 columns.
+__global__ __launch_bounds__(256) void gemm_stream_reduce(const float* __restrict__ part,
+                                                          float* __restrict__ y, StreamArgs a,
+                                                          int CW, int batch, int accumulate) {
+  const int cps = a.NCH / a.ksl;
+  const int64_t quads = static_cast<int64_t>(batch) * a.M * (a.N / 4);
+  for (int64_t id = blockIdx.x * 256ll + threadIdx.x; id < quads; id += static_cast<int64_t>(gridDim.x) * 256) {
+    const int n = static_cast<int>(id % (a.N / 4)) * 4;
+    const int64_t zm = id / (a.N / 4);
+    const int m = static_cast<int>(zm % a.M), z = static_cast<int>(zm / a.M);
+    const int t = z * a.NB + n / CW, c = n % CW;
+    const int q0 = (t * cps) / a.nu, q1 = ((t + 1) * cps - 1) / a.nu;
+    float* yp = y + z * a.sy + static_cast<int64_t>(m) * a.ldy + n;
+    float4 sum = accumulate ? make_float4(yp[0], yp[1], yp[2], yp[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sl = 0; sl < a.ksl; ++sl)
+      for (int q = q0; q <= q1; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(
+            part + ((static_cast<int64_t>(sl) * a.ntiles + t) * a.jmax + q - q0) * a.M * CW +
+            static_cast<int64_t>(m) * CW + c);
+        sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+      }
+    yp[0] = sum.x; yp[1] = sum.y; yp[2] = sum.z; yp[3] = sum.w;
+  }
+}
+
+template <typename XT, int TN, int R, bool DET>
 hipError_t launch_t(const GemmArgs& g, const StreamArgs& a, int grid, hipStream_t s) {
   const int64_t rows = static_cast<int64_t>(g.batch) * g.M;
   const int gx = static_cast<int>(std::min<int64_t>((g.N + 1023) / 1024, 64));
   const int gy = static_cast<int>(std::min<int64_t>(rows, 4096));
-  if (!g.accumulate)
+  if (!g.accumulate && !a.part)
     hipLaunchKernelGGL(zero_rows_stream, dim3(gx, gy), dim3(256), 0, s,
                        static_cast<float*>(g.y), g.ldy, g.sy, g.M, g.N, g.batch);
-  hipLaunchKernelGGL((gemm_stream_kernel<XT, TN, R>), dim3(grid), dim3(512), 0, s,
+  hipLaunchKernelGGL((gemm_stream_kernel<XT, TN, R, DET>), dim3(grid), dim3(512), 0, s,
                      static_cast<const XT*>(g.x), static_cast<const bf16raw*>(g.w),
                      static_cast<float*>(g.y), a);
+  if constexpr (DET) {
+    const int64_t quads = rows * (g.N / 4);
+    const int rg = static_cast<int>(std::min<int64_t>((quads + 255) / 256, 4096));
+    hipLaunchKernelGGL(gemm_stream_reduce, dim3(rg), dim3(256), 0, s, a.part,
+                       static_cast<float*>(g.y), a, 64 * TN, g.batch, g.accumulate ? 1 : 0);
+  }
   return hipGetLastError();
 }
 
 template <typename XT, int TN>
 hipError_t launch_r(const GemmArgs& g, const StreamArgs& a, int grid, int R, hipStream_t s) {
+  if (a.part)  // the deterministic form is built for the planned ring only
+    return R == 4 ? launch_t<XT, TN, 4, true>(g, a, grid, s) : hipErrorInvalidValue;
   switch (R) {
-    case 4: return launch_t<XT, TN, 4>(g, a, grid, s);
-    case 8: return launch_t<XT, TN, 8>(g, a, grid, s);
-    case 12: if constexpr (TN <= 2) return launch_t<XT, TN, 12>(g, a, grid, s); else break;
-    case 16: if constexpr (TN <= 2) return launch_t<XT, TN, 16>(g, a, grid, s); else break;
-    case 20: if constexpr (TN <= 2) return launch_t<XT, TN, 20>(g, a, grid, s); else break;
+    case 4: return launch_t<XT, TN, 4, false>(g, a, grid, s);
+    case 8: return launch_t<XT, TN, 8, false>(g, a, grid, s);
+    case 12: if constexpr (TN <= 2) return launch_t<XT, TN, 12, false>(g, a, grid, s); else break;
+    case 16: if constexpr (TN <= 2) return launch_t<XT, TN, 16, false>(g, a, grid, s); else break;
+    case 20: if constexpr (TN <= 2) return launch_t<XT, TN, 20, false>(g, a, grid, s); else break;
     default: break;
   }
   return hipErrorInvalidValue;
@@ -413,8 +472,8 @@ void gemm_stream_plan(const GemmArgs& g, int* tn, int* grid, int* ring) {
   *tn = 1; *grid = 1; *ring = 4;
 }
 
-hipError_t launch_gemm_stream_with(const GemmArgs& g, int tn, int grid, int ring, hipStream_t s) {
-  if (!gemm_stream_plan_ok(g, tn, grid, ring)) return hipErrorInvalidValue;
+namespace {
+StreamArgs stream_args(const GemmArgs& g, int tn, int grid) {
   StreamArgs a;
   a.ldx = g.ldx; a.sx = g.sx; a.ldw = g.ldw; a.sw = g.sw; a.ldy = g.ldy; a.sy = g.sy;
   a.M = g.M; a.N = g.N;
@@ -425,6 +484,19 @@ hipError_t launch_gemm_stream_with(const GemmArgs& g, int tn, int grid, int ring
   if (g.batch == 1 && grid % 8 == 0)
     for (int k = 8; k > 1; k /= 2)
       if (a.NCH % k == 0) { a.ksl = k; break; }
+  a.part = nullptr;
+  a.ntiles = g.batch * a.NB;
+  const int cps = a.NCH / a.ksl;
+  a.jmax = (cps + a.nu - 1) / a.nu + 1;  // runs that can meet one tile inside a slice
+  return a;
+}
+
+size_t part_bytes(const GemmArgs& g, const StreamArgs& a, int tn) {
+  return static_cast<size_t>(a.ksl) * a.ntiles * a.jmax * g.M * 64 * tn * sizeof(float);
+}
+
+hipError_t launch_args(const GemmArgs& g, const StreamArgs& a, int tn, int grid, int ring,
+                       hipStream_t s) {
   if (g.x_bf16) {
     switch (tn) {
       case 4: return launch_r<bf16raw, 4>(g, a, grid, ring, s);
@@ -437,6 +509,32 @@ hipError_t launch_gemm_stream_with(const GemmArgs& g, int tn, int grid, int ring
     case 2: return launch_r<float, 2>(g, a, grid, ring, s);
     default: return launch_r<float, 1>(g, a, grid, ring, s);
   }
+}
+}  // namespace
+
+size_t gemm_stream_det_workspace_bytes(const GemmArgs& g) {
+  if (!gemm_stream_supported(g)) return 0;
+  int tn = 1, grid = 1, ring = 4;
+  gemm_stream_plan(g, &tn, &grid, &ring);
+  return part_bytes(g, stream_args(g, tn, grid), tn);
+}
+
+hipError_t launch_gemm_stream_det(const GemmArgs& g, void* part, size_t bytes, hipStream_t s) {
+  int tn = 1, grid = 1, ring = 4;
+  gemm_stream_plan(g, &tn, &grid, &ring);
+  if (!gemm_stream_plan_ok(g, tn, grid, ring)) return hipErrorInvalidValue;
+  StreamArgs a = stream_args(g, tn, grid);
+  if (!part || bytes < part_bytes(g, a, tn) || (reinterpret_cast<uintptr_t>(part) & 15) ||
+      g.N % 4 || (g.ldy % 4) || (g.sy % 4) || (reinterpret_cast<uintptr_t>(g.y) & 15))
+    return hipErrorInvalidValue;
+  a.part = static_cast<float*>(part);
+  return launch_args(g, a, tn, grid, ring, s);
+}
+
+hipError_t launch_gemm_stream_with(const GemmArgs& g, int tn, int grid, int ring, hipStream_t s) {
+  if (!gemm_stream_plan_ok(g, tn, grid, ring)) return hipErrorInvalidValue;
+  const StreamArgs a = stream_args(g, tn, grid);
+  return launch_args(g, a, tn, grid, ring, s);
 }
 
 hipError_t launch_gemm_stream(const GemmArgs& g, hipStream_t s) {

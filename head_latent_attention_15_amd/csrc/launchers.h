@@ -119,6 +119,11 @@ void gemm_stream_plan(const GemmArgs& g, int* tn, int* grid, int* ring);
 bool gemm_stream_plan_ok(const GemmArgs& g, int tn, int grid, int ring);
 hipError_t launch_gemm_stream_with(const GemmArgs& g, int tn, int grid, int ring, hipStream_t s);
 hipError_t launch_gemm_stream(const GemmArgs& g, hipStream_t s);
+// Deterministic form: partial tiles into a workspace of gemm_stream_det_workspace_bytes(g)
+// (0 where the kernel does not apply), then a fixed-order sum into y.  Needs N, ldy and sy
+// multiples of 4 and 16-byte aligned y and workspace.
+size_t gemm_stream_det_workspace_bytes(const GemmArgs& g);
+hipError_t launch_gemm_stream_det(const GemmArgs& g, void* part, size_t bytes, hipStream_t s);
 // Activation-stationary form for M <= 64, N a multiple of 128 and K of 256: a workgroup
 // stages one k slice (32 s values) of x in LDS once and streams the weights of a run of
 // 128 tn-column tiles in it.  The plan picks tn (1, 2), s (8, 12, 16, 20) and the grid.

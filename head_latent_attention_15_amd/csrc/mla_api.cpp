@@ -776,6 +776,53 @@ mla_status_t mla_linear_strided(const void* x, mla_dtype_t x_dtype, int64_t ldx,
                 stream);
 }
 
+static mla::GemmArgs det_args(const void* x, mla_dtype_t x_dtype, int64_t ldx, const void* w,
+                              int32_t M, int32_t N, int32_t K, float* y, int64_t ldy,
+                              int32_t accumulate) {
+  mla::GemmArgs g;
+  g.x = x; g.ldx = ldx; g.sx = 0; g.x_bf16 = x_dtype == MLA_BF16;
+  g.w = w; g.ldw = K; g.sw = 0; g.w_bf16 = 1; g.w_nk = true;
+  g.y = y; g.ldy = ldy; g.sy = 0; g.y_bf16 = 0;
+  g.M = M; g.N = N; g.K = K; g.batch = 1;
+  g.accumulate = accumulate != 0;
+  return g;
+}
+
+size_t mla_linear_deterministic_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  if (M < 1 || N < 1 || K < 1) return 0;
+  // any 256-byte aligned pointers and dense strides: the size depends on the shape only
+  static const char probe[1] = {0};
+  const void* p = reinterpret_cast<const void*>(
+      (reinterpret_cast<uintptr_t>(probe) + 255) & ~static_cast<uintptr_t>(255));
+  const mla::GemmArgs g = det_args(p, MLA_F32, K, p, M, N, K, static_cast<float*>(const_cast<void*>(p)), N, 0);
+  return mla::gemm_stream_det_workspace_bytes(g);
+}
+
+mla_status_t mla_linear_deterministic(const void* x, mla_dtype_t x_dtype, int64_t ldx,
+                                      const void* w, mla_dtype_t w_dtype, int32_t M, int32_t N,
+                                      int32_t K, float* y, int64_t ldy, int32_t accumulate,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "mla_linear_deterministic";
+  if (!x || !w || !y || !workspace) return fail(MLA_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (M < 1 || N < 1 || K < 1) return fail(MLA_ERR_SHAPE, "%s: sizes must be >= 1", fn);
+  if (ldx < K || ldy < N)
+    return fail(MLA_ERR_SHAPE, "%s: row strides ldx %lld < K or ldy %lld < N", fn,
+                static_cast<long long>(ldx), static_cast<long long>(ldy));
+  if (!is_dtype(x_dtype) || w_dtype != MLA_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: bf16 weights required", fn);
+  const mla::GemmArgs g = det_args(x, x_dtype, ldx, w, M, N, K, y, ldy, accumulate);
+  const size_t need = mla::gemm_stream_det_workspace_bytes(g);
+  if (need == 0 || N % 4 || ldy % 4 || (reinterpret_cast<uintptr_t>(y) & 15) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 15))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "%s: needs M <= 64, N %% 64 == 0, K %% 128 == 0, ldx %% 8 == 0, ldy %% 4 == 0 "
+                "and 16-byte aligned x, w, y and workspace (M %d, N %d, K %d)", fn, M, N, K);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, workspace_bytes, need);
+  return launched(mla::launch_gemm_stream_det(g, workspace, workspace_bytes, as_stream(stream)),
+                  "deterministic linear GEMM");
+}
+
 mla_status_t mla_linear_planned(const void* x, mla_dtype_t x_dtype, const void* w,
                                 mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K, float* y,
                                 int32_t kernel, int32_t tile, int32_t split, int32_t ring,

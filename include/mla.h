@@ -489,6 +489,26 @@ mla_status_t mla_linear_strided(const void* x, mla_dtype_t x_dtype, int64_t ldx,
                                 mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K, float* y,
                                 int64_t ldy, int32_t accumulate, void* stream);
 
+/* mla_linear_strided with results that are bit-identical from run to run: the k range is
+ * still split over workgroups, but each workgroup stores its partial sums of a column tile
+ * in that tile's own slot of a caller workspace (plain stores, no atomics) and a second
+ * launch adds the slots of every tile in one fixed order into y (after y's prior value when
+ * accumulate != 0).  Same products and roundings as mla_linear up to the order of the fp32
+ * additions, which is fixed here.  Used for the projections of a decode step
+ * ([W^DQ; W^DKV; W^KR] h, W^O [o_1; ...; o_H]; qiita.com/joule/items/57d9b3f4fc27959eaa0d,
+ * "Query の圧縮", "Attention 計算").
+ *   x [M rows of ldx] x_dtype (f32 or bf16);  w [N][K] bf16;  y [M rows of ldy] fp32
+ *   workspace: at least mla_linear_deterministic_workspace_bytes(M, N, K) bytes, 16-byte
+ *   aligned, caller-owned, scratch (its contents on entry do not matter)
+ * Needs M <= 64, N % 64 == 0, K % 128 == 0, ldx % 8 == 0, ldy % 4 == 0 and 16-byte aligned
+ * x, w, y, workspace, else UNSUPPORTED.
+ * Errors: NULL, SHAPE (sizes < 1, ldx < K, ldy < N), UNSUPPORTED, WORKSPACE (too small). */
+size_t mla_linear_deterministic_workspace_bytes(int32_t M, int32_t N, int32_t K);
+mla_status_t mla_linear_deterministic(const void* x, mla_dtype_t x_dtype, int64_t ldx,
+                                      const void* w, mla_dtype_t w_dtype, int32_t M, int32_t N,
+                                      int32_t K, float* y, int64_t ldy, int32_t accumulate,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Device-side check of the paging indices: counts sequences whose seq_len is negative or
  * exceeds max_pages_per_seq*page_size, and referenced block-table entries outside
  * [0, num_pages).  Writes the count to *dev_count (device int32; 0 = valid).

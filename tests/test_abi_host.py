@@ -268,3 +268,24 @@ def test_combine_out_proj_validation():
     assert L.mla_combine_out_proj(*args(wdt=0)) == mla.MLA_ERR_UNSUPPORTED
     assert L.mla_combine_out_proj(*args(pdt=5)) == mla.MLA_ERR_UNSUPPORTED
     assert L.mla_combine_out_proj(*args(o=FAKE + 8)) == mla.MLA_ERR_UNSUPPORTED
+
+
+def test_linear_deterministic_validation():
+    """mla_linear_deterministic refuses bad arguments before launching, and sizes its
+    workspace from the shape alone."""
+    L = mla.lib
+    need = L.mla_linear_deterministic_workspace_bytes(64, 5120, 16384)
+    assert need > 0
+    assert L.mla_linear_deterministic_workspace_bytes(64, 100, 128) == 0   # N % 64 != 0
+    assert L.mla_linear_deterministic_workspace_bytes(65, 512, 128) == 0   # M > 64
+    assert L.mla_linear_deterministic_workspace_bytes(0, 512, 128) == 0
+    # x, x_dtype, ldx, w, w_dtype, M, N, K, y, ldy, accumulate, workspace, bytes, stream
+    args = lambda **k: [k.get("x", FAKE), 0, k.get("ldx", 16384), FAKE, k.get("wdt", 1), 64, 5120,
+                        16384, FAKE, k.get("ldy", 5120), 0, k.get("ws", FAKE),
+                        k.get("bytes", need), None]
+    assert L.mla_linear_deterministic(*args(x=None)) == mla.MLA_ERR_NULL
+    assert L.mla_linear_deterministic(*args(ws=None)) == mla.MLA_ERR_NULL
+    assert L.mla_linear_deterministic(*args(ldx=100)) == mla.MLA_ERR_SHAPE
+    assert L.mla_linear_deterministic(*args(wdt=0)) == mla.MLA_ERR_UNSUPPORTED
+    assert L.mla_linear_deterministic(*args(ldy=5122)) == mla.MLA_ERR_UNSUPPORTED
+    assert L.mla_linear_deterministic(*args(bytes=need - 1)) == mla.MLA_ERR_WORKSPACE

@@ -465,13 +465,14 @@ def test_stream_read_runs(mla):
 
 
 # ------------------------------------------------------------------ full decode layer
-def layer_on_gpu(mla, x, S, stacked=False, fused=False, qpath=False):
+def layer_on_gpu(mla, x, S, stacked=False, fused=False, qpath=False, det=False):
     """The whole decode layer through the C ABI: projections, cache append, absorption,
     attention + combine, W^UV and W^O.  stacked: the projections that share an input run as
     one product over their stacked weights ([W^DQ; W^DKV; W^KR] h, then [W^UQ; W^QR] c^Q
     with c^Q read in place), and the append and absorption read their inputs in place from
     those outputs through the row-strided entry points.  qpath (with stacked): the query
-    side (W^UQ, W^QR, RoPE, absorption) is one mla_query_path launch instead."""
+    side (W^UQ, W^QR, RoPE, absorption) is one mla_query_path launch instead.  det (with
+    stacked and fused): the two remaining projections run with a fixed summation order."""
     s = x["shape"]
     B, H, d_h, d_c, d_R, d, d_cq = s.B, s.H, s.d_h, s.d_c, s.d_R, x["d"], x["d_cq"]
     w = {k: dev(v) for k, v in x["weights"].items()}
@@ -487,7 +488,13 @@ def layer_on_gpu(mla, x, S, stacked=False, fused=False, qpath=False):
         w_b = torch.cat([w["w_uq"], w["w_qr"]]).contiguous()
         y_a = torch.empty(B, d_cq + d_c + d_R, **f32)
         y_b = torch.empty(B, H * (d_h + d_R), **f32)
-        mla.mla_linear(h, w_a, y_a)
+        if det:
+            ws_lin = torch.empty(max(mla.mla_linear_deterministic_workspace_bytes(B, w_a.shape[0], d),
+                                     mla.mla_linear_deterministic_workspace_bytes(B, d, H * d_h)),
+                                 dtype=torch.uint8, device="cuda")
+            mla.mla_linear_deterministic(h, w_a, y_a, ws_lin)
+        else:
+            mla.mla_linear(h, w_a, y_a)
         mla.mla_kv_append_strided(y_a[:, d_cq:d_cq + d_c].unsqueeze(1),
                                   y_a[:, d_cq + d_c:].unsqueeze(1), before, bt, cache,
                                   x["rope_base"])
@@ -521,7 +528,10 @@ def layer_on_gpu(mla, x, S, stacked=False, fused=False, qpath=False):
         lse_part = torch.empty(B, H, S, **f32)
         mla.mla_decode_attn(q_lat, q_pe, cache, bt, seq_lens, x["scale"], S, o_part, lse_part)
         mla.mla_combine_out_proj(o_part, lse_part, w["w_uv"], o_heads)
-        mla.mla_linear(o_heads.view(B, H * d_h), w["w_o"], u)
+        if det:
+            mla.mla_linear_deterministic(o_heads.view(B, H * d_h), w["w_o"], u, ws_lin)
+        else:
+            mla.mla_linear(o_heads.view(B, H * d_h), w["w_o"], u)
     else:
         ws = torch.empty(max(1, mla.mla_decode_workspace_bytes(B, H, d_c, S)), dtype=torch.uint8,
                          device="cuda")
@@ -533,15 +543,16 @@ def layer_on_gpu(mla, x, S, stacked=False, fused=False, qpath=False):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("stacked,fused,qpath", [(False, False, False), (True, False, False),
-                                                (True, True, False), (True, True, True)],
-                         ids=["separate", "stacked", "stacked-fused", "stacked-fused-qpath"])
-def test_full_layer_b64_t2k_sampled(mla, stacked, fused, qpath):
+@pytest.mark.parametrize("stacked,fused,qpath,det",
+                         [(False, False, False, False), (True, False, False, False),
+                          (True, True, False, False), (True, True, True, True)],
+                         ids=["separate", "stacked", "stacked-fused", "stacked-fused-qpath-det"])
+def test_full_layer_b64_t2k_sampled(mla, stacked, fused, qpath, det):
     """Full layer at d=5120, H=128, B=64, 2048 prior tokens + 1 appended: all 64 rows of
     u on the GPU; sequences 0 and 37 through the oracle's expanded path."""
     x = W.layer_b64_t2k()
-    say(f"layer_b64_t2k stacked={stacked} fused={fused} qpath={qpath}")
-    u, cache = layer_on_gpu(mla, x, S=4, stacked=stacked, fused=fused, qpath=qpath)
+    say(f"layer_b64_t2k stacked={stacked} fused={fused} qpath={qpath} det={det}")
+    u, cache = layer_on_gpu(mla, x, S=4, stacked=stacked, fused=fused, qpath=qpath, det=det)
     pick = [0, 37]
     ref = oracle.decode_layer(W.to_f64(x["h"]), {k: W.to_f64(v) for k, v in x["weights"].items()},
                               W.to_f64(x["cache"]), x["block_table"].numpy(),
@@ -557,20 +568,36 @@ def test_full_layer_b64_t2k_sampled(mla, stacked, fused, qpath):
         assert_bf16(row, want, "appended row")
 
 
-@pytest.mark.parametrize("stacked,fused,qpath", [(False, False, False), (True, False, False),
-                                                (True, True, False), (True, True, True)],
-                         ids=["separate", "stacked", "stacked-fused", "stacked-fused-qpath"])
-def test_small_layer_chain(mla, stacked, fused, qpath):
+@pytest.mark.parametrize("stacked,fused,qpath,det",
+                         [(False, False, False, False), (True, False, False, False),
+                          (True, True, False, False), (True, True, True, False),
+                          (True, True, True, True)],
+                         ids=["separate", "stacked", "stacked-fused", "stacked-fused-qpath",
+                              "stacked-fused-qpath-det"])
+def test_small_layer_chain(mla, stacked, fused, qpath, det):
     """A small layer (d=256, H=16, d_c=512, d_R=64, B=5, 100 prior tokens) end to end on all
     rows (d_c^Q = 384 where the one-launch query side runs, which needs a multiple of 384)."""
     x = W.layer_b64_t2k(seed=21, B=5, T=100, d=256, H=16, d_cq=384 if qpath else 96)
-    say(f"small layer stacked={stacked} fused={fused} qpath={qpath}")
-    u, _ = layer_on_gpu(mla, x, S=2, stacked=stacked, fused=fused, qpath=qpath)
+    say(f"small layer stacked={stacked} fused={fused} qpath={qpath} det={det}")
+    u, _ = layer_on_gpu(mla, x, S=2, stacked=stacked, fused=fused, qpath=qpath, det=det)
     ref = oracle.decode_layer(W.to_f64(x["h"]), {k: W.to_f64(v) for k, v in x["weights"].items()},
                               W.to_f64(x["cache"]), x["block_table"].numpy(),
                               x["seq_lens_before"].numpy(), x["shape"].d_h, x["shape"].d_R,
                               x["rope_base"], x["scale"])
     assert_bf16(host64(u), ref["u"], "small layer u")
+
+
+def test_layer_chain_reruns_bit_identical(mla):
+    """The decode layer with the fixed-order projections, the one-launch query side and the
+    fused combine: two runs from the same cache give u bit for bit (every sum in the chain
+    has one order), at the DeepSeek-V2 sizes."""
+    x = W.layer_b64_t2k()
+    say("layer_b64_t2k rerun determinism")
+    cache0 = x["cache"].clone()
+    u1, _ = layer_on_gpu(mla, x, S=4, stacked=True, fused=True, qpath=True, det=True)
+    x["cache"] = cache0
+    u2, _ = layer_on_gpu(mla, x, S=4, stacked=True, fused=True, qpath=True, det=True)
+    assert torch.equal(u1, u2)
 
 
 def test_linear_and_outproj_against_matmul(mla):
