@@ -358,7 +358,8 @@ __global__ __launch_bounds__(256) void zero_rows_stream(float* __restrict__ y, i
 
 // Deterministic form, second pass: y[z][m][n] (+)= the partial tiles of column tile
 // t = z * NB + n / CW summed slice by slice, run by run (runs q0 .. q1 of each slice cover
-// the tile's units t * cps .. (t + 1) * cps - 1).  One thread per 4 columns.
+// the tile's units t * cps .. (t + 1) * cps - 1).  One thread per 4 columns; the slots are
+// loaded eight at a time (independent loads in flight together) and added in that order.
 __global__ __launch_bounds__(256) void gemm_stream_reduce(const float* __restrict__ part,
                                                           float* __restrict__ y, StreamArgs a,
                                                           int CW, int batch, int accumulate) {
@@ -369,17 +370,28 @@ __global__ __launch_bounds__(256) void gemm_stream_reduce(const float* __restric
     const int64_t zm = id / (a.N / 4);
     const int m = static_cast<int>(zm % a.M), z = static_cast<int>(zm / a.M);
     const int t = z * a.NB + n / CW, c = n % CW;
-    const int q0 = (t * cps) / a.nu, q1 = ((t + 1) * cps - 1) / a.nu;
+    const int q0 = (t * cps) / a.nu, nq = ((t + 1) * cps - 1) / a.nu - q0 + 1;
+    const int slots = a.ksl * nq;  // slot i: slice i / nq, run q0 + i % nq
+    const float* base = part + static_cast<int64_t>(t) * a.jmax * a.M * CW +
+                        static_cast<int64_t>(m) * CW + c;
+    const int64_t slice_stride = static_cast<int64_t>(a.ntiles) * a.jmax * a.M * CW;
     float* yp = y + z * a.sy + static_cast<int64_t>(m) * a.ldy + n;
-    float4 sum = accumulate ? make_float4(yp[0], yp[1], yp[2], yp[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sl = 0; sl < a.ksl; ++sl)
-      for (int q = q0; q <= q1; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(
-            part + ((static_cast<int64_t>(sl) * a.ntiles + t) * a.jmax + q - q0) * a.M * CW +
-            static_cast<int64_t>(m) * CW + c);
-        sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+    float4 sum = accumulate ? *reinterpret_cast<const float4*>(yp) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i0 = 0; i0 < slots; i0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = min(i0 + k, slots - 1);
+        v[k] = *reinterpret_cast<const float4*>(base + (i / nq) * slice_stride +
+                                                static_cast<int64_t>(i % nq) * a.M * CW);
       }
-    yp[0] = sum.x; yp[1] = sum.y; yp[2] = sum.z; yp[3] = sum.w;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (i0 + k < slots) {
+          sum.x += v[k].x; sum.y += v[k].y; sum.z += v[k].z; sum.w += v[k].w;
+        }
+    }
+    *reinterpret_cast<float4*>(yp) = sum;
   }
 }
 
