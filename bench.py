@@ -45,26 +45,37 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 ROW_BYTES = 576 * 2             # one cached token: c^KV (512) + k^R (64), bf16
 FLOP_PER_TOKEN_HEAD = 2 * (576 + 512)
 N_CACHE_COPIES = 4
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_dsv2_b32_t4k_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "head_latent_attention_15_amd", "csrc", "attn_mfma.hip")
+# rocprofv3 counter summary and kernel source of each attention kernel the headline can time
+TRAFFIC = {
+    "wide": ("attn_wide_dsv2_b32_t4k_traffic.json", "attn_wide.hip"),
+    "heads": ("attn_mfma_dsv2_b32_t4k_traffic.json", "attn_mfma.hip"),
+    "cols": ("attn_cols_dsv2_b32_t4k_traffic.json", "attn_cols.hip"),
+}
+KERNEL_NAMES = {
+    "wide": "attn_wide_kernel<bf16 partials> (4 waves x 32 heads, 32x32x16 MFMA)",
+    "heads": "attn_mfma_kernel<8, bf16 partials> (8 waves x 16 heads)",
+    "cols": "attn_cols_kernel<bf16 partials> (8 waves: scores by 16-head blocks, latent "
+            "product by 64-column blocks)",
+}
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def kernel_source_hash(kernel: str) -> str:
+    src = os.path.join(ROOT, "head_latent_attention_15_amd", "csrc", TRAFFIC[kernel][1])
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+def measured_traffic(kernel: str):
+    """HBM bytes per attention launch of `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
     try:
-        t = json.load(open(TRAFFIC_FILE))
+        t = json.load(open(os.path.join(ROOT, "profiles", TRAFFIC[kernel][0])))
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if t.get("kernel_source_sha256_16") != kernel_source_hash(kernel):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -571,9 +582,9 @@ def main():
     ap.add_argument("--warmup-seconds", type=float, default=0.5,
                     help="keep warming up until this much time has passed (clocks settle)")
     ap.add_argument("--splits", type=int, default=0, help="split count (0: library suggestion)")
-    ap.add_argument("--kernel", default="auto", choices=["auto", "cols", "heads"],
-                    help="attention kernel timed alone beside the step (auto: the library's "
-                         "choice, the head-partitioned kernel)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "wide", "heads", "cols"],
+                    help="attention kernel of the step (auto: the library's choice, the kernel "
+                         "with 32 heads per wavefront for 128 heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32)
     ap.add_argument("--cpu-baseline-only", action="store_true",
@@ -658,7 +669,8 @@ def main():
     attn_f32_calls = attn_calls_for(args.kernel, o_part_f32)  # the same with fp32 partials
     combine_f32 = mla.bind(mla.mla_splitk_combine, o_part_f32, lse_part, out, lse)
     fused_calls = fused_calls_for(o_part)  # one launch that merges the splits itself
-    other = "heads" if args.kernel == "cols" else "cols"
+    kernel = "wide" if args.kernel == "auto" else args.kernel  # the library's choice at H = 128
+    other = "heads" if kernel != "heads" else "wide"  # timed alone beside it
     other_calls = attn_calls_for(other, o_part)
 
     def step_fused(k):
@@ -740,7 +752,7 @@ def main():
     # the dominant kernel of the step is the attention: its algorithmic bytes per launch
     # over its average back-to-back launch duration
     achieved = attn_alg_bytes / attn_s / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic(kernel)
     result = {
         "metric": METRIC,
         "value": round(cache_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -757,7 +769,7 @@ def main():
         "config": {"workload": "dsv2_b32_t4k", "B": B, "T": T, "H": H, "d_c": 512, "d_R": 64,
                    "page_size": 64, "num_splits": S, "split_partials": "bf16",
                    "split_merge": "combine kernel (mla_splitk_combine)",
-                   "attention_kernel": "heads" if args.kernel != "cols" else "cols",
+                   "attention_kernel": kernel,
                    "cache_copies": N_CACHE_COPIES, "parallelism": "none"},
         "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "query_tokens_per_s": round(B / (ms_step * 1e-3), 1),
@@ -778,9 +790,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
                      "frac_of_lds_dma_ceiling": round(achieved / stream_gbps_lds, 4),
-                     "kernel": ("attn_cols_kernel<bf16 partials> (8 waves: scores by 16-head "
-                                "blocks, latent product by 64-column blocks)" if args.kernel == "cols"
-                                else "attn_mfma_kernel<8, bf16 partials> (8 waves x 16 heads)"),
+                     "kernel": KERNEL_NAMES[kernel],
                      "bytes_per_launch_algorithmic": attn_alg_bytes},
     }
     del caches

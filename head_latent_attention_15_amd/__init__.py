@@ -488,14 +488,15 @@ def mla_decode_attn_multi(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_
         S, _dev(o_part, "o_part"), _dtype_code(o_part), _dev(lse_part, "lse_part", torch.float32),
         code, _stream(stream))
 
-ATTN_KERNELS = {"auto": 0, "heads": 1, "cols": 2, "generic": 3}
+ATTN_KERNELS = {"auto": 0, "heads": 1, "cols": 2, "generic": 3, "wide": 4}
 
 
 def mla_decode_attn_planned(q_lat, q_pe, kv_cache, block_table, seq_lens, softmax_scale,
                             num_splits, o_part, lse_part=None, kernel="auto", stream=None):
     """mla_decode_attn (q_lat [B,H,d_c]) or mla_decode_attn_multi (q_lat [B,n_q,H,d_c]) on an
     explicit kernel: "auto", "heads" (16 heads per wavefront), "cols" (column-partitioned,
-    H = 128) or "generic" (VALU), or the integer code."""
+    H = 128), "generic" (VALU) or "wide" (32 heads per wavefront, H = 128), or the integer
+    code."""
     torch = _torch()
     if q_lat.dim() == 3:
         B, H, d_c = q_lat.shape

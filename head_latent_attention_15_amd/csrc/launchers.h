@@ -62,6 +62,10 @@ bool attn_mfma_grid_resident(const PagedArgs& a);
 // wavefronts (each LDS fragment read feeds several MFMAs).
 hipError_t launch_attn_cols_bf16_512_64(const PagedArgs& a, hipStream_t s);
 bool attn_cols_supported(const PagedArgs& a);
+// The same products for 128 heads with four wavefronts of 32 heads on the 32 x 32 x 16
+// MFMA (each LDS fragment read feeds 32 heads).
+hipError_t launch_attn_wide_bf16_512_64(const PagedArgs& a, hipStream_t s);
+bool attn_wide_supported(const PagedArgs& a);
 
 // Split-K combine fused with the W^UV up-projection (d_c = 512, d_h = 128, S <= 64, bf16
 // W^UV): o_heads[b][i] = W^UV_i combine_s(o_part[b][i][s], lse_part[b][i][s]).

@@ -190,7 +190,7 @@ static mla_status_t decode_attn(const void* q_lat, const void* q_pe, const void*
   a.n_q = n_q;
   hipStream_t s = as_stream(stream);
 
-  if (kernel < 0 || kernel > 3) return fail(MLA_ERR_UNSUPPORTED, "attention kernel %d unknown", kernel);
+  if (kernel < 0 || kernel > 4) return fail(MLA_ERR_UNSUPPORTED, "attention kernel %d unknown", kernel);
   if (dtype == MLA_FP8) {
     if (a.d_c != 512 || a.d_R != 64 || !mla::attn_mfma_fp8_supported(a) || (kernel != 0 && kernel != 1))
       return fail(MLA_ERR_UNSUPPORTED, "fp8 cache: d_latent 512, d_rope 64, H = 128, pages of "
@@ -205,14 +205,24 @@ static mla_status_t decode_attn(const void* q_lat, const void* q_pe, const void*
   }
   if (dtype == MLA_BF16 && a.d_c == 512 && a.d_R == 64 && a.H <= 128) {
     const bool cols = mla::attn_cols_supported(a), heads = mla::attn_mfma_supported(a);
-    if (kernel == 0) kernel = heads ? 1 : cols ? 2 : 3;
+    const bool merging = merge != nullptr && num_splits > 1;
+    if (kernel == 0) {
+      // A fused call runs on the head-partitioned kernel (whose in-launch merge it takes
+      // when the grid fits, and whose two launches it runs otherwise, with the same bits);
+      // otherwise 128 heads take the 32-heads-per-wavefront kernel (fewer LDS reads and
+      // MFMA issues per tile).
+      if (merging && heads) kernel = 1;
+      else kernel = mla::attn_wide_supported(a) ? 4 : heads ? 1 : cols ? 2 : 3;
+    }
     if (kernel == 2 && !cols)
       return fail(MLA_ERR_UNSUPPORTED, "attention kernel 2 needs H = 128, pages of >= 32 tokens "
                   "(a power of two), <= 1024 pages per split and 16-byte aligned tensors");
     if (kernel == 1 && !heads)
       return fail(MLA_ERR_UNSUPPORTED, "attention kernel 1 needs H in {16, 32, 64, 128}, pages of "
                   ">= 32 tokens (a power of two), <= 1024 pages per split, aligned tensors");
-    const bool merging = merge != nullptr && num_splits > 1;
+    if (kernel == 4 && !mla::attn_wide_supported(a))
+      return fail(MLA_ERR_UNSUPPORTED, "attention kernel 4 needs H = 128, pages of >= 32 tokens "
+                  "(a power of two), <= 1024 pages per split and 16-byte aligned tensors");
     if (merging && kernel == 1 && num_splits <= 64 && mla::attn_mfma_grid_resident(a)) {
       a.merge_cnt = merge->counters;
       a.out = merge->out;
@@ -220,7 +230,8 @@ static mla_status_t decode_attn(const void* q_lat, const void* q_pe, const void*
       return launched(mla::launch_attn_mfma_bf16_512_64(a, s), "attention (bf16 MFMA, merged splits)");
     }
     mla_status_t st2;
-    if (kernel == 2) st2 = launched(mla::launch_attn_cols_bf16_512_64(a, s), "attention (bf16 MFMA, column-partitioned)");
+    if (kernel == 4) st2 = launched(mla::launch_attn_wide_bf16_512_64(a, s), "attention (bf16 MFMA, 32 heads per wavefront)");
+    else if (kernel == 2) st2 = launched(mla::launch_attn_cols_bf16_512_64(a, s), "attention (bf16 MFMA, column-partitioned)");
     else if (kernel == 1) st2 = launched(mla::launch_attn_mfma_bf16_512_64(a, s), "attention (bf16 MFMA)");
     else st2 = launched(mla::launch_attn_generic_bf16_512_64(a, s), "attention (bf16 generic)");
     if (st2 != MLA_OK || !merging) return st2;
@@ -231,8 +242,8 @@ static mla_status_t decode_attn(const void* q_lat, const void* q_pe, const void*
   }
   if (merge != nullptr)
     return fail(MLA_ERR_UNSUPPORTED, "mla_decode_fused: d_latent 512, d_rope 64, BF16 only");
-  if (kernel == 1 || kernel == 2)
-    return fail(MLA_ERR_UNSUPPORTED, "attention kernels 1 and 2 need d_latent 512, d_rope 64, BF16");
+  if (kernel == 1 || kernel == 2 || kernel == 4)
+    return fail(MLA_ERR_UNSUPPORTED, "attention kernels 1, 2 and 4 need d_latent 512, d_rope 64, BF16");
   if (dtype == MLA_F32 && a.d_c == 64 && a.d_R == 16 && a.H <= 64)
     return launched(mla::launch_attn_generic_f32_64_16(a, s), "attention (fp32)");
   return fail(MLA_ERR_UNSUPPORTED,

@@ -286,10 +286,12 @@ mla_status_t mla_decode_attn_multi(const void* q_lat, const void* q_pe, const vo
  * that cover each kernel: 0 = the library's choice (as mla_decode_attn_multi), 1 = the
  * head-partitioned MFMA kernel (16 heads per wavefront; H in {16, 32, 64, 128}), 2 = the
  * column-partitioned MFMA kernel (H = 128; each wavefront owns 64 latent columns of the
- * weighted sum), 3 = the generic VALU kernel.  Kernels 1 and 2 need d_latent 512,
- * d_rope 64, BF16, pages of >= 32 tokens (a power of two), at most 1024 pages per split
- * and 16-byte aligned q_lat, q_pe, kv_cache (and o_part for 2).  Same results, within
- * rounding order, as mla_decode_attn_multi.
+ * weighted sum), 3 = the generic VALU kernel, 4 = the MFMA kernel with 32 heads per
+ * wavefront on the 32 x 32 x 16 MFMA (H = 128; four wavefronts, each fragment read from LDS
+ * feeds 32 heads).  Kernels 1, 2 and 4 need d_latent 512, d_rope 64, BF16, pages of >= 32
+ * tokens (a power of two), at most 1024 pages per split and 16-byte aligned q_lat, q_pe,
+ * kv_cache (and o_part for 2 and 4).  Same results, within rounding order, as
+ * mla_decode_attn_multi.
  * Errors: as mla_decode_attn_multi, plus UNSUPPORTED for a kernel the shape cannot take. */
 mla_status_t mla_decode_attn_planned(const void* q_lat, const void* q_pe, const void* kv_cache,
                                      const int32_t* block_table, const int32_t* seq_lens,

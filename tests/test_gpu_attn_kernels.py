@@ -1,6 +1,7 @@
 """GPU parity of each bf16 MFMA attention kernel, chosen explicitly through
-mla_decode_attn_planned: "heads" (16 heads per wavefront for both products) and "cols"
-(the latent product partitioned by columns, 128 heads).  Each kernel against the fp64
+mla_decode_attn_planned: "heads" (16 heads per wavefront for both products), "cols"
+(the latent product partitioned by columns, 128 heads) and "wide" (32 heads per wavefront on
+the 32 x 32 x 16 MFMA, 128 heads).  Each kernel against the fp64
 oracle on the same seeded inputs; indexing (which tokens are read) bit-exact."""
 import numpy as np
 import pytest
@@ -12,7 +13,7 @@ from tests.gpu_util import assert_bf16, dev, errors, host64, say
 
 pytestmark = pytest.mark.gpu
 
-KERNELS = ["heads", "cols"]
+KERNELS = ["heads", "cols", "wide"]
 
 
 @pytest.fixture(scope="module")
@@ -200,11 +201,12 @@ def test_multi_token(mla, kernel):
         assert float(out[0, 0].abs().max()) == 0.0
 
 
-def test_cols_kernel_rejects_other_head_counts(mla):
+@pytest.mark.parametrize("kernel", ["cols", "wide"])
+def test_128_head_kernels_reject_other_head_counts(mla, kernel):
     inp = W.paged_attention(3, B=1, H=64, seq_lens=[100])
-    say("cols rejects H=64")
+    say(f"{kernel} rejects H=64")
     with pytest.raises(mla.MLAError):
-        attend(mla, inp, 1, "cols")
+        attend(mla, inp, 1, kernel)
 
 
 @pytest.mark.slow
