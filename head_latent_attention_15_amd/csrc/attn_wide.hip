@@ -101,20 +101,43 @@ void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restri
   const uint32_t smem_lds = static_cast<uint32_t>(reinterpret_cast<size_t>(lsm));
 
   const int b = blockIdx.x, s = blockIdx.y, bq = b * n_q + blockIdx.z;
-  const int L = seq_lens[b] - (n_q - 1 - static_cast<int>(blockIdx.z));
   const int j0 = s * (pages_per_split << log2P);
-  const int j1 = min(L, j0 + (pages_per_split << log2P));
-  const int64_t prow0 = static_cast<int64_t>(bq) * H * S + s;
-  const int hstride = S;
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, n32 = lane & 31;
   const int h0 = WH * w;
-  const int P = 1 << log2P;
+
+  // The queries need neither the sequence length nor the block table, so their loads go out
+  // first, with those two scalar loads in flight beside them.  The B operand of S^T = K Q^T
+  // for k-step kk wants lane (hf, n32) to hold head h0 + n32, features 16 kk + 8 hf .. + 7:
+  // two lanes per head, so loading it in place touches 32 rows per instruction.  Instead each
+  // wave loads its 32 query rows in order, 1 KB per instruction, in three parts (q~ features
+  // 0-255 and 256-511: two half rows per load; q^R: eight rows per load), and transposes them
+  // through LDS below.
+  constexpr int QA = 16, QC = 4;  // loads per wave: each q~ part, q^R
+  bf16x8_t rawa[QA], rawb[QA], rawc[QC];
+  {
+    const int64_t qrow0 = static_cast<int64_t>(bq) * H + h0;
+    const bf16raw* ql = q_lat + (qrow0 + (lane >> 5)) * DC + 8 * (lane & 31);  // rows 2 i + hf
+    const bf16raw* qp = q_pe + (qrow0 + (lane >> 3)) * DR + 8 * (lane & 7);     // rows 8 i + lane / 8
+#pragma unroll
+    for (int i = 0; i < QA; ++i) rawa[i] = *reinterpret_cast<const bf16x8_t*>(ql + 2 * DC * i);
+#pragma unroll
+    for (int i = 0; i < QA; ++i) rawb[i] = *reinterpret_cast<const bf16x8_t*>(ql + 2 * DC * i + DC / 2);
+#pragma unroll
+    for (int i = 0; i < QC; ++i) rawc[i] = *reinterpret_cast<const bf16x8_t*>(qp + 8 * DR * i);
+  }
   const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_pages;
+  const int pg0 = __builtin_amdgcn_readfirstlane((j0 >> log2P) < max_pages ? bt_row[j0 >> log2P] : 0);
+
+  const int L = seq_lens[b] - (n_q - 1 - static_cast<int>(blockIdx.z));
+  const int j1 = min(L, j0 + (pages_per_split << log2P));
+  const int64_t prow0 = static_cast<int64_t>(bq) * H * S + s;
+  const int hstride = S;
+  const int P = 1 << log2P;
 
   if (j0 >= j1) {  // empty split: o = 0, lse = -inf
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the query loads land before the exit
     for (int e = tid; e < H * DC; e += WW * 64) {
       const int h = e / DC, c = e % DC;
       st(o_part + (prow0 + static_cast<int64_t>(h) * hstride) * DC + c, 0.f);
@@ -132,77 +155,56 @@ void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restri
   const int npages = (j1 - j0 + P - 1) >> log2P;
 
   // Copy r of this wave fills LDS chunk 64 (w + 4 r) + lane of a tile buffer: row t, stored
-  // position p, which holds logical chunk p ^ swz(t).  Entry (t << 16) | source byte offset
-  // in the row, the same for every tile; rows past the split's last token repeat it.
-  uint32_t centry[W_COPIES];
+  // position p, which holds logical chunk p ^ swz(t).  Its source offset in a full tile is the
+  // same for every tile (kept in registers); in a tile past the split's last token (TAIL) the
+  // rows past it repeat it, and the offset is recomputed with that clamp.
+  uint32_t cfull[W_COPIES];
 #pragma unroll
-  for (int r = 0; r < W_COPIES; ++r) {
-    const unsigned chunk = 64u * (w + WW * r) + lane;
-    const unsigned t = chunk / CHUNKS, c = (chunk % CHUNKS) ^ swz(t);
-    centry[r] = (t << 16) | (c * 16);
-  }
-  auto issue_copy = [&](const char* base, unsigned last, uint32_t lds_tile, int r) {
-    const uint32_t e = centry[r];
-    dma16(base, __umul24(min(e >> 16, last), static_cast<unsigned>(ROW_BYTES)) + (e & 0xffffu),
-          lds_tile + (w + WW * r) * 1024);
+  for (int r = 0; r < W_COPIES; ++r) cfull[r] = tile_chunk_voff(64u * (w + WW * r) + lane, TILE - 1);
+  auto issue_copy = [&](const char* base, unsigned last, uint32_t lds_tile, int r, auto tail) {
+    uint32_t voff = cfull[r];
+    if constexpr (decltype(tail)::value) voff = tile_chunk_voff(64u * (w + WW * r) + lane, last);
+    dma16(base, voff, lds_tile + (w + WW * r) * 1024);
   };
+  const std::true_type clamped;
+  const std::false_type unclamped;
 
-  // ---- prologue.  The queries go out first (they need no block-table entry), then tile 0's
-  //      copies from its page (one scalar load), then the split's block-table entries into
-  //      LDS; the first barrier waits for all of it.  The copies of tiles 1 and 2 go out during
-  //      tile 0's score steps, so no prologue wait covers a tile that is not read yet.
-  //      The B operand of S^T = K Q^T for k-step kk wants lane (hf, n32) to hold head
-  //      h0 + n32, features 16 kk + 8 hf .. + 7: two lanes per head, so loading it in place
-  //      touches 32 rows per instruction.  Instead each wave loads its 32 query rows in
-  //      order (64 consecutive 16-byte chunks per instruction) in two rounds of 288 features
-  //      (q~ then the rest of q~ and q^R) and transposes them through LDS (tile buffers 1-3
-  //      are free until tile 0's score steps): chunk c of round-row n at slot 37 n + c of the
-  //      wave's area, one slot of padding per row, so the reads of the B layout are
-  //      conflict-free.
-  constexpr int QROW = 37;                 // 16-byte slots per staged query row
-  constexpr int QAREA = WH * QROW * 16;    // staging bytes per wave and round
-  static_assert(TILE_BYTES + WW * QAREA <= W_NBUF * TILE_BYTES, "query staging fits tiles 1-3");
-  constexpr int QLOADS = WH * 36 / 64;     // 18 loads per wave and round
+  // ---- prologue.  Tile 0's copies go out behind the queries, then the split's block-table
+  //      entries into LDS; the first barrier waits for all of it.  The copies of tiles 1 and
+  //      2 go out during tile 0's score steps, so no prologue wait covers a tile that is not
+  //      read yet.  The queries are transposed through LDS (tile buffers 1-3 are free until
+  //      tile 0's score steps): row n's chunk c of a q~ part at slot 33 n + c of the wave's
+  //      first area, of q^R at slot 9 n + c of its second; one slot of padding per row keeps
+  //      the reads of the B layout conflict-free.
+  constexpr int QSA = 33 * 16 * WH, QSC = 9 * 16 * WH;  // staging bytes per wave
+  static_assert(TILE_BYTES + WW * (QSA + QSC) <= W_NBUF * TILE_BYTES, "query staging fits tiles 1-3");
   bf16x8_t qf[W_KSTEPS];
   {
-    const int64_t qrow0 = static_cast<int64_t>(bq) * H + h0;
-    auto qchunk = [&](int r, int i) {  // chunk 64 i + lane of round r: row n, chunk c
-      const unsigned q = 64u * i + lane;
-      const unsigned n = __umul24(q, 1821u) >> 16;  // q / 36 for q < 1152
-      const unsigned c = q - 36u * n;
-      const int f = 288 * r + 8 * static_cast<int>(c);
-      const bf16raw* src = f < DC ? q_lat + (qrow0 + n) * DC + f : q_pe + (qrow0 + n) * DR + (f - DC);
-      return *reinterpret_cast<const bf16x8_t*>(src);
-    };
-    bf16x8_t raw0[QLOADS], raw1[QLOADS];
-#pragma unroll
-    for (int i = 0; i < QLOADS; ++i) raw0[i] = qchunk(0, i);
-#pragma unroll
-    for (int i = 0; i < QLOADS; ++i) raw1[i] = qchunk(1, i);
     {
-      const char* base0 = page_base(__builtin_amdgcn_readfirstlane(bt_row[j0 >> log2P]), j0);
+      const char* base0 = page_base(pg0, j0);
 #pragma unroll
       for (int r = 0; r < W_COPIES; ++r)
-        issue_copy(base0, static_cast<unsigned>(j1 - 1 - j0), smem_lds, r);
+        issue_copy(base0, static_cast<unsigned>(j1 - 1 - j0), smem_lds, r, clamped);
     }
-    lds_char_t* const qarea = lsm + TILE_BYTES + w * QAREA;
-    auto stage = [&](const bf16x8_t* raw) {
+    lds_char_t* const qa = lsm + TILE_BYTES + w * QSA;
+    lds_char_t* const qc = lsm + TILE_BYTES + WW * QSA + w * QSC;
+    // load i of a q~ part holds row 2 i + hf, chunk n32; of q^R, row 8 i + lane / 8, chunk lane % 8
+    auto stage_a = [&](const bf16x8_t* raw) {
 #pragma unroll
-      for (int i = 0; i < QLOADS; ++i) {
-        const unsigned q = 64u * i + lane;
-        const unsigned n = __umul24(q, 1821u) >> 16;
-        *(lds_bf16x8_t*)(qarea + 16 * (QROW * n + (q - 36u * n))) = raw[i];
-      }
+      for (int i = 0; i < QA; ++i) *(lds_bf16x8_t*)(qa + 16 * (33 * (2 * i + hf) + n32)) = raw[i];
     };
-    auto unstage = [&](int r) {
+    auto unstage_a = [&](int k0) {  // k-steps k0 .. k0 + 15: chunks 2 k + hf of row n32
 #pragma unroll
-      for (int k = 0; k < 18; ++k)
-        qf[18 * r + k] = *(const lds_bf16x8_t*)(qarea + 16 * (QROW * n32 + 2 * k + hf));
+      for (int k = 0; k < 16; ++k) qf[k0 + k] = *(const lds_bf16x8_t*)(qa + 16 * (33 * n32 + 2 * k + hf));
     };
-    stage(raw0);
-    unstage(0);  // (LDS operations of one wave complete in order: no wait between)
-    stage(raw1);
-    unstage(1);
+#pragma unroll
+    for (int i = 0; i < QC; ++i) *(lds_bf16x8_t*)(qc + 16 * (9 * (8 * i + (lane >> 3)) + (lane & 7))) = rawc[i];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qf[32 + k] = *(const lds_bf16x8_t*)(qc + 16 * (9 * n32 + 2 * k + hf));
+    stage_a(rawa);
+    unstage_a(0);  // (LDS operations of one wave complete in order: no wait between)
+    stage_a(rawb);
+    unstage_a(16);
   }
   lds_i32_t* const ptab = (lds_i32_t*)(lsm + W_PAGE_TABLE);
   for (int e = tid; e < npages; e += WW * 64) ptab[e] = bt_row[(j0 >> log2P) + e];
@@ -213,24 +215,23 @@ void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restri
   // Lane offsets inside a tile buffer, the same for every tile:
   //   kb[j]: K fragment of k-step kk (kk & 3 == j): row n32, logical chunk 2 kk + hf; k-step
   //     kk adds 128 (kk >> 2).
-  //   vb[ks][r][c1]: V^T fragment of column tile ct (ct & 1 == c1), token step ks, read r:
-  //     rows 16 ks + 8 r + 4 hf + (n >> 2) (n = lane & 15), columns 32 ct + 16 g1 + 4 (n & 3)
-  //     .. + 3 (g1 = lane >> 4 & 1); column tile ct adds 128 (ct >> 1).
+  //   vb[r][c1]: V^T fragment of column tile ct (ct & 1 == c1), token step 0, read r: rows
+  //     8 r + 4 hf + (n >> 2) (n = lane & 15), columns 32 ct + 16 g1 + 4 (n & 3) .. + 3
+  //     (g1 = lane >> 4 & 1); column tile ct adds 128 (ct >> 1).  Token step 1 reads rows 16
+  //     further down, where the swizzle flips chunk bit 2: vb[r][c1 ^ 1] + 16 rows.
   int kb[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) kb[j] = n32 * ROW_BYTES + 16 * ((2 * j + hf) ^ swz(n32));
-  int vb[2][2][2];
+  int vb[2][2];
   {
     const int n = lane & 15, g1 = (lane >> 4) & 1;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int r = 0; r < 2; ++r) {
+      const int t = 8 * r + 4 * hf + (n >> 2);
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int t = 16 * ks + 8 * r + 4 * hf + (n >> 2);
-#pragma unroll
-        for (int c1 = 0; c1 < 2; ++c1)
-          vb[ks][r][c1] = t * ROW_BYTES + 16 * ((4 * c1 + 2 * g1 + ((n >> 1) & 1)) ^ swz(t)) + 8 * (n & 1);
-      }
+      for (int c1 = 0; c1 < 2; ++c1)
+        vb[r][c1] = t * ROW_BYTES + 16 * ((4 * c1 + 2 * g1 + ((n >> 1) & 1)) ^ swz(t)) + 8 * (n & 1);
+    }
   }
 
   f32x16_t o[W_CT];
@@ -251,11 +252,13 @@ void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restri
   // Scores of tile it (two accumulation chains, summed), with this wave's copies of tile it+2
   // (or, near the end of the split, tile it again into the retired buffer, so every tile
   // issues the same copies and every wait counts alike) spread over the k-steps.  Tile 0's
-  // score steps (FIRST) issue the copies of tiles 1 and 2, one every second step.
-  auto scores = [&](int it, auto first) -> f32x16_t {
+  // score steps (FIRST) issue the copies of tiles 1 and 2, one every second step.  TAIL:
+  // some copied tile reaches past the split's last token (its rows are clamped).
+  auto copy_tb = [&](int it) { return j0 + (it + 2 < ntiles ? it + 2 : min(it, ntiles - 1)) * TILE; };
+  auto scores = [&](int it, auto first, auto tail) -> f32x16_t {
     constexpr bool FIRST = decltype(first)::value;
     const lds_char_t* tile = lsm + (it % W_NBUF) * TILE_BYTES;
-    const int tb2 = j0 + (it + 2 < ntiles ? it + 2 : min(it, ntiles - 1)) * TILE;
+    const int tb2 = copy_tb(it);
     const char* base2 = copy_src(tb2);
     const unsigned last2 = static_cast<unsigned>(j1 - 1 - tb2);
     const uint32_t lds2 = smem_lds + ((it + 2) % W_NBUF) * TILE_BYTES;
@@ -266,7 +269,7 @@ void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restri
     auto k_frag = [&](int kk) {
       return *(const lds_bf16x8_t*)(tile + kb[kk & 3] + 128 * (kk >> 2));
     };
-    constexpr int KRING = 4;
+    constexpr int KRING = 6;
     bf16x8_t ka[KRING];
 #pragma unroll
     for (int i = 0; i < KRING - 1; ++i) ka[i] = k_frag(i);
@@ -278,10 +281,10 @@ void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restri
       else if (kk & 1) mfma32_v(s1, ka[kk % KRING], qf[kk]);
       else mfma32_v(s0, ka[kk % KRING], qf[kk]);
       if constexpr (FIRST) {
-        if (kk % 2 == 0 && kk / 2 < W_COPIES) issue_copy(base1, last1, smem_lds + TILE_BYTES, kk / 2);
-        else if (kk % 2 == 0) issue_copy(base2, last2, lds2, kk / 2 - W_COPIES);
+        if (kk % 2 == 0 && kk / 2 < W_COPIES) issue_copy(base1, last1, smem_lds + TILE_BYTES, kk / 2, tail);
+        else if (kk % 2 == 0) issue_copy(base2, last2, lds2, kk / 2 - W_COPIES, tail);
       } else if (kk % 4 == 0) {
-        issue_copy(base2, last2, lds2, kk / 4);
+        issue_copy(base2, last2, lds2, kk / 4, tail);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -334,7 +337,7 @@ void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restri
 #pragma unroll
     for (int r = 0; r < 2; ++r)
       half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4_t*)(tile + vb[ks][r][ct & 1] + 128 * (ct >> 1)));
+          (lds_i16x4_t*)(tile + vb[r][(ct & 1) ^ ks] + 128 * (ct >> 1) + 16 * ROW_BYTES * ks));
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
   };
   auto pv = [&](int it, bf16x8_t p0, bf16x8_t p1, auto soft, const f32x16_t& sc, bf16x8_t& n0,
@@ -368,7 +371,7 @@ void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restri
   block_barrier();
   bf16x8_t p0, p1;
   {
-    f32x16_t sc = scores(0, std::integral_constant<bool, true>());
+    f32x16_t sc = scores(0, std::true_type(), clamped);
     mask_tail(sc, 0);
     float tmax = sc[0];
 #pragma unroll
@@ -385,7 +388,8 @@ void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restri
   for (int it = 1; it < ntiles; ++it) {
     wait_vmcnt<W_COPIES>();  // own copies of tile it landed (tile it+1's may be in flight)
     block_barrier();
-    f32x16_t sc = scores(it, std::integral_constant<bool, false>());
+    f32x16_t sc = j1 - copy_tb(it) >= TILE ? scores(it, std::false_type(), unclamped)
+                                            : scores(it, std::false_type(), clamped);
     mask_tail(sc, it);
     bf16x8_t n0, n1;
     pv(it - 1, p0, p1, std::integral_constant<bool, true>(), sc, n0, n1);
