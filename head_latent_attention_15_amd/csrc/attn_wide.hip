@@ -405,23 +405,37 @@ void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restri
 
   // ---- epilogue: lane (hf, n32) holds head h0 + n32, columns 32 ct + 8 j + 4 hf + i of
   //      register 4 j + i of o[ct]; a head block whose scores left the reference range is
-  //      recomputed exactly.  bf16 partials go through LDS (the tile buffers are free now), so
-  //      each store writes one whole 1 KB row: wave w's 32 rows sit at 32 KB w, row h's chunk
-  //      c (columns 8 c .. 8 c + 7) at position c ^ h.
+  //      recomputed exactly.  The partials go through LDS (the tile buffers are free now), so
+  //      each store writes 1 KB of one row: wave w's 32 rows sit at 32 KB w; for bf16, row
+  //      h's chunk c (columns 8 c .. 8 c + 7) at position c ^ h.
   const bool fallback = __any(out_of_range);
   const float lt = lsum + __shfl_xor(lsum, 32, 64);
   const float inv = 1.f / lt;
   if (!fallback && lse_part != nullptr && hf == 0)
     lse_part[prow0 + static_cast<int64_t>(h0 + n32) * hstride] = (m_ref + __log2f(lt)) * LN2;
   if constexpr (std::is_same<OT, float>::value) {
+    // fp32: the same in two halves of 256 columns (32 KB per wave each); row h's chunk c
+    // (columns 4 c .. 4 c + 3 of the half) at position c ^ h
+    block_barrier();  // every wave's last tile reads are done
     if (!fallback) {
-      float* dst = o_part + (prow0 + static_cast<int64_t>(h0 + n32) * hstride) * DC + 4 * hf;
+      lds_char_t* const stage = lsm + w * (WH * DC * 2);
+      float* dst = o_part + prow0 * DC + 4 * lane;
 #pragma unroll
-      for (int ct = 0; ct < W_CT; ++ct)
+      for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<f32x4_t*>(dst + 32 * ct + 8 * j) =
-              f32x4_t{o[ct][4 * j], o[ct][4 * j + 1], o[ct][4 * j + 2], o[ct][4 * j + 3]} * inv;
+        for (int ct = 0; ct < W_CT / 2; ++ct)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x16_t& a = o[8 * half + ct];
+            *(lds_f32x4_t*)(stage + n32 * (DC * 2) + 16 * ((8 * ct + 2 * j + hf) ^ n32)) =
+                f32x4_t{a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]} * inv;
+          }
+#pragma unroll
+        for (int h = 0; h < WH; ++h) {
+          const f32x4_t v = *(const lds_f32x4_t*)(stage + h * (DC * 2) + 16 * (lane ^ h));
+          *reinterpret_cast<f32x4_t*>(dst + static_cast<int64_t>(h0 + h) * hstride * DC + 256 * half) = v;
+        }
+      }
     }
   } else {
     block_barrier();  // every wave's last tile reads are done
