@@ -39,6 +39,7 @@
 // bf16-rounded weights the PV product consumes (v_dot2 with ones).
 #include "attn_common.h"
 #include "launchers.h"
+#include "ragged_plan.h"
 
 #include <type_traits>
 
@@ -85,24 +86,27 @@ __device__ __forceinline__ void chain_drain(f32x16_t& x, f32x16_t& y) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(x), "+v"(y));
 }
 
-// One workgroup of four wavefronts per (sequence, split) (blockIdx.x, blockIdx.y) and query
-// token (blockIdx.z), as attn_mfma_kernel: token t of n_q sits at position seq_len - n_q + t,
-// its queries and partials are row bq = b n_q + t, and the splits of a sequence share its
-// XCD.  Wavefront w owns heads 32 w .. 32 w + 31.
-template <typename OT>
-__global__ __launch_bounds__(WW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restrict__ q_pe,
-                      const bf16raw* __restrict__ cache, const int32_t* __restrict__ block_table,
-                      const int32_t* __restrict__ seq_lens, int H, int log2P, int max_pages,
-                      int pages_per_split, int S, float scale_log2, OT* __restrict__ o_part,
-                      float* __restrict__ lse_part, int n_q) {
+// The attention of one split: tokens j0 .. j1-1 of sequence b (j1 = split_end(), read after
+// the query loads are issued) with the queries of row bq; the partial of head h goes to row
+// prow0 + h * hstride of o_part / lse_part.  Every thread of the workgroup calls it with the
+// same arguments.  Wavefront w owns heads 32 w .. 32 w + 31.  KRING: K fragments in flight
+// in the score loop (6; 4 where the caller keeps more state live, as the ragged kernel).
+template <typename OT, int KRING, typename SplitEnd>
+__device__ __forceinline__ void wide_split(
+    const bf16raw* __restrict__ q_lat, const bf16raw* __restrict__ q_pe,
+    const bf16raw* __restrict__ cache, const int32_t* __restrict__ block_table, int H,
+    int log2P, int max_pages, float scale_log2, OT* __restrict__ o_part,
+    float* __restrict__ lse_part, int b, int bq, int j0, SplitEnd split_end, int64_t prow0,
+    int hstride) {
   __shared__ __attribute__((aligned(16))) char smem[W_LDS_BYTES];
   lds_char_t* const lsm = (lds_char_t*)smem;
   const uint32_t smem_lds = static_cast<uint32_t>(reinterpret_cast<size_t>(lsm));
 
-  const int b = blockIdx.x, s = blockIdx.y, bq = b * n_q + blockIdx.z;
-  const int j0 = s * (pages_per_split << log2P);
-  const int tid = threadIdx.x, lane = tid & 63;
+  // the thread index is made opaque here, so that when this runs in a loop over pieces
+  // nothing derived from it is hoisted out of the loop and kept live across the pieces
+  int tid_opaque = threadIdx.x;
+  asm volatile("" : "+v"(tid_opaque));
+  const int tid = tid_opaque, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, n32 = lane & 31;
   const int h0 = WH * w;
@@ -130,10 +134,7 @@ void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restri
   const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_pages;
   const int pg0 = __builtin_amdgcn_readfirstlane((j0 >> log2P) < max_pages ? bt_row[j0 >> log2P] : 0);
 
-  const int L = seq_lens[b] - (n_q - 1 - static_cast<int>(blockIdx.z));
-  const int j1 = min(L, j0 + (pages_per_split << log2P));
-  const int64_t prow0 = static_cast<int64_t>(bq) * H * S + s;
-  const int hstride = S;
+  const int j1 = split_end();
   const int P = 1 << log2P;
 
   if (j0 >= j1) {  // empty split: o = 0, lse = -inf
@@ -269,7 +270,6 @@ void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restri
     auto k_frag = [&](int kk) {
       return *(const lds_bf16x8_t*)(tile + kb[kk & 3] + 128 * (kk >> 2));
     };
-    constexpr int KRING = 6;
     bf16x8_t ka[KRING];
 #pragma unroll
     for (int i = 0; i < KRING - 1; ++i) ka[i] = k_frag(i);
@@ -462,6 +462,69 @@ void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restri
                                     hstride, scale_log2, o_part, lse_part, h0, WH, lane);
 }
 
+// One workgroup of four wavefronts per (sequence, split) (blockIdx.x, blockIdx.y) and query
+// token (blockIdx.z), as attn_mfma_kernel: token t of n_q sits at position seq_len - n_q + t,
+// its queries and partials are row bq = b n_q + t, and the splits of a sequence share its
+// XCD.
+template <typename OT>
+__global__ __launch_bounds__(WW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restrict__ q_pe,
+                      const bf16raw* __restrict__ cache, const int32_t* __restrict__ block_table,
+                      const int32_t* __restrict__ seq_lens, int H, int log2P, int max_pages,
+                      int pages_per_split, int S, float scale_log2, OT* __restrict__ o_part,
+                      float* __restrict__ lse_part, int n_q) {
+  const int b = blockIdx.x, s = blockIdx.y, z = blockIdx.z, bq = b * n_q + z;
+  const int j0 = s * (pages_per_split << log2P);
+  wide_split<OT, 6>(q_lat, q_pe, cache, block_table, H, log2P, max_pages, scale_log2, o_part,
+                    lse_part, b, bq, j0,
+                 [&] { return min(seq_lens[b] - (n_q - 1 - z), j0 + (pages_per_split << log2P)); },
+                 static_cast<int64_t>(bq) * H * S + s, S);
+}
+
+// Flattened work list for ragged batches (ragged_plan.h): range r of the batch's cached
+// pages goes to one workgroup, which runs wide_split on each sequence piece inside it; the
+// partial of head h from piece i of sequence b is row first_b H + h count_b + i, as in
+// attn_mfma_ragged_kernel, so the same slot-table combine merges them.
+template <typename OT>
+__global__ __launch_bounds__(WW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_wide_ragged_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restrict__ q_pe,
+                             const bf16raw* __restrict__ cache,
+                             const int32_t* __restrict__ block_table,
+                             const int32_t* __restrict__ seq_lens, int B, int H, int log2P,
+                             int max_pages, float scale_log2, OT* __restrict__ o_part,
+                             float* __restrict__ lse_part, int* __restrict__ seq_slots,
+                             int* __restrict__ err) {
+  int W = 0, tot = 0;
+  if (ragged::plan_ranges(seq_lens, B, log2P, W_MAX_SPLIT_PAGES, seq_slots, err, W, tot)) return;
+  // the plan's scalars wait in LDS between pieces (registers are full inside the split body)
+  __shared__ int plan[2];
+  if (threadIdx.x == 0) {
+    plan[0] = W;
+    plan[1] = tot;
+  }
+  __syncthreads();
+  for (int k = 0;; ++k) {
+    const int Wk = __builtin_amdgcn_readfirstlane(
+        *static_cast<volatile __attribute__((address_space(3))) int*>(
+            (__attribute__((address_space(3))) int*)plan));
+    const int tk = __builtin_amdgcn_readfirstlane(
+        *static_cast<volatile __attribute__((address_space(3))) int*>(
+            (__attribute__((address_space(3))) int*)plan + 1));
+    const int rk = __builtin_amdgcn_readfirstlane(ragged::range_of(blockIdx.x, gridDim.x));
+    const int lo = rk * Wk, hi = min(lo + Wk, tk);
+    ragged::Piece pc;
+    if (!ragged::ragged_piece(seq_lens, B, log2P, Wk, rk, lo, hi, k, &pc)) break;
+    // the previous piece's partial stores are done, and its last LDS reads too, before this
+    // piece's loads and copies reuse the registers and buffers
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int j1 = pc.j1;
+    wide_split<OT, 4>(q_lat, q_pe, cache, block_table, H, log2P, max_pages, scale_log2, o_part,
+                      lse_part, pc.b, pc.b, pc.j0, [&] { return j1; },
+                   static_cast<int64_t>(pc.first) * H + pc.index, pc.count);
+  }
+}
+
 template <typename OT>
 hipError_t launch_wide_t(const PagedArgs& a, hipStream_t st) {
   const float log2e = 1.4426950408889634f;
@@ -484,6 +547,18 @@ bool attn_wide_supported(const PagedArgs& a) {
          a.pages_per_split <= W_MAX_SPLIT_PAGES && a.B <= 65535 && a.n_q >= 1 &&
          a.n_q <= 65535 && aligned16w(a.q_lat) && aligned16w(a.q_pe) && aligned16w(a.cache) &&
          aligned16w(a.o_part);
+}
+
+hipError_t launch_attn_wide_ragged(const PagedArgs& a, int grid, int* seq_slots, int* err,
+                                   hipStream_t st) {
+  if (!attn_wide_supported(a) || !a.part_bf16) return hipErrorInvalidValue;
+  const float log2e = 1.4426950408889634f;
+  hipLaunchKernelGGL((attn_wide_ragged_kernel<bf16raw>), dim3(grid), dim3(WW * 64), 0, st,
+                     static_cast<const bf16raw*>(a.q_lat), static_cast<const bf16raw*>(a.q_pe),
+                     static_cast<const bf16raw*>(a.cache), a.block_table, a.seq_lens, a.B, a.H,
+                     __builtin_ctz(static_cast<unsigned>(a.page_size)), a.max_pages,
+                     a.scale * log2e, static_cast<bf16raw*>(a.o_part), a.lse_part, seq_slots, err);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_wide_bf16_512_64(const PagedArgs& a, hipStream_t s) {

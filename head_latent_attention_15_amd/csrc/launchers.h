@@ -66,6 +66,9 @@ bool attn_cols_supported(const PagedArgs& a);
 // MFMA (each LDS fragment read feeds 32 heads).
 hipError_t launch_attn_wide_bf16_512_64(const PagedArgs& a, hipStream_t s);
 bool attn_wide_supported(const PagedArgs& a);
+// Its flattened ragged work list (as launch_attn_mfma_ragged; bf16 partials).
+hipError_t launch_attn_wide_ragged(const PagedArgs& a, int grid, int* seq_slots, int* err,
+                                   hipStream_t s);
 
 // Split-K combine fused with the W^UV up-projection (d_c = 512, d_h = 128, S <= 64, bf16
 // W^UV): o_heads[b][i] = W^UV_i combine_s(o_part[b][i][s], lse_part[b][i][s]).

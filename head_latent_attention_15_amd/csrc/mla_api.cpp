@@ -403,8 +403,11 @@ mla_status_t mla_decode_ragged(const void* q_lat, const void* q_pe, const void* 
   a.o_part = ws + l.part_off;
   a.part_bf16 = 1;
   hipStream_t s = as_stream(stream);
-  st = launched(mla::launch_attn_mfma_ragged(a, grid, seq_slots, seq_slots + 2 * a.B, s),
-                "attention (flattened ragged work list)");
+  st = mla::attn_wide_supported(a)
+           ? launched(mla::launch_attn_wide_ragged(a, grid, seq_slots, seq_slots + 2 * a.B, s),
+                      "attention (flattened ragged work list, 32 heads per wavefront)")
+           : launched(mla::launch_attn_mfma_ragged(a, grid, seq_slots, seq_slots + 2 * a.B, s),
+                      "attention (flattened ragged work list)");
   if (st != MLA_OK) return st;
   return launched(mla::launch_combine_slots(a.o_part, 1, a.lse_part, seq_slots, a.B, a.H, out,
                                             lse_out, s),
