@@ -790,6 +790,11 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
                      "frac_of_lds_dma_ceiling": round(achieved / stream_gbps_lds, 4),
+                     # frac is the attention kernel alone; the whole step (attention +
+                     # combine, algorithmic bytes over ms_per_step) is step_frac, the figure
+                     # value and ms_per_step describe
+                     "step_frac": round(step_alg_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "frac_applies_to": "attention kernel alone (step_frac: attention + combine)",
                      "kernel": KERNEL_NAMES[kernel],
                      "bytes_per_launch_algorithmic": attn_alg_bytes},
     }

@@ -423,6 +423,9 @@ mla_status_t mla_splitk_combine(const void* o_part, mla_dtype_t part_dtype,
     return fail(MLA_ERR_SHAPE, "mla_splitk_combine: bad sizes B=%d H=%d S=%d d_c=%d", B, H,
                 num_splits, d_c);
   if (d_c % 4 != 0) return fail(MLA_ERR_SHAPE, "mla_splitk_combine: d_c %d %% 4 != 0", d_c);
+  // the kernels load partials and store out with 8- and 16-byte accesses
+  if ((reinterpret_cast<uintptr_t>(o_part) & 15) != 0 || (reinterpret_cast<uintptr_t>(out) & 15) != 0)
+    return fail(MLA_ERR_SHAPE, "mla_splitk_combine: o_part and out must be 16-byte aligned");
   if (!is_dtype(part_dtype))
     return fail(MLA_ERR_UNSUPPORTED, "mla_splitk_combine: unknown partial dtype %d", part_dtype);
   return launched(mla::launch_splitk_combine(o_part, part_dtype == MLA_BF16, lse_part, B, H,

@@ -305,9 +305,9 @@ mla_status_t mla_decode_attn_planned(const void* q_lat, const void* q_pe, const 
  *   M = max_s lse_s; w_s = e^{lse_s - M} (0 for lse_s = -inf)
  *   out[b][i][:] = sum_s w_s o_part[b][i][s][:] / sum_s w_s;  lse_out = M + ln sum_s w_s
  * All splits empty: out = 0, lse_out = -inf.
- *   o_part [B][H][S][d_c] in part_dtype (F32 or BF16), lse_part [B][H][S] fp32;
- *   out [B][H][d_c] fp32 (fp32 weights and sums);  lse_out [B][H] fp32 or NULL.
- * Errors: NULL, SHAPE (sizes < 1, d_c % 4), UNSUPPORTED (part_dtype). */
+ *   o_part [B][H][S][d_c] in part_dtype (F32 or BF16), 16-byte aligned; lse_part [B][H][S] fp32;
+ *   out [B][H][d_c] fp32 (fp32 weights and sums), 16-byte aligned;  lse_out [B][H] fp32 or NULL.
+ * Errors: NULL, SHAPE (sizes < 1, d_c % 4, misaligned o_part / out), UNSUPPORTED (part_dtype). */
 mla_status_t mla_splitk_combine(const void* o_part, mla_dtype_t part_dtype,
                                 const float* lse_part, int32_t B, int32_t H, int32_t num_splits,
                                 int32_t d_c, float* out, float* lse_out, void* stream);

@@ -117,6 +117,9 @@ def test_combine_validation():
     assert L.mla_splitk_combine(FAKE, BF16, FAKE, 1, 1, 0, 512, FAKE, None, None) == mla.MLA_ERR_SHAPE
     assert L.mla_splitk_combine(FAKE, F32, FAKE, 1, 1, 2, 510, FAKE, None, None) == mla.MLA_ERR_SHAPE
     assert L.mla_splitk_combine(FAKE, 7, FAKE, 1, 1, 2, 512, FAKE, None, None) == mla.MLA_ERR_UNSUPPORTED
+    # 8- and 16-byte kernel accesses: misaligned partials or output are refused
+    assert L.mla_splitk_combine(FAKE + 8, BF16, FAKE, 1, 1, 2, 512, FAKE, None, None) == mla.MLA_ERR_SHAPE
+    assert L.mla_splitk_combine(FAKE, F32, FAKE, 1, 1, 2, 64, FAKE + 4, None, None) == mla.MLA_ERR_SHAPE
 
 
 def test_attn_rejects_unknown_partial_dtype():
