@@ -439,6 +439,8 @@ def fp8_rows(mla, torch, inp, num_cus, steps, n_copies):
     lse = torch.empty(B, H, device=dev)
     calls = [mla.bind(mla.mla_decode_attn_planned, q_lat, q_pe, c, bt, sl, inp["scale"], S, o_part,
                       lse_part) for c in caches]
+    heads = [mla.bind(mla.mla_decode_attn_planned, q_lat, q_pe, c, bt, sl, inp["scale"], S, o_part,
+                      lse_part, kernel="heads") for c in caches]
     combine = mla.bind(mla.mla_splitk_combine, o_part, lse_part, out, lse)
     t0 = time.perf_counter()
     k = 0
@@ -450,12 +452,15 @@ def fp8_rows(mla, torch, inp, num_cus, steps, n_copies):
             torch.cuda.synchronize()
     step_ms = timed_ms(torch, lambda k: (calls[k % n_copies](), combine()), steps)
     attn_ms = timed_ms(torch, lambda k: calls[k % n_copies](), steps)
+    heads_ms = timed_ms(torch, lambda k: heads[k % n_copies](), steps)
     tokens = B * T
     fp8_bytes = tokens * 656
     attn_bytes = fp8_bytes + B * H * 576 * 2 + bt.numel() * 4 + B * 4
     del caches
     return {"workload": "dsv2_b32_t4k over fp8 latent rows (MLA_FP8, 656 B per token)",
-            "num_splits": S, "us_per_step": round(step_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
+            "num_splits": S, "attention_kernel": "wide (32 heads per wavefront)",
+            "us_per_step": round(step_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
+            "attn_us_heads_kernel": round(heads_ms * 1e3, 2),
             "cache_bytes": fp8_bytes, "cache_GBps_step": round(fp8_bytes / (step_ms * 1e-3) / 1e9, 1),
             "attn_GBps": round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1),
             "attn_frac": round(attn_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),

@@ -1,6 +1,7 @@
-// Pieces shared by the two bf16 MFMA attention kernels (attn_mfma.hip, attn_cols.hip):
+// Pieces shared by the MFMA attention kernels (attn_mfma.hip, attn_cols.hip, attn_wide.hip):
 // the cache-tile geometry in LDS, its 16-byte-chunk swizzle, the HBM -> LDS copy issued
-// from inline assembly and the explicit wait counts that go with it.
+// from inline assembly and the explicit wait counts that go with it, and the staging of
+// fp8 rows into that tile layout.
 #pragma once
 
 #include "device_common.h"
@@ -55,6 +56,15 @@ __device__ __forceinline__ uint32_t tile_chunk_voff(unsigned chunk, unsigned las
   return __umul24(trow, static_cast<unsigned>(ROW_BYTES)) + c * 16;
 }
 
+// fp8 latent rows (656 bytes: 512 E4M3 codes, 64 bf16 k^R values, 4 fp32 block scales, one
+// per 128 codes) are copied into LDS raw, a tile of 32 rows as 41 chunks of 16 bytes per row
+// in 21 wave-wide copies of 1 KB, and converted there into the bf16 tile layout above.
+constexpr int FP8_ROW_BYTES = 656;
+constexpr int FP8_ROW_CHUNKS = FP8_ROW_BYTES / 16;                  // 41
+constexpr int FP8_TILE_CHUNKS = TILE * FP8_ROW_CHUNKS;               // 1312
+constexpr int FP8_COPIES = (FP8_TILE_CHUNKS + 63) / 64;              // 21 wave copies
+constexpr int FP8_STAGE_BYTES = FP8_COPIES * 1024;                   // 21504
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
@@ -91,6 +101,73 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
       : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+// Copy q (0 .. 20) of a raw fp8 tile whose first row is at `base`: lane l moves chunk
+// n = 64 q + l, i.e. row n / 41, bytes 16 (n % 41) .. of it, to staging byte 16 n (stage_lds
+// + 1024 q + 16 l); lanes past the tile's 1312 chunks re-read its last chunk into the
+// buffer's tail.  Rows past `last` repeat row `last`.
+__device__ __forceinline__ void fp8_tile_copy(const char* base, unsigned last, uint32_t stage_lds,
+                                              unsigned q, int lane) {
+  int ln = lane;
+  asm volatile("" : "+v"(ln));  // recomputed at every copy (no live ranges across the loop)
+  const unsigned n = min(64u * q + ln, static_cast<unsigned>(FP8_TILE_CHUNKS - 1));
+  const unsigned t = __umul24(n, 3197u) >> 17;  // n / 41 for n < 1312
+  const unsigned c = n - __umul24(t, static_cast<unsigned>(FP8_ROW_CHUNKS));
+  const unsigned row = min(t, last);
+  dma16(base, __umul24(row, static_cast<unsigned>(FP8_ROW_BYTES)) + 16u * c, stage_lds + q * 1024);
+}
+
+// Latent chunk e (0 .. 2047) of a bf16 tile from the staged raw rows at src: row t = e / 64,
+// logical chunk c = e % 64 (latent values 8 c .. 8 c + 7: 8 codes of block c / 16 times that
+// block's power-of-two scale, exact in bf16), stored at position c ^ swz(t) of dst.
+__device__ __forceinline__ void fp8_convert_latent(const lds_char_t* src, lds_char_t* dst, int e) {
+  asm volatile("" : "+v"(e));
+  const unsigned t = static_cast<unsigned>(e) >> 6, c = static_cast<unsigned>(e) & 63u;
+  const lds_char_t* row = src + __umul24(t, static_cast<unsigned>(FP8_ROW_BYTES));
+  typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+  const u32x2_t codes = *(const __attribute__((address_space(3))) u32x2_t*)(row + 8 * c);
+  const float sc = *(const lds_f32_t*)(row + 640 + 4 * (c >> 4));
+  i32x4_t v;
+  v[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], sc, false));
+  v[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], sc, true));
+  v[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], sc, false));
+  v[3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], sc, true));
+  *(__attribute__((address_space(3))) i32x4_t*)(dst + t * ROW_BYTES + 16 * (c ^ swz(t))) = v;
+}
+
+// k^R chunk e (0 .. 255) of a bf16 tile: row t = e / 8, logical chunk 64 + e % 8, the bf16
+// bytes 16 (e % 8) .. of the raw row's k^R part as they are.
+__device__ __forceinline__ void fp8_copy_rope(const lds_char_t* src, lds_char_t* dst, int e) {
+  asm volatile("" : "+v"(e));
+  const unsigned t = static_cast<unsigned>(e) >> 3, c = 64u + (static_cast<unsigned>(e) & 7u);
+  const lds_char_t* row = src + __umul24(t, static_cast<unsigned>(FP8_ROW_BYTES));
+  *(__attribute__((address_space(3))) i32x4_t*)(dst + t * ROW_BYTES + 16 * (c ^ swz(t))) =
+      *(const __attribute__((address_space(3))) i32x4_t*)(row + 512 + 16 * (c - 64));
+}
+
+// Chunk e (0 .. 2303) of a bf16 tile from the staged raw rows at src: row t = e / 72,
+// logical chunk c = e % 72, stored at position c ^ swz(t) of dst; c < 64 holds latent values
+// 8 c .. 8 c + 7 (8 codes of block c / 16 times that block's scale: a power of two, so the
+// product is exact in bf16), c >= 64 the k^R bytes 16 (c - 64) .. as they are.
+__device__ __forceinline__ void fp8_convert_chunk(const lds_char_t* src, lds_char_t* dst, int e) {
+  asm volatile("" : "+v"(e));
+  const unsigned t = __umul24(static_cast<unsigned>(e), 7282u) >> 19;  // e / 72
+  const unsigned c = static_cast<unsigned>(e) - __umul24(t, static_cast<unsigned>(CHUNKS));
+  const lds_char_t* row = src + __umul24(t, static_cast<unsigned>(FP8_ROW_BYTES));
+  i32x4_t v;
+  if (c < 64) {
+    typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+    const u32x2_t codes = *(const __attribute__((address_space(3))) u32x2_t*)(row + 8 * c);
+    const float sc = *(const lds_f32_t*)(row + 640 + 4 * (c >> 4));
+    v[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], sc, false));
+    v[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], sc, true));
+    v[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], sc, false));
+    v[3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], sc, true));
+  } else {
+    v = *(const __attribute__((address_space(3))) i32x4_t*)(row + 512 + 16 * (c - 64));
+  }
+  *(__attribute__((address_space(3))) i32x4_t*)(dst + t * ROW_BYTES + 16 * (c ^ swz(t))) = v;
+}
 
 // round-to-nearest-even pack of two floats (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ bf16x2_t to_bf16x2(float a, float b) {

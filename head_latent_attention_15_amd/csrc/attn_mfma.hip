@@ -60,15 +60,8 @@ constexpr int PAGE_TABLE = VOFF_TABLE + TILE_WAVE_COPIES * 64 * 4;  // after 36 
 constexpr int MAX_SPLIT_PAGES = 1024;               // block-table entries of one split in LDS
 constexpr int LDS_BYTES = PAGE_TABLE + MAX_SPLIT_PAGES * 4;
 static_assert(LDS_BYTES <= 163840, "LDS per workgroup");
-// fp8 latent rows (656 bytes: 512 E4M3 codes, 64 bf16 k^R, 4 fp32 block scales) are
-// staged raw and converted into the same bf16 tile buffers: three of those, two staging
-// buffers (a tile of rows is 41 chunks of 16 bytes x 32 rows, copied as 21 wave-wide copies
-// of 1 KB), then the block table.
-constexpr int FP8_ROW_BYTES = 656;
-constexpr int FP8_ROW_CHUNKS = FP8_ROW_BYTES / 16;                  // 41
-constexpr int FP8_TILE_CHUNKS = TILE * FP8_ROW_CHUNKS;               // 1312
-constexpr int FP8_COPIES = (FP8_TILE_CHUNKS + 63) / 64;              // 21 wave copies
-constexpr int FP8_STAGE_BYTES = FP8_COPIES * 1024;                   // 21504
+// fp8 latent rows are staged raw and converted into the same bf16 tile buffers: three of
+// those, two staging buffers, then the block table.
 constexpr int FP8_NBUF = 3;
 constexpr int FP8_STAGE = FP8_NBUF * TILE_BYTES;
 constexpr int FP8_PAGE_TABLE = FP8_STAGE + 2 * FP8_STAGE_BYTES;
@@ -230,55 +223,26 @@ __device__ __forceinline__ void attn_split(
   // 1312 chunks re-read its last chunk into the buffer's tail.  Rows past the split's end
   // repeat its last valid row.
   auto fp8_copy = [&](const char* base, int tb, int stage, int r) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
     const unsigned q = min(static_cast<unsigned>(w + NW * r), static_cast<unsigned>(FP8_COPIES - 1));
-    const unsigned n = min(64u * q + ln, static_cast<unsigned>(FP8_TILE_CHUNKS - 1));
-    const unsigned t = __umul24(n, 3197u) >> 17;  // n / 41 for n < 1312
-    const unsigned c = n - __umul24(t, static_cast<unsigned>(FP8_ROW_CHUNKS));
-    const unsigned row = min(t, static_cast<unsigned>(j1 - 1 - tb));
-    dma16(base, __umul24(row, static_cast<unsigned>(FP8_ROW_BYTES)) + 16u * c,
-          smem_lds + FP8_STAGE + stage * FP8_STAGE_BYTES + q * 1024);
+    fp8_tile_copy(base, static_cast<unsigned>(j1 - 1 - tb),
+                  smem_lds + FP8_STAGE + stage * FP8_STAGE_BYTES, q, lane);
   };
   auto fp8_issue_tile = [&](int tb, int stage) {
     const char* base = tile_base(tb);
 #pragma unroll
     for (int r = 0; r < COPIES; ++r) fp8_copy(base, tb, stage, r);
   };
-  // Converts the staged raw rows of a tile into bf16 buffer buf: chunk e (0 .. 2303) of the
-  // bf16 tile is row t = e / 72, logical chunk c = e % 72, stored at position c ^ swz(t);
-  // c < 64 holds latent values 8 c .. 8 c + 7 (8 codes of block c / 16 times that block's
-  // scale), c >= 64 the k^R bytes 16 (c - 64) .. as they are.  Thread tid takes chunks
-  // tid, tid + NT, ...
+  // Converts the staged raw rows of a tile into bf16 buffer buf (fp8_convert_chunk); thread
+  // tid takes chunks tid, tid + NT, ...
   constexpr int CONV = (TILE_CHUNKS + NT - 1) / NT;  // chunks per thread and tile
-  auto fp8_convert_chunk = [&](int stage, int buf, int i) {
-    const lds_char_t* src = lsm + FP8_STAGE + stage * FP8_STAGE_BYTES;
-    lds_char_t* dst = lsm + buf * TILE_BYTES;
-    {
-      int e = tid + NT * i;
-      asm volatile("" : "+v"(e));
-      if (TILE_CHUNKS % NT != 0 && e >= TILE_CHUNKS) return;
-      const unsigned t = __umul24(static_cast<unsigned>(e), 7282u) >> 19;  // e / 72
-      const unsigned c = static_cast<unsigned>(e) - __umul24(t, static_cast<unsigned>(CHUNKS));
-      const lds_char_t* row = src + __umul24(t, static_cast<unsigned>(FP8_ROW_BYTES));
-      i32x4_t v;
-      if (c < 64) {
-        typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
-        const u32x2_t codes = *(const __attribute__((address_space(3))) u32x2_t*)(row + 8 * c);
-        const float sc = *(const lds_f32_t*)(row + 640 + 4 * (c >> 4));
-        v[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], sc, false));
-        v[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[0], sc, true));
-        v[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], sc, false));
-        v[3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[1], sc, true));
-      } else {
-        v = *(const __attribute__((address_space(3))) i32x4_t*)(row + 512 + 16 * (c - 64));
-      }
-      *(__attribute__((address_space(3))) i32x4_t*)(dst + t * ROW_BYTES + 16 * (c ^ swz(t))) = v;
-    }
+  auto fp8_convert_chunk_i = [&](int stage, int buf, int i) {
+    const int e = tid + NT * i;
+    if (TILE_CHUNKS % NT != 0 && e >= TILE_CHUNKS) return;
+    fp8_convert_chunk(lsm + FP8_STAGE + stage * FP8_STAGE_BYTES, lsm + buf * TILE_BYTES, e);
   };
   auto fp8_convert = [&](int stage, int buf) {
 #pragma unroll
-    for (int i = 0; i < CONV; ++i) fp8_convert_chunk(stage, buf, i);
+    for (int i = 0; i < CONV; ++i) fp8_convert_chunk_i(stage, buf, i);
   };
   // The copy coordinates do not depend on the tile: the workgroup writes them once to an
   // LDS table, row t << 16 | chunk byte offset, and a copy inside the loop reads its lane's

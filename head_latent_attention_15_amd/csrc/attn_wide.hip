@@ -57,6 +57,13 @@ constexpr int W_PAGE_TABLE = W_NBUF * TILE_BYTES;      // LDS block table of the
 constexpr int W_MAX_SPLIT_PAGES = 1024;
 constexpr int W_LDS_BYTES = W_PAGE_TABLE + W_MAX_SPLIT_PAGES * 4;
 static_assert(W_LDS_BYTES <= 163840, "LDS per workgroup");
+// fp8 rows: three bf16 tile buffers, two raw staging buffers, then the block table
+constexpr int W8_NBUF = 3;
+constexpr int W8_STAGE = W8_NBUF * TILE_BYTES;
+constexpr int W8_PAGE_TABLE = W8_STAGE + 2 * FP8_STAGE_BYTES;
+constexpr int W8_LDS_BYTES = W8_PAGE_TABLE + W_MAX_SPLIT_PAGES * 4;
+static_assert(W8_LDS_BYTES <= 163840, "LDS per workgroup (fp8 rows)");
+constexpr int W8_COPIES = (FP8_COPIES + WW - 1) / WW;  // 6 raw copies per tile and wave
 constexpr int W_COPIES = TILE_WAVE_COPIES / WW;        // 9 wave-wide copies per tile and wave
 static_assert(W_COPIES * WW == TILE_WAVE_COPIES, "copies split evenly");
 constexpr int W_KSTEPS = ROW / 16;                     // 36 score k-steps of 16 features
@@ -91,14 +98,22 @@ __device__ __forceinline__ void chain_drain(f32x16_t& x, f32x16_t& y) {
 // prow0 + h * hstride of o_part / lse_part.  Every thread of the workgroup calls it with the
 // same arguments.  Wavefront w owns heads 32 w .. 32 w + 31.  KRING: K fragments in flight
 // in the score loop (6; 4 where the caller keeps more state live, as the ragged kernel).
-template <typename OT, int KRING, typename SplitEnd>
+// FP8: the cache holds fp8 rows (656 bytes); each tile is copied raw into one of two
+// staging buffers, all of its copies right after the barrier two tiles ahead of its use,
+// and converted by the whole workgroup into one of three bf16 tile buffers one tile ahead
+// (fp8_convert_chunk: code times its block's power-of-two scale, exact in bf16), so the
+// score and PV steps are the bf16 ones.
+template <typename OT, int KRING, bool FP8, typename SplitEnd>
 __device__ __forceinline__ void wide_split(
     const bf16raw* __restrict__ q_lat, const bf16raw* __restrict__ q_pe,
     const bf16raw* __restrict__ cache, const int32_t* __restrict__ block_table, int H,
     int log2P, int max_pages, float scale_log2, OT* __restrict__ o_part,
     float* __restrict__ lse_part, int b, int bq, int j0, SplitEnd split_end, int64_t prow0,
     int hstride) {
-  __shared__ __attribute__((aligned(16))) char smem[W_LDS_BYTES];
+  constexpr int NB = FP8 ? W8_NBUF : W_NBUF;             // bf16 tile buffers
+  constexpr int PTAB = FP8 ? W8_PAGE_TABLE : W_PAGE_TABLE;
+  constexpr int SRC_ROW = FP8 ? FP8_ROW_BYTES : ROW_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[FP8 ? W8_LDS_BYTES : W_LDS_BYTES];
   lds_char_t* const lsm = (lds_char_t*)smem;
   const uint32_t smem_lds = static_cast<uint32_t>(reinterpret_cast<size_t>(lsm));
 
@@ -150,7 +165,7 @@ __device__ __forceinline__ void wide_split(
 
   const char* cache_bytes = reinterpret_cast<const char*>(cache);
   auto page_base = [&](int pg, int tb) {
-    return cache_bytes + ((static_cast<int64_t>(pg) << log2P) + (tb & (P - 1))) * ROW_BYTES;
+    return cache_bytes + ((static_cast<int64_t>(pg) << log2P) + (tb & (P - 1))) * SRC_ROW;
   };
   const int ntiles = (j1 - j0 + TILE - 1) / TILE;
   const int npages = (j1 - j0 + P - 1) >> log2P;
@@ -169,6 +184,27 @@ __device__ __forceinline__ void wide_split(
   };
   const std::true_type clamped;
   const std::false_type unclamped;
+  // fp8 rows: this wave's copies q = w, w + 4, ... (the 21st repeated) of the raw tile at
+  // token tb into staging buffer `stage`
+  auto fp8_issue_tile = [&](const char* base, int tb, int stage) {
+#pragma unroll
+    for (int r = 0; r < W8_COPIES; ++r)
+      fp8_tile_copy(base, static_cast<unsigned>(j1 - 1 - tb), smem_lds + W8_STAGE + stage * FP8_STAGE_BYTES,
+                    min(static_cast<unsigned>(w + WW * r), static_cast<unsigned>(FP8_COPIES - 1)), lane);
+  };
+  // fp8 rows: this thread's 9 chunks of the bf16 tile in buffer buf from staging buffer
+  // stage: eight latent chunks, then one of k^R (so no wavefront branches on the kind)
+  auto fp8_convert = [&](int stage, int buf) {
+    static_assert(TILE * 64 == 8 * WW * 64 && TILE * 8 == WW * 64, "conversion chunks split evenly");
+    const lds_char_t* src = lsm + W8_STAGE + stage * FP8_STAGE_BYTES;
+    lds_char_t* dst = lsm + buf * TILE_BYTES;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      fp8_convert_latent(src, dst, tid + WW * 64 * i);
+      __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: registers are full
+    }
+    fp8_copy_rope(src, dst, tid);
+  };
 
   // ---- prologue.  Tile 0's copies go out behind the queries, then the split's block-table
   //      entries into LDS; the first barrier waits for all of it.  The copies of tiles 1 and
@@ -177,18 +213,28 @@ __device__ __forceinline__ void wide_split(
   //      tile 0's score steps): row n's chunk c of a q~ part at slot 33 n + c of the wave's
   //      first area, of q^R at slot 9 n + c of its second; one slot of padding per row keeps
   //      the reads of the B layout conflict-free.
+  //      With fp8 rows the raw tiles 0 and 1 go to the staging buffers instead, and the
+  //      queries are transposed through the bf16 tile buffers from their start (tile 0 is
+  //      converted after the first barrier).
   constexpr int QSA = 33 * 16 * WH, QSC = 9 * 16 * WH;  // staging bytes per wave
-  static_assert(TILE_BYTES + WW * (QSA + QSC) <= W_NBUF * TILE_BYTES, "query staging fits tiles 1-3");
+  constexpr int QBASE = FP8 ? 0 : TILE_BYTES;
+  static_assert(QBASE + WW * (QSA + QSC) <= NB * TILE_BYTES, "query staging fits the free tile buffers");
   bf16x8_t qf[W_KSTEPS];
   {
-    {
+    if constexpr (FP8) {
+      fp8_issue_tile(page_base(pg0, j0), j0, 0);
+      if (ntiles > 1) {
+        const int tb1 = j0 + TILE;
+        fp8_issue_tile(page_base(__builtin_amdgcn_readfirstlane(bt_row[tb1 >> log2P]), tb1), tb1, 1);
+      }
+    } else {
       const char* base0 = page_base(pg0, j0);
 #pragma unroll
       for (int r = 0; r < W_COPIES; ++r)
         issue_copy(base0, static_cast<unsigned>(j1 - 1 - j0), smem_lds, r, clamped);
     }
-    lds_char_t* const qa = lsm + TILE_BYTES + w * QSA;
-    lds_char_t* const qc = lsm + TILE_BYTES + WW * QSA + w * QSC;
+    lds_char_t* const qa = lsm + QBASE + w * QSA;
+    lds_char_t* const qc = lsm + QBASE + WW * QSA + w * QSC;
     // load i of a q~ part holds row 2 i + hf, chunk n32; of q^R, row 8 i + lane / 8, chunk lane % 8
     auto stage_a = [&](const bf16x8_t* raw) {
 #pragma unroll
@@ -207,7 +253,14 @@ __device__ __forceinline__ void wide_split(
     stage_a(rawb);
     unstage_a(16);
   }
-  lds_i32_t* const ptab = (lds_i32_t*)(lsm + W_PAGE_TABLE);
+  lds_i32_t* const ptab = (lds_i32_t*)(lsm + PTAB);
+  // tile buffer of tile it; with three buffers the offset is made opaque, since the compiler
+  // otherwise strength-reduces every fragment address of the loop into registers of its own
+  auto tile_at = [&](int it) -> const lds_char_t* {
+    int off = (it % NB) * TILE_BYTES;
+    if constexpr (NB != W_NBUF) asm volatile("" : "+s"(off));
+    return lsm + off;
+  };
   for (int e = tid; e < npages; e += WW * 64) ptab[e] = bt_row[(j0 >> log2P) + e];
   auto split_page = [&](int tb) {
     return __builtin_amdgcn_readfirstlane(ptab[(tb - j0) >> log2P]);
@@ -258,7 +311,7 @@ __device__ __forceinline__ void wide_split(
   auto copy_tb = [&](int it) { return j0 + (it + 2 < ntiles ? it + 2 : min(it, ntiles - 1)) * TILE; };
   auto scores = [&](int it, auto first, auto tail) -> f32x16_t {
     constexpr bool FIRST = decltype(first)::value;
-    const lds_char_t* tile = lsm + (it % W_NBUF) * TILE_BYTES;
+    const lds_char_t* tile = tile_at(it);
     const int tb2 = copy_tb(it);
     const char* base2 = copy_src(tb2);
     const unsigned last2 = static_cast<unsigned>(j1 - 1 - tb2);
@@ -280,7 +333,9 @@ __device__ __forceinline__ void wide_split(
       else if (kk == 1) s1 = mfma32_v_first(ka[1], qf[1]);
       else if (kk & 1) mfma32_v(s1, ka[kk % KRING], qf[kk]);
       else mfma32_v(s0, ka[kk % KRING], qf[kk]);
-      if constexpr (FIRST) {
+      if constexpr (FP8) {
+        // fp8 rows: the raw copies are issued at the barrier, not here
+      } else if constexpr (FIRST) {
         if (kk % 2 == 0 && kk / 2 < W_COPIES) issue_copy(base1, last1, smem_lds + TILE_BYTES, kk / 2, tail);
         else if (kk % 2 == 0) issue_copy(base2, last2, lds2, kk / 2 - W_COPIES, tail);
       } else if (kk % 4 == 0) {
@@ -343,7 +398,7 @@ __device__ __forceinline__ void wide_split(
   auto pv = [&](int it, bf16x8_t p0, bf16x8_t p1, auto soft, const f32x16_t& sc, bf16x8_t& n0,
                 bf16x8_t& n1) {
     constexpr bool SOFT = decltype(soft)::value;
-    const lds_char_t* tile = lsm + (it % W_NBUF) * TILE_BYTES;
+    const lds_char_t* tile = tile_at(it);
     constexpr int VRING = 4;
     constexpr int NST = 2 * W_CT;
     bf16x8_t va[VRING];
@@ -369,6 +424,14 @@ __device__ __forceinline__ void wide_split(
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // block table in LDS
   wait_vmcnt<0>();                                    // tile 0 and the queries
   block_barrier();
+  if constexpr (FP8) {
+    // raw tile 0 into bf16 buffer 0 (every wave's query reads of the buffers are done);
+    // then raw tile 2 into the staging buffer tile 0 left
+    fp8_convert(0, 0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    block_barrier();
+    if (ntiles > 2) fp8_issue_tile(copy_src(j0 + 2 * TILE), j0 + 2 * TILE, 0);
+  }
   bf16x8_t p0, p1;
   {
     f32x16_t sc = scores(0, std::true_type(), clamped);
@@ -385,11 +448,27 @@ __device__ __forceinline__ void wide_split(
     }
     soft_done(p0, p1);
   }
+  if constexpr (FP8) {
+    if (ntiles > 1) fp8_convert(1, 1);
+  }
   for (int it = 1; it < ntiles; ++it) {
-    wait_vmcnt<W_COPIES>();  // own copies of tile it landed (tile it+1's may be in flight)
-    block_barrier();
-    f32x16_t sc = j1 - copy_tb(it) >= TILE ? scores(it, std::false_type(), unclamped)
-                                            : scores(it, std::false_type(), clamped);
+    f32x16_t sc;
+    if constexpr (FP8) {
+      // Barrier it publishes bf16 tile it (converted during tile it-1) and raw tile it+1
+      // (copied since barrier it-1).  Then raw tile it+2 goes to the staging buffer raw tile
+      // it left, and raw tile it+1 is converted into the buffer tile it-2 left.
+      wait_vmcnt<0>();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      block_barrier();
+      if (it + 2 < ntiles) fp8_issue_tile(copy_src(j0 + (it + 2) * TILE), j0 + (it + 2) * TILE, it & 1);
+      if (it + 1 < ntiles) fp8_convert((it + 1) & 1, (it + 1) % NB);
+      sc = scores(it, std::false_type(), unclamped);
+    } else {
+      wait_vmcnt<W_COPIES>();  // own copies of tile it landed (tile it+1's may be in flight)
+      block_barrier();
+      sc = j1 - copy_tb(it) >= TILE ? scores(it, std::false_type(), unclamped)
+                                    : scores(it, std::false_type(), clamped);
+    }
     mask_tail(sc, it);
     bf16x8_t n0, n1;
     pv(it - 1, p0, p1, std::integral_constant<bool, true>(), sc, n0, n1);
@@ -458,15 +537,15 @@ __device__ __forceinline__ void wide_split(
     }
   }
   if (fallback)
-    split_exact_fallback<OT, false>(q_lat, q_pe, cache, bt_row, log2P, j0, j1, bq, H, prow0,
-                                    hstride, scale_log2, o_part, lse_part, h0, WH, lane);
+    split_exact_fallback<OT, FP8>(q_lat, q_pe, cache, bt_row, log2P, j0, j1, bq, H, prow0,
+                                  hstride, scale_log2, o_part, lse_part, h0, WH, lane);
 }
 
 // One workgroup of four wavefronts per (sequence, split) (blockIdx.x, blockIdx.y) and query
 // token (blockIdx.z), as attn_mfma_kernel: token t of n_q sits at position seq_len - n_q + t,
 // its queries and partials are row bq = b n_q + t, and the splits of a sequence share its
-// XCD.
-template <typename OT>
+// XCD.  FP8: the cache holds fp8 rows.
+template <typename OT, bool FP8>
 __global__ __launch_bounds__(WW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restrict__ q_pe,
                       const bf16raw* __restrict__ cache, const int32_t* __restrict__ block_table,
@@ -475,7 +554,7 @@ void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restri
                       float* __restrict__ lse_part, int n_q) {
   const int b = blockIdx.x, s = blockIdx.y, z = blockIdx.z, bq = b * n_q + z;
   const int j0 = s * (pages_per_split << log2P);
-  wide_split<OT, 6>(q_lat, q_pe, cache, block_table, H, log2P, max_pages, scale_log2, o_part,
+  wide_split<OT, 6, FP8>(q_lat, q_pe, cache, block_table, H, log2P, max_pages, scale_log2, o_part,
                     lse_part, b, bq, j0,
                  [&] { return min(seq_lens[b] - (n_q - 1 - z), j0 + (pages_per_split << log2P)); },
                  static_cast<int64_t>(bq) * H * S + s, S);
@@ -519,16 +598,16 @@ void attn_wide_ragged_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* _
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int j1 = pc.j1;
-    wide_split<OT, 4>(q_lat, q_pe, cache, block_table, H, log2P, max_pages, scale_log2, o_part,
+    wide_split<OT, 4, false>(q_lat, q_pe, cache, block_table, H, log2P, max_pages, scale_log2, o_part,
                       lse_part, pc.b, pc.b, pc.j0, [&] { return j1; },
                    static_cast<int64_t>(pc.first) * H + pc.index, pc.count);
   }
 }
 
-template <typename OT>
+template <typename OT, bool FP8>
 hipError_t launch_wide_t(const PagedArgs& a, hipStream_t st) {
   const float log2e = 1.4426950408889634f;
-  hipLaunchKernelGGL((attn_wide_kernel<OT>), dim3(a.B, a.num_splits, a.n_q), dim3(WW * 64), 0, st,
+  hipLaunchKernelGGL((attn_wide_kernel<OT, FP8>), dim3(a.B, a.num_splits, a.n_q), dim3(WW * 64), 0, st,
                      static_cast<const bf16raw*>(a.q_lat), static_cast<const bf16raw*>(a.q_pe),
                      static_cast<const bf16raw*>(a.cache), a.block_table, a.seq_lens, a.H,
                      __builtin_ctz(static_cast<unsigned>(a.page_size)), a.max_pages,
@@ -563,7 +642,12 @@ hipError_t launch_attn_wide_ragged(const PagedArgs& a, int grid, int* seq_slots,
 
 hipError_t launch_attn_wide_bf16_512_64(const PagedArgs& a, hipStream_t s) {
   if (!attn_wide_supported(a)) return hipErrorInvalidValue;
-  return a.part_bf16 ? launch_wide_t<bf16raw>(a, s) : launch_wide_t<float>(a, s);
+  return a.part_bf16 ? launch_wide_t<bf16raw, false>(a, s) : launch_wide_t<float, false>(a, s);
+}
+
+hipError_t launch_attn_wide_fp8(const PagedArgs& a, hipStream_t s) {
+  if (!attn_wide_supported(a)) return hipErrorInvalidValue;
+  return a.part_bf16 ? launch_wide_t<bf16raw, true>(a, s) : launch_wide_t<float, true>(a, s);
 }
 
 }  // namespace mla

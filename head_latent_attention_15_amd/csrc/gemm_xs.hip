@@ -109,25 +109,6 @@ __global__ __launch_bounds__(512) void gemm_xs_kernel(const XT* x, const bf16raw
   const int ntl = a.nt;
   const int nsteps = S * ntl;
 
-  // ---- x slice: raw rows by LDS DMA.  The slab (row t at t * RAWROW) is filled by 1 KB
-  //      copies in order; lane l of copy i fills bytes 1024 i + 16 l, i.e. row t = that /
-  //      RAWROW, from x[min(t, M - 1)][k0 ..] (a copy may span two rows)
-  constexpr int NCOPY = 64 * RAWROW / 1024;
-  static_assert(NCOPY % 8 == 0, "copies split evenly over the waves");
-  {
-    const char* xb = reinterpret_cast<const char*>(x + k0);
-#pragma unroll
-    for (int i = 0; i < NCOPY / 8; ++i) {
-      const int cp = wave * (NCOPY / 8) + i;
-      const int byte = cp * 1024 + lane * 16;
-      const int t = byte / RAWROW, o = byte - t * RAWROW;
-      const int srow = min(t, a.M - 1);
-      dma16(xb, static_cast<uint32_t>(srow * a.ldx * sizeof(XT)) + static_cast<uint32_t>(o),
-            smem_lds + cp * 1024);
-    }
-  }
-  asm volatile("" ::: "memory");  // the weight loads below stay behind the copies
-
   // ---- weights: lane (g, r) of wave wv reads rows tile * CW + 16 (TN wv + j) + r
   const bf16raw* wlane[TN];
 #pragma unroll
@@ -147,10 +128,30 @@ __global__ __launch_bounds__(512) void gemm_xs_kernel(const XT* x, const bf16raw
 #pragma unroll
     for (int j = 0; j < TN; ++j) wf[i][j] = w_frag(0, i, j);
 
-  // ---- wait for this wave's copies (issued before the R - 1 steps of weight loads), then
-  //      for everyone's; convert in place
-  static_assert(TN * (R - 1) < 64, "wait count fits the counter");
-  wait_vmcnt<TN * (R - 1)>();
+  // ---- x slice: raw rows by LDS DMA.  The slab (row t at t * RAWROW) is filled by 1 KB
+  //      copies in order; lane l of copy i fills bytes 1024 i + 16 l, i.e. row t = that /
+  //      RAWROW, from x[min(t, M - 1)][k0 ..] (a copy may span two rows)
+  constexpr int NCOPY = 64 * RAWROW / 1024;
+  static_assert(NCOPY % 8 == 0, "copies split evenly over the waves");
+  {
+    const char* xb = reinterpret_cast<const char*>(x + k0);
+#pragma unroll
+    for (int i = 0; i < NCOPY / 8; ++i) {
+      const int cp = wave * (NCOPY / 8) + i;
+      const int byte = cp * 1024 + lane * 16;
+      const int t = byte / RAWROW, o = byte - t * RAWROW;
+      const int srow = min(t, a.M - 1);
+      dma16(xb, static_cast<uint32_t>(srow * a.ldx * sizeof(XT)) + static_cast<uint32_t>(o),
+            smem_lds + cp * 1024);
+    }
+  }
+  asm volatile("" ::: "memory");  // the copies stay behind the weight prefetches
+
+  // ---- wait for everything this wave issued (the weight prefetches went out first, so
+  //      they are in flight beside the copies), then for everyone's copies; convert in
+  //      place.  Counting to zero keeps the wait independent of how many loads the
+  //      compiler emits for the prefetch.
+  wait_vmcnt<0>();
   __syncthreads();
   if constexpr (SPLIT_X) {
     // thread t converts 16-byte raw pieces q = t + 512 i (4 floats each) of the slab,
@@ -234,15 +235,17 @@ __global__ __launch_bounds__(512) void gemm_xs_kernel(const XT* x, const bf16raw
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt) {
+        if (16 * mt < a.M) {  // wave-uniform: 16-row tiles wholly past M add nothing
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // rows past M add zero to row 0 instead: no branch in the loop
-          const int m = 16 * mt + 4 * g + e;
-          const bool ok = m < a.M;
-          atomicAdd(yt + static_cast<int64_t>(ok ? m : 0) * a.ldy + 16 * j, ok ? acc[j][mt][e] : 0.f);
-          acc[j][mt][e] = 0.f;
+          for (int e = 0; e < 4; ++e) {
+            const int m = 16 * mt + 4 * g + e;
+            if (m < a.M) atomicAdd(yt + static_cast<int64_t>(m) * a.ldy + 16 * j, acc[j][mt][e]);
+          }
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[j][mt][e] = 0.f;
+      }
     // keep the accumulators in their own registers across tiles (folded into the next
     // MFMA as a zero operand, they were renamed into registers the weight ring uses, and
     // the first MFMA of every tile then waited for nearly the whole ring)

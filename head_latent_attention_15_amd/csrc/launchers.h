@@ -69,6 +69,8 @@ bool attn_wide_supported(const PagedArgs& a);
 // Its flattened ragged work list (as launch_attn_mfma_ragged; bf16 partials).
 hipError_t launch_attn_wide_ragged(const PagedArgs& a, int grid, int* seq_slots, int* err,
                                    hipStream_t s);
+// The same split-grid kernel over fp8 latent rows (raw rows staged in LDS and converted to bf16 there).
+hipError_t launch_attn_wide_fp8(const PagedArgs& a, hipStream_t s);
 
 // Split-K combine fused with the W^UV up-projection (d_c = 512, d_h = 128, S <= 64, bf16
 // W^UV): o_heads[b][i] = W^UV_i combine_s(o_part[b][i][s], lse_part[b][i][s]).

@@ -192,11 +192,16 @@ static mla_status_t decode_attn(const void* q_lat, const void* q_pe, const void*
 
   if (kernel < 0 || kernel > 4) return fail(MLA_ERR_UNSUPPORTED, "attention kernel %d unknown", kernel);
   if (dtype == MLA_FP8) {
-    if (a.d_c != 512 || a.d_R != 64 || !mla::attn_mfma_fp8_supported(a) || (kernel != 0 && kernel != 1))
+    if (a.d_c != 512 || a.d_R != 64 || !mla::attn_mfma_fp8_supported(a) ||
+        (kernel != 0 && kernel != 1 && kernel != 4) || (kernel == 4 && !mla::attn_wide_supported(a)))
       return fail(MLA_ERR_UNSUPPORTED, "fp8 cache: d_latent 512, d_rope 64, H = 128, pages of "
                   ">= 32 tokens (a power of two), <= 1024 pages per split, aligned tensors, "
-                  "kernel 0 or 1");
-    const mla_status_t st2 = launched(mla::launch_attn_mfma_fp8(a, s), "attention (fp8 cache)");
+                  "kernel 0, 1 or 4");
+    // the library's choice is the kernel with 32 heads per wavefront
+    if (kernel == 0) kernel = mla::attn_wide_supported(a) ? 4 : 1;
+    const mla_status_t st2 =
+        kernel == 4 ? launched(mla::launch_attn_wide_fp8(a, s), "attention (fp8 cache, 32 heads per wavefront)")
+                    : launched(mla::launch_attn_mfma_fp8(a, s), "attention (fp8 cache)");
     if (st2 != MLA_OK || merge == nullptr || num_splits == 1) return st2;
     return launched(mla::launch_splitk_combine(o_part, part_dtype == MLA_BF16, lse_part,
                                                a.B * n_q, a.H, num_splits, a.d_c, merge->out,

@@ -251,8 +251,9 @@ mla_status_t mla_quantize_cache(const void* src, mla_dtype_t src_dtype, int64_t 
  *   With num_splits == 1, o_part is the final o~ [B][H][d_latent] and lse_part may be NULL.
  * softmax_scale is normally 1/sqrt(d_h + d_R) (1/sqrt(192) at DeepSeek-V2 shape).
  * Supported: (d_latent, d_rope, dtype) = (512, 64, BF16) with H <= 128, (512, 64, FP8)
- * with H = 128 (the head-partitioned kernel, staging raw rows and converting them to bf16
- * in LDS), or (64, 16, F32) with H <= 64; otherwise UNSUPPORTED.
+ * with H = 128 (raw rows staged in LDS and converted to bf16 there, on the kernel with 32
+ * heads per wavefront when the tensors are 16-byte aligned, else the head-partitioned one),
+ * or (64, 16, F32) with H <= 64; otherwise UNSUPPORTED.
  * Errors: NULL, SHAPE (sizes < 1, page_size % 16, odd d_rope, num_splits < 1,
  * seq_lens bound max_pages_per_seq*page_size does not fit int32), UNSUPPORTED. */
 mla_status_t mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_cache,
@@ -290,8 +291,8 @@ mla_status_t mla_decode_attn_multi(const void* q_lat, const void* q_pe, const vo
  * wavefront on the 32 x 32 x 16 MFMA (H = 128; four wavefronts, each fragment read from LDS
  * feeds 32 heads).  Kernels 1, 2 and 4 need d_latent 512, d_rope 64, BF16, pages of >= 32
  * tokens (a power of two), at most 1024 pages per split and 16-byte aligned q_lat, q_pe,
- * kv_cache (and o_part for 2 and 4).  Same results, within rounding order, as
- * mla_decode_attn_multi.
+ * kv_cache (and o_part for 2 and 4); MLA_FP8 rows run on kernel 1 or 4.  Same results,
+ * within rounding order, as mla_decode_attn_multi.
  * Errors: as mla_decode_attn_multi, plus UNSUPPORTED for a kernel the shape cannot take. */
 mla_status_t mla_decode_attn_planned(const void* q_lat, const void* q_pe, const void* kv_cache,
                                      const int32_t* block_table, const int32_t* seq_lens,

@@ -105,7 +105,7 @@ def _fp8_problem(seed, B, seq_lens, H=128):
     return inp
 
 
-def attend_fp8(mla, inp, S, part, q_lat=None, q_pe=None, cache_bytes=None):
+def attend_fp8(mla, inp, S, part, q_lat=None, q_pe=None, cache_bytes=None, kernel="auto"):
     q_lat = dev(inp["q_lat"] if q_lat is None else q_lat)
     q_pe = dev(inp["q_pe"] if q_pe is None else q_pe)
     cache = dev(torch.from_numpy(inp["fp8"]) if cache_bytes is None else cache_bytes)
@@ -113,7 +113,8 @@ def attend_fp8(mla, inp, S, part, q_lat=None, q_pe=None, cache_bytes=None):
     rows = q_lat.shape[0] * (q_lat.shape[1] if q_lat.dim() == 4 else 1)
     o_part = torch.empty(rows, 128, S, 512, device="cuda", dtype=part if S > 1 else torch.float32)
     lse_part = torch.empty(rows, 128, S, device="cuda")
-    mla.mla_decode_attn_planned(q_lat, q_pe, cache, bt, sl, inp["scale"], S, o_part, lse_part)
+    mla.mla_decode_attn_planned(q_lat, q_pe, cache, bt, sl, inp["scale"], S, o_part, lse_part,
+                                kernel=kernel)
     if S == 1:
         torch.cuda.synchronize()
         return o_part.view(rows, 128, 512), lse_part.view(rows, 128)
@@ -139,21 +140,41 @@ def oracle_fp8(inp):
     return np.stack(o), np.stack(lse)
 
 
+FP8_KERNELS = ["heads", "wide"]
+
+
+@pytest.mark.parametrize("kernel", FP8_KERNELS)
 @pytest.mark.parametrize("S,part", [(1, torch.float32), (3, torch.float32), (8, torch.bfloat16),
                                     (64, torch.bfloat16)])
-def test_fp8_attention_against_oracle(mla, S, part):
+def test_fp8_attention_against_oracle(mla, S, part, kernel):
     inp = _fp8_problem(70, 5, [1, 31, 33, 700, 2050])
-    say(f"fp8 attention S={S} part={part}")
-    out, lse = attend_fp8(mla, inp, S, part)
+    say(f"fp8 attention S={S} part={part} kernel={kernel}")
+    out, lse = attend_fp8(mla, inp, S, part, kernel=kernel)
     o_ref, lse_ref = oracle_fp8(inp)
-    assert_bf16(host64(out), o_ref, f"fp8 S={S}")
+    assert_bf16(host64(out), o_ref, f"fp8 S={S} {kernel}")
     assert errors(host64(lse), lse_ref)[0] <= 2e-2
 
 
-def test_fp8_single_token_bit_exact(mla):
+@pytest.mark.parametrize("kernel", FP8_KERNELS)
+def test_fp8_split_tile_counts(mla, kernel):
+    """Splits of one, two, three and four 32-token tiles, full and ragged (the raw-row
+    staging runs two tiles ahead of the products, so each short count takes its own
+    path through the prologue), against the oracle."""
+    lens = [32, 33, 64, 65, 96, 97, 127, 128, 129, 1024, 1025]
+    inp = _fp8_problem(76, len(lens), lens)
+    say(f"fp8 tile counts kernel={kernel}")
+    for S in (1, 4, 8):
+        out, lse = attend_fp8(mla, inp, S, torch.float32, kernel=kernel)
+        o_ref, lse_ref = oracle_fp8(inp)
+        assert_bf16(host64(out), o_ref, f"fp8 tile counts S={S} {kernel}")
+        assert errors(host64(lse), lse_ref)[0] <= 2e-2
+
+
+@pytest.mark.parametrize("kernel", FP8_KERNELS)
+def test_fp8_single_token_bit_exact(mla, kernel):
     inp = _fp8_problem(71, 4, [1, 1, 1, 1])
-    say("fp8 single token")
-    out, _ = attend_fp8(mla, inp, 1, torch.float32)
+    say(f"fp8 single token kernel={kernel}")
+    out, _ = attend_fp8(mla, inp, 1, torch.float32, kernel=kernel)
     out = out.cpu()
     bt = inp["block_table"]
     for b in range(4):
@@ -161,7 +182,8 @@ def test_fp8_single_token_bit_exact(mla):
         assert torch.equal(out[b], want), f"seq {b}"
 
 
-def test_fp8_spike_takes_exact_fallback(mla):
+@pytest.mark.parametrize("kernel", FP8_KERNELS)
+def test_fp8_spike_takes_exact_fallback(mla, kernel):
     """Heads whose scores jump far above their reference take the exact fallback, which
     reads the fp8 rows itself: they select the dequantised spike row bit for bit."""
     seq_lens = [64, 129, 1000]
@@ -178,8 +200,8 @@ def test_fp8_spike_takes_exact_fallback(mla):
         inp["cache"][int(bt[b, j // 64]), j % 64, 512] = 64.0
     inp["fp8"] = F8.quantize_rows(inp["cache"].double().numpy())
     inp["deq"] = torch.from_numpy(F8.dequantize_rows(inp["fp8"]))
-    say("fp8 spike fallback")
-    out, _ = attend_fp8(mla, inp, 4, torch.float32)
+    say(f"fp8 spike fallback kernel={kernel}")
+    out, _ = attend_fp8(mla, inp, 4, torch.float32, kernel=kernel)
     out = out.cpu()
     for b, j in enumerate(spikes):
         want = inp["deq"][int(bt[b, j // 64]), j % 64, :512].float()
@@ -190,12 +212,13 @@ def test_fp8_spike_takes_exact_fallback(mla):
     assert_bf16(host64(out)[:, rest], o_ref[:, rest], "fp8 spike other heads")
 
 
-def test_fp8_multi_token(mla):
+@pytest.mark.parametrize("kernel", FP8_KERNELS)
+def test_fp8_multi_token(mla, kernel):
     n_q = 2
     inp = _fp8_problem(73, 3, [5, 300, 1100])
     q_lat, q_pe = W.multi_queries(74, 3, n_q, 128)
-    say("fp8 multi-token")
-    out, _ = attend_fp8(mla, inp, 4, torch.bfloat16, q_lat=q_lat, q_pe=q_pe)
+    say(f"fp8 multi-token kernel={kernel}")
+    out, _ = attend_fp8(mla, inp, 4, torch.bfloat16, q_lat=q_lat, q_pe=q_pe, kernel=kernel)
     o_ref, _ = oracle.paged_decode_multi(W.to_f64(q_lat), W.to_f64(q_pe), inp["deq"].numpy(),
                                          inp["block_table"].numpy(), inp["seq_lens"].numpy(),
                                          n_q, 512, inp["scale"])
@@ -203,11 +226,12 @@ def test_fp8_multi_token(mla):
 
 
 @pytest.mark.slow
-def test_fp8_dsv2_b32_t4k_full(mla):
+@pytest.mark.parametrize("kernel", FP8_KERNELS)
+def test_fp8_dsv2_b32_t4k_full(mla, kernel):
     """The headline shape over fp8 rows quantised on the GPU: the bytes of 4096 sampled
     rows against the oracle, then every output against the oracle on the dequantised rows."""
     inp = W.dsv2_b32_t4k()
-    say("fp8 dsv2_b32_t4k")
+    say(f"fp8 dsv2_b32_t4k kernel={kernel}")
     fp8 = quantize_gpu(mla, inp["cache"])
     flat = fp8.view(-1, 656).cpu().numpy()
     idx = np.random.default_rng(75).choice(flat.shape[0], 4096, replace=False)
@@ -216,7 +240,7 @@ def test_fp8_dsv2_b32_t4k_full(mla):
     inp["fp8"] = flat.reshape(fp8.shape)
     inp["deq"] = torch.from_numpy(F8.dequantize_rows(inp["fp8"]))
     S = mla.mla_suggest_num_splits(32, 4096, 0, 64, 256)
-    out, lse = attend_fp8(mla, inp, S, torch.bfloat16, cache_bytes=fp8)
+    out, lse = attend_fp8(mla, inp, S, torch.bfloat16, cache_bytes=fp8, kernel=kernel)
     o_ref, lse_ref = oracle_fp8(inp)
     m, r = assert_bf16(host64(out), o_ref, "fp8 dsv2_b32_t4k")
     print(f"fp8 dsv2_b32_t4k: max-abs {m:.3e} rel-L2 {r:.3e}")
