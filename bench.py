@@ -138,13 +138,14 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     roofline (every step is HBM-bound at this batch); then the whole chain, and the fp64
     oracle's layer on a few of the sequences.  In the chain every result is the same from
     run to run (checked: two runs, u bit for bit): [W^DQ; W^DKV; W^KR] h and W^O are split-k
-    products summed in a fixed order (mla_linear_deterministic), the append reads its inputs
-    in place, the query side ([W^UQ; W^QR] c^Q, RoPE, absorption) is one launch reading c^Q in
+    products summed in a fixed order (mla_linear_deterministic), the first one's summing
+    launch also writes the new token's cache row with its RoPE (mla_linear_deterministic_
+    append), the query side ([W^UQ; W^QR] c^Q, RoPE, absorption) is one launch reading c^Q in
     place (its weights packed once at load time, outside the timing), and the split-K combine
     is fused with W^UV.  Timed beside it: the chain with fp32-atomic projections
     accumulating into outputs cleared by one fill, with the query side as two launches (the
-    stacked product, then the absorption), with the combine and W^UV as two launches, and
-    the chain of separate products.  The fused steps' algorithmic bytes are their weights,
+    stacked product, then the absorption), with the combine and W^UV as two launches, with
+    the first product and the append as two launches, and the chain of separate products.  The fused steps' algorithmic bytes are their weights,
     inputs and outputs: q^C, q^R and the combined latent are never stored."""
     x = W.layer_b64_t2k()
     s = x["shape"]
@@ -177,12 +178,15 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     ws_lin = torch.empty(max(mla.mla_linear_deterministic_workspace_bytes(B, n_a, d),
                              mla.mla_linear_deterministic_workspace_bytes(B, d, H * d_h)),
                          dtype=torch.uint8, device="cuda")
+    append_bytes = B * (d_c + d_R) * 2  # the new rows written to the cache
+    det_a = mla.bind(mla.mla_linear_deterministic, h, w_a, y_a, ws_lin)
+    append = mla.bind(mla.mla_kv_append_strided, c_kv.unsqueeze(1), k_r.unsqueeze(1), before, bt,
+                      cache, x["rope_base"])
     rows = [
-        ("7 mla_linear_deterministic [W^DQ; W^DKV; W^KR] h",
-         [mla.bind(mla.mla_linear_deterministic, h, w_a, y_a, ws_lin)], nb(w_a) + nb(h) + nb(y_a)),
-        ("2 mla_kv_append_strided", [mla.bind(mla.mla_kv_append_strided, c_kv.unsqueeze(1),
-                                              k_r.unsqueeze(1), before, bt, cache, x["rope_base"])],
-         B * (d_c + d_R) * 4 + B * (d_c + d_R) * 2),
+        ("7+2 mla_linear_deterministic_append ([W^DQ; W^DKV; W^KR] h, RoPE and the cache append "
+         "in its summing launch)",
+         [mla.bind(mla.mla_linear_deterministic_append, h, w_a, y_a, ws_lin, d_cq, before, bt,
+                   cache, x["rope_base"])], nb(w_a) + nb(h) + nb(y_a) + append_bytes),
         ("7+1 mla_query_path (W^UQ, W^QR, RoPE, absorption in one launch)",
          [mla.bind(mla.mla_query_path, c_q, w_pack, seq_lens, x["rope_base"], q_lat, q_pe)],
          nb(w_b) + nb(w["w_uk"]) + B * d_cq * 4 + nb(q_lat) + nb(q_pe)),
@@ -197,7 +201,13 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
          [mla.bind(mla.mla_linear_deterministic, o_heads.view(B, H * d_h), w["w_o"], u, ws_lin)],
          nb(w["w_o"]) + nb(o_heads) + nb(u)),
     ]
-    # the same two products with fp32 atomic split-k (not in the main chain)
+    # the fused first step as its two calls, and the same two products with fp32 atomic split-k
+    # (not in the main chain)
+    split_rows = [
+        ("7 mla_linear_deterministic [W^DQ; W^DKV; W^KR] h (the first step's product alone)",
+         det_a, nb(w_a) + nb(h) + nb(y_a)),
+        ("2 mla_kv_append_strided (the first step's append as its own launch)", append,
+         B * (d_c + d_R) * 4 + append_bytes)]
     atomic_rows = [
         ("7 mla_linear [W^DQ; W^DKV; W^KR] h",
          mla.bind(mla.mla_linear, h, w_a, y_a), nb(w_a) + nb(h) + nb(y_a)),
@@ -215,7 +225,7 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     unfused_back = [
         mla.bind(mla.mla_decode, q_lat, q_pe, cache, bt, seq_lens, x["scale"], S, ws, o_lat),
         mla.bind(mla.mla_out_proj, o_lat, w["w_uv"], None, o_heads),
-        rows[5][1][0]]
+        rows[4][1][0]]
     # the same layer with one product per weight and dense intermediates
     sep = {k: torch.empty(B, n, **f32) for k, n in
            (("c_q", d_cq), ("q_c", H * d_h), ("q_r", H * d_R), ("c_kv", d_c), ("k_r", d_R))}
@@ -244,14 +254,16 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     main_chain = run_calls(chain)
     # the atomic split-k products accumulating into outputs cleared together by one fill at
     # the start of the layer (y_a and u share one buffer), so they launch no zero fills
-    acc_chain = ([mla.bind(mla.mla_linear_strided, h, w_a, y_a, accumulate=True)] + chain[1:5]
-                 + [mla.bind(mla.mla_linear_strided, o_heads.view(B, H * d_h), w["w_o"], u,
-                             accumulate=True)])
+    acc_chain = ([mla.bind(mla.mla_linear_strided, h, w_a, y_a, accumulate=True), append]
+                 + chain[1:4] + [mla.bind(mla.mla_linear_strided, o_heads.view(B, H * d_h),
+                                          w["w_o"], u, accumulate=True)])
     atomic_chain = run_calls(acc_chain, fill=True)
     # attention + combine, then W^UV: two launches in place of the fused one
-    unfused_chain = run_calls(chain[:3] + unfused_back[:2] + chain[5:])
+    unfused_chain = run_calls(chain[:2] + unfused_back[:2] + chain[4:])
     # the query side as two launches in place of mla_query_path
-    two_launch_chain = run_calls(chain[:2] + [c for _, c, _ in two_launch_query] + chain[3:])
+    two_launch_chain = run_calls(chain[:1] + [c for _, c, _ in two_launch_query] + chain[2:])
+    # the product and the append as two launches in place of the fused first step
+    split_append_chain = run_calls([det_a, append] + chain[1:])
 
     main_chain()
     torch.cuda.synchronize()
@@ -265,6 +277,9 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     two_launch_chain()
     torch.cuda.synchronize()
     two_vs_one = float((u - u_det).abs().max() / u_det.abs().max())
+    split_append_chain()
+    torch.cuda.synchronize()
+    split_append_identical = bool(torch.equal(u, u_det))
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < 0.3:
         for c in separate:
@@ -273,6 +288,7 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
         atomic_chain()
         unfused_chain()
         two_launch_chain()
+        split_append_chain()
         torch.cuda.synchronize()
 
     def timed(fn, n=20):
@@ -293,6 +309,12 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
         out[name] = {"us": round(us, 2), "bytes_algorithmic": int(byts), "GBps": round(gbps, 1),
                      "roofline_frac": round(gbps / HBM_PEAK_GBPS, 4)}
         total_bytes += byts
+    for name, call, byts in split_rows:
+        us = timed(call)
+        gbps = byts / us / 1e3
+        out[name + " (not in the chain)"] = {
+            "us": round(us, 2), "bytes_algorithmic": int(byts), "GBps": round(gbps, 1),
+            "roofline_frac": round(gbps / HBM_PEAK_GBPS, 4)}
     for name, call, byts in atomic_rows:
         us = timed(call)
         gbps = byts / us / 1e3
@@ -312,6 +334,7 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
     atomic_us = timed(atomic_chain)
     unfused_us = timed(unfused_chain)
     two_launch_us = timed(two_launch_chain)
+    split_append_us = timed(split_append_chain)
 
     # Offline folds, measured only, with the weights prepared once by the library outside the
     # timing.  W~ = W^UK^T W^UQ ([H d_c, d_c^Q], 201 MB of bf16) makes q~ = W~ c^Q one
@@ -357,14 +380,17 @@ def layer_rows(mla, W, torch, oracle_seqs: int):
            "chain_GBps": round(total_bytes / chain_us / 1e3, 1),
            "chain_roofline_frac": round(total_bytes / chain_us / 1e3 / HBM_PEAK_GBPS, 4),
            "sequences_per_s": round(B / (chain_us * 1e-6), 1),
-           "chain_schedule": "one stream; stacked projections with a fixed summation order; "
-                             "the query side in one launch; combine fused with W^UV",
+           "chain_schedule": "one stream; stacked projections with a fixed summation order, "
+                             "the cache append in the first one's summing launch; the query "
+                             "side in one launch; combine fused with W^UV",
            "chain_bit_identical_reruns": rerun_identical,
            "chain_atomic_projections_us": round(atomic_us, 2),
            "atomic_vs_deterministic_max_rel_diff_u": round(atomic_vs_det, 6),
            "chain_two_launch_query_us": round(two_launch_us, 2),
            "two_launch_query_vs_one_max_rel_diff_u": round(two_vs_one, 6),
            "chain_unfused_combine_us": round(unfused_us, 2),
+           "chain_separate_append_us": round(split_append_us, 2),
+           "separate_append_vs_fused_u_bit_identical": split_append_identical,
            "chain_separate_products_us": round(separate_us, 2)}
     if oracle_seqs > 0:
         import oracle

@@ -86,6 +86,9 @@ _SIGNATURES = {
     "mla_linear_deterministic_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "mla_linear_deterministic": (_I32, [_P, _I32, _I64, _P, _I32, _I32, _I32, _I32, _P, _I64,
                                         _I32, _P, _SZ, _P]),
+    "mla_linear_deterministic_append": (_I32, [_P, _I32, _I64, _P, _I32, _I32, _I32, _I32, _P,
+                                               _I64, _P, _SZ, _I32, _P, _P, _P, _F, _SP, _I32,
+                                               _P]),
     "mla_linear_strided": (_I32, [_P, _I32, _I64, _P, _I32, _I32, _I32, _I32, _P, _I64, _I32,
                                   _P]),
     "mla_linear_planned": (_I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _P, _I32, _I32, _I32,
@@ -799,6 +802,28 @@ def mla_linear_deterministic(x, w, y, workspace, accumulate=False, stream=None):
     _invoke("mla_linear_deterministic", x_ptr, _dtype_code(x), ldx, _dev(w, "w", None, 2),
             _dtype_code(w), M, N, K, y_ptr, ldy, int(bool(accumulate)),
             _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+
+
+def mla_linear_deterministic_append(x, w, y, workspace, append_col, seq_lens_before,
+                                    block_table, kv_cache, rope_base, d_latent=512, stream=None):
+    """mla_linear_deterministic whose summing launch also appends the new token of each
+    sequence: [y[b, c:c+d_c] | RoPE(y[b, c+d_c:c+d_c+d_R], pos)] to the bf16 cache at
+    pos = seq_lens_before[b] (c = append_col, d_c = d_latent, d_R = cache row - d_c)."""
+    torch = _torch()
+    M, K = x.shape
+    N = w.shape[0]
+    _expect(w.shape[1] == K and tuple(y.shape) == (M, N), "shapes must be x[M,K] w[N,K] y[M,N]")
+    _expect(kv_cache.dtype == torch.bfloat16 and kv_cache.dim() == 3, "kv_cache must be bf16 [pages, P, row]")
+    _expect(block_table.shape[0] == M and tuple(seq_lens_before.shape) == (M,), "batch mismatch")
+    shp = paged_shape(kv_cache, block_table, 1, int(d_latent))
+    x_ptr, ldx = _dev_rows(x, "x", None, 2, 1)
+    y_ptr, ldy = _dev_rows(y, "y", torch.float32, 2, 1)
+    _invoke("mla_linear_deterministic_append", x_ptr, _dtype_code(x), ldx, _dev(w, "w", None, 2),
+            _dtype_code(w), M, N, K, y_ptr, ldy, _dev(workspace, "workspace", torch.uint8),
+            workspace.numel(), int(append_col),
+            _dev(seq_lens_before, "seq_lens_before", torch.int32, 1),
+            _dev(block_table, "block_table", torch.int32, 2), _dev(kv_cache, "kv_cache", None, 3),
+            float(rope_base), ctypes.byref(shp), _cache_code(kv_cache), _stream(stream))
 
 
 def mla_linear_planned(x, w, y, kernel, tile, split, ring, stream=None):

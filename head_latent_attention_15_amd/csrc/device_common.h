@@ -39,14 +39,24 @@ template <typename T> __device__ __forceinline__ void st(T* p, float v) { Elem<T
 
 // Rotation of one RoPE pair (x0, x1) at position pos for pair index k of a d-wide vector:
 // angle pos * base^(-2k/d), evaluated in fp64 so that long positions keep full precision.
-__device__ __forceinline__ void rope_pair(float x0, float x1, int64_t pos, int k, int d,
-                                          float base, float* y0, float* y1) {
+// rope_angle and rope_rotate are its two halves, for callers that compute the angle ahead
+// of the values (same operations, same results).
+__device__ __forceinline__ void rope_angle(int64_t pos, int k, int d, float base, double* s,
+                                           double* c) {
   const double theta = pow(static_cast<double>(base), -2.0 * static_cast<double>(k) / d);
   const double ang = static_cast<double>(pos) * theta;
-  double s, c;
-  sincos(ang, &s, &c);
+  sincos(ang, s, c);
+}
+__device__ __forceinline__ void rope_rotate(float x0, float x1, double s, double c, float* y0,
+                                            float* y1) {
   *y0 = static_cast<float>(static_cast<double>(x0) * c - static_cast<double>(x1) * s);
   *y1 = static_cast<float>(static_cast<double>(x0) * s + static_cast<double>(x1) * c);
+}
+__device__ __forceinline__ void rope_pair(float x0, float x1, int64_t pos, int k, int d,
+                                          float base, float* y0, float* y1) {
+  double s, c;
+  rope_angle(pos, k, d, base, &s, &c);
+  rope_rotate(x0, x1, s, c, y0, y1);
 }
 
 // a * b rounded to fp32 on its own: never contracted into a following add (FMA), so a

@@ -360,9 +360,13 @@ __global__ __launch_bounds__(256) void zero_rows_stream(float* __restrict__ y, i
 // t = z * NB + n / CW summed slice by slice, run by run (runs q0 .. q1 of each slice cover
 // the tile's units t * cps .. (t + 1) * cps - 1).  One thread per 4 columns; the slots are
 // loaded eight at a time (independent loads in flight together) and added in that order.
+// With app.cache set (batch 1), the quads of row m inside [c^KV | k^R] also go to the new
+// token's cache row (AppendArgs): the same fp32 sums, rounded to bf16, k^R pairs rotated
+// first, exactly as the separate append kernel does with them.
 __global__ __launch_bounds__(256) void gemm_stream_reduce(const float* __restrict__ part,
                                                           float* __restrict__ y, StreamArgs a,
-                                                          int CW, int batch, int accumulate) {
+                                                          int CW, int batch, int accumulate,
+                                                          AppendArgs app) {
   const int cps = a.NCH / a.ksl;
   const int64_t quads = static_cast<int64_t>(batch) * a.M * (a.N / 4);
   for (int64_t id = blockIdx.x * 256ll + threadIdx.x; id < quads; id += static_cast<int64_t>(gridDim.x) * 256) {
@@ -376,6 +380,19 @@ __global__ __launch_bounds__(256) void gemm_stream_reduce(const float* __restric
                         static_cast<int64_t>(m) * CW + c;
     const int64_t slice_stride = static_cast<int64_t>(a.ntiles) * a.jmax * a.M * CW;
     float* yp = y + z * a.sy + static_cast<int64_t>(m) * a.ldy + n;
+    // a quad of k^R to append: its two rotations are computed first, while the slot loads
+    // below are in flight
+    const int ac = n - app.col;  // column inside [c^KV | k^R]
+    const bool app_row = app.cache != nullptr && ac >= 0 && ac < app.d_c + app.d_R;
+    const bool app_rope = app_row && ac >= app.d_c;  // quads never straddle c^KV and k^R
+    int pos = 0;
+    double rs[2] = {0.0, 0.0}, rc[2] = {1.0, 1.0};
+    if (app_row) pos = app.seq_lens_before[m];
+    if (app_rope) {
+      const int k = (ac - app.d_c) / 2;
+      rope_angle(pos, k, app.d_R, app.base, &rs[0], &rc[0]);
+      rope_angle(pos, k + 1, app.d_R, app.base, &rs[1], &rc[1]);
+    }
     float4 sum = accumulate ? *reinterpret_cast<const float4*>(yp) : make_float4(0.f, 0.f, 0.f, 0.f);
     for (int i0 = 0; i0 < slots; i0 += 8) {
       float4 v[8];
@@ -392,11 +409,24 @@ __global__ __launch_bounds__(256) void gemm_stream_reduce(const float* __restric
         }
     }
     *reinterpret_cast<float4*>(yp) = sum;
+    if (app_row) {
+      const int page = app.block_table[static_cast<int64_t>(m) * app.max_pages + pos / app.page_size];
+      bf16raw* row = static_cast<bf16raw*>(app.cache) +
+                     (static_cast<int64_t>(page) * app.page_size + pos % app.page_size) * (app.d_c + app.d_R);
+      float v[4] = {sum.x, sum.y, sum.z, sum.w};
+      if (app_rope) {
+        rope_rotate(sum.x, sum.y, rs[0], rc[0], &v[0], &v[1]);
+        rope_rotate(sum.z, sum.w, rs[1], rc[1], &v[2], &v[3]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st(row + ac + i, v[i]);
+    }
   }
 }
 
 template <typename XT, int TN, int R, bool DET>
-hipError_t launch_t(const GemmArgs& g, const StreamArgs& a, int grid, hipStream_t s) {
+hipError_t launch_t(const GemmArgs& g, const StreamArgs& a, int grid, hipStream_t s,
+                    const AppendArgs& app) {
   const int64_t rows = static_cast<int64_t>(g.batch) * g.M;
   const int gx = static_cast<int>(std::min<int64_t>((g.N + 1023) / 1024, 64));
   const int gy = static_cast<int>(std::min<int64_t>(rows, 4096));
@@ -410,21 +440,23 @@ hipError_t launch_t(const GemmArgs& g, const StreamArgs& a, int grid, hipStream_
     const int64_t quads = rows * (g.N / 4);
     const int rg = static_cast<int>(std::min<int64_t>((quads + 255) / 256, 4096));
     hipLaunchKernelGGL(gemm_stream_reduce, dim3(rg), dim3(256), 0, s, a.part,
-                       static_cast<float*>(g.y), a, 64 * TN, g.batch, g.accumulate ? 1 : 0);
+                       static_cast<float*>(g.y), a, 64 * TN, g.batch, g.accumulate ? 1 : 0, app);
   }
   return hipGetLastError();
 }
 
 template <typename XT, int TN>
-hipError_t launch_r(const GemmArgs& g, const StreamArgs& a, int grid, int R, hipStream_t s) {
+hipError_t launch_r(const GemmArgs& g, const StreamArgs& a, int grid, int R, hipStream_t s,
+                    const AppendArgs& app) {
   if (a.part)  // the deterministic form is built for the planned ring only
-    return R == 4 ? launch_t<XT, TN, 4, true>(g, a, grid, s) : hipErrorInvalidValue;
+    return R == 4 ? launch_t<XT, TN, 4, true>(g, a, grid, s, app) : hipErrorInvalidValue;
+  if (app.cache != nullptr) return hipErrorInvalidValue;  // the append rides on the summing launch
   switch (R) {
-    case 4: return launch_t<XT, TN, 4, false>(g, a, grid, s);
-    case 8: return launch_t<XT, TN, 8, false>(g, a, grid, s);
-    case 12: if constexpr (TN <= 2) return launch_t<XT, TN, 12, false>(g, a, grid, s); else break;
-    case 16: if constexpr (TN <= 2) return launch_t<XT, TN, 16, false>(g, a, grid, s); else break;
-    case 20: if constexpr (TN <= 2) return launch_t<XT, TN, 20, false>(g, a, grid, s); else break;
+    case 4: return launch_t<XT, TN, 4, false>(g, a, grid, s, app);
+    case 8: return launch_t<XT, TN, 8, false>(g, a, grid, s, app);
+    case 12: if constexpr (TN <= 2) return launch_t<XT, TN, 12, false>(g, a, grid, s, app); else break;
+    case 16: if constexpr (TN <= 2) return launch_t<XT, TN, 16, false>(g, a, grid, s, app); else break;
+    case 20: if constexpr (TN <= 2) return launch_t<XT, TN, 20, false>(g, a, grid, s, app); else break;
     default: break;
   }
   return hipErrorInvalidValue;
@@ -508,18 +540,18 @@ size_t part_bytes(const GemmArgs& g, const StreamArgs& a, int tn) {
 }
 
 hipError_t launch_args(const GemmArgs& g, const StreamArgs& a, int tn, int grid, int ring,
-                       hipStream_t s) {
+                       hipStream_t s, const AppendArgs& app = AppendArgs()) {
   if (g.x_bf16) {
     switch (tn) {
-      case 4: return launch_r<bf16raw, 4>(g, a, grid, ring, s);
-      case 2: return launch_r<bf16raw, 2>(g, a, grid, ring, s);
-      default: return launch_r<bf16raw, 1>(g, a, grid, ring, s);
+      case 4: return launch_r<bf16raw, 4>(g, a, grid, ring, s, app);
+      case 2: return launch_r<bf16raw, 2>(g, a, grid, ring, s, app);
+      default: return launch_r<bf16raw, 1>(g, a, grid, ring, s, app);
     }
   }
   switch (tn) {
-    case 4: return launch_r<float, 4>(g, a, grid, ring, s);
-    case 2: return launch_r<float, 2>(g, a, grid, ring, s);
-    default: return launch_r<float, 1>(g, a, grid, ring, s);
+    case 4: return launch_r<float, 4>(g, a, grid, ring, s, app);
+    case 2: return launch_r<float, 2>(g, a, grid, ring, s, app);
+    default: return launch_r<float, 1>(g, a, grid, ring, s, app);
   }
 }
 }  // namespace
@@ -531,7 +563,8 @@ size_t gemm_stream_det_workspace_bytes(const GemmArgs& g) {
   return part_bytes(g, stream_args(g, tn, grid), tn);
 }
 
-hipError_t launch_gemm_stream_det(const GemmArgs& g, void* part, size_t bytes, hipStream_t s) {
+hipError_t launch_gemm_stream_det(const GemmArgs& g, void* part, size_t bytes, hipStream_t s,
+                                  const AppendArgs& app) {
   int tn = 1, grid = 1, ring = 4;
   gemm_stream_plan(g, &tn, &grid, &ring);
   if (!gemm_stream_plan_ok(g, tn, grid, ring)) return hipErrorInvalidValue;
@@ -539,8 +572,11 @@ hipError_t launch_gemm_stream_det(const GemmArgs& g, void* part, size_t bytes, h
   if (!part || bytes < part_bytes(g, a, tn) || (reinterpret_cast<uintptr_t>(part) & 15) ||
       g.N % 4 || (g.ldy % 4) || (g.sy % 4) || (reinterpret_cast<uintptr_t>(g.y) & 15))
     return hipErrorInvalidValue;
+  if (app.cache != nullptr &&
+      (g.batch != 1 || app.col % 4 || app.d_c % 4 || app.d_R % 4 || app.col + app.d_c + app.d_R > g.N))
+    return hipErrorInvalidValue;
   a.part = static_cast<float*>(part);
-  return launch_args(g, a, tn, grid, ring, s);
+  return launch_args(g, a, tn, grid, ring, s, app);
 }
 
 hipError_t launch_gemm_stream_with(const GemmArgs& g, int tn, int grid, int ring, hipStream_t s) {

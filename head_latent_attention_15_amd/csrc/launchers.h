@@ -132,7 +132,19 @@ hipError_t launch_gemm_stream(const GemmArgs& g, hipStream_t s);
 // (0 where the kernel does not apply), then a fixed-order sum into y.  Needs N, ldy and sy
 // multiples of 4 and 16-byte aligned y and workspace.
 size_t gemm_stream_det_workspace_bytes(const GemmArgs& g);
-hipError_t launch_gemm_stream_det(const GemmArgs& g, void* part, size_t bytes, hipStream_t s);
+// The new token's cache row written by the second (summing) launch: row b of y holds c^KV
+// at columns col .. col + d_c - 1 and k^R (before RoPE) right after it; the row
+// [c^KV | RoPE(k^R, pos)] goes to the bf16 cache at position pos = seq_lens_before[b], as
+// launch_kv_append writes it for one new token.  cache == nullptr: no append.
+struct AppendArgs {
+  void* cache = nullptr;
+  const int32_t* seq_lens_before = nullptr;
+  const int32_t* block_table = nullptr;
+  int col = 0, d_c = 0, d_R = 0, page_size = 0, max_pages = 0;
+  float base = 0.f;
+};
+hipError_t launch_gemm_stream_det(const GemmArgs& g, void* part, size_t bytes, hipStream_t s,
+                                  const AppendArgs& app = AppendArgs());
 // Activation-stationary form for M <= 64, N a multiple of 128 and K of 256: a workgroup
 // stages one k slice (32 s values) of x in LDS once and streams the weights of a run of
 // 128 tn-column tiles in it.  The plan picks tn (1, 2), s (8, 12, 16, 20) and the grid.

@@ -845,6 +845,54 @@ mla_status_t mla_linear_deterministic(const void* x, mla_dtype_t x_dtype, int64_
                   "deterministic linear GEMM");
 }
 
+mla_status_t mla_linear_deterministic_append(
+    const void* x, mla_dtype_t x_dtype, int64_t ldx, const void* w, mla_dtype_t w_dtype,
+    int32_t M, int32_t N, int32_t K, float* y, int64_t ldy, void* workspace,
+    size_t workspace_bytes, int32_t append_col, const int32_t* seq_lens_before,
+    const int32_t* block_table, void* kv_cache, float rope_base, const mla_paged_shape_t* shape,
+    mla_dtype_t cache_dtype, void* stream) {
+  const char* fn = "mla_linear_deterministic_append";
+  if (!x || !w || !y || !workspace || !seq_lens_before || !block_table || !kv_cache)
+    return fail(MLA_ERR_NULL, "%s: a required pointer is NULL", fn);
+  mla_status_t st = check_paged_shape(shape);
+  if (st != MLA_OK) return st;
+  if (M < 1 || N < 1 || K < 1) return fail(MLA_ERR_SHAPE, "%s: sizes must be >= 1", fn);
+  if (ldx < K || ldy < N)
+    return fail(MLA_ERR_SHAPE, "%s: row strides ldx %lld < K or ldy %lld < N", fn,
+                static_cast<long long>(ldx), static_cast<long long>(ldy));
+  if (shape->batch != M)
+    return fail(MLA_ERR_SHAPE, "%s: M %d rows but a batch of %d sequences", fn, M, shape->batch);
+  if (append_col < 0 || static_cast<int64_t>(append_col) + shape->d_latent + shape->d_rope > N)
+    return fail(MLA_ERR_SHAPE, "%s: columns %d .. %d + d_latent + d_rope outside the %d columns",
+                fn, append_col, append_col, N);
+  if (!std::isfinite(rope_base)) return fail(MLA_ERR_SHAPE, "%s: rope_base", fn);
+  if (!is_dtype(x_dtype) || w_dtype != MLA_BF16 || cache_dtype != MLA_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: bf16 weights and a bf16 cache required", fn);
+  if (append_col % 4 || shape->d_latent % 4 || shape->d_rope % 4)
+    return fail(MLA_ERR_UNSUPPORTED, "%s: append_col, d_latent and d_rope must be multiples of 4", fn);
+  const mla::GemmArgs g = det_args(x, x_dtype, ldx, w, M, N, K, y, ldy, 0);
+  const size_t need = mla::gemm_stream_det_workspace_bytes(g);
+  if (need == 0 || N % 4 || ldy % 4 || (reinterpret_cast<uintptr_t>(y) & 15) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 15))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "%s: needs M <= 64, N %% 64 == 0, K %% 128 == 0, ldx %% 8 == 0, ldy %% 4 == 0 "
+                "and 16-byte aligned x, w, y and workspace (M %d, N %d, K %d)", fn, M, N, K);
+  if (workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, workspace_bytes, need);
+  mla::AppendArgs app;
+  app.cache = kv_cache;
+  app.seq_lens_before = seq_lens_before;
+  app.block_table = block_table;
+  app.col = append_col;
+  app.d_c = shape->d_latent;
+  app.d_R = shape->d_rope;
+  app.page_size = shape->page_size;
+  app.max_pages = shape->max_pages_per_seq;
+  app.base = rope_base;
+  return launched(mla::launch_gemm_stream_det(g, workspace, workspace_bytes, as_stream(stream), app),
+                  "deterministic linear GEMM with cache append");
+}
+
 mla_status_t mla_linear_planned(const void* x, mla_dtype_t x_dtype, const void* w,
                                 mla_dtype_t w_dtype, int32_t M, int32_t N, int32_t K, float* y,
                                 int32_t kernel, int32_t tile, int32_t split, int32_t ring,

@@ -512,6 +512,31 @@ mla_status_t mla_linear_deterministic(const void* x, mla_dtype_t x_dtype, int64_
                                       int32_t K, float* y, int64_t ldy, int32_t accumulate,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* mla_linear_deterministic (accumulate 0) that also appends the new token of every sequence
+ * to the paged cache in its second (summing) launch: the RoPE and the append fused into the
+ * down-projection ([W^DQ; W^DKV; W^KR] h gives c^KV and k^R of the new token: qiita.com/joule/
+ * items/57d9b3f4fc27959eaa0d, "Query の圧縮" and "RoPE の扱い"; "論文解説: DeepSeek-V2 …",
+ * "Decoupled RoPE": the cache keeps c^KV and the rotated k^R, 576 elements per token).
+ * y is written exactly as mla_linear_deterministic writes it, and the cache rows exactly as
+ * mla_kv_append_strided(c_kv = y + append_col, k_r = y + append_col + d_latent, n_new = 1)
+ * would write them from that y: row b of y is sequence b, its row
+ * [y[b][append_col .. +d_latent) | RoPE(y[b][append_col+d_latent .. +d_rope), pos)] (rounded
+ * to bf16) goes to position pos = seq_lens_before[b] through the block table; no other cache
+ * byte is written.  One launch fewer than the two calls, with the same bits.
+ *   x, w, y, workspace: as mla_linear_deterministic, with M == shape->batch
+ *   seq_lens_before [B], block_table [B][max_pages_per_seq]: int32, device
+ *   kv_cache: bf16 rows of d_latent + d_rope (cache_dtype must be MLA_BF16)
+ * Errors: NULL, SHAPE (as mla_linear_deterministic and check of the paged shape; M !=
+ * batch; append_col + d_latent + d_rope > N), UNSUPPORTED (as mla_linear_deterministic; a
+ * cache dtype other than BF16; append_col, d_latent or d_rope not a multiple of 4),
+ * WORKSPACE. */
+mla_status_t mla_linear_deterministic_append(
+    const void* x, mla_dtype_t x_dtype, int64_t ldx, const void* w, mla_dtype_t w_dtype,
+    int32_t M, int32_t N, int32_t K, float* y, int64_t ldy, void* workspace,
+    size_t workspace_bytes, int32_t append_col, const int32_t* seq_lens_before,
+    const int32_t* block_table, void* kv_cache, float rope_base, const mla_paged_shape_t* shape,
+    mla_dtype_t cache_dtype, void* stream);
+
 /* Device-side check of the paging indices: counts sequences whose seq_len is negative or
  * exceeds max_pages_per_seq*page_size, and referenced block-table entries outside
  * [0, num_pages).  Writes the count to *dev_count (device int32; 0 = valid).

@@ -88,3 +88,51 @@ def test_deterministic_linear_strided_views(mla):
     ref = host64(xb)[:, :K] @ host64(w).T
     assert errors(host64(yb)[:, 128:128 + N], ref)[0] <= 1e-4
     assert torch.all(yb[:, :128] == 7.0) and torch.all(yb[:, 128 + N:] == 7.0)
+
+
+@pytest.mark.parametrize("B,seq_lens_before", [
+    (64, [2048] * 64),                                  # the decode layer: B = 64, 2048 prior tokens
+    (5, [0, 63, 64, 700, 1023]),                        # ragged, page boundaries, permuted pages
+])
+def test_deterministic_linear_append_matches_two_calls(mla, B, seq_lens_before):
+    """The fused down-projection + append writes y and the cache exactly as
+    mla_linear_deterministic followed by mla_kv_append_strided (n_new = 1) on that y: y bit
+    for bit, every cache byte bit for bit (the new rows, and nothing else).  The new rows
+    also match the oracle's RoPE of the same fp32 y within bf16 rounding."""
+    import oracle
+    d, d_cq, d_c, d_R = 5120, 1536, 512, 64
+    N = d_cq + d_c + d_R
+    g = torch.Generator().manual_seed(90 + B)
+    h = torch.randn(B, d, generator=g)
+    w = (torch.randn(N, d, generator=g) / math.sqrt(d)).to(torch.bfloat16)
+    lens = [s + 1 for s in seq_lens_before]             # room for the appended token
+    inp = W.paged_attention(91 + B, B=B, H=1, seq_lens=lens, extra_pages=2)
+    cache0 = inp["cache"]
+    bt, before = dev(inp["block_table"]), dev(torch.tensor(seq_lens_before, dtype=torch.int32))
+    ws = torch.empty(mla.mla_linear_deterministic_workspace_bytes(B, N, d), dtype=torch.uint8,
+                     device="cuda")
+    say(f"deterministic linear + append B={B}")
+    hd, wd = dev(h), dev(w)
+    y_ref = torch.full((B, N), float("nan"), device="cuda")
+    c_ref = dev(cache0.clone())
+    mla.mla_linear_deterministic(hd, wd, y_ref, ws)
+    mla.mla_kv_append_strided(y_ref[:, d_cq:d_cq + d_c].unsqueeze(1),
+                              y_ref[:, d_cq + d_c:].unsqueeze(1), before, bt, c_ref, 10000.0)
+    y = torch.full((B, N), float("nan"), device="cuda")
+    c = dev(cache0.clone())
+    mla.mla_linear_deterministic_append(hd, wd, y, ws, d_cq, before, bt, c, 10000.0)
+    torch.cuda.synchronize()
+    assert torch.equal(y.cpu().view(torch.int32), y_ref.cpu().view(torch.int32))
+    got, want = c.cpu(), c_ref.cpu()
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    yc = y.cpu().double().numpy()
+    P = cache0.shape[1]
+    changed = (got.view(torch.int16) != cache0.view(torch.int16)).any(dim=2)
+    for b, pos in enumerate(seq_lens_before):
+        pg, slot = int(inp["block_table"][b, pos // P]), pos % P
+        changed[pg, slot] = False
+        row = got[pg, slot].double().numpy()
+        ref = np.concatenate([yc[b, d_cq:d_cq + d_c],
+                              oracle.rope(yc[b, d_cq + d_c:], pos, 10000.0)])
+        assert np.all(np.abs(row - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30), b
+    assert not bool(changed.any()), "bytes outside the appended rows changed"
