@@ -465,14 +465,16 @@ def test_stream_read_runs(mla):
 
 
 # ------------------------------------------------------------------ full decode layer
-def layer_on_gpu(mla, x, S, stacked=False, fused=False, qpath=False, det=False):
+def layer_on_gpu(mla, x, S, stacked=False, fused=False, qpath=False, det=False, append_fused=False):
     """The whole decode layer through the C ABI: projections, cache append, absorption,
     attention + combine, W^UV and W^O.  stacked: the projections that share an input run as
     one product over their stacked weights ([W^DQ; W^DKV; W^KR] h, then [W^UQ; W^QR] c^Q
     with c^Q read in place), and the append and absorption read their inputs in place from
     those outputs through the row-strided entry points.  qpath (with stacked): the query
     side (W^UQ, W^QR, RoPE, absorption) is one mla_query_path launch instead.  det (with
-    stacked and fused): the two remaining projections run with a fixed summation order."""
+    stacked and fused): the two remaining projections run with a fixed summation order.
+    append_fused (with det): the cache append runs in the down-projection's summing launch
+    (mla_linear_deterministic_append)."""
     s = x["shape"]
     B, H, d_h, d_c, d_R, d, d_cq = s.B, s.H, s.d_h, s.d_c, s.d_R, x["d"], x["d_cq"]
     w = {k: dev(v) for k, v in x["weights"].items()}
@@ -492,12 +494,17 @@ def layer_on_gpu(mla, x, S, stacked=False, fused=False, qpath=False, det=False):
             ws_lin = torch.empty(max(mla.mla_linear_deterministic_workspace_bytes(B, w_a.shape[0], d),
                                      mla.mla_linear_deterministic_workspace_bytes(B, d, H * d_h)),
                                  dtype=torch.uint8, device="cuda")
-            mla.mla_linear_deterministic(h, w_a, y_a, ws_lin)
+            if append_fused:
+                mla.mla_linear_deterministic_append(h, w_a, y_a, ws_lin, d_cq, before, bt, cache,
+                                                    x["rope_base"])
+            else:
+                mla.mla_linear_deterministic(h, w_a, y_a, ws_lin)
         else:
             mla.mla_linear(h, w_a, y_a)
-        mla.mla_kv_append_strided(y_a[:, d_cq:d_cq + d_c].unsqueeze(1),
-                                  y_a[:, d_cq + d_c:].unsqueeze(1), before, bt, cache,
-                                  x["rope_base"])
+        if not append_fused:
+            mla.mla_kv_append_strided(y_a[:, d_cq:d_cq + d_c].unsqueeze(1),
+                                      y_a[:, d_cq + d_c:].unsqueeze(1), before, bt, cache,
+                                      x["rope_base"])
         if qpath:  # the query side in one launch, c^Q read in place
             w_pack = mla.mla_pack_query_weights(w["w_uq"], w["w_qr"], w["w_uk"], H)
             mla.mla_query_path(y_a[:, :d_cq], w_pack, seq_lens, x["rope_base"], q_lat, q_pe)
@@ -543,17 +550,22 @@ def layer_on_gpu(mla, x, S, stacked=False, fused=False, qpath=False, det=False):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("stacked,fused,qpath,det",
-                         [(False, False, False, False), (True, False, False, False),
-                          (True, True, False, False), (True, True, True, True)],
-                         ids=["separate", "stacked", "stacked-fused", "stacked-fused-qpath-det"])
-def test_full_layer_b64_t2k_sampled(mla, stacked, fused, qpath, det):
+@pytest.mark.parametrize("stacked,fused,qpath,det,append_fused",
+                         [(False, False, False, False, False), (True, False, False, False, False),
+                          (True, True, False, False, False), (True, True, True, True, False),
+                          (True, True, True, True, True)],
+                         ids=["separate", "stacked", "stacked-fused", "stacked-fused-qpath-det",
+                              "bench-chain"])
+def test_full_layer_b64_t2k_sampled(mla, stacked, fused, qpath, det, append_fused):
     """Full layer at d=5120, H=128, B=64, 2048 prior tokens + 1 appended: all 64 rows of
-    u on the GPU; sequences 0 and 37 through the oracle's expanded path."""
+    u on the GPU; sequences 0 and 37 through the oracle's expanded path, and every one of
+    the 64 sequences for the chain the bench times (bench-chain)."""
     x = W.layer_b64_t2k()
-    say(f"layer_b64_t2k stacked={stacked} fused={fused} qpath={qpath} det={det}")
-    u, cache = layer_on_gpu(mla, x, S=4, stacked=stacked, fused=fused, qpath=qpath, det=det)
-    pick = [0, 37]
+    say(f"layer_b64_t2k stacked={stacked} fused={fused} qpath={qpath} det={det} "
+        f"append_fused={append_fused}")
+    u, cache = layer_on_gpu(mla, x, S=4, stacked=stacked, fused=fused, qpath=qpath, det=det,
+                            append_fused=append_fused)
+    pick = list(range(64)) if append_fused else [0, 37]
     ref = oracle.decode_layer(W.to_f64(x["h"]), {k: W.to_f64(v) for k, v in x["weights"].items()},
                               W.to_f64(x["cache"]), x["block_table"].numpy(),
                               x["seq_lens_before"].numpy(), x["shape"].d_h, x["shape"].d_R,
@@ -588,15 +600,17 @@ def test_small_layer_chain(mla, stacked, fused, qpath, det):
 
 
 def test_layer_chain_reruns_bit_identical(mla):
-    """The decode layer with the fixed-order projections, the one-launch query side and the
-    fused combine: two runs from the same cache give u bit for bit (every sum in the chain
+    """The decode layer with the fixed-order projections (the append in the first one's
+    summing launch), the one-launch query side and the fused combine: two runs from the same cache give u bit for bit (every sum in the chain
     has one order), at the DeepSeek-V2 sizes."""
     x = W.layer_b64_t2k()
     say("layer_b64_t2k rerun determinism")
     cache0 = x["cache"].clone()
-    u1, _ = layer_on_gpu(mla, x, S=4, stacked=True, fused=True, qpath=True, det=True)
+    u1, _ = layer_on_gpu(mla, x, S=4, stacked=True, fused=True, qpath=True, det=True,
+                         append_fused=True)
     x["cache"] = cache0
-    u2, _ = layer_on_gpu(mla, x, S=4, stacked=True, fused=True, qpath=True, det=True)
+    u2, _ = layer_on_gpu(mla, x, S=4, stacked=True, fused=True, qpath=True, det=True,
+                         append_fused=True)
     assert torch.equal(u1, u2)
 
 
