@@ -28,9 +28,11 @@
  *     there: out-of-range values are undefined behaviour.  mla_validate_indices checks
  *     them on the device beforehand.
  *   - Results are deterministic for fixed inputs and arguments, except the projections
- *     (mla_linear*, mla_out_proj) with bf16 weights: their long reductions are split over
- *     workgroups that add into the fp32 output atomically, so the last bits of y / u /
- *     o_heads can differ between runs.
+ *     mla_linear, mla_linear_strided, mla_linear_planned and mla_out_proj with bf16
+ *     weights: their long reductions are split over workgroups that add into the fp32
+ *     output atomically, so the last bits of y / u / o_heads can differ between runs.
+ *     mla_linear_deterministic and mla_linear_deterministic_append sum the same split in
+ *     one fixed order and are bit-identical from run to run.
  *
  * Paged latent cache: kv_cache[num_pages][page_size][d_latent + d_rope]; a row is
  * [c^KV (d_latent) | RoPE(k^R) (d_rope)].  Token j (0-based) of sequence b lives at
