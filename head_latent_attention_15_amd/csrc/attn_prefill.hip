@@ -13,16 +13,18 @@
 //
 // One workgroup of 8 wavefronts per (sequence, head, block of 256 queries), wavefront w
 // owning queries 32 w .. 32 w + 31 of the block as two 16-query tiles.  Keys go through LDS
-// in 64-key blocks, one 640-byte row per key [k^C_i (128) | k^R (64) | v^C_i (128)] with the
-// 16-byte-chunk XOR swizzle of the decode tiles (a row stride of 128 mod 256 bytes, as
-// there), so the row-strided K reads and the transposing V reads are conflict-free.  Per
-// key block a wave computes S^T = K Q^T (tokens as the MFMA M dimension, 4 key tiles x 6
-// k-steps x 2 query tiles = 48 MFMAs, each K fragment feeding both query tiles, Q resident
-// in VGPRs; the key permutation inside each 32-key half makes the C layout of S^T the B
-// layout of P^T), an online softmax per query (running maximum, accumulators rescaled when
-// it moves), and O^T += V^T P^T (32 MFMAs, each V^T fragment feeding both query tiles).
-// Blocks are staged with plain global loads double-buffered through registers.  Workgroups
-// of late query blocks (the most keys) are numbered first.
+// in 64-key blocks of three regions, one per source tensor: k^C_i rows (256 bytes), k^R rows
+// (128 bytes) and v^C_i rows (256 bytes), each row's 16-byte chunks XOR-permuted by its row
+// index so that the row-strided K reads and the transposing V reads are conflict-free.  The
+// regions are filled by LDS-DMA copies (1 KB of consecutive LDS per wave-wide copy, the
+// permutation carried by the per-lane source addresses) into three buffers, two blocks
+// ahead of their use, so one barrier per block both publishes block kb+1 and retires block
+// kb.  Per key block a wave computes S^T = K Q^T (tokens as the MFMA M dimension, 4 key
+// tiles x 6 k-steps x 2 query tiles = 48 MFMAs, each K fragment feeding both query tiles,
+// Q resident in VGPRs; the key permutation inside each 32-key half makes the C layout of
+// S^T the B layout of P^T), an online softmax per query (running maximum, accumulators
+// rescaled when it moves), and O^T += V^T P^T (32 MFMAs, each V^T fragment feeding both
+// query tiles).  Workgroups of late query blocks (the most keys) are numbered first.
 #include "attn_common.h"
 #include "launchers.h"
 
@@ -32,16 +34,19 @@ namespace {
 using namespace attn;
 
 constexpr int PF_DH = 128, PF_DR = 64, PF_DQK = PF_DH + PF_DR;  // 192
-constexpr int PF_ROW = (PF_DQK + PF_DH) * 2;                     // 640 bytes: k^C | k^R | v^C
-constexpr int PF_ROW_CHUNKS = PF_ROW / 16;                       // 40
 constexpr int PF_KB = 64;                                        // keys per block
-constexpr int PF_TILE = PF_KB * PF_ROW;                          // 40960 bytes
-constexpr int PF_CHUNKS = PF_KB * PF_ROW_CHUNKS;                 // 2560
+constexpr int PF_KC = 0;                                         // k^C region: 64 rows x 256 B
+constexpr int PF_KR = PF_KC + PF_KB * PF_DH * 2;                 // k^R region: 64 rows x 128 B
+constexpr int PF_V = PF_KR + PF_KB * PF_DR * 2;                  // v^C region: 64 rows x 256 B
+constexpr int PF_TILE = PF_V + PF_KB * PF_DH * 2;                // 40960 bytes per block
+constexpr int PF_NBUF = 3;
 constexpr int PF_NW = 8, PF_NT = PF_NW * 64;
 constexpr int PF_QT = 2;                                         // 16-query tiles per wave
 constexpr int PF_QB = 16 * PF_QT * PF_NW;                        // 256 queries per workgroup
-constexpr int PF_LOADS = (PF_CHUNKS + PF_NT - 1) / PF_NT;        // 5 chunks per thread
+constexpr int PF_COPIES = PF_TILE / 1024 / PF_NW;                // 5 wave-wide copies per block
+static_assert(PF_COPIES * PF_NW * 1024 == PF_TILE, "copies split evenly over the waves");
 constexpr int PF_KSTEPS = PF_DQK / 32;                           // 6
+constexpr float PF_SLACK = 8.0f;  // log2 units a block maximum may exceed the reference by
 constexpr int PF_MT = PF_KB / 16;                                // 4 key M tiles
 constexpr int PF_CT = PF_DH / 16;                                // 8 value column tiles
 
@@ -50,8 +55,9 @@ __global__ __launch_bounds__(PF_NT) void attn_prefill_kernel(
     const bf16raw* __restrict__ k_c, const bf16raw* __restrict__ k_pe,
     const bf16raw* __restrict__ v_c, int T, int H, float scale_log2, float* __restrict__ out,
     float* __restrict__ lse_out) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * PF_TILE];
+  __shared__ __attribute__((aligned(16))) char smem[PF_NBUF * PF_TILE];
   lds_char_t* const lsm = (lds_char_t*)smem;
+  const uint32_t smem_lds = static_cast<uint32_t>(reinterpret_cast<size_t>(lsm));
   const int nqb = (T + PF_QB - 1) / PF_QB;
   // heads in x: the first workgroups are the last query blocks (the most keys) of every
   // head, so the longest work starts first
@@ -80,51 +86,75 @@ __global__ __launch_bounds__(PF_NT) void attn_prefill_kernel(
       qf[qt][kk] = *reinterpret_cast<const bf16x8_t*>(kk < 4 ? qc + 32 * kk : qp + 32 * (kk - 4));
   }
 
-  // ---- staging: thread tid moves LDS chunks e = tid + 512 i (i < 5) of a block: row
-  //      t = e / 40 (key kb*64 + t, keys past T repeat T - 1), stored position p = e % 40
-  //      holding logical chunk c = p ^ swz(t): c < 16 k^C, c < 24 k^R, else v^C
-  auto chunk_src = [&](int kb, int e) -> const bf16raw* {
-    const int t = e / PF_ROW_CHUNKS, p = e - t * PF_ROW_CHUNKS;
-    const int c = p ^ swz(t & 31);
-    const int64_t key = tok0 + min(kb * PF_KB + t, T - 1);
-    if (c < 16) return k_c + (key * H + h) * PF_DH + 8 * c;
-    if (c < 24) return k_pe + key * PF_DR + 8 * (c - 16);
-    return v_c + (key * H + h) * PF_DH + 8 * (c - 24);
-  };
-  i32x4_t stage[PF_LOADS];
-  auto load_block = [&](int kb) {
+  // ---- staging.  Row t of a block is key kb*64 + t (keys past T repeat T - 1); stored
+  //      position p of a row holds logical chunk p ^ f(t):
+  //        k^C (16 chunks): fk(t) = (t & 3) | ((t >> 3) & 3) << 2
+  //        k^R (8 chunks):  fr(t) = ((t >> 1) & 1) | ((t >> 3) & 3) << 1
+  //        v^C (16 chunks): fv(t) = 2 (t & 3)
+  //      (the 16 rows a K fragment read touches get 16 different positions; the 4 rows of a
+  //      transposing V read, 4 different 32-byte pieces).  Copy r of wave w: r = 0, 1: k^C
+  //      rows 4 q .. 4 q + 3 (q = w + 8 r); r = 2: k^R rows 8 w .. 8 w + 7; r = 3, 4: v^C rows
+  //      4 q .. 4 q + 3 (q = w + 8 (r - 3)); lane l fills 16 bytes of the 1 KB it covers.
+  auto fk = [](int t) { return (t & 3) | (((t >> 3) & 3) << 2); };
+  auto fr = [](int t) { return ((t >> 1) & 1) | (((t >> 3) & 3) << 1); };
+  auto fv = [](int t) { return 2 * (t & 3); };
+  auto issue_block = [&](int kb, int buf) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // recomputed at every block (no live ranges across the loop)
+    const int last = T - 1 - kb * PF_KB;  // rows past it repeat it
+    const int64_t key0 = tok0 + static_cast<int64_t>(kb) * PF_KB;
+    const char* kc_base = reinterpret_cast<const char*>(k_c + (key0 * H + h) * PF_DH);
+    const char* kr_base = reinterpret_cast<const char*>(k_pe + key0 * PF_DR);
+    const char* v_base = reinterpret_cast<const char*>(v_c + (key0 * H + h) * PF_DH);
+    const uint32_t hrow = static_cast<uint32_t>(H) * PF_DH * 2;  // bytes between keys (k^C, v^C)
+    const uint32_t lds = smem_lds + buf * PF_TILE;
 #pragma unroll
-    for (int i = 0; i < PF_LOADS; ++i) {
-      const int e = tid + PF_NT * i;
-      if (e < PF_CHUNKS) stage[i] = *reinterpret_cast<const i32x4_t*>(chunk_src(kb, e));
+    for (int r = 0; r < 2; ++r) {  // k^C
+      const int q = w + PF_NW * r, t = 4 * q + (ln >> 4), p = ln & 15;
+      dma16(kc_base, static_cast<uint32_t>(min(t, last)) * hrow + 16u * (p ^ fk(t)),
+            lds + PF_KC + q * 1024);
     }
-  };
-  auto store_block = [&](int buf) {
+    {  // k^R
+      const int t = 8 * w + (ln >> 3), p = ln & 7;
+      dma16(kr_base, static_cast<uint32_t>(min(t, last)) * (PF_DR * 2) + 16u * (p ^ fr(t)),
+            lds + PF_KR + w * 1024);
+    }
 #pragma unroll
-    for (int i = 0; i < PF_LOADS; ++i) {
-      const int e = tid + PF_NT * i;
-      if (e < PF_CHUNKS) *(__attribute__((address_space(3))) i32x4_t*)(lsm + buf * PF_TILE + 16 * e) = stage[i];
+    for (int r = 0; r < 2; ++r) {  // v^C
+      const int q = w + PF_NW * r, t = 4 * q + (ln >> 4), p = ln & 15;
+      dma16(v_base, static_cast<uint32_t>(min(t, last)) * hrow + 16u * (p ^ fv(t)),
+            lds + PF_V + q * 1024);
     }
   };
 
-  // K fragments: row r of key M tile mt is key 32 (mt >> 1) + 8 (r >> 2) + 4 (mt & 1) + (r & 3),
-  // logical chunk 4 par + g (k-step kk adds 128 (kk >> 1)); the 32-key halves repeat the
-  // decode tile's rows (the swizzle period is 32 rows), so half (mt >> 1) adds 32 rows.
-  // V^T fragments: key half ks, rows 32 ks + 8 gg + 4 r + (rr >> 2), chunks 24 + 2 ct (+1).
-  int kb_off[2][2];
+  // K fragments: row r of key M tile mt is key 32 (mt >> 1) + 8 (r >> 2) + 4 (mt & 1) + (r & 3);
+  // k-step kk reads logical chunk 4 kk + g of k^C (kk < 4) or 4 (kk - 4) + g of k^R; the
+  // 32-key halves add 32 rows (the permutations depend on t mod 32 only).
+  // V^T fragments: key half ks, rows 32 ks + 8 g + 4 r + (r16 >> 2), logical chunks
+  // 8 (ct >> 2) + 2 (ct & 3) + e (e = (r16 & 3) >> 1), byte 8 (r16 & 1) of the chunk; the
+  // permutation fv flips chunk bits 1-2 only, so the 8 (ct >> 2) stays an added offset.
+  int kc_row[2], kc_x[2], kr_row[2], kr_x[2];
 #pragma unroll
   for (int m1 = 0; m1 < 2; ++m1) {
     const int t = 8 * (r16 >> 2) + 4 * m1 + (r16 & 3);
-#pragma unroll
-    for (int par = 0; par < 2; ++par) kb_off[m1][par] = t * PF_ROW + 16 * ((4 * par + g) ^ swz(t));
+    kc_row[m1] = PF_KC + t * PF_DH * 2;
+    kc_x[m1] = fk(t);
+    kr_row[m1] = PF_KR + t * PF_DR * 2;
+    kr_x[m1] = fr(t);
   }
+  auto k_off = [&](int mt, int kk) {
+    const int m1 = mt & 1;
+    return kk < 4 ? kc_row[m1] + (mt >> 1) * 32 * PF_DH * 2 + 16 * ((4 * kk + g) ^ kc_x[m1])
+                  : kr_row[m1] + (mt >> 1) * 32 * PF_DR * 2 + 16 * ((4 * (kk - 4) + g) ^ kr_x[m1]);
+  };
   int vb[2][4];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int t = 8 * g + 4 * r + (r16 >> 2);
     const int e = (r16 & 3) >> 1;
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) vb[r][c4] = t * PF_ROW + 16 * ((2 * c4 + e) ^ swz(t)) + 8 * (r16 & 1);
+    for (int c4 = 0; c4 < 4; ++c4)
+      vb[r][c4] = PF_V + t * PF_DH * 2 + 16 * ((2 * c4 + e) ^ fv(t)) + 8 * (r16 & 1);
   }
 
   f32x4_t o[PF_QT][PF_CT];
@@ -132,20 +162,29 @@ __global__ __launch_bounds__(PF_NT) void attn_prefill_kernel(
   for (int qt = 0; qt < PF_QT; ++qt)
 #pragma unroll
     for (int ct = 0; ct < PF_CT; ++ct) o[qt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[PF_QT], l_run[PF_QT];  // of query qw + 16 qt + r16, alike in its four lanes
+  // of query qw + 16 qt + r16: the softmax reference (alike in its four lanes) and this
+  // lane's part of the denominator
+  float m_run[PF_QT], l_run[PF_QT];
+  const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
 #pragma unroll
   for (int qt = 0; qt < PF_QT; ++qt) {
     m_run[qt] = -INFINITY;
     l_run[qt] = 0.f;
   }
 
-  load_block(0);
-  store_block(0);
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __syncthreads();
+  // blocks 0 and 1 (behind the query loads, so waiting for block 0 covers those too)
+  issue_block(0, 0);
+  if (nkb > 1) {
+    issue_block(1, 1);
+    wait_vmcnt<PF_COPIES>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  block_barrier();
   for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + 1 < nkb) load_block(kb + 1);  // in flight while this block is consumed
-    const lds_char_t* tile = lsm + (kb & 1) * PF_TILE;
+    // block kb+2 into the buffer block kb-1 left (every wave finished it before barrier kb)
+    if (kb + 2 < nkb) issue_block(kb + 2, (kb + 2) % PF_NBUF);
+    const lds_char_t* tile = lsm + (kb % PF_NBUF) * PF_TILE;
     if (kb * PF_KB <= qw + 16 * PF_QT - 1) {  // this wave's queries see some key of the block
       // ---- S^T (64 keys x 16 queries per query tile): each K fragment feeds both tiles
       f32x4_t sacc[PF_QT][PF_MT];
@@ -157,24 +196,24 @@ __global__ __launch_bounds__(PF_NT) void attn_prefill_kernel(
       for (int kk = 0; kk < PF_KSTEPS; ++kk)
 #pragma unroll
         for (int mt = 0; mt < PF_MT; ++mt) {
-          const bf16x8_t kf = *(const lds_bf16x8_t*)(tile + (mt >> 1) * 32 * PF_ROW +
-                                                     kb_off[mt & 1][kk & 1] + (kk >> 1) * 128);
+          const bf16x8_t kf = *(const lds_bf16x8_t*)(tile + k_off(mt, kk));
 #pragma unroll
           for (int qt = 0; qt < PF_QT; ++qt)
             sacc[qt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qt][kk], sacc[qt][mt], 0, 0, 0);
         }
       // ---- online softmax (log2 domain) per query tile: lane (g, r16) holds keys
-      //      32 (mt >> 1) + 8 g + 4 (mt & 1) + i of its query; keys after it get weight 0
+      //      32 (mt >> 1) + 8 g + 4 (mt & 1) + i of its query; keys after it get weight 0.
+      //      The maximum is taken on the raw scores (the scale is positive); each weight is
+      //      2^(s scale - m) with one rounding in the fma.  The reference m moves only when a
+      //      block's maximum passes it by more than PF_SLACK (log2 units), so weights stay
+      //      below 2^PF_SLACK and the accumulators are rescaled rarely; every lane keeps its
+      //      own part of the denominator (summed over the four lanes of a query at the end),
+      //      summing the bf16-rounded weights the PV product consumes.
       bf16x8_t pt[PF_QT][2];  // P^T operands of the two 32-key halves
       const bool diagonal = kb * PF_KB + PF_KB - 1 > qw;  // some key after some query
 #pragma unroll
       for (int qt = 0; qt < PF_QT; ++qt) {
         const int my_q = qw + 16 * qt + r16;
-        float bmax = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < PF_MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sacc[qt][mt][i] *= scale_log2;
         if (diagonal) {
 #pragma unroll
           for (int mt = 0; mt < PF_MT; ++mt)
@@ -184,13 +223,16 @@ __global__ __launch_bounds__(PF_NT) void attn_prefill_kernel(
               if (key > my_q) sacc[qt][mt][i] = -INFINITY;
             }
         }
+        float bmax = -INFINITY;
 #pragma unroll
         for (int mt = 0; mt < PF_MT; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, sacc[qt][mt][i]);
         bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
         bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-        const float m_new = fmaxf(m_run[qt], bmax);  // finite: key 0 is seen by every query
+        // finite: key 0 is seen by every query
+        const float cand = mul_rn(bmax, scale_log2);
+        const float m_new = cand > m_run[qt] + PF_SLACK ? cand : m_run[qt];
         const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_new);
         float psum = 0.f;
 #pragma unroll
@@ -201,19 +243,18 @@ __global__ __launch_bounds__(PF_NT) void attn_prefill_kernel(
 #pragma unroll
             for (int hlf = 0; hlf < 2; ++hlf) {
               const f32x4_t& sv = sacc[qt][2 * ks + m1];
-              pp[2 * m1 + hlf] = to_bf16x2(__builtin_amdgcn_exp2f(sv[2 * hlf] - m_new),
-                                           __builtin_amdgcn_exp2f(sv[2 * hlf + 1] - m_new));
-              psum += static_cast<float>(pp[2 * m1 + hlf][0]) + static_cast<float>(pp[2 * m1 + hlf][1]);
+              pp[2 * m1 + hlf] =
+                  to_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * hlf], scale_log2, -m_new)),
+                            __builtin_amdgcn_exp2f(__builtin_fmaf(sv[2 * hlf + 1], scale_log2, -m_new)));
+              psum = __builtin_amdgcn_fdot2_f32_bf16(pp[2 * m1 + hlf], ones2, psum, false);
             }
           pt[qt][ks] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
                                                __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3),
                                                0, 1, 2, 3, 4, 5, 6, 7);
         }
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
         l_run[qt] = l_run[qt] * alpha + psum;
         m_run[qt] = m_new;
-        if (__any(alpha != 1.f)) {  // the running maximum moved for some query
+        if (__any(alpha != 1.f)) {  // the reference moved for some query
 #pragma unroll
           for (int ct = 0; ct < PF_CT; ++ct) o[qt][ct] *= alpha;
         }
@@ -228,7 +269,7 @@ __global__ __launch_bounds__(PF_NT) void attn_prefill_kernel(
 #pragma unroll
           for (int r = 0; r < 2; ++r)
             half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4_t*)(tile + ks * 32 * PF_ROW + vb[r][ct & 3] + 128 * (3 + (ct >> 2))));
+                (lds_i16x4_t*)(tile + ks * 32 * PF_DH * 2 + vb[r][ct & 3] + 128 * (ct >> 2)));
           const bf16x8_t vf = __builtin_bit_cast(
               bf16x8_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
@@ -237,10 +278,10 @@ __global__ __launch_bounds__(PF_NT) void attn_prefill_kernel(
         }
     }
     if (kb + 1 < nkb) {
-      // buffer (kb + 1) & 1 was last read in block kb - 1, before the previous barrier
-      store_block((kb + 1) & 1);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __syncthreads();  // publishes block kb + 1; every wave is past its reads of block kb
+      // this wave's copies of block kb+1 landed (block kb+2's may still be in flight)
+      if (kb + 2 < nkb) wait_vmcnt<PF_COPIES>();
+      else wait_vmcnt<0>();
+      block_barrier();  // publishes block kb + 1; every wave is past its reads of block kb
     }
   }
 
@@ -248,13 +289,16 @@ __global__ __launch_bounds__(PF_NT) void attn_prefill_kernel(
 #pragma unroll
   for (int qt = 0; qt < PF_QT; ++qt) {
     const int my_q = qw + 16 * qt + r16;
+    float l = l_run[qt];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
     if (my_q < T) {
-      const float inv = 1.f / l_run[qt];
+      const float inv = 1.f / l;
       float* dst = out + ((tok0 + my_q) * H + h) * PF_DH + 4 * g;
 #pragma unroll
       for (int ct = 0; ct < PF_CT; ++ct) *reinterpret_cast<f32x4_t*>(dst + 16 * ct) = o[qt][ct] * inv;
       if (lse_out != nullptr && g == 0)
-        lse_out[(tok0 + my_q) * H + h] = (m_run[qt] + __log2f(l_run[qt])) * LN2;
+        lse_out[(tok0 + my_q) * H + h] = (m_run[qt] + __log2f(l)) * LN2;
     }
   }
 }
