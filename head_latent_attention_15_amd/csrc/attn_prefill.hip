@@ -22,9 +22,9 @@
 // kb.  Per key block a wave computes S^T = K Q^T (tokens as the MFMA M dimension, 4 key
 // tiles x 6 k-steps x 2 query tiles = 48 MFMAs, each K fragment feeding both query tiles,
 // Q resident in VGPRs; the key permutation inside each 32-key half makes the C layout of
-// S^T the B layout of P^T), an online softmax per query (running maximum, accumulators
-// rescaled when it moves), and O^T += V^T P^T (32 MFMAs, each V^T fragment feeding both
-// query tiles).  Workgroups of late query blocks (the most keys) are numbered first.
+// S^T the B layout of P^T), an online softmax per query (a reference that moves with the
+// running maximum when that passes it by a set margin, accumulators rescaled then), and
+// O^T += V^T P^T (32 MFMAs, each V^T fragment feeding both query tiles).  Workgroups of late query blocks (the most keys) are numbered first.
 #include "attn_common.h"
 #include "launchers.h"
 
