@@ -292,3 +292,33 @@ def test_linear_deterministic_validation():
     assert L.mla_linear_deterministic(*args(wdt=0)) == mla.MLA_ERR_UNSUPPORTED
     assert L.mla_linear_deterministic(*args(ldy=5122)) == mla.MLA_ERR_UNSUPPORTED
     assert L.mla_linear_deterministic(*args(bytes=need - 1)) == mla.MLA_ERR_WORKSPACE
+
+
+def test_linear_deterministic_append_validation():
+    """mla_linear_deterministic_append refuses bad arguments before launching: the product's
+    own checks, a batch that is not M, a column range past N, a cache that is not bf16, and
+    column offsets that are not multiples of 4."""
+    L = mla.lib
+    M, N, K = 64, 2112, 5120
+    need = L.mla_linear_deterministic_workspace_bytes(M, N, K)
+    assert need > 0
+
+    def call(**k):
+        shp = mla._PagedShape(k.get("batch", M), 1, k.get("d_c", 512), k.get("d_r", 64), 64, 33,
+                              2112)
+        return L.mla_linear_deterministic_append(
+            k.get("x", FAKE), 0, K, FAKE, 1, M, N, K, FAKE, N, k.get("ws", FAKE),
+            k.get("bytes", need), k.get("col", 1536), k.get("before", FAKE), FAKE,
+            k.get("cache", FAKE), k.get("base", 10000.0), ctypes.byref(shp), k.get("cdt", 1), None)
+
+    assert call(x=None) == mla.MLA_ERR_NULL
+    assert call(cache=None) == mla.MLA_ERR_NULL
+    assert call(before=None) == mla.MLA_ERR_NULL
+    assert call(batch=63) == mla.MLA_ERR_SHAPE
+    assert call(col=1600) == mla.MLA_ERR_SHAPE        # 1600 + 512 + 64 > 2112
+    assert call(col=-4) == mla.MLA_ERR_SHAPE
+    assert call(base=float("inf")) == mla.MLA_ERR_SHAPE
+    assert call(cdt=0) == mla.MLA_ERR_UNSUPPORTED     # fp32 cache rows
+    assert call(cdt=2) == mla.MLA_ERR_UNSUPPORTED     # fp8 cache rows
+    assert call(col=1534) == mla.MLA_ERR_UNSUPPORTED  # not a multiple of 4
+    assert call(bytes=need - 1) == mla.MLA_ERR_WORKSPACE
