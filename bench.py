@@ -567,6 +567,19 @@ def config_row(mla, torch, inp, name, num_cus, steps, n_copies, kernel="auto", f
         flat[k % n_copies]()
     torch.cuda.synchronize()
     flat_ms = timed_ms(torch, lambda k: flat[k % n_copies](), steps)
+    fp8_ms = None
+    if flattened:  # the same work list over fp8 rows (quantised on the GPU, outside the timing)
+        f8 = []
+        for c in caches:
+            f8.append(torch.empty(c.shape[:-1] + (656,), dtype=torch.uint8, device=dev))
+            mla.mla_quantize_cache(c, f8[-1])
+        flat8 = [mla.bind(mla.mla_decode_ragged, q_lat, q_pe, c, bt, sld, inp["scale"], ws, out, lse)
+                 for c in f8]
+        for k in range(2 * n_copies):
+            flat8[k % n_copies]()
+        torch.cuda.synchronize()
+        fp8_ms = timed_ms(torch, lambda k: flat8[k % n_copies](), steps)
+        del flat8, f8
     step_ms = flat_ms if flattened else split_ms
     tokens = int(sl.sum())
     attn_bytes = tokens * ROW_BYTES + B * H * 576 * 2 + bt.numel() * 4 + B * 4
@@ -584,7 +597,9 @@ def config_row(mla, torch, inp, name, num_cus, steps, n_copies, kernel="auto", f
             "step_frac": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "attn_GBps": round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1),
             "attn_frac": round(attn_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "query_tokens_per_s": round(B / (step_ms * 1e-3), 1)}
+            "query_tokens_per_s": round(B / (step_ms * 1e-3), 1),
+            "us_flattened_fp8_rows": round(fp8_ms * 1e3, 2) if fp8_ms else None,
+            "fp8_cache_GBps": round(tokens * 656 / (fp8_ms * 1e-3) / 1e9, 1) if fp8_ms else None}
 
 
 def _us(ms):

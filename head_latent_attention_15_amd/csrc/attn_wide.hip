@@ -563,8 +563,8 @@ void attn_wide_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restri
 // Flattened work list for ragged batches (ragged_plan.h): range r of the batch's cached
 // pages goes to one workgroup, which runs wide_split on each sequence piece inside it; the
 // partial of head h from piece i of sequence b is row first_b H + h count_b + i, as in
-// attn_mfma_ragged_kernel, so the same slot-table combine merges them.
-template <typename OT>
+// attn_mfma_ragged_kernel, so the same slot-table combine merges them.  FP8: fp8 cache rows.
+template <typename OT, bool FP8>
 __global__ __launch_bounds__(WW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_wide_ragged_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* __restrict__ q_pe,
                              const bf16raw* __restrict__ cache,
@@ -598,7 +598,7 @@ void attn_wide_ragged_kernel(const bf16raw* __restrict__ q_lat, const bf16raw* _
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int j1 = pc.j1;
-    wide_split<OT, 4, false>(q_lat, q_pe, cache, block_table, H, log2P, max_pages, scale_log2, o_part,
+    wide_split<OT, 4, FP8>(q_lat, q_pe, cache, block_table, H, log2P, max_pages, scale_log2, o_part,
                       lse_part, pc.b, pc.b, pc.j0, [&] { return j1; },
                    static_cast<int64_t>(pc.first) * H + pc.index, pc.count);
   }
@@ -629,10 +629,11 @@ bool attn_wide_supported(const PagedArgs& a) {
 }
 
 hipError_t launch_attn_wide_ragged(const PagedArgs& a, int grid, int* seq_slots, int* err,
-                                   hipStream_t st) {
+                                   hipStream_t st, bool fp8) {
   if (!attn_wide_supported(a) || !a.part_bf16) return hipErrorInvalidValue;
   const float log2e = 1.4426950408889634f;
-  hipLaunchKernelGGL((attn_wide_ragged_kernel<bf16raw>), dim3(grid), dim3(WW * 64), 0, st,
+  const auto kernel = fp8 ? attn_wide_ragged_kernel<bf16raw, true> : attn_wide_ragged_kernel<bf16raw, false>;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(WW * 64), 0, st,
                      static_cast<const bf16raw*>(a.q_lat), static_cast<const bf16raw*>(a.q_pe),
                      static_cast<const bf16raw*>(a.cache), a.block_table, a.seq_lens, a.B, a.H,
                      __builtin_ctz(static_cast<unsigned>(a.page_size)), a.max_pages,

@@ -66,9 +66,10 @@ bool attn_cols_supported(const PagedArgs& a);
 // MFMA (each LDS fragment read feeds 32 heads).
 hipError_t launch_attn_wide_bf16_512_64(const PagedArgs& a, hipStream_t s);
 bool attn_wide_supported(const PagedArgs& a);
-// Its flattened ragged work list (as launch_attn_mfma_ragged; bf16 partials).
+// Its flattened ragged work list (as launch_attn_mfma_ragged; bf16 partials); fp8: the
+// cache holds fp8 rows.
 hipError_t launch_attn_wide_ragged(const PagedArgs& a, int grid, int* seq_slots, int* err,
-                                   hipStream_t s);
+                                   hipStream_t s, bool fp8 = false);
 // The same split-grid kernel over fp8 latent rows (raw rows staged in LDS and converted to bf16 there).
 hipError_t launch_attn_wide_fp8(const PagedArgs& a, hipStream_t s);
 

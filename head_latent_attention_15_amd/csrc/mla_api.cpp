@@ -389,10 +389,11 @@ mla_status_t mla_decode_ragged(const void* q_lat, const void* q_pe, const void* 
   a.num_splits = 1;
   a.pages_per_split = 1;
   a.n_q = 1;
-  if (dtype != MLA_BF16 || !mla::attn_mfma_supported(a))
-    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_ragged: needs BF16, d_latent 512, d_rope 64, "
-                "H in {16, 32, 64, 128}, pages of >= 32 tokens (a power of two) and 16-byte "
-                "aligned tensors");
+  const bool fp8 = dtype == MLA_FP8;
+  if ((dtype != MLA_BF16 && !fp8) || !mla::attn_mfma_supported(a))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_ragged: needs BF16 or FP8 rows, d_latent 512, "
+                "d_rope 64, H in {16, 32, 64, 128} (128 for FP8), pages of >= 32 tokens (a power "
+                "of two) and 16-byte aligned tensors");
   if ((reinterpret_cast<uintptr_t>(out) & 15) != 0)
     return fail(MLA_ERR_SHAPE, "mla_decode_ragged: out is not 16-byte aligned");
   const int grid = ragged_grid(a.num_pages);
@@ -407,9 +408,12 @@ mla_status_t mla_decode_ragged(const void* q_lat, const void* q_pe, const void* 
   a.lse_part = reinterpret_cast<float*>(ws + l.lse_off);
   a.o_part = ws + l.part_off;
   a.part_bf16 = 1;
+  if (fp8 && !mla::attn_wide_supported(a))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode_ragged: FP8 rows need H = 128 and 16-byte "
+                "aligned tensors");
   hipStream_t s = as_stream(stream);
   st = mla::attn_wide_supported(a)
-           ? launched(mla::launch_attn_wide_ragged(a, grid, seq_slots, seq_slots + 2 * a.B, s),
+           ? launched(mla::launch_attn_wide_ragged(a, grid, seq_slots, seq_slots + 2 * a.B, s, fp8),
                       "attention (flattened ragged work list, 32 heads per wavefront)")
            : launched(mla::launch_attn_mfma_ragged(a, grid, seq_slots, seq_slots + 2 * a.B, s),
                       "attention (flattened ragged work list)");

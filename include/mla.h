@@ -376,8 +376,9 @@ int32_t mla_decode_fused_single_launch(const mla_paged_shape_t* shape, int32_t n
  * Returns 0 for a NULL shape or a size below 1. */
 size_t mla_decode_ragged_workspace_bytes(const mla_paged_shape_t* shape);
 
-/* Decode for ragged batches (one query token per sequence, lengths free, BF16,
- * d_latent 512, d_rope 64, H in {16, 32, 64, 128}): the same result as mla_decode, with the
+/* Decode for ragged batches (one query token per sequence, lengths free, BF16 rows with
+ * H in {16, 32, 64, 128} or MLA_FP8 rows with H = 128, d_latent 512, d_rope 64): the same
+ * result as mla_decode, with the
  * work cut for the device instead of per sequence.  The cached pages of the whole batch,
  * concatenated in sequence order, are divided into one equal range per compute unit, so
  * every workgroup streams the same number of pages whatever the mix of lengths; a range

@@ -245,3 +245,29 @@ def test_fp8_dsv2_b32_t4k_full(mla, kernel):
     m, r = assert_bf16(host64(out), o_ref, "fp8 dsv2_b32_t4k")
     print(f"fp8 dsv2_b32_t4k: max-abs {m:.3e} rel-L2 {r:.3e}")
     assert errors(host64(lse), lse_ref)[0] <= 2e-2
+
+
+def test_fp8_ragged_work_list(mla):
+    """mla_decode_ragged over fp8 rows (flattened work list, kernel with 32 heads per
+    wavefront): ragged lengths incl. an empty sequence and single-tile pieces, a permuted
+    pool, every output against the oracle on the dequantised rows."""
+    lens = [0, 1, 33, 64, 700, 2050, 4097, 95]
+    inp = _fp8_problem(77, len(lens), lens)
+    say("fp8 ragged work list")
+    q_lat, q_pe = dev(inp["q_lat"]), dev(inp["q_pe"])
+    cache = dev(torch.from_numpy(inp["fp8"]))
+    bt, sl = dev(inp["block_table"]), dev(inp["seq_lens"])
+    B = len(lens)
+    ws = torch.full((mla.mla_decode_ragged_workspace_bytes(cache, bt, 128, 512),), 0xFF,
+                    dtype=torch.uint8, device="cuda")
+    out = torch.full((B, 128, 512), float("nan"), device="cuda")
+    lse = torch.full((B, 128), float("nan"), device="cuda")
+    mla.mla_decode_ragged(q_lat, q_pe, cache, bt, sl, inp["scale"], ws, out, lse)
+    torch.cuda.synchronize()
+    assert int(ws[8 * B:8 * B + 4].view(torch.int32).item()) == 0
+    o_ref, lse_ref = oracle_fp8(inp)
+    empty = [b for b, n in enumerate(lens) if n == 0]
+    rest = [b for b, n in enumerate(lens) if n > 0]
+    assert torch.all(out[empty] == 0) and torch.all(torch.isinf(lse[empty]))
+    assert_bf16(host64(out)[rest], o_ref[rest], "fp8 ragged")
+    assert errors(host64(lse)[rest], lse_ref[rest])[0] <= 2e-2
