@@ -100,9 +100,9 @@ __device__ __forceinline__ void chain_drain(f32x16_t& x, f32x16_t& y) {
 // in the score loop (6; 4 where the caller keeps more state live, as the ragged kernel).
 // FP8: the cache holds fp8 rows (656 bytes); each tile is copied raw into one of two
 // staging buffers, all of its copies right after the barrier two tiles ahead of its use,
-// and converted by the whole workgroup into one of three bf16 tile buffers one tile ahead
-// (fp8_convert_chunk: code times its block's power-of-two scale, exact in bf16), so the
-// score and PV steps are the bf16 ones.
+// and converted by the whole workgroup into one of three bf16 tile buffers one tile ahead,
+// spread over the score steps of the tile before (code times its block's power-of-two
+// scale, exact in bf16), so the score and PV steps are the bf16 ones.
 template <typename OT, int KRING, bool FP8, typename SplitEnd>
 __device__ __forceinline__ void wide_split(
     const bf16raw* __restrict__ q_lat, const bf16raw* __restrict__ q_pe,
@@ -309,7 +309,7 @@ __device__ __forceinline__ void wide_split(
   // score steps (FIRST) issue the copies of tiles 1 and 2, one every second step.  TAIL:
   // some copied tile reaches past the split's last token (its rows are clamped).
   auto copy_tb = [&](int it) { return j0 + (it + 2 < ntiles ? it + 2 : min(it, ntiles - 1)) * TILE; };
-  auto scores = [&](int it, auto first, auto tail) -> f32x16_t {
+  auto scores = [&](int it, auto first, auto tail, auto conv) -> f32x16_t {
     constexpr bool FIRST = decltype(first)::value;
     const lds_char_t* tile = tile_at(it);
     const int tb2 = copy_tb(it);
@@ -341,11 +341,26 @@ __device__ __forceinline__ void wide_split(
       } else if (kk % 4 == 0) {
         issue_copy(base2, last2, lds2, kk / 4, tail);
       }
+      conv(kk);
       __builtin_amdgcn_sched_barrier(0);
     }
     chain_drain(s0, s1);
     return s0 + s1;
   };
+
+  // fp8 rows: the conversion of raw tile `it` into its bf16 buffer spread over the score
+  // steps (latent chunk u at step 4 u, the k^R chunk at step 32)
+  auto conv_of = [&](int it, bool on) {
+    const lds_char_t* csrc = lsm + W8_STAGE + (it & 1) * FP8_STAGE_BYTES;
+    lds_char_t* cdst = const_cast<lds_char_t*>(tile_at(it));
+    return [=](int kk) {
+      if (on && (kk & 3) == 0) {
+        if (kk < 32) fp8_convert_latent(csrc, cdst, tid + WW * 64 * (kk >> 2));
+        else fp8_copy_rope(csrc, cdst, tid);
+      }
+    };
+  };
+  const auto no_conv = [](int) {};
 
   // tokens at or past j1 (last tile of the split only) get weight 0
   auto mask_tail = [&](f32x16_t& sc, int it) {
@@ -434,7 +449,9 @@ __device__ __forceinline__ void wide_split(
   }
   bf16x8_t p0, p1;
   {
-    f32x16_t sc = scores(0, std::true_type(), clamped);
+    f32x16_t sc;
+    if constexpr (FP8) sc = scores(0, std::true_type(), clamped, conv_of(1, ntiles > 1));
+    else sc = scores(0, std::true_type(), clamped, no_conv);
     mask_tail(sc, 0);
     float tmax = sc[0];
 #pragma unroll
@@ -448,26 +465,23 @@ __device__ __forceinline__ void wide_split(
     }
     soft_done(p0, p1);
   }
-  if constexpr (FP8) {
-    if (ntiles > 1) fp8_convert(1, 1);
-  }
   for (int it = 1; it < ntiles; ++it) {
     f32x16_t sc;
     if constexpr (FP8) {
       // Barrier it publishes bf16 tile it (converted during tile it-1) and raw tile it+1
       // (copied since barrier it-1).  Then raw tile it+2 goes to the staging buffer raw tile
-      // it left, and raw tile it+1 is converted into the buffer tile it-2 left.
+      // it left, and raw tile it+1 is converted into the buffer tile it-2 left during the
+      // score steps of tile it.
       wait_vmcnt<0>();
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       block_barrier();
       if (it + 2 < ntiles) fp8_issue_tile(copy_src(j0 + (it + 2) * TILE), j0 + (it + 2) * TILE, it & 1);
-      if (it + 1 < ntiles) fp8_convert((it + 1) & 1, (it + 1) % NB);
-      sc = scores(it, std::false_type(), unclamped);
+      sc = scores(it, std::false_type(), unclamped, conv_of(it + 1, it + 1 < ntiles));
     } else {
       wait_vmcnt<W_COPIES>();  // own copies of tile it landed (tile it+1's may be in flight)
       block_barrier();
-      sc = j1 - copy_tb(it) >= TILE ? scores(it, std::false_type(), unclamped)
-                                    : scores(it, std::false_type(), clamped);
+      sc = j1 - copy_tb(it) >= TILE ? scores(it, std::false_type(), unclamped, no_conv)
+                                    : scores(it, std::false_type(), clamped, no_conv);
     }
     mask_tail(sc, it);
     bf16x8_t n0, n1;
