@@ -13,7 +13,10 @@
 // a tile are flushed when the run leaves the tile: into y with fp32 atomics (y zeroed first
 // unless the caller accumulates), or, in the deterministic form, with plain stores into the
 // tile's own slot of a caller workspace, which gemm_stream_reduce then sums in one fixed
-// order (slice, then run) into y.
+// order (slice, then run) into y.  For [W^DQ; W^DKV; W^KR] h that summing launch can also
+// write the new token's cache row [c^KV | RoPE(k^R)] (qiita.com/joule "RoPE の扱い";
+// "論文解説: DeepSeek-V2 …", "Decoupled RoPE"): it is the first point where whole rows of
+// c^KV and k^R exist, since the product splits their k range over workgroups.
 //
 // A workgroup has two roles.  Waves 0-3 (consumers) own TN column tiles of 16 each and all
 // four 16-row tiles of x; the bf16 weight rows go from HBM straight into MFMA B-operand
