@@ -244,14 +244,15 @@ __device__ __forceinline__ void wide_split(
 #pragma unroll
       for (int k = 0; k < 16; ++k) qf[k0 + k] = *(const lds_bf16x8_t*)(qa + 16 * (33 * n32 + 2 * k + hf));
     };
-#pragma unroll
-    for (int i = 0; i < QC; ++i) *(lds_bf16x8_t*)(qc + 16 * (9 * (8 * i + (lane >> 3)) + (lane & 7))) = rawc[i];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) qf[32 + k] = *(const lds_bf16x8_t*)(qc + 16 * (9 * n32 + 2 * k + hf));
+    // in the order the loads were issued (and land): q~ features 0-255, 256-511, then q^R
     stage_a(rawa);
     unstage_a(0);  // (LDS operations of one wave complete in order: no wait between)
     stage_a(rawb);
     unstage_a(16);
+#pragma unroll
+    for (int i = 0; i < QC; ++i) *(lds_bf16x8_t*)(qc + 16 * (9 * (8 * i + (lane >> 3)) + (lane & 7))) = rawc[i];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qf[32 + k] = *(const lds_bf16x8_t*)(qc + 16 * (9 * n32 + 2 * k + hf));
   }
   lds_i32_t* const ptab = (lds_i32_t*)(lsm + PTAB);
   // tile buffer of tile it; with three buffers the offset is made opaque, since the compiler
