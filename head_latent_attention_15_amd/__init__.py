@@ -110,7 +110,7 @@ def header_functions() -> list[str]:
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m head_latent_attention_15_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python head_latent_attention_15_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in _SIGNATURES.items():
         fn = getattr(lib, name)

@@ -1,6 +1,6 @@
 """Build libmla.so (HIP, gfx950) in-tree.
 
-    python -m head_latent_attention_15_amd.build        # or: python head_latent_attention_15_amd/build.py
+    python head_latent_attention_15_amd/build.py   (the package itself needs the library to import)
 
 Compiles every source under csrc/ with hipcc for --offload-arch=gfx950 and links the
 shared library next to this file.  Object files go to _build/ at the repository root.
