@@ -23,7 +23,7 @@ offline folds, and the fp64 CPU oracle on all host cores and on one thread.
 Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline] [--no-layer]
-                    [--no-configs] [--headline-only]
+                    [--no-configs] [--headline-only] [--layer-only] [--prefill-only]
 """
 from __future__ import annotations
 
@@ -646,6 +646,8 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline step and its attention alone (for a kernel "
                          "trace of exactly those launches)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill attention (for a kernel trace of its launches)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for --pmc runs)")
     args = ap.parse_args()
@@ -678,6 +680,10 @@ def main():
         row = config_row(mla, torch, gen[0](), args.config, num_cus, args.steps, gen[1],
                          flattened=gen[2])
         print(json.dumps({args.config: row}), flush=True)
+        return
+    if args.prefill_only:
+        log("prefill only")
+        print(json.dumps({"prefill": prefill_row(mla, torch, args.steps)}), flush=True)
         return
     if args.layer_only:
         log("layer_b64_t2k only")
